@@ -1,0 +1,285 @@
+/*
+ * Plain fp64 CPU oracle for packed variable-length conv1d + selective scan.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this file's library. It shares no
+ * code, header, table or helper with the HIP library, and it never runs on
+ * the product path.
+ *
+ * Sources (pages, by address):
+ *   [P5] Shanghai AI Lab HPC/NDS article on packed variable-length Mamba-1
+ *        training, https://gitcode.csdn.net/69d8cc1b54b52172bc6872cb.html
+ *   [P1] practitioner article on variable-length Mamba-1 training,
+ *        https://lpnh.cn/news/2780078
+ *
+ * What is computed is the plain definition the packed method is meant to
+ * reach: every packed sequence behaves exactly as if it were run alone with
+ * zero initial conv and SSM state ([P5] "Mamba block中的步骤": only the
+ * sequence-wise steps see neighbouring tokens; [P5] "基本原理": reset the SSM
+ * state at every sequence boundary; [P1] section 3.2: zero states at each
+ * document start). Every loop below walks tokens in packed order and applies
+ * that reset at the head tokens, so packed and per-sequence runs execute the
+ * same floating-point operations in the same order.
+ *
+ * Inputs are fp64 arrays (the caller widens the stored bf16/fp32 bits
+ * exactly). Layouts are token-major: a (T, D) array has element (t, d) at
+ * t*D + d; B and C are (T, N); A is (D, N); the conv weight is (D, W) with
+ * w[d*W + W-1] multiplying the current token (PyTorch depthwise conv1d
+ * cross-correlation order). Channel ranges [d0, d1) let a caller split the
+ * channels over threads; channels never interact except through the sums
+ * dB and dC, which each call accumulates into the buffers it is given.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_CU_SEQLENS 3
+#define ORACLE_ERR_ALLOC 6
+
+static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+/*
+ * position_indices from cu_seqlens. [P5] "conv1d_pack 算子": pack() emits, for
+ * every packed token, its position inside its own sequence; lengths
+ * [4,2,3,7] give 0,1,2,3,0,1,0,1,2,0,1,2,3,4,5,6. cu_seqlens follows the
+ * FlashAttention varlen convention ([P5] "基本原理"): cu[0] = 0, cu[nseq] = T,
+ * non-decreasing (zero-length sequences allowed).
+ * head[t] = 1 marks the first token of a sequence (pos 0).
+ */
+int oracle_pack_indices(const int32_t *cu, int32_t nseq, int64_t T, int32_t *pos, uint8_t *head)
+{
+    if (nseq < 0 || T < 0) return ORACLE_ERR_CU_SEQLENS;
+    if (cu[0] != 0 || (int64_t)cu[nseq] != T) return ORACLE_ERR_CU_SEQLENS;
+    for (int32_t s = 0; s < nseq; ++s)
+        if (cu[s + 1] < cu[s]) return ORACLE_ERR_CU_SEQLENS;
+    for (int32_t s = 0; s < nseq; ++s) {
+        for (int64_t t = cu[s]; t < cu[s + 1]; ++t) {
+            pos[t] = (int32_t)(t - cu[s]);
+            if (head) head[t] = (t == cu[s]) ? 1 : 0;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * conv1d_pack forward. [P5] "conv1d_pack 算子": the causal depthwise conv looks
+ * back W-1 tokens and must stop at its sequence's head token. Tap k (k tokens
+ * back) contributes iff k <= pos[t], i.e. iff token t-k lies in the same
+ * sequence. Result: the zero-left-padded causal conv of each sequence alone.
+ *   v[t,d] = b[d] + sum_{k=0}^{W-1} [k <= pos[t]] * w[d, W-1-k] * x[t-k, d]
+ *   u[t,d] = silu ? v * sigmoid(v) : v
+ * b may be NULL (no bias). v may be NULL.
+ */
+void oracle_conv_fwd(int64_t T, int32_t D, int32_t W, const int32_t *pos,
+                     const double *x, const double *w, const double *b, int silu,
+                     int32_t d0, int32_t d1, double *v, double *u)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t d = d0; d < d1; ++d) {
+            double acc = b ? b[d] : 0.0;
+            for (int32_t k = 0; k < W; ++k)
+                if (k <= pos[t]) acc += w[(int64_t)d * W + (W - 1 - k)] * x[(t - k) * D + d];
+            if (v) v[t * D + d] = acc;
+            u[t * D + d] = silu ? acc * sigmoid(acc) : acc;
+        }
+    }
+}
+
+/*
+ * Selective scan forward with resets. [P5] "SSM_pack算子" and "基本原理": state
+ * flows across packed sequences only through the recurrence, so the state is
+ * reset at every head token. The recurrence is Mamba-1's discretised form
+ * (exp(delta*A) decay, delta*B*u input), per channel d and state n:
+ *   h_t = head(t) ? delta_t B_t u_t : exp(delta_t A) h_{t-1} + delta_t B_t u_t
+ *   y_t = sum_n C_t[n] h_t[n] + Dp[d] u_t
+ *   out_t = y_t * silu(z_t)        (no gate when z is NULL)
+ * At a head the previous state is not read at all (a select, not a multiply
+ * by zero), so a non-finite state can never cross a boundary.
+ * Dp may be NULL (no skip). y and hs may be NULL; hs receives every state,
+ * (T, D, N) at ((t*D)+d)*N + n, for small inspection cases.
+ */
+int oracle_scan_fwd(int64_t T, int32_t D, int32_t N, const int32_t *pos,
+                    const double *u, const double *delta, const double *A,
+                    const double *B, const double *C, const double *Dp, const double *z,
+                    int32_t d0, int32_t d1, double *y, double *out, double *hs)
+{
+    double *h = (double *)calloc((size_t)(N > 0 ? N : 1), sizeof(double));
+    if (!h) return ORACLE_ERR_ALLOC;
+    for (int32_t d = d0; d < d1; ++d) {
+        for (int64_t t = 0; t < T; ++t) {
+            const int head = pos[t] == 0;
+            const double dt = delta[t * D + d];
+            const double uu = u[t * D + d];
+            double acc = 0.0;
+            for (int32_t n = 0; n < N; ++n) {
+                const double bu = dt * B[t * N + n] * uu;
+                if (head) {
+                    h[n] = bu;
+                } else {
+                    const double a = exp(dt * A[(int64_t)d * N + n]);
+                    h[n] = a * h[n] + bu;
+                }
+                acc += C[t * N + n] * h[n];
+                if (hs) hs[(t * D + d) * N + n] = h[n];
+            }
+            if (Dp) acc += Dp[d] * uu;
+            if (y) y[t * D + d] = acc;
+            out[t * D + d] = z ? acc * (z[t * D + d] * sigmoid(z[t * D + d])) : acc;
+        }
+    }
+    free(h);
+    return ORACLE_OK;
+}
+
+/*
+ * Selective scan backward: the chain rule of oracle_scan_fwd, written out.
+ * Given dout = dL/dout (T, D):
+ *   g = dout * silu(z)                      (dL/dy)
+ *   dz = dout * y * s * (1 + z (1 - s)),  s = sigmoid(z)
+ *   dDp[d] = sum_t g u,   du starts at g * Dp[d]
+ * then per state n, t descending, with carry c (dL/dh_t through h_{t+1}):
+ *   dh = g C_t[n] + c
+ *   dC[t,n] += g h_t[n]
+ *   dB[t,n] += dh delta_t u_t
+ *   du[t]   += dh delta_t B_t[n]
+ *   ddelta[t] += dh (B_t[n] u_t + [not head] A a_t h_{t-1})
+ *   dA[d,n] += [not head] dh delta_t a_t h_{t-1}
+ *   c = [not head] a_t dh        ([P5] "基本原理": no gradient crosses a head)
+ * with a_t = exp(delta_t A[d,n]). dB and dC (T, N) are ACCUMULATED into (the
+ * caller zeroes them, and sums per-thread buffers); all other outputs are
+ * overwritten for channels [d0, d1). Dp, z may be NULL; dz may be NULL.
+ */
+int oracle_scan_bwd(int64_t T, int32_t D, int32_t N, const int32_t *pos,
+                    const double *u, const double *delta, const double *A,
+                    const double *B, const double *C, const double *Dp, const double *z,
+                    const double *dout, int32_t d0, int32_t d1,
+                    double *du, double *ddelta, double *dA, double *dB, double *dC,
+                    double *dDp, double *dz)
+{
+    double *hs = (double *)malloc((size_t)(T > 0 ? T : 1) * (size_t)(N > 0 ? N : 1) * sizeof(double));
+    double *ys = (double *)malloc((size_t)(T > 0 ? T : 1) * sizeof(double));
+    double *c = (double *)calloc((size_t)(N > 0 ? N : 1), sizeof(double));
+    if (!hs || !ys || !c) { free(hs); free(ys); free(c); return ORACLE_ERR_ALLOC; }
+    for (int32_t d = d0; d < d1; ++d) {
+        /* forward, keeping every state of this channel */
+        for (int64_t t = 0; t < T; ++t) {
+            const int head = pos[t] == 0;
+            const double dt = delta[t * D + d];
+            const double uu = u[t * D + d];
+            double acc = 0.0;
+            for (int32_t n = 0; n < N; ++n) {
+                const double bu = dt * B[t * N + n] * uu;
+                double hn;
+                if (head) {
+                    hn = bu;
+                } else {
+                    const double a = exp(dt * A[(int64_t)d * N + n]);
+                    hn = a * hs[(t - 1) * N + n] + bu;
+                }
+                hs[t * N + n] = hn;
+                acc += C[t * N + n] * hn;
+            }
+            if (Dp) acc += Dp[d] * uu;
+            ys[t] = acc;
+        }
+        /* reverse */
+        for (int32_t n = 0; n < N; ++n) c[n] = 0.0;
+        double dDp_acc = 0.0;
+        double *dA_d = dA + (int64_t)d * N;
+        for (int32_t n = 0; n < N; ++n) dA_d[n] = 0.0;
+        for (int64_t t = T - 1; t >= 0; --t) {
+            const int head = pos[t] == 0;
+            const double dt = delta[t * D + d];
+            const double uu = u[t * D + d];
+            const double go = dout[t * D + d];
+            double g = go;
+            if (z) {
+                const double zz = z[t * D + d];
+                const double s = sigmoid(zz);
+                g = go * (zz * s);
+                if (dz) dz[t * D + d] = go * ys[t] * s * (1.0 + zz * (1.0 - s));
+            } else if (dz) {
+                dz[t * D + d] = 0.0;
+            }
+            double du_acc = Dp ? g * Dp[d] : 0.0;
+            double ddt = 0.0;
+            dDp_acc += g * uu;
+            for (int32_t n = 0; n < N; ++n) {
+                const double Bn = B[t * N + n];
+                const double dh = g * C[t * N + n] + c[n];
+                dC[t * N + n] += g * hs[t * N + n];
+                dB[t * N + n] += dh * dt * uu;
+                du_acc += dh * dt * Bn;
+                if (head) {
+                    ddt += dh * (Bn * uu);
+                    c[n] = 0.0;
+                } else {
+                    const double An = A[(int64_t)d * N + n];
+                    const double a = exp(dt * An);
+                    const double hp = hs[(t - 1) * N + n];
+                    ddt += dh * (Bn * uu + An * a * hp);
+                    dA_d[n] += dh * dt * a * hp;
+                    c[n] = a * dh;
+                }
+            }
+            du[t * D + d] = du_acc;
+            ddelta[t * D + d] = ddt;
+        }
+        if (dDp) dDp[d] = dDp_acc;
+    }
+    free(hs); free(ys); free(c);
+    return ORACLE_OK;
+}
+
+/*
+ * conv1d_pack backward: the chain rule of oracle_conv_fwd. [P5]
+ * "conv1d_pack 算子": dx and dweight need the same early stop, and the
+ * backward needs the position W-1 tokens ahead: token s receives from token
+ * s+k only if pos[s+k] >= k (s+k is in the same sequence as s).
+ *   gv[t] = silu ? du[t] * s(v) * (1 + v (1 - s(v))) : du[t],  s = sigmoid
+ *   db[d]        = sum_t gv[t]
+ *   dw[d, W-1-k] = sum_t [k <= pos[t]] gv[t] x[t-k]
+ *   dx[s]        = sum_k [s+k < T and k <= pos[s+k]] w[d, W-1-k] gv[s+k]
+ * b may be NULL; db may be NULL. Overwrites outputs for channels [d0, d1).
+ */
+int oracle_conv_bwd(int64_t T, int32_t D, int32_t W, const int32_t *pos,
+                    const double *x, const double *w, const double *b, int silu,
+                    const double *du, int32_t d0, int32_t d1,
+                    double *dx, double *dw, double *db)
+{
+    double *gv = (double *)malloc((size_t)(T > 0 ? T : 1) * sizeof(double));
+    if (!gv) return ORACLE_ERR_ALLOC;
+    for (int32_t d = d0; d < d1; ++d) {
+        for (int64_t t = 0; t < T; ++t) {
+            double v = b ? b[d] : 0.0;
+            for (int32_t k = 0; k < W; ++k)
+                if (k <= pos[t]) v += w[(int64_t)d * W + (W - 1 - k)] * x[(t - k) * D + d];
+            const double g = du[t * D + d];
+            if (silu) {
+                const double s = sigmoid(v);
+                gv[t] = g * s * (1.0 + v * (1.0 - s));
+            } else {
+                gv[t] = g;
+            }
+        }
+        double dbd = 0.0;
+        for (int64_t t = 0; t < T; ++t) dbd += gv[t];
+        if (db) db[d] = dbd;
+        for (int32_t k = 0; k < W; ++k) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < T; ++t)
+                if (k <= pos[t]) acc += gv[t] * x[(t - k) * D + d];
+            dw[(int64_t)d * W + (W - 1 - k)] = acc;
+        }
+        for (int64_t s = 0; s < T; ++s) {
+            double acc = 0.0;
+            for (int32_t k = 0; k < W; ++k)
+                if (s + k < T && k <= pos[s + k]) acc += w[(int64_t)d * W + (W - 1 - k)] * gv[s + k];
+            dx[s * D + d] = acc;
+        }
+    }
+    free(gv);
+    return ORACLE_OK;
+}

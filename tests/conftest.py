@@ -1,0 +1,24 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def pytest_collection_modifyitems(config, items):
+    # GPU tests fail loudly on a box without a GPU instead of silently passing;
+    # on the CPU container they are deselected with -m "not gpu".
+    pass
+
+
+@pytest.fixture(scope="session")
+def orc():
+    import oracle
+    return oracle.get()

@@ -1,0 +1,396 @@
+"""Pins of the fp64 oracle against facts fixed by the pages and by mathematics.
+
+Each check takes an oracle instance and raises AssertionError on failure, so
+the same checks run against the real oracle (test_oracle_pins.py) and against
+copies with a planted mistake (the mutation test there), which must fail at
+least one of them.
+
+Pages: [P5] Shanghai AI Lab article on packed variable-length Mamba-1
+training (https://gitcode.csdn.net/69d8cc1b54b52172bc6872cb.html);
+[P1] https://lpnh.cn/news/2780078 (variable-length Mamba-1 training).
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def read_golden(name: str) -> dict:
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            out[key] = np.array([int(v) for v in vals], dtype=np.int64)
+    return out
+
+
+def cu_of(lengths):
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    return cu
+
+
+def rand_case(rng, lengths, D=3, N=3, W=4, gate=True, skip=True, bias=True):
+    """Small random fp64 case (values need no bf16 rounding here)."""
+    T = int(sum(lengths))
+    c = {
+        "lengths": list(lengths), "cu": cu_of(lengths), "T": T, "D": D, "N": N, "W": W,
+        "x": rng.standard_normal((T, D)),
+        "w": rng.uniform(-0.5, 0.5, (D, W)),
+        "b": rng.standard_normal(D) * 0.3 if bias else None,
+        "delta": np.log1p(np.exp(rng.standard_normal((T, D)) * 0.5 - 2.0)),
+        "A": -rng.uniform(0.5, 4.0, (D, N)),
+        "B": rng.standard_normal((T, N)),
+        "C": rng.standard_normal((T, N)),
+        "Dp": rng.standard_normal(D) if skip else None,
+        "z": rng.standard_normal((T, D)) if gate else None,
+        "dout": rng.standard_normal((T, D)),
+    }
+    return c
+
+
+def rows_of(cu, s):
+    return np.arange(cu[s], cu[s + 1])
+
+
+def _fwd(orc, c, x=None, w=None, b=None, delta=None, A=None, B=None, C=None, Dp=None, z=None):
+    g = lambda k, v: c[k] if v is None else v
+    return orc.forward(g("x", x), g("w", w), g("b", b), g("delta", delta), g("A", A), g("B", B),
+                       g("C", C), g("Dp", Dp), g("z", z), c["cu"])
+
+
+def _bwd(orc, c):
+    return orc.backward(c["x"], c["w"], c["b"], c["delta"], c["A"], c["B"], c["C"], c["Dp"], c["z"],
+                        c["cu"], c["dout"])
+
+
+def _sub(c, s):
+    """Sequence s of case c, alone."""
+    r = rows_of(c["cu"], s)
+    d = dict(c)
+    for k in ("x", "delta", "B", "C", "z", "dout"):
+        if c[k] is not None:
+            d[k] = c[k][r]
+    d["lengths"] = [len(r)]
+    d["cu"] = cu_of([len(r)])
+    d["T"] = len(r)
+    return d
+
+
+# --------------------------------------------------------------------------
+# position_indices ([P5] "conv1d_pack 算子", figure (a))
+# --------------------------------------------------------------------------
+
+def check_golden_pack(orc):
+    g = read_golden("pack_4_2_3_7.txt")
+    assert list(cu_of(g["lengths"])) == list(g["cu_seqlens"])
+    pos, head = orc.pack_indices(g["cu_seqlens"], int(g["cu_seqlens"][-1]))
+    assert pos.tolist() == g["position_indices"].tolist(), pos
+    assert head.tolist() == g["heads"].tolist(), head
+
+
+def check_pack_rejects_bad_cu(orc):
+    bad = [([1, 4, 6], 6), ([0, 4, 3, 6], 6), ([0, 4, 6], 7), ([0, 4, 6], 5)]
+    for cu, T in bad:
+        try:
+            orc.pack_indices(np.array(cu, dtype=np.int32), T)
+        except ValueError:
+            continue
+        raise AssertionError(f"accepted invalid cu_seqlens {cu} with T={T}")
+    # zero-length sequences are allowed and emit nothing
+    pos, head = orc.pack_indices(np.array([0, 2, 2, 5, 5], dtype=np.int32), 5)
+    assert pos.tolist() == [0, 1, 0, 1, 2] and head.tolist() == [1, 0, 1, 0, 0]
+
+
+# --------------------------------------------------------------------------
+# P1: packed == each sequence alone ([P5] "Mamba block中的步骤", "基本原理")
+# --------------------------------------------------------------------------
+
+def check_packed_equals_alone(orc, seeds=range(6)):
+    for seed in seeds:
+        rng = np.random.default_rng(100 + seed)
+        nseq = int(rng.integers(1, 7))
+        lengths = [int(v) for v in rng.integers(1, 10, nseq)]
+        W = int(rng.integers(1, 5))
+        c = rand_case(rng, lengths, W=W, gate=bool(seed % 2 == 0), skip=bool(seed % 3 != 1))
+        F = _fwd(orc, c)
+        G = _bwd(orc, c)
+        sums = {k: 0.0 for k in ("dA", "dD", "dw", "db")}
+        for s in range(nseq):
+            r = rows_of(c["cu"], s)
+            cs = _sub(c, s)
+            Fs = _fwd(orc, cs)
+            Gs = _bwd(orc, cs)
+            for k in ("u", "y", "out"):
+                assert np.array_equal(F[k][r], Fs[k]), (seed, s, k)
+            for k in ("du", "ddelta", "dz", "dx", "dB", "dC"):
+                assert np.array_equal(G[k][r], Gs[k]), (seed, s, k)
+            for k in sums:
+                if Gs[k] is not None:
+                    sums[k] = sums[k] + Gs[k]
+        # P6: packed parameter gradients are the per-sequence (grad-accum) sums
+        for k, v in sums.items():
+            if G[k] is None:
+                continue
+            np.testing.assert_allclose(G[k], v, rtol=1e-12, atol=1e-12, err_msg=f"{k} seed {seed}")
+
+
+# --------------------------------------------------------------------------
+# P2: closed forms
+# --------------------------------------------------------------------------
+
+def check_scan_closed_form(orc):
+    """Constant delta, A, B, C per (channel, state); D = 0; no gate.
+    h_t = sum_{s=head}^{t} a^{t-s} delta B u_s, checked by the O(L^2) sum;
+    for constant u, h_t = delta B u (1 - a^{p+1}) / (1 - a), p = pos[t]."""
+    rng = np.random.default_rng(7)
+    lengths = [5, 1, 8, 3]
+    T = sum(lengths); D, N = 2, 3
+    cu = cu_of(lengths)
+    pos, _ = orc.pack_indices(cu, T)
+    dl = rng.uniform(0.05, 0.5, D)
+    A = -rng.uniform(0.5, 3.0, (D, N))
+    Bc = rng.standard_normal(N); Cc = rng.standard_normal(N)
+    delta = np.tile(dl, (T, 1)); B = np.tile(Bc, (T, 1)); C = np.tile(Cc, (T, 1))
+    u = rng.standard_normal((T, D))
+    y, out, hs = orc.scan_fwd(u, delta, A, B, C, None, None, pos, states=True)
+    for t in range(T):
+        p = int(pos[t])
+        for d in range(D):
+            for n in range(N):
+                a = np.exp(dl[d] * A[d, n])
+                ref = sum(a ** (t - s) * dl[d] * Bc[n] * u[s, d] for s in range(t - p, t + 1))
+                assert abs(hs[t, d, n] - ref) <= 1e-12 * max(1.0, abs(ref)), (t, d, n)
+            yref = sum(Cc[n] * hs[t, d, n] for n in range(N))
+            assert abs(y[t, d] - yref) <= 1e-12 * max(1.0, abs(yref))
+    assert np.array_equal(y, out)  # no gate, no skip
+    uc = np.tile(rng.standard_normal(D), (T, 1))
+    _, _, hs2 = orc.scan_fwd(uc, delta, A, B, C, None, None, pos, states=True)
+    for t in range(T):
+        p = int(pos[t])
+        for d in range(D):
+            for n in range(N):
+                a = np.exp(dl[d] * A[d, n])
+                ref = dl[d] * Bc[n] * uc[t, d] * (1 - a ** (p + 1)) / (1 - a)
+                assert abs(hs2[t, d, n] - ref) <= 1e-11 * max(1.0, abs(ref)), (t, d, n)
+    # A = 0: the geometric sum degenerates to delta B u (p + 1)
+    _, _, hs3 = orc.scan_fwd(uc, delta, np.zeros((D, N)), B, C, None, None, pos, states=True)
+    for t in range(T):
+        ref = (pos[t] + 1) * dl[:, None] * Bc[None, :] * uc[t][:, None]
+        np.testing.assert_allclose(hs3[t], ref, rtol=1e-13, atol=1e-15)
+
+
+def check_conv_closed_form(orc):
+    """Constant x per channel: v = b + x sum_{k <= min(p, W-1)} w[W-1-k]."""
+    rng = np.random.default_rng(8)
+    lengths = [6, 1, 2, 5]
+    T = sum(lengths); D, W = 3, 4
+    pos, _ = orc.pack_indices(cu_of(lengths), T)
+    w = rng.uniform(-0.5, 0.5, (D, W)); b = rng.standard_normal(D)
+    xc = rng.standard_normal(D)
+    x = np.tile(xc, (T, 1))
+    v, u = orc.conv_fwd(x, w, b, pos, silu=True)
+    for t in range(T):
+        m = min(int(pos[t]), W - 1)
+        ref = b + xc * np.array([sum(w[d, W - 1 - k] for k in range(m + 1)) for d in range(D)])
+        np.testing.assert_allclose(v[t], ref, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(u, v / (1 + np.exp(-v)), rtol=1e-14, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# P3: zero state entering every head; non-finite values never cross a head
+# --------------------------------------------------------------------------
+
+def check_zero_state_at_heads(orc):
+    rng = np.random.default_rng(9)
+    c = rand_case(rng, [3, 1, 4, 2, 5])
+    pos, head = orc.pack_indices(c["cu"], c["T"])
+    _, u = orc.conv_fwd(c["x"], c["w"], c["b"], pos)
+    _, _, hs = orc.scan_fwd(u, c["delta"], c["A"], c["B"], c["C"], c["Dp"], c["z"], pos, states=True)
+    for t in np.nonzero(head)[0]:
+        # the state after a head is exactly its own input term: the state that
+        # entered was zero and the decay was never applied
+        ref = (c["delta"][t][:, None] * c["B"][t][None, :]) * u[t][:, None]
+        assert np.array_equal(hs[t], ref), t
+
+
+def check_nonfinite_isolated(orc):
+    rng = np.random.default_rng(10)
+    lengths = [4, 3, 5, 2]
+    c = rand_case(rng, lengths)
+    F0 = _fwd(orc, c)
+    G0 = _bwd(orc, c)
+    cu = c["cu"]
+    for victim, (key, val) in enumerate([("x", np.inf), ("delta", np.nan), ("B", -np.inf), ("z", np.nan)]):
+        bad = {k: (None if c[k] is None else c[k].copy()) for k in ("x", "delta", "B", "z")}
+        t = int(cu[victim]) + 1 if lengths[victim] > 1 else int(cu[victim])
+        bad[key][t] = val
+        F1 = _fwd(orc, c, **bad)
+        cb = dict(c); cb.update(bad)
+        G1 = _bwd(orc, cb)
+        for s in range(len(lengths)):
+            if s == victim:
+                continue
+            r = rows_of(cu, s)
+            for k in ("u", "y", "out"):
+                assert np.array_equal(F1[k][r], F0[k][r]), (key, s, k)
+            for k in ("du", "ddelta", "dz", "dx", "dB", "dC"):
+                assert np.array_equal(G1[k][r], G0[k][r]), (key, s, k)
+
+
+# --------------------------------------------------------------------------
+# P4: special cases that reduce to library routines
+# --------------------------------------------------------------------------
+
+def check_conv_matches_torch(orc):
+    rng = np.random.default_rng(11)
+    for W in (1, 2, 3, 4):
+        lengths = [5, 1, 7, 2]
+        c = rand_case(rng, lengths, D=4, W=W)
+        pos, _ = orc.pack_indices(c["cu"], c["T"])
+        v, _ = orc.conv_fwd(c["x"], c["w"], c["b"], pos, silu=False)
+        for s in range(len(lengths)):
+            r = rows_of(c["cu"], s)
+            xs = torch.from_numpy(c["x"][r].T.copy())[None]             # (1, D, L)
+            wt = torch.from_numpy(c["w"].copy())[:, None, :]            # (D, 1, W)
+            ref = torch.nn.functional.conv1d(xs, wt, torch.from_numpy(c["b"].copy()),
+                                             padding=W - 1, groups=c["D"])[0, :, :len(r)].T.numpy()
+            np.testing.assert_allclose(v[r], ref, rtol=1e-13, atol=1e-14, err_msg=f"W={W} seq {s}")
+
+
+def check_scan_cumsum(orc):
+    """N = 1, A = 0, delta = 1, B = C = 1, D = 0, no gate: a per-sequence cumsum."""
+    rng = np.random.default_rng(12)
+    lengths = [3, 6, 1, 4]
+    T = sum(lengths); D = 3
+    cu = cu_of(lengths)
+    pos, _ = orc.pack_indices(cu, T)
+    u = rng.standard_normal((T, D))
+    ones = np.ones((T, 1))
+    y, out = orc.scan_fwd(u, np.ones((T, D)), np.zeros((D, 1)), ones, ones, None, None, pos)
+    for s in range(len(lengths)):
+        r = rows_of(cu, s)
+        np.testing.assert_allclose(y[r], np.cumsum(u[r], axis=0), rtol=1e-14, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# P5: every gradient against central finite differences of sum(dout * out)
+# --------------------------------------------------------------------------
+
+def check_finite_differences(orc, gate=True, skip=True, bias=True, seed=13, lengths=(4, 2, 3, 7)):
+    rng = np.random.default_rng(seed)
+    c = rand_case(rng, list(lengths), D=3, N=3, W=4, gate=gate, skip=skip, bias=bias)
+    G = _bwd(orc, c)
+
+    def loss(**kw):
+        return float(np.sum(c["dout"] * _fwd(orc, c, **kw)["out"]))
+
+    pairs = [("x", "dx"), ("w", "dw"), ("b", "db"), ("delta", "ddelta"), ("A", "dA"), ("B", "dB"),
+             ("C", "dC"), ("Dp", "dD"), ("z", "dz")]
+    for pk, gk in pairs:
+        if c[pk] is None:
+            continue
+        p = c[pk]
+        fd = np.zeros_like(p)
+        for idx in np.ndindex(p.shape):
+            h = 1e-6 * max(1.0, abs(p[idx]))
+            pp = p.copy(); pp[idx] += h
+            pm = p.copy(); pm[idx] -= h
+            fd[idx] = (loss(**{pk: pp}) - loss(**{pk: pm})) / (2 * h)
+        an = G[gk]
+        scale = max(1e-3, float(np.max(np.abs(an))))
+        err = float(np.max(np.abs(fd - an)))
+        assert err <= 1e-6 * scale, f"{gk}: fd mismatch {err:.3e} (scale {scale:.3e})"
+
+
+# --------------------------------------------------------------------------
+# P7: right-padded layout ([P5] "目前处理变长序列的方法", padding; [P1] 2.2)
+# --------------------------------------------------------------------------
+
+def check_padded_layout(orc):
+    rng = np.random.default_rng(14)
+    lengths = [5, 2, 7, 3]
+    c = rand_case(rng, lengths)
+    F = _fwd(orc, c); G = _bwd(orc, c)
+    Lmax = max(lengths)
+    nseq = len(lengths)
+    cu = c["cu"]
+    # each sequence right-padded with zeros to Lmax; pads continue the position
+    rows = []
+    for s in range(nseq):
+        r = rows_of(cu, s)
+        rows.append(np.concatenate([r, -np.ones(Lmax - len(r), dtype=np.int64)]))
+    rows = np.concatenate(rows)
+    real = rows >= 0
+
+    def pad(a):
+        if a is None:
+            return None
+        out = np.zeros((len(rows),) + a.shape[1:])
+        out[real] = a[rows[real]]
+        return out
+
+    cp = dict(c)
+    for k in ("x", "delta", "B", "C", "z", "dout"):
+        cp[k] = pad(c[k])
+    cp["cu"] = cu_of([Lmax] * nseq)
+    Fp = _fwd(orc, cp); Gp = _bwd(orc, cp)
+    for k in ("u", "y", "out"):
+        assert np.array_equal(Fp[k][real], F[k][rows[real]]), k
+    for k in ("du", "ddelta", "dz", "dx", "dB", "dC"):
+        np.testing.assert_allclose(Gp[k][real], G[k][rows[real]], rtol=1e-13, atol=1e-13, err_msg=k)
+    for k in ("dA", "dD", "dw", "db"):
+        np.testing.assert_allclose(Gp[k], G[k], rtol=1e-12, atol=1e-12, err_msg=k)
+
+
+# --------------------------------------------------------------------------
+# P8: chunk composition with the affine carry operator
+# --------------------------------------------------------------------------
+
+def check_chunk_composition(orc):
+    """Cut the time axis anywhere; summarise each piece as the affine map
+    h_out = P h_in + S (P = 0 once the piece holds a head); composing the maps
+    left to right and re-running each piece from its h_in gives the sequential
+    states. Written here independently of the oracle's loop."""
+    rng = np.random.default_rng(15)
+    lengths = [7, 1, 12, 4, 9]
+    c = rand_case(rng, lengths, D=2, N=3)
+    T = c["T"]
+    pos, head = orc.pack_indices(c["cu"], T)
+    u = rng.standard_normal((T, c["D"]))
+    _, _, hs = orc.scan_fwd(u, c["delta"], c["A"], c["B"], c["C"], None, None, pos, states=True)
+    a = np.exp(c["delta"][:, :, None] * c["A"][None, :, :])                     # (T, D, N)
+    bu = (c["delta"][:, :, None] * c["B"][:, None, :]) * u[:, :, None]
+    for trial in range(5):
+        cuts = sorted(set([0, T] + [int(v) for v in rng.integers(1, T, int(rng.integers(1, 8)))]))
+        hin = np.zeros(a.shape[1:])
+        got = np.zeros_like(hs)
+        for lo, hi in zip(cuts[:-1], cuts[1:]):
+            P = np.ones(a.shape[1:]); S = np.zeros(a.shape[1:])
+            for t in range(lo, hi):
+                if head[t]:
+                    P = np.zeros_like(P); S = bu[t].copy()
+                else:
+                    P = a[t] * P; S = a[t] * S + bu[t]
+            h = hin
+            for t in range(lo, hi):
+                h = bu[t] if head[t] else a[t] * h + bu[t]
+                got[t] = h
+            hin = P * hin + S
+            np.testing.assert_allclose(hin, got[hi - 1], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(got, hs, rtol=1e-12, atol=1e-14)
+
+
+ALL_CHECKS = [
+    check_golden_pack, check_pack_rejects_bad_cu, check_packed_equals_alone, check_scan_closed_form,
+    check_conv_closed_form, check_zero_state_at_heads, check_nonfinite_isolated,
+    check_conv_matches_torch, check_scan_cumsum, check_finite_differences, check_padded_layout,
+    check_chunk_composition,
+]

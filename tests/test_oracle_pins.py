@@ -1,0 +1,85 @@
+"""CPU tests: the oracle against its pins, and the pins against planted mistakes.
+
+The mutation test copies the oracle's C source, plants one plausible mistake
+(a dropped term, an off-by-one, a wrong sign or index, a multiply-by-zero
+reset), builds the copy with gcc, and requires at least one pin to fail.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle as oracle_mod
+from tests import oracle_checks as oc
+
+
+@pytest.mark.parametrize("check", oc.ALL_CHECKS, ids=lambda f: f.__name__)
+def test_pin(orc, check):
+    check(orc)
+
+
+def test_finite_differences_no_gate_no_skip_no_bias(orc):
+    oc.check_finite_differences(orc, gate=False, skip=False, bias=False, seed=21, lengths=(1, 5, 2))
+
+
+def test_finite_differences_single_token_sequences(orc):
+    oc.check_finite_differences(orc, seed=22, lengths=(1, 1, 3, 1))
+
+
+# (function, text as written, planted mistake)
+MUTATIONS = [
+    ("conv: tap kept one step too early", "if (k <= pos[t]) acc += w", "if (k < pos[t]) acc += w"),
+    ("conv: taps in reverse order", "w[(int64_t)d * W + (W - 1 - k)] * x[(t - k) * D + d];\n            if (v)",
+     "w[(int64_t)d * W + k] * x[(t - k) * D + d];\n            if (v)"),
+    ("scan: skip term dropped", "if (Dp) acc += Dp[d] * uu;\n            if (y)", "if (y)"),
+    ("scan: reset multiplies by zero", "h[n] = bu;\n                } else {\n                    const double a = exp(dt * A[(int64_t)d * N + n]);\n                    h[n] = a * h[n] + bu;",
+     "h[n] = exp(dt * A[(int64_t)d * N + n]) * (0.0 * h[n]) + bu;\n                } else {\n                    const double a = exp(dt * A[(int64_t)d * N + n]);\n                    h[n] = a * h[n] + bu;"),
+    ("scan: decay sign flipped", "const double a = exp(dt * A[(int64_t)d * N + n]);\n                    h[n] = a * h[n] + bu;",
+     "const double a = exp(-dt * A[(int64_t)d * N + n]);\n                    h[n] = a * h[n] + bu;"),
+    ("scan: no reset at heads", "const int head = pos[t] == 0;\n            const double dt = delta[t * D + d];\n            const double uu = u[t * D + d];\n            double acc = 0.0;\n            for (int32_t n = 0; n < N; ++n) {\n                const double bu = dt * B[t * N + n] * uu;\n                if (head) {\n                    h[n] = bu;",
+     "const int head = t == 0;\n            const double dt = delta[t * D + d];\n            const double uu = u[t * D + d];\n            double acc = 0.0;\n            for (int32_t n = 0; n < N; ++n) {\n                const double bu = dt * B[t * N + n] * uu;\n                if (head) {\n                    h[n] = bu;"),
+    ("bwd: dA loses the delta factor", "dA_d[n] += dh * dt * a * hp;", "dA_d[n] += dh * a * hp;"),
+    ("bwd: carry crosses heads", "ddt += dh * (Bn * uu);\n                    c[n] = 0.0;", "ddt += dh * (Bn * uu);\n                    c[n] = dh;"),
+    ("bwd: previous state index off by one", "const double hp = hs[(t - 1) * N + n];", "const double hp = hs[t * N + n];"),
+    ("bwd: dz uses the wrong sigmoid derivative", "s * (1.0 + zz * (1.0 - s))", "s * (1.0 + zz * s)"),
+    ("bwd: dB misses u", "dB[t * N + n] += dh * dt * uu;", "dB[t * N + n] += dh * dt;"),
+    ("bwd: dC uses the previous state", "dC[t * N + n] += g * hs[t * N + n];", "dC[t * N + n] += g * (t > 0 ? hs[(t - 1) * N + n] : 0.0);"),
+    ("conv bwd: reverse rule off by one", "if (s + k < T && k <= pos[s + k])", "if (s + k < T && k < pos[s + k])"),
+    ("conv bwd: dw tap index transposed", "dw[(int64_t)d * W + (W - 1 - k)] = acc;", "dw[(int64_t)d * W + k] = acc;"),
+    ("conv bwd: silu derivative drops a term", "gv[t] = g * s * (1.0 + v * (1.0 - s));", "gv[t] = g * s;"),
+    ("pack: heads off by one", "pos[t] = (int32_t)(t - cu[s]);", "pos[t] = (int32_t)(t - cu[s] + (s > 0));"),
+]
+
+
+@pytest.fixture(scope="module")
+def mutant_dir():
+    d = tempfile.mkdtemp(prefix="oracle_mut_")
+    yield d
+    shutil.rmtree(d, ignore_errors=True)
+
+
+@pytest.mark.parametrize("name,orig,planted", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(mutant_dir, name, orig, planted):
+    src = open(oracle_mod._SRC).read()
+    assert src.count(orig) == 1, f"mutation anchor not unique/found: {name}"
+    idx = MUTATIONS.index((name, orig, planted))
+    c_path = os.path.join(mutant_dir, f"m{idx}.c")
+    so_path = os.path.join(mutant_dir, f"m{idx}.so")
+    with open(c_path, "w") as f:
+        f.write(src.replace(orig, planted))
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", c_path, "-o", so_path, "-lm"],
+                   check=True)
+    mut = oracle_mod.Oracle(so_path)
+    failed = []
+    for check in oc.ALL_CHECKS:
+        try:
+            check(mut)
+        except AssertionError:
+            failed.append(check.__name__)
+        except (ValueError, IndexError, FloatingPointError):
+            failed.append(check.__name__)
+    assert failed, f"planted mistake '{name}' passed every pin"
