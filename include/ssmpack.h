@@ -1,0 +1,162 @@
+/*
+ * ssmpack: packed variable-length Mamba-1 sequence operators for MI355X
+ * (gfx950). C ABI of libssmpack.so.
+ *
+ * Pages the operations come from (cited below by tag):
+ *   [P5] Shanghai AI Lab HPC/NDS article on packed variable-length Mamba-1
+ *        training, https://gitcode.csdn.net/69d8cc1b54b52172bc6872cb.html
+ *   [P1] practitioner article on variable-length Mamba-1 training,
+ *        https://lpnh.cn/news/2780078
+ *   [P3] XTuner variable-length attention guide (Packer, cumulative_len,
+ *        position_ids), on pwwt.cn
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are packed and token-major: a (T, D) tensor holds element
+ *    (t, d) at t*D + d, contiguous. T is the total packed token count; a
+ *    batch of packs is passed flattened, one cu_seqlens over all of them.
+ *  - All tensor pointers are DEVICE pointers. The caller owns every buffer;
+ *    the library never allocates. Workspace sizes are queried first.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
+ *    default stream) and returns once its kernels are queued.
+ *  - Host-checkable arguments are validated before anything is launched and
+ *    reported synchronously as an ssmp_status; nothing is launched then.
+ *    Launch failures are reported as SSMP_ERR_HIP. Validity of device-side
+ *    cu_seqlens is reported through varlen_pack_indices' dev_err word.
+ *  - `dtype` (ssmp_dtype) is the storage type of the (T, D) and (T, N)
+ *    tensors. Parameters (A, D skip, conv weight and bias) are always fp32;
+ *    so are their gradients and dB, dC. Activation gradients (du, ddelta,
+ *    dz, dx) use `dtype`. bf16 results are rounded to nearest even from
+ *    fp32 arithmetic; recurrent state and all sums are fp32.
+ *  - Gradient buffers are overwritten, never accumulated into.
+ */
+#ifndef SSMPACK_H
+#define SSMPACK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SSMP_OK = 0,
+    SSMP_ERR_NULL = 1,        /* a required pointer is NULL */
+    SSMP_ERR_SHAPE = 2,       /* a size is out of range, or sizes overflow */
+    SSMP_ERR_CU_SEQLENS = 3,  /* cu_seqlens invalid (written to dev_err) */
+    SSMP_ERR_UNSUPPORTED = 4, /* dtype, d_state or conv width not supported */
+    SSMP_ERR_HIP = 5,         /* a kernel launch failed */
+    SSMP_ERR_WORKSPACE = 6    /* workspace missing or smaller than queried */
+} ssmp_status;
+
+typedef enum { SSMP_F32 = 0, SSMP_BF16 = 1 } ssmp_dtype;
+
+/* Static English text for a status code; never NULL. */
+const char *ssmp_status_string(int status);
+
+/* Version of this ABI (incremented on any incompatible change). */
+int ssmp_abi_version(void);
+
+/*
+ * varlen_pack_indices — position_indices from cu_seqlens.
+ * [P5] section "conv1d_pack 算子", figure (a): pack() emits, per packed token,
+ * its position inside its own sequence (lengths [4,2,3,7] give
+ * 0,1,2,3,0,1,0,1,2,0,1,2,3,4,5,6). cu_seqlens follows the FlashAttention
+ * varlen convention the article keeps ([P5] "基本原理"; [P3] cumulative_len).
+ *
+ *   cu_seqlens  device int32 [nseq+1]: cu[0] = 0, non-decreasing,
+ *               cu[nseq] = T (zero-length sequences allowed)
+ *   pos         device int32 [T] out: pos[t] = t - cu[s] for cu[s] <= t < cu[s+1]
+ *   heads       device uint8 [T] out, nullable: 1 where pos[t] == 0, else 0
+ *   dev_err     device int32 [1] out, nullable: 0 if cu_seqlens is valid,
+ *               else SSMP_ERR_CU_SEQLENS. With an invalid cu_seqlens, pos is
+ *               still written in bounds (0 <= pos[t] <= t) but meaningless.
+ * Host errors: SSMP_ERR_NULL (cu_seqlens or pos NULL with T > 0),
+ * SSMP_ERR_SHAPE (nseq < 1, T < 0, T >= 2^31).
+ */
+int varlen_pack_indices(const int32_t *cu_seqlens, int32_t nseq, int64_t T,
+                        int32_t *pos, uint8_t *heads, int32_t *dev_err, void *stream);
+
+/*
+ * conv1d_pack_fwd — causal depthwise conv of width W that stops at each
+ * sequence's head token, then optional SiLU.
+ * [P5] "conv1d_pack 算子": the conv looks back W-1 tokens and terminates
+ * early at a head; [P1] 2.2: no tap may cross a document boundary.
+ *   u[t,d] = act(b[d] + sum_{k=0}^{min(pos[t],W-1)} w[d,W-1-k] * x[t-k,d])
+ * with act = SiLU if silu != 0, identity otherwise.
+ *   x    (T, D) dtype          w  fp32 (D, W); w[d,W-1] multiplies token t
+ *   b    fp32 (D), nullable    pos int32 (T) from varlen_pack_indices
+ *   u    (T, D) dtype out
+ * Supports 1 <= W <= 4. Taps k > t are never read, whatever pos holds.
+ * Errors: SSMP_ERR_NULL, SSMP_ERR_SHAPE (T < 0, D < 1, T*D >= 2^40),
+ * SSMP_ERR_UNSUPPORTED (W outside 1..4, unknown dtype).
+ */
+int conv1d_pack_fwd(const void *x, const float *w, const float *b, const int32_t *pos, void *u,
+                    int64_t T, int32_t D, int32_t W, int32_t dtype, int32_t silu, void *stream);
+
+/*
+ * conv1d_pack_bwd — gradients of conv1d_pack_fwd given du = dL/du.
+ * [P5] "conv1d_pack 算子": dx and dweight stop early too; the reverse position
+ * comes from pos W-1 tokens ahead: token s receives from s+k only if
+ * pos[s+k] >= k.
+ *   dx (T, D) dtype out;  dw fp32 (D, W) out;  db fp32 (D) out, nullable
+ * workspace: device memory of at least conv1d_pack_bwd_workspace_bytes(T, D, W)
+ * bytes (per-tile partial sums of dw and db; contents need not be
+ * initialised). Sums over tokens are deterministic (fixed order).
+ * Errors as conv1d_pack_fwd, plus SSMP_ERR_WORKSPACE.
+ */
+size_t conv1d_pack_bwd_workspace_bytes(int64_t T, int32_t D, int32_t W);
+int conv1d_pack_bwd(const void *x, const float *w, const float *b, const int32_t *pos,
+                    const void *du, void *dx, float *dw, float *db,
+                    void *workspace, size_t workspace_bytes,
+                    int64_t T, int32_t D, int32_t W, int32_t dtype, int32_t silu, void *stream);
+
+/*
+ * selective_scan_pack_fwd — the selective scan with the state reset to zero
+ * at every head token ([P5] "SSM_pack算子" and "基本原理": the state flows
+ * across packed sequences only through the recurrence, so it is reset at
+ * each boundary). Per channel d and state n:
+ *   h_t = exp(delta_t A[d,n]) h_{t-1} + delta_t B_t[n] u_t   (h_{t-1} = 0 at a head)
+ *   y_t = sum_n C_t[n] h_t[n] + Dskip[d] u_t
+ *   out_t = y_t * SiLU(z_t)                                   (out = y if z is NULL)
+ *   u, delta, z, out  (T, D) dtype;  B, C (T, N) dtype (shared by all channels)
+ *   A  fp32 (D, N);  Dskip fp32 (D), nullable;  pos int32 (T)
+ *   delta is used as given (already positive).
+ * workspace: device memory of selective_scan_pack_workspace_bytes(T, D, N)
+ * bytes. The forward writes fp32 state checkpoints into it that
+ * selective_scan_pack_bwd reads; keep it untouched between the two calls,
+ * and pass the backward the same inputs.
+ * Supports N in {1, 2, 4, 8, 16}.
+ * Errors: SSMP_ERR_NULL, SSMP_ERR_SHAPE, SSMP_ERR_UNSUPPORTED, SSMP_ERR_WORKSPACE.
+ */
+size_t selective_scan_pack_workspace_bytes(int64_t T, int32_t D, int32_t N);
+int selective_scan_pack_fwd(const void *u, const void *delta, const float *A, const void *B,
+                            const void *C, const float *Dskip, const void *z, const int32_t *pos,
+                            void *out, void *workspace, size_t workspace_bytes,
+                            int64_t T, int32_t D, int32_t N, int32_t dtype, void *stream);
+
+/*
+ * selective_scan_pack_bwd — gradients of selective_scan_pack_fwd given
+ * dout = dL/dout, by a reverse scan whose carry is cut at every head (no
+ * gradient crosses a sequence boundary).
+ *   du, ddelta (T, D) dtype out
+ *   dA fp32 (D, N) out; dB, dC fp32 (T, N) out (sums over channels)
+ *   dD fp32 (D) out, nullable (must be NULL iff Dskip is NULL)
+ *   dz (T, D) dtype out, nullable (must be NULL iff z is NULL)
+ * The workspace must hold the forward's checkpoints (same inputs, same
+ * workspace, no call on it in between). Sums over tokens and channels are
+ * deterministic.
+ * Errors as selective_scan_pack_fwd.
+ */
+int selective_scan_pack_bwd(const void *u, const void *delta, const float *A, const void *B,
+                            const void *C, const float *Dskip, const void *z, const int32_t *pos,
+                            const void *dout, void *workspace, size_t workspace_bytes,
+                            void *du, void *ddelta, float *dA, float *dB, float *dC,
+                            float *dD, void *dz,
+                            int64_t T, int32_t D, int32_t N, int32_t dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSMPACK_H */

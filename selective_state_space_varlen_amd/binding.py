@@ -1,0 +1,202 @@
+"""ctypes binding of libssmpack.so: argument marshalling only.
+
+Each function here has the name of the C entry point it calls and does
+nothing but check tensors, allocate outputs and workspaces with torch, and
+pass raw device pointers and the current HIP stream. Every step of the
+computation runs in the library's HIP kernels; there is no CPU path. If the
+library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssmpack.so")
+
+SSMP_F32, SSMP_BF16 = 0, 1
+
+_c_i32, _c_i64, _c_sz, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+_SIGNATURES = {
+    "ssmp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "ssmp_abi_version": (ctypes.c_int, []),
+    "varlen_pack_indices": (ctypes.c_int, [_c_vp, _c_i32, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "conv1d_pack_fwd": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
+                                       _c_vp]),
+    "conv1d_pack_bwd_workspace_bytes": (_c_sz, [_c_i64, _c_i32, _c_i32]),
+    "conv1d_pack_bwd": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz,
+                                       _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp]),
+    "selective_scan_pack_workspace_bytes": (_c_sz, [_c_i64, _c_i32, _c_i32]),
+    "selective_scan_pack_fwd": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                               _c_vp, _c_sz, _c_i64, _c_i32, _c_i32, _c_i32, _c_vp]),
+    "selective_scan_pack_bwd": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                               _c_vp, _c_sz, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                               _c_i64, _c_i32, _c_i32, _c_i32, _c_vp]),
+}
+
+EXPORTED = tuple(_SIGNATURES)
+
+_lib = None
+
+
+class SsmpError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = load().ssmp_status_string(status).decode() if status >= 0 else "?"
+        super().__init__(f"{fn} failed: status {status} ({msg})")
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libssmpack.so not found at {path}; build it with "
+                           f"`python -m selective_state_space_varlen_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SSMP_BF16
+    if t.dtype == torch.float32:
+        return SSMP_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _check(t: Optional[torch.Tensor], name: str, shape=None, dtype=None, device=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _call(name: str, *args):
+    st = getattr(load(), name)(*args)
+    if st != 0:
+        raise SsmpError(name, st)
+
+
+# ---------------------------------------------------------------------------
+def varlen_pack_indices(cu_seqlens: torch.Tensor, T: int, heads: bool = True, dev_err: bool = True):
+    """cu_seqlens (int32, device) -> (pos int32 [T], heads uint8 [T] or None,
+    dev_err int32 [1] or None). dev_err holds 0 or SSMP_ERR_CU_SEQLENS."""
+    _check(cu_seqlens, "cu_seqlens", dtype=torch.int32)
+    dev = cu_seqlens.device
+    pos = torch.empty(T, dtype=torch.int32, device=dev)
+    hd = torch.empty(T, dtype=torch.uint8, device=dev) if heads else None
+    err = torch.empty(1, dtype=torch.int32, device=dev) if dev_err else None
+    _call("varlen_pack_indices", _ptr(cu_seqlens), cu_seqlens.numel() - 1, T, _ptr(pos), _ptr(hd), _ptr(err),
+          _stream(cu_seqlens))
+    return pos, hd, err
+
+
+def conv1d_pack_fwd(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor], pos: torch.Tensor,
+                    silu: bool = True, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    T, D = x.shape
+    W = w.shape[1]
+    _check(x, "x"); _check(w, "w", (D, W), torch.float32, x.device); _check(b, "b", (D,), torch.float32, x.device)
+    _check(pos, "pos", (T,), torch.int32, x.device)
+    u = torch.empty_like(x) if out is None else out
+    _check(u, "u", (T, D), x.dtype, x.device)
+    _call("conv1d_pack_fwd", _ptr(x), _ptr(w), _ptr(b), _ptr(pos), _ptr(u), T, D, W, _dtype_code(x), int(silu),
+          _stream(x))
+    return u
+
+
+def conv1d_pack_bwd_workspace_bytes(T: int, D: int, W: int) -> int:
+    return int(load().conv1d_pack_bwd_workspace_bytes(T, D, W))
+
+
+def conv1d_pack_bwd(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor], pos: torch.Tensor,
+                    du: torch.Tensor, silu: bool = True, workspace: Optional[torch.Tensor] = None,
+                    want_db: bool = True):
+    T, D = x.shape
+    W = w.shape[1]
+    _check(x, "x"); _check(w, "w", (D, W), torch.float32, x.device); _check(b, "b", (D,), torch.float32, x.device)
+    _check(pos, "pos", (T,), torch.int32, x.device); _check(du, "du", (T, D), x.dtype, x.device)
+    dx = torch.empty_like(x)
+    dw = torch.empty((D, W), dtype=torch.float32, device=x.device)
+    db = torch.empty((D,), dtype=torch.float32, device=x.device) if want_db else None
+    nbytes = conv1d_pack_bwd_workspace_bytes(T, D, W)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    _call("conv1d_pack_bwd", _ptr(x), _ptr(w), _ptr(b), _ptr(pos), _ptr(du), _ptr(dx), _ptr(dw), _ptr(db),
+          _ptr(workspace), workspace.numel() * workspace.element_size(), T, D, W, _dtype_code(x), int(silu),
+          _stream(x))
+    return dx, dw, db
+
+
+def selective_scan_pack_workspace_bytes(T: int, D: int, N: int) -> int:
+    return int(load().selective_scan_pack_workspace_bytes(T, D, N))
+
+
+def selective_scan_pack_fwd(u, delta, A, B, C, Dskip, z, pos, workspace: Optional[torch.Tensor] = None,
+                            out: Optional[torch.Tensor] = None):
+    """Returns (out, workspace); keep the workspace for the backward."""
+    T, D = u.shape
+    N = A.shape[1]
+    dev = u.device
+    _check(u, "u"); _check(delta, "delta", (T, D), u.dtype, dev); _check(A, "A", (D, N), torch.float32, dev)
+    _check(B, "B", (T, N), u.dtype, dev); _check(C, "C", (T, N), u.dtype, dev)
+    _check(Dskip, "Dskip", (D,), torch.float32, dev); _check(z, "z", (T, D), u.dtype, dev)
+    _check(pos, "pos", (T,), torch.int32, dev)
+    nbytes = selective_scan_pack_workspace_bytes(T, D, N)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(u) if out is None else out
+    _check(o, "out", (T, D), u.dtype, dev)
+    _call("selective_scan_pack_fwd", _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z),
+          _ptr(pos), _ptr(o), _ptr(workspace), workspace.numel() * workspace.element_size(), T, D, N,
+          _dtype_code(u), _stream(u))
+    return o, workspace
+
+
+def selective_scan_pack_bwd(u, delta, A, B, C, Dskip, z, pos, dout, workspace: torch.Tensor):
+    """Gradients of sum(dout * out); the workspace must come from the forward."""
+    T, D = u.shape
+    N = A.shape[1]
+    dev = u.device
+    _check(u, "u"); _check(delta, "delta", (T, D), u.dtype, dev); _check(A, "A", (D, N), torch.float32, dev)
+    _check(B, "B", (T, N), u.dtype, dev); _check(C, "C", (T, N), u.dtype, dev)
+    _check(Dskip, "Dskip", (D,), torch.float32, dev); _check(z, "z", (T, D), u.dtype, dev)
+    _check(pos, "pos", (T,), torch.int32, dev); _check(dout, "dout", (T, D), u.dtype, dev)
+    _check(workspace, "workspace", device=dev)
+    du = torch.empty_like(u)
+    ddelta = torch.empty_like(u)
+    dA = torch.empty((D, N), dtype=torch.float32, device=dev)
+    dB = torch.empty((T, N), dtype=torch.float32, device=dev)
+    dC = torch.empty((T, N), dtype=torch.float32, device=dev)
+    dD = torch.empty((D,), dtype=torch.float32, device=dev) if Dskip is not None else None
+    dz = torch.empty_like(u) if z is not None else None
+    _call("selective_scan_pack_bwd", _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z),
+          _ptr(pos), _ptr(dout), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(du),
+          _ptr(ddelta), _ptr(dA), _ptr(dB), _ptr(dC), _ptr(dD), _ptr(dz), T, D, N, _dtype_code(u), _stream(u))
+    return {"du": du, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "dz": dz}

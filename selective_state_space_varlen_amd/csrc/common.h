@@ -1,0 +1,78 @@
+// Device helpers shared by the ssmpack kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ssmpack.h"
+
+namespace ssmp {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// bf16 is carried as its 16 raw bits. Widening is exact; narrowing rounds to
+// nearest even (one v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __builtin_bit_cast(float, bits << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t word) { return __builtin_bit_cast(float, word & 0xffff0000u); }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+template <typename T>
+struct Elt;
+
+template <>
+struct Elt<float> {
+    static __device__ __forceinline__ float ld(const float* __restrict__ p, size_t i) { return p[i]; }
+    static __device__ __forceinline__ void st(float* __restrict__ p, size_t i, float v) { p[i] = v; }
+};
+
+template <>
+struct Elt<uint16_t> {
+    static __device__ __forceinline__ float ld(const uint16_t* __restrict__ p, size_t i) { return bf16_to_f32(p[i]); }
+    static __device__ __forceinline__ void st(uint16_t* __restrict__ p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// One row of NS values of a (T, N) tensor at a wave-uniform address. bf16
+// rows are read as 32-bit words (N even) so the loads stay scalar.
+template <int NS>
+__device__ __forceinline__ void load_row(const float* __restrict__ p, float (&v)[NS]) {
+#pragma unroll
+    for (int n = 0; n < NS; ++n) v[n] = p[n];
+}
+
+template <int NS>
+__device__ __forceinline__ void load_row(const uint16_t* __restrict__ p, float (&v)[NS]) {
+    if constexpr (NS % 2 == 0) {
+        const uint32_t* __restrict__ q = reinterpret_cast<const uint32_t*>(p);
+#pragma unroll
+        for (int n = 0; n < NS / 2; ++n) {
+            const uint32_t w = q[n];
+            v[2 * n] = bf16_to_f32(w);
+            v[2 * n + 1] = bf16_hi_to_f32(w);
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < NS; ++n) v[n] = bf16_to_f32(p[n]);
+    }
+}
+
+// 2^x on the transcendental unit (v_exp_f32). Results below the normal range
+// flush to zero, which only ever removes a decayed contribution.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Logistic sigmoid 1 / (1 + e^-v) from v_exp_f32 and v_rcp_f32 (about 2 ulp).
+__device__ __forceinline__ float sigmoid_fast(float v) {
+    return __builtin_amdgcn_rcpf(1.0f + exp2_fast(-v * kLog2e));
+}
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+}  // namespace ssmp
+
+// Host-side: launch check.
+#define SSMP_LAUNCH_CHECK()                                   \
+    do {                                                      \
+        if (hipGetLastError() != hipSuccess) return SSMP_ERR_HIP; \
+    } while (0)

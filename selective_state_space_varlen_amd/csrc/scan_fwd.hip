@@ -1,0 +1,227 @@
+// selective_scan_pack forward.
+//
+// Shanghai AI Lab article on packed variable-length Mamba-1 training
+// (gitcode.csdn.net/69d8cc1b54b52172bc6872cb.html), sections "SSM_pack算子" and
+// "基本原理": the state crosses packed sequences only through the recurrence,
+// so it is reset to zero at every head token. Per channel d, state n:
+//   h_t = exp(delta_t A[d,n]) h_{t-1} + delta_t B_t[n] u_t   (h_{t-1} = 0 at heads)
+//   y_t = sum_n C_t[n] h_t[n] + Dskip[d] u_t,   out_t = y_t SiLU(z_t)
+//
+// Mapping: one lane per channel, the d_state values in VGPRs, one wave per
+// (chunk of kLC tokens, 64 channels); B_t and C_t are the same for the whole
+// wave and arrive through scalar loads. The time axis is joined across
+// chunks by the article's reset rule applied to the affine carry
+// (h_out = P h_in + S, with the multiplier P zeroed once a head has been
+// passed):
+//   1. summary: per chunk, from its last head (or its start) to its end,
+//      S = end state from zero and P = product of decays (0 if a head was
+//      seen). Skipped when the next chunk starts with a head.
+//   2. carry: per (n, d), a sequential pass over chunks gives the state
+//      entering each chunk.
+//   3. output: each chunk replays its tokens from that state, writes out and
+//      stores the state every kCK tokens for the backward.
+#include "scan_common.h"
+
+namespace ssmp {
+
+template <typename T, int NS>
+__global__ __launch_bounds__(64) void k_scan_fwd_summary(const T* __restrict__ u, const T* __restrict__ delta,
+                                                         const float* __restrict__ A, const T* __restrict__ B,
+                                                         const int32_t* __restrict__ pos, float* __restrict__ P,
+                                                         float* __restrict__ S, int64_t T_, int D) {
+    const int lane = threadIdx.x;
+    const Tile tl = tile_of(D);
+    const int d = tl.g * kWave + lane;
+    const bool act = d < D;
+    const int dd = act ? d : D - 1;
+    const int64_t c = tl.c;
+    const int64_t t0 = c * kLC;
+    const int64_t t1 = (t0 + kLC < T_) ? t0 + kLC : T_;
+    if (t1 >= T_) return;          // last chunk: no successor needs it
+    if (pos[t1] == 0) return;      // successor starts at a head: its carry is zero
+
+    // last head in [t0, t1)
+    int64_t ts = t0;
+    bool has_head = false;
+    for (int64_t base = t0; base < t1; base += kWave) {
+        const int64_t t = base + lane;
+        const bool f = (t < t1) && pos[t] == 0;
+        const uint64_t m = __ballot(f);
+        if (m) {
+            has_head = true;
+            ts = base + 63 - __builtin_clzll(m);
+        }
+    }
+    float A2[NS], h[NS], p[NS];
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+        A2[n] = A[(size_t)dd * NS + n] * kLog2e;
+        h[n] = 0.0f;
+        p[n] = 1.0f;
+    }
+    for (int64_t t = ts; t < t1; ++t) {
+        const float dt = Elt<T>::ld(delta, (size_t)t * D + dd);
+        const float dtu = dt * Elt<T>::ld(u, (size_t)t * D + dd);
+        float Bv[NS];
+        load_row<NS>(B + (size_t)t * NS, Bv);
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            const float a = exp2_fast(dt * A2[n]);
+            h[n] = __builtin_fmaf(a, h[n], dtu * Bv[n]);
+            p[n] *= a;
+        }
+    }
+    if (act) {
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            const size_t o = ((size_t)c * NS + n) * D + d;
+            P[o] = has_head ? 0.0f : p[n];
+            S[o] = h[n];
+        }
+    }
+}
+
+// State entering each chunk, written to the checkpoint slot of its first token.
+template <int NS>
+__global__ __launch_bounds__(256) void k_scan_fwd_carry(const float* __restrict__ P, const float* __restrict__ S,
+                                                        const int32_t* __restrict__ pos, float* __restrict__ ckpt,
+                                                        int64_t T_, int D, int64_t nchunk) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // n*D + d
+    const int64_t ND = (int64_t)NS * D;
+    if (i >= ND) return;
+    float h = 0.0f;
+    for (int64_t c = 0; c < nchunk; ++c) {
+        ckpt[(size_t)(c * (kLC / kCK)) * ND + i] = h;
+        const int64_t t1 = (c + 1) * kLC;
+        if (t1 >= T_) break;
+        if (pos[t1] == 0) {
+            h = 0.0f;
+        } else {
+            // P == 0 marks a chunk holding a head: select, so that a
+            // non-finite state before the head cannot leak through 0 * h
+            const float Pc = P[(size_t)c * ND + i], Sc = S[(size_t)c * ND + i];
+            h = (Pc == 0.0f) ? Sc : __builtin_fmaf(Pc, h, Sc);
+        }
+    }
+}
+
+template <typename T, int NS>
+__global__ __launch_bounds__(64) void k_scan_fwd_out(const T* __restrict__ u, const T* __restrict__ delta,
+                                                     const float* __restrict__ A, const T* __restrict__ B,
+                                                     const T* __restrict__ C, const float* __restrict__ Dskip,
+                                                     const T* __restrict__ z, const int32_t* __restrict__ pos,
+                                                     T* __restrict__ out, float* __restrict__ ckpt, int64_t T_,
+                                                     int D) {
+    const int lane = threadIdx.x;
+    const Tile tl = tile_of(D);
+    const int d = tl.g * kWave + lane;
+    const bool act = d < D;
+    const int dd = act ? d : D - 1;
+    const int64_t c = tl.c;
+    const int64_t t0 = c * kLC;
+    const int64_t t1 = (t0 + kLC < T_) ? t0 + kLC : T_;
+    const size_t ND = (size_t)NS * D;
+
+    float A2[NS], h[NS];
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+        A2[n] = A[(size_t)dd * NS + n] * kLog2e;
+        h[n] = ckpt[(size_t)(t0 / kCK) * ND + (size_t)n * D + dd];
+    }
+    const float Dv = Dskip ? Dskip[dd] : 0.0f;
+    const bool gate = z != nullptr;
+
+    for (int64_t tb = t0; tb < t1; tb += kCK) {
+        if (tb != t0 && act) {
+#pragma unroll
+            for (int n = 0; n < NS; ++n) ckpt[(size_t)(tb / kCK) * ND + (size_t)n * D + d] = h[n];
+        }
+        const int nt = (int)((tb + kCK < t1) ? kCK : t1 - tb);
+#pragma unroll 4
+        for (int k = 0; k < nt; ++k) {
+            const int64_t t = tb + k;
+            const size_t e = (size_t)t * D + dd;
+            const float dt = Elt<T>::ld(delta, e);
+            const float uu = Elt<T>::ld(u, e);
+            const float dtu = dt * uu;
+            float Bv[NS], Cv[NS];
+            load_row<NS>(B + (size_t)t * NS, Bv);
+            load_row<NS>(C + (size_t)t * NS, Cv);
+            if (pos[t] == 0) {
+#pragma unroll
+                for (int n = 0; n < NS; ++n) h[n] = 0.0f;
+            }
+            float y = 0.0f;
+#pragma unroll
+            for (int n = 0; n < NS; ++n) {
+                const float a = exp2_fast(dt * A2[n]);
+                h[n] = __builtin_fmaf(a, h[n], dtu * Bv[n]);
+                y = __builtin_fmaf(Cv[n], h[n], y);
+            }
+            y = __builtin_fmaf(Dv, uu, y);
+            if (gate) {
+                const float zz = Elt<T>::ld(z, e);
+                y *= zz * sigmoid_fast(zz);
+            }
+            if (act) Elt<T>::st(out, (size_t)t * D + d, y);
+        }
+    }
+}
+
+template <typename T, int NS>
+static int scan_fwd_launch(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                           const float* Dskip, const void* z, const int32_t* pos, void* out, float* ws, int64_t T_,
+                           int D, hipStream_t s) {
+    const ScanWs L = scan_ws_layout(T_, D, NS);
+    const dim3 grid((unsigned)(L.ngroup * L.nchunk));
+    if (L.nchunk > 1) {
+        k_scan_fwd_summary<T, NS><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, (const T*)B, pos,
+                                                         ws + L.P, ws + L.S, T_, D);
+        SSMP_LAUNCH_CHECK();
+    }
+    const int64_t ND = (int64_t)NS * D;
+    k_scan_fwd_carry<NS><<<(unsigned)((ND + 255) / 256), 256, 0, s>>>(ws + L.P, ws + L.S, pos, ws + L.ckpt, T_, D,
+                                                                      L.nchunk);
+    SSMP_LAUNCH_CHECK();
+    k_scan_fwd_out<T, NS><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, (const T*)B, (const T*)C, Dskip,
+                                                 (const T*)z, pos, (T*)out, ws + L.ckpt, T_, D);
+    SSMP_LAUNCH_CHECK();
+    return SSMP_OK;
+}
+
+template <typename T>
+static int scan_fwd_dispatch(int N, const void* u, const void* delta, const float* A, const void* B, const void* C,
+                             const float* Dskip, const void* z, const int32_t* pos, void* out, float* ws, int64_t T_,
+                             int D, hipStream_t s) {
+    switch (N) {
+        case 1: return scan_fwd_launch<T, 1>(u, delta, A, B, C, Dskip, z, pos, out, ws, T_, D, s);
+        case 2: return scan_fwd_launch<T, 2>(u, delta, A, B, C, Dskip, z, pos, out, ws, T_, D, s);
+        case 4: return scan_fwd_launch<T, 4>(u, delta, A, B, C, Dskip, z, pos, out, ws, T_, D, s);
+        case 8: return scan_fwd_launch<T, 8>(u, delta, A, B, C, Dskip, z, pos, out, ws, T_, D, s);
+        case 16: return scan_fwd_launch<T, 16>(u, delta, A, B, C, Dskip, z, pos, out, ws, T_, D, s);
+        default: return SSMP_ERR_UNSUPPORTED;
+    }
+}
+
+}  // namespace ssmp
+
+extern "C" size_t selective_scan_pack_workspace_bytes(int64_t T, int32_t D, int32_t N) {
+    if (T <= 0 || D <= 0 || N <= 0) return 0;
+    return ssmp::scan_ws_layout(T, D, N).total * sizeof(float);
+}
+
+extern "C" int selective_scan_pack_fwd(const void* u, const void* delta, const float* A, const void* B,
+                                       const void* C, const float* Dskip, const void* z, const int32_t* pos,
+                                       void* out, void* workspace, size_t workspace_bytes, int64_t T, int32_t D,
+                                       int32_t N, int32_t dtype, void* stream) {
+    using namespace ssmp;
+    int st = scan_check_args(T, D, N, dtype);
+    if (st) return st;
+    if (T == 0) return SSMP_OK;
+    if (!u || !delta || !A || !B || !C || !pos || !out) return SSMP_ERR_NULL;
+    if (!workspace || workspace_bytes < selective_scan_pack_workspace_bytes(T, D, N)) return SSMP_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* ws = static_cast<float*>(workspace);
+    return dtype == SSMP_BF16 ? scan_fwd_dispatch<uint16_t>(N, u, delta, A, B, C, Dskip, z, pos, out, ws, T, D, s)
+                              : scan_fwd_dispatch<float>(N, u, delta, A, B, C, Dskip, z, pos, out, ws, T, D, s);
+}

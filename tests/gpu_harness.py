@@ -1,0 +1,89 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and the
+fp64 oracle on the same seeded inputs, and compare to the stated tolerances.
+
+Tolerances (max |err| over a tensor, relative to max |reference| of it):
+  outputs:   1e-5 for fp32 inputs, 2e-2 for bf16 inputs (fp32 state)
+  gradients: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs
+The bf16 bound covers the rounding of every bf16 result (2^-9 relative) plus
+fp32 accumulation; the oracle reads the same rounded input values.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import synth
+
+TOL_OUT = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
+TOL_GRAD = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_dev(t):
+    return None if t is None else t.to(dev()).contiguous()
+
+
+def npy(t):
+    return None if t is None else t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def assert_close(got, ref, tol, name):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, f"{name}: shape {got.shape} vs {ref.shape}"
+    if ref.size == 0:
+        return
+    scale = float(np.max(np.abs(ref)))
+    err = np.abs(got - ref)
+    worst = float(np.max(err)) if np.all(np.isfinite(err)) else float("inf")
+    assert worst <= tol * max(scale, 1e-30), (
+        f"{name}: max|err| {worst:.3e} > {tol:g} * max|ref| {scale:.3e} "
+        f"at {np.unravel_index(int(np.nanargmax(np.where(np.isfinite(err), err, np.inf))), err.shape)}")
+
+
+class Dev:
+    """Device copies of an Inputs batch plus cu_seqlens and pos."""
+
+    def __init__(self, inp: synth.Inputs):
+        self.inp = inp
+        import selective_state_space_varlen_amd as ssp
+        self.ssp = ssp
+        for k in ("x", "z", "B", "C", "delta", "A", "Dp", "w", "b", "dout", "u"):
+            setattr(self, k, to_dev(getattr(inp, k)))
+        self.cu = torch.from_numpy(inp.cu_seqlens).to(dev())
+        self.pos, self.heads, self.err = ssp.varlen_pack_indices(self.cu, inp.T)
+
+    def forward(self, gate=True, skip=True, bias=True):
+        return self.ssp.forward(self.x, self.w, self.b if bias else None, self.delta, self.A, self.B, self.C,
+                                self.Dp if skip else None, self.z if gate else None, self.cu, pos=self.pos)
+
+    def backward(self, fwd, gate=True, skip=True, bias=True):
+        return self.ssp.backward(self.x, self.w, self.b if bias else None, self.delta, self.A, self.B, self.C,
+                                 self.Dp if skip else None, self.z if gate else None, fwd, self.dout)
+
+
+def oracle_pipeline(orc, inp: synth.Inputs, gate=True, skip=True, bias=True, threads=8, backward=False,
+                    channels=None):
+    """Oracle forward (and backward) of the whole pipeline, optionally on a
+    channel subset (channels never interact except through dB/dC, which a
+    subset run does not give in full)."""
+    sl = slice(None) if channels is None else channels
+    x = synth.f64(inp.x)[:, sl]
+    w = synth.f64(inp.w)[sl]
+    b = synth.f64(inp.b)[sl] if bias else None
+    delta = synth.f64(inp.delta)[:, sl]
+    A = synth.f64(inp.A)[sl]
+    Dp = synth.f64(inp.Dp)[sl] if skip else None
+    z = synth.f64(inp.z)[:, sl] if gate else None
+    B = synth.f64(inp.B)
+    C = synth.f64(inp.C)
+    F = orc.forward(x, w, b, delta, A, B, C, Dp, z, inp.cu_seqlens, threads=threads)
+    if not backward:
+        return F
+    dout = synth.f64(inp.dout)[:, sl]
+    G = orc.backward(x, w, b, delta, A, B, C, Dp, z, inp.cu_seqlens, dout, threads=threads)
+    F.update(G)
+    return F

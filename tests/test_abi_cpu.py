@@ -1,0 +1,97 @@
+"""CPU tests of the C ABI: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host before launching
+anything (these paths make no HIP call, so they run without a GPU)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssmpack.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(", src, re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from selective_state_space_varlen_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libssmpack.so is not built (run __graft_entry__.build())")
+    return binding.load()
+
+
+def test_header_lists_the_entry_points():
+    names = declared_functions()
+    for n in ("varlen_pack_indices", "conv1d_pack_fwd", "conv1d_pack_bwd", "selective_scan_pack_fwd",
+              "selective_scan_pack_bwd", "selective_scan_pack_workspace_bytes", "conv1d_pack_bwd_workspace_bytes",
+              "ssmp_status_string", "ssmp_abi_version"):
+        assert n in names, n
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from selective_state_space_varlen_amd import binding
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in ssmpack.h but not exported"
+    assert sorted(binding.EXPORTED) == declared_functions()
+
+
+def test_status_strings(lib):
+    assert lib.ssmp_status_string(0) == b"ok"
+    for s in range(1, 7):
+        assert lib.ssmp_status_string(s) and lib.ssmp_status_string(s) != b"unknown status"
+    assert lib.ssmp_status_string(99) == b"unknown status"
+    assert lib.ssmp_abi_version() == 1
+
+
+def test_workspace_sizes(lib):
+    # checkpoints (one fp32 state per 16 tokens) dominate the scan workspace
+    T, D, N = 32768, 4096, 16
+    ws = lib.selective_scan_pack_workspace_bytes(T, D, N)
+    assert ws >= (T // 16) * D * N * 4
+    assert lib.selective_scan_pack_workspace_bytes(0, D, N) == 0
+    assert lib.conv1d_pack_bwd_workspace_bytes(T, D, 4) >= 5 * D * 4
+    assert lib.conv1d_pack_bwd_workspace_bytes(0, D, 4) == 0
+
+
+NULL = None
+
+
+def test_host_validation(lib):
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+    # varlen_pack_indices: nseq < 1, T out of range, NULL cu_seqlens
+    assert lib.varlen_pack_indices(fake, 0, 4, fake, NULL, NULL, NULL) == 2
+    assert lib.varlen_pack_indices(fake, 1, -1, fake, NULL, NULL, NULL) == 2
+    assert lib.varlen_pack_indices(fake, 1, 1 << 31, fake, NULL, NULL, NULL) == 2
+    assert lib.varlen_pack_indices(NULL, 1, 4, fake, NULL, NULL, NULL) == 1
+    assert lib.varlen_pack_indices(fake, 1, 4, NULL, NULL, NULL, NULL) == 1
+    # conv: width, dtype, D, NULLs
+    assert lib.conv1d_pack_fwd(fake, fake, NULL, fake, fake, 8, 4, 5, 1, 1, NULL) == 4
+    assert lib.conv1d_pack_fwd(fake, fake, NULL, fake, fake, 8, 4, 0, 1, 1, NULL) == 4
+    assert lib.conv1d_pack_fwd(fake, fake, NULL, fake, fake, 8, 4, 4, 7, 1, NULL) == 4
+    assert lib.conv1d_pack_fwd(fake, fake, NULL, fake, fake, 8, 0, 4, 1, 1, NULL) == 2
+    assert lib.conv1d_pack_fwd(NULL, fake, NULL, fake, fake, 8, 4, 4, 1, 1, NULL) == 1
+    assert lib.conv1d_pack_bwd(fake, fake, NULL, fake, fake, fake, fake, NULL, NULL, 0, 8, 4, 4, 1, 1, NULL) == 6
+    assert lib.conv1d_pack_bwd(fake, fake, NULL, fake, fake, fake, fake, NULL, fake, 4, 8, 4, 4, 1, 1, NULL) == 6
+    # scan: d_state, dtype, NULLs, workspace
+    args = [fake] * 9
+    assert lib.selective_scan_pack_fwd(*args, fake, 1 << 30, 8, 4, 3, 1, NULL) == 4
+    assert lib.selective_scan_pack_fwd(*args, fake, 1 << 30, 8, 4, 32, 1, NULL) == 4
+    assert lib.selective_scan_pack_fwd(*args, fake, 1 << 30, 8, 4, 16, 2, NULL) == 4
+    assert lib.selective_scan_pack_fwd(*args, fake, 1 << 30, -1, 4, 16, 1, NULL) == 2
+    assert lib.selective_scan_pack_fwd(*args, NULL, 0, 8, 4, 16, 1, NULL) == 6
+    assert lib.selective_scan_pack_fwd(*args, fake, 16, 8, 4, 16, 1, NULL) == 6
+    nul_u = [NULL] + [fake] * 8
+    assert lib.selective_scan_pack_fwd(*nul_u, fake, 1 << 30, 8, 4, 16, 1, NULL) == 1
+    b = [fake] * 9 + [fake, 1 << 30] + [fake] * 7
+    assert lib.selective_scan_pack_bwd(*b, 8, 4, 3, 1, NULL) == 4
+    # dD must be given exactly when Dskip is
+    b2 = [fake] * 5 + [NULL] + [fake] * 3 + [fake, 1 << 30] + [fake] * 7
+    assert lib.selective_scan_pack_bwd(*b2, 8, 4, 16, 1, NULL) == 1

@@ -1,0 +1,256 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle,
+element by element, on seeded inputs that span several tiles and a ragged
+tail, plus the edge cases of the method (single-token and zero-length
+sequences, heads on chunk boundaries, one sequence across many chunks,
+ragged channel groups, every supported d_state and conv width)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests.gpu_harness import TOL_GRAD, TOL_OUT, Dev, assert_close, npy, oracle_pipeline, to_dev
+from tests.oracle_checks import read_golden
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import selective_state_space_varlen_amd as ssp
+    ssp.load()
+
+
+def ssp():
+    import selective_state_space_varlen_amd as m
+    return m
+
+
+# ---------------------------------------------------------------------------
+# varlen_pack_indices: bit-exact
+# ---------------------------------------------------------------------------
+
+def test_pack_indices_golden():
+    g = read_golden("pack_4_2_3_7.txt")
+    cu = torch.tensor(g["cu_seqlens"], dtype=torch.int32, device="cuda")
+    pos, heads, err = ssp().varlen_pack_indices(cu, 16)
+    torch.cuda.synchronize()
+    assert pos.cpu().tolist() == g["position_indices"].tolist()
+    assert heads.cpu().tolist() == g["heads"].tolist()
+    assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_pack_indices_random(orc, seed):
+    rng = np.random.default_rng(seed)
+    lengths = [int(v) for v in rng.integers(0, 3000, 200)]
+    lengths[3] = 0
+    lengths[-1] = 1
+    cu = synth.cu_seqlens_of(lengths)
+    T = int(cu[-1])
+    pos, heads, err = ssp().varlen_pack_indices(torch.from_numpy(cu).cuda(), T)
+    rpos, rhead = orc.pack_indices(cu, T)
+    assert np.array_equal(pos.cpu().numpy(), rpos)
+    assert np.array_equal(heads.cpu().numpy(), rhead)
+    assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("cu", [[1, 4, 6], [0, 4, 3, 6], [0, 4, 7]])
+def test_pack_indices_rejects_bad_cu(cu):
+    T = 6
+    pos, _, err = ssp().varlen_pack_indices(torch.tensor(cu, dtype=torch.int32, device="cuda"), T)
+    p = pos.cpu().numpy()
+    assert int(err.item()) == 3
+    assert np.all(p >= 0) and np.all(p <= np.arange(T))
+
+
+# ---------------------------------------------------------------------------
+# conv1d_pack
+# ---------------------------------------------------------------------------
+
+CONV_CASES = [
+    # (dtype, D, W, silu, lengths)
+    (torch.float32, 8, 4, True, [4, 2, 3, 7]),
+    (torch.float32, 100, 3, True, [1, 5, 130, 2, 70, 1]),
+    (torch.float32, 64, 1, False, [33, 1, 1, 200]),
+    (torch.bfloat16, 512, 4, True, [700, 1, 3, 322, 129]),
+    (torch.bfloat16, 100, 4, True, [1, 5, 130, 2, 70, 1]),   # D % 8 != 0: per-element path
+    (torch.bfloat16, 256, 2, False, [256, 128, 3, 1]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CONV_CASES)))
+def test_conv_parity(orc, case):
+    dtype, D, W, silu, lengths = CONV_CASES[case]
+    inp = synth.make_inputs(2, D=D, dtype=dtype, lengths=lengths, seed=40 + case, with_dout=True)
+    w = torch.rand((D, W), generator=torch.Generator().manual_seed(case)) - 0.5
+    b = torch.randn(D, generator=torch.Generator().manual_seed(100 + case)) * 0.2
+    d = Dev(inp)
+    wd, bd = to_dev(w), to_dev(b)
+    u = ssp().conv1d_pack_fwd(d.x, wd, bd, d.pos, silu=silu)
+    dx, dw, db = ssp().conv1d_pack_bwd(d.x, wd, bd, d.pos, d.dout, silu=silu)
+    pos, _ = orc.pack_indices(inp.cu_seqlens, inp.T)
+    _, ru = orc.conv_fwd(synth.f64(inp.x), w.double().numpy(), b.double().numpy(), pos, silu=silu, threads=4)
+    rdx, rdw, rdb = orc.conv_bwd(synth.f64(inp.x), w.double().numpy(), b.double().numpy(), pos,
+                                 synth.f64(inp.dout), silu=silu, threads=4)
+    assert_close(npy(u), ru, TOL_OUT[dtype], "u")
+    assert_close(npy(dx), rdx, TOL_GRAD[dtype], "dx")
+    assert_close(npy(dw), rdw, TOL_GRAD[dtype], "dw")
+    assert_close(npy(db), rdb, TOL_GRAD[dtype], "db")
+
+
+# ---------------------------------------------------------------------------
+# selective_scan_pack, forward and backward
+# ---------------------------------------------------------------------------
+
+SCAN_CASES = {
+    "workload0": dict(wl=0),
+    "workload1-small": dict(wl=1, n_packs=1, D=96),
+    "workload2-small": dict(wl=2, n_packs=2, D=128),
+    "workload3-small": dict(wl=3, n_packs=1, pack_len=8192, D=64),
+    "one-sequence-12-chunks": dict(wl=2, lengths=[3000], D=64),
+    "all-single-tokens": dict(wl=2, lengths=[1] * 600, D=64),
+    "ragged-tail-fp32": dict(wl=2, lengths=[255, 1, 256, 257, 3, 100], D=65, dtype=torch.float32),
+    "heads-on-chunk-starts": dict(wl=2, lengths=[256, 256, 512, 17], D=64),
+    "zero-length-sequences": dict(wl=2, lengths=[5, 0, 300, 0, 0, 40, 1000], D=70),
+    "d_state-1-fp32": dict(wl=2, lengths=[300, 2, 500], D=33, N=1, dtype=torch.float32),
+    "d_state-2": dict(wl=2, lengths=[300, 2, 500], D=64, N=2),
+    "d_state-8-fp32": dict(wl=2, lengths=[700, 90], D=130, N=8, dtype=torch.float32),
+    "no-gate-no-skip": dict(wl=2, lengths=[400, 1, 299], D=64, gate=False, skip=False),
+    "single-token-pack": dict(wl=2, lengths=[1], D=64),
+}
+
+
+def _scan_case(name):
+    spec = dict(SCAN_CASES[name])
+    gate = spec.pop("gate", True)
+    skip = spec.pop("skip", True)
+    wl = spec.pop("wl")
+    inp = synth.make_inputs(wl, with_u=True, with_dout=True, **spec)
+    return inp, gate, skip
+
+
+def run_scan_gpu(inp, gate, skip):
+    d = Dev(inp)
+    z = d.z if gate else None
+    Dp = d.Dp if skip else None
+    out, ws = ssp().selective_scan_pack_fwd(d.u, d.delta, d.A, d.B, d.C, Dp, z, d.pos)
+    g = ssp().selective_scan_pack_bwd(d.u, d.delta, d.A, d.B, d.C, Dp, z, d.pos, d.dout, ws)
+    torch.cuda.synchronize()
+    return out, g
+
+
+def run_scan_oracle(orc, inp, gate, skip, threads=8):
+    pos, _ = orc.pack_indices(inp.cu_seqlens, inp.T)
+    args = (synth.f64(inp.u), synth.f64(inp.delta), synth.f64(inp.A), synth.f64(inp.B), synth.f64(inp.C),
+            synth.f64(inp.Dp) if skip else None, synth.f64(inp.z) if gate else None, pos)
+    _, rout = orc.scan_fwd(*args, threads=threads)
+    rg = orc.scan_bwd(*args, synth.f64(inp.dout), threads=threads)
+    return rout, rg
+
+
+@pytest.mark.parametrize("name", list(SCAN_CASES))
+def test_scan_parity(orc, name):
+    inp, gate, skip = _scan_case(name)
+    out, g = run_scan_gpu(inp, gate, skip)
+    rout, rg = run_scan_oracle(orc, inp, gate, skip)
+    to, tg = TOL_OUT[inp.dtype], TOL_GRAD[inp.dtype]
+    assert_close(npy(out), rout, to, "out")
+    for k in ("du", "ddelta", "dA", "dB", "dC"):
+        assert_close(npy(g[k]), rg[k], tg, k)
+    if skip:
+        assert_close(npy(g["dD"]), rg["dD"], tg, "dD")
+    if gate:
+        assert_close(npy(g["dz"]), rg["dz"], tg, "dz")
+
+
+def test_scan_deterministic():
+    inp, gate, skip = _scan_case("workload2-small")
+    o1, g1 = run_scan_gpu(inp, gate, skip)
+    o2, g2 = run_scan_gpu(inp, gate, skip)
+    assert torch.equal(o1, o2)
+    for k in g1:
+        if g1[k] is not None:
+            assert torch.equal(g1[k], g2[k]), k
+
+
+def test_scan_nonfinite_isolated():
+    """Inf in one sequence's input changes no other sequence's results."""
+    inp, gate, skip = _scan_case("workload2-small")
+    o0, g0 = run_scan_gpu(inp, gate, skip)
+    cu = inp.cu_seqlens
+    victim = 1
+    bad = inp.u.clone()
+    bad[int(cu[victim]) + 3, 5] = float("inf")
+    inp.u = bad
+    o1, g1 = run_scan_gpu(inp, gate, skip)
+    keep = np.ones(inp.T, dtype=bool)
+    keep[cu[victim]:cu[victim + 1]] = False
+    keep_t = torch.from_numpy(keep).cuda()
+    assert torch.equal(o0[keep_t], o1[keep_t])
+    for k in ("du", "ddelta", "dz", "dB", "dC"):
+        assert torch.equal(g0[k][keep_t], g1[k][keep_t]), k
+
+
+# ---------------------------------------------------------------------------
+# the whole pipeline (pack indices -> conv + SiLU -> gated scan, and back)
+# ---------------------------------------------------------------------------
+
+PIPE_CASES = {
+    "workload0": dict(wl=0),
+    "workload2-small": dict(wl=2, n_packs=2, D=256),
+    "workload1-small": dict(wl=1, n_packs=1, D=192),
+}
+
+
+@pytest.mark.parametrize("name", list(PIPE_CASES))
+def test_pipeline_parity(orc, name):
+    spec = dict(PIPE_CASES[name])
+    wl = spec.pop("wl")
+    inp = synth.make_inputs(wl, with_dout=True, **spec)
+    d = Dev(inp)
+    F = d.forward()
+    G = d.backward(F)
+    torch.cuda.synchronize()
+    R = oracle_pipeline(orc, inp, backward=True)
+    to, tg = TOL_OUT[inp.dtype], TOL_GRAD[inp.dtype]
+    assert np.array_equal(F["pos"].cpu().numpy(), R["pos"])
+    assert_close(npy(F["u"]), R["u"], to, "u")
+    assert_close(npy(F["out"]), R["out"], to, "out")
+    for k in ("dx", "dw", "db", "ddelta", "dA", "dB", "dC", "dD", "dz"):
+        assert_close(npy(G[k]), R[k], tg, k)
+
+
+def test_padded_layout_matches_packed():
+    """Right-padded layout (pads at each sequence's end, not counted) gives
+    the packed results on real tokens, on the same GPU kernels."""
+    inp = synth.make_inputs(2, n_packs=1, D=128, with_u=True, with_dout=True)
+    out, g = run_scan_gpu(inp, True, True)
+    Lmax = max(inp.lengths)
+    rows = np.concatenate([np.concatenate([np.arange(inp.cu_seqlens[s], inp.cu_seqlens[s + 1]),
+                                           -np.ones(Lmax - L, dtype=np.int64)])
+                           for s, L in enumerate(inp.lengths)])
+    real = rows >= 0
+
+    def pad(t):
+        o = torch.zeros((len(rows),) + tuple(t.shape[1:]), dtype=t.dtype)
+        o[torch.from_numpy(real)] = t[torch.from_numpy(rows[real])]
+        return o
+
+    import copy
+    p = copy.copy(inp)
+    for k in ("u", "delta", "z", "B", "C", "dout"):
+        setattr(p, k, pad(getattr(inp, k)))
+    p.lengths = [Lmax] * len(inp.lengths)
+    p.cu_seqlens = synth.cu_seqlens_of(p.lengths)
+    p.T = len(rows)
+    pout, pg = run_scan_gpu(p, True, True)
+    r = torch.from_numpy(real).cuda()
+    idx = torch.from_numpy(rows[real]).cuda()
+    assert_close(npy(pout[r]), npy(out[idx]), 2e-2, "out")
+    for k in ("du", "ddelta", "dz"):
+        assert_close(npy(pg[k][r]), npy(g[k][idx]), 2e-2, k)
+    for k in ("dA", "dD"):
+        assert_close(npy(pg[k]), npy(g[k]), 1e-3, k)
