@@ -1,0 +1,304 @@
+"""Benchmark: packed conv1d_pack + selective_scan_pack, forward and backward,
+at the Mamba-1.4B block shape (d_inner 4096, d_state 16, conv width 4, bf16
+inputs with fp32 state; 8 packs of 4096 tokens, lengths uniform in
+[64, 2048]; upstream gradient N(0, 1)).
+
+One step = the whole hot path over one batch already resident in HBM:
+varlen_pack_indices -> conv1d_pack_fwd -> selective_scan_pack_fwd ->
+selective_scan_pack_bwd -> conv1d_pack_bwd. Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-layouts] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, vendor figure
+
+# Algorithmic bytes (each operator reads its inputs once and writes its
+# outputs once; bf16 (T, D) tensors, bf16 B/C rows, fp32 dB/dC rows, int32
+# positions; per-launch parameter traffic is O(D N) and left out).
+def algo_bytes(T: int, D: int, N: int, elt: int = 2) -> dict:
+    return {
+        "pack_indices": T * 4 + T * 1,                              # write pos + heads
+        "conv_fwd": T * (D * 2 * elt + 4),                           # x in, u out, pos
+        "scan_fwd": T * (D * 4 * elt + 2 * N * elt + 4),             # u, delta, z in; out; B, C; pos
+        "scan_bwd": T * (D * 7 * elt + 2 * N * elt + 2 * N * 4 + 4),  # u,delta,z,dout in; du,ddelta,dz out; B,C; dB,dC; pos
+        "conv_bwd": T * (D * 3 * elt + 4),                           # x, du in; dx out; pos
+    }
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Workload:
+    """Device-resident inputs, outputs and workspaces of one packed batch."""
+
+    def __init__(self, inp: synth.Inputs, cu=None, dev="cuda:0"):
+        import selective_state_space_varlen_amd as ssp
+        self.ssp = ssp
+        self.inp = inp
+        self.T, self.D, self.N, self.W = inp.T, inp.D, inp.N, inp.W
+        d = torch.device(dev)
+        for k in ("x", "z", "B", "C", "delta", "A", "Dp", "w", "b", "dout"):
+            setattr(self, k, getattr(inp, k).to(d).contiguous())
+        cu_np = inp.cu_seqlens if cu is None else cu
+        self.cu = torch.from_numpy(np.ascontiguousarray(cu_np, dtype=np.int32)).to(d)
+        T, D, N, W = self.T, self.D, self.N, self.W
+        e = lambda *s, dt=self.x.dtype: torch.empty(*s, dtype=dt, device=d)
+        self.pos = e(T, dt=torch.int32)
+        self.u = e(T, D)
+        self.out = e(T, D)
+        self.scan_ws = e(max(ssp.selective_scan_pack_workspace_bytes(T, D, N), 1), dt=torch.uint8)
+        self.conv_ws = e(max(ssp.conv1d_pack_bwd_workspace_bytes(T, D, W), 1), dt=torch.uint8)
+        self.g = {"du": e(T, D), "ddelta": e(T, D), "dz": e(T, D), "dA": e(D, N, dt=torch.float32),
+                  "dB": e(T, N, dt=torch.float32), "dC": e(T, N, dt=torch.float32), "dD": e(D, dt=torch.float32)}
+        self.dx = e(T, D)
+        self.dw = e(D, W, dt=torch.float32)
+        self.db = e(D, dt=torch.float32)
+
+    def step(self, ev=None):
+        s = self.ssp
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        s.varlen_pack_indices(self.cu, self.T, heads=False, dev_err=False, out=self.pos)
+        rec(1)
+        s.conv1d_pack_fwd(self.x, self.w, self.b, self.pos, silu=True, out=self.u)
+        rec(2)
+        s.selective_scan_pack_fwd(self.u, self.delta, self.A, self.B, self.C, self.Dp, self.z, self.pos,
+                                  workspace=self.scan_ws, out=self.out)
+        rec(3)
+        s.selective_scan_pack_bwd(self.u, self.delta, self.A, self.B, self.C, self.Dp, self.z, self.pos, self.dout,
+                                  self.scan_ws, out=self.g)
+        rec(4)
+        s.conv1d_pack_bwd(self.x, self.w, self.b, self.pos, self.g["du"], silu=True, workspace=self.conv_ws,
+                          out=(self.dx, self.dw, self.db))
+        rec(5)
+
+
+OPS = ["pack_indices", "conv_fwd", "scan_fwd", "scan_bwd", "conv_bwd"]
+
+
+def time_steps(wl: Workload, steps: int, warmup: int, per_op: bool = True):
+    for _ in range(warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)] if per_op else None
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        wl.step(evs[i] if per_op else None)
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ops = None
+    if per_op:
+        ops = {}
+        for j, name in enumerate(OPS):
+            ops[name] = float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
+    return total_ms, ops
+
+
+def padded_layout(inp: synth.Inputs, pack_len: int):
+    """Each pack's sequences right-padded to that pack's longest one (zeros,
+    not counted as tokens)."""
+    cu = inp.cu_seqlens
+    rows, lengths = [], []
+    start = 0
+    seqs = list(range(len(inp.lengths)))
+    while start < len(seqs):
+        # sequences of one pack
+        p0 = cu[seqs[start]]
+        end = start
+        while end < len(seqs) and cu[seqs[end] + 1] <= p0 + pack_len:
+            end += 1
+        Lmax = max(inp.lengths[s] for s in seqs[start:end])
+        for s in seqs[start:end]:
+            r = np.arange(cu[s], cu[s + 1])
+            rows.append(np.concatenate([r, -np.ones(Lmax - len(r), dtype=np.int64)]))
+            lengths.append(Lmax)
+        start = end
+    rows = np.concatenate(rows)
+    real = rows >= 0
+    import copy
+    p = copy.copy(inp)
+    for k in ("x", "z", "B", "C", "delta", "dout"):
+        t = getattr(inp, k)
+        o = torch.zeros((len(rows),) + tuple(t.shape[1:]), dtype=t.dtype)
+        o[torch.from_numpy(real)] = t[torch.from_numpy(rows[real])]
+        setattr(p, k, o)
+    p.lengths = lengths
+    p.cu_seqlens = synth.cu_seqlens_of(lengths)
+    p.T = len(rows)
+    return p
+
+
+def per_sequence_loop(wl: Workload, steps: int, warmup: int) -> float:
+    """The gradient-accumulation layout: one launch chain per sequence, then
+    parameter gradients summed over sequences."""
+    ssp = wl.ssp
+    cu = wl.inp.cu_seqlens
+    segs = [(int(cu[i]), int(cu[i + 1])) for i in range(len(cu) - 1) if cu[i + 1] > cu[i]]
+    cus = [torch.tensor([0, b - a], dtype=torch.int32, device=wl.x.device) for a, b in segs]
+    acc = {k: torch.zeros_like(wl.g[k]) for k in ("dA", "dD")}
+    acc["dw"], acc["db"] = torch.zeros_like(wl.dw), torch.zeros_like(wl.db)
+
+    def one_step():
+        for k in acc:
+            acc[k].zero_()
+        for (a, b), c in zip(segs, cus):
+            L = b - a
+            pos = wl.pos[a:b]
+            ssp.varlen_pack_indices(c, L, heads=False, dev_err=False, out=pos)
+            x = wl.x[a:b]
+            u = ssp.conv1d_pack_fwd(x, wl.w, wl.b, pos, silu=True, out=wl.u[a:b])
+            args = (u, wl.delta[a:b], wl.A, wl.B[a:b], wl.C[a:b], wl.Dp, wl.z[a:b], pos)
+            ssp.selective_scan_pack_fwd(*args, workspace=wl.scan_ws, out=wl.out[a:b])
+            g = {k: wl.g[k][a:b] for k in ("du", "ddelta", "dz", "dB", "dC")}
+            g["dA"], g["dD"] = wl.g["dA"], wl.g["dD"]
+            ssp.selective_scan_pack_bwd(*args, wl.dout[a:b], wl.scan_ws, out=g)
+            ssp.conv1d_pack_bwd(x, wl.w, wl.b, pos, g["du"], silu=True, workspace=wl.conv_ws,
+                                out=(wl.dx[a:b], wl.dw, wl.db))
+            acc["dA"].add_(wl.g["dA"]); acc["dD"].add_(wl.g["dD"])
+            acc["dw"].add_(wl.dw); acc["db"].add_(wl.db)
+
+    for _ in range(warmup):
+        one_step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True); t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        one_step()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def cpu_baseline(inp: synth.Inputs, channels: int, threads: int) -> dict:
+    """The fp64 oracle (as it stands) on a bounded sample: every token of the
+    workload, a subset of its channels; tokens/s scaled to all channels."""
+    import oracle
+    orc = oracle.get()
+    sl = slice(0, channels)
+    f = synth.f64
+    x, w, b = f(inp.x)[:, sl], f(inp.w)[sl], f(inp.b)[sl]
+    delta, A, Dp, z, dout = f(inp.delta)[:, sl], f(inp.A)[sl], f(inp.Dp)[sl], f(inp.z)[:, sl], f(inp.dout)[:, sl]
+    B, C = f(inp.B), f(inp.C)
+    t = time.perf_counter()
+    orc.forward(x, w, b, delta, A, B, C, Dp, z, inp.cu_seqlens, threads=threads)
+    orc.backward(x, w, b, delta, A, B, C, Dp, z, inp.cu_seqlens, dout, threads=threads)
+    sec = time.perf_counter() - t
+    return {"value": inp.T * (channels / inp.D) / sec, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fwd+bwd of all {inp.T} tokens of the workload on {channels} of {inp.D} channels "
+                      f"({sec:.1f} s wall on {threads} threads), scaled by {inp.D}/{channels}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4])
+    ap.add_argument("--no-layouts", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-channels", type=int, default=512)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path has no collectives "
+                                   "(packs are independent, so data parallelism needs no exchange on the path)"}))
+        sys.exit(2)
+    assert torch.cuda.is_available(), "needs a GPU"
+
+    wl_id = args.workload
+    spec = synth.WORKLOADS[wl_id]
+    log(f"[bench] generating workload {wl_id} ({synth.NAMES[wl_id]})")
+    inp = synth.make_inputs(wl_id, with_dout=True)
+    T, D, N = inp.T, inp.D, inp.N
+    wl = Workload(inp)
+    log(f"[bench] T={T} D={D} N={N} nseq={inp.nseq}; warmup {args.warmup}, timing {args.steps} steps")
+    total_ms, ops = time_steps(wl, args.steps, args.warmup, per_op=True)
+    # a second timed pass without per-op events (the headline number)
+    total_ms, _ = time_steps(wl, args.steps, 1, per_op=False)
+    ms_step = total_ms / args.steps
+    tok_s = T / (ms_step * 1e-3)
+    ab = algo_bytes(T, D, N)
+    step_bytes = sum(ab.values())
+    hbm_gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    ops_gbs = {k: ab[k] / (ops[k] * 1e-3) / 1e9 for k in OPS}
+    dominant = max(OPS, key=lambda k: ops[k])
+    roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(ops_gbs[dominant], 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ops_gbs[dominant] / PEAK_HBM_GBS, 4), "traffic": None,
+                "avg_ms": round(ops[dominant], 4), "algo_bytes_per_launch": ab[dominant]}
+    log("[bench] per-op ms: " + ", ".join(f"{k} {ops[k]:.3f}" for k in OPS))
+    log("[bench] per-op algorithmic GB/s: " + ", ".join(f"{k} {ops_gbs[k]:.0f}" for k in OPS))
+
+    layouts = None
+    if not args.no_layouts:
+        layouts = {"packed": round(tok_s, 1)}
+        cu_concat = np.arange(0, T + 1, spec.pack_len, dtype=np.int32)
+        wc = Workload(inp, cu=cu_concat)
+        ms_c, _ = time_steps(wc, max(3, args.steps // 2), 2, per_op=False)
+        layouts["concat_no_reset"] = round(T / (ms_c / max(3, args.steps // 2) * 1e-3), 1)
+        del wc
+        pinp = padded_layout(inp, spec.pack_len)
+        wp = Workload(pinp)
+        ms_p, _ = time_steps(wp, max(3, args.steps // 2), 2, per_op=False)
+        layouts["padded"] = round(T / (ms_p / max(3, args.steps // 2) * 1e-3), 1)
+        layouts["padded_rows"] = pinp.T
+        del wp, pinp
+        ms_s = per_sequence_loop(wl, max(2, args.steps // 5), 1)
+        layouts["per_sequence_loop"] = round(T / (ms_s * 1e-3), 1)
+        log(f"[bench] layouts tokens/s: {layouts}")
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        threads = min(16, os.cpu_count() or 1)
+        ch = min(args.cpu_channels, D)
+        log(f"[bench] oracle baseline on {ch} channels, {threads} threads")
+        cpu = cpu_baseline(inp, ch, threads)
+
+    line = {
+        "metric": "packed tokens/s + HBM GB/s (% peak), conv1d_pack+scan fwd/bwd, 1.4B shape",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": synth.NAMES[wl_id], "d_inner": D, "d_state": N, "conv_width": inp.W,
+                   "packs": spec.n_packs, "pack_len": spec.pack_len, "tokens": T, "sequences": inp.nseq,
+                   "state_dtype": "fp32"},
+        "hbm_gbs": round(hbm_gbs, 1),
+        "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
+        "ops_ms": {k: round(v, 4) for k, v in ops.items()},
+        "ops_algo_gbs": {k: round(v, 1) for k, v in ops_gbs.items()},
+        "roofline": roofline,
+        "layouts_tokens_per_s": layouts,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

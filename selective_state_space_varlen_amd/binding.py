@@ -105,12 +105,14 @@ def _call(name: str, *args):
 
 
 # ---------------------------------------------------------------------------
-def varlen_pack_indices(cu_seqlens: torch.Tensor, T: int, heads: bool = True, dev_err: bool = True):
+def varlen_pack_indices(cu_seqlens: torch.Tensor, T: int, heads: bool = True, dev_err: bool = True,
+                        out: Optional[torch.Tensor] = None):
     """cu_seqlens (int32, device) -> (pos int32 [T], heads uint8 [T] or None,
     dev_err int32 [1] or None). dev_err holds 0 or SSMP_ERR_CU_SEQLENS."""
     _check(cu_seqlens, "cu_seqlens", dtype=torch.int32)
     dev = cu_seqlens.device
-    pos = torch.empty(T, dtype=torch.int32, device=dev)
+    pos = torch.empty(T, dtype=torch.int32, device=dev) if out is None else out
+    _check(pos, "pos", (T,), torch.int32, dev)
     hd = torch.empty(T, dtype=torch.uint8, device=dev) if heads else None
     err = torch.empty(1, dtype=torch.int32, device=dev) if dev_err else None
     _call("varlen_pack_indices", _ptr(cu_seqlens), cu_seqlens.numel() - 1, T, _ptr(pos), _ptr(hd), _ptr(err),
@@ -137,14 +139,20 @@ def conv1d_pack_bwd_workspace_bytes(T: int, D: int, W: int) -> int:
 
 def conv1d_pack_bwd(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor], pos: torch.Tensor,
                     du: torch.Tensor, silu: bool = True, workspace: Optional[torch.Tensor] = None,
-                    want_db: bool = True):
+                    want_db: bool = True, out: Optional[tuple] = None):
+    """Returns (dx, dw, db); `out` may supply those three buffers."""
     T, D = x.shape
     W = w.shape[1]
     _check(x, "x"); _check(w, "w", (D, W), torch.float32, x.device); _check(b, "b", (D,), torch.float32, x.device)
     _check(pos, "pos", (T,), torch.int32, x.device); _check(du, "du", (T, D), x.dtype, x.device)
-    dx = torch.empty_like(x)
-    dw = torch.empty((D, W), dtype=torch.float32, device=x.device)
-    db = torch.empty((D,), dtype=torch.float32, device=x.device) if want_db else None
+    if out is not None:
+        dx, dw, db = out
+    else:
+        dx = torch.empty_like(x)
+        dw = torch.empty((D, W), dtype=torch.float32, device=x.device)
+        db = torch.empty((D,), dtype=torch.float32, device=x.device) if want_db else None
+    _check(dx, "dx", (T, D), x.dtype, x.device); _check(dw, "dw", (D, W), torch.float32, x.device)
+    _check(db, "db", (D,), torch.float32, x.device)
     nbytes = conv1d_pack_bwd_workspace_bytes(T, D, W)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
@@ -179,8 +187,10 @@ def selective_scan_pack_fwd(u, delta, A, B, C, Dskip, z, pos, workspace: Optiona
     return o, workspace
 
 
-def selective_scan_pack_bwd(u, delta, A, B, C, Dskip, z, pos, dout, workspace: torch.Tensor):
-    """Gradients of sum(dout * out); the workspace must come from the forward."""
+def selective_scan_pack_bwd(u, delta, A, B, C, Dskip, z, pos, dout, workspace: torch.Tensor,
+                            out: Optional[dict] = None):
+    """Gradients of sum(dout * out); the workspace must come from the forward.
+    `out` may supply the result buffers (a dict shaped like the return value)."""
     T, D = u.shape
     N = A.shape[1]
     dev = u.device
@@ -189,13 +199,20 @@ def selective_scan_pack_bwd(u, delta, A, B, C, Dskip, z, pos, dout, workspace: t
     _check(Dskip, "Dskip", (D,), torch.float32, dev); _check(z, "z", (T, D), u.dtype, dev)
     _check(pos, "pos", (T,), torch.int32, dev); _check(dout, "dout", (T, D), u.dtype, dev)
     _check(workspace, "workspace", device=dev)
-    du = torch.empty_like(u)
-    ddelta = torch.empty_like(u)
-    dA = torch.empty((D, N), dtype=torch.float32, device=dev)
-    dB = torch.empty((T, N), dtype=torch.float32, device=dev)
-    dC = torch.empty((T, N), dtype=torch.float32, device=dev)
-    dD = torch.empty((D,), dtype=torch.float32, device=dev) if Dskip is not None else None
-    dz = torch.empty_like(u) if z is not None else None
+    if out is not None:
+        du, ddelta, dA, dB, dC, dD, dz = (out[k] for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz"))
+    else:
+        du = torch.empty_like(u)
+        ddelta = torch.empty_like(u)
+        dA = torch.empty((D, N), dtype=torch.float32, device=dev)
+        dB = torch.empty((T, N), dtype=torch.float32, device=dev)
+        dC = torch.empty((T, N), dtype=torch.float32, device=dev)
+        dD = torch.empty((D,), dtype=torch.float32, device=dev) if Dskip is not None else None
+        dz = torch.empty_like(u) if z is not None else None
+    _check(du, "du", (T, D), u.dtype, dev); _check(ddelta, "ddelta", (T, D), u.dtype, dev)
+    _check(dA, "dA", (D, N), torch.float32, dev); _check(dB, "dB", (T, N), torch.float32, dev)
+    _check(dC, "dC", (T, N), torch.float32, dev); _check(dD, "dD", (D,), torch.float32, dev)
+    _check(dz, "dz", (T, D), u.dtype, dev)
     _call("selective_scan_pack_bwd", _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z),
           _ptr(pos), _ptr(dout), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(du),
           _ptr(ddelta), _ptr(dA), _ptr(dB), _ptr(dC), _ptr(dD), _ptr(dz), T, D, N, _dtype_code(u), _stream(u))

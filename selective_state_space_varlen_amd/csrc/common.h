@@ -67,6 +67,16 @@ __device__ __forceinline__ float sigmoid_fast(float v) {
     return __builtin_amdgcn_rcpf(1.0f + exp2_fast(-v * kLog2e));
 }
 
+// Ordering point for LDS traffic inside a one-wave workgroup. A wave's LDS
+// operations execute in issue order, so no hardware barrier is needed; this
+// only stops the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void wave_sync() { __builtin_amdgcn_wave_barrier(); }
+
+// Value of the neighbouring lane (lane ^ 1) through DPP, without the LDS path.
+__device__ __forceinline__ float swap_adjacent(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
 }  // namespace ssmp

@@ -8,9 +8,11 @@
 //   dh_t   = g_t C_t[n] + c_{t+1}            c_t = [t not a head] a_t dh_t
 //   dC_t  += g_t h_t          dB_t += dh_t delta_t u_t      (summed over channels)
 //   du_t   = g_t Dskip + delta_t sum_n dh_t B_t[n]
-//   ddelta_t = u_t sum_n dh_t B_t[n] + sum_n [not head] A dh_t a_t h_{t-1}
-//   dA    += [not head] delta_t dh_t a_t h_{t-1}       dDskip += g_t u_t
+//   ddelta_t = u_t sum_n dh_t B_t[n] + sum_n [not head] A r_t,  r_t = dh_t a_t h_{t-1}
+//   dA    += [not head] delta_t r_t                      dDskip += g_t u_t
 //   dz_t   = dout_t y_t s (1 + z_t (1 - s)),  s = sigmoid(z_t)
+// r_t is formed as dh_t (h_t - delta_t u_t B_t[n]) = dh_t h_t - dB_t-term B_t[n],
+// so only the state after each token is needed.
 //
 // Time parallelism mirrors the forward, in reverse: a chunk's carry out of
 // its first token is c_out = P' c_in + S' with
@@ -18,13 +20,14 @@
 // which one forward sweep over the chunk's leading tokens yields. A
 // sequential pass over chunks (right to left) turns these into the carry
 // entering each chunk. The main kernel then walks each chunk backwards in
-// kCK-token blocks: it restarts from the forward's checkpoint, rebuilds the
+// kCK-token blocks (inputs staged through LDS, the next block in flight): it
+// restarts from the forward's checkpoint at the block start, rebuilds the
 // states at kK-token sub-chunk starts (kept in LDS), and for each sub-chunk
-// replays kK tokens with their states and decays held in VGPRs before
-// running the reverse step over them. dB and dC (sums over channels) are
-// reduced across the wave through LDS and written per channel group; dA and
-// dDskip are written per chunk; small kernels finish both sums in a fixed
-// order, so results are deterministic.
+// replays kK tokens with their states and decays held in VGPRs before running
+// the reverse step over them. dB and dC (sums over channels) are reduced
+// across the wave through LDS and written per channel group; dA and dDskip
+// are written per chunk; small kernels finish both sums in a fixed order, so
+// results are deterministic.
 #include "scan_common.h"
 
 namespace ssmp {
@@ -34,10 +37,12 @@ namespace ssmp {
 // ---------------------------------------------------------------------------
 template <typename T, int NS>
 __global__ __launch_bounds__(64) void k_scan_bwd_summary(const T* __restrict__ delta, const float* __restrict__ A,
-                                                         const T* __restrict__ C, const T* __restrict__ z,
+                                                         const float* __restrict__ bc, const T* __restrict__ z,
                                                          const T* __restrict__ dout, const int32_t* __restrict__ pos,
                                                          float* __restrict__ Pr, float* __restrict__ Sr, int64_t T_,
-                                                         int D) {
+                                                         int D, int vec) {
+    using St = Stager<T, 3>;
+    __shared__ __attribute__((aligned(16))) T lds[3 * kCK * kWave];
     const int lane = threadIdx.x;
     const Tile tl = tile_of(D);
     const int d = tl.g * kWave + lane;
@@ -68,21 +73,32 @@ __global__ __launch_bounds__(64) void k_scan_bwd_summary(const T* __restrict__ d
         pf[n] = 1.0f;
         sr[n] = 0.0f;
     }
-    for (int64_t t = t0; t < fh; ++t) {
-        const size_t e = (size_t)t * D + dd;
-        const float dt = Elt<T>::ld(delta, e);
-        float g = Elt<T>::ld(dout, e);
-        if (gate) {
-            const float zz = Elt<T>::ld(z, e);
-            g *= zz * sigmoid_fast(zz);
-        }
-        float Cv[NS];
-        load_row<NS>(C + (size_t)t * NS, Cv);
+    const T* const src[3] = {delta, gate ? z : delta, dout};
+    St st;
+    st.fetch(src, t0, T_, D, tl.g, lane, vec);
+    for (int64_t tb = t0; tb < fh; tb += kCK) {
+        st.commit(lds, src, tb, T_, D, tl.g, lane, vec);
+        wave_sync();
+        if (tb + kCK < fh) st.fetch(src, tb + kCK, T_, D, tl.g, lane, vec);
 #pragma unroll
-        for (int n = 0; n < NS; ++n) {
-            pf[n] *= exp2_fast(dt * A2[n]);
-            sr[n] = __builtin_fmaf(pf[n], g * Cv[n], sr[n]);
+        for (int k = 0; k < kCK; ++k) {
+            const int64_t t = tb + k;
+            if (t < fh) {
+                const float dt = St::get(lds, 0, k, lane);
+                float g = St::get(lds, 2, k, lane);
+                if (gate) {
+                    const float zz = St::get(lds, 1, k, lane);
+                    g *= zz * sigmoid_fast(zz);
+                }
+                const float* __restrict__ row = bc + (size_t)t * 2 * NS;
+#pragma unroll
+                for (int n = 0; n < NS; ++n) {
+                    pf[n] *= exp2_fast(dt * A2[n]);
+                    sr[n] = __builtin_fmaf(pf[n], g * row[NS + n], sr[n]);
+                }
+            }
         }
+        wave_sync();
     }
     if (act) {
 #pragma unroll
@@ -120,13 +136,12 @@ __global__ __launch_bounds__(256) void k_scan_bwd_carry(const float* __restrict_
 // ---------------------------------------------------------------------------
 // 3. the reverse pass
 // ---------------------------------------------------------------------------
-template <typename T, int NS>
+template <typename T>
 struct BwdArgs {
     const T* u;
     const T* delta;
     const float* A;
-    const T* B;
-    const T* C;
+    const float* bc;
     const float* Dskip;
     const T* z;
     const T* dout;
@@ -141,199 +156,242 @@ struct BwdArgs {
     float* dBC;
     int64_t T_;
     int D;
+    int vec;
 };
-
-// Forward step of one token (shared by the replays).
-template <typename T, int NS>
-__device__ __forceinline__ void fwd_step(const BwdArgs<T, NS>& p, int64_t t, int dd, const float (&A2)[NS],
-                                         float (&h)[NS]) {
-    const size_t e = (size_t)t * p.D + dd;
-    const float dt = Elt<T>::ld(p.delta, e);
-    const float dtu = dt * Elt<T>::ld(p.u, e);
-    float Bv[NS];
-    load_row<NS>(p.B + (size_t)t * NS, Bv);
-    if (p.pos[t] == 0) {
-#pragma unroll
-        for (int n = 0; n < NS; ++n) h[n] = 0.0f;
-    }
-#pragma unroll
-    for (int n = 0; n < NS; ++n) h[n] = __builtin_fmaf(exp2_fast(dt * A2[n]), h[n], dtu * Bv[n]);
-}
 
 constexpr int kRedStride = kWave + 4;  // LDS row stride (floats) of the dB/dC transpose
 
-template <typename T, int NS>
-__global__ __launch_bounds__(64) void k_scan_bwd_main(BwdArgs<T, NS> p) {
+// LPC lanes share a channel, each holding NS/LPC of its states, so a wave
+// covers 64/LPC channels. Two lanes per channel halve the registers and LDS a
+// wave needs, which lets two or more waves share a SIMD; per-channel sums over
+// the states are completed with one DPP exchange between the lane pair.
+template <typename T, int NS, int LPC>
+__global__ __launch_bounds__(64) void k_scan_bwd_main(BwdArgs<T> p) {
+    constexpr int NH = NS / LPC;      // states per lane
+    constexpr int CW = kWave / LPC;   // channels per wave
+    static_assert(NH * LPC == NS && (LPC == 1 || LPC == 2), "lane split");
+    using St = Stager<T, 4, kCK, CW>;  // u, delta, z, dout
     constexpr int NSUB = kCK / kK;
-    __shared__ float sub[NSUB > 1 ? NSUB - 1 : 1][NS][kWave];
-    __shared__ __attribute__((aligned(16))) float red[2 * NS][kRedStride];
+    __shared__ __attribute__((aligned(16))) T lds[St::kElems];
+    __shared__ __attribute__((aligned(16))) float bcl[kCK * 2 * NS];  // B/C rows of the block
+    __shared__ float sub[NSUB > 1 ? NSUB - 1 : 1][NH][kWave];
+    __shared__ __attribute__((aligned(16))) float red[2 * NH][kRedStride];
 
     const int lane = threadIdx.x;
-    const Tile tl = tile_of(p.D);
+    const int ch = lane / LPC;        // channel within the group
+    const int sh = lane % LPC;        // which share of the states
+    const Tile tl = tile_of_w<CW>(p.D);
     const int g = tl.g;
-    const int d = g * kWave + lane;
+    const int d = g * CW + ch;
     const bool act = d < p.D;
+    const bool full = (g + 1) * CW <= p.D;
     const int dd = act ? d : p.D - 1;
     const int64_t c = tl.c;
     const int64_t t0 = c * kLC;
     const int64_t t1 = (t0 + kLC < p.T_) ? t0 + kLC : p.T_;
     const size_t ND = (size_t)NS * p.D;
     const bool gate = p.z != nullptr;
+    const int n0 = sh * NH;           // first state of this lane
+    const bool writer = sh == 0 && (full || act);
 
-    float A2[NS], carry[NS], dA[NS];
+    // lanes past D carry zeros throughout, so they add nothing to dB/dC
+    float A2[NH], carry[NH], dA[NH];
 #pragma unroll
-    for (int n = 0; n < NS; ++n) {
-        A2[n] = p.A[(size_t)dd * NS + n] * kLog2e;
-        carry[n] = p.cin[(size_t)c * ND + (size_t)n * p.D + dd];
-        dA[n] = 0.0f;
+    for (int i = 0; i < NH; ++i) {
+        A2[i] = p.A[(size_t)dd * NS + n0 + i] * kLog2e;
+        carry[i] = act ? p.cin[(size_t)c * ND + (size_t)(n0 + i) * p.D + dd] : 0.0f;
+        dA[i] = 0.0f;
     }
-    const float Dv = p.Dskip ? p.Dskip[dd] : 0.0f;
+    const float Dv = (p.Dskip && act) ? p.Dskip[dd] : 0.0f;
     float dDacc = 0.0f;
+    const T* const src[4] = {p.u, p.delta, gate ? p.z : p.u, p.dout};
+
+    // B/C rows of a block: kCK * 2NS floats, fetched with the block's inputs
+    constexpr int BCV = kCK * 2 * NS / 4;                 // float4 pieces
+    constexpr int BCP = (BCV + kWave - 1) / kWave;        // pieces per lane
+    float4 bcr[BCP];
+    auto fetch_bc = [&](int64_t tb) {
+        const float4* srcv = reinterpret_cast<const float4*>(p.bc + (size_t)tb * 2 * NS);
+        const int64_t lim = ((p.T_ - tb < kCK) ? (p.T_ - tb) : kCK) * 2 * NS / 4;
+#pragma unroll
+        for (int q = 0; q < BCP; ++q) {
+            const int idx = q * kWave + lane;
+            bcr[q] = (idx < BCV && idx < lim) ? srcv[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto commit_bc = [&]() {
+#pragma unroll
+        for (int q = 0; q < BCP; ++q) {
+            const int idx = q * kWave + lane;
+            if (idx < BCV) reinterpret_cast<float4*>(bcl)[idx] = bcr[q];
+        }
+    };
 
     const int64_t nblk = (t1 - t0 + kCK - 1) / kCK;
+    St st;
+    {
+        const int64_t tl0 = t0 + (nblk - 1) * kCK;
+        st.fetch(src, tl0, p.T_, p.D, g, lane, p.vec);
+        fetch_bc(tl0);
+    }
     for (int64_t jb = nblk - 1; jb >= 0; --jb) {
         const int64_t tb0 = t0 + jb * kCK;
-        const int64_t tb1 = (tb0 + kCK < t1) ? tb0 + kCK : t1;
-        const int nsub = (int)((tb1 - tb0 + kK - 1) / kK);
+        const int nb = (int)(((tb0 + kCK < t1) ? tb0 + kCK : t1) - tb0);  // tokens in this block
+        const int nsub = (nb + kK - 1) / kK;
         const float* hb = p.ckpt + (size_t)(tb0 / kCK) * ND;
+        const uint32_t heads = block_heads<kCK>(p.pos, tb0, p.T_, lane);
+        wave_sync();
+        st.commit(lds, src, tb0, p.T_, p.D, g, lane, p.vec);
+        commit_bc();
+        wave_sync();
+        if (jb > 0) {
+            st.fetch(src, tb0 - kCK, p.T_, p.D, g, lane, p.vec);
+            fetch_bc(tb0 - kCK);
+        }
 
         // states entering sub-chunks 1..nsub-1
         if (nsub > 1) {
-            float h[NS];
+            float h[NH];
 #pragma unroll
-            for (int n = 0; n < NS; ++n) h[n] = hb[(size_t)n * p.D + dd];
-            for (int i = 1; i < nsub; ++i) {
+            for (int i = 0; i < NH; ++i) h[i] = act ? hb[(size_t)(n0 + i) * p.D + dd] : 0.0f;
+            for (int sc = 1; sc < nsub; ++sc) {
 #pragma unroll
-                for (int k = 0; k < kK; ++k) fwd_step<T, NS>(p, tb0 + (int64_t)(i - 1) * kK + k, dd, A2, h);
+                for (int kk = 0; kk < kK; ++kk) {
+                    const int k = (sc - 1) * kK + kk;
+                    const float dt = St::get(lds, 1, k, ch);
+                    const float dtu = dt * St::get(lds, 0, k, ch);
+                    const float* row = bcl + k * 2 * NS + n0;
+                    reset_if<NH>((heads >> k) & 1u, h);
 #pragma unroll
-                for (int n = 0; n < NS; ++n) sub[i - 1][n][lane] = h[n];
+                    for (int i = 0; i < NH; ++i) h[i] = __builtin_fmaf(exp2_fast(dt * A2[i]), h[i], dtu * row[i]);
+                }
+#pragma unroll
+                for (int i = 0; i < NH; ++i) sub[sc - 1][i][lane] = h[i];
             }
         }
 
-        for (int i = nsub - 1; i >= 0; --i) {
-            const int64_t ts0 = tb0 + (int64_t)i * kK;
-            const int ns = (int)((ts0 + kK < tb1) ? kK : tb1 - ts0);
-            float hp0[NS];
-            if (i == 0) {
-#pragma unroll
-                for (int n = 0; n < NS; ++n) hp0[n] = hb[(size_t)n * p.D + dd];
-            } else {
-#pragma unroll
-                for (int n = 0; n < NS; ++n) hp0[n] = sub[i - 1][n][lane];
-            }
-            // replay: states hh[k] and decays aa[k] of the sub-chunk's tokens
-            float hh[kK][NS], aa[kK][NS], yk[kK];
+        for (int sc = nsub - 1; sc >= 0; --sc) {
+            const int kb = sc * kK;  // first token of the sub-chunk within the block
+            const int ns = (nb - kb < kK) ? nb - kb : kK;
+            // replay: the states hh[k] after each of the sub-chunk's tokens
+            float hh[kK][NH], yk[kK];
             {
-                float h[NS];
+                float h[NH];
+                if (sc == 0) {
 #pragma unroll
-                for (int n = 0; n < NS; ++n) h[n] = hp0[n];
+                    for (int i = 0; i < NH; ++i) h[i] = act ? hb[(size_t)(n0 + i) * p.D + dd] : 0.0f;
+                } else {
 #pragma unroll
-                for (int k = 0; k < kK; ++k) {
-                    if (k < ns) {
-                        const int64_t t = ts0 + k;
-                        const size_t e = (size_t)t * p.D + dd;
-                        const float dt = Elt<T>::ld(p.delta, e);
-                        const float uu = Elt<T>::ld(p.u, e);
+                    for (int i = 0; i < NH; ++i) h[i] = sub[sc - 1][i][lane];
+                }
+#pragma unroll
+                for (int kk = 0; kk < kK; ++kk) {
+                    if (kk < ns) {
+                        const int k = kb + kk;
+                        const float dt = St::get(lds, 1, k, ch);
+                        const float uu = St::get(lds, 0, k, ch);
                         const float dtu = dt * uu;
-                        float Bv[NS], Cv[NS];
-                        load_row<NS>(p.B + (size_t)t * NS, Bv);
-                        load_row<NS>(p.C + (size_t)t * NS, Cv);
-                        if (p.pos[t] == 0) {
-#pragma unroll
-                            for (int n = 0; n < NS; ++n) h[n] = 0.0f;
-                        }
+                        const float* row = bcl + k * 2 * NS + n0;
+                        reset_if<NH>((heads >> k) & 1u, h);
                         float y = 0.0f;
 #pragma unroll
-                        for (int n = 0; n < NS; ++n) {
-                            const float a = exp2_fast(dt * A2[n]);
-                            aa[k][n] = a;
-                            h[n] = __builtin_fmaf(a, h[n], dtu * Bv[n]);
-                            hh[k][n] = h[n];
-                            y = __builtin_fmaf(Cv[n], h[n], y);
+                        for (int i = 0; i < NH; ++i) {
+                            h[i] = __builtin_fmaf(exp2_fast(dt * A2[i]), h[i], dtu * row[i]);
+                            hh[kk][i] = h[i];
+                            y = __builtin_fmaf(row[NS + i], h[i], y);
                         }
-                        yk[k] = __builtin_fmaf(Dv, uu, y);
+                        if constexpr (LPC == 2) y += swap_adjacent(y);
+                        yk[kk] = __builtin_fmaf(Dv, uu, y);
                     }
                 }
             }
             // reverse over the sub-chunk
 #pragma unroll
-            for (int k = kK - 1; k >= 0; --k) {
-                if (k < ns) {
-                    const int64_t t = ts0 + k;
-                    const size_t e = (size_t)t * p.D + dd;
-                    const float dt = Elt<T>::ld(p.delta, e);
-                    const float uu = Elt<T>::ld(p.u, e);
-                    const float dtu = dt * uu;
-                    const float go = Elt<T>::ld(p.dout, e);
+            for (int kk = kK - 1; kk >= 0; --kk) {
+                if (kk < ns) {
+                    const int k = kb + kk;
+                    const int64_t t = tb0 + k;
+                    const float dt = St::get(lds, 1, k, ch);
+                    const float uu = St::get(lds, 0, k, ch);
+                    const float go = St::get(lds, 3, k, ch);
                     float gg = go, dzv = 0.0f;
                     if (gate) {
-                        const float zz = Elt<T>::ld(p.z, e);
+                        const float zz = St::get(lds, 2, k, ch);
                         const float sg = sigmoid_fast(zz);
                         gg = go * zz * sg;
-                        dzv = go * yk[k] * sg * (1.0f + zz * (1.0f - sg));
+                        dzv = go * yk[kk] * sg * (1.0f + zz * (1.0f - sg));
                     }
-                    float Bv[NS], Cv[NS];
-                    load_row<NS>(p.B + (size_t)t * NS, Bv);
-                    load_row<NS>(p.C + (size_t)t * NS, Cv);
-                    const bool head = p.pos[t] == 0;
+                    gg = act ? gg : 0.0f;
+                    const float dtu = act ? dt * uu : 0.0f;
+                    const float* row = bcl + k * 2 * NS + n0;
+                    const int col = sh * CW + ch;
                     float sumB = 0.0f, sumAr = 0.0f;
-                    const float gm = act ? gg : 0.0f;  // inactive lanes add nothing to dB/dC
-                    if (head) {
+                    if ((heads >> k) & 1u) {
+                        asm volatile("");
 #pragma unroll
-                        for (int n = 0; n < NS; ++n) {
-                            const float dh = __builtin_fmaf(gg, Cv[n], carry[n]);
-                            red[n][lane] = act ? dh * dtu : 0.0f;   // dB row
-                            red[NS + n][lane] = gm * hh[k][n];        // dC row
-                            sumB = __builtin_fmaf(dh, Bv[n], sumB);
-                            carry[n] = 0.0f;
+                        for (int i = 0; i < NH; ++i) {
+                            const float dh = __builtin_fmaf(gg, row[NS + i], carry[i]);
+                            red[i][col] = dh * dtu;             // dB row
+                            red[NH + i][col] = gg * hh[kk][i];  // dC row
+                            sumB = __builtin_fmaf(dh, row[i], sumB);
+                            carry[i] = 0.0f;
                         }
                     } else {
 #pragma unroll
-                        for (int n = 0; n < NS; ++n) {
-                            const float dh = __builtin_fmaf(gg, Cv[n], carry[n]);
-                            red[n][lane] = act ? dh * dtu : 0.0f;   // dB row
-                            red[NS + n][lane] = gm * hh[k][n];        // dC row
-                            sumB = __builtin_fmaf(dh, Bv[n], sumB);
-                            const float cc = aa[k][n] * dh;
-                            const float hprev = (k == 0) ? hp0[n] : hh[k > 0 ? k - 1 : 0][n];
-                            const float r = cc * hprev;
-                            sumAr = __builtin_fmaf(r, A2[n], sumAr);
-                            dA[n] = __builtin_fmaf(r, dt, dA[n]);
-                            carry[n] = cc;
+                        for (int i = 0; i < NH; ++i) {
+                            const float dh = __builtin_fmaf(gg, row[NS + i], carry[i]);
+                            const float db = dh * dtu;
+                            red[i][col] = db;
+                            red[NH + i][col] = gg * hh[kk][i];
+                            sumB = __builtin_fmaf(dh, row[i], sumB);
+                            // r = dh a h_{t-1} = dh (h_t - dtu B_n)
+                            const float r = __builtin_fmaf(-db, row[i], dh * hh[kk][i]);
+                            sumAr = __builtin_fmaf(r, A2[i], sumAr);
+                            dA[i] = __builtin_fmaf(r, dt, dA[i]);
+                            carry[i] = exp2_fast(dt * A2[i]) * dh;
                         }
+                    }
+                    if constexpr (LPC == 2) {
+                        sumB += swap_adjacent(sumB);
+                        sumAr += swap_adjacent(sumAr);
                     }
                     const float duv = __builtin_fmaf(gg, Dv, dt * sumB);
                     const float ddv = __builtin_fmaf(uu, sumB, sumAr * kLn2);
                     dDacc = __builtin_fmaf(gg, uu, dDacc);
-                    if (act) {
-                        Elt<T>::st(p.du, (size_t)t * p.D + d, duv);
-                        Elt<T>::st(p.ddelta, (size_t)t * p.D + d, ddv);
-                        if (gate) Elt<T>::st(p.dz, (size_t)t * p.D + d, dzv);
+                    if (writer) {
+                        const size_t e = (size_t)t * p.D + d;
+                        Elt<T>::st(p.du, e, duv);
+                        Elt<T>::st(p.ddelta, e, ddv);
+                        if (gate) Elt<T>::st(p.dz, e, dzv);
                     }
-                    // dB/dC: sum the wave's 64 channels. Lane l adds half a row
-                    // (value l/2, channels 32*(l%2) ..) and its neighbour the other.
-                    __syncthreads();
-                    const int j = lane >> 1, hf = lane & 1;
+                    // dB/dC of state n = sh'*NH + i: the sum of row i (dB) or
+                    // NH + i (dC) over columns sh'*CW .. sh'*CW + CW - 1. Two
+                    // lanes per output value, each adding half the columns.
+                    wave_sync();
+                    const int o = lane >> 1, hf = lane & 1;  // output o: kind o / NS, state o % NS
                     float v = 0.0f;
-                    if (j < 2 * NS) {
-                        const float4* row = reinterpret_cast<const float4*>(&red[j][hf * 32]);
+                    if (o < 2 * NS) {
+                        const int kind = o / NS, n = o % NS;
+                        const int rrow = kind * NH + (n % NH);
+                        const int c0 = (n / NH) * CW + hf * (CW / 2);
+                        const float4* rw = reinterpret_cast<const float4*>(&red[rrow][c0]);
 #pragma unroll
-                        for (int q = 0; q < 8; ++q) {
-                            const float4 r4 = row[q];
+                        for (int q = 0; q < CW / 8; ++q) {
+                            const float4 r4 = rw[q];
                             v += (r4.x + r4.y) + (r4.z + r4.w);
                         }
                     }
-                    v += __shfl_xor(v, 1);
-                    if (hf == 0 && j < 2 * NS) p.dBC[((size_t)g * p.T_ + t) * (2 * NS) + j] = v;
-                    __syncthreads();
+                    v += swap_adjacent(v);
+                    if (hf == 0 && o < 2 * NS) p.dBC[((size_t)g * p.T_ + t) * (2 * NS) + o] = v;
+                    wave_sync();
                 }
             }
         }
     }
     if (act) {
 #pragma unroll
-        for (int n = 0; n < NS; ++n) p.dApart[(size_t)c * ND + (size_t)n * p.D + d] = dA[n];
-        p.dDpart[(size_t)c * p.D + d] = dDacc;
+        for (int i = 0; i < NH; ++i) p.dApart[(size_t)c * ND + (size_t)(n0 + i) * p.D + d] = dA[i];
+        if (sh == 0) p.dDpart[(size_t)c * p.D + d] = dDacc;
     }
 }
 
@@ -382,27 +440,32 @@ static int scan_bwd_launch(const void* u, const void* delta, const float* A, con
     const ScanWs L = scan_ws_layout(T_, D, NS);
     const dim3 grid((unsigned)(L.ngroup * L.nchunk));
     const int64_t ND = (int64_t)NS * D;
+    const int vec = stage_vec_ok<T>(D, {u, delta, z, dout}) ? 1 : 0;
+    k_bc_to_f32<T, NS><<<(unsigned)((T_ * 2 * NS + 255) / 256), 256, 0, s>>>((const T*)B, (const T*)C, ws + L.bc,
+                                                                            T_);
+    SSMP_LAUNCH_CHECK();
     if (L.nchunk > 1) {
-        k_scan_bwd_summary<T, NS><<<grid, kWave, 0, s>>>((const T*)delta, A, (const T*)C, (const T*)z,
-                                                         (const T*)dout, pos, ws + L.Pr, ws + L.Sr, T_, D);
+        k_scan_bwd_summary<T, NS><<<grid, kWave, 0, s>>>((const T*)delta, A, ws + L.bc, (const T*)z, (const T*)dout,
+                                                         pos, ws + L.Pr, ws + L.Sr, T_, D, vec);
         SSMP_LAUNCH_CHECK();
     }
     k_scan_bwd_carry<NS><<<(unsigned)((ND + 255) / 256), 256, 0, s>>>(ws + L.Pr, ws + L.Sr, pos, ws + L.cin, D,
                                                                       L.nchunk);
     SSMP_LAUNCH_CHECK();
-    BwdArgs<T, NS> a;
-    a.u = (const T*)u; a.delta = (const T*)delta; a.A = A; a.B = (const T*)B; a.C = (const T*)C; a.Dskip = Dskip;
+    BwdArgs<T> a;
+    a.u = (const T*)u; a.delta = (const T*)delta; a.A = A; a.bc = ws + L.bc; a.Dskip = Dskip;
     a.z = (const T*)z; a.dout = (const T*)dout; a.pos = pos; a.ckpt = ws + L.ckpt; a.cin = ws + L.cin;
     a.du = (T*)du; a.ddelta = (T*)ddelta; a.dz = (T*)dz; a.dApart = ws + L.dApart; a.dDpart = ws + L.dDpart;
-    a.dBC = ws + L.dBC; a.T_ = T_; a.D = D;
-    k_scan_bwd_main<T, NS><<<grid, kWave, 0, s>>>(a);
+    a.dBC = ws + L.dBC; a.T_ = T_; a.D = D; a.vec = vec;
+    constexpr int LPC = NS >= 4 ? 2 : 1;
+    const int64_t ngroup = (D + kWave / LPC - 1) / (kWave / LPC);
+    k_scan_bwd_main<T, NS, LPC><<<(unsigned)(ngroup * L.nchunk), kWave, 0, s>>>(a);
     SSMP_LAUNCH_CHECK();
     const int64_t nrp = ND > D ? ND : D;
     k_scan_bwd_reduce_params<NS><<<(unsigned)((nrp + 255) / 256), 256, 0, s>>>(ws + L.dApart, ws + L.dDpart,
                                                                                L.nchunk, D, dA, dD);
     SSMP_LAUNCH_CHECK();
-    k_scan_bwd_reduce_bc<NS><<<(unsigned)((T_ * 2 * NS + 255) / 256), 256, 0, s>>>(ws + L.dBC, L.ngroup, T_, dB,
-                                                                                   dC);
+    k_scan_bwd_reduce_bc<NS><<<(unsigned)((T_ * 2 * NS + 255) / 256), 256, 0, s>>>(ws + L.dBC, ngroup, T_, dB, dC);
     SSMP_LAUNCH_CHECK();
     return SSMP_OK;
 }

@@ -1,4 +1,5 @@
-// Shared layout of the selective-scan workspace and tiling constants.
+// Shared tiling, workspace layout and staging helpers of the selective-scan
+// kernels.
 #pragma once
 
 #include "common.h"
@@ -7,9 +8,10 @@ namespace ssmp {
 
 // Time tiling. A chunk of kLC tokens is the unit of time parallelism: one
 // wave walks it serially for 64 channels, and chunks are joined by the affine
-// carry h_out = P h_in + S (P = 0 once the chunk holds a head). The forward
-// also stores the state every kCK tokens; the backward restarts from those
-// and replays kK-token sub-chunks with their states held in registers.
+// carry h_out = P h_in + S (P = 0 once the chunk holds a head). Tokens are
+// staged in blocks of kCK; the forward stores the state at every block start
+// and the backward restarts from those, replaying kK-token sub-chunks whose
+// states stay in registers.
 constexpr int kLC = 256;
 constexpr int kCK = 16;
 constexpr int kK = 4;
@@ -20,13 +22,14 @@ struct ScanWs {
     int64_t nchunk;   // chunks of kLC tokens
     int64_t ngroup;   // channel groups of 64
     // offsets in floats from the workspace base
-    size_t ckpt;      // [nck][N][D]
+    size_t ckpt;      // [nck][N][D]      forward -> backward
+    size_t bc;        // [T][2N]          fp32 copy of the B and C rows (each pass makes its own)
     size_t P, S;      // [nchunk][N][D]   forward: chunk decay and local end state
     size_t Pr, Sr;    // [nchunk][N][D]   backward: reverse-carry summaries
     size_t cin;       // [nchunk][N][D]   backward: carry entering each chunk from the right
     size_t dApart;    // [nchunk][N][D]
     size_t dDpart;    // [nchunk][D]
-    size_t dBC;       // [ngroup][T][2N]
+    size_t dBC;       // [ceil(D/32)][T][2N]  per channel-group partial sums of dB, dC
     size_t total;     // floats
 };
 
@@ -36,19 +39,19 @@ inline ScanWs scan_ws_layout(int64_t T, int D, int N) {
     w.nchunk = (T + kLC - 1) / kLC;
     w.ngroup = (D + kWave - 1) / kWave;
     const size_t ND = (size_t)N * D;
+    auto up = [](size_t v) { return (v + 63) & ~size_t(63); };  // 256-byte aligned regions
     size_t off = 0;
-    w.ckpt = off; off += (size_t)w.nck * ND;
+    w.ckpt = off; off = up(off + (size_t)w.nck * ND);
+    w.bc = off; off = up(off + (size_t)T * 2 * N);
     const size_t scratch = off;
-    // forward scratch
-    w.P = scratch; w.S = w.P + (size_t)w.nchunk * ND;
-    const size_t fwd_end = w.S + (size_t)w.nchunk * ND;
-    // backward scratch (reuses the same region)
-    w.Pr = scratch; w.Sr = w.Pr + (size_t)w.nchunk * ND;
-    w.cin = w.Sr + (size_t)w.nchunk * ND;
-    w.dApart = w.cin + (size_t)w.nchunk * ND;
-    w.dDpart = w.dApart + (size_t)w.nchunk * ND;
-    w.dBC = w.dDpart + (size_t)w.nchunk * D;
-    const size_t bwd_end = w.dBC + (size_t)w.ngroup * (size_t)T * 2 * N;
+    w.P = scratch; w.S = up(w.P + (size_t)w.nchunk * ND);
+    const size_t fwd_end = up(w.S + (size_t)w.nchunk * ND);
+    w.Pr = scratch; w.Sr = up(w.Pr + (size_t)w.nchunk * ND);
+    w.cin = up(w.Sr + (size_t)w.nchunk * ND);
+    w.dApart = up(w.cin + (size_t)w.nchunk * ND);
+    w.dDpart = up(w.dApart + (size_t)w.nchunk * ND);
+    w.dBC = up(w.dDpart + (size_t)w.nchunk * D);
+    const size_t bwd_end = up(w.dBC + (size_t)((D + 31) / 32) * (size_t)T * 2 * N);
     w.total = fwd_end > bwd_end ? fwd_end : bwd_end;
     return w;
 }
@@ -72,6 +75,120 @@ inline int scan_check_args(int64_t T, int D, int N, int dtype) {
     if (!(N == 1 || N == 2 || N == 4 || N == 8 || N == 16)) return SSMP_ERR_UNSUPPORTED;
     if (dtype != SSMP_F32 && dtype != SSMP_BF16) return SSMP_ERR_UNSUPPORTED;
     return SSMP_OK;
+}
+
+// B and C rows of every token as fp32, interleaved: bc[t] = [B_t (N), C_t (N)],
+// so one wave-uniform scalar load brings both rows of a token.
+template <typename T, int NS>
+__global__ __launch_bounds__(256) void k_bc_to_f32(const T* __restrict__ B, const T* __restrict__ C,
+                                                  float* __restrict__ bc, int64_t T_) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // t*2NS + j
+    if (i >= T_ * 2 * NS) return;
+    const int64_t t = i / (2 * NS);
+    const int j = (int)(i % (2 * NS));
+    bc[i] = (j < NS) ? Elt<T>::ld(B, (size_t)t * NS + j) : Elt<T>::ld(C, (size_t)t * NS + (j - NS));
+}
+
+template <int NS>
+__device__ __forceinline__ void load_bc(const float* __restrict__ bc, int64_t t, float (&Bv)[NS], float (&Cv)[NS]) {
+    const float* __restrict__ row = bc + (size_t)t * 2 * NS;
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+        Bv[n] = row[n];
+        Cv[n] = row[NS + n];
+    }
+}
+
+// Head flags of the BT tokens of a block as a wave-uniform bit mask (bit k:
+// token tb+k starts a sequence). Lanes k < BT each read one position.
+template <int BT = kCK>
+__device__ __forceinline__ uint32_t block_heads(const int32_t* __restrict__ pos, int64_t tb, int64_t T_, int lane) {
+    const int64_t t = tb + lane;
+    const bool f = (lane < BT) && (t < T_) && pos[t] == 0;
+    return (uint32_t)__ballot(f);
+}
+
+// Reset of the state at a head token. Heads are rare, so this stays a real
+// (wave-uniform) branch: the empty volatile asm keeps the compiler from
+// turning it into a select on every state of every token.
+template <int NS>
+__device__ __forceinline__ void reset_if(bool head, float (&h)[NS]) {
+    if (head) {
+        asm volatile("");
+#pragma unroll
+        for (int n = 0; n < NS; ++n) h[n] = 0.0f;
+    }
+}
+
+// Staging of R per-lane (T, D) inputs for one BT-token block of a 64-channel
+// group into LDS, laid out [r][k][64]. With 16-byte aligned rows (D a
+// multiple of 16 / sizeof(T)) the block is fetched into registers with
+// 16-byte loads one block ahead, and committed to LDS when the block starts;
+// otherwise each lane copies its own elements at commit time.
+template <typename T, int R, int BT = kCK, int CW = kWave>
+struct Stager {
+    static constexpr int EPV = 16 / (int)sizeof(T);      // elements per 16-byte piece
+    static constexpr int PPR = CW / EPV;                  // pieces per row of CW channels
+    static constexpr int NP = R * BT * PPR / kWave;       // pieces per lane
+    static_assert((R * BT * PPR) % kWave == 0, "staging shape");
+    static constexpr int kElems = R * BT * CW;            // LDS elements of one block
+    uint4 reg[NP];
+
+    __device__ __forceinline__ void fetch(const T* const (&src)[R], int64_t tb, int64_t T_, int D, int g, int lane,
+                                          bool vec) {
+        if (!vec) return;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int q = p * kWave + lane;
+            const int row = q / PPR, j = q % PPR;
+            const int r = row / BT, k = row % BT;
+            const int64_t t = tb + k;
+            const int ch = g * CW + j * EPV;
+            // pieces outside the tensor stage zeros, so lanes past D only see finite inputs
+            reg[p] = (t < T_ && ch < D) ? *reinterpret_cast<const uint4*>(src[r] + (size_t)t * D + ch)
+                                        : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+
+    __device__ __forceinline__ void commit(T* lds, const T* const (&src)[R], int64_t tb, int64_t T_, int D, int g,
+                                           int lane, bool vec) {
+        if (vec) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const int q = p * kWave + lane;
+                const int row = q / PPR, j = q % PPR;
+                *reinterpret_cast<uint4*>(lds + row * CW + j * EPV) = reg[p];
+            }
+        } else if (lane < CW) {
+            const int d = g * CW + lane;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                for (int k = 0; k < BT; ++k) {
+                    const int64_t t = tb + k;
+                    lds[(r * BT + k) * CW + lane] = (t < T_ && d < D) ? src[r][(size_t)t * D + d] : T(0);
+                }
+        }
+    }
+
+    // element (r, k) of channel c (0 <= c < CW) of the committed block
+    static __device__ __forceinline__ float get(const T* lds, int r, int k, int c) {
+        return Elt<T>::ld(lds, (size_t)(r * BT + k) * CW + c);
+    }
+};
+
+// Tile of the flat grid over (chunk, group of CW channels), group fastest.
+template <int CW>
+__device__ __forceinline__ Tile tile_of_w(int D) {
+    const unsigned ng = (unsigned)((D + CW - 1) / CW);
+    return Tile{(int)(blockIdx.x % ng), (int64_t)(blockIdx.x / ng)};
+}
+
+template <typename T>
+inline bool stage_vec_ok(int D, std::initializer_list<const void*> ptrs) {
+    if (D % (16 / (int)sizeof(T)) != 0) return false;
+    for (const void* p : ptrs)
+        if (p && (reinterpret_cast<uintptr_t>(p) & 15u)) return false;
+    return true;
 }
 
 }  // namespace ssmp

@@ -8,27 +8,34 @@
 //   y_t = sum_n C_t[n] h_t[n] + Dskip[d] u_t,   out_t = y_t SiLU(z_t)
 //
 // Mapping: one lane per channel, the d_state values in VGPRs, one wave per
-// (chunk of kLC tokens, 64 channels); B_t and C_t are the same for the whole
-// wave and arrive through scalar loads. The time axis is joined across
-// chunks by the article's reset rule applied to the affine carry
-// (h_out = P h_in + S, with the multiplier P zeroed once a head has been
-// passed):
+// (chunk of kLC tokens, 64 channels). B_t and C_t are the same for the whole
+// wave: an fp32 copy made first arrives through scalar loads. Per-lane inputs
+// are staged through LDS in kCK-token blocks, the next block in flight while
+// the current one is computed. The time axis is joined across chunks by the
+// article's reset rule applied to the affine carry (h_out = P h_in + S, with
+// the multiplier P zeroed once a head is passed):
 //   1. summary: per chunk, from its last head (or its start) to its end,
 //      S = end state from zero and P = product of decays (0 if a head was
 //      seen). Skipped when the next chunk starts with a head.
 //   2. carry: per (n, d), a sequential pass over chunks gives the state
 //      entering each chunk.
 //   3. output: each chunk replays its tokens from that state, writes out and
-//      stores the state every kCK tokens for the backward.
+//      stores the state at every block start for the backward.
 #include "scan_common.h"
 
 namespace ssmp {
 
+constexpr int kFwdBlock = 8;  // tokens per staged block in the forward kernels
+static_assert(kCK % kFwdBlock == 0, "checkpoints fall on block starts");
+
 template <typename T, int NS>
 __global__ __launch_bounds__(64) void k_scan_fwd_summary(const T* __restrict__ u, const T* __restrict__ delta,
-                                                         const float* __restrict__ A, const T* __restrict__ B,
+                                                         const float* __restrict__ A, const float* __restrict__ bc,
                                                          const int32_t* __restrict__ pos, float* __restrict__ P,
-                                                         float* __restrict__ S, int64_t T_, int D) {
+                                                         float* __restrict__ S, int64_t T_, int D, int vec) {
+    constexpr int BT = kFwdBlock;
+    using St = Stager<T, 2, BT>;
+    __shared__ __attribute__((aligned(16))) T lds[St::kElems];
     const int lane = threadIdx.x;
     const Tile tl = tile_of(D);
     const int d = tl.g * kWave + lane;
@@ -59,17 +66,30 @@ __global__ __launch_bounds__(64) void k_scan_fwd_summary(const T* __restrict__ u
         h[n] = 0.0f;
         p[n] = 1.0f;
     }
-    for (int64_t t = ts; t < t1; ++t) {
-        const float dt = Elt<T>::ld(delta, (size_t)t * D + dd);
-        const float dtu = dt * Elt<T>::ld(u, (size_t)t * D + dd);
-        float Bv[NS];
-        load_row<NS>(B + (size_t)t * NS, Bv);
+    const T* const src[2] = {u, delta};
+    St st;
+    const int64_t tb0 = t0 + ((ts - t0) / BT) * BT;
+    st.fetch(src, tb0, T_, D, tl.g, lane, vec);
+    for (int64_t tb = tb0; tb < t1; tb += BT) {
+        st.commit(lds, src, tb, T_, D, tl.g, lane, vec);
+        wave_sync();
+        if (tb + BT < t1) st.fetch(src, tb + BT, T_, D, tl.g, lane, vec);
 #pragma unroll
-        for (int n = 0; n < NS; ++n) {
-            const float a = exp2_fast(dt * A2[n]);
-            h[n] = __builtin_fmaf(a, h[n], dtu * Bv[n]);
-            p[n] *= a;
+        for (int k = 0; k < BT; ++k) {
+            const int64_t t = tb + k;
+            if (t >= ts && t < t1) {
+                const float dt = St::get(lds, 1, k, lane);
+                const float dtu = dt * St::get(lds, 0, k, lane);
+                const float* __restrict__ row = bc + (size_t)t * 2 * NS;
+#pragma unroll
+                for (int n = 0; n < NS; ++n) {
+                    const float a = exp2_fast(dt * A2[n]);
+                    h[n] = __builtin_fmaf(a, h[n], dtu * row[n]);
+                    p[n] *= a;
+                }
+            }
         }
+        wave_sync();
     }
     if (act) {
 #pragma unroll
@@ -107,11 +127,13 @@ __global__ __launch_bounds__(256) void k_scan_fwd_carry(const float* __restrict_
 
 template <typename T, int NS>
 __global__ __launch_bounds__(64) void k_scan_fwd_out(const T* __restrict__ u, const T* __restrict__ delta,
-                                                     const float* __restrict__ A, const T* __restrict__ B,
-                                                     const T* __restrict__ C, const float* __restrict__ Dskip,
-                                                     const T* __restrict__ z, const int32_t* __restrict__ pos,
-                                                     T* __restrict__ out, float* __restrict__ ckpt, int64_t T_,
-                                                     int D) {
+                                                     const float* __restrict__ A, const float* __restrict__ bc,
+                                                     const float* __restrict__ Dskip, const T* __restrict__ z,
+                                                     const int32_t* __restrict__ pos, T* __restrict__ out,
+                                                     float* __restrict__ ckpt, int64_t T_, int D, int vec) {
+    constexpr int BT = kFwdBlock;
+    using St = Stager<T, 3, BT>;
+    __shared__ __attribute__((aligned(16))) T lds[St::kElems];
     const int lane = threadIdx.x;
     const Tile tl = tile_of(D);
     const int d = tl.g * kWave + lane;
@@ -121,50 +143,54 @@ __global__ __launch_bounds__(64) void k_scan_fwd_out(const T* __restrict__ u, co
     const int64_t t0 = c * kLC;
     const int64_t t1 = (t0 + kLC < T_) ? t0 + kLC : T_;
     const size_t ND = (size_t)NS * D;
+    const bool gate = z != nullptr;
+    const bool full = (tl.g + 1) * kWave <= D;  // every lane of the wave holds a channel
 
     float A2[NS], h[NS];
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
         A2[n] = A[(size_t)dd * NS + n] * kLog2e;
-        h[n] = ckpt[(size_t)(t0 / kCK) * ND + (size_t)n * D + dd];
+        h[n] = act ? ckpt[(size_t)(t0 / kCK) * ND + (size_t)n * D + dd] : 0.0f;
     }
-    const float Dv = Dskip ? Dskip[dd] : 0.0f;
-    const bool gate = z != nullptr;
-
-    for (int64_t tb = t0; tb < t1; tb += kCK) {
-        if (tb != t0 && act) {
+    const float Dv = (Dskip && act) ? Dskip[dd] : 0.0f;
+    const T* const src[3] = {u, delta, gate ? z : u};
+    St st;
+    st.fetch(src, t0, T_, D, tl.g, lane, vec);
+    for (int64_t tb = t0; tb < t1; tb += BT) {
+        if (tb != t0 && (tb % kCK) == 0 && act) {
 #pragma unroll
             for (int n = 0; n < NS; ++n) ckpt[(size_t)(tb / kCK) * ND + (size_t)n * D + d] = h[n];
         }
-        const int nt = (int)((tb + kCK < t1) ? kCK : t1 - tb);
-#pragma unroll 4
-        for (int k = 0; k < nt; ++k) {
+        const uint32_t heads = block_heads<BT>(pos, tb, T_, lane);
+        st.commit(lds, src, tb, T_, D, tl.g, lane, vec);
+        wave_sync();
+        if (tb + BT < t1) st.fetch(src, tb + BT, T_, D, tl.g, lane, vec);
+        T* __restrict__ orow = out + (size_t)tb * D + d;
+#pragma unroll
+        for (int k = 0; k < BT; ++k) {
             const int64_t t = tb + k;
-            const size_t e = (size_t)t * D + dd;
-            const float dt = Elt<T>::ld(delta, e);
-            const float uu = Elt<T>::ld(u, e);
-            const float dtu = dt * uu;
-            float Bv[NS], Cv[NS];
-            load_row<NS>(B + (size_t)t * NS, Bv);
-            load_row<NS>(C + (size_t)t * NS, Cv);
-            if (pos[t] == 0) {
+            if (t < t1) {
+                const float dt = St::get(lds, 1, k, lane);
+                const float uu = St::get(lds, 0, k, lane);
+                const float dtu = dt * uu;
+                const float* __restrict__ row = bc + (size_t)t * 2 * NS;
+                reset_if<NS>((heads >> k) & 1u, h);
+                float y = 0.0f;
 #pragma unroll
-                for (int n = 0; n < NS; ++n) h[n] = 0.0f;
+                for (int n = 0; n < NS; ++n) {
+                    const float a = exp2_fast(dt * A2[n]);
+                    h[n] = __builtin_fmaf(a, h[n], dtu * row[n]);
+                    y = __builtin_fmaf(row[NS + n], h[n], y);
+                }
+                y = __builtin_fmaf(Dv, uu, y);
+                if (gate) {
+                    const float zz = St::get(lds, 2, k, lane);
+                    y *= zz * sigmoid_fast(zz);
+                }
+                if (full || act) Elt<T>::st(orow, (size_t)k * D, y);
             }
-            float y = 0.0f;
-#pragma unroll
-            for (int n = 0; n < NS; ++n) {
-                const float a = exp2_fast(dt * A2[n]);
-                h[n] = __builtin_fmaf(a, h[n], dtu * Bv[n]);
-                y = __builtin_fmaf(Cv[n], h[n], y);
-            }
-            y = __builtin_fmaf(Dv, uu, y);
-            if (gate) {
-                const float zz = Elt<T>::ld(z, e);
-                y *= zz * sigmoid_fast(zz);
-            }
-            if (act) Elt<T>::st(out, (size_t)t * D + d, y);
         }
+        wave_sync();
     }
 }
 
@@ -174,17 +200,21 @@ static int scan_fwd_launch(const void* u, const void* delta, const float* A, con
                            int D, hipStream_t s) {
     const ScanWs L = scan_ws_layout(T_, D, NS);
     const dim3 grid((unsigned)(L.ngroup * L.nchunk));
+    const int vec = stage_vec_ok<T>(D, {u, delta, z}) ? 1 : 0;
+    k_bc_to_f32<T, NS><<<(unsigned)((T_ * 2 * NS + 255) / 256), 256, 0, s>>>((const T*)B, (const T*)C, ws + L.bc,
+                                                                            T_);
+    SSMP_LAUNCH_CHECK();
     if (L.nchunk > 1) {
-        k_scan_fwd_summary<T, NS><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, (const T*)B, pos,
-                                                         ws + L.P, ws + L.S, T_, D);
+        k_scan_fwd_summary<T, NS><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, ws + L.bc, pos, ws + L.P,
+                                                         ws + L.S, T_, D, vec);
         SSMP_LAUNCH_CHECK();
     }
     const int64_t ND = (int64_t)NS * D;
     k_scan_fwd_carry<NS><<<(unsigned)((ND + 255) / 256), 256, 0, s>>>(ws + L.P, ws + L.S, pos, ws + L.ckpt, T_, D,
                                                                       L.nchunk);
     SSMP_LAUNCH_CHECK();
-    k_scan_fwd_out<T, NS><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, (const T*)B, (const T*)C, Dskip,
-                                                 (const T*)z, pos, (T*)out, ws + L.ckpt, T_, D);
+    k_scan_fwd_out<T, NS><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, ws + L.bc, Dskip, (const T*)z, pos,
+                                                 (T*)out, ws + L.ckpt, T_, D, vec);
     SSMP_LAUNCH_CHECK();
     return SSMP_OK;
 }
