@@ -1,0 +1,81 @@
+"""GPU parity at the full workload sizes, through the same library calls the
+benchmark times (varlen_pack_indices -> conv1d_pack_fwd ->
+selective_scan_pack_fwd -> selective_scan_pack_bwd -> conv1d_pack_bwd).
+
+The oracle cannot redo the whole batch in seconds, so it checks samples it
+can compute exactly:
+  * every token of a spread of channels (first, last, and ones inside each
+    64-channel group boundary region): channels interact only through dB and
+    dC, so a channel-subset oracle run gives exact references for u, out,
+    dx, du, ddelta, dz and the per-channel sums dA, dD, dconv_w, dconv_b;
+  * dB and dC of sampled whole sequences, from the oracle run on those
+    sequences alone with every channel (packed == each sequence alone).
+Position indices are compared in full, bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests.gpu_harness import TOL_GRAD, TOL_OUT, Dev, assert_close, npy
+
+pytestmark = pytest.mark.gpu
+
+
+def sampled_channels(D):
+    ch = {0, 1, 31, 32, 63, 64, D // 2 - 1, D // 2, D - 65, D - 64, D - 2, D - 1}
+    rng = np.random.default_rng(D)
+    ch |= set(int(v) for v in rng.integers(0, D, 8))
+    return np.array(sorted(c for c in ch if 0 <= c < D))
+
+
+def pick_sequences(lengths, k=2):
+    """The shortest sequence and one of middling length."""
+    order = np.argsort(lengths, kind="stable")
+    return sorted({int(order[0]), int(order[len(order) // 2])})[:k]
+
+
+@pytest.mark.parametrize("workload", [4, 1, 3])
+def test_fullsize_sampled(orc, workload):
+    assert torch.cuda.is_available()
+    print(f"[fullsize] workload {workload} ({synth.NAMES[workload]})", flush=True)
+    inp = synth.make_inputs(workload, with_dout=True)
+    d = Dev(inp)
+    F = d.forward()
+    G = d.backward(F)
+    torch.cuda.synchronize()
+    dt = inp.dtype
+    to, tg = TOL_OUT[dt], TOL_GRAD[dt]
+
+    rpos, _ = orc.pack_indices(inp.cu_seqlens, inp.T)
+    assert np.array_equal(F["pos"].cpu().numpy(), rpos)
+
+    # every token of sampled channels
+    ch = sampled_channels(inp.D)
+    f = synth.f64
+    x, w, b = f(inp.x)[:, ch], f(inp.w)[ch], f(inp.b)[ch]
+    delta, A, Dp, z, dout = f(inp.delta)[:, ch], f(inp.A)[ch], f(inp.Dp)[ch], f(inp.z)[:, ch], f(inp.dout)[:, ch]
+    B, C = f(inp.B), f(inp.C)
+    Rf = orc.forward(x, w, b, delta, A, B, C, Dp, z, inp.cu_seqlens, threads=16)
+    Rb = orc.backward(x, w, b, delta, A, B, C, Dp, z, inp.cu_seqlens, dout, threads=16)
+    cht = torch.from_numpy(ch).cuda()
+    assert_close(npy(F["u"][:, cht]), Rf["u"], to, "u")
+    assert_close(npy(F["out"][:, cht]), Rf["out"], to, "out")
+    for k in ("dx", "du", "ddelta", "dz"):
+        assert_close(npy(G[k][:, cht]), Rb[k], tg, k)
+    for k in ("dA", "dw"):
+        assert_close(npy(G[k][cht]), Rb[k], tg, k)
+    for k in ("dD", "db"):
+        assert_close(npy(G[k][cht]), Rb[k], tg, k)
+
+    # dB, dC of sampled sequences, all channels
+    for s in pick_sequences(inp.lengths):
+        lo, hi = int(inp.cu_seqlens[s]), int(inp.cu_seqlens[s + 1])
+        one = np.array([0, hi - lo], dtype=np.int32)
+        sl = slice(lo, hi)
+        R = orc.backward(f(inp.x)[sl], f(inp.w), f(inp.b), f(inp.delta)[sl], f(inp.A), f(inp.B)[sl], f(inp.C)[sl],
+                         f(inp.Dp), f(inp.z)[sl], one, f(inp.dout)[sl], threads=16)
+        assert_close(npy(G["dB"][lo:hi]), R["dB"], tg, f"dB seq {s} (len {hi - lo})")
+        assert_close(npy(G["dC"][lo:hi]), R["dC"], tg, f"dC seq {s} (len {hi - lo})")
