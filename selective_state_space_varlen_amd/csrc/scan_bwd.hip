@@ -35,26 +35,69 @@ namespace ssmp {
 // ---------------------------------------------------------------------------
 // 1. reverse-carry summaries
 // ---------------------------------------------------------------------------
-template <typename T, int NS>
-__global__ __launch_bounds__(64) void k_scan_bwd_summary(const T* __restrict__ delta, const float* __restrict__ A,
+// One block of the reverse-carry summary: for tokens s from the chunk start,
+// sr += exp2(A2 * sum_{r<=s} delta_r) * g_s * C_s. The decay product is formed
+// from a compensated running sum of delta (exact in real arithmetic).
+// SAFE blocks stop at `nt`; fast blocks are full.
+template <bool SAFE, bool GATE, typename T, int NS, int BT, typename St>
+__device__ __forceinline__ void bsum_block(const T* lds, const float* __restrict__ bc, int64_t tb, int nt,
+                                           const float (&A2)[NS], float (&sr)[NS], float& sdt, float& cdt,
+                                           int lane) {
+    const float* __restrict__ rows = bc + (size_t)tb * 2 * NS + NS;  // C rows
+    float cur[NS];
+#pragma unroll
+    for (int n = 0; n < NS; ++n) cur[n] = rows[n];
+#pragma unroll
+    for (int k = 0; k < BT; ++k) {
+        if constexpr (SAFE) {
+            if (k >= nt) break;
+        }
+        float nxt[NS];
+        const bool more = SAFE ? (k + 1 < nt) : (k + 1 < BT);
+        if (more) {
+#pragma unroll
+            for (int n = 0; n < NS; ++n) nxt[n] = rows[(k + 1) * 2 * NS + n];
+        }
+        const float dt = St::get(lds, 0, k, lane);
+        float g = St::get(lds, 2, k, lane);
+        if constexpr (GATE) {
+            const float zz = St::get(lds, 1, k, lane);
+            g *= zz * sigmoid_fast(zz);
+        }
+        const float yk = dt - cdt;
+        const float tk = sdt + yk;
+        cdt = (tk - sdt) - yk;
+        sdt = tk;
+#pragma unroll
+        for (int n = 0; n < NS; ++n) sr[n] = __builtin_fmaf(exp2_fast(A2[n] * sdt), g * cur[n], sr[n]);
+        if (more) {
+#pragma unroll
+            for (int n = 0; n < NS; ++n) cur[n] = nxt[n];
+        }
+    }
+}
+
+template <typename T, int NS, bool GATE>
+__global__ __launch_bounds__(64, 4) void k_scan_bwd_summary(const T* __restrict__ delta, const float* __restrict__ A,
                                                          const float* __restrict__ bc, const T* __restrict__ z,
                                                          const T* __restrict__ dout, const int32_t* __restrict__ pos,
                                                          float* __restrict__ Pr, float* __restrict__ Sr, int64_t T_,
-                                                         int D, int vec) {
-    using St = Stager<T, 3>;
-    __shared__ __attribute__((aligned(16))) T lds[3 * kCK * kWave];
+                                                         int D, int vec, int lc) {
+    constexpr int BT = 8;
+    using St = Stager<T, 3, BT>;
+    __shared__ __attribute__((aligned(16))) T lds[St::kElems];
     const int lane = threadIdx.x;
     const Tile tl = tile_of(D);
     const int d = tl.g * kWave + lane;
     const bool act = d < D;
     const int dd = act ? d : D - 1;
     const int64_t c = tl.c;
-    const int64_t t0 = c * kLC;
-    const int64_t t1 = (t0 + kLC < T_) ? t0 + kLC : T_;
+    const int64_t t0 = c * lc;
+    const int64_t t1 = (t0 + lc < T_) ? t0 + lc : T_;
     if (c == 0) return;            // nothing to the left
     if (pos[t0] == 0) return;      // starts at a head: carries nothing out
 
-    // first head in (t0, t1)
+    // first head in (t0, t1): the summary covers [t0, fh)
     int64_t fh = t1;
     for (int64_t base = t0; base < t1; base += kWave) {
         const int64_t t = base + lane;
@@ -65,46 +108,32 @@ __global__ __launch_bounds__(64) void k_scan_bwd_summary(const T* __restrict__ d
             break;
         }
     }
-    const bool gate = z != nullptr;
-    float A2[NS], pf[NS], sr[NS];
+    float A2[NS], sr[NS];
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
         A2[n] = A[(size_t)dd * NS + n] * kLog2e;
-        pf[n] = 1.0f;
         sr[n] = 0.0f;
     }
-    const T* const src[3] = {delta, gate ? z : delta, dout};
+    float sdt = 0.0f, cdt = 0.0f;
+    const T* const src[3] = {delta, GATE ? z : delta, dout};
     St st;
     st.fetch(src, t0, T_, D, tl.g, lane, vec);
-    for (int64_t tb = t0; tb < fh; tb += kCK) {
+    for (int64_t tb = t0; tb < fh; tb += BT) {
+        wave_sync();
         st.commit(lds, src, tb, T_, D, tl.g, lane, vec);
         wave_sync();
-        if (tb + kCK < fh) st.fetch(src, tb + kCK, T_, D, tl.g, lane, vec);
-#pragma unroll
-        for (int k = 0; k < kCK; ++k) {
-            const int64_t t = tb + k;
-            if (t < fh) {
-                const float dt = St::get(lds, 0, k, lane);
-                float g = St::get(lds, 2, k, lane);
-                if (gate) {
-                    const float zz = St::get(lds, 1, k, lane);
-                    g *= zz * sigmoid_fast(zz);
-                }
-                const float* __restrict__ row = bc + (size_t)t * 2 * NS;
-#pragma unroll
-                for (int n = 0; n < NS; ++n) {
-                    pf[n] *= exp2_fast(dt * A2[n]);
-                    sr[n] = __builtin_fmaf(pf[n], g * row[NS + n], sr[n]);
-                }
-            }
-        }
-        wave_sync();
+        if (tb + BT < fh) st.fetch(src, tb + BT, T_, D, tl.g, lane, vec);
+        const int nt = (int)((tb + BT < fh) ? BT : fh - tb);
+        if (nt == BT)
+            bsum_block<false, GATE, T, NS, BT, St>(lds, bc, tb, BT, A2, sr, sdt, cdt, lane);
+        else
+            bsum_block<true, GATE, T, NS, BT, St>(lds, bc, tb, nt, A2, sr, sdt, cdt, lane);
     }
     if (act) {
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
             const size_t o = ((size_t)c * NS + n) * D + d;
-            Pr[o] = (fh < t1) ? 0.0f : pf[n];
+            Pr[o] = (fh < t1) ? 0.0f : exp2_fast(A2[n] * sdt);
             Sr[o] = sr[n];
         }
     }
@@ -116,7 +145,7 @@ __global__ __launch_bounds__(64) void k_scan_bwd_summary(const T* __restrict__ d
 template <int NS>
 __global__ __launch_bounds__(256) void k_scan_bwd_carry(const float* __restrict__ Pr, const float* __restrict__ Sr,
                                                         const int32_t* __restrict__ pos, float* __restrict__ cin,
-                                                        int D, int64_t nchunk) {
+                                                        int D, int64_t nchunk, int lc) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t ND = (int64_t)NS * D;
     if (i >= ND) return;
@@ -124,7 +153,7 @@ __global__ __launch_bounds__(256) void k_scan_bwd_carry(const float* __restrict_
     for (int64_t c = nchunk - 1; c >= 0; --c) {
         cin[(size_t)c * ND + i] = cc;
         if (c == 0) break;
-        if (pos[c * kLC] == 0) {
+        if (pos[c * lc] == 0) {
             cc = 0.0f;
         } else {
             const float Pc = Pr[(size_t)c * ND + i], Sc = Sr[(size_t)c * ND + i];
@@ -157,15 +186,153 @@ struct BwdArgs {
     int64_t T_;
     int D;
     int vec;
+    int lc;
 };
 
 constexpr int kRedStride = kWave + 4;  // LDS row stride (floats) of the dB/dC transpose
+
+// Replay of one kK-token sub-chunk from its entering state h: the states hh[k]
+// after each token and the pre-gate outputs yk[k]. SAFE sub-chunks may be
+// short (ns < kK) and may hold heads; the fast ones are full and head-free.
+template <bool SAFE, int NS, int LPC, typename St, typename T>
+__device__ __forceinline__ void bwd_replay(const T* lds, const float* bcl, int kb, int ns, uint32_t heads, int ch,
+                                           int n0, const float (&A2)[NS / LPC], float (&h)[NS / LPC],
+                                           float (&hh)[kK][NS / LPC], float (&yk)[kK], float Dv) {
+    // on return h holds the state after the last replayed token
+    constexpr int NH = NS / LPC;
+#pragma unroll
+    for (int kk = 0; kk < kK; ++kk) {
+        if constexpr (SAFE) {
+            if (kk >= ns) break;
+        }
+        const int k = kb + kk;
+        const float dt = St::get(lds, 1, k, ch);
+        const float uu = St::get(lds, 0, k, ch);
+        const float dtu = dt * uu;
+        const float* row = bcl + k * 2 * NS + n0;
+        if constexpr (SAFE) reset_if<NH>((heads >> k) & 1u, h);
+        float y = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NH; ++i) {
+            h[i] = __builtin_fmaf(exp2_fast(dt * A2[i]), h[i], dtu * row[i]);
+            hh[kk][i] = h[i];
+            y = __builtin_fmaf(row[NS + i], h[i], y);
+        }
+        if constexpr (LPC == 2) y += swap_adjacent(y);
+        yk[kk] = __builtin_fmaf(Dv, uu, y);
+    }
+}
+
+// Per-block output rows: du, ddelta, dz (dtype T) and the group's dB/dC partials.
+template <typename T>
+struct BwdRows {
+    T* du;
+    T* ddelta;
+    T* dz;
+    float* dbc;
+};
+
+// Reverse step over one sub-chunk (tokens kb + ns - 1 down to kb).
+template <bool SAFE, bool GATE, int NS, int LPC, typename St, typename T>
+__device__ __forceinline__ void bwd_reverse(const T* lds, const float* bcl, float (*red)[kRedStride], int kb, int ns,
+                                            uint32_t heads, int lane, int ch, int sh, int n0, bool act, bool full,
+                                            int D, int d, const float (&A2)[NS / LPC], float (&carry)[NS / LPC],
+                                            float (&dA)[NS / LPC], float& dDacc, float Dv,
+                                            const float (&hin)[NS / LPC], const float (&hh)[kK][NS / LPC],
+                                            const float (&yk)[kK], const BwdRows<T>& rows) {
+    constexpr int NH = NS / LPC;
+    constexpr int CW = kWave / LPC;
+#pragma unroll
+    for (int kk = kK - 1; kk >= 0; --kk) {
+        if constexpr (SAFE) {
+            if (kk >= ns) continue;
+        }
+        const int k = kb + kk;
+        const float dt = St::get(lds, 1, k, ch);
+        const float uu = St::get(lds, 0, k, ch);
+        const float go = St::get(lds, 3, k, ch);
+        float gg = go, dzv = 0.0f;
+        if constexpr (GATE) {
+            const float zz = St::get(lds, 2, k, ch);
+            const float sg = sigmoid_fast(zz);
+            gg = go * zz * sg;
+            dzv = go * yk[kk] * sg * (1.0f + zz * (1.0f - sg));
+        }
+        gg = act ? gg : 0.0f;  // lanes past D add nothing to dB/dC
+        const float dtu = act ? dt * uu : 0.0f;
+        const float* row = bcl + k * 2 * NS + n0;
+        const int col = sh * CW + ch;
+        float sumB = 0.0f, sumAr = 0.0f;
+        const bool head = SAFE && ((heads >> k) & 1u);
+        if (head) {
+            asm volatile("");
+#pragma unroll
+            for (int i = 0; i < NH; ++i) {
+                const float dh = __builtin_fmaf(gg, row[NS + i], carry[i]);
+                red[i][col] = dh * dtu;             // dB row
+                red[NH + i][col] = gg * hh[kk][i];  // dC row
+                sumB = __builtin_fmaf(dh, row[i], sumB);
+                carry[i] = 0.0f;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NH; ++i) {
+                const float dh = __builtin_fmaf(gg, row[NS + i], carry[i]);
+                red[i][col] = dh * dtu;
+                red[NH + i][col] = gg * hh[kk][i];
+                sumB = __builtin_fmaf(dh, row[i], sumB);
+                // carry to t-1: a_t dh_t; r = dh_t a_t h_{t-1}
+                carry[i] = exp2_fast(dt * A2[i]) * dh;
+                const float r = carry[i] * (kk == 0 ? hin[i] : hh[kk > 0 ? kk - 1 : 0][i]);
+                sumAr = __builtin_fmaf(r, A2[i], sumAr);
+                dA[i] = __builtin_fmaf(r, dt, dA[i]);
+            }
+        }
+        if constexpr (LPC == 2) {
+            sumB += swap_adjacent(sumB);
+            sumAr += swap_adjacent(sumAr);
+        }
+        const float duv = __builtin_fmaf(gg, Dv, dt * sumB);
+        const float ddv = __builtin_fmaf(uu, sumB, sumAr * kLn2);
+        dDacc = __builtin_fmaf(gg, uu, dDacc);
+        // both lanes of a pair hold the same values and store the same bytes
+        const uint32_t e = (uint32_t)(k * D + d);  // < kCK * D, fits 32 bits
+        if (full || act) {
+            Elt<T>::st(rows.du, e, duv);
+            Elt<T>::st(rows.ddelta, e, ddv);
+            if constexpr (GATE) Elt<T>::st(rows.dz, e, dzv);
+        }
+        // dB/dC of state n: the sum of row (n % NH) (dB) or NH + n % NH (dC)
+        // over the columns of share n / NH. Two lanes per output value, each
+        // adding half the columns; both then hold the total.
+        wave_sync();
+        const int o = lane >> 1, hf = lane & 1;  // output o: kind o / NS, state o % NS
+        constexpr bool all_out = 4 * NS >= kWave;
+        float v = 0.0f;
+        if (all_out || o < 2 * NS) {
+            const int kind = o / NS, n = o % NS;
+            const int rrow = kind * NH + (n % NH);
+            const int c0 = (n / NH) * CW + hf * (CW / 2);
+            const float4* rw = reinterpret_cast<const float4*>(&red[rrow][c0]);
+            float4 r4 = rw[0];
+            v = (r4.x + r4.y) + (r4.z + r4.w);
+#pragma unroll
+            for (int q = 1; q < CW / 8; ++q) {
+                r4 = rw[q];
+                v += (r4.x + r4.y) + (r4.z + r4.w);
+            }
+        }
+        v += swap_adjacent(v);
+        if (all_out || o < 2 * NS) rows.dbc[(uint32_t)(k * 2 * NS + o)] = v;
+        wave_sync();
+    }
+}
 
 // LPC lanes share a channel, each holding NS/LPC of its states, so a wave
 // covers 64/LPC channels. Two lanes per channel halve the registers and LDS a
 // wave needs, which lets two or more waves share a SIMD; per-channel sums over
 // the states are completed with one DPP exchange between the lane pair.
-template <typename T, int NS, int LPC>
+template <typename T, int NS, int LPC, bool GATE>
 __global__ __launch_bounds__(64) void k_scan_bwd_main(BwdArgs<T> p) {
     constexpr int NH = NS / LPC;      // states per lane
     constexpr int CW = kWave / LPC;   // channels per wave
@@ -187,24 +354,23 @@ __global__ __launch_bounds__(64) void k_scan_bwd_main(BwdArgs<T> p) {
     const bool full = (g + 1) * CW <= p.D;
     const int dd = act ? d : p.D - 1;
     const int64_t c = tl.c;
-    const int64_t t0 = c * kLC;
-    const int64_t t1 = (t0 + kLC < p.T_) ? t0 + kLC : p.T_;
+    const int64_t t0 = c * p.lc;
+    const int64_t t1 = (t0 + p.lc < p.T_) ? t0 + p.lc : p.T_;
     const size_t ND = (size_t)NS * p.D;
-    const bool gate = p.z != nullptr;
     const int n0 = sh * NH;           // first state of this lane
-    const bool writer = sh == 0 && (full || act);
+    const int D = p.D;
 
     // lanes past D carry zeros throughout, so they add nothing to dB/dC
     float A2[NH], carry[NH], dA[NH];
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
         A2[i] = p.A[(size_t)dd * NS + n0 + i] * kLog2e;
-        carry[i] = act ? p.cin[(size_t)c * ND + (size_t)(n0 + i) * p.D + dd] : 0.0f;
+        carry[i] = act ? p.cin[(size_t)c * ND + (size_t)(n0 + i) * D + dd] : 0.0f;
         dA[i] = 0.0f;
     }
     const float Dv = (p.Dskip && act) ? p.Dskip[dd] : 0.0f;
     float dDacc = 0.0f;
-    const T* const src[4] = {p.u, p.delta, gate ? p.z : p.u, p.dout};
+    const T* const src[4] = {p.u, p.delta, GATE ? p.z : p.u, p.dout};
 
     // B/C rows of a block: kCK * 2NS floats, fetched with the block's inputs
     constexpr int BCV = kCK * 2 * NS / 4;                 // float4 pieces
@@ -212,18 +378,23 @@ __global__ __launch_bounds__(64) void k_scan_bwd_main(BwdArgs<T> p) {
     float4 bcr[BCP];
     auto fetch_bc = [&](int64_t tb) {
         const float4* srcv = reinterpret_cast<const float4*>(p.bc + (size_t)tb * 2 * NS);
-        const int64_t lim = ((p.T_ - tb < kCK) ? (p.T_ - tb) : kCK) * 2 * NS / 4;
+        if (tb + kCK <= p.T_ && BCV % kWave == 0) {
 #pragma unroll
-        for (int q = 0; q < BCP; ++q) {
-            const int idx = q * kWave + lane;
-            bcr[q] = (idx < BCV && idx < lim) ? srcv[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int q = 0; q < BCP; ++q) bcr[q] = srcv[q * kWave + lane];
+        } else {
+            const int64_t lim = ((p.T_ - tb < kCK) ? (p.T_ - tb) : kCK) * 2 * NS / 4;
+#pragma unroll
+            for (int q = 0; q < BCP; ++q) {
+                const int idx = q * kWave + lane;
+                bcr[q] = (idx < BCV && idx < lim) ? srcv[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
     };
     auto commit_bc = [&]() {
 #pragma unroll
         for (int q = 0; q < BCP; ++q) {
             const int idx = q * kWave + lane;
-            if (idx < BCV) reinterpret_cast<float4*>(bcl)[idx] = bcr[q];
+            if (BCV % kWave == 0 || idx < BCV) reinterpret_cast<float4*>(bcl)[idx] = bcr[q];
         }
     };
 
@@ -231,7 +402,7 @@ __global__ __launch_bounds__(64) void k_scan_bwd_main(BwdArgs<T> p) {
     St st;
     {
         const int64_t tl0 = t0 + (nblk - 1) * kCK;
-        st.fetch(src, tl0, p.T_, p.D, g, lane, p.vec);
+        st.fetch(src, tl0, p.T_, D, g, lane, p.vec);
         fetch_bc(tl0);
     }
     for (int64_t jb = nblk - 1; jb >= 0; --jb) {
@@ -241,30 +412,28 @@ __global__ __launch_bounds__(64) void k_scan_bwd_main(BwdArgs<T> p) {
         const float* hb = p.ckpt + (size_t)(tb0 / kCK) * ND;
         const uint32_t heads = block_heads<kCK>(p.pos, tb0, p.T_, lane);
         wave_sync();
-        st.commit(lds, src, tb0, p.T_, p.D, g, lane, p.vec);
+        st.commit(lds, src, tb0, p.T_, D, g, lane, p.vec);
         commit_bc();
         wave_sync();
         if (jb > 0) {
-            st.fetch(src, tb0 - kCK, p.T_, p.D, g, lane, p.vec);
+            st.fetch(src, tb0 - kCK, p.T_, D, g, lane, p.vec);
             fetch_bc(tb0 - kCK);
         }
+        const BwdRows<T> rows{p.du + (size_t)tb0 * D, p.ddelta + (size_t)tb0 * D,
+                              GATE ? p.dz + (size_t)tb0 * D : nullptr,
+                              p.dBC + ((size_t)g * p.T_ + tb0) * (2 * NS)};
 
-        // states entering sub-chunks 1..nsub-1
+        // states entering sub-chunks 1..nsub-1 (those sub-chunks are all full)
         if (nsub > 1) {
             float h[NH];
 #pragma unroll
-            for (int i = 0; i < NH; ++i) h[i] = act ? hb[(size_t)(n0 + i) * p.D + dd] : 0.0f;
+            for (int i = 0; i < NH; ++i) h[i] = act ? hb[(size_t)(n0 + i) * D + dd] : 0.0f;
             for (int sc = 1; sc < nsub; ++sc) {
-#pragma unroll
-                for (int kk = 0; kk < kK; ++kk) {
-                    const int k = (sc - 1) * kK + kk;
-                    const float dt = St::get(lds, 1, k, ch);
-                    const float dtu = dt * St::get(lds, 0, k, ch);
-                    const float* row = bcl + k * 2 * NS + n0;
-                    reset_if<NH>((heads >> k) & 1u, h);
-#pragma unroll
-                    for (int i = 0; i < NH; ++i) h[i] = __builtin_fmaf(exp2_fast(dt * A2[i]), h[i], dtu * row[i]);
-                }
+                float hh[kK][NH], yk[kK];
+                if (heads == 0)
+                    bwd_replay<false, NS, LPC, St>(lds, bcl, (sc - 1) * kK, kK, 0u, ch, n0, A2, h, hh, yk, Dv);
+                else
+                    bwd_replay<true, NS, LPC, St>(lds, bcl, (sc - 1) * kK, kK, heads, ch, n0, A2, h, hh, yk, Dv);
 #pragma unroll
                 for (int i = 0; i < NH; ++i) sub[sc - 1][i][lane] = h[i];
             }
@@ -273,125 +442,32 @@ __global__ __launch_bounds__(64) void k_scan_bwd_main(BwdArgs<T> p) {
         for (int sc = nsub - 1; sc >= 0; --sc) {
             const int kb = sc * kK;  // first token of the sub-chunk within the block
             const int ns = (nb - kb < kK) ? nb - kb : kK;
-            // replay: the states hh[k] after each of the sub-chunk's tokens
-            float hh[kK][NH], yk[kK];
-            {
-                float h[NH];
-                if (sc == 0) {
+            float h[NH], hin[NH], hh[kK][NH], yk[kK];
+            if (sc == 0) {
 #pragma unroll
-                    for (int i = 0; i < NH; ++i) h[i] = act ? hb[(size_t)(n0 + i) * p.D + dd] : 0.0f;
-                } else {
+                for (int i = 0; i < NH; ++i) h[i] = act ? hb[(size_t)(n0 + i) * D + dd] : 0.0f;
+            } else {
 #pragma unroll
-                    for (int i = 0; i < NH; ++i) h[i] = sub[sc - 1][i][lane];
-                }
-#pragma unroll
-                for (int kk = 0; kk < kK; ++kk) {
-                    if (kk < ns) {
-                        const int k = kb + kk;
-                        const float dt = St::get(lds, 1, k, ch);
-                        const float uu = St::get(lds, 0, k, ch);
-                        const float dtu = dt * uu;
-                        const float* row = bcl + k * 2 * NS + n0;
-                        reset_if<NH>((heads >> k) & 1u, h);
-                        float y = 0.0f;
-#pragma unroll
-                        for (int i = 0; i < NH; ++i) {
-                            h[i] = __builtin_fmaf(exp2_fast(dt * A2[i]), h[i], dtu * row[i]);
-                            hh[kk][i] = h[i];
-                            y = __builtin_fmaf(row[NS + i], h[i], y);
-                        }
-                        if constexpr (LPC == 2) y += swap_adjacent(y);
-                        yk[kk] = __builtin_fmaf(Dv, uu, y);
-                    }
-                }
+                for (int i = 0; i < NH; ++i) h[i] = sub[sc - 1][i][lane];
             }
-            // reverse over the sub-chunk
 #pragma unroll
-            for (int kk = kK - 1; kk >= 0; --kk) {
-                if (kk < ns) {
-                    const int k = kb + kk;
-                    const int64_t t = tb0 + k;
-                    const float dt = St::get(lds, 1, k, ch);
-                    const float uu = St::get(lds, 0, k, ch);
-                    const float go = St::get(lds, 3, k, ch);
-                    float gg = go, dzv = 0.0f;
-                    if (gate) {
-                        const float zz = St::get(lds, 2, k, ch);
-                        const float sg = sigmoid_fast(zz);
-                        gg = go * zz * sg;
-                        dzv = go * yk[kk] * sg * (1.0f + zz * (1.0f - sg));
-                    }
-                    gg = act ? gg : 0.0f;
-                    const float dtu = act ? dt * uu : 0.0f;
-                    const float* row = bcl + k * 2 * NS + n0;
-                    const int col = sh * CW + ch;
-                    float sumB = 0.0f, sumAr = 0.0f;
-                    if ((heads >> k) & 1u) {
-                        asm volatile("");
-#pragma unroll
-                        for (int i = 0; i < NH; ++i) {
-                            const float dh = __builtin_fmaf(gg, row[NS + i], carry[i]);
-                            red[i][col] = dh * dtu;             // dB row
-                            red[NH + i][col] = gg * hh[kk][i];  // dC row
-                            sumB = __builtin_fmaf(dh, row[i], sumB);
-                            carry[i] = 0.0f;
-                        }
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < NH; ++i) {
-                            const float dh = __builtin_fmaf(gg, row[NS + i], carry[i]);
-                            const float db = dh * dtu;
-                            red[i][col] = db;
-                            red[NH + i][col] = gg * hh[kk][i];
-                            sumB = __builtin_fmaf(dh, row[i], sumB);
-                            // r = dh a h_{t-1} = dh (h_t - dtu B_n)
-                            const float r = __builtin_fmaf(-db, row[i], dh * hh[kk][i]);
-                            sumAr = __builtin_fmaf(r, A2[i], sumAr);
-                            dA[i] = __builtin_fmaf(r, dt, dA[i]);
-                            carry[i] = exp2_fast(dt * A2[i]) * dh;
-                        }
-                    }
-                    if constexpr (LPC == 2) {
-                        sumB += swap_adjacent(sumB);
-                        sumAr += swap_adjacent(sumAr);
-                    }
-                    const float duv = __builtin_fmaf(gg, Dv, dt * sumB);
-                    const float ddv = __builtin_fmaf(uu, sumB, sumAr * kLn2);
-                    dDacc = __builtin_fmaf(gg, uu, dDacc);
-                    if (writer) {
-                        const size_t e = (size_t)t * p.D + d;
-                        Elt<T>::st(p.du, e, duv);
-                        Elt<T>::st(p.ddelta, e, ddv);
-                        if (gate) Elt<T>::st(p.dz, e, dzv);
-                    }
-                    // dB/dC of state n = sh'*NH + i: the sum of row i (dB) or
-                    // NH + i (dC) over columns sh'*CW .. sh'*CW + CW - 1. Two
-                    // lanes per output value, each adding half the columns.
-                    wave_sync();
-                    const int o = lane >> 1, hf = lane & 1;  // output o: kind o / NS, state o % NS
-                    float v = 0.0f;
-                    if (o < 2 * NS) {
-                        const int kind = o / NS, n = o % NS;
-                        const int rrow = kind * NH + (n % NH);
-                        const int c0 = (n / NH) * CW + hf * (CW / 2);
-                        const float4* rw = reinterpret_cast<const float4*>(&red[rrow][c0]);
-#pragma unroll
-                        for (int q = 0; q < CW / 8; ++q) {
-                            const float4 r4 = rw[q];
-                            v += (r4.x + r4.y) + (r4.z + r4.w);
-                        }
-                    }
-                    v += swap_adjacent(v);
-                    if (hf == 0 && o < 2 * NS) p.dBC[((size_t)g * p.T_ + t) * (2 * NS) + o] = v;
-                    wave_sync();
-                }
+            for (int i = 0; i < NH; ++i) hin[i] = h[i];
+            const uint32_t sub_heads = (heads >> kb) & ((1u << kK) - 1u);
+            if (sub_heads == 0 && ns == kK) {
+                bwd_replay<false, NS, LPC, St>(lds, bcl, kb, kK, 0u, ch, n0, A2, h, hh, yk, Dv);
+                bwd_reverse<false, GATE, NS, LPC, St>(lds, bcl, red, kb, kK, 0u, lane, ch, sh, n0, act, full, D, d,
+                                                      A2, carry, dA, dDacc, Dv, hin, hh, yk, rows);
+            } else {
+                bwd_replay<true, NS, LPC, St>(lds, bcl, kb, ns, heads, ch, n0, A2, h, hh, yk, Dv);
+                bwd_reverse<true, GATE, NS, LPC, St>(lds, bcl, red, kb, ns, heads, lane, ch, sh, n0, act, full, D, d,
+                                                     A2, carry, dA, dDacc, Dv, hin, hh, yk, rows);
             }
         }
     }
     if (act) {
 #pragma unroll
-        for (int i = 0; i < NH; ++i) p.dApart[(size_t)c * ND + (size_t)(n0 + i) * p.D + d] = dA[i];
-        if (sh == 0) p.dDpart[(size_t)c * p.D + d] = dDacc;
+        for (int i = 0; i < NH; ++i) p.dApart[(size_t)c * ND + (size_t)(n0 + i) * D + d] = dA[i];
+        if (sh == 0) p.dDpart[(size_t)c * D + d] = dDacc;
     }
 }
 
@@ -438,32 +514,43 @@ static int scan_bwd_launch(const void* u, const void* delta, const float* A, con
                            void* du, void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, int64_t T_,
                            int D, hipStream_t s) {
     const ScanWs L = scan_ws_layout(T_, D, NS);
-    const dim3 grid((unsigned)(L.ngroup * L.nchunk));
+    const int lc = bwd_chunk_len(T_, D, NS);
+    const int64_t nchunk = (T_ + lc - 1) / lc;
+    const dim3 grid((unsigned)(L.ngroup * nchunk));  // summary kernel: 64 channels per wave
     const int64_t ND = (int64_t)NS * D;
     const int vec = stage_vec_ok<T>(D, {u, delta, z, dout}) ? 1 : 0;
     k_bc_to_f32<T, NS><<<(unsigned)((T_ * 2 * NS + 255) / 256), 256, 0, s>>>((const T*)B, (const T*)C, ws + L.bc,
                                                                             T_);
     SSMP_LAUNCH_CHECK();
-    if (L.nchunk > 1) {
-        k_scan_bwd_summary<T, NS><<<grid, kWave, 0, s>>>((const T*)delta, A, ws + L.bc, (const T*)z, (const T*)dout,
-                                                         pos, ws + L.Pr, ws + L.Sr, T_, D, vec);
+    if (nchunk > 1) {
+        if (z)
+            k_scan_bwd_summary<T, NS, true><<<grid, kWave, 0, s>>>((const T*)delta, A, ws + L.bc, (const T*)z,
+                                                                   (const T*)dout, pos, ws + L.Pr, ws + L.Sr, T_, D,
+                                                                   vec, lc);
+        else
+            k_scan_bwd_summary<T, NS, false><<<grid, kWave, 0, s>>>((const T*)delta, A, ws + L.bc, nullptr,
+                                                                    (const T*)dout, pos, ws + L.Pr, ws + L.Sr, T_, D,
+                                                                    vec, lc);
         SSMP_LAUNCH_CHECK();
     }
     k_scan_bwd_carry<NS><<<(unsigned)((ND + 255) / 256), 256, 0, s>>>(ws + L.Pr, ws + L.Sr, pos, ws + L.cin, D,
-                                                                      L.nchunk);
+                                                                      nchunk, lc);
     SSMP_LAUNCH_CHECK();
     BwdArgs<T> a;
     a.u = (const T*)u; a.delta = (const T*)delta; a.A = A; a.bc = ws + L.bc; a.Dskip = Dskip;
     a.z = (const T*)z; a.dout = (const T*)dout; a.pos = pos; a.ckpt = ws + L.ckpt; a.cin = ws + L.cin;
     a.du = (T*)du; a.ddelta = (T*)ddelta; a.dz = (T*)dz; a.dApart = ws + L.dApart; a.dDpart = ws + L.dDpart;
-    a.dBC = ws + L.dBC; a.T_ = T_; a.D = D; a.vec = vec;
-    constexpr int LPC = NS >= 4 ? 2 : 1;
+    a.dBC = ws + L.dBC; a.T_ = T_; a.D = D; a.vec = vec; a.lc = lc;
+    constexpr int LPC = NS >= 4 ? 2 : 1;  // bwd_lanes_per_channel
     const int64_t ngroup = (D + kWave / LPC - 1) / (kWave / LPC);
-    k_scan_bwd_main<T, NS, LPC><<<(unsigned)(ngroup * L.nchunk), kWave, 0, s>>>(a);
+    if (z)
+        k_scan_bwd_main<T, NS, LPC, true><<<(unsigned)(ngroup * nchunk), kWave, 0, s>>>(a);
+    else
+        k_scan_bwd_main<T, NS, LPC, false><<<(unsigned)(ngroup * nchunk), kWave, 0, s>>>(a);
     SSMP_LAUNCH_CHECK();
     const int64_t nrp = ND > D ? ND : D;
     k_scan_bwd_reduce_params<NS><<<(unsigned)((nrp + 255) / 256), 256, 0, s>>>(ws + L.dApart, ws + L.dDpart,
-                                                                               L.nchunk, D, dA, dD);
+                                                                               nchunk, D, dA, dD);
     SSMP_LAUNCH_CHECK();
     k_scan_bwd_reduce_bc<NS><<<(unsigned)((T_ * 2 * NS + 255) / 256), 256, 0, s>>>(ws + L.dBC, ngroup, T_, dB, dC);
     SSMP_LAUNCH_CHECK();

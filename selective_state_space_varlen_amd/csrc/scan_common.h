@@ -6,20 +6,36 @@
 
 namespace ssmp {
 
-// Time tiling. A chunk of kLC tokens is the unit of time parallelism: one
-// wave walks it serially for 64 channels, and chunks are joined by the affine
-// carry h_out = P h_in + S (P = 0 once the chunk holds a head). Tokens are
-// staged in blocks of kCK; the forward stores the state at every block start
-// and the backward restarts from those, replaying kK-token sub-chunks whose
-// states stay in registers.
-constexpr int kLC = 256;
+// Time tiling. A chunk of lc tokens is the unit of time parallelism: one wave
+// walks it serially for a group of channels, and chunks are joined by the
+// affine carry h_out = P h_in + S (P = 0 once the chunk holds a head). Every
+// chunk whose successor continues a sequence costs a summary pass, so chunks
+// are as long as the grid allows: the longest power of two (64 .. 2048 tokens)
+// that still gives kMinWaves waves. Tokens are staged in blocks of kCK; the
+// forward stores the state at every block start and the backward restarts
+// from those, replaying kK-token sub-chunks whose states stay in registers.
 constexpr int kCK = 16;
 constexpr int kK = 4;
-static_assert(kLC % kCK == 0 && kCK % kK == 0, "tiling");
+constexpr int kLCMin = 64, kLCMax = 2048;
+constexpr int64_t kMinWaves = 8192;  // eight per SIMD on 256 CUs: enough to hide load latency
+static_assert(kLCMin % kCK == 0 && kCK % kK == 0, "tiling");
+
+// channels per wave: the forward gives each channel one lane; the backward
+// two lanes (d_state >= 4) or one
+inline int bwd_lanes_per_channel(int N) { return N >= 4 ? 2 : 1; }
+
+inline int scan_chunk_len(int64_t T, int D, int chw) {
+    const int64_t ng = (D + chw - 1) / chw;
+    int lc = kLCMax;
+    while (lc > kLCMin && ng * ((T + lc - 1) / lc) < kMinWaves) lc >>= 1;
+    return lc;
+}
+inline int fwd_chunk_len(int64_t T, int D) { return scan_chunk_len(T, D, kWave); }
+inline int bwd_chunk_len(int64_t T, int D, int N) { return scan_chunk_len(T, D, kWave / bwd_lanes_per_channel(N)); }
 
 struct ScanWs {
     int64_t nck;      // checkpoint slots: slot j holds the state entering token j*kCK
-    int64_t nchunk;   // chunks of kLC tokens
+    int64_t nchunk;   // chunks (the larger count of the forward's and the backward's chunking)
     int64_t ngroup;   // channel groups of 64
     // offsets in floats from the workspace base
     size_t ckpt;      // [nck][N][D]      forward -> backward
@@ -36,7 +52,11 @@ struct ScanWs {
 inline ScanWs scan_ws_layout(int64_t T, int D, int N) {
     ScanWs w{};
     w.nck = (T + kCK - 1) / kCK;
-    w.nchunk = (T + kLC - 1) / kLC;
+    {
+        const int64_t lf = fwd_chunk_len(T, D), lb = bwd_chunk_len(T, D, N);
+        const int64_t nf = (T + lf - 1) / lf, nb = (T + lb - 1) / lb;
+        w.nchunk = nf > nb ? nf : nb;
+    }
     w.ngroup = (D + kWave - 1) / kWave;
     const size_t ND = (size_t)N * D;
     auto up = [](size_t v) { return (v + 63) & ~size_t(63); };  // 256-byte aligned regions
@@ -70,7 +90,7 @@ __device__ __forceinline__ Tile tile_of(int D) {
 inline int scan_check_args(int64_t T, int D, int N, int dtype) {
     if (T < 0 || D < 1) return SSMP_ERR_SHAPE;
     if (T >= (int64_t(1) << 31)) return SSMP_ERR_SHAPE;
-    if (((T + kLC - 1) / kLC) * ((D + kWave - 1) / kWave) >= (int64_t(1) << 31)) return SSMP_ERR_SHAPE;
+    if (((T + kLCMin - 1) / kLCMin) * ((D + 31) / 32) >= (int64_t(1) << 31)) return SSMP_ERR_SHAPE;
     if ((T * (int64_t)D) >= (int64_t(1) << 40)) return SSMP_ERR_SHAPE;
     if (!(N == 1 || N == 2 || N == 4 || N == 8 || N == 16)) return SSMP_ERR_UNSUPPORTED;
     if (dtype != SSMP_F32 && dtype != SSMP_BF16) return SSMP_ERR_UNSUPPORTED;
@@ -137,6 +157,17 @@ struct Stager {
     __device__ __forceinline__ void fetch(const T* const (&src)[R], int64_t tb, int64_t T_, int D, int g, int lane,
                                           bool vec) {
         if (!vec) return;
+        if (tb + BT <= T_ && (g + 1) * CW <= D) {
+            // whole block inside the tensor: no per-piece bounds
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const int q = p * kWave + lane;
+                const int row = q / PPR, j = q % PPR;
+                const int r = row / BT, k = row % BT;
+                reg[p] = *reinterpret_cast<const uint4*>(src[r] + (size_t)(tb + k) * D + g * CW + j * EPV);
+            }
+            return;
+        }
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int q = p * kWave + lane;

@@ -8,7 +8,7 @@
 //   y_t = sum_n C_t[n] h_t[n] + Dskip[d] u_t,   out_t = y_t SiLU(z_t)
 //
 // Mapping: one lane per channel, the d_state values in VGPRs, one wave per
-// (chunk of kLC tokens, 64 channels). B_t and C_t are the same for the whole
+// (chunk of lc tokens, 64 channels). B_t and C_t are the same for the whole
 // wave: an fp32 copy made first arrives through scalar loads. Per-lane inputs
 // are staged through LDS in kCK-token blocks, the next block in flight while
 // the current one is computed. The time axis is joined across chunks by the
@@ -28,11 +28,53 @@ namespace ssmp {
 constexpr int kFwdBlock = 8;  // tokens per staged block in the forward kernels
 static_assert(kCK % kFwdBlock == 0, "checkpoints fall on block starts");
 
+// B (and C) rows of BT tokens from the fp32 copy, prefetched one token ahead
+// so the scalar loads of token k+1 overlap the arithmetic of token k.
+template <int NROW>
+__device__ __forceinline__ void load_rowv(const float* __restrict__ p, float (&v)[NROW]) {
+#pragma unroll
+    for (int j = 0; j < NROW; ++j) v[j] = p[j];
+}
+
+// Summary recurrence over one block: h = a h + dtu B from zero state. SAFE
+// blocks skip tokens before `first` or past `nt`; fast blocks hold neither.
+template <bool SAFE, typename T, int NS, int BT, typename St>
+__device__ __forceinline__ void summary_block(const T* lds, const float* __restrict__ bc, int64_t tb, int first,
+                                              int nt, const float (&A2)[NS], float (&h)[NS], float& sdt, float& cdt,
+                                              int lane) {
+    const float* __restrict__ rows = bc + (size_t)tb * 2 * NS;
+    float cur[NS];
+    load_rowv<NS>(rows + (SAFE ? first : 0) * 2 * NS, cur);
+#pragma unroll
+    for (int k = 0; k < BT; ++k) {
+        if constexpr (SAFE) {
+            if (k < first) continue;
+            if (k >= nt) break;
+        }
+        float nxt[NS];
+        const bool more = SAFE ? (k + 1 < nt) : (k + 1 < BT);
+        if (more) load_rowv<NS>(rows + (k + 1) * 2 * NS, nxt);
+        const float dt = St::get(lds, 1, k, lane);
+        const float dtu = dt * St::get(lds, 0, k, lane);
+        // compensated sum of delta: the chunk's decay is exp2(A2 * sum delta)
+        const float yk = dt - cdt;
+        const float tk = sdt + yk;
+        cdt = (tk - sdt) - yk;
+        sdt = tk;
+#pragma unroll
+        for (int n = 0; n < NS; ++n) h[n] = __builtin_fmaf(exp2_fast(dt * A2[n]), h[n], dtu * cur[n]);
+        if (more) {
+#pragma unroll
+            for (int n = 0; n < NS; ++n) cur[n] = nxt[n];
+        }
+    }
+}
+
 template <typename T, int NS>
-__global__ __launch_bounds__(64) void k_scan_fwd_summary(const T* __restrict__ u, const T* __restrict__ delta,
+__global__ __launch_bounds__(64, 4) void k_scan_fwd_summary(const T* __restrict__ u, const T* __restrict__ delta,
                                                          const float* __restrict__ A, const float* __restrict__ bc,
                                                          const int32_t* __restrict__ pos, float* __restrict__ P,
-                                                         float* __restrict__ S, int64_t T_, int D, int vec) {
+                                                         float* __restrict__ S, int64_t T_, int D, int vec, int lc) {
     constexpr int BT = kFwdBlock;
     using St = Stager<T, 2, BT>;
     __shared__ __attribute__((aligned(16))) T lds[St::kElems];
@@ -42,12 +84,12 @@ __global__ __launch_bounds__(64) void k_scan_fwd_summary(const T* __restrict__ u
     const bool act = d < D;
     const int dd = act ? d : D - 1;
     const int64_t c = tl.c;
-    const int64_t t0 = c * kLC;
-    const int64_t t1 = (t0 + kLC < T_) ? t0 + kLC : T_;
+    const int64_t t0 = c * lc;
+    const int64_t t1 = (t0 + lc < T_) ? t0 + lc : T_;
     if (t1 >= T_) return;          // last chunk: no successor needs it
     if (pos[t1] == 0) return;      // successor starts at a head: its carry is zero
 
-    // last head in [t0, t1)
+    // last head in [t0, t1): the summary starts there from a zero state
     int64_t ts = t0;
     bool has_head = false;
     for (int64_t base = t0; base < t1; base += kWave) {
@@ -59,43 +101,34 @@ __global__ __launch_bounds__(64) void k_scan_fwd_summary(const T* __restrict__ u
             ts = base + 63 - __builtin_clzll(m);
         }
     }
-    float A2[NS], h[NS], p[NS];
+    float A2[NS], h[NS];
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
         A2[n] = A[(size_t)dd * NS + n] * kLog2e;
         h[n] = 0.0f;
-        p[n] = 1.0f;
     }
+    float sdt = 0.0f, cdt = 0.0f;
     const T* const src[2] = {u, delta};
     St st;
     const int64_t tb0 = t0 + ((ts - t0) / BT) * BT;
     st.fetch(src, tb0, T_, D, tl.g, lane, vec);
     for (int64_t tb = tb0; tb < t1; tb += BT) {
+        wave_sync();
         st.commit(lds, src, tb, T_, D, tl.g, lane, vec);
         wave_sync();
         if (tb + BT < t1) st.fetch(src, tb + BT, T_, D, tl.g, lane, vec);
-#pragma unroll
-        for (int k = 0; k < BT; ++k) {
-            const int64_t t = tb + k;
-            if (t >= ts && t < t1) {
-                const float dt = St::get(lds, 1, k, lane);
-                const float dtu = dt * St::get(lds, 0, k, lane);
-                const float* __restrict__ row = bc + (size_t)t * 2 * NS;
-#pragma unroll
-                for (int n = 0; n < NS; ++n) {
-                    const float a = exp2_fast(dt * A2[n]);
-                    h[n] = __builtin_fmaf(a, h[n], dtu * row[n]);
-                    p[n] *= a;
-                }
-            }
-        }
-        wave_sync();
+        const int first = (int)((ts > tb) ? ts - tb : 0);
+        const int nt = (int)((tb + BT < t1) ? BT : t1 - tb);
+        if (first == 0 && nt == BT)
+            summary_block<false, T, NS, BT, St>(lds, bc, tb, 0, BT, A2, h, sdt, cdt, lane);
+        else
+            summary_block<true, T, NS, BT, St>(lds, bc, tb, first, nt, A2, h, sdt, cdt, lane);
     }
     if (act) {
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
             const size_t o = ((size_t)c * NS + n) * D + d;
-            P[o] = has_head ? 0.0f : p[n];
+            P[o] = has_head ? 0.0f : exp2_fast(A2[n] * sdt);
             S[o] = h[n];
         }
     }
@@ -105,14 +138,14 @@ __global__ __launch_bounds__(64) void k_scan_fwd_summary(const T* __restrict__ u
 template <int NS>
 __global__ __launch_bounds__(256) void k_scan_fwd_carry(const float* __restrict__ P, const float* __restrict__ S,
                                                         const int32_t* __restrict__ pos, float* __restrict__ ckpt,
-                                                        int64_t T_, int D, int64_t nchunk) {
+                                                        int64_t T_, int D, int64_t nchunk, int lc) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // n*D + d
     const int64_t ND = (int64_t)NS * D;
     if (i >= ND) return;
     float h = 0.0f;
     for (int64_t c = 0; c < nchunk; ++c) {
-        ckpt[(size_t)(c * (kLC / kCK)) * ND + i] = h;
-        const int64_t t1 = (c + 1) * kLC;
+        ckpt[(size_t)(c * (lc / kCK)) * ND + i] = h;
+        const int64_t t1 = (c + 1) * lc;
         if (t1 >= T_) break;
         if (pos[t1] == 0) {
             h = 0.0f;
@@ -125,12 +158,53 @@ __global__ __launch_bounds__(256) void k_scan_fwd_carry(const float* __restrict_
     }
 }
 
-template <typename T, int NS>
-__global__ __launch_bounds__(64) void k_scan_fwd_out(const T* __restrict__ u, const T* __restrict__ delta,
+// Output recurrence over one block of BT tokens. SAFE blocks may end early
+// (nt < BT) and may hold heads; fast blocks are full and head-free, so their
+// tokens run straight through with the next token's B/C rows in flight.
+template <bool SAFE, bool GATE, typename T, int NS, int BT, typename St>
+__device__ __forceinline__ void out_block(const T* lds, const float* __restrict__ bc, int64_t tb, int nt,
+                                          uint32_t heads, const float (&A2)[NS], float (&h)[NS], float Dv, int lane,
+                                          T* __restrict__ ob, int D, int d, bool store) {
+    const float* __restrict__ rows = bc + (size_t)tb * 2 * NS;
+    float cur[2 * NS];
+    load_rowv<2 * NS>(rows, cur);
+#pragma unroll
+    for (int k = 0; k < BT; ++k) {
+        if constexpr (SAFE) {
+            if (k >= nt) break;
+        }
+        float nxt[2 * NS];
+        const bool more = SAFE ? (k + 1 < nt) : (k + 1 < BT);
+        if (more) load_rowv<2 * NS>(rows + (k + 1) * 2 * NS, nxt);
+        const float dt = St::get(lds, 1, k, lane);
+        const float uu = St::get(lds, 0, k, lane);
+        const float dtu = dt * uu;
+        if constexpr (SAFE) reset_if<NS>((heads >> k) & 1u, h);
+        float y = 0.0f;
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            h[n] = __builtin_fmaf(exp2_fast(dt * A2[n]), h[n], dtu * cur[n]);
+            y = __builtin_fmaf(cur[NS + n], h[n], y);
+        }
+        y = __builtin_fmaf(Dv, uu, y);
+        if constexpr (GATE) {
+            const float zz = St::get(lds, 2, k, lane);
+            y *= zz * sigmoid_fast(zz);
+        }
+        if (store) Elt<T>::st(ob, (size_t)(k * D + d), y);
+        if (more) {
+#pragma unroll
+            for (int j = 0; j < 2 * NS; ++j) cur[j] = nxt[j];
+        }
+    }
+}
+
+template <typename T, int NS, bool GATE>
+__global__ __launch_bounds__(64, 4) void k_scan_fwd_out(const T* __restrict__ u, const T* __restrict__ delta,
                                                      const float* __restrict__ A, const float* __restrict__ bc,
                                                      const float* __restrict__ Dskip, const T* __restrict__ z,
                                                      const int32_t* __restrict__ pos, T* __restrict__ out,
-                                                     float* __restrict__ ckpt, int64_t T_, int D, int vec) {
+                                                     float* __restrict__ ckpt, int64_t T_, int D, int vec, int lc) {
     constexpr int BT = kFwdBlock;
     using St = Stager<T, 3, BT>;
     __shared__ __attribute__((aligned(16))) T lds[St::kElems];
@@ -140,11 +214,10 @@ __global__ __launch_bounds__(64) void k_scan_fwd_out(const T* __restrict__ u, co
     const bool act = d < D;
     const int dd = act ? d : D - 1;
     const int64_t c = tl.c;
-    const int64_t t0 = c * kLC;
-    const int64_t t1 = (t0 + kLC < T_) ? t0 + kLC : T_;
+    const int64_t t0 = c * lc;
+    const int64_t t1 = (t0 + lc < T_) ? t0 + lc : T_;
     const size_t ND = (size_t)NS * D;
-    const bool gate = z != nullptr;
-    const bool full = (tl.g + 1) * kWave <= D;  // every lane of the wave holds a channel
+    const bool store = act || (tl.g + 1) * kWave <= D;
 
     float A2[NS], h[NS];
 #pragma unroll
@@ -153,7 +226,7 @@ __global__ __launch_bounds__(64) void k_scan_fwd_out(const T* __restrict__ u, co
         h[n] = act ? ckpt[(size_t)(t0 / kCK) * ND + (size_t)n * D + dd] : 0.0f;
     }
     const float Dv = (Dskip && act) ? Dskip[dd] : 0.0f;
-    const T* const src[3] = {u, delta, gate ? z : u};
+    const T* const src[3] = {u, delta, GATE ? z : u};
     St st;
     st.fetch(src, t0, T_, D, tl.g, lane, vec);
     for (int64_t tb = t0; tb < t1; tb += BT) {
@@ -162,35 +235,16 @@ __global__ __launch_bounds__(64) void k_scan_fwd_out(const T* __restrict__ u, co
             for (int n = 0; n < NS; ++n) ckpt[(size_t)(tb / kCK) * ND + (size_t)n * D + d] = h[n];
         }
         const uint32_t heads = block_heads<BT>(pos, tb, T_, lane);
+        wave_sync();
         st.commit(lds, src, tb, T_, D, tl.g, lane, vec);
         wave_sync();
         if (tb + BT < t1) st.fetch(src, tb + BT, T_, D, tl.g, lane, vec);
-        T* __restrict__ orow = out + (size_t)tb * D + d;
-#pragma unroll
-        for (int k = 0; k < BT; ++k) {
-            const int64_t t = tb + k;
-            if (t < t1) {
-                const float dt = St::get(lds, 1, k, lane);
-                const float uu = St::get(lds, 0, k, lane);
-                const float dtu = dt * uu;
-                const float* __restrict__ row = bc + (size_t)t * 2 * NS;
-                reset_if<NS>((heads >> k) & 1u, h);
-                float y = 0.0f;
-#pragma unroll
-                for (int n = 0; n < NS; ++n) {
-                    const float a = exp2_fast(dt * A2[n]);
-                    h[n] = __builtin_fmaf(a, h[n], dtu * row[n]);
-                    y = __builtin_fmaf(row[NS + n], h[n], y);
-                }
-                y = __builtin_fmaf(Dv, uu, y);
-                if (gate) {
-                    const float zz = St::get(lds, 2, k, lane);
-                    y *= zz * sigmoid_fast(zz);
-                }
-                if (full || act) Elt<T>::st(orow, (size_t)k * D, y);
-            }
-        }
-        wave_sync();
+        const int nt = (int)((tb + BT < t1) ? BT : t1 - tb);
+        T* __restrict__ ob = out + (size_t)tb * D;
+        if (heads == 0 && nt == BT)
+            out_block<false, GATE, T, NS, BT, St>(lds, bc, tb, BT, 0u, A2, h, Dv, lane, ob, D, d, store);
+        else
+            out_block<true, GATE, T, NS, BT, St>(lds, bc, tb, nt, heads, A2, h, Dv, lane, ob, D, d, store);
     }
 }
 
@@ -199,22 +253,28 @@ static int scan_fwd_launch(const void* u, const void* delta, const float* A, con
                            const float* Dskip, const void* z, const int32_t* pos, void* out, float* ws, int64_t T_,
                            int D, hipStream_t s) {
     const ScanWs L = scan_ws_layout(T_, D, NS);
-    const dim3 grid((unsigned)(L.ngroup * L.nchunk));
+    const int lc = fwd_chunk_len(T_, D);
+    const int64_t nchunk = (T_ + lc - 1) / lc;
+    const dim3 grid((unsigned)(L.ngroup * nchunk));
     const int vec = stage_vec_ok<T>(D, {u, delta, z}) ? 1 : 0;
     k_bc_to_f32<T, NS><<<(unsigned)((T_ * 2 * NS + 255) / 256), 256, 0, s>>>((const T*)B, (const T*)C, ws + L.bc,
                                                                             T_);
     SSMP_LAUNCH_CHECK();
-    if (L.nchunk > 1) {
+    if (nchunk > 1) {
         k_scan_fwd_summary<T, NS><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, ws + L.bc, pos, ws + L.P,
-                                                         ws + L.S, T_, D, vec);
+                                                         ws + L.S, T_, D, vec, lc);
         SSMP_LAUNCH_CHECK();
     }
     const int64_t ND = (int64_t)NS * D;
     k_scan_fwd_carry<NS><<<(unsigned)((ND + 255) / 256), 256, 0, s>>>(ws + L.P, ws + L.S, pos, ws + L.ckpt, T_, D,
-                                                                      L.nchunk);
+                                                                      nchunk, lc);
     SSMP_LAUNCH_CHECK();
-    k_scan_fwd_out<T, NS><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, ws + L.bc, Dskip, (const T*)z, pos,
-                                                 (T*)out, ws + L.ckpt, T_, D, vec);
+    if (z)
+        k_scan_fwd_out<T, NS, true><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, ws + L.bc, Dskip,
+                                                           (const T*)z, pos, (T*)out, ws + L.ckpt, T_, D, vec, lc);
+    else
+        k_scan_fwd_out<T, NS, false><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, ws + L.bc, Dskip,
+                                                            nullptr, pos, (T*)out, ws + L.ckpt, T_, D, vec, lc);
     SSMP_LAUNCH_CHECK();
     return SSMP_OK;
 }
