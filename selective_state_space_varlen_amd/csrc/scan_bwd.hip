@@ -25,7 +25,8 @@
 // states at kK-token sub-chunk starts (kept in LDS), and for each sub-chunk
 // replays kK tokens with their states and decays held in VGPRs before running
 // the reverse step over them. dB and dC (sums over channels) are reduced
-// across the wave through LDS and written per channel group; dA and dDskip
+// across each wave and then across the workgroup's waves through LDS, and
+// written per workgroup channel group; dA and dDskip
 // are written per chunk; small kernels finish both sums in a fixed order, so
 // results are deterministic.
 #include "scan_common.h"
@@ -223,7 +224,8 @@ __device__ __forceinline__ void bwd_replay(const T* lds, const float* bcl, int k
     }
 }
 
-// Per-block output rows: du, ddelta, dz (dtype T) and the group's dB/dC partials.
+// Per-block outputs: du, ddelta, dz rows (dtype T) and the wave's per-token
+// dB/dC sums (LDS, [kCK][2NS]).
 template <typename T>
 struct BwdRows {
     T* du;
@@ -332,23 +334,33 @@ __device__ __forceinline__ void bwd_reverse(const T* lds, const float* bcl, floa
 // covers 64/LPC channels. Two lanes per channel halve the registers and LDS a
 // wave needs, which lets two or more waves share a SIMD; per-channel sums over
 // the states are completed with one DPP exchange between the lane pair.
-template <typename T, int NS, int LPC, bool GATE>
-__global__ __launch_bounds__(64) void k_scan_bwd_main(BwdArgs<T> p) {
+// A workgroup holds WV waves on adjacent channel groups of one chunk: they
+// share the staged B/C rows of each block, and add their per-token dB/dC sums
+// in LDS, so one partial row per WV*64/LPC channels reaches memory.
+template <typename T, int NS, int LPC, int WV, bool GATE>
+__global__ __launch_bounds__(kWave * WV, 2) void k_scan_bwd_main(BwdArgs<T> p) {
     constexpr int NH = NS / LPC;      // states per lane
     constexpr int CW = kWave / LPC;   // channels per wave
     static_assert(NH * LPC == NS && (LPC == 1 || LPC == 2), "lane split");
+    static_assert(CW * WV >= kWave, "dB/dC partial rows are sized for groups of at least 64 channels");
     using St = Stager<T, 4, kCK, CW>;  // u, delta, z, dout
     constexpr int NSUB = kCK / kK;
-    __shared__ __attribute__((aligned(16))) T lds[St::kElems];
-    __shared__ __attribute__((aligned(16))) float bcl[kCK * 2 * NS];  // B/C rows of the block
-    __shared__ float sub[NSUB > 1 ? NSUB - 1 : 1][NH][kWave];
-    __shared__ __attribute__((aligned(16))) float red[2 * NH][kRedStride];
+    constexpr int NT = kWave * WV;     // threads
+    constexpr int BCW = 2 * NS;        // dB/dC values per token
+    __shared__ __attribute__((aligned(16))) T lds[WV][St::kElems];
+    __shared__ __attribute__((aligned(16))) float bcl[kCK * BCW];  // B/C rows of the block
+    __shared__ float sub[WV][NSUB > 1 ? NSUB - 1 : 1][NH][kWave];
+    __shared__ __attribute__((aligned(16))) float red[WV][2 * NH][kRedStride];
+    __shared__ float blk[WV][kCK * BCW];  // per-wave dB/dC sums of the block's tokens
 
-    const int lane = threadIdx.x;
-    const int ch = lane / LPC;        // channel within the group
+    const int tid = threadIdx.x;
+    const int wv = tid / kWave;
+    const int lane = tid % kWave;
+    const int ch = lane / LPC;        // channel within the wave's group
     const int sh = lane % LPC;        // which share of the states
-    const Tile tl = tile_of_w<CW>(p.D);
-    const int g = tl.g;
+    const Tile tl = tile_of_w<CW * WV>(p.D);
+    const int gw = tl.g;              // workgroup channel group
+    const int g = gw * WV + wv;       // wave channel group
     const int d = g * CW + ch;
     const bool act = d < p.D;
     const bool full = (g + 1) * CW <= p.D;
@@ -359,6 +371,7 @@ __global__ __launch_bounds__(64) void k_scan_bwd_main(BwdArgs<T> p) {
     const size_t ND = (size_t)NS * p.D;
     const int n0 = sh * NH;           // first state of this lane
     const int D = p.D;
+    T* const mylds = lds[wv];
 
     // lanes past D carry zeros throughout, so they add nothing to dB/dC
     float A2[NH], carry[NH], dA[NH];
@@ -373,28 +386,24 @@ __global__ __launch_bounds__(64) void k_scan_bwd_main(BwdArgs<T> p) {
     const T* const src[4] = {p.u, p.delta, GATE ? p.z : p.u, p.dout};
 
     // B/C rows of a block: kCK * 2NS floats, fetched with the block's inputs
-    constexpr int BCV = kCK * 2 * NS / 4;                 // float4 pieces
-    constexpr int BCP = (BCV + kWave - 1) / kWave;        // pieces per lane
+    // by the first BCV threads of the workgroup
+    constexpr int BCV = kCK * BCW / 4;                    // float4 pieces
+    constexpr int BCP = (BCV + NT - 1) / NT;              // pieces per thread
     float4 bcr[BCP];
     auto fetch_bc = [&](int64_t tb) {
-        const float4* srcv = reinterpret_cast<const float4*>(p.bc + (size_t)tb * 2 * NS);
-        if (tb + kCK <= p.T_ && BCV % kWave == 0) {
+        const float4* srcv = reinterpret_cast<const float4*>(p.bc + (size_t)tb * BCW);
+        const int64_t lim = ((p.T_ - tb < kCK) ? (p.T_ - tb) : kCK) * BCW / 4;
 #pragma unroll
-            for (int q = 0; q < BCP; ++q) bcr[q] = srcv[q * kWave + lane];
-        } else {
-            const int64_t lim = ((p.T_ - tb < kCK) ? (p.T_ - tb) : kCK) * 2 * NS / 4;
-#pragma unroll
-            for (int q = 0; q < BCP; ++q) {
-                const int idx = q * kWave + lane;
-                bcr[q] = (idx < BCV && idx < lim) ? srcv[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+        for (int q = 0; q < BCP; ++q) {
+            const int idx = q * NT + tid;
+            bcr[q] = (idx < BCV && idx < lim) ? srcv[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
     auto commit_bc = [&]() {
 #pragma unroll
         for (int q = 0; q < BCP; ++q) {
-            const int idx = q * kWave + lane;
-            if (BCV % kWave == 0 || idx < BCV) reinterpret_cast<float4*>(bcl)[idx] = bcr[q];
+            const int idx = q * NT + tid;
+            if (idx < BCV) reinterpret_cast<float4*>(bcl)[idx] = bcr[q];
         }
     };
 
@@ -411,17 +420,16 @@ __global__ __launch_bounds__(64) void k_scan_bwd_main(BwdArgs<T> p) {
         const int nsub = (nb + kK - 1) / kK;
         const float* hb = p.ckpt + (size_t)(tb0 / kCK) * ND;
         const uint32_t heads = block_heads<kCK>(p.pos, tb0, p.T_, lane);
-        wave_sync();
-        st.commit(lds, src, tb0, p.T_, D, g, lane, p.vec);
+        __syncthreads();  // every wave is done with the previous block's bcl and blk
+        st.commit(mylds, src, tb0, p.T_, D, g, lane, p.vec);
         commit_bc();
-        wave_sync();
+        __syncthreads();
         if (jb > 0) {
             st.fetch(src, tb0 - kCK, p.T_, D, g, lane, p.vec);
             fetch_bc(tb0 - kCK);
         }
         const BwdRows<T> rows{p.du + (size_t)tb0 * D, p.ddelta + (size_t)tb0 * D,
-                              GATE ? p.dz + (size_t)tb0 * D : nullptr,
-                              p.dBC + ((size_t)g * p.T_ + tb0) * (2 * NS)};
+                              GATE ? p.dz + (size_t)tb0 * D : nullptr, blk[wv]};
 
         // states entering sub-chunks 1..nsub-1 (those sub-chunks are all full)
         if (nsub > 1) {
@@ -431,11 +439,11 @@ __global__ __launch_bounds__(64) void k_scan_bwd_main(BwdArgs<T> p) {
             for (int sc = 1; sc < nsub; ++sc) {
                 float hh[kK][NH], yk[kK];
                 if (heads == 0)
-                    bwd_replay<false, NS, LPC, St>(lds, bcl, (sc - 1) * kK, kK, 0u, ch, n0, A2, h, hh, yk, Dv);
+                    bwd_replay<false, NS, LPC, St>(mylds, bcl, (sc - 1) * kK, kK, 0u, ch, n0, A2, h, hh, yk, Dv);
                 else
-                    bwd_replay<true, NS, LPC, St>(lds, bcl, (sc - 1) * kK, kK, heads, ch, n0, A2, h, hh, yk, Dv);
+                    bwd_replay<true, NS, LPC, St>(mylds, bcl, (sc - 1) * kK, kK, heads, ch, n0, A2, h, hh, yk, Dv);
 #pragma unroll
-                for (int i = 0; i < NH; ++i) sub[sc - 1][i][lane] = h[i];
+                for (int i = 0; i < NH; ++i) sub[wv][sc - 1][i][lane] = h[i];
             }
         }
 
@@ -448,20 +456,30 @@ __global__ __launch_bounds__(64) void k_scan_bwd_main(BwdArgs<T> p) {
                 for (int i = 0; i < NH; ++i) h[i] = act ? hb[(size_t)(n0 + i) * D + dd] : 0.0f;
             } else {
 #pragma unroll
-                for (int i = 0; i < NH; ++i) h[i] = sub[sc - 1][i][lane];
+                for (int i = 0; i < NH; ++i) h[i] = sub[wv][sc - 1][i][lane];
             }
 #pragma unroll
             for (int i = 0; i < NH; ++i) hin[i] = h[i];
             const uint32_t sub_heads = (heads >> kb) & ((1u << kK) - 1u);
             if (sub_heads == 0 && ns == kK) {
-                bwd_replay<false, NS, LPC, St>(lds, bcl, kb, kK, 0u, ch, n0, A2, h, hh, yk, Dv);
-                bwd_reverse<false, GATE, NS, LPC, St>(lds, bcl, red, kb, kK, 0u, lane, ch, sh, n0, act, full, D, d,
-                                                      A2, carry, dA, dDacc, Dv, hin, hh, yk, rows);
+                bwd_replay<false, NS, LPC, St>(mylds, bcl, kb, kK, 0u, ch, n0, A2, h, hh, yk, Dv);
+                bwd_reverse<false, GATE, NS, LPC, St>(mylds, bcl, red[wv], kb, kK, 0u, lane, ch, sh, n0, act, full,
+                                                      D, d, A2, carry, dA, dDacc, Dv, hin, hh, yk, rows);
             } else {
-                bwd_replay<true, NS, LPC, St>(lds, bcl, kb, ns, heads, ch, n0, A2, h, hh, yk, Dv);
-                bwd_reverse<true, GATE, NS, LPC, St>(lds, bcl, red, kb, ns, heads, lane, ch, sh, n0, act, full, D, d,
-                                                     A2, carry, dA, dDacc, Dv, hin, hh, yk, rows);
+                bwd_replay<true, NS, LPC, St>(mylds, bcl, kb, ns, heads, ch, n0, A2, h, hh, yk, Dv);
+                bwd_reverse<true, GATE, NS, LPC, St>(mylds, bcl, red[wv], kb, ns, heads, lane, ch, sh, n0, act, full,
+                                                     D, d, A2, carry, dA, dDacc, Dv, hin, hh, yk, rows);
             }
+        }
+
+        // the workgroup's dB/dC sums of the block, waves added in order
+        __syncthreads();
+        float* const dst = p.dBC + ((size_t)gw * p.T_ + tb0) * BCW;
+        for (int e = tid; e < nb * BCW; e += NT) {
+            float v = blk[0][e];
+#pragma unroll
+            for (int w = 1; w < WV; ++w) v += blk[w][e];
+            dst[e] = v;
         }
     }
     if (act) {
@@ -542,11 +560,13 @@ static int scan_bwd_launch(const void* u, const void* delta, const float* A, con
     a.du = (T*)du; a.ddelta = (T*)ddelta; a.dz = (T*)dz; a.dApart = ws + L.dApart; a.dDpart = ws + L.dDpart;
     a.dBC = ws + L.dBC; a.T_ = T_; a.D = D; a.vec = vec; a.lc = lc;
     constexpr int LPC = NS >= 4 ? 2 : 1;  // bwd_lanes_per_channel
-    const int64_t ngroup = (D + kWave / LPC - 1) / (kWave / LPC);
+    constexpr int WV = bwd_waves_per_group(sizeof(T));
+    const int64_t ngroup = bwd_bc_groups(D, NS, sizeof(T));
+    const dim3 mgrid((unsigned)(ngroup * nchunk));
     if (z)
-        k_scan_bwd_main<T, NS, LPC, true><<<(unsigned)(ngroup * nchunk), kWave, 0, s>>>(a);
+        k_scan_bwd_main<T, NS, LPC, WV, true><<<mgrid, kWave * WV, 0, s>>>(a);
     else
-        k_scan_bwd_main<T, NS, LPC, false><<<(unsigned)(ngroup * nchunk), kWave, 0, s>>>(a);
+        k_scan_bwd_main<T, NS, LPC, WV, false><<<mgrid, kWave * WV, 0, s>>>(a);
     SSMP_LAUNCH_CHECK();
     const int64_t nrp = ND > D ? ND : D;
     k_scan_bwd_reduce_params<NS><<<(unsigned)((nrp + 255) / 256), 256, 0, s>>>(ws + L.dApart, ws + L.dDpart,

@@ -23,6 +23,14 @@ static_assert(kLCMin % kCK == 0 && kCK % kK == 0, "tiling");
 // channels per wave: the forward gives each channel one lane; the backward
 // two lanes (d_state >= 4) or one
 inline int bwd_lanes_per_channel(int N) { return N >= 4 ? 2 : 1; }
+// waves per backward workgroup: four for 2-byte inputs; two for fp32, whose
+// larger staging tiles would otherwise leave one workgroup per CU
+constexpr int bwd_waves_per_group(size_t elt_bytes) { return elt_bytes == 2 ? 4 : 2; }
+// channel groups of the backward's dB/dC partial rows (at most ceil(D/64))
+inline int64_t bwd_bc_groups(int D, int N, size_t elt_bytes) {
+    const int64_t cw = (int64_t)(kWave / bwd_lanes_per_channel(N)) * bwd_waves_per_group(elt_bytes);
+    return (D + cw - 1) / cw;
+}
 
 inline int scan_chunk_len(int64_t T, int D, int chw) {
     const int64_t ng = (D + chw - 1) / chw;
@@ -45,7 +53,7 @@ struct ScanWs {
     size_t cin;       // [nchunk][N][D]   backward: carry entering each chunk from the right
     size_t dApart;    // [nchunk][N][D]
     size_t dDpart;    // [nchunk][D]
-    size_t dBC;       // [ceil(D/32)][T][2N]  per channel-group partial sums of dB, dC
+    size_t dBC;       // [<= ceil(D/64)][T][2N]  per channel-group partial sums of dB, dC
     size_t total;     // floats
 };
 
@@ -71,7 +79,7 @@ inline ScanWs scan_ws_layout(int64_t T, int D, int N) {
     w.dApart = up(w.cin + (size_t)w.nchunk * ND);
     w.dDpart = up(w.dApart + (size_t)w.nchunk * ND);
     w.dBC = up(w.dDpart + (size_t)w.nchunk * D);
-    const size_t bwd_end = up(w.dBC + (size_t)((D + 31) / 32) * (size_t)T * 2 * N);
+    const size_t bwd_end = up(w.dBC + (size_t)((D + kWave - 1) / kWave) * (size_t)T * 2 * N);
     w.total = fwd_end > bwd_end ? fwd_end : bwd_end;
     return w;
 }
