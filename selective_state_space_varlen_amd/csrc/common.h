@@ -77,6 +77,24 @@ __device__ __forceinline__ float swap_adjacent(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
 }
 
+// sum_{r < n} p[r * stride], added in the order r = 0, 1, ..., n-1 (so the
+// result does not depend on the batch size), with kB loads in flight at a time
+// instead of one.
+template <int kB = 16>
+__device__ __forceinline__ float ordered_sum(const float* __restrict__ p, int64_t n, size_t stride) {
+    float acc = 0.0f;
+    int64_t r = 0;
+    for (; r + kB <= n; r += kB) {
+        float v[kB];
+#pragma unroll
+        for (int j = 0; j < kB; ++j) v[j] = p[(size_t)(r + j) * stride];
+#pragma unroll
+        for (int j = 0; j < kB; ++j) acc += v[j];
+    }
+    for (; r < n; ++r) acc += p[(size_t)r * stride];
+    return acc;
+}
+
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
 }  // namespace ssmp

@@ -11,80 +11,74 @@
 // vector) and a run of RT consecutive tokens, slides a W-token window of x in
 // registers, and reads the per-token position once per token (the same
 // address for the whole wave). Consecutive lanes own consecutive vectors, so
-// a wave reads 1 KiB of one row per load.
+// a wave reads 1 KiB of one row per load. Tokens are taken in batches of kG
+// whose loads are all issued before the first is used, so each wave keeps
+// kG (forward) or 2 kG (backward) row loads in flight.
 #include "common.h"
 
 namespace ssmp {
 
-template <typename T>
-struct Vec;
-template <>
-struct Vec<uint16_t> {
-    static constexpr int V = 8;
-    using raw = uint4;
-    static __device__ __forceinline__ void unpack(const raw& r, float (&f)[V]) {
-        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[2 * i] = bf16_to_f32(w[i]);
-            f[2 * i + 1] = bf16_hi_to_f32(w[i]);
-        }
-    }
-    static __device__ __forceinline__ raw pack(const float (&f)[V]) {
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            w[i] = (uint32_t)f32_to_bf16(f[2 * i]) | ((uint32_t)f32_to_bf16(f[2 * i + 1]) << 16);
-        return make_uint4(w[0], w[1], w[2], w[3]);
-    }
-};
-template <>
-struct Vec<float> {
-    static constexpr int V = 4;
-    using raw = float4;
-    static __device__ __forceinline__ void unpack(const raw& r, float (&f)[V]) {
-        f[0] = r.x; f[1] = r.y; f[2] = r.z; f[3] = r.w;
-    }
-    static __device__ __forceinline__ raw pack(const float (&f)[V]) { return make_float4(f[0], f[1], f[2], f[3]); }
-};
+// V adjacent elements of one row moved as a single load or store of
+// V * sizeof(T) bytes (V = 1 is the unaligned fallback).
+template <int BYTES>
+struct RawOf;
+template <> struct RawOf<16> { using type = uint4; };
+template <> struct RawOf<8> { using type = uint2; };
+template <> struct RawOf<4> { using type = uint32_t; };
+template <> struct RawOf<2> { using type = uint16_t; };
 
-// Scalar fallback when D is not a multiple of the vector width.
-template <typename T>
-struct Vec1 {
-    static constexpr int V = 1;
-};
-
-template <typename T, bool VEC>
+template <typename T, int V_>
 struct Access {
-    static constexpr int V = VEC ? Vec<T>::V : 1;
-    static __device__ __forceinline__ void load(const T* __restrict__ p, float (&f)[V]) {
-        if constexpr (VEC) {
-            Vec<T>::unpack(*reinterpret_cast<const typename Vec<T>::raw*>(p), f);
-        } else {
-            f[0] = Elt<T>::ld(p, 0);
-        }
+    static constexpr int V = V_;
+    using Raw = typename RawOf<V * (int)sizeof(T)>::type;
+    struct Arr {
+        T v[V];
+    };
+    static __device__ __forceinline__ Raw load_raw(const T* __restrict__ p) {
+        return *reinterpret_cast<const Raw*>(p);
     }
+    static __device__ __forceinline__ void unpack(const Raw& r, float (&f)[V]) {
+        const Arr a = __builtin_bit_cast(Arr, r);
+#pragma unroll
+        for (int i = 0; i < V; ++i) f[i] = Elt<T>::ld(a.v, i);
+    }
+    static __device__ __forceinline__ void load(const T* __restrict__ p, float (&f)[V]) { unpack(load_raw(p), f); }
     static __device__ __forceinline__ void store(T* __restrict__ p, const float (&f)[V]) {
-        if constexpr (VEC) {
-            *reinterpret_cast<typename Vec<T>::raw*>(p) = Vec<T>::pack(f);
-        } else {
-            Elt<T>::st(p, 0, f[0]);
-        }
+        Arr a;
+#pragma unroll
+        for (int i = 0; i < V; ++i) Elt<T>::st(a.v, i, f[i]);
+        *reinterpret_cast<Raw*>(p) = __builtin_bit_cast(Raw, a);
     }
 };
+
+// elements per access: 16 bytes in the forward; 8 in the backward, whose
+// per-channel state (taps, window, gradient sums) would otherwise cost two
+// waves per SIMD
+template <typename T> constexpr int kFwdV = 16 / (int)sizeof(T);
+template <typename T> constexpr int kBwdV = 8 / (int)sizeof(T);
 
 constexpr int kConvFwdRun = 32;   // tokens per thread, forward
-constexpr int kConvBwdRun = 128;  // tokens per thread, backward (sets the partial-sum count)
+constexpr int kConvBwdRun = 64;   // tokens per thread, backward
+constexpr int kConvBwdRuns = 4;   // runs per backward workgroup (summed there before the partials)
+constexpr int kG = 8;             // tokens per load batch
+static_assert(kConvFwdRun % kG == 0 && kConvBwdRun % kG == 0, "runs hold whole batches");
+
+// taps used at token t: k <= kmax (pos[t] caps the look-back at the head)
+__device__ __forceinline__ int conv_kmax(int32_t pos_t, int64_t t, int W) {
+    int kmax = pos_t;
+    if (kmax > W - 1) kmax = W - 1;
+    if ((int64_t)kmax > t) kmax = (int)t;
+    return kmax;
+}
 
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
-template <typename T, bool VEC>
+template <typename T, int V>
 __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const float* __restrict__ w,
                                                   const float* __restrict__ b, const int32_t* __restrict__ pos,
                                                   T* __restrict__ u, int64_t T_, int D, int W, int silu) {
-    using A = Access<T, VEC>;
-    constexpr int V = A::V;
+    using A = Access<T, V>;
     const int nvec = D / V;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int cv = (int)(gid % nvec);
@@ -113,24 +107,36 @@ __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const
             for (int i = 0; i < V; ++i) xw[k][i] = 0.0f;
         }
     }
-    for (int64_t t = t0; t < t1; ++t) {
-        A::load(x + (size_t)t * D + d0, xw[0]);
-        int kmax = pos[t];
-        if (kmax > W - 1) kmax = W - 1;
-        if ((int64_t)kmax > t) kmax = (int)t;
-        float o[V];
+    for (int64_t tb = t0; tb < t1; tb += kG) {
+        const int ng = (int)((t1 - tb < kG) ? t1 - tb : kG);
+        typename A::Raw raw[kG];
+        int32_t pk[kG];
 #pragma unroll
-        for (int i = 0; i < V; ++i) {
-            float acc = bias[i];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) acc += (k <= kmax) ? wk[k][i] * xw[k][i] : 0.0f;
-            o[i] = silu ? acc * sigmoid_fast(acc) : acc;
+        for (int g = 0; g < kG; ++g) {
+            const int64_t t = tb + (g < ng ? g : ng - 1);  // a short batch repeats its last token
+            raw[g] = A::load_raw(x + (size_t)t * D + d0);
+            pk[g] = pos[t];
         }
-        A::store(u + (size_t)t * D + d0, o);
 #pragma unroll
-        for (int k = 3; k > 0; --k)
+        for (int g = 0; g < kG; ++g) {
+            if (g >= ng) break;
+            const int64_t t = tb + g;
+            A::unpack(raw[g], xw[0]);
+            const int kmax = conv_kmax(pk[g], t, W);
+            float o[V];
 #pragma unroll
-            for (int i = 0; i < V; ++i) xw[k][i] = xw[k - 1][i];
+            for (int i = 0; i < V; ++i) {
+                float acc = bias[i];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) acc += (k <= kmax) ? wk[k][i] * xw[k][i] : 0.0f;
+                o[i] = silu ? acc * sigmoid_fast(acc) : acc;
+            }
+            A::store(u + (size_t)t * D + d0, o);
+#pragma unroll
+            for (int k = 3; k > 0; --k)
+#pragma unroll
+                for (int i = 0; i < V; ++i) xw[k][i] = xw[k - 1][i];
+        }
     }
 }
 
@@ -139,52 +145,31 @@ __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const
 // ---------------------------------------------------------------------------
 // Per thread: tokens [t0, t1). gv[t] = du[t] * act'(v[t]) is produced for
 // t in [t0, min(t1 + 3, T)); dx[s] for s in [t0, t1) collects
-// sum_k [k <= pos[s+k]] w[W-1-k] gv[s+k]; dw and db partial sums over
-// [t0, t1) go to part[run][j][d] (j = tap k for k < 4, j = 4 for the bias).
-template <typename T, bool VEC>
-__global__ __launch_bounds__(256) void k_conv_bwd(const T* __restrict__ x, const float* __restrict__ w,
-                                                  const float* __restrict__ b, const int32_t* __restrict__ pos,
-                                                  const T* __restrict__ du, T* __restrict__ dx,
-                                                  float* __restrict__ part, int64_t T_, int D, int W, int silu) {
-    using A = Access<T, VEC>;
-    constexpr int V = A::V;
+// sum_k [k <= kmax(s+k)] w_k gv[s+k], emitted once gv[s+3] is known (the
+// last four gv and their kmax are kept). dw and db sums over [t0, t1) are
+// added over the workgroup's kConvBwdRuns runs in LDS, in a fixed order, and
+// written to part[group][j][d] (j = tap k for k < 4, j = 4 for the bias).
+// A workgroup is kConvBwdRuns waves: the same 64 vectors, consecutive runs.
+template <typename T, int V>
+__global__ __launch_bounds__(kWave * kConvBwdRuns) void k_conv_bwd(
+    const T* __restrict__ x, const float* __restrict__ w, const float* __restrict__ b,
+    const int32_t* __restrict__ pos, const T* __restrict__ du, T* __restrict__ dx, float* __restrict__ part,
+    int64_t T_, int D, int W, int silu) {
+    using A = Access<T, V>;
+    __shared__ float red[kConvBwdRuns][5][kWave * V];
     const int nvec = D / V;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int cv = (int)(gid % nvec);
-    const int64_t run = gid / nvec;
+    const int nvg = (nvec + kWave - 1) / kWave;  // 64-vector groups
+    const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int vg = (int)(blockIdx.x % nvg);
+    const int64_t grp = blockIdx.x / nvg;           // workgroup's run group
+    const int cv = vg * kWave + lane;
+    const bool actv = cv < nvec;
+    const int64_t run = grp * kConvBwdRuns + wv;
     const int64_t t0 = run * kConvBwdRun;
-    if (t0 >= T_) return;
     const int64_t t1 = (t0 + kConvBwdRun < T_) ? t0 + kConvBwdRun : T_;
     const int64_t tend = (t1 + 3 < T_) ? t1 + 3 : T_;
-    const int d0 = cv * V;
+    const int d0 = (actv ? cv : 0) * V;
 
-    float wk[4][V], bias[V];
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-        bias[i] = b ? b[d0 + i] : 0.0f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) wk[k][i] = (k < W) ? w[(size_t)(d0 + i) * W + (W - 1 - k)] : 0.0f;
-    }
-    float xw[4][V];
-#pragma unroll
-    for (int k = 1; k < 4; ++k) {
-        const int64_t tk = t0 - k;
-        if (tk >= 0) {
-            A::load(x + (size_t)tk * D + d0, xw[k]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < V; ++i) xw[k][i] = 0.0f;
-        }
-    }
-    // gq[j][i] = gv[t-j] masked for the dx contribution of tap j:
-    // gq[j] = [j <= kmax(t-j)] * gv[t-j]; kept for j = 0..3
-    float gq[4][4][V];  // [age j][tap k][i]: contribution of token t-j to dx[t-j-k]
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-#pragma unroll
-            for (int i = 0; i < V; ++i) gq[j][k][i] = 0.0f;
     float dwp[4][V], dbp[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
@@ -192,74 +177,130 @@ __global__ __launch_bounds__(256) void k_conv_bwd(const T* __restrict__ x, const
 #pragma unroll
         for (int k = 0; k < 4; ++k) dwp[k][i] = 0.0f;
     }
+    if (actv && t0 < T_) {
+        float wk[4][V], bias[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            bias[i] = b ? b[d0 + i] : 0.0f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) wk[k][i] = (k < W) ? w[(size_t)(d0 + i) * W + (W - 1 - k)] : 0.0f;
+        }
+        float xw[4][V];
+#pragma unroll
+        for (int k = 1; k < 4; ++k) {
+            const int64_t tk = t0 - k;
+            if (tk >= 0) {
+                A::load(x + (size_t)tk * D + d0, xw[k]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < V; ++i) xw[k][i] = 0.0f;
+            }
+        }
+        // gw[j] = gv[t-j], kw[j] = kmax(t-j) for the last four tokens (gv = 0 before t0)
+        float gw[4][V];
+        int kw[4] = {-1, -1, -1, -1};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < V; ++i) gw[j][i] = 0.0f;
 
-    for (int64_t t = t0; t < tend + 3; ++t) {
-        // shift ages
+        // one token step: shift the windows in, gv of token t (zero past tend), dx[t-3]
+        auto step = [&](int64_t t, bool have, const float (&g)[V], int kmax) {
 #pragma unroll
-        for (int j = 3; j > 0; --j)
+            for (int j = 3; j > 0; --j) {
+                kw[j] = kw[j - 1];
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-#pragma unroll
-                for (int i = 0; i < V; ++i) gq[j][k][i] = gq[j - 1][k][i];
-        if (t < tend) {
-            A::load(x + (size_t)t * D + d0, xw[0]);
-            float g[V];
-            A::load(du + (size_t)t * D + d0, g);
-            int kmax = pos[t];
-            if (kmax > W - 1) kmax = W - 1;
-            if ((int64_t)kmax > t) kmax = (int)t;
+                for (int i = 0; i < V; ++i) gw[j][i] = gw[j - 1][i];
+            }
+            kw[0] = have ? kmax : -1;
             const bool own = t < t1;  // dw/db sums only over this thread's tokens
 #pragma unroll
             for (int i = 0; i < V; ++i) {
-                float v = bias[i];
+                float gv = 0.0f;
+                if (have) {
+                    float v = bias[i];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) v += (k <= kmax) ? wk[k][i] * xw[k][i] : 0.0f;
-                float gv = g[i];
-                if (silu) {
-                    const float s = sigmoid_fast(v);
-                    gv = g[i] * s * (1.0f + v * (1.0f - s));
-                }
+                    for (int k = 0; k < 4; ++k) v += (k <= kmax) ? wk[k][i] * xw[k][i] : 0.0f;
+                    gv = g[i];
+                    if (silu) {
+                        const float sg = sigmoid_fast(v);
+                        gv = g[i] * sg * (1.0f + v * (1.0f - sg));
+                    }
+                    if (own) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const bool on = k <= kmax;
-                    gq[0][k][i] = on ? gv : 0.0f;
-                    if (own && on) dwp[k][i] += gv * xw[k][i];
+                        for (int k = 0; k < 4; ++k) dwp[k][i] += (k <= kmax) ? gv * xw[k][i] : 0.0f;
+                        dbp[i] += gv;
+                    }
                 }
-                if (own) dbp[i] += gv;
+                gw[0][i] = gv;
+            }
+            if (have) {
+#pragma unroll
+                for (int k = 3; k > 0; --k)
+#pragma unroll
+                    for (int i = 0; i < V; ++i) xw[k][i] = xw[k - 1][i];
+            }
+            // dx[s], s = t - 3: token s + k feeds tap k when k <= kmax(s + k)
+            const int64_t s = t - 3;
+            if (s >= t0 && s < t1) {
+                float o[V];
+#pragma unroll
+                for (int i = 0; i < V; ++i) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) acc += (k <= kw[3 - k]) ? wk[k][i] * gw[3 - k][i] : 0.0f;
+                    o[i] = acc;
+                }
+                A::store(dx + (size_t)s * D + d0, o);
+            }
+        };
+
+        for (int64_t tb = t0; tb < tend; tb += kG) {
+            const int ng = (int)((tend - tb < kG) ? tend - tb : kG);
+            typename A::Raw rx[kG], rg[kG];
+            int32_t pk[kG];
+#pragma unroll
+            for (int g = 0; g < kG; ++g) {
+                const int64_t t = tb + (g < ng ? g : ng - 1);  // a short batch repeats its last token
+                rx[g] = A::load_raw(x + (size_t)t * D + d0);
+                rg[g] = A::load_raw(du + (size_t)t * D + d0);
+                pk[g] = pos[t];
             }
 #pragma unroll
-            for (int k = 3; k > 0; --k)
-#pragma unroll
-                for (int i = 0; i < V; ++i) xw[k][i] = xw[k - 1][i];
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-#pragma unroll
-                for (int i = 0; i < V; ++i) gq[0][k][i] = 0.0f;
-        }
-        // dx[t-3] = sum_k w_k * gq[age 3-k][tap k]  (token t-3+k feeds tap k)
-        const int64_t s = t - 3;
-        if (s >= t0 && s < t1) {
-            float o[V];
-#pragma unroll
-            for (int i = 0; i < V; ++i) {
-                float acc = 0.0f;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) acc += wk[k][i] * gq[3 - k][k][i];
-                o[i] = acc;
+            for (int g = 0; g < kG; ++g) {
+                if (g >= ng) break;
+                const int64_t t = tb + g;
+                float gg[V];
+                A::unpack(rx[g], xw[0]);
+                A::unpack(rg[g], gg);
+                step(t, true, gg, conv_kmax(pk[g], t, W));
             }
-            A::store(dx + (size_t)s * D + d0, o);
         }
+        // the tensor ends before t1 + 3: flush the last dx rows
+        const float zero[V] = {};
+        for (int64_t t = tend; t < t1 + 3; ++t) step(t, false, zero, -1);
     }
+
+    // fixed-order sum of the workgroup's runs
 #pragma unroll
     for (int i = 0; i < V; ++i) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) part[((size_t)run * 5 + k) * D + d0 + i] = dwp[k][i];
-        part[((size_t)run * 5 + 4) * D + d0 + i] = dbp[i];
+        for (int k = 0; k < 4; ++k) red[wv][k][lane * V + i] = dwp[k][i];
+        red[wv][4][lane * V + i] = dbp[i];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 5 * kWave * V; e += kWave * kConvBwdRuns) {
+        const int j = e / (kWave * V), c = e % (kWave * V);
+        const int d = vg * kWave * V + c;
+        if (d >= nvec * V) continue;
+        float acc = red[0][j][c];
+#pragma unroll
+        for (int r = 1; r < kConvBwdRuns; ++r) acc += red[r][j][c];
+        part[((size_t)grp * 5 + j) * D + d] = acc;
     }
 }
 
-// dw[d, W-1-k] = sum_run part[run][k][d];  db[d] = sum_run part[run][4][d]
+// dw[d, W-1-k] = sum_g part[g][k][d];  db[d] = sum_g part[g][4][d]
 __global__ __launch_bounds__(256) void k_conv_bwd_reduce(const float* __restrict__ part, int64_t nrun, int D, int W,
                                                          float* __restrict__ dw, float* __restrict__ db) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -267,28 +308,34 @@ __global__ __launch_bounds__(256) void k_conv_bwd_reduce(const float* __restrict
     const int j = (int)(i / D), d = (int)(i % D);
     if (j < 4 && j >= W) return;
     if (j == 4 && !db) return;
-    float acc = 0.0f;
-    for (int64_t r = 0; r < nrun; ++r) acc += part[((size_t)r * 5 + j) * D + d];
+    const float acc = ordered_sum(part + (size_t)j * D + d, nrun, (size_t)5 * D);
     if (j < 4) dw[(size_t)d * W + (W - 1 - j)] = acc;
     else db[d] = acc;
 }
 
-static bool vec_ok(const void* p, int D, int V) {
-    return (D % V == 0) && ((reinterpret_cast<uintptr_t>(p) & 15u) == 0);
+// run groups of the backward (one partial row set each)
+static int64_t conv_bwd_groups(int64_t T_) {
+    const int64_t span = (int64_t)kConvBwdRun * kConvBwdRuns;
+    return (T_ + span - 1) / span;
+}
+
+static bool vec_ok(const void* p, int D, int V, size_t elt) {
+    return (D % V == 0) && ((reinterpret_cast<uintptr_t>(p) % (V * elt)) == 0);
 }
 
 template <typename T>
 static int launch_fwd(const void* x, const float* w, const float* b, const int32_t* pos, void* u, int64_t T_, int D,
                       int W, int silu, hipStream_t s) {
-    const bool vec = vec_ok(x, D, Vec<T>::V) && vec_ok(u, D, Vec<T>::V);
-    const int V = vec ? Vec<T>::V : 1;
+    constexpr int VV = kFwdV<T>;
+    const bool vec = vec_ok(x, D, VV, sizeof(T)) && vec_ok(u, D, VV, sizeof(T));
+    const int V = vec ? VV : 1;
     const int64_t nthreads = (int64_t)(D / V) * ((T_ + kConvFwdRun - 1) / kConvFwdRun);
     const int64_t blocks = (nthreads + 255) / 256;
     if (blocks > 0x7fffffff) return SSMP_ERR_SHAPE;
     if (vec)
-        k_conv_fwd<T, true><<<(unsigned)blocks, 256, 0, s>>>((const T*)x, w, b, pos, (T*)u, T_, D, W, silu);
+        k_conv_fwd<T, VV><<<(unsigned)blocks, 256, 0, s>>>((const T*)x, w, b, pos, (T*)u, T_, D, W, silu);
     else
-        k_conv_fwd<T, false><<<(unsigned)blocks, 256, 0, s>>>((const T*)x, w, b, pos, (T*)u, T_, D, W, silu);
+        k_conv_fwd<T, 1><<<(unsigned)blocks, 256, 0, s>>>((const T*)x, w, b, pos, (T*)u, T_, D, W, silu);
     SSMP_LAUNCH_CHECK();
     return SSMP_OK;
 }
@@ -296,20 +343,21 @@ static int launch_fwd(const void* x, const float* w, const float* b, const int32
 template <typename T>
 static int launch_bwd(const void* x, const float* w, const float* b, const int32_t* pos, const void* du, void* dx,
                       float* dw, float* db, float* part, int64_t T_, int D, int W, int silu, hipStream_t s) {
-    const bool vec = vec_ok(x, D, Vec<T>::V) && vec_ok(du, D, Vec<T>::V) && vec_ok(dx, D, Vec<T>::V);
-    const int V = vec ? Vec<T>::V : 1;
-    const int64_t nrun = (T_ + kConvBwdRun - 1) / kConvBwdRun;
-    const int64_t nthreads = (int64_t)(D / V) * nrun;
-    const int64_t blocks = (nthreads + 255) / 256;
+    constexpr int VV = kBwdV<T>;
+    const bool vec = vec_ok(x, D, VV, sizeof(T)) && vec_ok(du, D, VV, sizeof(T)) && vec_ok(dx, D, VV, sizeof(T));
+    const int V = vec ? VV : 1;
+    const int64_t ngrp = conv_bwd_groups(T_);
+    const int64_t nvg = (D / V + kWave - 1) / kWave;
+    const int64_t blocks = nvg * ngrp;
     if (blocks > 0x7fffffff) return SSMP_ERR_SHAPE;
     if (vec)
-        k_conv_bwd<T, true><<<(unsigned)blocks, 256, 0, s>>>((const T*)x, w, b, pos, (const T*)du, (T*)dx, part, T_,
-                                                               D, W, silu);
+        k_conv_bwd<T, VV><<<(unsigned)blocks, kWave * kConvBwdRuns, 0, s>>>(
+            (const T*)x, w, b, pos, (const T*)du, (T*)dx, part, T_, D, W, silu);
     else
-        k_conv_bwd<T, false><<<(unsigned)blocks, 256, 0, s>>>((const T*)x, w, b, pos, (const T*)du, (T*)dx, part, T_,
-                                                                D, W, silu);
+        k_conv_bwd<T, 1><<<(unsigned)blocks, kWave * kConvBwdRuns, 0, s>>>(
+            (const T*)x, w, b, pos, (const T*)du, (T*)dx, part, T_, D, W, silu);
     SSMP_LAUNCH_CHECK();
-    k_conv_bwd_reduce<<<(unsigned)((5 * (int64_t)D + 255) / 256), 256, 0, s>>>(part, nrun, D, W, dw, db);
+    k_conv_bwd_reduce<<<(unsigned)((5 * (int64_t)D + 255) / 256), 256, 0, s>>>(part, ngrp, D, W, dw, db);
     SSMP_LAUNCH_CHECK();
     return SSMP_OK;
 }
@@ -339,8 +387,7 @@ extern "C" int conv1d_pack_fwd(const void* x, const float* w, const float* b, co
 extern "C" size_t conv1d_pack_bwd_workspace_bytes(int64_t T, int32_t D, int32_t W) {
     (void)W;
     if (T <= 0 || D <= 0) return 0;
-    const int64_t nrun = (T + ssmp::kConvBwdRun - 1) / ssmp::kConvBwdRun;
-    return (size_t)nrun * 5 * (size_t)D * sizeof(float);
+    return (size_t)ssmp::conv_bwd_groups(T) * 5 * (size_t)D * sizeof(float);
 }
 
 extern "C" int conv1d_pack_bwd(const void* x, const float* w, const float* b, const int32_t* pos, const void* du,

@@ -147,18 +147,33 @@ template <int NS>
 __global__ __launch_bounds__(256) void k_scan_bwd_carry(const float* __restrict__ Pr, const float* __restrict__ Sr,
                                                         const int32_t* __restrict__ pos, float* __restrict__ cin,
                                                         int D, int64_t nchunk, int lc) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t ND = (int64_t)NS * D;
-    if (i >= ND) return;
+    const bool act = i0 < ND;
+    const int64_t i = act ? i0 : ND - 1;  // lanes past the end run along (ballots need the wave) but store nothing
+    // the summaries of kB chunks are loaded before the chain walks through them
+    constexpr int kB = 16;
+    const int lane = threadIdx.x % kWave;
     float cc = 0.0f;
-    for (int64_t c = nchunk - 1; c >= 0; --c) {
-        cin[(size_t)c * ND + i] = cc;
-        if (c == 0) break;
-        if (pos[c * lc] == 0) {
-            cc = 0.0f;
-        } else {
-            const float Pc = Pr[(size_t)c * ND + i], Sc = Sr[(size_t)c * ND + i];
-            cc = (Pc == 0.0f) ? Sc : __builtin_fmaf(Pc, cc, Sc);  // select at heads, as in the forward
+    for (int64_t cb = nchunk - 1; cb >= 0; cb -= kB) {
+        // bit j: chunk cb - j >= 1 starts at a head
+        const int64_t cj = cb - lane;
+        const uint64_t heads = __ballot(lane < kB && cj >= 1 && pos[(cj >= 1 ? cj : 0) * lc] == 0);
+        float Pv[kB], Sv[kB];
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+            const int64_t c = cb - j;
+            const int64_t cl = c > 0 ? c : 0;  // c <= 0 loads chunk 0 and is not combined
+            Pv[j] = Pr[(size_t)cl * ND + i];
+            Sv[j] = Sr[(size_t)cl * ND + i];
+        }
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+            const int64_t c = cb - j;
+            if (act && c >= 0) cin[(size_t)c * ND + i] = cc;
+            // select at heads, as in the forward
+            const float cn = ((heads >> j) & 1u) ? 0.0f : (Pv[j] == 0.0f) ? Sv[j] : __builtin_fmaf(Pv[j], cc, Sv[j]);
+            cc = (c >= 1) ? cn : cc;
         }
     }
 }
@@ -500,16 +515,11 @@ __global__ __launch_bounds__(256) void k_scan_bwd_reduce_params(const float* __r
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // n*D + d
     const int64_t ND = (int64_t)NS * D;
     if (i < ND) {
-        float acc = 0.0f;
-        for (int64_t c = 0; c < nchunk; ++c) acc += dApart[(size_t)c * ND + i];
+        const float acc = ordered_sum(dApart + i, nchunk, (size_t)ND);
         const int n = (int)(i / D), d = (int)(i % D);
         dA[(size_t)d * NS + n] = acc;
     }
-    if (dD && i < D) {
-        float acc = 0.0f;
-        for (int64_t c = 0; c < nchunk; ++c) acc += dDpart[(size_t)c * D + i];
-        dD[i] = acc;
-    }
+    if (dD && i < D) dD[i] = ordered_sum(dDpart + i, nchunk, (size_t)D);
 }
 
 template <int NS>
@@ -518,8 +528,7 @@ __global__ __launch_bounds__(256) void k_scan_bwd_reduce_bc(const float* __restr
                                                             float* __restrict__ dC) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // t*2NS + j
     if (i >= T_ * 2 * NS) return;
-    float acc = 0.0f;
-    for (int64_t gi = 0; gi < ngroup; ++gi) acc += dBC[(size_t)gi * T_ * 2 * NS + i];
+    const float acc = ordered_sum<8>(dBC + i, ngroup, (size_t)T_ * 2 * NS);
     const int64_t t = i / (2 * NS);
     const int j = (int)(i % (2 * NS));
     if (j < NS) dB[t * NS + j] = acc;

@@ -139,21 +139,35 @@ template <int NS>
 __global__ __launch_bounds__(256) void k_scan_fwd_carry(const float* __restrict__ P, const float* __restrict__ S,
                                                         const int32_t* __restrict__ pos, float* __restrict__ ckpt,
                                                         int64_t T_, int D, int64_t nchunk, int lc) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // n*D + d
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // n*D + d
     const int64_t ND = (int64_t)NS * D;
-    if (i >= ND) return;
+    const bool act = i0 < ND;
+    const int64_t i = act ? i0 : ND - 1;  // lanes past the end run along (ballots need the wave) but store nothing
+    // the summaries of kB chunks are loaded before the chain walks through them;
+    // chunk c hands its state on iff chunk c + 1 exists ((c + 1) lc < T)
+    constexpr int kB = 16;
+    const int lane = threadIdx.x % kWave;
     float h = 0.0f;
-    for (int64_t c = 0; c < nchunk; ++c) {
-        ckpt[(size_t)(c * (lc / kCK)) * ND + i] = h;
-        const int64_t t1 = (c + 1) * lc;
-        if (t1 >= T_) break;
-        if (pos[t1] == 0) {
-            h = 0.0f;
-        } else {
+    for (int64_t cb = 0; cb < nchunk; cb += kB) {
+        // bit j: chunk cb + j + 1 exists and starts at a head
+        const int64_t tn = (cb + lane + 1) * lc;
+        const uint64_t heads = __ballot(lane < kB && tn < T_ && pos[tn < T_ ? tn : 0] == 0);
+        float Pv[kB], Sv[kB];
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+            const int64_t c = cb + j;
+            const int64_t cl = c + 1 < nchunk ? c : 0;  // chunks that hand nothing on load chunk 0
+            Pv[j] = P[(size_t)cl * ND + i];
+            Sv[j] = S[(size_t)cl * ND + i];
+        }
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+            const int64_t c = cb + j;
+            if (act && c < nchunk) ckpt[(size_t)(c * (lc / kCK)) * ND + i] = h;
             // P == 0 marks a chunk holding a head: select, so that a
             // non-finite state before the head cannot leak through 0 * h
-            const float Pc = P[(size_t)c * ND + i], Sc = S[(size_t)c * ND + i];
-            h = (Pc == 0.0f) ? Sc : __builtin_fmaf(Pc, h, Sc);
+            const float hn = ((heads >> j) & 1u) ? 0.0f : (Pv[j] == 0.0f) ? Sv[j] : __builtin_fmaf(Pv[j], h, Sv[j]);
+            h = (c + 1 < nchunk) ? hn : h;
         }
     }
 }

@@ -78,6 +78,9 @@ CONV_CASES = [
     (torch.bfloat16, 512, 4, True, [700, 1, 3, 322, 129]),
     (torch.bfloat16, 100, 4, True, [1, 5, 130, 2, 70, 1]),   # D % 8 != 0: per-element path
     (torch.bfloat16, 256, 2, False, [256, 128, 3, 1]),
+    (torch.bfloat16, 102, 4, True, [3, 260, 1, 40]),         # D % 4 != 0: per-element backward too
+    (torch.float32, 33, 2, True, [9, 1, 300, 2]),            # odd D
+    (torch.bfloat16, 520, 4, True, [300, 1, 2, 600, 17]),    # a partial 64-vector group
 ]
 
 
