@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 
 import synth  # noqa: E402
 
+COPY_CALIB_BYTES = 256 << 20
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, vendor figure
 PEAK_FP32_TFLOPS = 157.3  # MI355X fp32 vector, vendor figure (counts packed FP32, which this build does not use)
 
@@ -224,6 +225,9 @@ def main():
     ap.add_argument("--no-layouts", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-channels", type=int, default=1024)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="after timing, run one plain 256 MiB device copy (a known byte count for "
+                         "calibrating hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path has no collectives "
@@ -264,6 +268,15 @@ def main():
                     "traffic": None, "avg_ms": round(ops[dominant], 4), "algo_bytes_per_launch": ab[dominant]}
     log("[bench] per-op ms: " + ", ".join(f"{k} {ops[k]:.3f}" for k in OPS))
     log("[bench] per-op algorithmic GB/s: " + ", ".join(f"{k} {ops_gbs[k]:.0f}" for k in OPS))
+
+    if args.copy_calib:
+        src = torch.empty(COPY_CALIB_BYTES // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {COPY_CALIB_BYTES} bytes read, {COPY_CALIB_BYTES} bytes written")
+        del src, dst
 
     layouts = None
     if not args.no_layouts:

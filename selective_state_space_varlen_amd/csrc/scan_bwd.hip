@@ -44,6 +44,18 @@ template <bool SAFE, bool GATE, typename T, int NS, int BT, typename St>
 __device__ __forceinline__ void bsum_block(const T* lds, const float* __restrict__ bc, int64_t tb, int nt,
                                            const float (&A2)[NS], float (&sr)[NS], float& sdt, float& cdt,
                                            int lane) {
+    // the block's per-lane inputs are read from LDS before the first scalar
+    // load: a wait for LDS data also waits for scalar loads in flight
+    float dtv[BT], gv[BT];
+#pragma unroll
+    for (int k = 0; k < BT; ++k) {
+        dtv[k] = St::get(lds, 0, k, lane);
+        gv[k] = St::get(lds, 2, k, lane);
+        if constexpr (GATE) {
+            const float zz = St::get(lds, 1, k, lane);
+            gv[k] *= zz * sigmoid_fast(zz);
+        }
+    }
     const float* __restrict__ rows = bc + (size_t)tb * 2 * NS + NS;  // C rows
     float cur[NS];
 #pragma unroll
@@ -59,12 +71,8 @@ __device__ __forceinline__ void bsum_block(const T* lds, const float* __restrict
 #pragma unroll
             for (int n = 0; n < NS; ++n) nxt[n] = rows[(k + 1) * 2 * NS + n];
         }
-        const float dt = St::get(lds, 0, k, lane);
-        float g = St::get(lds, 2, k, lane);
-        if constexpr (GATE) {
-            const float zz = St::get(lds, 1, k, lane);
-            g *= zz * sigmoid_fast(zz);
-        }
+        const float dt = dtv[k];
+        const float g = gv[k];
         const float yk = dt - cdt;
         const float tk = sdt + yk;
         cdt = (tk - sdt) - yk;

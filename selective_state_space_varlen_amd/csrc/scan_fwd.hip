@@ -42,6 +42,14 @@ template <bool SAFE, typename T, int NS, int BT, typename St>
 __device__ __forceinline__ void summary_block(const T* lds, const float* __restrict__ bc, int64_t tb, int first,
                                               int nt, const float (&A2)[NS], float (&h)[NS], float& sdt, float& cdt,
                                               int lane) {
+    // the block's per-lane inputs are read from LDS before the first scalar
+    // load: a wait for LDS data also waits for scalar loads in flight
+    float dtv[BT], uv[BT];
+#pragma unroll
+    for (int k = 0; k < BT; ++k) {
+        dtv[k] = St::get(lds, 1, k, lane);
+        uv[k] = St::get(lds, 0, k, lane);
+    }
     const float* __restrict__ rows = bc + (size_t)tb * 2 * NS;
     float cur[NS];
     load_rowv<NS>(rows + (SAFE ? first : 0) * 2 * NS, cur);
@@ -54,8 +62,8 @@ __device__ __forceinline__ void summary_block(const T* lds, const float* __restr
         float nxt[NS];
         const bool more = SAFE ? (k + 1 < nt) : (k + 1 < BT);
         if (more) load_rowv<NS>(rows + (k + 1) * 2 * NS, nxt);
-        const float dt = St::get(lds, 1, k, lane);
-        const float dtu = dt * St::get(lds, 0, k, lane);
+        const float dt = dtv[k];
+        const float dtu = dt * uv[k];
         // compensated sum of delta: the chunk's decay is exp2(A2 * sum delta)
         const float yk = dt - cdt;
         const float tk = sdt + yk;
@@ -179,6 +187,15 @@ template <bool SAFE, bool GATE, typename T, int NS, int BT, typename St>
 __device__ __forceinline__ void out_block(const T* lds, const float* __restrict__ bc, int64_t tb, int nt,
                                           uint32_t heads, const float (&A2)[NS], float (&h)[NS], float Dv, int lane,
                                           T* __restrict__ ob, int D, int d, bool store) {
+    // the block's per-lane inputs are read from LDS before the first scalar
+    // load: a wait for LDS data also waits for scalar loads in flight
+    float dtv[BT], uv[BT], zv[BT];
+#pragma unroll
+    for (int k = 0; k < BT; ++k) {
+        dtv[k] = St::get(lds, 1, k, lane);
+        uv[k] = St::get(lds, 0, k, lane);
+        if constexpr (GATE) zv[k] = St::get(lds, 2, k, lane);
+    }
     const float* __restrict__ rows = bc + (size_t)tb * 2 * NS;
     float cur[2 * NS];
     load_rowv<2 * NS>(rows, cur);
@@ -190,8 +207,8 @@ __device__ __forceinline__ void out_block(const T* lds, const float* __restrict_
         float nxt[2 * NS];
         const bool more = SAFE ? (k + 1 < nt) : (k + 1 < BT);
         if (more) load_rowv<2 * NS>(rows + (k + 1) * 2 * NS, nxt);
-        const float dt = St::get(lds, 1, k, lane);
-        const float uu = St::get(lds, 0, k, lane);
+        const float dt = dtv[k];
+        const float uu = uv[k];
         const float dtu = dt * uu;
         if constexpr (SAFE) reset_if<NS>((heads >> k) & 1u, h);
         float y = 0.0f;
@@ -202,7 +219,7 @@ __device__ __forceinline__ void out_block(const T* lds, const float* __restrict_
         }
         y = __builtin_fmaf(Dv, uu, y);
         if constexpr (GATE) {
-            const float zz = St::get(lds, 2, k, lane);
+            const float zz = zv[k];
             y *= zz * sigmoid_fast(zz);
         }
         if (store) Elt<T>::st(ob, (size_t)(k * D + d), y);
