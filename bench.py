@@ -26,7 +26,7 @@ if ROOT not in sys.path:
 
 import synth  # noqa: E402
 
-COPY_CALIB_BYTES = 256 << 20
+COPY_CALIB_BYTES = 1 << 30
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, vendor figure
 PEAK_FP32_TFLOPS = 157.3  # MI355X fp32 vector, vendor figure (counts packed FP32, which this build does not use)
 
@@ -226,7 +226,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-channels", type=int, default=1024)
     ap.add_argument("--copy-calib", action="store_true",
-                    help="after timing, run one plain 256 MiB device copy (a known byte count for "
+                    help="after timing, run one plain 1 GiB device copy (a known byte count for "
                          "calibrating hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -270,13 +270,17 @@ def main():
     log("[bench] per-op algorithmic GB/s: " + ", ".join(f"{k} {ops_gbs[k]:.0f}" for k in OPS))
 
     if args.copy_calib:
+        # src is written, then a second buffer of the same size pushes it out of
+        # the caches, so the copy (one hipMemcpy device-to-device dispatch)
+        # reads all of src from HBM
         src = torch.empty(COPY_CALIB_BYTES // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        evict = torch.empty_like(src).fill_(2.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: {COPY_CALIB_BYTES} bytes read, {COPY_CALIB_BYTES} bytes written")
-        del src, dst
+        del src, evict, dst
 
     layouts = None
     if not args.no_layouts:

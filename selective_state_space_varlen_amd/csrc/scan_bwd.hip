@@ -139,50 +139,84 @@ __global__ __launch_bounds__(64, 4) void k_scan_bwd_summary(const T* __restrict_
             bsum_block<true, GATE, T, NS, BT, St>(lds, bc, tb, nt, A2, sr, sdt, cdt, lane);
     }
     if (act) {
+        // the decay exp2(A2[n] * sdt) depends on n only through A: keep sdt
+        // (NaN where a head cuts the sub-chunk, i.e. decay 0) per channel
+        Pr[(size_t)c * D + d] = (fh < t1) ? __builtin_nanf("") : sdt;
 #pragma unroll
-        for (int n = 0; n < NS; ++n) {
-            const size_t o = ((size_t)c * NS + n) * D + d;
-            Pr[o] = (fh < t1) ? 0.0f : exp2_fast(A2[n] * sdt);
-            Sr[o] = sr[n];
-        }
+        for (int n = 0; n < NS; ++n) Sr[((size_t)c * NS + n) * D + d] = sr[n];
     }
 }
 
 // ---------------------------------------------------------------------------
-// 2. carries, right to left: cin[c] = carry entering chunk c from chunk c+1
+// 2. carries, right to left over the summary sub-chunks (lc tokens here; 2^logR
+//    per main chunk): cin[m] = carry entering main chunk m from its right, i.e.
+//    the carry entering its last sub-chunk
 // ---------------------------------------------------------------------------
+// Pr holds each sub-chunk's sum of delta per channel (NaN: a head cuts it).
 template <int NS>
 __global__ __launch_bounds__(256) void k_scan_bwd_carry(const float* __restrict__ Pr, const float* __restrict__ Sr,
+                                                        const float* __restrict__ A,
                                                         const int32_t* __restrict__ pos, float* __restrict__ cin,
-                                                        int D, int64_t nchunk, int lc) {
+                                                        int D, int64_t nchunk, int lc, int logR) {
     const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t ND = (int64_t)NS * D;
     const bool act = i0 < ND;
     const int64_t i = act ? i0 : ND - 1;  // lanes past the end run along (ballots need the wave) but store nothing
-    // the summaries of kB chunks are loaded before the chain walks through them
+    // The summaries of kB chunks are loaded before the chain walks through
+    // them, and the next kB are loaded while it does. Lane j < kB also loads
+    // the position at the start of chunk cb - j (head test). Addresses step by
+    // a fixed stride: the chain runs one wave per SIMD, so per-step index
+    // arithmetic is not hidden by other waves.
     constexpr int kB = 16;
     const int lane = threadIdx.x % kWave;
-    float cc = 0.0f;
-    for (int64_t cb = nchunk - 1; cb >= 0; cb -= kB) {
-        // bit j: chunk cb - j >= 1 starts at a head
+    struct Batch {
+        float P[kB], S[kB];
+        int32_t hp;  // pos at the start of chunk cb - lane (lanes < kB, chunks >= 1)
+    };
+    const int dch = (int)(i % D);
+    const float A2 = A[(size_t)dch * NS + (int)(i / D)] * kLog2e;
+    auto load = [&](Batch& b, int64_t cb) {
         const int64_t cj = cb - lane;
-        const uint64_t heads = __ballot(lane < kB && cj >= 1 && pos[(cj >= 1 ? cj : 0) * lc] == 0);
-        float Pv[kB], Sv[kB];
+        b.hp = (lane < kB && cj >= 1) ? pos[cj * lc] : 1;
+        const float* p = Pr + (size_t)cb * D + dch;
+        const float* q = Sr + (size_t)cb * ND + i;
 #pragma unroll
         for (int j = 0; j < kB; ++j) {
-            const int64_t c = cb - j;
-            const int64_t cl = c > 0 ? c : 0;  // c <= 0 loads chunk 0 and is not combined
-            Pv[j] = Pr[(size_t)cl * ND + i];
-            Sv[j] = Sr[(size_t)cl * ND + i];
+            if (cb - j >= 0) {
+                b.P[j] = *p;
+                b.S[j] = *q;
+            } else {
+                b.P[j] = 0.0f;
+                b.S[j] = 0.0f;
+            }
+            p -= D;
+            q -= ND;
         }
+    };
+    float cc = 0.0f;
+    // main chunk c >> logR is entered from the right through its last
+    // sub-chunk; the stores walk the main chunks from the last one down
+    float* cp = cin + (size_t)((nchunk - 1) >> logR) * ND + i;
+    const int64_t rmask = ((int64_t)1 << logR) - 1;
+    Batch cur, nxt;
+    load(cur, nchunk - 1);
+    for (int64_t cb = nchunk - 1; cb >= 0; cb -= kB) {
+        if (cb - kB >= 0) load(nxt, cb - kB);
+        const uint64_t heads = __ballot(cur.hp == 0);  // bit j: chunk cb - j >= 1 starts at a head
 #pragma unroll
         for (int j = 0; j < kB; ++j) {
             const int64_t c = cb - j;
-            if (act && c >= 0) cin[(size_t)c * ND + i] = cc;
+            if (c >= 0 && (((c + 1) & rmask) == 0 || c == nchunk - 1)) {
+                if (act) *cp = cc;
+                cp -= ND;
+            }
             // select at heads, as in the forward
-            const float cn = ((heads >> j) & 1u) ? 0.0f : (Pv[j] == 0.0f) ? Sv[j] : __builtin_fmaf(Pv[j], cc, Sv[j]);
+            const float tj = cur.P[j];
+            const float Pj = (tj != tj) ? 0.0f : exp2_fast(A2 * tj);
+            const float cn = ((heads >> j) & 1u) ? 0.0f : (Pj == 0.0f) ? cur.S[j] : __builtin_fmaf(Pj, cc, cur.S[j]);
             cc = (c >= 1) ? cn : cc;
         }
+        cur = nxt;
     }
 }
 
@@ -551,25 +585,27 @@ static int scan_bwd_launch(const void* u, const void* delta, const float* A, con
     const ScanWs L = scan_ws_layout(T_, D, NS);
     const int lc = bwd_chunk_len(T_, D, NS);
     const int64_t nchunk = (T_ + lc - 1) / lc;
-    const dim3 grid((unsigned)(L.ngroup * nchunk));  // summary kernel: 64 channels per wave
+    const int ls = bwd_sum_len(T_, D, NS);  // summary sub-chunk: lc = 2^logR ls
+    const int logR = __builtin_ctz((unsigned)(lc / ls));
+    const dim3 grid((unsigned)(L.ngroup * L.nsum));  // summary kernel: 64 channels per wave
     const int64_t ND = (int64_t)NS * D;
     const int vec = stage_vec_ok<T>(D, {u, delta, z, dout}) ? 1 : 0;
     k_bc_to_f32<T, NS><<<(unsigned)((T_ * 2 * NS + 255) / 256), 256, 0, s>>>((const T*)B, (const T*)C, ws + L.bc,
                                                                             T_);
     SSMP_LAUNCH_CHECK();
-    if (nchunk > 1) {
+    if (L.nsum > 1) {
         if (z)
             k_scan_bwd_summary<T, NS, true><<<grid, kWave, 0, s>>>((const T*)delta, A, ws + L.bc, (const T*)z,
                                                                    (const T*)dout, pos, ws + L.Pr, ws + L.Sr, T_, D,
-                                                                   vec, lc);
+                                                                   vec, ls);
         else
             k_scan_bwd_summary<T, NS, false><<<grid, kWave, 0, s>>>((const T*)delta, A, ws + L.bc, nullptr,
                                                                     (const T*)dout, pos, ws + L.Pr, ws + L.Sr, T_, D,
-                                                                    vec, lc);
+                                                                    vec, ls);
         SSMP_LAUNCH_CHECK();
     }
-    k_scan_bwd_carry<NS><<<(unsigned)((ND + 255) / 256), 256, 0, s>>>(ws + L.Pr, ws + L.Sr, pos, ws + L.cin, D,
-                                                                      nchunk, lc);
+    k_scan_bwd_carry<NS><<<(unsigned)((ND + 255) / 256), 256, 0, s>>>(ws + L.Pr, ws + L.Sr, A, pos, ws + L.cin,
+                                                                      D, L.nsum, ls, logR);
     SSMP_LAUNCH_CHECK();
     BwdArgs<T> a;
     a.u = (const T*)u; a.delta = (const T*)delta; a.A = A; a.bc = ws + L.bc; a.Dskip = Dskip;

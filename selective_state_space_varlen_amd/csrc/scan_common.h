@@ -40,16 +40,25 @@ inline int scan_chunk_len(int64_t T, int D, int chw) {
 }
 inline int fwd_chunk_len(int64_t T, int D) { return scan_chunk_len(T, D, kWave); }
 inline int bwd_chunk_len(int64_t T, int D, int N) { return scan_chunk_len(T, D, kWave / bwd_lanes_per_channel(N)); }
+// The backward's reverse-carry summaries run over sub-chunks of the main
+// kernel's chunks (down to kLCMin tokens): a summary wave's work depends on
+// where the heads fall, and more, shorter waves even it out across the SIMDs.
+constexpr int kBwdSumSplit = 4;
+inline int bwd_sum_len(int64_t T, int D, int N) {
+    const int ls = bwd_chunk_len(T, D, N) / kBwdSumSplit;
+    return ls < kLCMin ? kLCMin : ls;
+}
 
 struct ScanWs {
     int64_t nck;      // checkpoint slots: slot j holds the state entering token j*kCK
     int64_t nchunk;   // chunks (the larger count of the forward's and the backward's chunking)
+    int64_t nsum;     // backward summary sub-chunks
     int64_t ngroup;   // channel groups of 64
     // offsets in floats from the workspace base
     size_t ckpt;      // [nck][N][D]      forward -> backward
     size_t bc;        // [T][2N]          fp32 copy of the B and C rows (each pass makes its own)
-    size_t P, S;      // [nchunk][N][D]   forward: chunk decay and local end state
-    size_t Pr, Sr;    // [nchunk][N][D]   backward: reverse-carry summaries
+    size_t P, S;      // forward: P [nchunk][D] sum of delta (NaN: cut by a head), S [nchunk][N][D] local end state
+    size_t Pr, Sr;    // backward, per summary sub-chunk: Pr [nsum][D] as P, Sr [nsum][N][D] reverse carry
     size_t cin;       // [nchunk][N][D]   backward: carry entering each chunk from the right
     size_t dApart;    // [nchunk][N][D]
     size_t dDpart;    // [nchunk][D]
@@ -64,6 +73,8 @@ inline ScanWs scan_ws_layout(int64_t T, int D, int N) {
         const int64_t lf = fwd_chunk_len(T, D), lb = bwd_chunk_len(T, D, N);
         const int64_t nf = (T + lf - 1) / lf, nb = (T + lb - 1) / lb;
         w.nchunk = nf > nb ? nf : nb;
+        const int64_t ls = bwd_sum_len(T, D, N);
+        w.nsum = (T + ls - 1) / ls;
     }
     w.ngroup = (D + kWave - 1) / kWave;
     const size_t ND = (size_t)N * D;
@@ -72,10 +83,10 @@ inline ScanWs scan_ws_layout(int64_t T, int D, int N) {
     w.ckpt = off; off = up(off + (size_t)w.nck * ND);
     w.bc = off; off = up(off + (size_t)T * 2 * N);
     const size_t scratch = off;
-    w.P = scratch; w.S = up(w.P + (size_t)w.nchunk * ND);
+    w.P = scratch; w.S = up(w.P + (size_t)w.nchunk * D);
     const size_t fwd_end = up(w.S + (size_t)w.nchunk * ND);
-    w.Pr = scratch; w.Sr = up(w.Pr + (size_t)w.nchunk * ND);
-    w.cin = up(w.Sr + (size_t)w.nchunk * ND);
+    w.Pr = scratch; w.Sr = up(w.Pr + (size_t)w.nsum * D);
+    w.cin = up(w.Sr + (size_t)w.nsum * ND);
     w.dApart = up(w.cin + (size_t)w.nchunk * ND);
     w.dDpart = up(w.dApart + (size_t)w.nchunk * ND);
     w.dBC = up(w.dDpart + (size_t)w.nchunk * D);

@@ -16,7 +16,9 @@
 // the multiplier P zeroed once a head is passed):
 //   1. summary: per chunk, from its last head (or its start) to its end,
 //      S = end state from zero and P = product of decays (0 if a head was
-//      seen). Skipped when the next chunk starts with a head.
+//      seen). P[n] = exp2(A2[n] sum delta) is kept as the channel's sum of
+//      delta (NaN for 0), N times fewer bytes. Skipped when the next chunk
+//      starts with a head.
 //   2. carry: per (n, d), a sequential pass over chunks gives the state
 //      entering each chunk.
 //   3. output: each chunk replays its tokens from that state, writes out and
@@ -133,50 +135,83 @@ __global__ __launch_bounds__(64, 4) void k_scan_fwd_summary(const T* __restrict_
             summary_block<true, T, NS, BT, St>(lds, bc, tb, first, nt, A2, h, sdt, cdt, lane);
     }
     if (act) {
+        // the chunk's decay exp2(A2[n] * sdt) depends on n only through A: keep
+        // sdt (NaN where a head cuts the chunk, i.e. decay 0) per channel
+        P[(size_t)c * D + d] = has_head ? __builtin_nanf("") : sdt;
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
             const size_t o = ((size_t)c * NS + n) * D + d;
-            P[o] = has_head ? 0.0f : exp2_fast(A2[n] * sdt);
             S[o] = h[n];
         }
     }
 }
 
 // State entering each chunk, written to the checkpoint slot of its first token.
+// P holds each chunk's sum of delta per channel (NaN: a head cuts the chunk).
 template <int NS>
 __global__ __launch_bounds__(256) void k_scan_fwd_carry(const float* __restrict__ P, const float* __restrict__ S,
+                                                        const float* __restrict__ A,
                                                         const int32_t* __restrict__ pos, float* __restrict__ ckpt,
                                                         int64_t T_, int D, int64_t nchunk, int lc) {
     const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // n*D + d
     const int64_t ND = (int64_t)NS * D;
     const bool act = i0 < ND;
     const int64_t i = act ? i0 : ND - 1;  // lanes past the end run along (ballots need the wave) but store nothing
-    // the summaries of kB chunks are loaded before the chain walks through them;
-    // chunk c hands its state on iff chunk c + 1 exists ((c + 1) lc < T)
+    // The summaries of kB chunks are loaded before the chain walks through
+    // them, and the next kB are loaded while it does. Chunk c hands its state
+    // on iff chunk c + 1 exists ((c + 1) lc < T); lane j < kB also loads the
+    // position at the start of chunk cb + j + 1 (head test). Addresses step
+    // by a fixed stride: the chain runs one wave per SIMD, so per-step index
+    // arithmetic is not hidden by other waves.
     constexpr int kB = 16;
     const int lane = threadIdx.x % kWave;
-    float h = 0.0f;
-    for (int64_t cb = 0; cb < nchunk; cb += kB) {
-        // bit j: chunk cb + j + 1 exists and starts at a head
+    struct Batch {
+        float P[kB], S[kB];
+        int32_t hp;
+    };
+    const int dch = (int)(i % D);
+    const float A2 = A[(size_t)dch * NS + (int)(i / D)] * kLog2e;
+    auto load = [&](Batch& b, int64_t cb) {
         const int64_t tn = (cb + lane + 1) * lc;
-        const uint64_t heads = __ballot(lane < kB && tn < T_ && pos[tn < T_ ? tn : 0] == 0);
-        float Pv[kB], Sv[kB];
+        b.hp = (lane < kB && tn < T_) ? pos[tn] : 1;
+        const float* p = P + (size_t)cb * D + dch;
+        const float* q = S + (size_t)cb * ND + i;
 #pragma unroll
         for (int j = 0; j < kB; ++j) {
-            const int64_t c = cb + j;
-            const int64_t cl = c + 1 < nchunk ? c : 0;  // chunks that hand nothing on load chunk 0
-            Pv[j] = P[(size_t)cl * ND + i];
-            Sv[j] = S[(size_t)cl * ND + i];
+            if (cb + j + 1 < nchunk) {
+                b.P[j] = *p;
+                b.S[j] = *q;
+            } else {
+                b.P[j] = 0.0f;
+                b.S[j] = 0.0f;
+            }
+            p += D;
+            q += ND;
         }
+    };
+    float h = 0.0f;
+    float* kp = ckpt + i;  // checkpoint slot of chunk c's first token
+    const size_t kstride = (size_t)(lc / kCK) * ND;
+    Batch cur, nxt;
+    load(cur, 0);
+    for (int64_t cb = 0; cb < nchunk; cb += kB) {
+        if (cb + kB < nchunk) load(nxt, cb + kB);
+        const uint64_t heads = __ballot(cur.hp == 0);  // bit j: chunk cb + j + 1 starts at a head
 #pragma unroll
         for (int j = 0; j < kB; ++j) {
             const int64_t c = cb + j;
-            if (act && c < nchunk) ckpt[(size_t)(c * (lc / kCK)) * ND + i] = h;
-            // P == 0 marks a chunk holding a head: select, so that a
+            if (c < nchunk) {
+                if (act) *kp = h;
+                kp += kstride;
+            }
+            // decay 0 marks a chunk holding a head: select, so that a
             // non-finite state before the head cannot leak through 0 * h
-            const float hn = ((heads >> j) & 1u) ? 0.0f : (Pv[j] == 0.0f) ? Sv[j] : __builtin_fmaf(Pv[j], h, Sv[j]);
+            const float tj = cur.P[j];
+            const float Pj = (tj != tj) ? 0.0f : exp2_fast(A2 * tj);
+            const float hn = ((heads >> j) & 1u) ? 0.0f : (Pj == 0.0f) ? cur.S[j] : __builtin_fmaf(Pj, h, cur.S[j]);
             h = (c + 1 < nchunk) ? hn : h;
         }
+        cur = nxt;
     }
 }
 
@@ -297,8 +332,8 @@ static int scan_fwd_launch(const void* u, const void* delta, const float* A, con
         SSMP_LAUNCH_CHECK();
     }
     const int64_t ND = (int64_t)NS * D;
-    k_scan_fwd_carry<NS><<<(unsigned)((ND + 255) / 256), 256, 0, s>>>(ws + L.P, ws + L.S, pos, ws + L.ckpt, T_, D,
-                                                                      nchunk, lc);
+    k_scan_fwd_carry<NS><<<(unsigned)((ND + 255) / 256), 256, 0, s>>>(ws + L.P, ws + L.S, A, pos, ws + L.ckpt, T_,
+                                                                      D, nchunk, lc);
     SSMP_LAUNCH_CHECK();
     if (z)
         k_scan_fwd_out<T, NS, true><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, ws + L.bc, Dskip,
