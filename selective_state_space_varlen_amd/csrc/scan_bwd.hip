@@ -20,11 +20,10 @@
 // which one forward sweep over the chunk's leading tokens yields. A
 // sequential pass over chunks (right to left) turns these into the carry
 // entering each chunk. The main kernel then walks each chunk backwards in
-// kCK-token blocks (inputs staged through LDS, the next block in flight): it
-// restarts from the forward's checkpoint at the block start, rebuilds the
-// states at kK-token sub-chunk starts (kept in LDS), and for each sub-chunk
-// replays kK tokens with their states and decays held in VGPRs before running
-// the reverse step over them. dB and dC (sums over channels) are reduced
+// kBB-token blocks (inputs staged through LDS, the next block in flight); each
+// kK-token sub-chunk restarts from the forward's checkpoint at its first token
+// and replays its tokens with their states held in VGPRs before running the
+// reverse step over them. dB and dC (sums over channels) are reduced
 // across each wave and then across the workgroup's waves through LDS, and
 // written per workgroup channel group; dA and dDskip
 // are written per chunk; small kernels finish both sums in a fixed order, so
@@ -282,7 +281,7 @@ __device__ __forceinline__ void bwd_replay(const T* lds, const float* bcl, int k
 }
 
 // Per-block outputs: du, ddelta, dz rows (dtype T) and the wave's per-token
-// dB/dC sums (LDS, [kCK][2NS]).
+// dB/dC sums (LDS, [kBB][2NS]).
 template <typename T>
 struct BwdRows {
     T* du;
@@ -355,7 +354,7 @@ __device__ __forceinline__ void bwd_reverse(const T* lds, const float* bcl, floa
         const float ddv = __builtin_fmaf(uu, sumB, sumAr * kLn2);
         dDacc = __builtin_fmaf(gg, uu, dDacc);
         // both lanes of a pair hold the same values and store the same bytes
-        const uint32_t e = (uint32_t)(k * D + d);  // < kCK * D, fits 32 bits
+        const uint32_t e = (uint32_t)(k * D + d);  // < kBB * D, fits 32 bits
         if (full || act) {
             Elt<T>::st(rows.du, e, duv);
             Elt<T>::st(rows.ddelta, e, ddv);
@@ -400,15 +399,13 @@ __global__ __launch_bounds__(kWave * WV, 2) void k_scan_bwd_main(BwdArgs<T> p) {
     constexpr int CW = kWave / LPC;   // channels per wave
     static_assert(NH * LPC == NS && (LPC == 1 || LPC == 2), "lane split");
     static_assert(CW * WV >= kWave, "dB/dC partial rows are sized for groups of at least 64 channels");
-    using St = Stager<T, 4, kCK, CW>;  // u, delta, z, dout
-    constexpr int NSUB = kCK / kK;
+    using St = Stager<T, 4, kBB, CW>;  // u, delta, z, dout
     constexpr int NT = kWave * WV;     // threads
     constexpr int BCW = 2 * NS;        // dB/dC values per token
     __shared__ __attribute__((aligned(16))) T lds[WV][St::kElems];
-    __shared__ __attribute__((aligned(16))) float bcl[kCK * BCW];  // B/C rows of the block
-    __shared__ float sub[WV][NSUB > 1 ? NSUB - 1 : 1][NH][kWave];
+    __shared__ __attribute__((aligned(16))) float bcl[kBB * BCW];  // B/C rows of the block
     __shared__ __attribute__((aligned(16))) float red[WV][2 * NH][kRedStride];
-    __shared__ float blk[WV][kCK * BCW];  // per-wave dB/dC sums of the block's tokens
+    __shared__ float blk[WV][kBB * BCW];  // per-wave dB/dC sums of the block's tokens
 
     const int tid = threadIdx.x;
     const int wv = tid / kWave;
@@ -442,14 +439,14 @@ __global__ __launch_bounds__(kWave * WV, 2) void k_scan_bwd_main(BwdArgs<T> p) {
     float dDacc = 0.0f;
     const T* const src[4] = {p.u, p.delta, GATE ? p.z : p.u, p.dout};
 
-    // B/C rows of a block: kCK * 2NS floats, fetched with the block's inputs
+    // B/C rows of a block: kBB * 2NS floats, fetched with the block's inputs
     // by the first BCV threads of the workgroup
-    constexpr int BCV = kCK * BCW / 4;                    // float4 pieces
+    constexpr int BCV = kBB * BCW / 4;                    // float4 pieces
     constexpr int BCP = (BCV + NT - 1) / NT;              // pieces per thread
     float4 bcr[BCP];
     auto fetch_bc = [&](int64_t tb) {
         const float4* srcv = reinterpret_cast<const float4*>(p.bc + (size_t)tb * BCW);
-        const int64_t lim = ((p.T_ - tb < kCK) ? (p.T_ - tb) : kCK) * BCW / 4;
+        const int64_t lim = ((p.T_ - tb < kBB) ? (p.T_ - tb) : kBB) * BCW / 4;
 #pragma unroll
         for (int q = 0; q < BCP; ++q) {
             const int idx = q * NT + tid;
@@ -464,59 +461,49 @@ __global__ __launch_bounds__(kWave * WV, 2) void k_scan_bwd_main(BwdArgs<T> p) {
         }
     };
 
-    const int64_t nblk = (t1 - t0 + kCK - 1) / kCK;
+    // Each sub-chunk restarts from the checkpoint at its first token; the
+    // next sub-chunk's state (kK tokens earlier) is loaded while this one runs.
+    auto load_state = [&](int64_t ts, float (&hs)[NH]) {
+        const float* hp = p.ckpt + (size_t)(ts / kCK) * ND;
+#pragma unroll
+        for (int i = 0; i < NH; ++i) hs[i] = act ? hp[(size_t)(n0 + i) * D + dd] : 0.0f;
+    };
+
+    const int64_t nblk = (t1 - t0 + kBB - 1) / kBB;
     St st;
+    float hn[NH];
     {
-        const int64_t tl0 = t0 + (nblk - 1) * kCK;
+        const int64_t tl0 = t0 + (nblk - 1) * kBB;
         st.fetch(src, tl0, p.T_, D, g, lane, p.vec);
         fetch_bc(tl0);
+        load_state(tl0 + ((t1 - tl0 - 1) / kK) * kK, hn);  // last sub-chunk of the chunk
     }
     for (int64_t jb = nblk - 1; jb >= 0; --jb) {
-        const int64_t tb0 = t0 + jb * kCK;
-        const int nb = (int)(((tb0 + kCK < t1) ? tb0 + kCK : t1) - tb0);  // tokens in this block
+        const int64_t tb0 = t0 + jb * kBB;
+        const int nb = (int)(((tb0 + kBB < t1) ? tb0 + kBB : t1) - tb0);  // tokens in this block
         const int nsub = (nb + kK - 1) / kK;
-        const float* hb = p.ckpt + (size_t)(tb0 / kCK) * ND;
-        const uint32_t heads = block_heads<kCK>(p.pos, tb0, p.T_, lane);
+        const uint32_t heads = block_heads<kBB>(p.pos, tb0, p.T_, lane);
         __syncthreads();  // every wave is done with the previous block's bcl and blk
         st.commit(mylds, src, tb0, p.T_, D, g, lane, p.vec);
         commit_bc();
         __syncthreads();
         if (jb > 0) {
-            st.fetch(src, tb0 - kCK, p.T_, D, g, lane, p.vec);
-            fetch_bc(tb0 - kCK);
+            st.fetch(src, tb0 - kBB, p.T_, D, g, lane, p.vec);
+            fetch_bc(tb0 - kBB);
         }
         const BwdRows<T> rows{p.du + (size_t)tb0 * D, p.ddelta + (size_t)tb0 * D,
                               GATE ? p.dz + (size_t)tb0 * D : nullptr, blk[wv]};
-
-        // states entering sub-chunks 1..nsub-1 (those sub-chunks are all full)
-        if (nsub > 1) {
-            float h[NH];
-#pragma unroll
-            for (int i = 0; i < NH; ++i) h[i] = act ? hb[(size_t)(n0 + i) * D + dd] : 0.0f;
-            for (int sc = 1; sc < nsub; ++sc) {
-                float hh[kK][NH], yk[kK];
-                if (heads == 0)
-                    bwd_replay<false, NS, LPC, St>(mylds, bcl, (sc - 1) * kK, kK, 0u, ch, n0, A2, h, hh, yk, Dv);
-                else
-                    bwd_replay<true, NS, LPC, St>(mylds, bcl, (sc - 1) * kK, kK, heads, ch, n0, A2, h, hh, yk, Dv);
-#pragma unroll
-                for (int i = 0; i < NH; ++i) sub[wv][sc - 1][i][lane] = h[i];
-            }
-        }
 
         for (int sc = nsub - 1; sc >= 0; --sc) {
             const int kb = sc * kK;  // first token of the sub-chunk within the block
             const int ns = (nb - kb < kK) ? nb - kb : kK;
             float h[NH], hin[NH], hh[kK][NH], yk[kK];
-            if (sc == 0) {
 #pragma unroll
-                for (int i = 0; i < NH; ++i) h[i] = act ? hb[(size_t)(n0 + i) * D + dd] : 0.0f;
-            } else {
-#pragma unroll
-                for (int i = 0; i < NH; ++i) h[i] = sub[wv][sc - 1][i][lane];
+            for (int i = 0; i < NH; ++i) {
+                h[i] = hn[i];
+                hin[i] = hn[i];
             }
-#pragma unroll
-            for (int i = 0; i < NH; ++i) hin[i] = h[i];
+            if (tb0 + kb - kK >= t0) load_state(tb0 + kb - kK, hn);
             const uint32_t sub_heads = (heads >> kb) & ((1u << kK) - 1u);
             if (sub_heads == 0 && ns == kK) {
                 bwd_replay<false, NS, LPC, St>(mylds, bcl, kb, kK, 0u, ch, n0, A2, h, hh, yk, Dv);

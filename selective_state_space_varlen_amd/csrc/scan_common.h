@@ -11,14 +11,17 @@ namespace ssmp {
 // affine carry h_out = P h_in + S (P = 0 once the chunk holds a head). Every
 // chunk whose successor continues a sequence costs a summary pass, so chunks
 // are as long as the grid allows: the longest power of two (64 .. 2048 tokens)
-// that still gives kMinWaves waves. Tokens are staged in blocks of kCK; the
-// forward stores the state at every block start and the backward restarts
-// from those, replaying kK-token sub-chunks whose states stay in registers.
-constexpr int kCK = 16;
+// that still gives kMinWaves waves. The forward stores the state entering
+// every kCK-th token; the backward stages its inputs in kBB-token blocks and
+// restarts each kK-token sub-chunk from its checkpoint, replaying it with the
+// states in registers. Checkpoints cost 16 B of HBM per (t, d) each way, which
+// the ALU-bound scans absorb, and spare the backward a second replay pass.
+constexpr int kCK = 4;
 constexpr int kK = 4;
+constexpr int kBB = 16;
 constexpr int kLCMin = 64, kLCMax = 2048;
 constexpr int64_t kMinWaves = 8192;  // eight per SIMD on 256 CUs: enough to hide load latency
-static_assert(kLCMin % kCK == 0 && kCK % kK == 0, "tiling");
+static_assert(kK == kCK && kBB % kK == 0 && kLCMin % kBB == 0, "tiling");
 
 // channels per wave: the forward gives each channel one lane; the backward
 // two lanes (d_state >= 4) or one
@@ -140,7 +143,7 @@ __device__ __forceinline__ void load_bc(const float* __restrict__ bc, int64_t t,
 
 // Head flags of the BT tokens of a block as a wave-uniform bit mask (bit k:
 // token tb+k starts a sequence). Lanes k < BT each read one position.
-template <int BT = kCK>
+template <int BT = kBB>
 __device__ __forceinline__ uint32_t block_heads(const int32_t* __restrict__ pos, int64_t tb, int64_t T_, int lane) {
     const int64_t t = tb + lane;
     const bool f = (lane < BT) && (t < T_) && pos[t] == 0;
@@ -164,7 +167,7 @@ __device__ __forceinline__ void reset_if(bool head, float (&h)[NS]) {
 // multiple of 16 / sizeof(T)) the block is fetched into registers with
 // 16-byte loads one block ahead, and committed to LDS when the block starts;
 // otherwise each lane copies its own elements at commit time.
-template <typename T, int R, int BT = kCK, int CW = kWave>
+template <typename T, int R, int BT = kBB, int CW = kWave>
 struct Stager {
     static constexpr int EPV = 16 / (int)sizeof(T);      // elements per 16-byte piece
     static constexpr int PPR = CW / EPV;                  // pieces per row of CW channels

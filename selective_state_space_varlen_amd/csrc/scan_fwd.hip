@@ -22,13 +22,13 @@
 //   2. carry: per (n, d), a sequential pass over chunks gives the state
 //      entering each chunk.
 //   3. output: each chunk replays its tokens from that state, writes out and
-//      stores the state at every block start for the backward.
+//      stores the state entering every kCK-th token for the backward.
 #include "scan_common.h"
 
 namespace ssmp {
 
 constexpr int kFwdBlock = 8;  // tokens per staged block in the forward kernels
-static_assert(kCK % kFwdBlock == 0, "checkpoints fall on block starts");
+static_assert(kFwdBlock % kCK == 0, "a block holds whole checkpoint intervals");
 
 // B (and C) rows of BT tokens from the fp32 copy, prefetched one token ahead
 // so the scalar loads of token k+1 overlap the arithmetic of token k.
@@ -218,10 +218,14 @@ __global__ __launch_bounds__(256) void k_scan_fwd_carry(const float* __restrict_
 // Output recurrence over one block of BT tokens. SAFE blocks may end early
 // (nt < BT) and may hold heads; fast blocks are full and head-free, so their
 // tokens run straight through with the next token's B/C rows in flight.
+// The state entering every kCK-th token goes to its checkpoint slot (ck:
+// the slot of the block's first token), except at the chunk start (skip0),
+// whose slot the carry pass wrote.
 template <bool SAFE, bool GATE, typename T, int NS, int BT, typename St>
 __device__ __forceinline__ void out_block(const T* lds, const float* __restrict__ bc, int64_t tb, int nt,
                                           uint32_t heads, const float (&A2)[NS], float (&h)[NS], float Dv, int lane,
-                                          T* __restrict__ ob, int D, int d, bool store) {
+                                          T* __restrict__ ob, int D, int d, bool store, float* __restrict__ ck,
+                                          size_t ND, bool skip0, bool act) {
     // the block's per-lane inputs are read from LDS before the first scalar
     // load: a wait for LDS data also waits for scalar loads in flight
     float dtv[BT], uv[BT], zv[BT];
@@ -238,6 +242,10 @@ __device__ __forceinline__ void out_block(const T* lds, const float* __restrict_
     for (int k = 0; k < BT; ++k) {
         if constexpr (SAFE) {
             if (k >= nt) break;
+        }
+        if (k % kCK == 0 && act && !(k == 0 && skip0)) {
+#pragma unroll
+            for (int n = 0; n < NS; ++n) ck[(size_t)(k / kCK) * ND + (size_t)n * D + d] = h[n];
         }
         float nxt[2 * NS];
         const bool more = SAFE ? (k + 1 < nt) : (k + 1 < BT);
@@ -296,10 +304,6 @@ __global__ __launch_bounds__(64, 4) void k_scan_fwd_out(const T* __restrict__ u,
     St st;
     st.fetch(src, t0, T_, D, tl.g, lane, vec);
     for (int64_t tb = t0; tb < t1; tb += BT) {
-        if (tb != t0 && (tb % kCK) == 0 && act) {
-#pragma unroll
-            for (int n = 0; n < NS; ++n) ckpt[(size_t)(tb / kCK) * ND + (size_t)n * D + d] = h[n];
-        }
         const uint32_t heads = block_heads<BT>(pos, tb, T_, lane);
         wave_sync();
         st.commit(lds, src, tb, T_, D, tl.g, lane, vec);
@@ -307,10 +311,13 @@ __global__ __launch_bounds__(64, 4) void k_scan_fwd_out(const T* __restrict__ u,
         if (tb + BT < t1) st.fetch(src, tb + BT, T_, D, tl.g, lane, vec);
         const int nt = (int)((tb + BT < t1) ? BT : t1 - tb);
         T* __restrict__ ob = out + (size_t)tb * D;
+        float* __restrict__ ck = ckpt + (size_t)(tb / kCK) * ND;
         if (heads == 0 && nt == BT)
-            out_block<false, GATE, T, NS, BT, St>(lds, bc, tb, BT, 0u, A2, h, Dv, lane, ob, D, d, store);
+            out_block<false, GATE, T, NS, BT, St>(lds, bc, tb, BT, 0u, A2, h, Dv, lane, ob, D, d, store, ck, ND,
+                                                  tb == t0, act);
         else
-            out_block<true, GATE, T, NS, BT, St>(lds, bc, tb, nt, heads, A2, h, Dv, lane, ob, D, d, store);
+            out_block<true, GATE, T, NS, BT, St>(lds, bc, tb, nt, heads, A2, h, Dv, lane, ob, D, d, store, ck, ND,
+                                                 tb == t0, act);
     }
 }
 
