@@ -7,13 +7,25 @@
 // stops dx and dweight the same way, taking the reverse position from the
 // position index W-1 tokens ahead.
 //
-// Both kernels stream HBM: a thread owns V adjacent channels (one 16-byte
-// vector) and a run of RT consecutive tokens, slides a W-token window of x in
-// registers, and reads the per-token position once per token (the same
-// address for the whole wave). Consecutive lanes own consecutive vectors, so
-// a wave reads 1 KiB of one row per load. Tokens are taken in batches of kG
-// whose loads are all issued before the first is used, so each wave keeps
-// kG (forward) or 2 kG (backward) row loads in flight.
+// Both kernels stream HBM: a thread owns V adjacent channels (one vector
+// load) and runs of consecutive tokens. Consecutive lanes own consecutive
+// vectors, so a wave reads 1 KiB (forward) or 512 B (backward) of one row per
+// load.
+//
+// Forward: runs of kRun tokens whose row loads (the run's and its W-1 halo
+// rows) are all issued before the first is used. A thread loads its taps and
+// bias once and takes kFwdPasses runs, one per pass over the tensor, so the
+// waves running at any one time cover a narrow band of rows. Measured on
+// MI355X, that streams at about the rate of a plain copy; long per-thread
+// runs spread the concurrent accesses over ~100 MB and halve it, and loading
+// the taps for every short run costs as much again. Halo rows are read again
+// by the neighbouring run and mostly hit in L2.
+//
+// Backward: the same runs and passes; a run also recomputes the activation
+// gradient of the W - 1 tokens after it, which its dx rows need, and its
+// workgroup sums the taps' and bias's gradients over its waves.
+#include <type_traits>
+
 #include "common.h"
 
 namespace ssmp {
@@ -57,11 +69,10 @@ struct Access {
 template <typename T> constexpr int kFwdV = 16 / (int)sizeof(T);
 template <typename T> constexpr int kBwdV = 8 / (int)sizeof(T);
 
-constexpr int kConvFwdRun = 32;   // tokens per thread, forward
-constexpr int kConvBwdRun = 64;   // tokens per thread, backward
-constexpr int kConvBwdRuns = 4;   // runs per backward workgroup (summed there before the partials)
-constexpr int kG = 8;             // tokens per load batch
-static_assert(kConvFwdRun % kG == 0 && kConvBwdRun % kG == 0, "runs hold whole batches");
+constexpr int kRun = 8;            // forward: tokens per run
+constexpr int kFwdPasses = 4;      // forward: runs per thread, one per pass
+constexpr int kConvBwdRuns = 4;    // backward: waves per workgroup, on consecutive runs
+constexpr int kConvBwdGroups = 128; // backward: workgroups per 64 vectors (a pass covers 512 runs)
 
 // taps used at token t: k <= kmax (pos[t] caps the look-back at the head)
 __device__ __forceinline__ int conv_kmax(int32_t pos_t, int64_t t, int W) {
@@ -74,61 +85,70 @@ __device__ __forceinline__ int conv_kmax(int32_t pos_t, int64_t t, int W) {
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
-template <typename T, int V>
+template <typename T, int V, int W>
 __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const float* __restrict__ w,
                                                   const float* __restrict__ b, const int32_t* __restrict__ pos,
-                                                  T* __restrict__ u, int64_t T_, int D, int W, int silu) {
+                                                  T* __restrict__ u, int64_t T_, int D, int silu) {
     using A = Access<T, V>;
     const int nvec = D / V;
+    const int64_t nrun = (T_ + kRun - 1) / kRun;
+    const int64_t S = (nrun + kFwdPasses - 1) / kFwdPasses;  // runs per pass
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int cv = (int)(gid % nvec);
-    const int64_t t0 = (gid / nvec) * kConvFwdRun;
-    if (t0 >= T_) return;
-    const int64_t t1 = (t0 + kConvFwdRun < T_) ? t0 + kConvFwdRun : T_;
+    const int64_t r0 = gid / nvec;
+    if (r0 >= S) return;
     const int d0 = cv * V;
 
-    // wk[k][i]: weight of the tap k tokens back, for channel d0+i (0 beyond W)
+    // wk[k][i]: weight of the tap k tokens back, for channel d0+i
     float wk[4][V], bias[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         bias[i] = b ? b[d0 + i] : 0.0f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) wk[k][i] = (k < W) ? w[(size_t)(d0 + i) * W + (W - 1 - k)] : 0.0f;
+        for (int k = 0; k < W; ++k) wk[k][i] = w[(size_t)(d0 + i) * W + (W - 1 - k)];
     }
-    // window xw[k] = x[t-k]; tokens before 0 are never selected
-    float xw[4][V];
+    // one run; FULL runs (kRun tokens) are straight-line code, so every load
+    // stays ahead of the arithmetic
+    auto run = [&](auto full_tag, int64_t t0, int nt) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        // rows t0-3 .. t0+kRun-1; rows outside [0, T) load row t0 and are never selected
+        typename A::Raw raw[kRun + 3];
+        int32_t pk[kRun];
 #pragma unroll
-    for (int k = 1; k < 4; ++k) {
-        const int64_t tk = t0 - k;
-        if (tk >= 0) {
-            A::load(x + (size_t)tk * D + d0, xw[k]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < V; ++i) xw[k][i] = 0.0f;
-        }
-    }
-    for (int64_t tb = t0; tb < t1; tb += kG) {
-        const int ng = (int)((t1 - tb < kG) ? t1 - tb : kG);
-        typename A::Raw raw[kG];
-        int32_t pk[kG];
-#pragma unroll
-        for (int g = 0; g < kG; ++g) {
-            const int64_t t = tb + (g < ng ? g : ng - 1);  // a short batch repeats its last token
-            raw[g] = A::load_raw(x + (size_t)t * D + d0);
-            pk[g] = pos[t];
+        for (int j = 0; j < kRun + 3; ++j) {
+            const int64_t t = t0 - 3 + j;
+            const bool in = t >= 0 && (FULL ? j < 3 + kRun : t < T_);
+            raw[j] = A::load_raw(x + (size_t)(in ? t : t0) * D + d0);
         }
 #pragma unroll
-        for (int g = 0; g < kG; ++g) {
-            if (g >= ng) break;
-            const int64_t t = tb + g;
-            A::unpack(raw[g], xw[0]);
-            const int kmax = conv_kmax(pk[g], t, W);
+        for (int j = 0; j < kRun; ++j) pk[j] = pos[t0 + ((FULL || j < nt) ? j : 0)];
+        // no head within W - 1 tokens before any of the run's tokens: every tap
+        // is used, with no per-element selects (heads are rare)
+        bool clean = t0 >= W - 1;
+#pragma unroll
+        for (int j = 0; j < kRun; ++j) clean = clean && pk[j] >= W - 1;
+        // window xw[k] = x[t-k]
+        float xw[4][V];
+#pragma unroll
+        for (int k = 1; k < 4; ++k) A::unpack(raw[3 - k], xw[k]);
+#pragma unroll
+        for (int j = 0; j < kRun; ++j) {
+            if (!FULL && j >= nt) break;
+            const int64_t t = t0 + j;
+            A::unpack(raw[j + 3], xw[0]);
+            int kmax = pk[j] < W - 1 ? pk[j] : W - 1;
+            if (t0 < W - 1 && kmax > (int)t) kmax = (int)t;  // only the first tokens of the tensor
             float o[V];
 #pragma unroll
             for (int i = 0; i < V; ++i) {
                 float acc = bias[i];
+                if (clean) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) acc += (k <= kmax) ? wk[k][i] * xw[k][i] : 0.0f;
+                    for (int k = 0; k < W; ++k) acc = __builtin_fmaf(wk[k][i], xw[k][i], acc);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < W; ++k) acc += (k <= kmax) ? wk[k][i] * xw[k][i] : 0.0f;
+                }
                 o[i] = silu ? acc * sigmoid_fast(acc) : acc;
             }
             A::store(u + (size_t)t * D + d0, o);
@@ -137,38 +157,48 @@ __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const
 #pragma unroll
                 for (int i = 0; i < V; ++i) xw[k][i] = xw[k - 1][i];
         }
+    };
+    for (int ps = 0; ps < kFwdPasses; ++ps) {
+        const int64_t t0 = (r0 + ps * S) * kRun;
+        if (t0 >= T_) break;
+        if (t0 + kRun <= T_)
+            run(std::true_type{}, t0, kRun);
+        else
+            run(std::false_type{}, t0, (int)(T_ - t0));
     }
 }
 
 // ---------------------------------------------------------------------------
 // backward
 // ---------------------------------------------------------------------------
-// Per thread: tokens [t0, t1). gv[t] = du[t] * act'(v[t]) is produced for
-// t in [t0, min(t1 + 3, T)); dx[s] for s in [t0, t1) collects
-// sum_k [k <= kmax(s+k)] w_k gv[s+k], emitted once gv[s+3] is known (the
-// last four gv and their kmax are kept). dw and db sums over [t0, t1) are
-// added over the workgroup's kConvBwdRuns runs in LDS, in a fixed order, and
-// written to part[group][j][d] (j = tap k for k < 4, j = 4 for the bias).
-// A workgroup is kConvBwdRuns waves: the same 64 vectors, consecutive runs.
-template <typename T, int V>
+// For a run [t0, t0 + kRun): gv[t] = du[t] * act'(v[t]) for t in
+// [t0, t0 + kRun + W - 1) (the last W - 1 are the next run's, recomputed
+// here); dx[s] = sum_k [k <= kmax(s+k)] w_k gv[s+k] for s in the run; dw and
+// db collect the run's own tokens. A workgroup is kConvBwdRuns waves on the
+// same 64 vectors; wave w takes runs (grp kConvBwdRuns + w) + i G kConvBwdRuns
+// for i = 0, 1, ..., so each pass of the G workgroups sweeps a band of
+// G kConvBwdRuns consecutive runs. The waves' dw/db sums are added in LDS in
+// a fixed order and written to part[grp][j][d] (j = tap k for k < 4, j = 4 for
+// the bias).
+template <typename T, int V, int W>
 __global__ __launch_bounds__(kWave * kConvBwdRuns) void k_conv_bwd(
     const T* __restrict__ x, const float* __restrict__ w, const float* __restrict__ b,
     const int32_t* __restrict__ pos, const T* __restrict__ du, T* __restrict__ dx, float* __restrict__ part,
-    int64_t T_, int D, int W, int silu) {
+    int64_t T_, int D, int silu) {
     using A = Access<T, V>;
+    constexpr int NX = kRun + 2 * (W - 1);  // x rows t0-(W-1) .. t0+kRun+W-2
+    constexpr int NG = kRun + W - 1;        // gv of tokens t0 .. t0+kRun+W-2
     __shared__ float red[kConvBwdRuns][5][kWave * V];
     const int nvec = D / V;
     const int nvg = (nvec + kWave - 1) / kWave;  // 64-vector groups
     const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int vg = (int)(blockIdx.x % nvg);
-    const int64_t grp = blockIdx.x / nvg;           // workgroup's run group
+    const int64_t grp = blockIdx.x / nvg;
+    const int64_t ngrp = gridDim.x / nvg;
     const int cv = vg * kWave + lane;
     const bool actv = cv < nvec;
-    const int64_t run = grp * kConvBwdRuns + wv;
-    const int64_t t0 = run * kConvBwdRun;
-    const int64_t t1 = (t0 + kConvBwdRun < T_) ? t0 + kConvBwdRun : T_;
-    const int64_t tend = (t1 + 3 < T_) ? t1 + 3 : T_;
     const int d0 = (actv ? cv : 0) * V;
+    const int64_t nrun = (T_ + kRun - 1) / kRun;
 
     float dwp[4][V], dbp[V];
 #pragma unroll
@@ -177,111 +207,125 @@ __global__ __launch_bounds__(kWave * kConvBwdRuns) void k_conv_bwd(
 #pragma unroll
         for (int k = 0; k < 4; ++k) dwp[k][i] = 0.0f;
     }
-    if (actv && t0 < T_) {
-        float wk[4][V], bias[V];
+    float wk[4][V], bias[V];
 #pragma unroll
-        for (int i = 0; i < V; ++i) {
-            bias[i] = b ? b[d0 + i] : 0.0f;
+    for (int i = 0; i < V; ++i) {
+        bias[i] = b ? b[d0 + i] : 0.0f;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) wk[k][i] = (k < W) ? w[(size_t)(d0 + i) * W + (W - 1 - k)] : 0.0f;
-        }
-        float xw[4][V];
-#pragma unroll
-        for (int k = 1; k < 4; ++k) {
-            const int64_t tk = t0 - k;
-            if (tk >= 0) {
-                A::load(x + (size_t)tk * D + d0, xw[k]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < V; ++i) xw[k][i] = 0.0f;
-            }
-        }
-        // gw[j] = gv[t-j], kw[j] = kmax(t-j) for the last four tokens (gv = 0 before t0)
-        float gw[4][V];
-        int kw[4] = {-1, -1, -1, -1};
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int i = 0; i < V; ++i) gw[j][i] = 0.0f;
-
-        // one token step: shift the windows in, gv of token t (zero past tend), dx[t-3]
-        auto step = [&](int64_t t, bool have, const float (&g)[V], int kmax) {
-#pragma unroll
-            for (int j = 3; j > 0; --j) {
-                kw[j] = kw[j - 1];
-#pragma unroll
-                for (int i = 0; i < V; ++i) gw[j][i] = gw[j - 1][i];
-            }
-            kw[0] = have ? kmax : -1;
-            const bool own = t < t1;  // dw/db sums only over this thread's tokens
-#pragma unroll
-            for (int i = 0; i < V; ++i) {
-                float gv = 0.0f;
-                if (have) {
-                    float v = bias[i];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) v += (k <= kmax) ? wk[k][i] * xw[k][i] : 0.0f;
-                    gv = g[i];
-                    if (silu) {
-                        const float sg = sigmoid_fast(v);
-                        gv = g[i] * sg * (1.0f + v * (1.0f - sg));
-                    }
-                    if (own) {
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) dwp[k][i] += (k <= kmax) ? gv * xw[k][i] : 0.0f;
-                        dbp[i] += gv;
-                    }
-                }
-                gw[0][i] = gv;
-            }
-            if (have) {
-#pragma unroll
-                for (int k = 3; k > 0; --k)
-#pragma unroll
-                    for (int i = 0; i < V; ++i) xw[k][i] = xw[k - 1][i];
-            }
-            // dx[s], s = t - 3: token s + k feeds tap k when k <= kmax(s + k)
-            const int64_t s = t - 3;
-            if (s >= t0 && s < t1) {
-                float o[V];
-#pragma unroll
-                for (int i = 0; i < V; ++i) {
-                    float acc = 0.0f;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) acc += (k <= kw[3 - k]) ? wk[k][i] * gw[3 - k][i] : 0.0f;
-                    o[i] = acc;
-                }
-                A::store(dx + (size_t)s * D + d0, o);
-            }
-        };
-
-        for (int64_t tb = t0; tb < tend; tb += kG) {
-            const int ng = (int)((tend - tb < kG) ? tend - tb : kG);
-            typename A::Raw rx[kG], rg[kG];
-            int32_t pk[kG];
-#pragma unroll
-            for (int g = 0; g < kG; ++g) {
-                const int64_t t = tb + (g < ng ? g : ng - 1);  // a short batch repeats its last token
-                rx[g] = A::load_raw(x + (size_t)t * D + d0);
-                rg[g] = A::load_raw(du + (size_t)t * D + d0);
-                pk[g] = pos[t];
-            }
-#pragma unroll
-            for (int g = 0; g < kG; ++g) {
-                if (g >= ng) break;
-                const int64_t t = tb + g;
-                float gg[V];
-                A::unpack(rx[g], xw[0]);
-                A::unpack(rg[g], gg);
-                step(t, true, gg, conv_kmax(pk[g], t, W));
-            }
-        }
-        // the tensor ends before t1 + 3: flush the last dx rows
-        const float zero[V] = {};
-        for (int64_t t = tend; t < t1 + 3; ++t) step(t, false, zero, -1);
+        for (int k = 0; k < W; ++k) wk[k][i] = w[(size_t)(d0 + i) * W + (W - 1 - k)];
     }
 
-    // fixed-order sum of the workgroup's runs
+    // one run; FULL runs (kRun own tokens and all W - 1 tokens after them
+    // inside the tensor) are straight-line code, so every load stays ahead of
+    // the arithmetic
+    auto run = [&](auto full_tag, int64_t t0) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const int nt = FULL ? kRun : (int)((T_ - t0 < kRun) ? T_ - t0 : kRun);  // own tokens
+        // rows outside [0, T) load row t0 and are never selected
+        typename A::Raw rx[NX], rg[NG];
+        int32_t pk[NG];
+#pragma unroll
+        for (int j = 0; j < NX; ++j) {
+            const int64_t t = t0 - (W - 1) + j;
+            const bool in = t >= 0 && (FULL || t < T_);
+            rx[j] = A::load_raw(x + (size_t)(in ? t : t0) * D + d0);
+        }
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+            const int64_t t = t0 + j;
+            const bool in = FULL || t < T_;
+            rg[j] = A::load_raw(du + (size_t)(in ? t : t0) * D + d0);
+            pk[j] = pos[in ? t : t0];
+        }
+        // no head within W - 1 tokens before any token of the run or of its W - 1
+        // successors (and all inside the tensor): no per-element selects
+        bool clean = FULL && t0 >= W - 1;
+#pragma unroll
+        for (int j = 0; j < NG; ++j) clean = clean && pk[j] >= W - 1;
+        // gv and kmax of tokens t0 .. t0+NG-1 (zero / -1 past the end)
+        float gw[NG][V];
+        int kw[NG];
+        float xw[4][V];
+#pragma unroll
+        for (int k = 1; k < W; ++k) A::unpack(rx[W - 1 - k], xw[k]);
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+            const int64_t t = t0 + j;
+            const bool have = FULL || t < T_;
+            A::unpack(rx[j + W - 1], xw[0]);
+            float g[V];
+            A::unpack(rg[j], g);
+            int kmax = pk[j] < W - 1 ? pk[j] : W - 1;
+            if (t0 < W - 1 && kmax > (int)t) kmax = (int)t;  // only the first tokens of the tensor
+            kmax = have ? kmax : -1;
+            kw[j] = kmax;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float v = bias[i];
+                if (clean) {
+#pragma unroll
+                    for (int k = 0; k < W; ++k) v = __builtin_fmaf(wk[k][i], xw[k][i], v);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < W; ++k) v += (k <= kmax) ? wk[k][i] * xw[k][i] : 0.0f;
+                }
+                float gv = g[i];
+                if (silu) {
+                    const float sg = sigmoid_fast(v);
+                    gv = g[i] * sg * (1.0f + v * (1.0f - sg));
+                }
+                gv = have ? gv : 0.0f;
+                gw[j][i] = gv;
+                if (j < kRun && (FULL || j < nt)) {  // dw/db: the run's own tokens
+                    if (clean) {
+#pragma unroll
+                        for (int k = 0; k < W; ++k) dwp[k][i] = __builtin_fmaf(gv, xw[k][i], dwp[k][i]);
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < W; ++k) dwp[k][i] += (k <= kmax) ? gv * xw[k][i] : 0.0f;
+                    }
+                    dbp[i] += gv;
+                }
+            }
+#pragma unroll
+            for (int k = W - 1; k > 0; --k)
+#pragma unroll
+                for (int i = 0; i < V; ++i) xw[k][i] = xw[k - 1][i];
+        }
+        // dx[s], s = t0 + j: token s + k feeds tap k when k <= kmax(s + k)
+#pragma unroll
+        for (int j = 0; j < kRun; ++j) {
+            if (!FULL && j >= nt) break;
+            float o[V];
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float acc = 0.0f;
+                if (clean) {
+#pragma unroll
+                    for (int k = 0; k < W; ++k) acc = __builtin_fmaf(wk[k][i], gw[j + k][i], acc);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < W; ++k) acc += (k <= kw[j + k]) ? wk[k][i] * gw[j + k][i] : 0.0f;
+                }
+                o[i] = acc;
+            }
+            A::store(dx + (size_t)(t0 + j) * D + d0, o);
+        }
+    };
+    // the run index is the same for the whole wave: keep it scalar, so row
+    // addresses are a scalar base plus the lane's column offset
+    const int64_t rfirst = (int64_t)__builtin_amdgcn_readfirstlane((int)(grp * kConvBwdRuns + wv));
+    if (actv) {
+        for (int64_t r = rfirst; r < nrun; r += ngrp * kConvBwdRuns) {
+            const int64_t t0 = r * kRun;
+            if (t0 + kRun + W - 1 <= T_)
+                run(std::true_type{}, t0);
+            else
+                run(std::false_type{}, t0);
+        }
+    }
+
+    // fixed-order sum of the workgroup's waves
 #pragma unroll
     for (int i = 0; i < V; ++i) {
 #pragma unroll
@@ -313,10 +357,12 @@ __global__ __launch_bounds__(256) void k_conv_bwd_reduce(const float* __restrict
     else db[d] = acc;
 }
 
-// run groups of the backward (one partial row set each)
+// workgroups per 64-vector group of the backward (one partial row set each):
+// enough for one pass to cover every run of a short input
 static int64_t conv_bwd_groups(int64_t T_) {
-    const int64_t span = (int64_t)kConvBwdRun * kConvBwdRuns;
-    return (T_ + span - 1) / span;
+    const int64_t nrun = (T_ + kRun - 1) / kRun;
+    const int64_t need = (nrun + kConvBwdRuns - 1) / kConvBwdRuns;
+    return need < kConvBwdGroups ? need : kConvBwdGroups;
 }
 
 static bool vec_ok(const void* p, int D, int V, size_t elt) {
@@ -329,13 +375,26 @@ static int launch_fwd(const void* x, const float* w, const float* b, const int32
     constexpr int VV = kFwdV<T>;
     const bool vec = vec_ok(x, D, VV, sizeof(T)) && vec_ok(u, D, VV, sizeof(T));
     const int V = vec ? VV : 1;
-    const int64_t nthreads = (int64_t)(D / V) * ((T_ + kConvFwdRun - 1) / kConvFwdRun);
+    const int64_t nrun = (T_ + kRun - 1) / kRun;
+    const int64_t nthreads = (int64_t)(D / V) * ((nrun + kFwdPasses - 1) / kFwdPasses);
     const int64_t blocks = (nthreads + 255) / 256;
     if (blocks > 0x7fffffff) return SSMP_ERR_SHAPE;
-    if (vec)
-        k_conv_fwd<T, VV><<<(unsigned)blocks, 256, 0, s>>>((const T*)x, w, b, pos, (T*)u, T_, D, W, silu);
-    else
-        k_conv_fwd<T, 1><<<(unsigned)blocks, 256, 0, s>>>((const T*)x, w, b, pos, (T*)u, T_, D, W, silu);
+#define SSMP_CONV_FWD(VX, WX) \
+    k_conv_fwd<T, VX, WX><<<(unsigned)blocks, 256, 0, s>>>((const T*)x, w, b, pos, (T*)u, T_, D, silu)
+#define SSMP_CONV_FWD_W(VX)        \
+    switch (W) {                   \
+        case 1: SSMP_CONV_FWD(VX, 1); break; \
+        case 2: SSMP_CONV_FWD(VX, 2); break; \
+        case 3: SSMP_CONV_FWD(VX, 3); break; \
+        default: SSMP_CONV_FWD(VX, 4); break; \
+    }
+    if (vec) {
+        SSMP_CONV_FWD_W(VV)
+    } else {
+        SSMP_CONV_FWD_W(1)
+    }
+#undef SSMP_CONV_FWD_W
+#undef SSMP_CONV_FWD
     SSMP_LAUNCH_CHECK();
     return SSMP_OK;
 }
@@ -350,12 +409,23 @@ static int launch_bwd(const void* x, const float* w, const float* b, const int32
     const int64_t nvg = (D / V + kWave - 1) / kWave;
     const int64_t blocks = nvg * ngrp;
     if (blocks > 0x7fffffff) return SSMP_ERR_SHAPE;
-    if (vec)
-        k_conv_bwd<T, VV><<<(unsigned)blocks, kWave * kConvBwdRuns, 0, s>>>(
-            (const T*)x, w, b, pos, (const T*)du, (T*)dx, part, T_, D, W, silu);
-    else
-        k_conv_bwd<T, 1><<<(unsigned)blocks, kWave * kConvBwdRuns, 0, s>>>(
-            (const T*)x, w, b, pos, (const T*)du, (T*)dx, part, T_, D, W, silu);
+#define SSMP_CONV_BWD(VX, WX)                                                  \
+    k_conv_bwd<T, VX, WX><<<(unsigned)blocks, kWave * kConvBwdRuns, 0, s>>>( \
+        (const T*)x, w, b, pos, (const T*)du, (T*)dx, part, T_, D, silu)
+#define SSMP_CONV_BWD_W(VX)                   \
+    switch (W) {                              \
+        case 1: SSMP_CONV_BWD(VX, 1); break;  \
+        case 2: SSMP_CONV_BWD(VX, 2); break;  \
+        case 3: SSMP_CONV_BWD(VX, 3); break;  \
+        default: SSMP_CONV_BWD(VX, 4); break; \
+    }
+    if (vec) {
+        SSMP_CONV_BWD_W(VV)
+    } else {
+        SSMP_CONV_BWD_W(1)
+    }
+#undef SSMP_CONV_BWD_W
+#undef SSMP_CONV_BWD
     SSMP_LAUNCH_CHECK();
     k_conv_bwd_reduce<<<(unsigned)((5 * (int64_t)D + 255) / 256), 256, 0, s>>>(part, ngrp, D, W, dw, db);
     SSMP_LAUNCH_CHECK();
