@@ -51,15 +51,17 @@ class Oracle:
         L.oracle_conv_fwd.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _ip,
                                       _dp, _dp, _dp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
                                       _dp, _dp]
-        L.oracle_scan_fwd.restype = ctypes.c_int
-        L.oracle_scan_fwd.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _ip,
-                                      _dp, _dp, _dp, _dp, _dp, _dp, _dp,
-                                      ctypes.c_int32, ctypes.c_int32, _dp, _dp, _dp]
-        L.oracle_scan_bwd.restype = ctypes.c_int
-        L.oracle_scan_bwd.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _ip,
-                                      _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
-                                      ctypes.c_int32, ctypes.c_int32,
-                                      _dp, _dp, _dp, _dp, _dp, _dp, _dp]
+        L.oracle_scan_fwd_ex.restype = ctypes.c_int
+        L.oracle_scan_fwd_ex.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _ip,
+                                         _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+                                         _dp, ctypes.c_int32, ctypes.c_double,
+                                         ctypes.c_int32, ctypes.c_int32, _dp, _dp, _dp]
+        L.oracle_scan_bwd_ex.restype = ctypes.c_int
+        L.oracle_scan_bwd_ex.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _ip,
+                                         _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+                                         _dp, ctypes.c_int32, ctypes.c_double, _dp,
+                                         ctypes.c_int32, ctypes.c_int32,
+                                         _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
         L.oracle_conv_bwd.restype = ctypes.c_int
         L.oracle_conv_bwd.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _ip,
                                       _dp, _dp, _dp, ctypes.c_int, _dp,
@@ -109,40 +111,46 @@ class Oracle:
             self._p(v), self._p(u)))
         return v, u
 
-    def scan_fwd(self, u, delta, A, B, C, Dp, z, pos, threads: int = 1, states: bool = False):
+    def scan_fwd(self, u, delta, A, B, C, Dp, z, pos, threads: int = 1, states: bool = False,
+                 delta_bias=None, delta_softplus: bool = False, gate_floor: float = 0.0):
+        """delta_bias / delta_softplus: the step is softplus(delta + bias) (or
+        delta + bias); gate_floor: the gate is silu(z) + gate_floor."""
         u = self._d(u); delta = self._d(delta); A = self._d(A); B = self._d(B); C = self._d(C)
-        Dp = self._d(Dp); z = self._d(z)
+        Dp = self._d(Dp); z = self._d(z); db = self._d(delta_bias)
         pos = np.ascontiguousarray(pos, dtype=np.int32)
         T, D = u.shape
         N = A.shape[1]
         y = np.zeros((T, D)); out = np.zeros((T, D))
         hs = np.zeros((T, D, N)) if states else None
-        rcs = self._run(self._blocks(D, threads), lambda d0, d1: self.lib.oracle_scan_fwd(
+        rcs = self._run(self._blocks(D, threads), lambda d0, d1: self.lib.oracle_scan_fwd_ex(
             T, D, N, self._p(pos, _ip), self._p(u), self._p(delta), self._p(A), self._p(B), self._p(C),
-            self._p(Dp), self._p(z), d0, d1, self._p(y), self._p(out), self._p(hs)))
+            self._p(Dp), self._p(z), self._p(db), int(delta_softplus), float(gate_floor),
+            d0, d1, self._p(y), self._p(out), self._p(hs)))
         if any(rcs):
             raise MemoryError("oracle_scan_fwd failed")
         return (y, out, hs) if states else (y, out)
 
-    def scan_bwd(self, u, delta, A, B, C, Dp, z, pos, dout, threads: int = 1):
+    def scan_bwd(self, u, delta, A, B, C, Dp, z, pos, dout, threads: int = 1,
+                 delta_bias=None, delta_softplus: bool = False, gate_floor: float = 0.0):
         u = self._d(u); delta = self._d(delta); A = self._d(A); B = self._d(B); C = self._d(C)
-        Dp = self._d(Dp); z = self._d(z); dout = self._d(dout)
+        Dp = self._d(Dp); z = self._d(z); dout = self._d(dout); db = self._d(delta_bias)
         pos = np.ascontiguousarray(pos, dtype=np.int32)
         T, D = u.shape
         N = A.shape[1]
         du = np.zeros((T, D)); ddelta = np.zeros((T, D)); dA = np.zeros((D, N))
-        dDp = np.zeros(D); dz = np.zeros((T, D))
+        dDp = np.zeros(D); dz = np.zeros((T, D)); ddb = np.zeros(D)
         blocks = self._blocks(D, threads)
         parts = [(np.zeros((T, N)), np.zeros((T, N))) for _ in blocks]
 
         def one(i):
             d0, d1 = blocks[i]
             dB_i, dC_i = parts[i]
-            return self.lib.oracle_scan_bwd(
+            return self.lib.oracle_scan_bwd_ex(
                 T, D, N, self._p(pos, _ip), self._p(u), self._p(delta), self._p(A), self._p(B),
-                self._p(C), self._p(Dp), self._p(z), self._p(dout), d0, d1,
+                self._p(C), self._p(Dp), self._p(z), self._p(db), int(delta_softplus), float(gate_floor),
+                self._p(dout), d0, d1,
                 self._p(du), self._p(ddelta), self._p(dA), self._p(dB_i), self._p(dC_i),
-                self._p(dDp), self._p(dz))
+                self._p(dDp), self._p(dz), self._p(ddb))
 
         if len(blocks) <= 1:
             rcs = [one(0)] if blocks else []
@@ -157,6 +165,7 @@ class Oracle:
             dC += dC_i
         res = {"du": du, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dz": dz}
         res["dD"] = dDp if Dp is not None else None
+        res["ddelta_bias"] = ddb if db is not None else None
         return res
 
     def conv_bwd(self, x, w, b, pos, du, silu: bool = True, threads: int = 1):

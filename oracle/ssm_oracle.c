@@ -39,6 +39,22 @@
 #define ORACLE_ERR_ALLOC 6
 
 static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+/* softplus(v) = log(1 + exp(v)), in a form that neither overflows nor loses
+ * the tail: max(v, 0) + log1p(exp(-|v|)) */
+static double softplus(double v) { return (v > 0.0 ? v : 0.0) + log1p(exp(-fabs(v))); }
+
+/* Step size as the scan uses it: delta_eff = softplus(delta + bias[d]) when
+ * softplus is set, else delta + bias[d] (bias may be NULL). Its derivative
+ * with respect to the stored delta is sigmoid(delta + bias[d]), or 1. */
+static double delta_eff(double raw, const double *bias, int32_t d, int sp)
+{
+    const double v = raw + (bias ? bias[d] : 0.0);
+    return sp ? softplus(v) : v;
+}
+static double delta_grad(double raw, const double *bias, int32_t d, int sp)
+{
+    return sp ? sigmoid(raw + (bias ? bias[d] : 0.0)) : 1.0;
+}
 
 /*
  * position_indices from cu_seqlens. [P5] "conv1d_pack 算子": pack() emits, for
@@ -94,23 +110,27 @@ void oracle_conv_fwd(int64_t T, int32_t D, int32_t W, const int32_t *pos,
  * (exp(delta*A) decay, delta*B*u input), per channel d and state n:
  *   h_t = head(t) ? delta_t B_t u_t : exp(delta_t A) h_{t-1} + delta_t B_t u_t
  *   y_t = sum_n C_t[n] h_t[n] + Dp[d] u_t
- *   out_t = y_t * silu(z_t)        (no gate when z is NULL)
+ *   out_t = y_t * (silu(z_t) + gate_floor)        (no gate when z is NULL)
+ * The gate floor is [P4] "修法" GateFloor: a positive offset on the gate so
+ * it stays above zero at zero input (0 = the plain SiLU gate). delta_t is the
+ * step as stored, or softplus(stored + bias) (delta_eff above).
  * At a head the previous state is not read at all (a select, not a multiply
  * by zero), so a non-finite state can never cross a boundary.
  * Dp may be NULL (no skip). y and hs may be NULL; hs receives every state,
  * (T, D, N) at ((t*D)+d)*N + n, for small inspection cases.
  */
-int oracle_scan_fwd(int64_t T, int32_t D, int32_t N, const int32_t *pos,
-                    const double *u, const double *delta, const double *A,
-                    const double *B, const double *C, const double *Dp, const double *z,
-                    int32_t d0, int32_t d1, double *y, double *out, double *hs)
+int oracle_scan_fwd_ex(int64_t T, int32_t D, int32_t N, const int32_t *pos,
+                       const double *u, const double *delta, const double *A,
+                       const double *B, const double *C, const double *Dp, const double *z,
+                       const double *dbias, int32_t sp, double gate_floor,
+                       int32_t d0, int32_t d1, double *y, double *out, double *hs)
 {
     double *h = (double *)calloc((size_t)(N > 0 ? N : 1), sizeof(double));
     if (!h) return ORACLE_ERR_ALLOC;
     for (int32_t d = d0; d < d1; ++d) {
         for (int64_t t = 0; t < T; ++t) {
             const int head = pos[t] == 0;
-            const double dt = delta[t * D + d];
+            const double dt = delta_eff(delta[t * D + d], dbias, d, sp);
             const double uu = u[t * D + d];
             double acc = 0.0;
             for (int32_t n = 0; n < N; ++n) {
@@ -126,17 +146,25 @@ int oracle_scan_fwd(int64_t T, int32_t D, int32_t N, const int32_t *pos,
             }
             if (Dp) acc += Dp[d] * uu;
             if (y) y[t * D + d] = acc;
-            out[t * D + d] = z ? acc * (z[t * D + d] * sigmoid(z[t * D + d])) : acc;
+            out[t * D + d] = z ? acc * (z[t * D + d] * sigmoid(z[t * D + d]) + gate_floor) : acc;
         }
     }
     free(h);
     return ORACLE_OK;
 }
 
+int oracle_scan_fwd(int64_t T, int32_t D, int32_t N, const int32_t *pos,
+                    const double *u, const double *delta, const double *A,
+                    const double *B, const double *C, const double *Dp, const double *z,
+                    int32_t d0, int32_t d1, double *y, double *out, double *hs)
+{
+    return oracle_scan_fwd_ex(T, D, N, pos, u, delta, A, B, C, Dp, z, NULL, 0, 0.0, d0, d1, y, out, hs);
+}
+
 /*
  * Selective scan backward: the chain rule of oracle_scan_fwd, written out.
  * Given dout = dL/dout (T, D):
- *   g = dout * silu(z)                      (dL/dy)
+ *   g = dout * (silu(z) + gate_floor)       (dL/dy)
  *   dz = dout * y * s * (1 + z (1 - s)),  s = sigmoid(z)
  *   dDp[d] = sum_t g u,   du starts at g * Dp[d]
  * then per state n, t descending, with carry c (dL/dh_t through h_{t+1}):
@@ -147,16 +175,19 @@ int oracle_scan_fwd(int64_t T, int32_t D, int32_t N, const int32_t *pos,
  *   ddelta[t] += dh (B_t[n] u_t + [not head] A a_t h_{t-1})
  *   dA[d,n] += [not head] dh delta_t a_t h_{t-1}
  *   c = [not head] a_t dh        ([P5] "基本原理": no gradient crosses a head)
- * with a_t = exp(delta_t A[d,n]). dB and dC (T, N) are ACCUMULATED into (the
- * caller zeroes them, and sums per-thread buffers); all other outputs are
- * overwritten for channels [d0, d1). Dp, z may be NULL; dz may be NULL.
+ * with a_t = exp(delta_t A[d,n]). ddelta is returned with respect to the
+ * stored delta (times sigmoid(delta + bias) under softplus), and ddbias[d] is
+ * its sum over t. dB and dC (T, N) are ACCUMULATED into (the caller zeroes
+ * them, and sums per-thread buffers); all other outputs are overwritten for
+ * channels [d0, d1). Dp, z, dbias may be NULL; dz, ddbias may be NULL.
  */
-int oracle_scan_bwd(int64_t T, int32_t D, int32_t N, const int32_t *pos,
-                    const double *u, const double *delta, const double *A,
-                    const double *B, const double *C, const double *Dp, const double *z,
-                    const double *dout, int32_t d0, int32_t d1,
-                    double *du, double *ddelta, double *dA, double *dB, double *dC,
-                    double *dDp, double *dz)
+int oracle_scan_bwd_ex(int64_t T, int32_t D, int32_t N, const int32_t *pos,
+                       const double *u, const double *delta, const double *A,
+                       const double *B, const double *C, const double *Dp, const double *z,
+                       const double *dbias, int32_t sp, double gate_floor,
+                       const double *dout, int32_t d0, int32_t d1,
+                       double *du, double *ddelta, double *dA, double *dB, double *dC,
+                       double *dDp, double *dz, double *ddbias)
 {
     double *hs = (double *)malloc((size_t)(T > 0 ? T : 1) * (size_t)(N > 0 ? N : 1) * sizeof(double));
     double *ys = (double *)malloc((size_t)(T > 0 ? T : 1) * sizeof(double));
@@ -166,7 +197,7 @@ int oracle_scan_bwd(int64_t T, int32_t D, int32_t N, const int32_t *pos,
         /* forward, keeping every state of this channel */
         for (int64_t t = 0; t < T; ++t) {
             const int head = pos[t] == 0;
-            const double dt = delta[t * D + d];
+            const double dt = delta_eff(delta[t * D + d], dbias, d, sp);
             const double uu = u[t * D + d];
             double acc = 0.0;
             for (int32_t n = 0; n < N; ++n) {
@@ -189,16 +220,17 @@ int oracle_scan_bwd(int64_t T, int32_t D, int32_t N, const int32_t *pos,
         double dDp_acc = 0.0;
         double *dA_d = dA + (int64_t)d * N;
         for (int32_t n = 0; n < N; ++n) dA_d[n] = 0.0;
+        double ddb_acc = 0.0;
         for (int64_t t = T - 1; t >= 0; --t) {
             const int head = pos[t] == 0;
-            const double dt = delta[t * D + d];
+            const double dt = delta_eff(delta[t * D + d], dbias, d, sp);
             const double uu = u[t * D + d];
             const double go = dout[t * D + d];
             double g = go;
             if (z) {
                 const double zz = z[t * D + d];
                 const double s = sigmoid(zz);
-                g = go * (zz * s);
+                g = go * (zz * s + gate_floor);
                 if (dz) dz[t * D + d] = go * ys[t] * s * (1.0 + zz * (1.0 - s));
             } else if (dz) {
                 dz[t * D + d] = 0.0;
@@ -225,12 +257,27 @@ int oracle_scan_bwd(int64_t T, int32_t D, int32_t N, const int32_t *pos,
                 }
             }
             du[t * D + d] = du_acc;
-            ddelta[t * D + d] = ddt;
+            /* through the step map: d delta_eff / d delta */
+            const double ddraw = ddt * delta_grad(delta[t * D + d], dbias, d, sp);
+            ddelta[t * D + d] = ddraw;
+            ddb_acc += ddraw;
         }
         if (dDp) dDp[d] = dDp_acc;
+        if (ddbias) ddbias[d] = ddb_acc;
     }
     free(hs); free(ys); free(c);
     return ORACLE_OK;
+}
+
+int oracle_scan_bwd(int64_t T, int32_t D, int32_t N, const int32_t *pos,
+                    const double *u, const double *delta, const double *A,
+                    const double *B, const double *C, const double *Dp, const double *z,
+                    const double *dout, int32_t d0, int32_t d1,
+                    double *du, double *ddelta, double *dA, double *dB, double *dC,
+                    double *dDp, double *dz)
+{
+    return oracle_scan_bwd_ex(T, D, N, pos, u, delta, A, B, C, Dp, z, NULL, 0, 0.0, dout, d0, d1,
+                              du, ddelta, dA, dB, dC, dDp, dz, NULL);
 }
 
 /*

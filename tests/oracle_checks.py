@@ -388,9 +388,93 @@ def check_chunk_composition(orc):
         np.testing.assert_allclose(got, hs, rtol=1e-12, atol=1e-14)
 
 
+
+
+# --------------------------------------------------------------------------
+# P9: step map (delta + bias, optionally through softplus) and gate floor
+# --------------------------------------------------------------------------
+
+def _scan_case(seed, lengths=(4, 2, 3, 7), D=3, N=3):
+    rng = np.random.default_rng(seed)
+    c = rand_case(rng, list(lengths), D=D, N=N)
+    return c, rng
+
+
+def _pos(orc, c):
+    return orc.pack_indices(c["cu"], c["T"])[0]
+
+
+def check_step_map_closed_forms(orc):
+    """softplus(0) = ln 2, softplus(v) -> v for large v and -> exp(v) for very
+    negative v: the extended step map with raw + bias at those points equals
+    the plain scan run on the closed-form step values."""
+    c, rng = _scan_case(31)
+    pos = _pos(orc, c)
+    u = rng.standard_normal((c["T"], c["D"]))
+    bias = rng.standard_normal(c["D"])
+    args = (u, None, c["A"], c["B"], c["C"], c["Dp"], c["z"], pos)
+    for v, closed in ((0.0, np.log(2.0)), (40.0, 40.0), (-40.0, np.exp(-40.0))):
+        raw = np.full((c["T"], c["D"]), v) - bias[None, :]
+        _, out_x = orc.scan_fwd(u, raw, *args[2:], delta_bias=bias, delta_softplus=True)
+        _, out_p = orc.scan_fwd(u, np.full((c["T"], c["D"]), closed), *args[2:])
+        np.testing.assert_allclose(out_x, out_p, rtol=1e-12, atol=1e-300, err_msg=f"softplus at {v}")
+    # bias alone shifts the step channel by channel
+    raw = c["delta"]
+    _, out_b = orc.scan_fwd(u, raw, *args[2:], delta_bias=bias * 0.01)
+    _, out_s = orc.scan_fwd(u, raw + bias[None, :] * 0.01, *args[2:])
+    np.testing.assert_allclose(out_b, out_s, rtol=1e-14, atol=1e-14, err_msg="bias per channel")
+
+
+def check_gate_floor_linear(orc):
+    """([P4] GateFloor) out = y (silu(z) + floor): out(floor) - out(0) = floor * y,
+    with y the pre-gate output, and the floor changes neither y nor dz."""
+    c, rng = _scan_case(32)
+    pos = _pos(orc, c)
+    u = rng.standard_normal((c["T"], c["D"]))
+    a = (u, c["delta"], c["A"], c["B"], c["C"], c["Dp"], c["z"], pos)
+    y0, out0 = orc.scan_fwd(*a)
+    y1, out1 = orc.scan_fwd(*a, gate_floor=0.07)
+    assert np.array_equal(y0, y1)
+    np.testing.assert_allclose(out1 - out0, 0.07 * y0, rtol=1e-12, atol=1e-13)
+    g0 = orc.scan_bwd(*a, c["dout"])
+    g1 = orc.scan_bwd(*a, c["dout"], gate_floor=0.07)
+    np.testing.assert_allclose(g1["dz"], g0["dz"], rtol=1e-14, atol=1e-14)
+
+
+def check_step_map_finite_differences(orc, seed=33):
+    """Gradients of sum(dout * out) through the step map and the gate floor
+    (scan alone), against central differences."""
+    c, rng = _scan_case(seed, lengths=(3, 1, 4))
+    pos = _pos(orc, c)
+    u = rng.standard_normal((c["T"], c["D"]))
+    bias = rng.standard_normal(c["D"]) * 0.5
+    raw = rng.standard_normal((c["T"], c["D"])) - 1.5
+    opts = dict(delta_softplus=True, gate_floor=0.05)
+    dout = c["dout"]
+
+    def loss(raw_=raw, bias_=bias, u_=u, z_=c["z"]):
+        _, out = orc.scan_fwd(u_, raw_, c["A"], c["B"], c["C"], c["Dp"], z_, pos, delta_bias=bias_, **opts)
+        return float(np.sum(dout * out))
+
+    G = orc.scan_bwd(u, raw, c["A"], c["B"], c["C"], c["Dp"], c["z"], pos, dout, delta_bias=bias, **opts)
+    for name, p, gk in (("raw_", raw, "ddelta"), ("bias_", bias, "ddelta_bias"), ("u_", u, "du"),
+                        ("z_", c["z"], "dz")):
+        fd = np.zeros_like(p)
+        for idx in np.ndindex(p.shape):
+            h = 1e-6 * max(1.0, abs(p[idx]))
+            pp = p.copy(); pp[idx] += h
+            pm = p.copy(); pm[idx] -= h
+            fd[idx] = (loss(**{name: pp}) - loss(**{name: pm})) / (2 * h)
+        an = G[gk]
+        scale = max(1e-3, float(np.max(np.abs(an))))
+        err = float(np.max(np.abs(fd - an)))
+        assert err <= 1e-6 * scale, f"{gk}: fd mismatch {err:.3e} (scale {scale:.3e})"
+
+
 ALL_CHECKS = [
     check_golden_pack, check_pack_rejects_bad_cu, check_packed_equals_alone, check_scan_closed_form,
     check_conv_closed_form, check_zero_state_at_heads, check_nonfinite_isolated,
     check_conv_matches_torch, check_scan_cumsum, check_finite_differences, check_padded_layout,
-    check_chunk_composition,
+    check_chunk_composition, check_step_map_closed_forms, check_gate_floor_linear,
+    check_step_map_finite_differences,
 ]

@@ -40,8 +40,8 @@ MUTATIONS = [
      "h[n] = exp(dt * A[(int64_t)d * N + n]) * (0.0 * h[n]) + bu;\n                } else {\n                    const double a = exp(dt * A[(int64_t)d * N + n]);\n                    h[n] = a * h[n] + bu;"),
     ("scan: decay sign flipped", "const double a = exp(dt * A[(int64_t)d * N + n]);\n                    h[n] = a * h[n] + bu;",
      "const double a = exp(-dt * A[(int64_t)d * N + n]);\n                    h[n] = a * h[n] + bu;"),
-    ("scan: no reset at heads", "const int head = pos[t] == 0;\n            const double dt = delta[t * D + d];\n            const double uu = u[t * D + d];\n            double acc = 0.0;\n            for (int32_t n = 0; n < N; ++n) {\n                const double bu = dt * B[t * N + n] * uu;\n                if (head) {\n                    h[n] = bu;",
-     "const int head = t == 0;\n            const double dt = delta[t * D + d];\n            const double uu = u[t * D + d];\n            double acc = 0.0;\n            for (int32_t n = 0; n < N; ++n) {\n                const double bu = dt * B[t * N + n] * uu;\n                if (head) {\n                    h[n] = bu;"),
+    ("scan: no reset at heads", "const int head = pos[t] == 0;\n            const double dt = delta_eff(delta[t * D + d], dbias, d, sp);\n            const double uu = u[t * D + d];\n            double acc = 0.0;\n            for (int32_t n = 0; n < N; ++n) {\n                const double bu = dt * B[t * N + n] * uu;\n                if (head) {\n                    h[n] = bu;",
+     "const int head = t == 0;\n            const double dt = delta_eff(delta[t * D + d], dbias, d, sp);\n            const double uu = u[t * D + d];\n            double acc = 0.0;\n            for (int32_t n = 0; n < N; ++n) {\n                const double bu = dt * B[t * N + n] * uu;\n                if (head) {\n                    h[n] = bu;"),
     ("bwd: dA loses the delta factor", "dA_d[n] += dh * dt * a * hp;", "dA_d[n] += dh * a * hp;"),
     ("bwd: carry crosses heads", "ddt += dh * (Bn * uu);\n                    c[n] = 0.0;", "ddt += dh * (Bn * uu);\n                    c[n] = dh;"),
     ("bwd: previous state index off by one", "const double hp = hs[(t - 1) * N + n];", "const double hp = hs[t * N + n];"),
@@ -52,6 +52,16 @@ MUTATIONS = [
     ("conv bwd: dw tap index transposed", "dw[(int64_t)d * W + (W - 1 - k)] = acc;", "dw[(int64_t)d * W + k] = acc;"),
     ("conv bwd: silu derivative drops a term", "gv[t] = g * s * (1.0 + v * (1.0 - s));", "gv[t] = g * s;"),
     ("pack: heads off by one", "pos[t] = (int32_t)(t - cu[s]);", "pos[t] = (int32_t)(t - cu[s] + (s > 0));"),
+    ("step map: softplus loses its log1p tail", "return (v > 0.0 ? v : 0.0) + log1p(exp(-fabs(v)));",
+     "return (v > 0.0 ? v : 0.0);"),
+    ("step map: bias read for the wrong channel", "const double v = raw + (bias ? bias[d] : 0.0);",
+     "const double v = raw + (bias ? bias[0] : 0.0);"),
+    ("step map: backward misses the softplus slope", "return sp ? sigmoid(raw + (bias ? bias[d] : 0.0)) : 1.0;",
+     "return 1.0;"),
+    ("gate floor: forward drops it", "acc * (z[t * D + d] * sigmoid(z[t * D + d]) + gate_floor)",
+     "acc * (z[t * D + d] * sigmoid(z[t * D + d]))"),
+    ("gate floor: backward drops it", "g = go * (zz * s + gate_floor);", "g = go * (zz * s);"),
+    ("step map: bias gradient keeps only one token", "ddb_acc += ddraw;", "ddb_acc = ddraw;"),
 ]
 
 
