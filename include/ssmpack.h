@@ -54,7 +54,8 @@ typedef enum { SSMP_F32 = 0, SSMP_BF16 = 1 } ssmp_dtype;
 /* Static English text for a status code; never NULL. */
 const char *ssmp_status_string(int status);
 
-/* Version of this ABI (incremented on any incompatible change). */
+/* Version of this ABI (incremented on any change to the set of entry points
+ * or their meaning; 2 added the _ex scan entry points). */
 int ssmp_abi_version(void);
 
 /*
@@ -154,6 +155,40 @@ int selective_scan_pack_bwd(const void *u, const void *delta, const float *A, co
                             void *du, void *ddelta, float *dA, float *dB, float *dC,
                             float *dD, void *dz,
                             int64_t T, int32_t D, int32_t N, int32_t dtype, void *stream);
+
+/*
+ * selective_scan_pack_fwd_ex / selective_scan_pack_bwd_ex — the same scan with
+ * two element-wise neighbours applied where it reads its inputs:
+ *   - the step map: the scan uses softplus(delta + delta_bias[d]) (when
+ *     delta_softplus is nonzero) or delta + delta_bias[d] in place of delta.
+ *     delta_bias is fp32 (D), nullable (no bias). The pages take the step as
+ *     given; this is Mamba-1's discretisation step, bias and softplus folded
+ *     in so that no separate (T, D) pass produces it.
+ *   - the gate floor: out = y * (SiLU(z) + gate_floor), [P4]
+ *     (aimodeling.com, near-zero embeddings in gated training) "修法"
+ *     GateFloor, a positive offset (there 0.01 .. 0.1) that keeps the gate
+ *     above zero at zero input. 0 is the plain SiLU gate; ignored without z.
+ * The backward returns ddelta with respect to the stored delta (times
+ * sigmoid(delta + bias) under softplus) and ddelta_bias fp32 (D), its sum over
+ * tokens (must be NULL iff delta_bias is NULL; deterministic). The forward and
+ * backward must be given the same options. selective_scan_pack_fwd and
+ * selective_scan_pack_bwd are these with (NULL, 0, 0.0f).
+ * Errors as selective_scan_pack_fwd / _bwd.
+ */
+int selective_scan_pack_fwd_ex(const void *u, const void *delta, const float *A, const void *B,
+                               const void *C, const float *Dskip, const void *z, const int32_t *pos,
+                               void *out, void *workspace, size_t workspace_bytes,
+                               int64_t T, int32_t D, int32_t N, int32_t dtype,
+                               const float *delta_bias, int32_t delta_softplus, float gate_floor,
+                               void *stream);
+int selective_scan_pack_bwd_ex(const void *u, const void *delta, const float *A, const void *B,
+                               const void *C, const float *Dskip, const void *z, const int32_t *pos,
+                               const void *dout, void *workspace, size_t workspace_bytes,
+                               void *du, void *ddelta, float *dA, float *dB, float *dC,
+                               float *dD, void *dz,
+                               int64_t T, int32_t D, int32_t N, int32_t dtype,
+                               const float *delta_bias, int32_t delta_softplus, float gate_floor,
+                               float *ddelta_bias, void *stream);
 
 #ifdef __cplusplus
 }

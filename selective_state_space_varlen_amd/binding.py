@@ -36,6 +36,13 @@ _SIGNATURES = {
     "selective_scan_pack_bwd": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
                                                _c_vp, _c_sz, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
                                                _c_i64, _c_i32, _c_i32, _c_i32, _c_vp]),
+    "selective_scan_pack_fwd_ex": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                                  _c_vp, _c_sz, _c_i64, _c_i32, _c_i32, _c_i32,
+                                                  _c_vp, _c_i32, ctypes.c_float, _c_vp]),
+    "selective_scan_pack_bwd_ex": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                                  _c_vp, _c_sz, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                                  _c_i64, _c_i32, _c_i32, _c_i32,
+                                                  _c_vp, _c_i32, ctypes.c_float, _c_vp, _c_vp]),
 }
 
 EXPORTED = tuple(_SIGNATURES)
@@ -166,9 +173,15 @@ def selective_scan_pack_workspace_bytes(T: int, D: int, N: int) -> int:
     return int(load().selective_scan_pack_workspace_bytes(T, D, N))
 
 
+def _extended(delta_bias, delta_softplus, gate_floor) -> bool:
+    return delta_bias is not None or bool(delta_softplus) or float(gate_floor) != 0.0
+
+
 def selective_scan_pack_fwd(u, delta, A, B, C, Dskip, z, pos, workspace: Optional[torch.Tensor] = None,
-                            out: Optional[torch.Tensor] = None):
-    """Returns (out, workspace); keep the workspace for the backward."""
+                            out: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                            delta_softplus: bool = False, gate_floor: float = 0.0):
+    """Returns (out, workspace); keep the workspace for the backward.
+    delta_bias / delta_softplus / gate_floor select selective_scan_pack_fwd_ex."""
     T, D = u.shape
     N = A.shape[1]
     dev = u.device
@@ -181,16 +194,23 @@ def selective_scan_pack_fwd(u, delta, A, B, C, Dskip, z, pos, workspace: Optiona
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     o = torch.empty_like(u) if out is None else out
     _check(o, "out", (T, D), u.dtype, dev)
-    _call("selective_scan_pack_fwd", _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z),
-          _ptr(pos), _ptr(o), _ptr(workspace), workspace.numel() * workspace.element_size(), T, D, N,
-          _dtype_code(u), _stream(u))
+    args = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(pos), _ptr(o),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), T, D, N, _dtype_code(u))
+    if _extended(delta_bias, delta_softplus, gate_floor):
+        _check(delta_bias, "delta_bias", (D,), torch.float32, dev)
+        _call("selective_scan_pack_fwd_ex", *args, _ptr(delta_bias), int(bool(delta_softplus)), float(gate_floor),
+              _stream(u))
+    else:
+        _call("selective_scan_pack_fwd", *args, _stream(u))
     return o, workspace
 
 
 def selective_scan_pack_bwd(u, delta, A, B, C, Dskip, z, pos, dout, workspace: torch.Tensor,
-                            out: Optional[dict] = None):
-    """Gradients of sum(dout * out); the workspace must come from the forward.
-    `out` may supply the result buffers (a dict shaped like the return value)."""
+                            out: Optional[dict] = None, delta_bias: Optional[torch.Tensor] = None,
+                            delta_softplus: bool = False, gate_floor: float = 0.0):
+    """Gradients of sum(dout * out); the workspace must come from the forward,
+    called with the same options. `out` may supply the result buffers (a dict
+    shaped like the return value; "ddelta_bias" is present iff delta_bias is)."""
     T, D = u.shape
     N = A.shape[1]
     dev = u.device
@@ -213,7 +233,21 @@ def selective_scan_pack_bwd(u, delta, A, B, C, Dskip, z, pos, dout, workspace: t
     _check(dA, "dA", (D, N), torch.float32, dev); _check(dB, "dB", (T, N), torch.float32, dev)
     _check(dC, "dC", (T, N), torch.float32, dev); _check(dD, "dD", (D,), torch.float32, dev)
     _check(dz, "dz", (T, D), u.dtype, dev)
-    _call("selective_scan_pack_bwd", _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z),
-          _ptr(pos), _ptr(dout), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(du),
-          _ptr(ddelta), _ptr(dA), _ptr(dB), _ptr(dC), _ptr(dD), _ptr(dz), T, D, N, _dtype_code(u), _stream(u))
-    return {"du": du, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "dz": dz}
+    args = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(pos), _ptr(dout),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(du), _ptr(ddelta), _ptr(dA),
+            _ptr(dB), _ptr(dC), _ptr(dD), _ptr(dz), T, D, N, _dtype_code(u))
+    res = {"du": du, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "dz": dz}
+    if _extended(delta_bias, delta_softplus, gate_floor):
+        _check(delta_bias, "delta_bias", (D,), torch.float32, dev)
+        ddb = None
+        if delta_bias is not None:
+            ddb = out.get("ddelta_bias") if out is not None else None
+            if ddb is None:
+                ddb = torch.empty((D,), dtype=torch.float32, device=dev)
+            _check(ddb, "ddelta_bias", (D,), torch.float32, dev)
+        _call("selective_scan_pack_bwd_ex", *args, _ptr(delta_bias), int(bool(delta_softplus)), float(gate_floor),
+              _ptr(ddb), _stream(u))
+        res["ddelta_bias"] = ddb
+    else:
+        _call("selective_scan_pack_bwd", *args, _stream(u))
+    return res

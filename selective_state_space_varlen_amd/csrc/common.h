@@ -77,6 +77,19 @@ __device__ __forceinline__ float swap_adjacent(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
 }
 
+// Zero n floats: where an empty input still has sums to report. A kernel,
+// not a memset, so that a caller may capture the call in a graph.
+template <int kUnused = 0>
+__global__ __launch_bounds__(256) void k_zero_f32(float* __restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+inline int zero_f32(float* p, int64_t n, hipStream_t s) {
+    if (!p || n <= 0) return SSMP_OK;
+    k_zero_f32<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(p, n);
+    return hipGetLastError() == hipSuccess ? SSMP_OK : SSMP_ERR_HIP;
+}
+
 // sum_{r < n} p[r * stride], added in the order r = 0, 1, ..., n-1 (so the
 // result does not depend on the batch size), with kB loads in flight at a time
 // instead of one.

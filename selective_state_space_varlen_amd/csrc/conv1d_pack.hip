@@ -470,9 +470,8 @@ extern "C" int conv1d_pack_bwd(const void* x, const float* w, const float* b, co
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (T == 0) {
         // empty input: the sums are zero
-        if (hipMemsetAsync(dw, 0, sizeof(float) * (size_t)D * W, s) != hipSuccess) return SSMP_ERR_HIP;
-        if (db && hipMemsetAsync(db, 0, sizeof(float) * (size_t)D, s) != hipSuccess) return SSMP_ERR_HIP;
-        return SSMP_OK;
+        if ((st = zero_f32(dw, (int64_t)D * W, s))) return st;
+        return zero_f32(db, D, s);
     }
     if (!x || !pos || !du || !dx) return SSMP_ERR_NULL;
     if (!workspace || workspace_bytes < conv1d_pack_bwd_workspace_bytes(T, D, W)) return SSMP_ERR_WORKSPACE;

@@ -42,7 +42,7 @@ namespace ssmp {
 template <bool SAFE, bool GATE, typename T, int NS, int BT, typename St>
 __device__ __forceinline__ void bsum_block(const T* lds, const float* __restrict__ bc, int64_t tb, int nt,
                                            const float (&A2)[NS], float (&sr)[NS], float& sdt, float& cdt,
-                                           int lane) {
+                                           int lane, const StepMap& sm, float gf) {
     // the block's per-lane inputs are read from LDS before the first scalar
     // load: a wait for LDS data also waits for scalar loads in flight
     float dtv[BT], gv[BT];
@@ -52,8 +52,12 @@ __device__ __forceinline__ void bsum_block(const T* lds, const float* __restrict
         gv[k] = St::get(lds, 2, k, lane);
         if constexpr (GATE) {
             const float zz = St::get(lds, 1, k, lane);
-            gv[k] *= zz * sigmoid_fast(zz);
+            gv[k] *= __builtin_fmaf(zz, sigmoid_fast(zz), gf);
         }
+    }
+    if (sm.on) {
+#pragma unroll
+        for (int k = 0; k < BT; ++k) dtv[k] = sm.eff(dtv[k]);
     }
     const float* __restrict__ rows = bc + (size_t)tb * 2 * NS + NS;  // C rows
     float cur[NS];
@@ -90,7 +94,7 @@ __global__ __launch_bounds__(64, 4) void k_scan_bwd_summary(const T* __restrict_
                                                          const float* __restrict__ bc, const T* __restrict__ z,
                                                          const T* __restrict__ dout, const int32_t* __restrict__ pos,
                                                          float* __restrict__ Pr, float* __restrict__ Sr, int64_t T_,
-                                                         int D, int vec, int lc) {
+                                                         int D, int vec, int lc, ScanOpts opt) {
     constexpr int BT = 8;
     using St = Stager<T, 3, BT>;
     __shared__ __attribute__((aligned(16))) T lds[St::kElems];
@@ -123,6 +127,7 @@ __global__ __launch_bounds__(64, 4) void k_scan_bwd_summary(const T* __restrict_
         sr[n] = 0.0f;
     }
     float sdt = 0.0f, cdt = 0.0f;
+    const StepMap sm = step_map(opt, dd);
     const T* const src[3] = {delta, GATE ? z : delta, dout};
     St st;
     st.fetch(src, t0, T_, D, tl.g, lane, vec);
@@ -133,9 +138,9 @@ __global__ __launch_bounds__(64, 4) void k_scan_bwd_summary(const T* __restrict_
         if (tb + BT < fh) st.fetch(src, tb + BT, T_, D, tl.g, lane, vec);
         const int nt = (int)((tb + BT < fh) ? BT : fh - tb);
         if (nt == BT)
-            bsum_block<false, GATE, T, NS, BT, St>(lds, bc, tb, BT, A2, sr, sdt, cdt, lane);
+            bsum_block<false, GATE, T, NS, BT, St>(lds, bc, tb, BT, A2, sr, sdt, cdt, lane, sm, opt.gate_floor);
         else
-            bsum_block<true, GATE, T, NS, BT, St>(lds, bc, tb, nt, A2, sr, sdt, cdt, lane);
+            bsum_block<true, GATE, T, NS, BT, St>(lds, bc, tb, nt, A2, sr, sdt, cdt, lane, sm, opt.gate_floor);
     }
     if (act) {
         // the decay exp2(A2[n] * sdt) depends on n only through A: keep sdt
@@ -239,11 +244,13 @@ struct BwdArgs {
     T* dz;
     float* dApart;
     float* dDpart;
+    float* dbpart;
     float* dBC;
     int64_t T_;
     int D;
     int vec;
     int lc;
+    ScanOpts opt;
 };
 
 constexpr int kRedStride = kWave + 4;  // LDS row stride (floats) of the dB/dC transpose
@@ -251,10 +258,10 @@ constexpr int kRedStride = kWave + 4;  // LDS row stride (floats) of the dB/dC t
 // Replay of one kK-token sub-chunk from its entering state h: the states hh[k]
 // after each token and the pre-gate outputs yk[k]. SAFE sub-chunks may be
 // short (ns < kK) and may hold heads; the fast ones are full and head-free.
-template <bool SAFE, int NS, int LPC, typename St, typename T>
+template <bool SAFE, bool XS, int NS, int LPC, typename St, typename T>
 __device__ __forceinline__ void bwd_replay(const T* lds, const float* bcl, int kb, int ns, uint32_t heads, int ch,
                                            int n0, const float (&A2)[NS / LPC], float (&h)[NS / LPC],
-                                           float (&hh)[kK][NS / LPC], float (&yk)[kK], float Dv) {
+                                           float (&hh)[kK][NS / LPC], float (&yk)[kK], float Dv, const StepMap& sm) {
     // on return h holds the state after the last replayed token
     constexpr int NH = NS / LPC;
 #pragma unroll
@@ -263,7 +270,7 @@ __device__ __forceinline__ void bwd_replay(const T* lds, const float* bcl, int k
             if (kk >= ns) break;
         }
         const int k = kb + kk;
-        const float dt = St::get(lds, 1, k, ch);
+        const float dt = XS ? sm.eff(St::get(lds, 1, k, ch)) : St::get(lds, 1, k, ch);
         const float uu = St::get(lds, 0, k, ch);
         const float dtu = dt * uu;
         const float* row = bcl + k * 2 * NS + n0;
@@ -291,13 +298,14 @@ struct BwdRows {
 };
 
 // Reverse step over one sub-chunk (tokens kb + ns - 1 down to kb).
-template <bool SAFE, bool GATE, int NS, int LPC, typename St, typename T>
+template <bool SAFE, bool GATE, bool XS, int NS, int LPC, typename St, typename T>
 __device__ __forceinline__ void bwd_reverse(const T* lds, const float* bcl, float (*red)[kRedStride], int kb, int ns,
                                             uint32_t heads, int lane, int ch, int sh, int n0, bool act, bool full,
                                             int D, int d, const float (&A2)[NS / LPC], float (&carry)[NS / LPC],
                                             float (&dA)[NS / LPC], float& dDacc, float Dv,
                                             const float (&hin)[NS / LPC], const float (&hh)[kK][NS / LPC],
-                                            const float (&yk)[kK], const BwdRows<T>& rows) {
+                                            const float (&yk)[kK], const BwdRows<T>& rows, const StepMap& sm,
+                                            float gf, float& dbacc) {
     constexpr int NH = NS / LPC;
     constexpr int CW = kWave / LPC;
 #pragma unroll
@@ -306,14 +314,15 @@ __device__ __forceinline__ void bwd_reverse(const T* lds, const float* bcl, floa
             if (kk >= ns) continue;
         }
         const int k = kb + kk;
-        const float dt = St::get(lds, 1, k, ch);
+        const float draw = St::get(lds, 1, k, ch);
+        const float dt = XS ? sm.eff(draw) : draw;
         const float uu = St::get(lds, 0, k, ch);
         const float go = St::get(lds, 3, k, ch);
         float gg = go, dzv = 0.0f;
         if constexpr (GATE) {
             const float zz = St::get(lds, 2, k, ch);
             const float sg = sigmoid_fast(zz);
-            gg = go * zz * sg;
+            gg = go * __builtin_fmaf(zz, sg, gf);
             dzv = go * yk[kk] * sg * (1.0f + zz * (1.0f - sg));
         }
         gg = act ? gg : 0.0f;  // lanes past D add nothing to dB/dC
@@ -351,7 +360,11 @@ __device__ __forceinline__ void bwd_reverse(const T* lds, const float* bcl, floa
             sumAr += swap_adjacent(sumAr);
         }
         const float duv = __builtin_fmaf(gg, Dv, dt * sumB);
-        const float ddv = __builtin_fmaf(uu, sumB, sumAr * kLn2);
+        float ddv = __builtin_fmaf(uu, sumB, sumAr * kLn2);
+        if constexpr (XS) {
+            ddv *= sm.slope(draw);  // with respect to the stored step
+            dbacc += act ? ddv : 0.0f;
+        }
         dDacc = __builtin_fmaf(gg, uu, dDacc);
         // both lanes of a pair hold the same values and store the same bytes
         const uint32_t e = (uint32_t)(k * D + d);  // < kBB * D, fits 32 bits
@@ -393,7 +406,7 @@ __device__ __forceinline__ void bwd_reverse(const T* lds, const float* bcl, floa
 // A workgroup holds WV waves on adjacent channel groups of one chunk: they
 // share the staged B/C rows of each block, and add their per-token dB/dC sums
 // in LDS, so one partial row per WV*64/LPC channels reaches memory.
-template <typename T, int NS, int LPC, int WV, bool GATE>
+template <typename T, int NS, int LPC, int WV, bool GATE, bool XS>
 __global__ __launch_bounds__(kWave * WV, 2) void k_scan_bwd_main(BwdArgs<T> p) {
     constexpr int NH = NS / LPC;      // states per lane
     constexpr int CW = kWave / LPC;   // channels per wave
@@ -436,7 +449,9 @@ __global__ __launch_bounds__(kWave * WV, 2) void k_scan_bwd_main(BwdArgs<T> p) {
         dA[i] = 0.0f;
     }
     const float Dv = (p.Dskip && act) ? p.Dskip[dd] : 0.0f;
-    float dDacc = 0.0f;
+    float dDacc = 0.0f, dbacc = 0.0f;
+    const StepMap sm = step_map(p.opt, dd);
+    const float gf = p.opt.gate_floor;
     const T* const src[4] = {p.u, p.delta, GATE ? p.z : p.u, p.dout};
 
     // B/C rows of a block: kBB * 2NS floats, fetched with the block's inputs
@@ -506,13 +521,15 @@ __global__ __launch_bounds__(kWave * WV, 2) void k_scan_bwd_main(BwdArgs<T> p) {
             if (tb0 + kb - kK >= t0) load_state(tb0 + kb - kK, hn);
             const uint32_t sub_heads = (heads >> kb) & ((1u << kK) - 1u);
             if (sub_heads == 0 && ns == kK) {
-                bwd_replay<false, NS, LPC, St>(mylds, bcl, kb, kK, 0u, ch, n0, A2, h, hh, yk, Dv);
-                bwd_reverse<false, GATE, NS, LPC, St>(mylds, bcl, red[wv], kb, kK, 0u, lane, ch, sh, n0, act, full,
-                                                      D, d, A2, carry, dA, dDacc, Dv, hin, hh, yk, rows);
+                bwd_replay<false, XS, NS, LPC, St>(mylds, bcl, kb, kK, 0u, ch, n0, A2, h, hh, yk, Dv, sm);
+                bwd_reverse<false, GATE, XS, NS, LPC, St>(mylds, bcl, red[wv], kb, kK, 0u, lane, ch, sh, n0, act,
+                                                          full, D, d, A2, carry, dA, dDacc, Dv, hin, hh, yk, rows,
+                                                          sm, gf, dbacc);
             } else {
-                bwd_replay<true, NS, LPC, St>(mylds, bcl, kb, ns, heads, ch, n0, A2, h, hh, yk, Dv);
-                bwd_reverse<true, GATE, NS, LPC, St>(mylds, bcl, red[wv], kb, ns, heads, lane, ch, sh, n0, act, full,
-                                                     D, d, A2, carry, dA, dDacc, Dv, hin, hh, yk, rows);
+                bwd_replay<true, XS, NS, LPC, St>(mylds, bcl, kb, ns, heads, ch, n0, A2, h, hh, yk, Dv, sm);
+                bwd_reverse<true, GATE, XS, NS, LPC, St>(mylds, bcl, red[wv], kb, ns, heads, lane, ch, sh, n0, act,
+                                                         full, D, d, A2, carry, dA, dDacc, Dv, hin, hh, yk, rows,
+                                                         sm, gf, dbacc);
             }
         }
 
@@ -530,6 +547,7 @@ __global__ __launch_bounds__(kWave * WV, 2) void k_scan_bwd_main(BwdArgs<T> p) {
 #pragma unroll
         for (int i = 0; i < NH; ++i) p.dApart[(size_t)c * ND + (size_t)(n0 + i) * D + d] = dA[i];
         if (sh == 0) p.dDpart[(size_t)c * D + d] = dDacc;
+        if (XS && sh == 0) p.dbpart[(size_t)c * D + d] = dbacc;
     }
 }
 
@@ -538,9 +556,10 @@ __global__ __launch_bounds__(kWave * WV, 2) void k_scan_bwd_main(BwdArgs<T> p) {
 // ---------------------------------------------------------------------------
 template <int NS>
 __global__ __launch_bounds__(256) void k_scan_bwd_reduce_params(const float* __restrict__ dApart,
-                                                                const float* __restrict__ dDpart, int64_t nchunk,
+                                                                const float* __restrict__ dDpart,
+                                                                const float* __restrict__ dbpart, int64_t nchunk,
                                                                 int D, float* __restrict__ dA,
-                                                                float* __restrict__ dD) {
+                                                                float* __restrict__ dD, float* __restrict__ dbias) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // n*D + d
     const int64_t ND = (int64_t)NS * D;
     if (i < ND) {
@@ -549,6 +568,7 @@ __global__ __launch_bounds__(256) void k_scan_bwd_reduce_params(const float* __r
         dA[(size_t)d * NS + n] = acc;
     }
     if (dD && i < D) dD[i] = ordered_sum(dDpart + i, nchunk, (size_t)D);
+    if (dbias && i < D) dbias[i] = ordered_sum(dbpart + i, nchunk, (size_t)D);
 }
 
 template <int NS>
@@ -568,7 +588,7 @@ template <typename T, int NS>
 static int scan_bwd_launch(const void* u, const void* delta, const float* A, const void* B, const void* C,
                            const float* Dskip, const void* z, const int32_t* pos, const void* dout, float* ws,
                            void* du, void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, int64_t T_,
-                           int D, hipStream_t s) {
+                           int D, const ScanOpts& opt, float* dbias, hipStream_t s) {
     const ScanWs L = scan_ws_layout(T_, D, NS);
     const int lc = bwd_chunk_len(T_, D, NS);
     const int64_t nchunk = (T_ + lc - 1) / lc;
@@ -584,11 +604,11 @@ static int scan_bwd_launch(const void* u, const void* delta, const float* A, con
         if (z)
             k_scan_bwd_summary<T, NS, true><<<grid, kWave, 0, s>>>((const T*)delta, A, ws + L.bc, (const T*)z,
                                                                    (const T*)dout, pos, ws + L.Pr, ws + L.Sr, T_, D,
-                                                                   vec, ls);
+                                                                   vec, ls, opt);
         else
             k_scan_bwd_summary<T, NS, false><<<grid, kWave, 0, s>>>((const T*)delta, A, ws + L.bc, nullptr,
                                                                     (const T*)dout, pos, ws + L.Pr, ws + L.Sr, T_, D,
-                                                                    vec, ls);
+                                                                    vec, ls, opt);
         SSMP_LAUNCH_CHECK();
     }
     k_scan_bwd_carry<NS><<<(unsigned)((ND + 255) / 256), 256, 0, s>>>(ws + L.Pr, ws + L.Sr, A, pos, ws + L.cin,
@@ -598,19 +618,27 @@ static int scan_bwd_launch(const void* u, const void* delta, const float* A, con
     a.u = (const T*)u; a.delta = (const T*)delta; a.A = A; a.bc = ws + L.bc; a.Dskip = Dskip;
     a.z = (const T*)z; a.dout = (const T*)dout; a.pos = pos; a.ckpt = ws + L.ckpt; a.cin = ws + L.cin;
     a.du = (T*)du; a.ddelta = (T*)ddelta; a.dz = (T*)dz; a.dApart = ws + L.dApart; a.dDpart = ws + L.dDpart;
-    a.dBC = ws + L.dBC; a.T_ = T_; a.D = D; a.vec = vec; a.lc = lc;
+    a.dbpart = ws + L.dbpart; a.dBC = ws + L.dBC; a.T_ = T_; a.D = D; a.vec = vec; a.lc = lc; a.opt = opt;
     constexpr int LPC = NS >= 4 ? 2 : 1;  // bwd_lanes_per_channel
     constexpr int WV = bwd_waves_per_group(sizeof(T));
     const int64_t ngroup = bwd_bc_groups(D, NS, sizeof(T));
     const dim3 mgrid((unsigned)(ngroup * nchunk));
-    if (z)
-        k_scan_bwd_main<T, NS, LPC, WV, true><<<mgrid, kWave * WV, 0, s>>>(a);
-    else
-        k_scan_bwd_main<T, NS, LPC, WV, false><<<mgrid, kWave * WV, 0, s>>>(a);
+    const bool xs = opt.delta_bias != nullptr || opt.softplus != 0;
+    if (z) {
+        if (xs)
+            k_scan_bwd_main<T, NS, LPC, WV, true, true><<<mgrid, kWave * WV, 0, s>>>(a);
+        else
+            k_scan_bwd_main<T, NS, LPC, WV, true, false><<<mgrid, kWave * WV, 0, s>>>(a);
+    } else {
+        if (xs)
+            k_scan_bwd_main<T, NS, LPC, WV, false, true><<<mgrid, kWave * WV, 0, s>>>(a);
+        else
+            k_scan_bwd_main<T, NS, LPC, WV, false, false><<<mgrid, kWave * WV, 0, s>>>(a);
+    }
     SSMP_LAUNCH_CHECK();
     const int64_t nrp = ND > D ? ND : D;
-    k_scan_bwd_reduce_params<NS><<<(unsigned)((nrp + 255) / 256), 256, 0, s>>>(ws + L.dApart, ws + L.dDpart,
-                                                                               nchunk, D, dA, dD);
+    k_scan_bwd_reduce_params<NS><<<(unsigned)((nrp + 255) / 256), 256, 0, s>>>(
+        ws + L.dApart, ws + L.dDpart, ws + L.dbpart, nchunk, D, dA, dD, xs ? dbias : nullptr);
     SSMP_LAUNCH_CHECK();
     k_scan_bwd_reduce_bc<NS><<<(unsigned)((T_ * 2 * NS + 255) / 256), 256, 0, s>>>(ws + L.dBC, ngroup, T_, dB, dC);
     SSMP_LAUNCH_CHECK();
@@ -621,11 +649,11 @@ template <typename T>
 static int scan_bwd_dispatch(int N, const void* u, const void* delta, const float* A, const void* B, const void* C,
                              const float* Dskip, const void* z, const int32_t* pos, const void* dout, float* ws,
                              void* du, void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz,
-                             int64_t T_, int D, hipStream_t s) {
+                             int64_t T_, int D, const ScanOpts& o, float* dbias, hipStream_t s) {
 #define SSMP_BWD_CASE(NV)                                                                                         \
     case NV:                                                                                                      \
         return scan_bwd_launch<T, NV>(u, delta, A, B, C, Dskip, z, pos, dout, ws, du, ddelta, dA, dB, dC, dD, dz, \
-                                      T_, D, s);
+                                      T_, D, o, dbias, s);
     switch (N) {
         SSMP_BWD_CASE(1)
         SSMP_BWD_CASE(2)
@@ -639,28 +667,42 @@ static int scan_bwd_dispatch(int N, const void* u, const void* delta, const floa
 
 }  // namespace ssmp
 
-extern "C" int selective_scan_pack_bwd(const void* u, const void* delta, const float* A, const void* B,
-                                       const void* C, const float* Dskip, const void* z, const int32_t* pos,
-                                       const void* dout, void* workspace, size_t workspace_bytes, void* du,
-                                       void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz,
-                                       int64_t T, int32_t D, int32_t N, int32_t dtype, void* stream) {
+extern "C" int selective_scan_pack_bwd_ex(const void* u, const void* delta, const float* A, const void* B,
+                                          const void* C, const float* Dskip, const void* z, const int32_t* pos,
+                                          const void* dout, void* workspace, size_t workspace_bytes, void* du,
+                                          void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz,
+                                          int64_t T, int32_t D, int32_t N, int32_t dtype, const float* delta_bias,
+                                          int32_t delta_softplus, float gate_floor, float* ddelta_bias,
+                                          void* stream) {
     using namespace ssmp;
     int st = scan_check_args(T, D, N, dtype);
     if (st) return st;
     if (!A || !dA) return SSMP_ERR_NULL;
     if ((Dskip == nullptr) != (dD == nullptr)) return SSMP_ERR_NULL;
     if ((z == nullptr) != (dz == nullptr)) return SSMP_ERR_NULL;
+    if ((delta_bias == nullptr) != (ddelta_bias == nullptr)) return SSMP_ERR_NULL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (T == 0) {
-        if (hipMemsetAsync(dA, 0, sizeof(float) * (size_t)D * N, s) != hipSuccess) return SSMP_ERR_HIP;
-        if (dD && hipMemsetAsync(dD, 0, sizeof(float) * (size_t)D, s) != hipSuccess) return SSMP_ERR_HIP;
-        return SSMP_OK;
+        // empty input: the sums are zero
+        if ((st = zero_f32(dA, (int64_t)D * N, s))) return st;
+        if ((st = zero_f32(dD, D, s))) return st;
+        return zero_f32(ddelta_bias, D, s);
     }
     if (!u || !delta || !B || !C || !pos || !dout || !du || !ddelta || !dB || !dC) return SSMP_ERR_NULL;
     if (!workspace || workspace_bytes < selective_scan_pack_workspace_bytes(T, D, N)) return SSMP_ERR_WORKSPACE;
     float* ws = static_cast<float*>(workspace);
+    const ScanOpts o{delta_bias, delta_softplus != 0 ? 1 : 0, gate_floor};
     return dtype == SSMP_BF16 ? scan_bwd_dispatch<uint16_t>(N, u, delta, A, B, C, Dskip, z, pos, dout, ws, du,
-                                                            ddelta, dA, dB, dC, dD, dz, T, D, s)
+                                                            ddelta, dA, dB, dC, dD, dz, T, D, o, ddelta_bias, s)
                               : scan_bwd_dispatch<float>(N, u, delta, A, B, C, Dskip, z, pos, dout, ws, du, ddelta,
-                                                         dA, dB, dC, dD, dz, T, D, s);
+                                                         dA, dB, dC, dD, dz, T, D, o, ddelta_bias, s);
+}
+
+extern "C" int selective_scan_pack_bwd(const void* u, const void* delta, const float* A, const void* B,
+                                       const void* C, const float* Dskip, const void* z, const int32_t* pos,
+                                       const void* dout, void* workspace, size_t workspace_bytes, void* du,
+                                       void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz,
+                                       int64_t T, int32_t D, int32_t N, int32_t dtype, void* stream) {
+    return selective_scan_pack_bwd_ex(u, delta, A, B, C, Dskip, z, pos, dout, workspace, workspace_bytes, du, ddelta,
+                                      dA, dB, dC, dD, dz, T, D, N, dtype, nullptr, 0, 0.0f, nullptr, stream);
 }

@@ -52,6 +52,45 @@ inline int bwd_sum_len(int64_t T, int D, int N) {
     return ls < kLCMin ? kLCMin : ls;
 }
 
+// Optional element-wise neighbours of the scan, applied where the scan reads
+// its inputs: the step is softplus(delta + bias[d]) (softplus set) or
+// delta + bias[d] (bias may be null), and the gate is silu(z) + gate_floor.
+struct ScanOpts {
+    const float* delta_bias;
+    int softplus;
+    float gate_floor;
+};
+
+// softplus(v) = max(v, 0) + log1p(exp(-|v|)); log1p(e) as log(w) e / (w - 1)
+// with w = 1 + e (exact-ish when e is tiny, where w - 1 rounds).
+__device__ __forceinline__ float softplus_f(float v) {
+    const float e = exp2_fast(-__builtin_fabsf(v) * kLog2e);
+    const float w = 1.0f + e;
+    const float lp = (w == 1.0f) ? e : __builtin_amdgcn_logf(w) * kLn2 * (e / (w - 1.0f));
+    return __builtin_fmaxf(v, 0.0f) + lp;
+}
+
+// The step map of one channel. Off (no bias, no softplus) it is the identity,
+// and every call site tests `on` first: a wave-uniform branch.
+struct StepMap {
+    float bias;
+    bool sp;
+    bool on;
+    __device__ __forceinline__ float eff(float raw) const {
+        const float v = raw + bias;
+        return sp ? softplus_f(v) : v;
+    }
+    // d eff / d raw
+    __device__ __forceinline__ float slope(float raw) const { return sp ? sigmoid_fast(raw + bias) : 1.0f; }
+};
+__device__ __forceinline__ StepMap step_map(const ScanOpts& o, int d) {
+    StepMap m;
+    m.bias = o.delta_bias ? o.delta_bias[d] : 0.0f;
+    m.sp = o.softplus != 0;
+    m.on = o.delta_bias != nullptr || o.softplus != 0;
+    return m;
+}
+
 struct ScanWs {
     int64_t nck;      // checkpoint slots: slot j holds the state entering token j*kCK
     int64_t nchunk;   // chunks (the larger count of the forward's and the backward's chunking)
@@ -65,6 +104,7 @@ struct ScanWs {
     size_t cin;       // [nchunk][N][D]   backward: carry entering each chunk from the right
     size_t dApart;    // [nchunk][N][D]
     size_t dDpart;    // [nchunk][D]
+    size_t dbpart;    // [nchunk][D]      backward: step-bias gradient partials
     size_t dBC;       // [<= ceil(D/64)][T][2N]  per channel-group partial sums of dB, dC
     size_t total;     // floats
 };
@@ -92,7 +132,8 @@ inline ScanWs scan_ws_layout(int64_t T, int D, int N) {
     w.cin = up(w.Sr + (size_t)w.nsum * ND);
     w.dApart = up(w.cin + (size_t)w.nchunk * ND);
     w.dDpart = up(w.dApart + (size_t)w.nchunk * ND);
-    w.dBC = up(w.dDpart + (size_t)w.nchunk * D);
+    w.dbpart = up(w.dDpart + (size_t)w.nchunk * D);
+    w.dBC = up(w.dbpart + (size_t)w.nchunk * D);
     const size_t bwd_end = up(w.dBC + (size_t)((D + kWave - 1) / kWave) * (size_t)T * 2 * N);
     w.total = fwd_end > bwd_end ? fwd_end : bwd_end;
     return w;

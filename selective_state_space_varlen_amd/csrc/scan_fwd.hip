@@ -43,7 +43,7 @@ __device__ __forceinline__ void load_rowv(const float* __restrict__ p, float (&v
 template <bool SAFE, typename T, int NS, int BT, typename St>
 __device__ __forceinline__ void summary_block(const T* lds, const float* __restrict__ bc, int64_t tb, int first,
                                               int nt, const float (&A2)[NS], float (&h)[NS], float& sdt, float& cdt,
-                                              int lane) {
+                                              int lane, const StepMap& sm) {
     // the block's per-lane inputs are read from LDS before the first scalar
     // load: a wait for LDS data also waits for scalar loads in flight
     float dtv[BT], uv[BT];
@@ -51,6 +51,10 @@ __device__ __forceinline__ void summary_block(const T* lds, const float* __restr
     for (int k = 0; k < BT; ++k) {
         dtv[k] = St::get(lds, 1, k, lane);
         uv[k] = St::get(lds, 0, k, lane);
+    }
+    if (sm.on) {
+#pragma unroll
+        for (int k = 0; k < BT; ++k) dtv[k] = sm.eff(dtv[k]);
     }
     const float* __restrict__ rows = bc + (size_t)tb * 2 * NS;
     float cur[NS];
@@ -84,7 +88,8 @@ template <typename T, int NS>
 __global__ __launch_bounds__(64, 4) void k_scan_fwd_summary(const T* __restrict__ u, const T* __restrict__ delta,
                                                          const float* __restrict__ A, const float* __restrict__ bc,
                                                          const int32_t* __restrict__ pos, float* __restrict__ P,
-                                                         float* __restrict__ S, int64_t T_, int D, int vec, int lc) {
+                                                         float* __restrict__ S, int64_t T_, int D, int vec, int lc,
+                                                         ScanOpts opt) {
     constexpr int BT = kFwdBlock;
     using St = Stager<T, 2, BT>;
     __shared__ __attribute__((aligned(16))) T lds[St::kElems];
@@ -117,6 +122,7 @@ __global__ __launch_bounds__(64, 4) void k_scan_fwd_summary(const T* __restrict_
         A2[n] = A[(size_t)dd * NS + n] * kLog2e;
         h[n] = 0.0f;
     }
+    const StepMap sm = step_map(opt, dd);
     float sdt = 0.0f, cdt = 0.0f;
     const T* const src[2] = {u, delta};
     St st;
@@ -130,9 +136,9 @@ __global__ __launch_bounds__(64, 4) void k_scan_fwd_summary(const T* __restrict_
         const int first = (int)((ts > tb) ? ts - tb : 0);
         const int nt = (int)((tb + BT < t1) ? BT : t1 - tb);
         if (first == 0 && nt == BT)
-            summary_block<false, T, NS, BT, St>(lds, bc, tb, 0, BT, A2, h, sdt, cdt, lane);
+            summary_block<false, T, NS, BT, St>(lds, bc, tb, 0, BT, A2, h, sdt, cdt, lane, sm);
         else
-            summary_block<true, T, NS, BT, St>(lds, bc, tb, first, nt, A2, h, sdt, cdt, lane);
+            summary_block<true, T, NS, BT, St>(lds, bc, tb, first, nt, A2, h, sdt, cdt, lane, sm);
     }
     if (act) {
         // the chunk's decay exp2(A2[n] * sdt) depends on n only through A: keep
@@ -221,11 +227,11 @@ __global__ __launch_bounds__(256) void k_scan_fwd_carry(const float* __restrict_
 // The state entering every kCK-th token goes to its checkpoint slot (ck:
 // the slot of the block's first token), except at the chunk start (skip0),
 // whose slot the carry pass wrote.
-template <bool SAFE, bool GATE, typename T, int NS, int BT, typename St>
+template <bool SAFE, bool GATE, bool XS, typename T, int NS, int BT, typename St>
 __device__ __forceinline__ void out_block(const T* lds, const float* __restrict__ bc, int64_t tb, int nt,
                                           uint32_t heads, const float (&A2)[NS], float (&h)[NS], float Dv, int lane,
                                           T* __restrict__ ob, int D, int d, bool store, float* __restrict__ ck,
-                                          size_t ND, bool skip0, bool act) {
+                                          size_t ND, bool skip0, bool act, const StepMap& sm, float gf) {
     // the block's per-lane inputs are read from LDS before the first scalar
     // load: a wait for LDS data also waits for scalar loads in flight
     float dtv[BT], uv[BT], zv[BT];
@@ -234,6 +240,10 @@ __device__ __forceinline__ void out_block(const T* lds, const float* __restrict_
         dtv[k] = St::get(lds, 1, k, lane);
         uv[k] = St::get(lds, 0, k, lane);
         if constexpr (GATE) zv[k] = St::get(lds, 2, k, lane);
+    }
+    if constexpr (XS) {
+#pragma unroll
+        for (int k = 0; k < BT; ++k) dtv[k] = sm.eff(dtv[k]);
     }
     const float* __restrict__ rows = bc + (size_t)tb * 2 * NS;
     float cur[2 * NS];
@@ -263,7 +273,7 @@ __device__ __forceinline__ void out_block(const T* lds, const float* __restrict_
         y = __builtin_fmaf(Dv, uu, y);
         if constexpr (GATE) {
             const float zz = zv[k];
-            y *= zz * sigmoid_fast(zz);
+            y *= __builtin_fmaf(zz, sigmoid_fast(zz), gf);
         }
         if (store) Elt<T>::st(ob, (size_t)(k * D + d), y);
         if (more) {
@@ -273,12 +283,13 @@ __device__ __forceinline__ void out_block(const T* lds, const float* __restrict_
     }
 }
 
-template <typename T, int NS, bool GATE>
+template <typename T, int NS, bool GATE, bool XS>
 __global__ __launch_bounds__(64, 4) void k_scan_fwd_out(const T* __restrict__ u, const T* __restrict__ delta,
                                                      const float* __restrict__ A, const float* __restrict__ bc,
                                                      const float* __restrict__ Dskip, const T* __restrict__ z,
                                                      const int32_t* __restrict__ pos, T* __restrict__ out,
-                                                     float* __restrict__ ckpt, int64_t T_, int D, int vec, int lc) {
+                                                     float* __restrict__ ckpt, int64_t T_, int D, int vec, int lc,
+                                                     ScanOpts opt) {
     constexpr int BT = kFwdBlock;
     using St = Stager<T, 3, BT>;
     __shared__ __attribute__((aligned(16))) T lds[St::kElems];
@@ -300,6 +311,7 @@ __global__ __launch_bounds__(64, 4) void k_scan_fwd_out(const T* __restrict__ u,
         h[n] = act ? ckpt[(size_t)(t0 / kCK) * ND + (size_t)n * D + dd] : 0.0f;
     }
     const float Dv = (Dskip && act) ? Dskip[dd] : 0.0f;
+    const StepMap sm = step_map(opt, dd);
     const T* const src[3] = {u, delta, GATE ? z : u};
     St st;
     st.fetch(src, t0, T_, D, tl.g, lane, vec);
@@ -313,18 +325,18 @@ __global__ __launch_bounds__(64, 4) void k_scan_fwd_out(const T* __restrict__ u,
         T* __restrict__ ob = out + (size_t)tb * D;
         float* __restrict__ ck = ckpt + (size_t)(tb / kCK) * ND;
         if (heads == 0 && nt == BT)
-            out_block<false, GATE, T, NS, BT, St>(lds, bc, tb, BT, 0u, A2, h, Dv, lane, ob, D, d, store, ck, ND,
-                                                  tb == t0, act);
+            out_block<false, GATE, XS, T, NS, BT, St>(lds, bc, tb, BT, 0u, A2, h, Dv, lane, ob, D, d, store, ck, ND,
+                                                  tb == t0, act, sm, opt.gate_floor);
         else
-            out_block<true, GATE, T, NS, BT, St>(lds, bc, tb, nt, heads, A2, h, Dv, lane, ob, D, d, store, ck, ND,
-                                                 tb == t0, act);
+            out_block<true, GATE, XS, T, NS, BT, St>(lds, bc, tb, nt, heads, A2, h, Dv, lane, ob, D, d, store, ck, ND,
+                                                 tb == t0, act, sm, opt.gate_floor);
     }
 }
 
 template <typename T, int NS>
 static int scan_fwd_launch(const void* u, const void* delta, const float* A, const void* B, const void* C,
                            const float* Dskip, const void* z, const int32_t* pos, void* out, float* ws, int64_t T_,
-                           int D, hipStream_t s) {
+                           int D, const ScanOpts& opt, hipStream_t s) {
     const ScanWs L = scan_ws_layout(T_, D, NS);
     const int lc = fwd_chunk_len(T_, D);
     const int64_t nchunk = (T_ + lc - 1) / lc;
@@ -335,19 +347,24 @@ static int scan_fwd_launch(const void* u, const void* delta, const float* A, con
     SSMP_LAUNCH_CHECK();
     if (nchunk > 1) {
         k_scan_fwd_summary<T, NS><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, ws + L.bc, pos, ws + L.P,
-                                                         ws + L.S, T_, D, vec, lc);
+                                                         ws + L.S, T_, D, vec, lc, opt);
         SSMP_LAUNCH_CHECK();
     }
     const int64_t ND = (int64_t)NS * D;
     k_scan_fwd_carry<NS><<<(unsigned)((ND + 255) / 256), 256, 0, s>>>(ws + L.P, ws + L.S, A, pos, ws + L.ckpt, T_,
                                                                       D, nchunk, lc);
     SSMP_LAUNCH_CHECK();
-    if (z)
-        k_scan_fwd_out<T, NS, true><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, ws + L.bc, Dskip,
-                                                           (const T*)z, pos, (T*)out, ws + L.ckpt, T_, D, vec, lc);
-    else
-        k_scan_fwd_out<T, NS, false><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, ws + L.bc, Dskip,
-                                                            nullptr, pos, (T*)out, ws + L.ckpt, T_, D, vec, lc);
+    const bool xs = opt.delta_bias != nullptr || opt.softplus != 0;
+#define SSMP_FWD_OUT(G, X)                                                                                       \
+    k_scan_fwd_out<T, NS, G, X><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, ws + L.bc, Dskip,         \
+                                                       G ? (const T*)z : nullptr, pos, (T*)out, ws + L.ckpt, T_, D, \
+                                                       vec, lc, opt)
+    if (z) {
+        if (xs) SSMP_FWD_OUT(true, true); else SSMP_FWD_OUT(true, false);
+    } else {
+        if (xs) SSMP_FWD_OUT(false, true); else SSMP_FWD_OUT(false, false);
+    }
+#undef SSMP_FWD_OUT
     SSMP_LAUNCH_CHECK();
     return SSMP_OK;
 }
@@ -355,13 +372,13 @@ static int scan_fwd_launch(const void* u, const void* delta, const float* A, con
 template <typename T>
 static int scan_fwd_dispatch(int N, const void* u, const void* delta, const float* A, const void* B, const void* C,
                              const float* Dskip, const void* z, const int32_t* pos, void* out, float* ws, int64_t T_,
-                             int D, hipStream_t s) {
+                             int D, const ScanOpts& o, hipStream_t s) {
     switch (N) {
-        case 1: return scan_fwd_launch<T, 1>(u, delta, A, B, C, Dskip, z, pos, out, ws, T_, D, s);
-        case 2: return scan_fwd_launch<T, 2>(u, delta, A, B, C, Dskip, z, pos, out, ws, T_, D, s);
-        case 4: return scan_fwd_launch<T, 4>(u, delta, A, B, C, Dskip, z, pos, out, ws, T_, D, s);
-        case 8: return scan_fwd_launch<T, 8>(u, delta, A, B, C, Dskip, z, pos, out, ws, T_, D, s);
-        case 16: return scan_fwd_launch<T, 16>(u, delta, A, B, C, Dskip, z, pos, out, ws, T_, D, s);
+        case 1: return scan_fwd_launch<T, 1>(u, delta, A, B, C, Dskip, z, pos, out, ws, T_, D, o, s);
+        case 2: return scan_fwd_launch<T, 2>(u, delta, A, B, C, Dskip, z, pos, out, ws, T_, D, o, s);
+        case 4: return scan_fwd_launch<T, 4>(u, delta, A, B, C, Dskip, z, pos, out, ws, T_, D, o, s);
+        case 8: return scan_fwd_launch<T, 8>(u, delta, A, B, C, Dskip, z, pos, out, ws, T_, D, o, s);
+        case 16: return scan_fwd_launch<T, 16>(u, delta, A, B, C, Dskip, z, pos, out, ws, T_, D, o, s);
         default: return SSMP_ERR_UNSUPPORTED;
     }
 }
@@ -373,10 +390,11 @@ extern "C" size_t selective_scan_pack_workspace_bytes(int64_t T, int32_t D, int3
     return ssmp::scan_ws_layout(T, D, N).total * sizeof(float);
 }
 
-extern "C" int selective_scan_pack_fwd(const void* u, const void* delta, const float* A, const void* B,
-                                       const void* C, const float* Dskip, const void* z, const int32_t* pos,
-                                       void* out, void* workspace, size_t workspace_bytes, int64_t T, int32_t D,
-                                       int32_t N, int32_t dtype, void* stream) {
+extern "C" int selective_scan_pack_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
+                                          const void* C, const float* Dskip, const void* z, const int32_t* pos,
+                                          void* out, void* workspace, size_t workspace_bytes, int64_t T, int32_t D,
+                                          int32_t N, int32_t dtype, const float* delta_bias, int32_t delta_softplus,
+                                          float gate_floor, void* stream) {
     using namespace ssmp;
     int st = scan_check_args(T, D, N, dtype);
     if (st) return st;
@@ -385,6 +403,15 @@ extern "C" int selective_scan_pack_fwd(const void* u, const void* delta, const f
     if (!workspace || workspace_bytes < selective_scan_pack_workspace_bytes(T, D, N)) return SSMP_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     float* ws = static_cast<float*>(workspace);
-    return dtype == SSMP_BF16 ? scan_fwd_dispatch<uint16_t>(N, u, delta, A, B, C, Dskip, z, pos, out, ws, T, D, s)
-                              : scan_fwd_dispatch<float>(N, u, delta, A, B, C, Dskip, z, pos, out, ws, T, D, s);
+    const ScanOpts o{delta_bias, delta_softplus != 0 ? 1 : 0, gate_floor};
+    return dtype == SSMP_BF16 ? scan_fwd_dispatch<uint16_t>(N, u, delta, A, B, C, Dskip, z, pos, out, ws, T, D, o, s)
+                              : scan_fwd_dispatch<float>(N, u, delta, A, B, C, Dskip, z, pos, out, ws, T, D, o, s);
+}
+
+extern "C" int selective_scan_pack_fwd(const void* u, const void* delta, const float* A, const void* B,
+                                       const void* C, const float* Dskip, const void* z, const int32_t* pos,
+                                       void* out, void* workspace, size_t workspace_bytes, int64_t T, int32_t D,
+                                       int32_t N, int32_t dtype, void* stream) {
+    return selective_scan_pack_fwd_ex(u, delta, A, B, C, Dskip, z, pos, out, workspace, workspace_bytes, T, D, N,
+                                      dtype, nullptr, 0, 0.0f, stream);
 }

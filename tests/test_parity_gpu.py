@@ -169,6 +169,53 @@ def test_scan_parity(orc, name):
         assert_close(npy(g["dz"]), rg["dz"], tg, "dz")
 
 
+# the step map (delta_bias, softplus) and the gate floor (selective_scan_pack_*_ex)
+EXT_CASES = {
+    "softplus-bias-floor": dict(wl=2, lengths=[700, 1, 400, 1200], D=128, opts=(True, True, 0.05)),
+    "bias-only": dict(wl=2, lengths=[300, 2, 500], D=64, opts=(True, False, 0.0)),
+    "softplus-no-bias-no-gate": dict(wl=2, lengths=[400, 1, 299], D=64, gate=False, opts=(False, True, 0.0)),
+    "floor-only-fp32-n4": dict(wl=2, lengths=[255, 1, 256, 257], D=65, N=4, dtype=torch.float32,
+                               opts=(False, False, 0.1)),
+    "softplus-bias-fp32-n8": dict(wl=2, lengths=[600, 90], D=130, N=8, dtype=torch.float32,
+                                  opts=(True, True, 0.02)),
+}
+
+
+@pytest.mark.parametrize("name", list(EXT_CASES))
+def test_scan_ext_parity(orc, name):
+    spec = dict(EXT_CASES[name])
+    has_bias, sp, floor = spec.pop("opts")
+    gate = spec.pop("gate", True)
+    inp = synth.make_inputs(spec.pop("wl"), with_u=True, with_dout=True, **spec)
+    rng = np.random.default_rng(7)
+    bias = (rng.standard_normal(inp.D) * 0.5).astype(np.float32) if has_bias else None
+    # stored steps chosen so that the mapped step keeps the workload's values
+    d64 = synth.f64(inp.delta)
+    raw = (np.log(np.expm1(d64)) if sp else d64) - (bias[None, :] if has_bias else 0.0)
+    inp.delta = synth.to_dtype(raw, inp.dtype)
+    d = Dev(inp)
+    z = d.z if gate else None
+    bt = to_dev(torch.from_numpy(bias)) if has_bias else None
+    kw = dict(delta_bias=bt, delta_softplus=sp, gate_floor=floor)
+    out, ws = ssp().selective_scan_pack_fwd(d.u, d.delta, d.A, d.B, d.C, d.Dp, z, d.pos, **kw)
+    g = ssp().selective_scan_pack_bwd(d.u, d.delta, d.A, d.B, d.C, d.Dp, z, d.pos, d.dout, ws, **kw)
+    torch.cuda.synchronize()
+    pos, _ = orc.pack_indices(inp.cu_seqlens, inp.T)
+    args = (synth.f64(inp.u), synth.f64(inp.delta), synth.f64(inp.A), synth.f64(inp.B), synth.f64(inp.C),
+            synth.f64(inp.Dp), synth.f64(inp.z) if gate else None, pos)
+    okw = dict(delta_bias=None if bias is None else bias.astype(np.float64), delta_softplus=sp, gate_floor=floor)
+    _, rout = orc.scan_fwd(*args, threads=8, **okw)
+    rg = orc.scan_bwd(*args, synth.f64(inp.dout), threads=8, **okw)
+    to, tg = TOL_OUT[inp.dtype], TOL_GRAD[inp.dtype]
+    assert_close(npy(out), rout, to, "out")
+    for k in ("du", "ddelta", "dA", "dB", "dC", "dD"):
+        assert_close(npy(g[k]), rg[k], tg, k)
+    if gate:
+        assert_close(npy(g["dz"]), rg["dz"], tg, "dz")
+    if has_bias:
+        assert_close(npy(g["ddelta_bias"]), rg["ddelta_bias"], tg, "ddelta_bias")
+
+
 def test_scan_deterministic():
     inp, gate, skip = _scan_case("workload2-small")
     o1, g1 = run_scan_gpu(inp, gate, skip)
