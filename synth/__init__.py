@@ -92,6 +92,27 @@ class Inputs:
         return len(self.lengths)
 
 
+def _draw_length(rng: np.random.Generator, kind: str) -> int:
+    """One document length from a workload's length distribution."""
+    if kind == "lognormal":
+        L = int(round(math.exp(rng.normal(math.log(800.0), 1.0))))
+        return min(max(L, 16), 4096)
+    if kind == "uniform":
+        return int(rng.integers(64, 2048, endpoint=True))
+    if kind == "buckets":
+        k = int(rng.integers(0, len(BUCKETS)))
+        lo = 0 if k == 0 else BUCKETS[k - 1]
+        return int(rng.integers(lo + 1, BUCKETS[k], endpoint=True))
+    raise ValueError(kind)
+
+
+def document_lengths(workload: int, n: int, seed: int = 0) -> list:
+    """A stream of `n` whole (uncut) document lengths drawn from a workload's
+    length distribution, in arrival order: the input of a packer."""
+    rng = np.random.default_rng(seed)
+    return [_draw_length(rng, WORKLOADS[workload].lengths) for _ in range(n)]
+
+
 def _pack_lengths(rng: np.random.Generator, kind: str, n_packs: int, pack_len: int) -> list:
     """Sequence lengths, pack by pack; every pack is filled exactly (the last
     sequence of a pack is cut to the remainder)."""
@@ -103,18 +124,7 @@ def _pack_lengths(rng: np.random.Generator, kind: str, n_packs: int, pack_len: i
         left = pack_len
         pack = []
         while left > 0:
-            if kind == "lognormal":
-                L = int(round(math.exp(rng.normal(math.log(800.0), 1.0))))
-                L = min(max(L, 16), 4096)
-            elif kind == "uniform":
-                L = int(rng.integers(64, 2048, endpoint=True))
-            elif kind == "buckets":
-                k = int(rng.integers(0, len(BUCKETS)))
-                lo = 0 if k == 0 else BUCKETS[k - 1]
-                L = int(rng.integers(lo + 1, BUCKETS[k], endpoint=True))
-            else:
-                raise ValueError(kind)
-            L = min(L, left)
+            L = min(_draw_length(rng, kind), left)
             pack.append(L)
             left -= L
         if kind == "buckets":
