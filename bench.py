@@ -185,6 +185,54 @@ def padded_layout(inp: synth.Inputs, pack_len: int):
     return p
 
 
+# (name, strategy, window); window 0 means one window over the whole stream
+PACK_STRATEGIES = (("sequential", 0, 1), ("greedy_w16", 1, 16), ("greedy_w128", 1, 128),
+                   ("greedy_w1024", 1, 1024), ("greedy_all", 1, 0))
+
+
+def packing_report(n_docs: int = 20000) -> dict:
+    """Padding rate of the host packer (varlen_pack_plan) on streams of whole
+    documents drawn from each workload's length mix, packs of the workload's
+    pack length, and the packer's own host time."""
+    import selective_state_space_varlen_amd as ssp
+    out = {}
+    for w in (1, 2, 3):
+        cap = synth.WORKLOADS[w].pack_len
+        docs = synth.document_lengths(w, n_docs, seed=100 + w)
+        row = {"capacity": cap, "documents": n_docs, "tokens": int(sum(docs))}
+        for name, strategy, window in PACK_STRATEGIES:
+            t0 = time.perf_counter()
+            plan = ssp.varlen_pack_plan(docs, cap, strategy, window or n_docs)
+            ms = (time.perf_counter() - t0) * 1e3
+            row[name] = {"padding_rate": round(plan.padding_rate, 5), "packs": plan.n_packs, "host_ms": round(ms, 3)}
+        out[synth.NAMES[w]] = row
+    return out
+
+
+def planned_batch(wl_id: int, strategy: int):
+    """Whole documents of a workload's length mix, as many as arrival-order
+    packing puts into the workload's pack count, packed by `strategy` (one
+    window over the batch) into packs of the pack length; each pack's unused
+    tail becomes one extra segment, so the kernels run every padding slot.
+    Returns (inputs, useful tokens, padding rate)."""
+    import selective_state_space_varlen_amd as ssp
+    spec = synth.WORKLOADS[wl_id]
+    stream = synth.document_lengths(wl_id, 64 * spec.n_packs, seed=200 + wl_id)
+    first = ssp.varlen_pack_plan(stream, spec.pack_len, 0)
+    assert first.n_packs > spec.n_packs
+    docs = stream[:int(first.pack_bounds[spec.n_packs])]
+    plan = ssp.varlen_pack_plan(docs, spec.pack_len, strategy, len(docs))
+    segs = []
+    for p in range(plan.n_packs):
+        ids = plan.order[plan.pack_bounds[p]:plan.pack_bounds[p + 1]]
+        segs += [docs[i] for i in ids]
+        load = sum(docs[i] for i in ids)
+        if load < spec.pack_len:
+            segs.append(spec.pack_len - load)
+    inp = synth.make_inputs(wl_id, lengths=segs, with_dout=True)
+    return inp, int(sum(docs)), plan.padding_rate
+
+
 def per_sequence_loop(wl: Workload, steps: int, warmup: int) -> float:
     """The gradient-accumulation layout: one launch chain per sequence, then
     parameter gradients summed over sequences."""
@@ -328,6 +376,16 @@ def main():
         del wp, pinp
         ms_s = per_sequence_loop(wl, max(2, args.steps // 5), 1)
         layouts["per_sequence_loop"] = round(T / (ms_s * 1e-3), 1)
+        # whole documents packed by the host packer, padding run as tokens;
+        # the rate counts document tokens only
+        for name, strategy in (("planned_sequential", 0), ("planned_greedy", 1)):
+            qinp, useful, rate = planned_batch(wl_id, strategy)
+            wq = Workload(qinp)
+            nq = max(3, args.steps // 2)
+            ms_q, _ = time_steps(wq, nq, 2, per_op=False)
+            layouts[name] = round(useful / (ms_q / nq * 1e-3), 1)
+            layouts[name + "_padding_rate"] = round(rate, 5)
+            del wq, qinp
         log(f"[bench] layouts tokens/s: {layouts}")
         torch.cuda.empty_cache()
 
@@ -360,6 +418,7 @@ def main():
         "ops_algo_gbs": {k: round(v, 1) for k, v in ops_gbs.items()},
         "roofline": roofline,
         "layouts_tokens_per_s": layouts,
+        "packing": packing_report(),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

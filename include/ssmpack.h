@@ -14,8 +14,9 @@
  *  - Tensors are packed and token-major: a (T, D) tensor holds element
  *    (t, d) at t*D + d, contiguous. T is the total packed token count; a
  *    batch of packs is passed flattened, one cu_seqlens over all of them.
- *  - All tensor pointers are DEVICE pointers. The caller owns every buffer;
- *    the library never allocates. Workspace sizes are queried first.
+ *  - All tensor pointers are DEVICE pointers (except varlen_pack_plan, a
+ *    host function). The caller owns every buffer; the library never
+ *    allocates device memory. Workspace sizes are queried first.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
  *    default stream) and returns once its kernels are queued.
  *  - Host-checkable arguments are validated before anything is launched and
@@ -55,7 +56,8 @@ typedef enum { SSMP_F32 = 0, SSMP_BF16 = 1 } ssmp_dtype;
 const char *ssmp_status_string(int status);
 
 /* Version of this ABI (incremented on any change to the set of entry points
- * or their meaning; 2 added the _ex scan entry points). */
+ * or their meaning; 2 added the _ex scan entry points, 3 the host packer
+ * varlen_pack_plan). */
 int ssmp_abi_version(void);
 
 /*
@@ -189,6 +191,44 @@ int selective_scan_pack_bwd_ex(const void *u, const void *delta, const float *A,
                                int64_t T, int32_t D, int32_t N, int32_t dtype,
                                const float *delta_bias, int32_t delta_softplus, float gate_floor,
                                float *ddelta_bias, void *stream);
+
+/* Packing strategies of varlen_pack_plan. */
+enum ssmp_pack_strategy {
+    SSMP_PACK_SEQUENTIAL = 0,   /* arrival order, seal when the next does not fit */
+    SSMP_PACK_LOCAL_GREEDY = 1  /* first-fit decreasing inside windows */
+};
+
+/*
+ * varlen_pack_plan — which sequences share a pack of `capacity` tokens.
+ * [P5] section "结论与讨论": the article packs sequences in arrival order,
+ * sealing a pack when the next sequence does not fit (19.1% padding on its
+ * pretraining corpus), and notes that sorting a window of pending sequences
+ * and packing them greedily brings padding down to as little as 0.46%.
+ * SSMP_PACK_LOCAL_GREEDY takes the greedy rule to be first-fit decreasing
+ * inside each run of `window` consecutive sequences: longest first, ties in
+ * arrival order, each into the lowest-numbered pack of the window with room,
+ * the window's packs sealed when it ends. Deterministic.
+ *
+ * HOST function: every pointer is a host pointer; the call is synchronous,
+ * uses no GPU and allocates only host scratch (O(window)).
+ *   lengths      int32 [nseq], 0 <= lengths[i] <= capacity, arrival order
+ *   window       sequences per window (LOCAL_GREEDY; >= 1); ignored otherwise
+ *   order        int32 [nseq] out: sequence indices, pack by pack
+ *   pack_bounds  int32 [nseq+1] out: pack p holds order[pack_bounds[p] ..
+ *                pack_bounds[p+1]); entries 0..n_packs are written
+ *   cu_seqlens   int32 [nseq+1] out: cumulative lengths along `order`, the
+ *                cu_seqlens of the packed batch without padding tokens
+ *   max_seqlen   int32 [nseq] out: longest sequence of each pack (0..n_packs-1)
+ *   n_packs      int32 [1] out
+ *   padding      int64 [1] out: n_packs * capacity - sum(lengths)
+ * Errors: SSMP_ERR_NULL, SSMP_ERR_SHAPE (nseq < 0, capacity < 1, a length
+ * outside [0, capacity], window < 1 for LOCAL_GREEDY, total >= 2^31),
+ * SSMP_ERR_UNSUPPORTED (unknown strategy). Arguments are checked before
+ * any output is written.
+ */
+int varlen_pack_plan(const int32_t *lengths, int32_t nseq, int32_t capacity, int32_t strategy,
+                     int32_t window, int32_t *order, int32_t *pack_bounds, int32_t *cu_seqlens,
+                     int32_t *max_seqlen, int32_t *n_packs, int64_t *padding);
 
 #ifdef __cplusplus
 }

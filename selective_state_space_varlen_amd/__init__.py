@@ -6,6 +6,7 @@ pipeline helper that chains the calls of one Mamba block's sequence-wise part.
 """
 from .binding import (  # noqa: F401
     EXPORTED,
+    PackPlan,
     SsmpError,
     conv1d_pack_bwd,
     conv1d_pack_bwd_workspace_bytes,
@@ -15,5 +16,6 @@ from .binding import (  # noqa: F401
     selective_scan_pack_fwd,
     selective_scan_pack_workspace_bytes,
     varlen_pack_indices,
+    varlen_pack_plan,
 )
 from .pipeline import forward, backward  # noqa: F401

@@ -9,15 +9,18 @@ library is missing, every call raises.
 from __future__ import annotations
 
 import ctypes
+import dataclasses
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libssmpack.so")
 
 SSMP_F32, SSMP_BF16 = 0, 1
+SSMP_PACK_SEQUENTIAL, SSMP_PACK_LOCAL_GREEDY = 0, 1
 
 _c_i32, _c_i64, _c_sz, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
@@ -43,6 +46,8 @@ _SIGNATURES = {
                                                   _c_vp, _c_sz, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
                                                   _c_i64, _c_i32, _c_i32, _c_i32,
                                                   _c_vp, _c_i32, ctypes.c_float, _c_vp, _c_vp]),
+    "varlen_pack_plan": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp,
+                                        _c_vp, _c_vp]),
 }
 
 EXPORTED = tuple(_SIGNATURES)
@@ -112,6 +117,49 @@ def _call(name: str, *args):
 
 
 # ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class PackPlan:
+    """Result of varlen_pack_plan (host arrays). Pack p holds the sequences
+    order[pack_bounds[p]:pack_bounds[p+1]]; cu_seqlens runs along `order`."""
+    capacity: int
+    order: np.ndarray        # int32 [nseq]
+    pack_bounds: np.ndarray  # int32 [n_packs + 1]
+    cu_seqlens: np.ndarray   # int32 [nseq + 1]
+    max_seqlen: np.ndarray   # int32 [n_packs]
+    padding: int             # n_packs * capacity - total tokens
+
+    @property
+    def n_packs(self) -> int:
+        return len(self.pack_bounds) - 1
+
+    @property
+    def padding_rate(self) -> float:
+        """Share of the packs' token slots left as padding."""
+        slots = self.n_packs * self.capacity
+        return self.padding / slots if slots else 0.0
+
+
+def varlen_pack_plan(lengths, capacity: int, strategy: int = SSMP_PACK_SEQUENTIAL, window: int = 1) -> PackPlan:
+    """Host call: group sequences of the given lengths (arrival order) into
+    packs of `capacity` tokens. No GPU is used."""
+    ln = np.ascontiguousarray(np.asarray(lengths, dtype=np.int64))
+    if ln.ndim != 1 or (ln.size and (ln.min() < np.iinfo(np.int32).min or ln.max() > np.iinfo(np.int32).max)):
+        raise ValueError("lengths must be a 1-D sequence of int32 values")
+    ln = ln.astype(np.int32)
+    n = ln.size
+    order = np.empty(n, np.int32)
+    bounds = np.empty(n + 1, np.int32)
+    cu = np.empty(n + 1, np.int32)
+    mx = np.empty(max(n, 1), np.int32)
+    npk = np.zeros(1, np.int32)
+    pad = np.zeros(1, np.int64)
+    _call("varlen_pack_plan", ln.ctypes.data_as(_c_vp), n, capacity, strategy, window, order.ctypes.data_as(_c_vp),
+          bounds.ctypes.data_as(_c_vp), cu.ctypes.data_as(_c_vp), mx.ctypes.data_as(_c_vp),
+          npk.ctypes.data_as(_c_vp), pad.ctypes.data_as(_c_vp))
+    k = int(npk[0])
+    return PackPlan(capacity, order, bounds[:k + 1].copy(), cu, mx[:k].copy(), int(pad[0]))
+
+
 def varlen_pack_indices(cu_seqlens: torch.Tensor, T: int, heads: bool = True, dev_err: bool = True,
                         out: Optional[torch.Tensor] = None):
     """cu_seqlens (int32, device) -> (pos int32 [T], heads uint8 [T] or None,

@@ -16,9 +16,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libssmpack.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["pack_indices.hip", "conv1d_pack.hip", "scan_fwd.hip", "scan_bwd.hip"]
+SOURCES = ["pack_indices.hip", "conv1d_pack.hip", "scan_fwd.hip", "scan_bwd.hip", "pack_plan.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # keep hipcc from emitting packed-FP32 instructions
@@ -28,9 +29,18 @@ FLAGS = [
 ]
 
 
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE]
+
+
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    """.hip sources go through hipcc for gfx950; .cpp sources are host-only
+    code and go through the host compiler."""
+    stem, ext = os.path.splitext(src)
+    obj = os.path.join(BUILD, stem + ".o")
+    if ext == ".hip":
+        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    else:
+        cmd = [CXX, *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
@@ -39,7 +49,8 @@ def _compile(src: str) -> str:
 
 
 def build(verbose: bool = True) -> str:
-    """Compile every kernel source for gfx950 and link libssmpack.so."""
+    """Compile every kernel source for gfx950 (and the host sources) and link
+    libssmpack.so."""
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))

@@ -304,3 +304,52 @@ def test_padded_layout_matches_packed():
         assert_close(npy(pg[k][r]), npy(g[k][idx]), 2e-2, k)
     for k in ("dA", "dD"):
         assert_close(npy(pg[k]), npy(g[k]), 1e-3, k)
+
+
+def test_planned_layout_parity(orc):
+    """Whole documents grouped by the host packer (first-fit decreasing) into
+    packs of 1024 tokens, each pack's unused tail run as one extra segment:
+    the pipeline matches the oracle on that layout, and every document's rows
+    match the same document run in arrival order."""
+    docs = synth.document_lengths(1, 400, seed=9)
+    docs = [max(1, L // 4) for L in docs][:40]
+    cap = 1024
+    plan = ssp().varlen_pack_plan(docs, cap, 1, len(docs))
+    arrival = synth.make_inputs(1, D=64, lengths=docs, with_dout=True)
+    rows, segs = [], []
+    for p in range(plan.n_packs):
+        ids = plan.order[plan.pack_bounds[p]:plan.pack_bounds[p + 1]]
+        for i in ids:
+            rows.append(np.arange(arrival.cu_seqlens[i], arrival.cu_seqlens[i + 1]))
+            segs.append(docs[i])
+        tail = cap - sum(docs[i] for i in ids)
+        if tail:
+            rows.append(-np.ones(tail, dtype=np.int64))
+            segs.append(tail)
+    rows = np.concatenate(rows)
+    real = rows >= 0
+    assert plan.cu_seqlens[-1] == real.sum() == sum(docs)
+    import copy
+    planned = copy.copy(arrival)
+    for k in ("x", "z", "B", "C", "delta", "dout"):
+        t = getattr(arrival, k)
+        o = torch.ones((len(rows),) + tuple(t.shape[1:]), dtype=t.dtype)  # padding slots hold ones
+        o[torch.from_numpy(real)] = t[torch.from_numpy(rows[real])]
+        setattr(planned, k, o)
+    planned.lengths, planned.cu_seqlens, planned.T = segs, synth.cu_seqlens_of(segs), len(rows)
+    assert planned.T == plan.n_packs * cap
+
+    dp, da = Dev(planned), Dev(arrival)
+    Fp, Fa = dp.forward(), da.forward()
+    Gp, Ga = dp.backward(Fp), da.backward(Fa)
+    torch.cuda.synchronize()
+    R = oracle_pipeline(orc, planned, backward=True)
+    to, tg = TOL_OUT[planned.dtype], TOL_GRAD[planned.dtype]
+    assert_close(npy(Fp["out"]), R["out"], to, "out")
+    for k in ("dx", "dw", "db", "ddelta", "dA", "dB", "dC", "dD", "dz"):
+        assert_close(npy(Gp[k]), R[k], tg, k)
+    r = torch.from_numpy(real).cuda()
+    idx = torch.from_numpy(rows[real]).cuda()
+    assert_close(npy(Fp["out"][r]), npy(Fa["out"][idx]), to, "out vs arrival order")
+    for k in ("dx", "ddelta", "dz"):
+        assert_close(npy(Gp[k][r]), npy(Ga[k][idx]), tg, k + " vs arrival order")
