@@ -66,6 +66,20 @@ class Oracle:
         L.oracle_conv_bwd.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _ip,
                                       _dp, _dp, _dp, ctypes.c_int, _dp,
                                       ctypes.c_int32, ctypes.c_int32, _dp, _dp, _dp]
+        i64, i32 = ctypes.c_int64, ctypes.c_int32
+        L.oracle_conv_fwd_state.restype = ctypes.c_int
+        L.oracle_conv_fwd_state.argtypes = [i64, i32, i32, _ip, i32, _dp, _dp, _dp, ctypes.c_int, _dp,
+                                            i32, i32, _dp, _dp, _dp]
+        L.oracle_conv_bwd_state.restype = ctypes.c_int
+        L.oracle_conv_bwd_state.argtypes = [i64, i32, i32, _ip, i32, _dp, _dp, _dp, ctypes.c_int, _dp, _dp, _dp,
+                                            i32, i32, _dp, _dp, _dp, _dp]
+        L.oracle_scan_fwd_state.restype = ctypes.c_int
+        L.oracle_scan_fwd_state.argtypes = [i64, i32, i32, _ip, i32, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+                                            _dp, i32, ctypes.c_double, _dp, i32, i32, _dp, _dp, _dp]
+        L.oracle_scan_bwd_state.restype = ctypes.c_int
+        L.oracle_scan_bwd_state.argtypes = [i64, i32, i32, _ip, i32, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+                                            _dp, i32, ctypes.c_double, _dp, _dp, _dp, i32, i32,
+                                            _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
 
     # ---------------------------------------------------------------- helpers
     @staticmethod
@@ -180,6 +194,94 @@ class Oracle:
         if any(rcs):
             raise MemoryError("oracle_conv_bwd failed")
         return dx, dw, db
+
+    # ------------------------------------- sequences that continue across packs
+    # State layouts: h0/hT/dhT/dh0 (nseq, D, N); xc0/xcT/dxcT/dxc0 (nseq, W-1, D).
+    def conv_fwd_state(self, x, w, b, cu_seqlens, xc0=None, silu: bool = True, threads: int = 1):
+        """conv1d_pack with per-sequence conv context; returns (v, u, xcT)."""
+        x = self._d(x); w = self._d(w); b = self._d(b); xc0 = self._d(xc0)
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        T, D = x.shape
+        W = w.shape[1]
+        nseq = len(cu) - 1
+        v = np.zeros((T, D)); u = np.zeros((T, D)); xcT = np.zeros((nseq, W - 1, D))
+        rcs = self._run(self._blocks(D, threads), lambda d0, d1: self.lib.oracle_conv_fwd_state(
+            T, D, W, self._p(cu, _ip), nseq, self._p(x), self._p(w), self._p(b), int(silu), self._p(xc0),
+            d0, d1, self._p(v), self._p(u), self._p(xcT)))
+        if any(rcs):
+            raise ValueError(f"oracle_conv_fwd_state failed {rcs}")
+        return v, u, xcT
+
+    def conv_bwd_state(self, x, w, b, cu_seqlens, du, xc0=None, dxcT=None, silu: bool = True, threads: int = 1):
+        """Returns (dx, dw, db, dxc0)."""
+        x = self._d(x); w = self._d(w); b = self._d(b); du = self._d(du)
+        xc0 = self._d(xc0); dxcT = self._d(dxcT)
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        T, D = x.shape
+        W = w.shape[1]
+        nseq = len(cu) - 1
+        dx = np.zeros((T, D)); dw = np.zeros((D, W)); db = np.zeros(D); dxc0 = np.zeros((nseq, W - 1, D))
+        rcs = self._run(self._blocks(D, threads), lambda d0, d1: self.lib.oracle_conv_bwd_state(
+            T, D, W, self._p(cu, _ip), nseq, self._p(x), self._p(w), self._p(b), int(silu), self._p(xc0),
+            self._p(du), self._p(dxcT), d0, d1, self._p(dx), self._p(dw), self._p(db), self._p(dxc0)))
+        if any(rcs):
+            raise ValueError(f"oracle_conv_bwd_state failed {rcs}")
+        return dx, dw, db, dxc0
+
+    def scan_fwd_state(self, u, delta, A, B, C, Dp, z, cu_seqlens, h0=None, threads: int = 1,
+                       delta_bias=None, delta_softplus: bool = False, gate_floor: float = 0.0):
+        """Returns (y, out, hT)."""
+        u = self._d(u); delta = self._d(delta); A = self._d(A); B = self._d(B); C = self._d(C)
+        Dp = self._d(Dp); z = self._d(z); db = self._d(delta_bias); h0 = self._d(h0)
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        T, D = u.shape
+        N = A.shape[1]
+        nseq = len(cu) - 1
+        y = np.zeros((T, D)); out = np.zeros((T, D)); hT = np.zeros((nseq, D, N))
+        rcs = self._run(self._blocks(D, threads), lambda d0, d1: self.lib.oracle_scan_fwd_state(
+            T, D, N, self._p(cu, _ip), nseq, self._p(u), self._p(delta), self._p(A), self._p(B), self._p(C),
+            self._p(Dp), self._p(z), self._p(db), int(delta_softplus), float(gate_floor), self._p(h0),
+            d0, d1, self._p(y), self._p(out), self._p(hT)))
+        if any(rcs):
+            raise ValueError(f"oracle_scan_fwd_state failed {rcs}")
+        return y, out, hT
+
+    def scan_bwd_state(self, u, delta, A, B, C, Dp, z, cu_seqlens, dout, h0=None, dhT=None, threads: int = 1,
+                       delta_bias=None, delta_softplus: bool = False, gate_floor: float = 0.0):
+        """scan_bwd's gradients plus "dh0" (nseq, D, N)."""
+        u = self._d(u); delta = self._d(delta); A = self._d(A); B = self._d(B); C = self._d(C)
+        Dp = self._d(Dp); z = self._d(z); dout = self._d(dout); db = self._d(delta_bias)
+        h0 = self._d(h0); dhT = self._d(dhT)
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        T, D = u.shape
+        N = A.shape[1]
+        nseq = len(cu) - 1
+        du = np.zeros((T, D)); ddelta = np.zeros((T, D)); dA = np.zeros((D, N))
+        dDp = np.zeros(D); dz = np.zeros((T, D)); ddb = np.zeros(D); dh0 = np.zeros((nseq, D, N))
+        blocks = self._blocks(D, threads)
+        parts = [(np.zeros((T, N)), np.zeros((T, N))) for _ in blocks]
+
+        def one(i):
+            d0, d1 = blocks[i]
+            dB_i, dC_i = parts[i]
+            return self.lib.oracle_scan_bwd_state(
+                T, D, N, self._p(cu, _ip), nseq, self._p(u), self._p(delta), self._p(A), self._p(B),
+                self._p(C), self._p(Dp), self._p(z), self._p(db), int(delta_softplus), float(gate_floor),
+                self._p(h0), self._p(dout), self._p(dhT), d0, d1,
+                self._p(du), self._p(ddelta), self._p(dA), self._p(dB_i), self._p(dC_i),
+                self._p(dDp), self._p(dz), self._p(ddb), self._p(dh0))
+
+        rcs = self._run([(i,) for i in range(len(blocks))], one)
+        if any(rcs):
+            raise ValueError(f"oracle_scan_bwd_state failed {rcs}")
+        dB = np.zeros((T, N)); dC = np.zeros((T, N))
+        for dB_i, dC_i in parts:
+            dB += dB_i
+            dC += dC_i
+        res = {"du": du, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dz": dz, "dh0": dh0}
+        res["dD"] = dDp if Dp is not None else None
+        res["ddelta_bias"] = ddb if db is not None else None
+        return res
 
     # ------------------------------------------------------ the whole pipeline
     def forward(self, x, w, b, delta, A, B, C, Dp, z, cu_seqlens, threads: int = 1):

@@ -330,3 +330,279 @@ int oracle_conv_bwd(int64_t T, int32_t D, int32_t W, const int32_t *pos,
     free(gv);
     return ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------------
+ * Sequences that continue across packs.
+ *
+ * [P5] "结论与讨论" proposes cutting a sequence that overruns a pack into two
+ * pieces that keep passing state, so that packs need no padding; [P1]
+ * section 3.2 describes segment-wise runs that reset, or hand on, the conv
+ * and SSM states at segment starts. The plain definition: sequence s runs
+ * alone, but starting from a given SSM state h0[s] (instead of zero) and with
+ * the W-1 inputs that precede it, xc0[s], visible to the causal conv
+ * (instead of zeros); it hands on its final SSM state hT[s] and its last W-1
+ * conv inputs xcT[s]. A piece that continues a sequence, given the previous
+ * piece's hT and xcT, then computes exactly what the uncut sequence would.
+ *
+ * These functions walk each sequence's tokens [cu[s], cu[s+1]) directly.
+ * State layouts: h0, hT, dhT, dh0 are (nseq, D, N) at (s*D + d)*N + n;
+ * xc0, xcT, dxcT, dxc0 are (nseq, W-1, D) at (s*(W-1) + j)*D + d, j = 0 the
+ * oldest input, j = W-2 the one just before the sequence's first token.
+ * Every state pointer may be NULL: a NULL initial state is zero, a NULL
+ * final-state gradient is zero, a NULL output is not written.
+ * ------------------------------------------------------------------------ */
+
+/* Input i of sequence s's extended input [xc0[s]; x[cu[s]:cu[s+1]]]:
+ * x itself for i >= cu[s], the conv context for cu[s]-(W-1) <= i < cu[s]. */
+static double conv_input(const double *x, const double *xc0, const int32_t *cu, int32_t s,
+                         int64_t i, int32_t D, int32_t W, int32_t d)
+{
+    if (i >= cu[s]) return x[i * D + d];
+    if (!xc0) return 0.0;
+    const int64_t j = i - ((int64_t)cu[s] - (W - 1));
+    return xc0[((int64_t)s * (W - 1) + j) * D + d];
+}
+
+/*
+ * conv1d_pack forward with conv context per sequence:
+ *   v[t,d] = b[d] + sum_{k=0}^{W-1} w[d, W-1-k] * X_s(t-k)
+ * where X_s is the extended input above (taps that reach before the
+ * context's start do not exist: k <= W-1 never does). xcT[s][j] = X_s(cu[s+1]
+ * - (W-1) + j): the last W-1 inputs of the extended sequence.
+ * With xc0 NULL this is oracle_conv_fwd term for term.
+ */
+int oracle_conv_fwd_state(int64_t T, int32_t D, int32_t W, const int32_t *cu, int32_t nseq,
+                          const double *x, const double *w, const double *b, int silu,
+                          const double *xc0, int32_t d0, int32_t d1, double *v, double *u, double *xcT)
+{
+    if (cu[0] != 0 || (int64_t)cu[nseq] != T) return ORACLE_ERR_CU_SEQLENS;
+    for (int32_t s = 0; s < nseq; ++s) {
+        if (cu[s + 1] < cu[s]) return ORACLE_ERR_CU_SEQLENS;
+        for (int64_t t = cu[s]; t < cu[s + 1]; ++t) {
+            for (int32_t d = d0; d < d1; ++d) {
+                double acc = b ? b[d] : 0.0;
+                for (int32_t k = 0; k < W; ++k) {
+                    if (t - k < cu[s] && !xc0) continue;  /* zero context: no term */
+                    acc += w[(int64_t)d * W + (W - 1 - k)] * conv_input(x, xc0, cu, s, t - k, D, W, d);
+                }
+                if (v) v[t * D + d] = acc;
+                u[t * D + d] = silu ? acc * sigmoid(acc) : acc;
+            }
+        }
+        if (xcT) {
+            for (int32_t j = 0; j < W - 1; ++j)
+                for (int32_t d = d0; d < d1; ++d)
+                    xcT[((int64_t)s * (W - 1) + j) * D + d] =
+                        conv_input(x, xc0, cu, s, (int64_t)cu[s + 1] - (W - 1) + j, D, W, d);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * conv1d_pack backward with conv context: the chain rule of
+ * oracle_conv_fwd_state for the loss sum(du * u) + sum(dxcT * xcT).
+ *   gv[t]         = du[t] * silu'(v[t])   (du[t] when silu is off)
+ *   db[d]         = sum_t gv[t]
+ *   dw[d, W-1-k]  = sum_t gv[t] X_s(t-k)
+ *   dX_s(i)       = sum_{k : cu[s] <= i+k < cu[s+1]} w[d, W-1-k] gv[i+k]
+ *                   + dxcT[s][i - (cu[s+1] - (W-1))]  when that index is in 0..W-2
+ * and dX_s(i) lands in dx[i] (i >= cu[s]) or dxc0[s][i - (cu[s] - (W-1))].
+ * dxcT, xc0 may be NULL; dxc0, db may be NULL. Overwrites its outputs for
+ * channels [d0, d1).
+ */
+int oracle_conv_bwd_state(int64_t T, int32_t D, int32_t W, const int32_t *cu, int32_t nseq,
+                          const double *x, const double *w, const double *b, int silu,
+                          const double *xc0, const double *du, const double *dxcT,
+                          int32_t d0, int32_t d1, double *dx, double *dw, double *db, double *dxc0)
+{
+    if (cu[0] != 0 || (int64_t)cu[nseq] != T) return ORACLE_ERR_CU_SEQLENS;
+    double *gv = (double *)malloc((size_t)(T > 0 ? T : 1) * sizeof(double));
+    if (!gv) return ORACLE_ERR_ALLOC;
+    for (int32_t d = d0; d < d1; ++d) {
+        double dbd = 0.0;
+        for (int32_t s = 0; s < nseq; ++s) {
+            for (int64_t t = cu[s]; t < cu[s + 1]; ++t) {
+                double vv = b ? b[d] : 0.0;
+                for (int32_t k = 0; k < W; ++k) {
+                    if (t - k < cu[s] && !xc0) continue;
+                    vv += w[(int64_t)d * W + (W - 1 - k)] * conv_input(x, xc0, cu, s, t - k, D, W, d);
+                }
+                const double g = du[t * D + d];
+                if (silu) {
+                    const double sg = sigmoid(vv);
+                    gv[t] = g * sg * (1.0 + vv * (1.0 - sg));
+                } else {
+                    gv[t] = g;
+                }
+            }
+        }
+        for (int64_t t = 0; t < T; ++t) dbd += gv[t];
+        for (int32_t k = 0; k < W; ++k) {
+            double acc = 0.0;
+            for (int32_t s = 0; s < nseq; ++s)
+                for (int64_t t = cu[s]; t < cu[s + 1]; ++t) {
+                    if (t - k < cu[s] && !xc0) continue;
+                    acc += gv[t] * conv_input(x, xc0, cu, s, t - k, D, W, d);
+                }
+            dw[(int64_t)d * W + (W - 1 - k)] = acc;
+        }
+        /* gradient of every extended input, context first */
+        for (int32_t s = 0; s < nseq; ++s) {
+            const int64_t a = cu[s], e = cu[s + 1];
+            for (int64_t i = a - (W - 1); i < e; ++i) {
+                double acc = 0.0;
+                for (int32_t k = 0; k < W; ++k)
+                    if (i + k >= a && i + k < e) acc += w[(int64_t)d * W + (W - 1 - k)] * gv[i + k];
+                const int64_t jt = i - (e - (W - 1));
+                if (dxcT && jt >= 0 && jt < W - 1) acc += dxcT[((int64_t)s * (W - 1) + jt) * D + d];
+                if (i >= a) {
+                    dx[i * D + d] = acc;
+                } else if (dxc0) {
+                    dxc0[((int64_t)s * (W - 1) + (i - (a - (W - 1)))) * D + d] = acc;
+                }
+            }
+        }
+        if (db) db[d] = dbd;
+    }
+    free(gv);
+    return ORACLE_OK;
+}
+
+/*
+ * Selective scan forward with an initial SSM state per sequence: the
+ * recurrence of oracle_scan_fwd_ex started from h_{cu[s]-1} = h0[s]:
+ *   h_t = exp(delta_t A) h_{t-1} + delta_t B_t u_t   for t in [cu[s], cu[s+1])
+ * and hT[s] = the state after the sequence's last token (h0[s], or zero, for
+ * an empty sequence). Outputs as oracle_scan_fwd_ex.
+ */
+int oracle_scan_fwd_state(int64_t T, int32_t D, int32_t N, const int32_t *cu, int32_t nseq,
+                          const double *u, const double *delta, const double *A,
+                          const double *B, const double *C, const double *Dp, const double *z,
+                          const double *dbias, int32_t sp, double gate_floor, const double *h0,
+                          int32_t d0, int32_t d1, double *y, double *out, double *hT)
+{
+    if (cu[0] != 0 || (int64_t)cu[nseq] != T) return ORACLE_ERR_CU_SEQLENS;
+    for (int32_t s = 0; s < nseq; ++s)
+        if (cu[s + 1] < cu[s]) return ORACLE_ERR_CU_SEQLENS;
+    double *h = (double *)calloc((size_t)(N > 0 ? N : 1), sizeof(double));
+    if (!h) return ORACLE_ERR_ALLOC;
+    for (int32_t d = d0; d < d1; ++d) {
+        for (int32_t s = 0; s < nseq; ++s) {
+            for (int32_t n = 0; n < N; ++n) h[n] = h0 ? h0[((int64_t)s * D + d) * N + n] : 0.0;
+            for (int64_t t = cu[s]; t < cu[s + 1]; ++t) {
+                const double dt = delta_eff(delta[t * D + d], dbias, d, sp);
+                const double uu = u[t * D + d];
+                double acc = 0.0;
+                for (int32_t n = 0; n < N; ++n) {
+                    const double a = exp(dt * A[(int64_t)d * N + n]);
+                    h[n] = a * h[n] + dt * B[t * N + n] * uu;
+                    acc += C[t * N + n] * h[n];
+                }
+                if (Dp) acc += Dp[d] * uu;
+                if (y) y[t * D + d] = acc;
+                out[t * D + d] = z ? acc * (z[t * D + d] * sigmoid(z[t * D + d]) + gate_floor) : acc;
+            }
+            if (hT)
+                for (int32_t n = 0; n < N; ++n) hT[((int64_t)s * D + d) * N + n] = h[n];
+        }
+    }
+    free(h);
+    return ORACLE_OK;
+}
+
+/*
+ * Selective scan backward with states: the chain rule of
+ * oracle_scan_fwd_state for the loss sum(dout * out) + sum(dhT * hT). Per
+ * sequence the reverse carry starts from dhT[s] (zero when NULL) at its last
+ * token; at the first token the previous state is h0[s]; what the carry holds
+ * after the first token is dL/dh0[s] (dhT[s] for an empty sequence).
+ * Sequences are walked last to first and tokens last to first, so the sums
+ * dA, dDp, ddbias are formed in the order oracle_scan_bwd_ex forms them.
+ * Other conventions as oracle_scan_bwd_ex; dh0 may be NULL.
+ */
+int oracle_scan_bwd_state(int64_t T, int32_t D, int32_t N, const int32_t *cu, int32_t nseq,
+                          const double *u, const double *delta, const double *A,
+                          const double *B, const double *C, const double *Dp, const double *z,
+                          const double *dbias, int32_t sp, double gate_floor, const double *h0,
+                          const double *dout, const double *dhT, int32_t d0, int32_t d1,
+                          double *du, double *ddelta, double *dA, double *dB, double *dC,
+                          double *dDp, double *dz, double *ddbias, double *dh0)
+{
+    if (cu[0] != 0 || (int64_t)cu[nseq] != T) return ORACLE_ERR_CU_SEQLENS;
+    for (int32_t s = 0; s < nseq; ++s)
+        if (cu[s + 1] < cu[s]) return ORACLE_ERR_CU_SEQLENS;
+    double *hs = (double *)malloc((size_t)(T > 0 ? T : 1) * (size_t)(N > 0 ? N : 1) * sizeof(double));
+    double *ys = (double *)malloc((size_t)(T > 0 ? T : 1) * sizeof(double));
+    double *c = (double *)calloc((size_t)(N > 0 ? N : 1), sizeof(double));
+    double *hinit = (double *)calloc((size_t)(N > 0 ? N : 1), sizeof(double));
+    if (!hs || !ys || !c || !hinit) { free(hs); free(ys); free(c); free(hinit); return ORACLE_ERR_ALLOC; }
+    for (int32_t d = d0; d < d1; ++d) {
+        /* forward, keeping every state of this channel */
+        for (int32_t s = 0; s < nseq; ++s) {
+            for (int64_t t = cu[s]; t < cu[s + 1]; ++t) {
+                const double dt = delta_eff(delta[t * D + d], dbias, d, sp);
+                const double uu = u[t * D + d];
+                double acc = 0.0;
+                for (int32_t n = 0; n < N; ++n) {
+                    const double hp = (t == cu[s]) ? (h0 ? h0[((int64_t)s * D + d) * N + n] : 0.0)
+                                                   : hs[(t - 1) * N + n];
+                    const double hn = exp(dt * A[(int64_t)d * N + n]) * hp + dt * B[t * N + n] * uu;
+                    hs[t * N + n] = hn;
+                    acc += C[t * N + n] * hn;
+                }
+                if (Dp) acc += Dp[d] * uu;
+                ys[t] = acc;
+            }
+        }
+        /* reverse, sequence by sequence */
+        double dDp_acc = 0.0, ddb_acc = 0.0;
+        double *dA_d = dA + (int64_t)d * N;
+        for (int32_t n = 0; n < N; ++n) dA_d[n] = 0.0;
+        for (int32_t s = nseq - 1; s >= 0; --s) {
+            for (int32_t n = 0; n < N; ++n) {
+                c[n] = dhT ? dhT[((int64_t)s * D + d) * N + n] : 0.0;
+                hinit[n] = h0 ? h0[((int64_t)s * D + d) * N + n] : 0.0;
+            }
+            for (int64_t t = (int64_t)cu[s + 1] - 1; t >= cu[s]; --t) {
+                const double dt = delta_eff(delta[t * D + d], dbias, d, sp);
+                const double uu = u[t * D + d];
+                const double go = dout[t * D + d];
+                double g = go;
+                if (z) {
+                    const double zz = z[t * D + d];
+                    const double sg = sigmoid(zz);
+                    g = go * (zz * sg + gate_floor);
+                    if (dz) dz[t * D + d] = go * ys[t] * sg * (1.0 + zz * (1.0 - sg));
+                } else if (dz) {
+                    dz[t * D + d] = 0.0;
+                }
+                double du_acc = Dp ? g * Dp[d] : 0.0;
+                double ddt = 0.0;
+                dDp_acc += g * uu;
+                for (int32_t n = 0; n < N; ++n) {
+                    const double Bn = B[t * N + n], An = A[(int64_t)d * N + n];
+                    const double dh = g * C[t * N + n] + c[n];
+                    const double a = exp(dt * An);
+                    const double hp = (t == cu[s]) ? hinit[n] : hs[(t - 1) * N + n];
+                    dC[t * N + n] += g * hs[t * N + n];
+                    dB[t * N + n] += dh * dt * uu;
+                    du_acc += dh * dt * Bn;
+                    ddt += dh * (Bn * uu + An * a * hp);
+                    dA_d[n] += dh * dt * a * hp;
+                    c[n] = a * dh;
+                }
+                du[t * D + d] = du_acc;
+                const double ddraw = ddt * delta_grad(delta[t * D + d], dbias, d, sp);
+                ddelta[t * D + d] = ddraw;
+                ddb_acc += ddraw;
+            }
+            if (dh0)
+                for (int32_t n = 0; n < N; ++n) dh0[((int64_t)s * D + d) * N + n] = c[n];
+        }
+        if (dDp) dDp[d] = dDp_acc;
+        if (ddbias) ddbias[d] = ddb_acc;
+    }
+    free(hs); free(ys); free(c); free(hinit);
+    return ORACLE_OK;
+}

@@ -471,10 +471,180 @@ def check_step_map_finite_differences(orc, seed=33):
         assert err <= 1e-6 * scale, f"{gk}: fd mismatch {err:.3e} (scale {scale:.3e})"
 
 
+# --------------------------------------------------------------------------
+# P10: sequences that continue across packs ([P5] "结论与讨论": cut a sequence at
+# a pack end and hand its state to the next piece; [P1] 3.2: segment-wise
+# runs that reset or pass the conv and SSM states)
+# --------------------------------------------------------------------------
+
+def _state_case(seed, lengths, D=3, N=3, W=4):
+    rng = np.random.default_rng(seed)
+    c = rand_case(rng, list(lengths), D=D, N=N, W=W)
+    nseq = len(lengths)
+    c["h0"] = rng.standard_normal((nseq, D, N))
+    c["xc0"] = rng.standard_normal((nseq, W - 1, D))
+    c["dhT"] = rng.standard_normal((nseq, D, N))
+    c["dxcT"] = rng.standard_normal((nseq, W - 1, D))
+    return c, rng
+
+
+def _pipe_state(orc, c, h0, xc0, x=None, w=None, b=None, delta=None, A=None, B=None, C=None, Dp=None, z=None):
+    """conv (+SiLU) with context, then the gated scan with initial states."""
+    g = lambda k, v: c[k] if v is None else v
+    _, u, xcT = orc.conv_fwd_state(g("x", x), g("w", w), g("b", b), c["cu"], xc0)
+    y, out, hT = orc.scan_fwd_state(u, g("delta", delta), g("A", A), g("B", B), g("C", C), g("Dp", Dp),
+                                    g("z", z), c["cu"], h0)
+    return {"u": u, "y": y, "out": out, "hT": hT, "xcT": xcT}
+
+
+def _pipe_state_bwd(orc, c, h0, xc0, dhT, dxcT):
+    _, u, _ = orc.conv_fwd_state(c["x"], c["w"], c["b"], c["cu"], xc0)
+    G = orc.scan_bwd_state(u, c["delta"], c["A"], c["B"], c["C"], c["Dp"], c["z"], c["cu"], c["dout"], h0, dhT)
+    dx, dw, db, dxc0 = orc.conv_bwd_state(c["x"], c["w"], c["b"], c["cu"], G["du"], xc0, dxcT)
+    G.update({"dx": dx, "dw": dw, "db": db, "dxc0": dxc0})
+    return G
+
+
+def check_states_zero_reduce_to_reset(orc):
+    """Zero (or absent) initial states and zero final-state gradients give the
+    reset-at-every-head results bit for bit, zero-length sequences included;
+    an empty sequence hands on its initial state and its gradient unchanged."""
+    c, rng = _state_case(41, (3, 0, 5, 1, 2, 0))
+    F = _fwd(orc, c)
+    G = _bwd(orc, c)
+    nseq, D, N, W = len(c["lengths"]), c["D"], c["N"], c["W"]
+    for h0, xc0, dhT, dxcT in ((None, None, None, None),
+                               (np.zeros((nseq, D, N)), np.zeros((nseq, W - 1, D)),
+                                np.zeros((nseq, D, N)), np.zeros((nseq, W - 1, D)))):
+        Fs = _pipe_state(orc, c, h0, xc0)
+        for k in ("u", "y", "out"):
+            assert np.array_equal(Fs[k], F[k]), k
+        Gs = _pipe_state_bwd(orc, c, h0, xc0, dhT, dxcT)
+        for k in ("dx", "dw", "db", "ddelta", "dA", "dB", "dC", "dD", "dz", "du"):
+            assert np.array_equal(Gs[k], G[k]), k
+        assert not Fs["hT"][1].any() and not Fs["xcT"][1].any()  # empty sequence, zero state
+    # with the step map and the gate floor too
+    pos = _pos(orc, c)
+    u = rng.standard_normal((c["T"], D))
+    bias = rng.standard_normal(D) * 0.5
+    opts = dict(delta_bias=bias, delta_softplus=True, gate_floor=0.05)
+    args = (u, c["delta"] - 1.0, c["A"], c["B"], c["C"], c["Dp"], c["z"])
+    y0, out0 = orc.scan_fwd(*args, pos, **opts)
+    y1, out1, _ = orc.scan_fwd_state(*args, c["cu"], None, **opts)
+    assert np.array_equal(y0, y1) and np.array_equal(out0, out1)
+    g0 = orc.scan_bwd(*args, pos, c["dout"], **opts)
+    g1 = orc.scan_bwd_state(*args, c["cu"], c["dout"], None, None, **opts)
+    for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddelta_bias"):
+        assert np.array_equal(g0[k], g1[k]), k
+    Fs = _pipe_state(orc, c, c["h0"], c["xc0"])
+    Gs = _pipe_state_bwd(orc, c, c["h0"], c["xc0"], c["dhT"], c["dxcT"])
+    for s in (1, 5):  # empty sequences
+        assert np.array_equal(Fs["hT"][s], c["h0"][s]) and np.array_equal(Fs["xcT"][s], c["xc0"][s])
+        assert np.array_equal(Gs["dh0"][s], c["dhT"][s]) and np.array_equal(Gs["dxc0"][s], c["dxcT"][s])
+
+
+def check_cut_and_carry(orc):
+    """A sequence cut into pieces that hand on hT and xcT (forward) and dh0 and
+    dxc0 (backward, last piece first) reproduces the uncut sequence: forward
+    bit for bit, gradients to rounding (the cut splits some sums in two).
+    Pieces of 1 and 2 tokens are shorter than the conv context."""
+    rng = np.random.default_rng(42)
+    L, cuts = 17, [5, 6, 8, 13]
+    c = rand_case(rng, [L], D=3, N=3, W=4)
+    F = _fwd(orc, c)
+    G = _bwd(orc, c)
+    edges = [0] + cuts + [L]
+    h0 = xc0 = None
+    outs, states = [], []
+    for a, e in zip(edges[:-1], edges[1:]):
+        piece = {k: (v[a:e] if isinstance(v, np.ndarray) and v.ndim >= 1 and v.shape[0] == L else v)
+                 for k, v in c.items()}
+        piece["cu"] = cu_of([e - a])
+        Fp = _pipe_state(orc, piece, h0, xc0)
+        outs.append(Fp)
+        states.append((piece, h0, xc0))
+        h0, xc0 = Fp["hT"], Fp["xcT"]
+    for k in ("u", "y", "out"):
+        assert np.array_equal(np.concatenate([o[k] for o in outs]), F[k]), k
+    dhT = dxcT = None
+    grads = []
+    for piece, h0, xc0 in reversed(states):
+        Gp = _pipe_state_bwd(orc, piece, h0, xc0, dhT, dxcT)
+        grads.insert(0, Gp)
+        dhT, dxcT = Gp["dh0"], Gp["dxc0"]
+    for k in ("du", "ddelta", "dz", "dx", "dB", "dC"):
+        got = np.concatenate([g[k] for g in grads])
+        np.testing.assert_allclose(got, G[k], rtol=1e-12, atol=1e-12 * np.max(np.abs(G[k])), err_msg=k)
+    for k in ("dA", "dD", "dw", "db"):
+        got = sum(g[k] for g in grads)
+        np.testing.assert_allclose(got, G[k], rtol=1e-11, atol=1e-12 * np.max(np.abs(G[k])), err_msg=k)
+
+
+def check_state_closed_forms(orc):
+    """No input (u = 0 into the scan; B arbitrary): h_t = a^(p+1) h0 with
+    a = exp(delta A) for constant delta, so hT = a^L h0 and y_t = C_t . h_t;
+    the gradient of sum(dout * y) + sum(dhT * hT) with respect to h0 is
+    sum_t dout_t C_t a^(p+1) + dhT a^L. The conv with context is numpy's
+    valid cross-correlation of [xc0; x], and xcT is its last W-1 inputs."""
+    c, rng = _state_case(43, (6, 1, 3))
+    T, D, N, W = c["T"], c["D"], c["N"], c["W"]
+    dl = rng.uniform(0.05, 0.5, D)
+    delta = np.tile(dl, (T, 1))
+    u = np.zeros((T, D))
+    y, _, hT = orc.scan_fwd_state(u, delta, c["A"], c["B"], c["C"], None, None, c["cu"], c["h0"])
+    G = orc.scan_bwd_state(u, delta, c["A"], c["B"], c["C"], None, None, c["cu"], c["dout"], c["h0"], c["dhT"])
+    for s, L in enumerate(c["lengths"]):
+        r = rows_of(c["cu"], s)
+        a = np.exp(dl[:, None] * c["A"])                       # (D, N)
+        p = np.arange(L)
+        decay = a[None, :, :] ** (p[:, None, None] + 1)         # (L, D, N)
+        h = decay * c["h0"][s][None]
+        np.testing.assert_allclose(y[r], np.einsum("tn,tdn->td", c["C"][r], h), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(hT[s], a ** L * c["h0"][s], rtol=1e-12, atol=1e-14)
+        want = np.einsum("td,tn,tdn->dn", c["dout"][r], c["C"][r], decay) + c["dhT"][s] * a ** L
+        np.testing.assert_allclose(G["dh0"][s], want, rtol=1e-12, atol=1e-14)
+    _, uu, xcT = orc.conv_fwd_state(c["x"], c["w"], c["b"], c["cu"], c["xc0"], silu=False)
+    for s, L in enumerate(c["lengths"]):
+        r = rows_of(c["cu"], s)
+        for d in range(D):
+            ext = np.concatenate([c["xc0"][s][:, d], c["x"][r, d]])
+            np.testing.assert_allclose(uu[r, d], np.correlate(ext, c["w"][d], "valid") + c["b"][d],
+                                       rtol=1e-13, atol=1e-13)
+            np.testing.assert_array_equal(xcT[s][:, d], ext[-(W - 1):])
+
+
+def check_state_finite_differences(orc):
+    """Every gradient of L = sum(dout * out) + sum(dhT * hT) + sum(dxcT * xcT)
+    through conv (with context) and scan (with initial states), against
+    central differences, on a pack with a sequence shorter than the context."""
+    c, rng = _state_case(44, (4, 2, 5))
+
+    def loss(h0=c["h0"], xc0=c["xc0"], **kw):
+        F = _pipe_state(orc, c, h0, xc0, **kw)
+        return float(np.sum(c["dout"] * F["out"]) + np.sum(c["dhT"] * F["hT"]) + np.sum(c["dxcT"] * F["xcT"]))
+
+    G = _pipe_state_bwd(orc, c, c["h0"], c["xc0"], c["dhT"], c["dxcT"])
+    pairs = [("h0", "dh0"), ("xc0", "dxc0"), ("x", "dx"), ("w", "dw"), ("b", "db"), ("delta", "ddelta"),
+             ("A", "dA"), ("B", "dB"), ("C", "dC"), ("Dp", "dD"), ("z", "dz")]
+    for pk, gk in pairs:
+        p = c[pk]
+        fd = np.zeros_like(p)
+        for idx in np.ndindex(p.shape):
+            h = 1e-6 * max(1.0, abs(p[idx]))
+            pp = p.copy(); pp[idx] += h
+            pm = p.copy(); pm[idx] -= h
+            fd[idx] = (loss(**{pk: pp}) - loss(**{pk: pm})) / (2 * h)
+        an = G[gk]
+        scale = max(1e-3, float(np.max(np.abs(an))))
+        err = float(np.max(np.abs(fd - an)))
+        assert err <= 1e-6 * scale, f"{gk}: fd mismatch {err:.3e} (scale {scale:.3e})"
+
+
 ALL_CHECKS = [
     check_golden_pack, check_pack_rejects_bad_cu, check_packed_equals_alone, check_scan_closed_form,
     check_conv_closed_form, check_zero_state_at_heads, check_nonfinite_isolated,
     check_conv_matches_torch, check_scan_cumsum, check_finite_differences, check_padded_layout,
     check_chunk_composition, check_step_map_closed_forms, check_gate_floor_linear,
-    check_step_map_finite_differences,
+    check_step_map_finite_differences, check_states_zero_reduce_to_reset, check_cut_and_carry,
+    check_state_closed_forms, check_state_finite_differences,
 ]

@@ -62,6 +62,31 @@ MUTATIONS = [
      "acc * (z[t * D + d] * sigmoid(z[t * D + d]))"),
     ("gate floor: backward drops it", "g = go * (zz * s + gate_floor);", "g = go * (zz * s);"),
     ("step map: bias gradient keeps only one token", "ddb_acc += ddraw;", "ddb_acc = ddraw;"),
+    ("state: initial state ignored", "for (int32_t n = 0; n < N; ++n) h[n] = h0 ? h0[((int64_t)s * D + d) * N + n] : 0.0;",
+     "for (int32_t n = 0; n < N; ++n) h[n] = 0.0;"),
+    ("state: final state transposed", "for (int32_t n = 0; n < N; ++n) hT[((int64_t)s * D + d) * N + n] = h[n];",
+     "for (int32_t n = 0; n < N; ++n) hT[((int64_t)s * N + n) * D + d] = h[n];"),
+    ("state bwd: final-state gradient ignored", "c[n] = dhT ? dhT[((int64_t)s * D + d) * N + n] : 0.0;",
+     "c[n] = 0.0;"),
+    ("state bwd: previous state at the head taken as zero",
+     "const double hp = (t == cu[s]) ? hinit[n] : hs[(t - 1) * N + n];",
+     "const double hp = (t == cu[s]) ? 0.0 : hs[(t - 1) * N + n];"),
+    ("state bwd: replay ignores the initial state",
+     "const double hp = (t == cu[s]) ? (h0 ? h0[((int64_t)s * D + d) * N + n] : 0.0)",
+     "const double hp = (t == cu[s]) ? 0.0"),
+    ("state bwd: initial-state gradient for the wrong sequence",
+     "for (int32_t n = 0; n < N; ++n) dh0[((int64_t)s * D + d) * N + n] = c[n];",
+     "for (int32_t n = 0; n < N; ++n) dh0[((int64_t)(nseq - 1 - s) * D + d) * N + n] = c[n];"),
+    ("conv context: oldest and newest swapped", "const int64_t j = i - ((int64_t)cu[s] - (W - 1));",
+     "const int64_t j = (int64_t)cu[s] - 1 - i;"),
+    ("conv context: final context drops the initial one",
+     "conv_input(x, xc0, cu, s, (int64_t)cu[s + 1] - (W - 1) + j, D, W, d);",
+     "conv_input(x, NULL, cu, s, (int64_t)cu[s + 1] - (W - 1) + j, D, W, d);"),
+    ("conv context bwd: gradient not passed through short sequences",
+     "if (dxcT && jt >= 0 && jt < W - 1) acc +=", "if (dxcT && jt >= 0 && jt < W - 1 && i >= a) acc +="),
+    ("conv context bwd: dw misses the context",
+     "if (t - k < cu[s] && !xc0) continue;\n                    acc += gv[t]",
+     "if (t - k < cu[s]) continue;\n                    acc += gv[t]"),
 ]
 
 
@@ -72,15 +97,42 @@ def mutant_dir():
     shutil.rmtree(d, ignore_errors=True)
 
 
-@pytest.mark.parametrize("name,orig,planted", MUTATIONS, ids=[m[0] for m in MUTATIONS])
-def test_planted_mistake_is_caught(mutant_dir, name, orig, planted):
+# Lines that the reset-only functions and the state-carrying ones share are
+# planted in each: (name, text, planted, k) plants in the k-th of exactly two
+# occurrences (0: the reset-only function, 1: the state-carrying one).
+_SHARED = [
+    ("bwd: dA loses the delta factor", "dA_d[n] += dh * dt * a * hp;", "dA_d[n] += dh * a * hp;"),
+    ("bwd: dB misses u", "dB[t * N + n] += dh * dt * uu;", "dB[t * N + n] += dh * dt;"),
+    ("bwd: dC uses the wrong state", "dC[t * N + n] += g * hs[t * N + n];",
+     "dC[t * N + n] += g * hs[(t > 0 ? t - 1 : t) * N + n];"),
+    ("conv bwd: dw tap index transposed", "dw[(int64_t)d * W + (W - 1 - k)] = acc;", "dw[(int64_t)d * W + k] = acc;"),
+    ("gate floor: forward drops it", "acc * (z[t * D + d] * sigmoid(z[t * D + d]) + gate_floor)",
+     "acc * (z[t * D + d] * sigmoid(z[t * D + d]))"),
+    ("step map: bias gradient keeps only one token", "ddb_acc += ddraw;", "ddb_acc = ddraw;"),
+]
+MUTATIONS = [m for m in MUTATIONS if m[1] not in {sh[1] for sh in _SHARED}]
+MUTATIONS = [m + (None,) for m in MUTATIONS] + [
+    (f"{name} [{which}]", orig, planted, k) for name, orig, planted in _SHARED
+    for k, which in ((0, "reset"), (1, "states"))]
+
+
+@pytest.mark.parametrize("name,orig,planted,nth", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(mutant_dir, name, orig, planted, nth):
     src = open(oracle_mod._SRC).read()
-    assert src.count(orig) == 1, f"mutation anchor not unique/found: {name}"
-    idx = MUTATIONS.index((name, orig, planted))
+    if nth is None:
+        assert src.count(orig) == 1, f"mutation anchor not unique/found: {name}"
+        mutated = src.replace(orig, planted)
+    else:
+        assert src.count(orig) == 2, f"shared anchor not found exactly twice: {name}"
+        at = src.index(orig)
+        if nth == 1:
+            at = src.index(orig, at + 1)
+        mutated = src[:at] + planted + src[at + len(orig):]
+    idx = MUTATIONS.index((name, orig, planted, nth))
     c_path = os.path.join(mutant_dir, f"m{idx}.c")
     so_path = os.path.join(mutant_dir, f"m{idx}.so")
     with open(c_path, "w") as f:
-        f.write(src.replace(orig, planted))
+        f.write(mutated)
     subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", c_path, "-o", so_path, "-lm"],
                    check=True)
     mut = oracle_mod.Oracle(so_path)
