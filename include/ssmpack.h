@@ -57,7 +57,7 @@ const char *ssmp_status_string(int status);
 
 /* Version of this ABI (incremented on any change to the set of entry points
  * or their meaning; 2 added the _ex scan entry points, 3 the host packer
- * varlen_pack_plan). */
+ * varlen_pack_plan, 4 the scan entry points with sequence states). */
 int ssmp_abi_version(void);
 
 /*
@@ -191,6 +191,48 @@ int selective_scan_pack_bwd_ex(const void *u, const void *delta, const float *A,
                                int64_t T, int32_t D, int32_t N, int32_t dtype,
                                const float *delta_bias, int32_t delta_softplus, float gate_floor,
                                float *ddelta_bias, void *stream);
+
+/*
+ * selective_scan_pack_fwd_states / _bwd_states — sequences that start from a
+ * given state and hand on their last one.
+ * [P5] section "结论与讨论" proposes cutting a sequence that overruns a pack into
+ * pieces that keep passing state, so packs need no padding; [P1] section 3.2
+ * runs long documents segment by segment, resetting or passing the SSM state
+ * at segment starts. These are the _ex entry points plus, per sequence s of
+ * cu_seqlens (device int32 [nseq+1], the one pos was built from):
+ *   initial_state   fp32 (nseq, D, N), nullable (zero): the state before the
+ *                   sequence's first token, h_{-1} = initial_state[s]; the
+ *                   recurrence then runs unchanged
+ *   final_state     fp32 (nseq, D, N) out, nullable: the state after its last
+ *                   token (initial_state[s], or zero, for an empty sequence)
+ *   dfinal_state    fp32 (nseq, D, N), nullable (zero): dL/d final_state
+ *   dinitial_state  fp32 (nseq, D, N) out, nullable: dL/d initial_state
+ * Element (s, d, n) is at (s*D + d)*N + n. A piece that continues a sequence
+ * gets the previous piece's final_state as its initial_state, and the
+ * previous piece's backward gets this piece's dinitial_state as its
+ * dfinal_state (so the later pack's backward runs first). The backward must
+ * be given the forward's initial_state. With every state pointer NULL these
+ * are the _ex entry points (cu_seqlens and nseq are then not read).
+ * Errors as the _ex entry points, plus SSMP_ERR_NULL (a state pointer without
+ * cu_seqlens) and SSMP_ERR_SHAPE (nseq < 1 with a state pointer).
+ */
+int selective_scan_pack_fwd_states(const void *u, const void *delta, const float *A, const void *B,
+                                   const void *C, const float *Dskip, const void *z, const int32_t *pos,
+                                   void *out, void *workspace, size_t workspace_bytes,
+                                   int64_t T, int32_t D, int32_t N, int32_t dtype,
+                                   const float *delta_bias, int32_t delta_softplus, float gate_floor,
+                                   const int32_t *cu_seqlens, int32_t nseq,
+                                   const float *initial_state, float *final_state, void *stream);
+int selective_scan_pack_bwd_states(const void *u, const void *delta, const float *A, const void *B,
+                                   const void *C, const float *Dskip, const void *z, const int32_t *pos,
+                                   const void *dout, void *workspace, size_t workspace_bytes,
+                                   void *du, void *ddelta, float *dA, float *dB, float *dC,
+                                   float *dD, void *dz,
+                                   int64_t T, int32_t D, int32_t N, int32_t dtype,
+                                   const float *delta_bias, int32_t delta_softplus, float gate_floor,
+                                   float *ddelta_bias, const int32_t *cu_seqlens, int32_t nseq,
+                                   const float *initial_state, const float *dfinal_state,
+                                   float *dinitial_state, void *stream);
 
 /* Packing strategies of varlen_pack_plan. */
 enum ssmp_pack_strategy {

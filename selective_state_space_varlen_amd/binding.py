@@ -46,6 +46,15 @@ _SIGNATURES = {
                                                   _c_vp, _c_sz, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
                                                   _c_i64, _c_i32, _c_i32, _c_i32,
                                                   _c_vp, _c_i32, ctypes.c_float, _c_vp, _c_vp]),
+    "selective_scan_pack_fwd_states": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                                      _c_vp, _c_vp, _c_sz, _c_i64, _c_i32, _c_i32, _c_i32,
+                                                      _c_vp, _c_i32, ctypes.c_float, _c_vp, _c_i32, _c_vp, _c_vp,
+                                                      _c_vp]),
+    "selective_scan_pack_bwd_states": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                                      _c_vp, _c_vp, _c_sz, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                                      _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32,
+                                                      _c_vp, _c_i32, ctypes.c_float, _c_vp, _c_vp, _c_i32,
+                                                      _c_vp, _c_vp, _c_vp, _c_vp]),
     "varlen_pack_plan": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp,
                                         _c_vp, _c_vp]),
 }
@@ -225,11 +234,26 @@ def _extended(delta_bias, delta_softplus, gate_floor) -> bool:
     return delta_bias is not None or bool(delta_softplus) or float(gate_floor) != 0.0
 
 
+def _states_args(cu_seqlens, nseq_from, D, N, dev):
+    _check(cu_seqlens, "cu_seqlens", dtype=torch.int32, device=dev)
+    if cu_seqlens is None:
+        raise ValueError("sequence states need cu_seqlens")
+    nseq = cu_seqlens.numel() - 1
+    for name, t in nseq_from:
+        _check(t, name, (nseq, D, N), torch.float32, dev)
+    return nseq
+
+
 def selective_scan_pack_fwd(u, delta, A, B, C, Dskip, z, pos, workspace: Optional[torch.Tensor] = None,
                             out: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
-                            delta_softplus: bool = False, gate_floor: float = 0.0):
+                            delta_softplus: bool = False, gate_floor: float = 0.0,
+                            cu_seqlens: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+                            final_state=False):
     """Returns (out, workspace); keep the workspace for the backward.
-    delta_bias / delta_softplus / gate_floor select selective_scan_pack_fwd_ex."""
+    delta_bias / delta_softplus / gate_floor select selective_scan_pack_fwd_ex.
+    cu_seqlens (with optional initial_state (nseq, D, N) fp32 and final_state:
+    True, or an output tensor) selects selective_scan_pack_fwd_states; the
+    return value is then (out, workspace, final_state or None)."""
     T, D = u.shape
     N = A.shape[1]
     dev = u.device
@@ -244,6 +268,17 @@ def selective_scan_pack_fwd(u, delta, A, B, C, Dskip, z, pos, workspace: Optiona
     _check(o, "out", (T, D), u.dtype, dev)
     args = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(pos), _ptr(o),
             _ptr(workspace), workspace.numel() * workspace.element_size(), T, D, N, _dtype_code(u))
+    if cu_seqlens is not None or initial_state is not None or final_state is not False:
+        _check(delta_bias, "delta_bias", (D,), torch.float32, dev)
+        fs = None
+        if final_state is True:
+            fs = torch.empty((cu_seqlens.numel() - 1, D, N), dtype=torch.float32, device=dev)
+        elif isinstance(final_state, torch.Tensor):
+            fs = final_state
+        nseq = _states_args(cu_seqlens, (("initial_state", initial_state), ("final_state", fs)), D, N, dev)
+        _call("selective_scan_pack_fwd_states", *args, _ptr(delta_bias), int(bool(delta_softplus)),
+              float(gate_floor), _ptr(cu_seqlens), nseq, _ptr(initial_state), _ptr(fs), _stream(u))
+        return o, workspace, fs
     if _extended(delta_bias, delta_softplus, gate_floor):
         _check(delta_bias, "delta_bias", (D,), torch.float32, dev)
         _call("selective_scan_pack_fwd_ex", *args, _ptr(delta_bias), int(bool(delta_softplus)), float(gate_floor),
@@ -255,10 +290,15 @@ def selective_scan_pack_fwd(u, delta, A, B, C, Dskip, z, pos, workspace: Optiona
 
 def selective_scan_pack_bwd(u, delta, A, B, C, Dskip, z, pos, dout, workspace: torch.Tensor,
                             out: Optional[dict] = None, delta_bias: Optional[torch.Tensor] = None,
-                            delta_softplus: bool = False, gate_floor: float = 0.0):
+                            delta_softplus: bool = False, gate_floor: float = 0.0,
+                            cu_seqlens: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+                            dfinal_state: Optional[torch.Tensor] = None, dinitial_state=False):
     """Gradients of sum(dout * out); the workspace must come from the forward,
     called with the same options. `out` may supply the result buffers (a dict
-    shaped like the return value; "ddelta_bias" is present iff delta_bias is)."""
+    shaped like the return value; "ddelta_bias" is present iff delta_bias is).
+    cu_seqlens (with optional initial_state, dfinal_state, dinitial_state:
+    True, or an output tensor) selects selective_scan_pack_bwd_states; the
+    result then holds "dinitial_state" (None unless asked for)."""
     T, D = u.shape
     N = A.shape[1]
     dev = u.device
@@ -285,6 +325,28 @@ def selective_scan_pack_bwd(u, delta, A, B, C, Dskip, z, pos, dout, workspace: t
             _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(du), _ptr(ddelta), _ptr(dA),
             _ptr(dB), _ptr(dC), _ptr(dD), _ptr(dz), T, D, N, _dtype_code(u))
     res = {"du": du, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "dz": dz}
+    if (cu_seqlens is not None or initial_state is not None or dfinal_state is not None
+            or dinitial_state is not False):
+        _check(delta_bias, "delta_bias", (D,), torch.float32, dev)
+        ddb = None
+        if delta_bias is not None:
+            ddb = out.get("ddelta_bias") if out is not None else None
+            if ddb is None:
+                ddb = torch.empty((D,), dtype=torch.float32, device=dev)
+            _check(ddb, "ddelta_bias", (D,), torch.float32, dev)
+        di = None
+        if dinitial_state is True:
+            di = torch.empty((cu_seqlens.numel() - 1, D, N), dtype=torch.float32, device=dev)
+        elif isinstance(dinitial_state, torch.Tensor):
+            di = dinitial_state
+        nseq = _states_args(cu_seqlens, (("initial_state", initial_state), ("dfinal_state", dfinal_state),
+                                         ("dinitial_state", di)), D, N, dev)
+        _call("selective_scan_pack_bwd_states", *args, _ptr(delta_bias), int(bool(delta_softplus)),
+              float(gate_floor), _ptr(ddb), _ptr(cu_seqlens), nseq, _ptr(initial_state), _ptr(dfinal_state),
+              _ptr(di), _stream(u))
+        res["ddelta_bias"] = ddb
+        res["dinitial_state"] = di
+        return res
     if _extended(delta_bias, delta_softplus, gate_floor):
         _check(delta_bias, "delta_bias", (D,), torch.float32, dev)
         ddb = None

@@ -142,6 +142,14 @@ __global__ __launch_bounds__(64, 4) void k_scan_bwd_summary(const T* __restrict_
         else
             bsum_block<true, GATE, T, NS, BT, St>(lds, bc, tb, nt, A2, sr, sdt, cdt, lane, sm, opt.gate_floor);
     }
+    if (opt.dhT && (fh < t1 || t1 == T_ || pos[t1] == 0)) {
+        // the range ends at a sequence's last token: the carry entering that
+        // token from the right is the sequence's final-state gradient, which
+        // reaches the range's start through every decay of the range
+        const float* __restrict__ gp = opt.dhT + ((size_t)seq_of(opt.cu, opt.nseq, fh - 1) * D + dd) * NS;
+#pragma unroll
+        for (int n = 0; n < NS; ++n) sr[n] = __builtin_fmaf(exp2_fast(A2[n] * sdt), gp[n], sr[n]);
+    }
     if (act) {
         // the decay exp2(A2[n] * sdt) depends on n only through A: keep sdt
         // (NaN where a head cuts the sub-chunk, i.e. decay 0) per channel
@@ -258,10 +266,13 @@ constexpr int kRedStride = kWave + 4;  // LDS row stride (floats) of the dB/dC t
 // Replay of one kK-token sub-chunk from its entering state h: the states hh[k]
 // after each token and the pre-gate outputs yk[k]. SAFE sub-chunks may be
 // short (ns < kK) and may hold heads; the fast ones are full and head-free.
-template <bool SAFE, bool XS, int NS, int LPC, typename St, typename T>
+// With initial states, a head starts from its sequence's h0 (this lane's
+// share of the states) instead of zero.
+template <bool SAFE, bool XS, bool ST, int NS, int LPC, typename St, typename T>
 __device__ __forceinline__ void bwd_replay(const T* lds, const float* bcl, int kb, int ns, uint32_t heads, int ch,
                                            int n0, const float (&A2)[NS / LPC], float (&h)[NS / LPC],
-                                           float (&hh)[kK][NS / LPC], float (&yk)[kK], float Dv, const StepMap& sm) {
+                                           float (&hh)[kK][NS / LPC], float (&yk)[kK], float Dv, const StepMap& sm,
+                                           const ScanOpts& opt, int64_t tb, int D, int dd) {
     // on return h holds the state after the last replayed token
     constexpr int NH = NS / LPC;
 #pragma unroll
@@ -274,7 +285,20 @@ __device__ __forceinline__ void bwd_replay(const T* lds, const float* bcl, int k
         const float uu = St::get(lds, 0, k, ch);
         const float dtu = dt * uu;
         const float* row = bcl + k * 2 * NS + n0;
-        if constexpr (SAFE) reset_if<NH>((heads >> k) & 1u, h);
+        if constexpr (SAFE) {
+            if ((heads >> k) & 1u) {
+                asm volatile("");
+                if (ST && opt.h0) {
+                    const float* __restrict__ hp =
+                        opt.h0 + ((size_t)seq_of(opt.cu, opt.nseq, tb + k) * D + dd) * NS + n0;
+#pragma unroll
+                    for (int i = 0; i < NH; ++i) h[i] = hp[i];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < NH; ++i) h[i] = 0.0f;
+                }
+            }
+        }
         float y = 0.0f;
 #pragma unroll
         for (int i = 0; i < NH; ++i) {
@@ -298,14 +322,14 @@ struct BwdRows {
 };
 
 // Reverse step over one sub-chunk (tokens kb + ns - 1 down to kb).
-template <bool SAFE, bool GATE, bool XS, int NS, int LPC, typename St, typename T>
+template <bool SAFE, bool GATE, bool XS, bool ST, int NS, int LPC, typename St, typename T>
 __device__ __forceinline__ void bwd_reverse(const T* lds, const float* bcl, float (*red)[kRedStride], int kb, int ns,
                                             uint32_t heads, int lane, int ch, int sh, int n0, bool act, bool full,
                                             int D, int d, const float (&A2)[NS / LPC], float (&carry)[NS / LPC],
                                             float (&dA)[NS / LPC], float& dDacc, float Dv,
                                             const float (&hin)[NS / LPC], const float (&hh)[kK][NS / LPC],
                                             const float (&yk)[kK], const BwdRows<T>& rows, const StepMap& sm,
-                                            float gf, float& dbacc) {
+                                            float gf, float& dbacc, const ScanOpts& opt, int64_t tb, int dd) {
     constexpr int NH = NS / LPC;
     constexpr int CW = kWave / LPC;
 #pragma unroll
@@ -333,13 +357,33 @@ __device__ __forceinline__ void bwd_reverse(const T* lds, const float* bcl, floa
         const bool head = SAFE && ((heads >> k) & 1u);
         if (head) {
             asm volatile("");
+            // With states, what the decay passes back out of the head is the
+            // initial state's gradient, the initial state is the previous
+            // state of the r term, and the carry into the token before the
+            // head (the previous sequence's last) is that sequence's
+            // final-state gradient.
+            const bool st = ST && (opt.h0 || opt.dh0);
+            const int64_t t = tb + k;
+            const size_t so = st ? ((size_t)seq_of(opt.cu, opt.nseq, t) * D + dd) * NS + n0 : 0;
+            const float* __restrict__ gp = (ST && opt.dhT && t > 0)
+                                               ? opt.dhT + ((size_t)seq_of(opt.cu, opt.nseq, t - 1) * D + dd) * NS + n0
+                                               : nullptr;
 #pragma unroll
             for (int i = 0; i < NH; ++i) {
                 const float dh = __builtin_fmaf(gg, row[NS + i], carry[i]);
                 red[i][col] = dh * dtu;             // dB row
                 red[NH + i][col] = gg * hh[kk][i];  // dC row
                 sumB = __builtin_fmaf(dh, row[i], sumB);
-                carry[i] = 0.0f;
+                if (st) {
+                    const float cr = exp2_fast(dt * A2[i]) * dh;
+                    if (opt.h0) {
+                        const float r = cr * opt.h0[so + i];
+                        sumAr = __builtin_fmaf(r, A2[i], sumAr);
+                        dA[i] = __builtin_fmaf(r, dt, dA[i]);
+                    }
+                    if (opt.dh0 && act) opt.dh0[so + i] = cr;
+                }
+                carry[i] = (gp && act) ? gp[i] : 0.0f;
             }
         } else {
 #pragma unroll
@@ -406,7 +450,7 @@ __device__ __forceinline__ void bwd_reverse(const T* lds, const float* bcl, floa
 // A workgroup holds WV waves on adjacent channel groups of one chunk: they
 // share the staged B/C rows of each block, and add their per-token dB/dC sums
 // in LDS, so one partial row per WV*64/LPC channels reaches memory.
-template <typename T, int NS, int LPC, int WV, bool GATE, bool XS>
+template <typename T, int NS, int LPC, int WV, bool GATE, bool XS, bool ST>
 __global__ __launch_bounds__(kWave * WV, 2) void k_scan_bwd_main(BwdArgs<T> p) {
     constexpr int NH = NS / LPC;      // states per lane
     constexpr int CW = kWave / LPC;   // channels per wave
@@ -447,6 +491,13 @@ __global__ __launch_bounds__(kWave * WV, 2) void k_scan_bwd_main(BwdArgs<T> p) {
         A2[i] = p.A[(size_t)dd * NS + n0 + i] * kLog2e;
         carry[i] = act ? p.cin[(size_t)c * ND + (size_t)(n0 + i) * D + dd] : 0.0f;
         dA[i] = 0.0f;
+    }
+    if (ST && p.opt.dhT && act && (t1 == p.T_ || p.pos[t1] == 0)) {
+        // the chunk ends at a sequence's last token (the carry pass hands it
+        // zero): it starts from that sequence's final-state gradient
+        const float* __restrict__ gp = p.opt.dhT + ((size_t)seq_of(p.opt.cu, p.opt.nseq, t1 - 1) * D + dd) * NS + n0;
+#pragma unroll
+        for (int i = 0; i < NH; ++i) carry[i] = gp[i];
     }
     const float Dv = (p.Dskip && act) ? p.Dskip[dd] : 0.0f;
     float dDacc = 0.0f, dbacc = 0.0f;
@@ -521,15 +572,17 @@ __global__ __launch_bounds__(kWave * WV, 2) void k_scan_bwd_main(BwdArgs<T> p) {
             if (tb0 + kb - kK >= t0) load_state(tb0 + kb - kK, hn);
             const uint32_t sub_heads = (heads >> kb) & ((1u << kK) - 1u);
             if (sub_heads == 0 && ns == kK) {
-                bwd_replay<false, XS, NS, LPC, St>(mylds, bcl, kb, kK, 0u, ch, n0, A2, h, hh, yk, Dv, sm);
-                bwd_reverse<false, GATE, XS, NS, LPC, St>(mylds, bcl, red[wv], kb, kK, 0u, lane, ch, sh, n0, act,
+                bwd_replay<false, XS, ST, NS, LPC, St>(mylds, bcl, kb, kK, 0u, ch, n0, A2, h, hh, yk, Dv, sm, p.opt, tb0,
+                                                   D, dd);
+                bwd_reverse<false, GATE, XS, ST, NS, LPC, St>(mylds, bcl, red[wv], kb, kK, 0u, lane, ch, sh, n0, act,
                                                           full, D, d, A2, carry, dA, dDacc, Dv, hin, hh, yk, rows,
-                                                          sm, gf, dbacc);
+                                                          sm, gf, dbacc, p.opt, tb0, dd);
             } else {
-                bwd_replay<true, XS, NS, LPC, St>(mylds, bcl, kb, ns, heads, ch, n0, A2, h, hh, yk, Dv, sm);
-                bwd_reverse<true, GATE, XS, NS, LPC, St>(mylds, bcl, red[wv], kb, ns, heads, lane, ch, sh, n0, act,
+                bwd_replay<true, XS, ST, NS, LPC, St>(mylds, bcl, kb, ns, heads, ch, n0, A2, h, hh, yk, Dv, sm, p.opt, tb0,
+                                                  D, dd);
+                bwd_reverse<true, GATE, XS, ST, NS, LPC, St>(mylds, bcl, red[wv], kb, ns, heads, lane, ch, sh, n0, act,
                                                          full, D, d, A2, carry, dA, dDacc, Dv, hin, hh, yk, rows,
-                                                         sm, gf, dbacc);
+                                                         sm, gf, dbacc, p.opt, tb0, dd);
             }
         }
 
@@ -624,17 +677,20 @@ static int scan_bwd_launch(const void* u, const void* delta, const float* A, con
     const int64_t ngroup = bwd_bc_groups(D, NS, sizeof(T));
     const dim3 mgrid((unsigned)(ngroup * nchunk));
     const bool xs = opt.delta_bias != nullptr || opt.softplus != 0;
+    // sequence states get kernels of their own, so the reset-only ones keep
+    // their register allocation
+    const bool st = opt.h0 != nullptr || opt.dhT != nullptr || opt.dh0 != nullptr;
+#define SSMP_BWD_MAIN(G, X, S) k_scan_bwd_main<T, NS, LPC, WV, G, X, S><<<mgrid, kWave * WV, 0, s>>>(a)
+#define SSMP_BWD_MAIN_S(G, X)               \
+    if (st) SSMP_BWD_MAIN(G, X, true);      \
+    else SSMP_BWD_MAIN(G, X, false)
     if (z) {
-        if (xs)
-            k_scan_bwd_main<T, NS, LPC, WV, true, true><<<mgrid, kWave * WV, 0, s>>>(a);
-        else
-            k_scan_bwd_main<T, NS, LPC, WV, true, false><<<mgrid, kWave * WV, 0, s>>>(a);
+        if (xs) { SSMP_BWD_MAIN_S(true, true); } else { SSMP_BWD_MAIN_S(true, false); }
     } else {
-        if (xs)
-            k_scan_bwd_main<T, NS, LPC, WV, false, true><<<mgrid, kWave * WV, 0, s>>>(a);
-        else
-            k_scan_bwd_main<T, NS, LPC, WV, false, false><<<mgrid, kWave * WV, 0, s>>>(a);
+        if (xs) { SSMP_BWD_MAIN_S(false, true); } else { SSMP_BWD_MAIN_S(false, false); }
     }
+#undef SSMP_BWD_MAIN_S
+#undef SSMP_BWD_MAIN
     SSMP_LAUNCH_CHECK();
     const int64_t nrp = ND > D ? ND : D;
     k_scan_bwd_reduce_params<NS><<<(unsigned)((nrp + 255) / 256), 256, 0, s>>>(
@@ -642,6 +698,11 @@ static int scan_bwd_launch(const void* u, const void* delta, const float* A, con
     SSMP_LAUNCH_CHECK();
     k_scan_bwd_reduce_bc<NS><<<(unsigned)((T_ * 2 * NS + 255) / 256), 256, 0, s>>>(ws + L.dBC, ngroup, T_, dB, dC);
     SSMP_LAUNCH_CHECK();
+    if (opt.dh0) {
+        const int64_t n = (int64_t)opt.nseq * ND;
+        k_empty_seq_states<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(opt.cu, opt.nseq, ND, opt.dhT, opt.dh0);
+        SSMP_LAUNCH_CHECK();
+    }
     return SSMP_OK;
 }
 
@@ -667,13 +728,15 @@ static int scan_bwd_dispatch(int N, const void* u, const void* delta, const floa
 
 }  // namespace ssmp
 
-extern "C" int selective_scan_pack_bwd_ex(const void* u, const void* delta, const float* A, const void* B,
-                                          const void* C, const float* Dskip, const void* z, const int32_t* pos,
-                                          const void* dout, void* workspace, size_t workspace_bytes, void* du,
-                                          void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz,
-                                          int64_t T, int32_t D, int32_t N, int32_t dtype, const float* delta_bias,
-                                          int32_t delta_softplus, float gate_floor, float* ddelta_bias,
-                                          void* stream) {
+extern "C" int selective_scan_pack_bwd_states(const void* u, const void* delta, const float* A, const void* B,
+                                              const void* C, const float* Dskip, const void* z, const int32_t* pos,
+                                              const void* dout, void* workspace, size_t workspace_bytes, void* du,
+                                              void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz,
+                                              int64_t T, int32_t D, int32_t N, int32_t dtype,
+                                              const float* delta_bias, int32_t delta_softplus, float gate_floor,
+                                              float* ddelta_bias, const int32_t* cu_seqlens, int32_t nseq,
+                                              const float* initial_state, const float* dfinal_state,
+                                              float* dinitial_state, void* stream) {
     using namespace ssmp;
     int st = scan_check_args(T, D, N, dtype);
     if (st) return st;
@@ -681,21 +744,51 @@ extern "C" int selective_scan_pack_bwd_ex(const void* u, const void* delta, cons
     if ((Dskip == nullptr) != (dD == nullptr)) return SSMP_ERR_NULL;
     if ((z == nullptr) != (dz == nullptr)) return SSMP_ERR_NULL;
     if ((delta_bias == nullptr) != (ddelta_bias == nullptr)) return SSMP_ERR_NULL;
+    const bool states = initial_state || dfinal_state || dinitial_state;
+    if (states) {
+        if (!cu_seqlens) return SSMP_ERR_NULL;
+        if (nseq < 1 || (int64_t)nseq * D * N >= (int64_t(1) << 40)) return SSMP_ERR_SHAPE;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
+    ScanOpts o{delta_bias, delta_softplus != 0 ? 1 : 0, gate_floor};
+    if (states) {
+        o.cu = cu_seqlens;
+        o.nseq = nseq;
+        o.h0 = initial_state;
+        o.dhT = dfinal_state;
+        o.dh0 = dinitial_state;
+    }
     if (T == 0) {
-        // empty input: the sums are zero
+        // empty input: the sums are zero, and every sequence hands its
+        // final-state gradient back unchanged
         if ((st = zero_f32(dA, (int64_t)D * N, s))) return st;
         if ((st = zero_f32(dD, D, s))) return st;
-        return zero_f32(ddelta_bias, D, s);
+        if ((st = zero_f32(ddelta_bias, D, s))) return st;
+        if (!dinitial_state) return SSMP_OK;
+        const int64_t ND = (int64_t)D * N, n = (int64_t)nseq * ND;
+        k_empty_seq_states<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(cu_seqlens, nseq, ND, dfinal_state,
+                                                                       dinitial_state);
+        return hipGetLastError() == hipSuccess ? SSMP_OK : SSMP_ERR_HIP;
     }
     if (!u || !delta || !B || !C || !pos || !dout || !du || !ddelta || !dB || !dC) return SSMP_ERR_NULL;
     if (!workspace || workspace_bytes < selective_scan_pack_workspace_bytes(T, D, N)) return SSMP_ERR_WORKSPACE;
     float* ws = static_cast<float*>(workspace);
-    const ScanOpts o{delta_bias, delta_softplus != 0 ? 1 : 0, gate_floor};
     return dtype == SSMP_BF16 ? scan_bwd_dispatch<uint16_t>(N, u, delta, A, B, C, Dskip, z, pos, dout, ws, du,
                                                             ddelta, dA, dB, dC, dD, dz, T, D, o, ddelta_bias, s)
                               : scan_bwd_dispatch<float>(N, u, delta, A, B, C, Dskip, z, pos, dout, ws, du, ddelta,
                                                          dA, dB, dC, dD, dz, T, D, o, ddelta_bias, s);
+}
+
+extern "C" int selective_scan_pack_bwd_ex(const void* u, const void* delta, const float* A, const void* B,
+                                          const void* C, const float* Dskip, const void* z, const int32_t* pos,
+                                          const void* dout, void* workspace, size_t workspace_bytes, void* du,
+                                          void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz,
+                                          int64_t T, int32_t D, int32_t N, int32_t dtype, const float* delta_bias,
+                                          int32_t delta_softplus, float gate_floor, float* ddelta_bias,
+                                          void* stream) {
+    return selective_scan_pack_bwd_states(u, delta, A, B, C, Dskip, z, pos, dout, workspace, workspace_bytes, du,
+                                          ddelta, dA, dB, dC, dD, dz, T, D, N, dtype, delta_bias, delta_softplus,
+                                          gate_floor, ddelta_bias, nullptr, 0, nullptr, nullptr, nullptr, stream);
 }
 
 extern "C" int selective_scan_pack_bwd(const void* u, const void* delta, const float* A, const void* B,

@@ -55,11 +55,50 @@ inline int bwd_sum_len(int64_t T, int D, int N) {
 // Optional element-wise neighbours of the scan, applied where the scan reads
 // its inputs: the step is softplus(delta + bias[d]) (softplus set) or
 // delta + bias[d] (bias may be null), and the gate is silu(z) + gate_floor.
+//
+// Sequences may also start from a given state and hand on their last one
+// (sequences cut at a pack end continue in the next pack): h0 is the state
+// before each sequence's first token, hT the state after its last, both
+// (nseq, D, N) fp32 with element (s, d, n) at (s*D + d)*N + n; the backward
+// takes dhT (the loss gradient with respect to hT) and returns dh0. Null
+// pointers switch each part off (h0 and dhT then count as zero). cu is the
+// device cu_seqlens, used to name the sequence of a head or end token.
 struct ScanOpts {
     const float* delta_bias;
     int softplus;
     float gate_floor;
+    const int32_t* cu = nullptr;
+    int nseq = 0;
+    const float* h0 = nullptr;
+    float* hT = nullptr;
+    const float* dhT = nullptr;
+    float* dh0 = nullptr;
 };
+
+// Sequence of token t: the largest s with cu[s] <= t (zero-length sequences
+// sharing that start come before it). Wave-uniform: every lane of a wave asks
+// about the same token, and it runs only at heads and ends. For any cu the
+// result stays in [0, nseq-1].
+__device__ __forceinline__ int seq_of(const int32_t* __restrict__ cu, int nseq, int64_t t) {
+    int lo = 0, hi = nseq - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)cu[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Sequences with no tokens hand on their initial state (or its gradient)
+// unchanged: dst[s] = src ? src[s] : 0 for every s with cu[s] == cu[s+1].
+// One thread per (s, d, n); other sequences are left to the scan kernels.
+template <int kUnused = 0>
+__global__ __launch_bounds__(256) void k_empty_seq_states(const int32_t* __restrict__ cu, int nseq, int64_t DN,
+                                                          const float* __restrict__ src, float* __restrict__ dst) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)nseq * DN) return;
+    const int s = (int)(i / DN);
+    if (cu[s] == cu[s + 1]) dst[i] = src ? src[i] : 0.0f;
+}
 
 // softplus(v) = max(v, 0) + log1p(exp(-|v|)); log1p(e) as log(w) e / (w - 1)
 // with w = 1 + e (exact-ish when e is tiny, where w - 1 rounds).
@@ -188,6 +227,16 @@ template <int BT = kBB>
 __device__ __forceinline__ uint32_t block_heads(const int32_t* __restrict__ pos, int64_t tb, int64_t T_, int lane) {
     const int64_t t = tb + lane;
     const bool f = (lane < BT) && (t < T_) && pos[t] == 0;
+    return (uint32_t)__ballot(f);
+}
+
+// End flags of the BT tokens of a block (bit k: token tb+k is the last of its
+// sequence, i.e. tb+k+1 is a head or the end of the pack). Lanes k < BT each
+// read one position, one token further on than block_heads.
+template <int BT = kBB>
+__device__ __forceinline__ uint32_t block_ends(const int32_t* __restrict__ pos, int64_t tb, int64_t T_, int lane) {
+    const int64_t t = tb + lane;
+    const bool f = (lane < BT) && (t < T_) && (t + 1 == T_ || pos[t + 1] == 0);
     return (uint32_t)__ballot(f);
 }
 

@@ -122,6 +122,12 @@ __global__ __launch_bounds__(64, 4) void k_scan_fwd_summary(const T* __restrict_
         A2[n] = A[(size_t)dd * NS + n] * kLog2e;
         h[n] = 0.0f;
     }
+    if (has_head && opt.h0) {
+        // from the last head on, the state starts at that sequence's initial state
+        const float* __restrict__ hp = opt.h0 + ((size_t)seq_of(opt.cu, opt.nseq, ts) * D + dd) * NS;
+#pragma unroll
+        for (int n = 0; n < NS; ++n) h[n] = hp[n];
+    }
     const StepMap sm = step_map(opt, dd);
     float sdt = 0.0f, cdt = 0.0f;
     const T* const src[2] = {u, delta};
@@ -227,11 +233,17 @@ __global__ __launch_bounds__(256) void k_scan_fwd_carry(const float* __restrict_
 // The state entering every kCK-th token goes to its checkpoint slot (ck:
 // the slot of the block's first token), except at the chunk start (skip0),
 // whose slot the carry pass wrote.
-template <bool SAFE, bool GATE, bool XS, typename T, int NS, int BT, typename St>
+//
+// With sequence states, a head starts from its sequence's initial state
+// instead of zero, and the state after an end token (ends: bit k) is that
+// sequence's final state; both occur only in SAFE blocks.
+template <bool SAFE, bool GATE, bool XS, bool ST, typename T, int NS, int BT, typename St>
 __device__ __forceinline__ void out_block(const T* lds, const float* __restrict__ bc, int64_t tb, int nt,
-                                          uint32_t heads, const float (&A2)[NS], float (&h)[NS], float Dv, int lane,
-                                          T* __restrict__ ob, int D, int d, bool store, float* __restrict__ ck,
-                                          size_t ND, bool skip0, bool act, const StepMap& sm, float gf) {
+                                          uint32_t heads, uint32_t ends, const float (&A2)[NS], float (&h)[NS],
+                                          float Dv, int lane, T* __restrict__ ob, int D, int d, int dd, bool store,
+                                          float* __restrict__ ck, size_t ND, bool skip0, bool act, const StepMap& sm,
+                                          const ScanOpts& opt) {
+    const float gf = opt.gate_floor;
     // the block's per-lane inputs are read from LDS before the first scalar
     // load: a wait for LDS data also waits for scalar loads in flight
     float dtv[BT], uv[BT], zv[BT];
@@ -263,12 +275,31 @@ __device__ __forceinline__ void out_block(const T* lds, const float* __restrict_
         const float dt = dtv[k];
         const float uu = uv[k];
         const float dtu = dt * uu;
-        if constexpr (SAFE) reset_if<NS>((heads >> k) & 1u, h);
+        if constexpr (SAFE) {
+            if ((heads >> k) & 1u) {
+                asm volatile("");
+                if (ST && opt.h0) {
+                    const float* __restrict__ hp = opt.h0 + ((size_t)seq_of(opt.cu, opt.nseq, tb + k) * D + dd) * NS;
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) h[n] = hp[n];
+                } else {
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) h[n] = 0.0f;
+                }
+            }
+        }
         float y = 0.0f;
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
             h[n] = __builtin_fmaf(exp2_fast(dt * A2[n]), h[n], dtu * cur[n]);
             y = __builtin_fmaf(cur[NS + n], h[n], y);
+        }
+        if constexpr (SAFE && ST) {
+            if (((ends >> k) & 1u) && act) {
+                float* __restrict__ hq = opt.hT + ((size_t)seq_of(opt.cu, opt.nseq, tb + k) * D + d) * NS;
+#pragma unroll
+                for (int n = 0; n < NS; ++n) hq[n] = h[n];
+            }
         }
         y = __builtin_fmaf(Dv, uu, y);
         if constexpr (GATE) {
@@ -283,7 +314,7 @@ __device__ __forceinline__ void out_block(const T* lds, const float* __restrict_
     }
 }
 
-template <typename T, int NS, bool GATE, bool XS>
+template <typename T, int NS, bool GATE, bool XS, bool ST>
 __global__ __launch_bounds__(64, 4) void k_scan_fwd_out(const T* __restrict__ u, const T* __restrict__ delta,
                                                      const float* __restrict__ A, const float* __restrict__ bc,
                                                      const float* __restrict__ Dskip, const T* __restrict__ z,
@@ -317,6 +348,7 @@ __global__ __launch_bounds__(64, 4) void k_scan_fwd_out(const T* __restrict__ u,
     st.fetch(src, t0, T_, D, tl.g, lane, vec);
     for (int64_t tb = t0; tb < t1; tb += BT) {
         const uint32_t heads = block_heads<BT>(pos, tb, T_, lane);
+        const uint32_t ends = (ST && opt.hT) ? block_ends<BT>(pos, tb, T_, lane) : 0u;
         wave_sync();
         st.commit(lds, src, tb, T_, D, tl.g, lane, vec);
         wave_sync();
@@ -324,12 +356,12 @@ __global__ __launch_bounds__(64, 4) void k_scan_fwd_out(const T* __restrict__ u,
         const int nt = (int)((tb + BT < t1) ? BT : t1 - tb);
         T* __restrict__ ob = out + (size_t)tb * D;
         float* __restrict__ ck = ckpt + (size_t)(tb / kCK) * ND;
-        if (heads == 0 && nt == BT)
-            out_block<false, GATE, XS, T, NS, BT, St>(lds, bc, tb, BT, 0u, A2, h, Dv, lane, ob, D, d, store, ck, ND,
-                                                  tb == t0, act, sm, opt.gate_floor);
+        if ((heads | ends) == 0 && nt == BT)
+            out_block<false, GATE, XS, ST, T, NS, BT, St>(lds, bc, tb, BT, 0u, 0u, A2, h, Dv, lane, ob, D, d, dd, store,
+                                                  ck, ND, tb == t0, act, sm, opt);
         else
-            out_block<true, GATE, XS, T, NS, BT, St>(lds, bc, tb, nt, heads, A2, h, Dv, lane, ob, D, d, store, ck, ND,
-                                                 tb == t0, act, sm, opt.gate_floor);
+            out_block<true, GATE, XS, ST, T, NS, BT, St>(lds, bc, tb, nt, heads, ends, A2, h, Dv, lane, ob, D, d, dd,
+                                                 store, ck, ND, tb == t0, act, sm, opt);
     }
 }
 
@@ -355,17 +387,29 @@ static int scan_fwd_launch(const void* u, const void* delta, const float* A, con
                                                                       D, nchunk, lc);
     SSMP_LAUNCH_CHECK();
     const bool xs = opt.delta_bias != nullptr || opt.softplus != 0;
-#define SSMP_FWD_OUT(G, X)                                                                                       \
-    k_scan_fwd_out<T, NS, G, X><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, ws + L.bc, Dskip,         \
-                                                       G ? (const T*)z : nullptr, pos, (T*)out, ws + L.ckpt, T_, D, \
-                                                       vec, lc, opt)
+    // sequence states get kernels of their own, so the reset-only ones keep
+    // their register allocation
+    const bool st = opt.h0 != nullptr || opt.hT != nullptr;
+#define SSMP_FWD_OUT(G, X, S)                                                                                    \
+    k_scan_fwd_out<T, NS, G, X, S><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, ws + L.bc, Dskip,      \
+                                                          G ? (const T*)z : nullptr, pos, (T*)out, ws + L.ckpt, T_, \
+                                                          D, vec, lc, opt)
+#define SSMP_FWD_OUT_S(G, X)                \
+    if (st) SSMP_FWD_OUT(G, X, true);       \
+    else SSMP_FWD_OUT(G, X, false)
     if (z) {
-        if (xs) SSMP_FWD_OUT(true, true); else SSMP_FWD_OUT(true, false);
+        if (xs) { SSMP_FWD_OUT_S(true, true); } else { SSMP_FWD_OUT_S(true, false); }
     } else {
-        if (xs) SSMP_FWD_OUT(false, true); else SSMP_FWD_OUT(false, false);
+        if (xs) { SSMP_FWD_OUT_S(false, true); } else { SSMP_FWD_OUT_S(false, false); }
     }
+#undef SSMP_FWD_OUT_S
 #undef SSMP_FWD_OUT
     SSMP_LAUNCH_CHECK();
+    if (opt.hT) {
+        const int64_t n = (int64_t)opt.nseq * ND;
+        k_empty_seq_states<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(opt.cu, opt.nseq, ND, opt.h0, opt.hT);
+        SSMP_LAUNCH_CHECK();
+    }
     return SSMP_OK;
 }
 
@@ -390,22 +434,52 @@ extern "C" size_t selective_scan_pack_workspace_bytes(int64_t T, int32_t D, int3
     return ssmp::scan_ws_layout(T, D, N).total * sizeof(float);
 }
 
+extern "C" int selective_scan_pack_fwd_states(const void* u, const void* delta, const float* A, const void* B,
+                                              const void* C, const float* Dskip, const void* z, const int32_t* pos,
+                                              void* out, void* workspace, size_t workspace_bytes, int64_t T,
+                                              int32_t D, int32_t N, int32_t dtype, const float* delta_bias,
+                                              int32_t delta_softplus, float gate_floor, const int32_t* cu_seqlens,
+                                              int32_t nseq, const float* initial_state, float* final_state,
+                                              void* stream) {
+    using namespace ssmp;
+    int st = scan_check_args(T, D, N, dtype);
+    if (st) return st;
+    const bool states = initial_state || final_state;
+    if (states) {
+        if (!cu_seqlens) return SSMP_ERR_NULL;
+        if (nseq < 1 || (int64_t)nseq * D * N >= (int64_t(1) << 40)) return SSMP_ERR_SHAPE;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ScanOpts o{delta_bias, delta_softplus != 0 ? 1 : 0, gate_floor};
+    if (states) {
+        o.cu = cu_seqlens;
+        o.nseq = nseq;
+        o.h0 = initial_state;
+        o.hT = final_state;
+    }
+    if (T == 0) {
+        // every sequence is empty: it hands on its initial state
+        if (!final_state) return SSMP_OK;
+        const int64_t ND = (int64_t)D * N, n = (int64_t)nseq * ND;
+        k_empty_seq_states<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(cu_seqlens, nseq, ND, initial_state,
+                                                                       final_state);
+        return hipGetLastError() == hipSuccess ? SSMP_OK : SSMP_ERR_HIP;
+    }
+    if (!u || !delta || !A || !B || !C || !pos || !out) return SSMP_ERR_NULL;
+    if (!workspace || workspace_bytes < selective_scan_pack_workspace_bytes(T, D, N)) return SSMP_ERR_WORKSPACE;
+    float* ws = static_cast<float*>(workspace);
+    return dtype == SSMP_BF16 ? scan_fwd_dispatch<uint16_t>(N, u, delta, A, B, C, Dskip, z, pos, out, ws, T, D, o, s)
+                              : scan_fwd_dispatch<float>(N, u, delta, A, B, C, Dskip, z, pos, out, ws, T, D, o, s);
+}
+
 extern "C" int selective_scan_pack_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
                                           const void* C, const float* Dskip, const void* z, const int32_t* pos,
                                           void* out, void* workspace, size_t workspace_bytes, int64_t T, int32_t D,
                                           int32_t N, int32_t dtype, const float* delta_bias, int32_t delta_softplus,
                                           float gate_floor, void* stream) {
-    using namespace ssmp;
-    int st = scan_check_args(T, D, N, dtype);
-    if (st) return st;
-    if (T == 0) return SSMP_OK;
-    if (!u || !delta || !A || !B || !C || !pos || !out) return SSMP_ERR_NULL;
-    if (!workspace || workspace_bytes < selective_scan_pack_workspace_bytes(T, D, N)) return SSMP_ERR_WORKSPACE;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    float* ws = static_cast<float*>(workspace);
-    const ScanOpts o{delta_bias, delta_softplus != 0 ? 1 : 0, gate_floor};
-    return dtype == SSMP_BF16 ? scan_fwd_dispatch<uint16_t>(N, u, delta, A, B, C, Dskip, z, pos, out, ws, T, D, o, s)
-                              : scan_fwd_dispatch<float>(N, u, delta, A, B, C, Dskip, z, pos, out, ws, T, D, o, s);
+    return selective_scan_pack_fwd_states(u, delta, A, B, C, Dskip, z, pos, out, workspace, workspace_bytes, T, D, N,
+                                          dtype, delta_bias, delta_softplus, gate_floor, nullptr, 0, nullptr,
+                                          nullptr, stream);
 }
 
 extern "C" int selective_scan_pack_fwd(const void* u, const void* delta, const float* A, const void* B,

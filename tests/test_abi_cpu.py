@@ -33,7 +33,7 @@ def test_header_lists_the_entry_points():
     for n in ("varlen_pack_indices", "conv1d_pack_fwd", "conv1d_pack_bwd", "selective_scan_pack_fwd",
               "selective_scan_pack_bwd", "selective_scan_pack_workspace_bytes", "conv1d_pack_bwd_workspace_bytes",
               "ssmp_status_string", "ssmp_abi_version", "selective_scan_pack_fwd_ex", "selective_scan_pack_bwd_ex",
-              "varlen_pack_plan"):
+              "varlen_pack_plan", "selective_scan_pack_fwd_states", "selective_scan_pack_bwd_states"):
         assert n in names, n
 
 
@@ -49,7 +49,7 @@ def test_status_strings(lib):
     for s in range(1, 7):
         assert lib.ssmp_status_string(s) and lib.ssmp_status_string(s) != b"unknown status"
     assert lib.ssmp_status_string(99) == b"unknown status"
-    assert lib.ssmp_abi_version() == 3
+    assert lib.ssmp_abi_version() == 4
 
 
 def test_workspace_sizes(lib):

@@ -353,3 +353,140 @@ def test_planned_layout_parity(orc):
     assert_close(npy(Fp["out"][r]), npy(Fa["out"][idx]), to, "out vs arrival order")
     for k in ("dx", "ddelta", "dz"):
         assert_close(npy(Gp[k][r]), npy(Ga[k][idx]), tg, k + " vs arrival order")
+
+
+# ---------------------------------------------------------------------------
+# sequence states (selective_scan_pack_*_states): initial and final SSM states
+# ---------------------------------------------------------------------------
+
+STATE_CASES = {
+    "bf16-mixed": dict(wl=2, lengths=[700, 0, 1, 400, 1200, 0], D=128),
+    "edges-on-chunk-bounds-fp32": dict(wl=2, lengths=[256, 256, 512, 17, 64, 64], D=65, dtype=torch.float32),
+    "one-sequence-many-chunks": dict(wl=2, lengths=[3000], D=64),
+    "single-tokens": dict(wl=2, lengths=[1] * 300, D=64),
+    "only-initial": dict(wl=2, lengths=[300, 2, 500, 129], D=64, parts=("h0",)),
+    "only-final": dict(wl=2, lengths=[300, 2, 500, 129], D=64, parts=("hT",)),
+    "only-gradient-path": dict(wl=2, lengths=[300, 2, 500, 129], D=64, parts=("dhT", "dh0")),
+    "d_state-1-fp32": dict(wl=2, lengths=[300, 2, 500], D=33, N=1, dtype=torch.float32),
+    "d_state-4-fp32": dict(wl=2, lengths=[255, 1, 256, 257], D=65, N=4, dtype=torch.float32),
+    "d_state-8": dict(wl=2, lengths=[700, 90, 0], D=130, N=8),
+    "no-gate-no-skip": dict(wl=2, lengths=[400, 1, 299], D=64, gate=False, skip=False),
+    "step-map-and-floor": dict(wl=2, lengths=[700, 1, 400, 1200], D=128, opts=(True, 0.05)),
+    "workload3-small": dict(wl=3, n_packs=1, pack_len=8192, D=64),
+}
+
+
+@pytest.mark.parametrize("name", list(STATE_CASES))
+def test_scan_states_parity(orc, name):
+    spec = dict(STATE_CASES[name])
+    parts = spec.pop("parts", ("h0", "hT", "dhT", "dh0"))
+    gate = spec.pop("gate", True)
+    skip = spec.pop("skip", True)
+    opts = spec.pop("opts", None)
+    inp = synth.make_inputs(spec.pop("wl"), with_u=True, with_dout=True, **spec)
+    nseq, D, N = inp.nseq, inp.D, inp.N
+    rng = np.random.default_rng(17)
+    h0 = rng.standard_normal((nseq, D, N)).astype(np.float32) if "h0" in parts else None
+    dhT = rng.standard_normal((nseq, D, N)).astype(np.float32) if "dhT" in parts else None
+    kw, okw = {}, {}
+    if opts is not None:
+        # softplus of (stored + bias) with the stored steps chosen to keep the workload's values
+        bias = (rng.standard_normal(D) * 0.5).astype(np.float32)
+        raw = np.log(np.expm1(synth.f64(inp.delta))) - bias[None, :]
+        inp.delta = synth.to_dtype(raw, inp.dtype)
+        kw = dict(delta_bias=to_dev(torch.from_numpy(bias)), delta_softplus=True, gate_floor=opts[1])
+        okw = dict(delta_bias=bias.astype(np.float64), delta_softplus=True, gate_floor=opts[1])
+    d = Dev(inp)
+    z = d.z if gate else None
+    Dp = d.Dp if skip else None
+    h0_d = to_dev(torch.from_numpy(h0)) if h0 is not None else None
+    dhT_d = to_dev(torch.from_numpy(dhT)) if dhT is not None else None
+    out, ws, hT = ssp().selective_scan_pack_fwd(d.u, d.delta, d.A, d.B, d.C, Dp, z, d.pos, cu_seqlens=d.cu,
+                                                initial_state=h0_d, final_state="hT" in parts, **kw)
+    g = ssp().selective_scan_pack_bwd(d.u, d.delta, d.A, d.B, d.C, Dp, z, d.pos, d.dout, ws, cu_seqlens=d.cu,
+                                      initial_state=h0_d, dfinal_state=dhT_d, dinitial_state="dh0" in parts, **kw)
+    torch.cuda.synchronize()
+    args = (synth.f64(inp.u), synth.f64(inp.delta), synth.f64(inp.A), synth.f64(inp.B), synth.f64(inp.C),
+            synth.f64(inp.Dp) if skip else None, synth.f64(inp.z) if gate else None, inp.cu_seqlens)
+    _, rout, rhT = orc.scan_fwd_state(*args, h0=h0, threads=8, **okw)
+    rg = orc.scan_bwd_state(*args, synth.f64(inp.dout), h0=h0, dhT=dhT, threads=8, **okw)
+    to, tg = TOL_OUT[inp.dtype], TOL_GRAD[inp.dtype]
+    assert_close(npy(out), rout, to, "out")
+    for k in ("du", "ddelta", "dA", "dB", "dC"):
+        assert_close(npy(g[k]), rg[k], tg, k)
+    if skip:
+        assert_close(npy(g["dD"]), rg["dD"], tg, "dD")
+    if gate:
+        assert_close(npy(g["dz"]), rg["dz"], tg, "dz")
+    if opts is not None:
+        assert_close(npy(g["ddelta_bias"]), rg["ddelta_bias"], tg, "ddelta_bias")
+    if "hT" in parts:
+        assert_close(npy(hT), rhT, to, "final_state")
+    else:
+        assert hT is None
+    if "dh0" in parts:
+        assert_close(npy(g["dinitial_state"]), rg["dh0"], tg, "dinitial_state")
+
+
+def test_scan_states_zero_match_reset_only():
+    """Zero initial states and zero final-state gradients give the reset-only
+    entry points' results bit for bit (the same arithmetic on the same data)."""
+    inp, gate, skip = _scan_case("zero-length-sequences")
+    out0, g0 = run_scan_gpu(inp, gate, skip)
+    d = Dev(inp)
+    zeros = torch.zeros((inp.nseq, inp.D, inp.N), dtype=torch.float32, device="cuda")
+    out1, ws, hT = ssp().selective_scan_pack_fwd(d.u, d.delta, d.A, d.B, d.C, d.Dp, d.z, d.pos, cu_seqlens=d.cu,
+                                                 initial_state=zeros, final_state=True)
+    g1 = ssp().selective_scan_pack_bwd(d.u, d.delta, d.A, d.B, d.C, d.Dp, d.z, d.pos, d.dout, ws, cu_seqlens=d.cu,
+                                       initial_state=zeros, dfinal_state=zeros, dinitial_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1)
+    for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD"):
+        assert torch.equal(g0[k], g1[k]), k
+    for s in range(inp.nseq):  # empty sequences hand on the zero state
+        if inp.lengths[s] == 0:
+            assert not hT[s].any() and not g1["dinitial_state"][s].any()
+
+
+def test_scan_cut_across_packs():
+    """One sequence cut at a pack end continues in the next pack: the second
+    pack starts from the first pack's final state, and the first pack's
+    backward takes the second's initial-state gradient. Per-token results
+    match the uncut sequence run in one pack; parameter gradients match the
+    sum over the two packs."""
+    inp = synth.make_inputs(2, lengths=[900, 1500, 700], D=128, with_u=True, with_dout=True)
+    cut = 900 + 611  # inside the second sequence, not on a chunk edge
+    whole = Dev(inp)
+    out_w, ws = ssp().selective_scan_pack_fwd(whole.u, whole.delta, whole.A, whole.B, whole.C, whole.Dp, whole.z,
+                                              whole.pos)
+    g_w = ssp().selective_scan_pack_bwd(whole.u, whole.delta, whole.A, whole.B, whole.C, whole.Dp, whole.z,
+                                        whole.pos, whole.dout, ws)
+    packs = []
+    for rows, lengths in ((slice(0, cut), [900, 611]), (slice(cut, inp.T), [1500 - 611, 700])):
+        import copy
+        p = copy.copy(inp)
+        for k in ("u", "delta", "z", "B", "C", "dout", "x"):
+            setattr(p, k, getattr(inp, k)[rows].contiguous())
+        p.lengths, p.cu_seqlens, p.T = lengths, synth.cu_seqlens_of(lengths), sum(lengths)
+        packs.append(Dev(p))
+    a, b = packs
+    D, N = inp.D, inp.N
+    out_a, ws_a, hT_a = ssp().selective_scan_pack_fwd(a.u, a.delta, a.A, a.B, a.C, a.Dp, a.z, a.pos,
+                                                      cu_seqlens=a.cu, final_state=True)
+    h0_b = torch.zeros((2, D, N), dtype=torch.float32, device="cuda")
+    h0_b[0] = hT_a[1]
+    out_b, ws_b, _ = ssp().selective_scan_pack_fwd(b.u, b.delta, b.A, b.B, b.C, b.Dp, b.z, b.pos, cu_seqlens=b.cu,
+                                                   initial_state=h0_b)
+    g_b = ssp().selective_scan_pack_bwd(b.u, b.delta, b.A, b.B, b.C, b.Dp, b.z, b.pos, b.dout, ws_b,
+                                        cu_seqlens=b.cu, initial_state=h0_b, dinitial_state=True)
+    dhT_a = torch.zeros((2, D, N), dtype=torch.float32, device="cuda")
+    dhT_a[1] = g_b["dinitial_state"][0]
+    g_a = ssp().selective_scan_pack_bwd(a.u, a.delta, a.A, a.B, a.C, a.Dp, a.z, a.pos, a.dout, ws_a,
+                                        cu_seqlens=a.cu, dfinal_state=dhT_a)
+    torch.cuda.synchronize()
+    tol = TOL_OUT[inp.dtype]
+    assert_close(npy(torch.cat([out_a, out_b])), npy(out_w), tol, "out")
+    for k in ("du", "ddelta", "dz", "dB", "dC"):
+        assert_close(npy(torch.cat([g_a[k], g_b[k]])), npy(g_w[k]), TOL_GRAD[inp.dtype], k)
+    for k in ("dA", "dD"):
+        assert_close(npy(g_a[k] + g_b[k]), npy(g_w[k]), 1e-3, k)
