@@ -57,7 +57,7 @@ const char *ssmp_status_string(int status);
 
 /* Version of this ABI (incremented on any change to the set of entry points
  * or their meaning; 2 added the _ex scan entry points, 3 the host packer
- * varlen_pack_plan, 4 the scan entry points with sequence states). */
+ * varlen_pack_plan, 4 the scan and conv entry points with sequence states). */
 int ssmp_abi_version(void);
 
 /*
@@ -113,6 +113,44 @@ int conv1d_pack_bwd(const void *x, const float *w, const float *b, const int32_t
                     const void *du, void *dx, float *dw, float *db,
                     void *workspace, size_t workspace_bytes,
                     int64_t T, int32_t D, int32_t W, int32_t dtype, int32_t silu, void *stream);
+
+/*
+ * conv1d_pack_fwd_states / conv1d_pack_bwd_states — the conv with a context
+ * per sequence: the W-1 inputs that precede a sequence's first token, which
+ * the reset otherwise treats as zeros. [P5] "结论与讨论" (a sequence cut at a
+ * pack end continues in the next pack) and [P1] section 3.2 (segment runs
+ * that reset or pass conv_states). With cu_seqlens (device int32 [nseq+1],
+ * the one pos was built from):
+ *   conv_initial   dtype (nseq, W-1, D), nullable (zeros): the context of
+ *                  sequence s, element (s, j, d) at (s*(W-1) + j)*D + d,
+ *                  j = 0 the oldest input, j = W-2 the one just before the
+ *                  sequence's first token
+ *   conv_final     dtype (nseq, W-1, D) out, nullable: the context a sequence
+ *                  hands on, its own last W-1 inputs (reaching into its
+ *                  context when shorter than W-1)
+ *   dconv_final    dtype (nseq, W-1, D), nullable (zero): dL/d conv_final
+ *   dconv_initial  dtype (nseq, W-1, D) out, nullable: dL/d conv_initial
+ * A piece that continues a sequence takes the previous piece's conv_final as
+ * its conv_initial (and the previous piece's backward takes this piece's
+ * dconv_initial as its dconv_final). The backward needs
+ * conv1d_pack_bwd_states_workspace_bytes(T, D, W, nseq) bytes of workspace
+ * (per-sequence corrections join the fixed-order sums). State buffers must
+ * not overlap one another or x, u, du, dx. With every state pointer NULL
+ * these are conv1d_pack_fwd / conv1d_pack_bwd.
+ * Errors as conv1d_pack_fwd / _bwd, plus SSMP_ERR_NULL (a state pointer
+ * without cu_seqlens) and SSMP_ERR_SHAPE (nseq < 1 with a state pointer).
+ */
+int conv1d_pack_fwd_states(const void *x, const float *w, const float *b, const int32_t *pos, void *u,
+                           int64_t T, int32_t D, int32_t W, int32_t dtype, int32_t silu,
+                           const int32_t *cu_seqlens, int32_t nseq, const void *conv_initial,
+                           void *conv_final, void *stream);
+size_t conv1d_pack_bwd_states_workspace_bytes(int64_t T, int32_t D, int32_t W, int32_t nseq);
+int conv1d_pack_bwd_states(const void *x, const float *w, const float *b, const int32_t *pos,
+                           const void *du, void *dx, float *dw, float *db,
+                           void *workspace, size_t workspace_bytes,
+                           int64_t T, int32_t D, int32_t W, int32_t dtype, int32_t silu,
+                           const int32_t *cu_seqlens, int32_t nseq, const void *conv_initial,
+                           const void *dconv_final, void *dconv_initial, void *stream);
 
 /*
  * selective_scan_pack_fwd — the selective scan with the state reset to zero

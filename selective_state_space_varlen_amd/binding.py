@@ -55,6 +55,12 @@ _SIGNATURES = {
                                                       _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32,
                                                       _c_vp, _c_i32, ctypes.c_float, _c_vp, _c_vp, _c_i32,
                                                       _c_vp, _c_vp, _c_vp, _c_vp]),
+    "conv1d_pack_fwd_states": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32,
+                                              _c_i32, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp]),
+    "conv1d_pack_bwd_states_workspace_bytes": (_c_sz, [_c_i64, _c_i32, _c_i32, _c_i32]),
+    "conv1d_pack_bwd_states": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz,
+                                              _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp,
+                                              _c_vp, _c_vp]),
     "varlen_pack_plan": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp,
                                         _c_vp, _c_vp]),
 }
@@ -184,14 +190,35 @@ def varlen_pack_indices(cu_seqlens: torch.Tensor, T: int, heads: bool = True, de
     return pos, hd, err
 
 
+def _out_or_new(spec, shape, dtype, dev):
+    if spec is True:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    return spec if isinstance(spec, torch.Tensor) else None
+
+
 def conv1d_pack_fwd(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor], pos: torch.Tensor,
-                    silu: bool = True, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    silu: bool = True, out: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
+                    conv_initial: Optional[torch.Tensor] = None, conv_final=False):
+    """Returns u. cu_seqlens (with optional conv_initial (nseq, W-1, D) and
+    conv_final: True, or an output tensor) selects conv1d_pack_fwd_states;
+    the return value is then (u, conv_final or None)."""
     T, D = x.shape
     W = w.shape[1]
     _check(x, "x"); _check(w, "w", (D, W), torch.float32, x.device); _check(b, "b", (D,), torch.float32, x.device)
     _check(pos, "pos", (T,), torch.int32, x.device)
     u = torch.empty_like(x) if out is None else out
     _check(u, "u", (T, D), x.dtype, x.device)
+    if cu_seqlens is not None or conv_initial is not None or conv_final is not False:
+        if cu_seqlens is None:
+            raise ValueError("conv states need cu_seqlens")
+        _check(cu_seqlens, "cu_seqlens", dtype=torch.int32, device=x.device)
+        nseq = cu_seqlens.numel() - 1
+        cf = _out_or_new(conv_final, (nseq, W - 1, D), x.dtype, x.device)
+        _check(conv_initial, "conv_initial", (nseq, W - 1, D), x.dtype, x.device)
+        _check(cf, "conv_final", (nseq, W - 1, D), x.dtype, x.device)
+        _call("conv1d_pack_fwd_states", _ptr(x), _ptr(w), _ptr(b), _ptr(pos), _ptr(u), T, D, W, _dtype_code(x),
+              int(silu), _ptr(cu_seqlens), nseq, _ptr(conv_initial), _ptr(cf), _stream(x))
+        return u, cf
     _call("conv1d_pack_fwd", _ptr(x), _ptr(w), _ptr(b), _ptr(pos), _ptr(u), T, D, W, _dtype_code(x), int(silu),
           _stream(x))
     return u
@@ -201,10 +228,19 @@ def conv1d_pack_bwd_workspace_bytes(T: int, D: int, W: int) -> int:
     return int(load().conv1d_pack_bwd_workspace_bytes(T, D, W))
 
 
+def conv1d_pack_bwd_states_workspace_bytes(T: int, D: int, W: int, nseq: int) -> int:
+    return int(load().conv1d_pack_bwd_states_workspace_bytes(T, D, W, nseq))
+
+
 def conv1d_pack_bwd(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor], pos: torch.Tensor,
                     du: torch.Tensor, silu: bool = True, workspace: Optional[torch.Tensor] = None,
-                    want_db: bool = True, out: Optional[tuple] = None):
-    """Returns (dx, dw, db); `out` may supply those three buffers."""
+                    want_db: bool = True, out: Optional[tuple] = None, cu_seqlens: Optional[torch.Tensor] = None,
+                    conv_initial: Optional[torch.Tensor] = None, dconv_final: Optional[torch.Tensor] = None,
+                    dconv_initial=False):
+    """Returns (dx, dw, db); `out` may supply those three buffers.
+    cu_seqlens (with optional conv_initial, dconv_final and dconv_initial:
+    True, or an output tensor) selects conv1d_pack_bwd_states; the return
+    value is then (dx, dw, db, dconv_initial or None)."""
     T, D = x.shape
     W = w.shape[1]
     _check(x, "x"); _check(w, "w", (D, W), torch.float32, x.device); _check(b, "b", (D,), torch.float32, x.device)
@@ -217,6 +253,21 @@ def conv1d_pack_bwd(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor],
         db = torch.empty((D,), dtype=torch.float32, device=x.device) if want_db else None
     _check(dx, "dx", (T, D), x.dtype, x.device); _check(dw, "dw", (D, W), torch.float32, x.device)
     _check(db, "db", (D,), torch.float32, x.device)
+    if cu_seqlens is not None or conv_initial is not None or dconv_final is not None or dconv_initial is not False:
+        if cu_seqlens is None:
+            raise ValueError("conv states need cu_seqlens")
+        _check(cu_seqlens, "cu_seqlens", dtype=torch.int32, device=x.device)
+        nseq = cu_seqlens.numel() - 1
+        dci = _out_or_new(dconv_initial, (nseq, W - 1, D), x.dtype, x.device)
+        for name, t in (("conv_initial", conv_initial), ("dconv_final", dconv_final), ("dconv_initial", dci)):
+            _check(t, name, (nseq, W - 1, D), x.dtype, x.device)
+        nbytes = conv1d_pack_bwd_states_workspace_bytes(T, D, W, nseq)
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+        _call("conv1d_pack_bwd_states", _ptr(x), _ptr(w), _ptr(b), _ptr(pos), _ptr(du), _ptr(dx), _ptr(dw),
+              _ptr(db), _ptr(workspace), workspace.numel() * workspace.element_size(), T, D, W, _dtype_code(x),
+              int(silu), _ptr(cu_seqlens), nseq, _ptr(conv_initial), _ptr(dconv_final), _ptr(dci), _stream(x))
+        return dx, dw, db, dci
     nbytes = conv1d_pack_bwd_workspace_bytes(T, D, W)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)

@@ -357,6 +357,133 @@ __global__ __launch_bounds__(256) void k_conv_bwd_reduce(const float* __restrict
     else db[d] = acc;
 }
 
+// ---------------------------------------------------------------------------
+// sequences with a conv context (conv1d_pack_*_states)
+// ---------------------------------------------------------------------------
+// ctx[s] holds the W-1 inputs before sequence s's first token ((nseq, W-1, D),
+// j = 0 the oldest); they stand in for the zeros of the reset. Only the first
+// W-1 tokens of a sequence see them, and only its last W-1 inputs make up the
+// context it hands on, so the streaming kernels above run unchanged and the
+// kernels below, one thread per (sequence, channel), redo the few tokens the
+// contexts touch.
+
+// input i of sequence s's extended input [ctx[s]; x[a:e)] (a = cu[s])
+template <typename T>
+__device__ __forceinline__ float ctx_input(const T* __restrict__ x, const T* __restrict__ ctx, int s, int64_t a,
+                                           int64_t i, int D, int W, int d) {
+    if (i >= a) return Elt<T>::ld(x, (size_t)i * D + d);
+    if (!ctx) return 0.0f;
+    return Elt<T>::ld(ctx, ((size_t)s * (W - 1) + (size_t)(i - (a - (W - 1)))) * D + d);
+}
+
+// forward: outputs of each sequence's first W-1 tokens with the context (ctx
+// non-null), and the context each sequence hands on (ctx_out non-null):
+// ctx_out[s][j] = input e - (W-1) + j of the extended input (e = cu[s+1])
+template <typename T, int W>
+__global__ __launch_bounds__(256) void k_conv_fwd_context(const T* __restrict__ x, const float* __restrict__ w,
+                                                          const float* __restrict__ b, const int32_t* __restrict__ cu,
+                                                          int nseq, const T* __restrict__ ctx, T* __restrict__ u,
+                                                          T* __restrict__ ctx_out, int D, int silu) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)nseq * D) return;
+    const int s = (int)(i / D), d = (int)(i % D);
+    const int64_t a = cu[s], e = cu[s + 1];
+    if (ctx) {
+        float wk[W];
+#pragma unroll
+        for (int k = 0; k < W; ++k) wk[k] = w[(size_t)d * W + (W - 1 - k)];
+        const float bias = b ? b[d] : 0.0f;
+        for (int j = 0; j < W - 1 && a + j < e; ++j) {
+            const int64_t t = a + j;
+            float acc = bias;
+#pragma unroll
+            for (int k = 0; k < W; ++k) acc = __builtin_fmaf(wk[k], ctx_input(x, ctx, s, a, t - k, D, W, d), acc);
+            Elt<T>::st(u, (size_t)t * D + d, silu ? acc * sigmoid_fast(acc) : acc);
+        }
+    }
+    if (ctx_out) {
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j)
+            Elt<T>::st(ctx_out, ((size_t)s * (W - 1) + j) * D + d, ctx_input(x, ctx, s, a, e - (W - 1) + j, D, W, d));
+    }
+}
+
+// backward: with a context, the first W-1 tokens' activation gradients change
+// (so do dx of those tokens and the tap and bias sums); the handed-on
+// context's gradient dctx_out adds to dx of the last W-1 inputs. This kernel
+// rewrites dx of those tokens in full, writes the context's gradient dctx,
+// and (with a context) per-sequence corrections of the tap and bias sums,
+// part[s][j][d] as the streaming kernel's partial rows, which the final
+// fixed-order reduction adds after them.
+template <typename T, int W>
+__global__ __launch_bounds__(256) void k_conv_bwd_context(
+    const T* __restrict__ x, const float* __restrict__ w, const float* __restrict__ b,
+    const int32_t* __restrict__ cu, int nseq, const T* __restrict__ ctx, const T* __restrict__ du,
+    const T* __restrict__ dctx_out, T* __restrict__ dx, T* __restrict__ dctx, float* __restrict__ part, int D,
+    int silu) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)nseq * D) return;
+    const int s = (int)(i / D), d = (int)(i % D);
+    const int64_t a = cu[s], e = cu[s + 1];
+    float wk[W];
+#pragma unroll
+    for (int k = 0; k < W; ++k) wk[k] = w[(size_t)d * W + (W - 1 - k)];
+    const float bias = b ? b[d] : 0.0f;
+    // pre-activation of token t (a <= t < e), with the context or with zeros
+    auto pre = [&](int64_t t, const T* c) {
+        float acc = bias;
+#pragma unroll
+        for (int k = 0; k < W; ++k) acc = __builtin_fmaf(wk[k], ctx_input(x, c, s, a, t - k, D, W, d), acc);
+        return acc;
+    };
+    auto grad = [&](int64_t t, float v) {
+        const float g = Elt<T>::ld(du, (size_t)t * D + d);
+        if (!silu) return g;
+        const float sg = sigmoid_fast(v);
+        return g * sg * (1.0f + v * (1.0f - sg));
+    };
+    // gradient of extended input p: taps of the tokens it feeds, plus the
+    // handed-on context's gradient if p is among the last W-1 inputs
+    auto input_grad = [&](int64_t p) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+            const int64_t t = p + k;
+            if (t >= a && t < e) acc = __builtin_fmaf(wk[k], grad(t, pre(t, ctx)), acc);
+        }
+        const int64_t jt = p - (e - (W - 1));
+        if (dctx_out && jt >= 0 && jt < W - 1) acc += Elt<T>::ld(dctx_out, ((size_t)s * (W - 1) + jt) * D + d);
+        return acc;
+    };
+    const int64_t first_end = ctx ? (a + W - 1 < e ? a + W - 1 : e) : a;
+    const int64_t last_start = dctx_out ? (e - (W - 1) > first_end ? e - (W - 1) : first_end) : e;
+    for (int64_t p = a; p < first_end; ++p) Elt<T>::st(dx, (size_t)p * D + d, input_grad(p));
+    for (int64_t p = last_start; p < e; ++p) Elt<T>::st(dx, (size_t)p * D + d, input_grad(p));
+    if (dctx) {
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j)
+            Elt<T>::st(dctx, ((size_t)s * (W - 1) + j) * D + d, input_grad(a - (W - 1) + j));
+    }
+    if (part) {
+        // the streaming kernel summed these tokens with a zero context
+        float dwc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, dbc = 0.0f;
+        for (int64_t t = a; t < first_end; ++t) {
+            const float gr = grad(t, pre(t, ctx));
+            const float gz = grad(t, pre(t, nullptr));
+            dbc += gr - gz;
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                const int64_t p = t - k;
+                dwc[k] += (p >= a) ? (gr - gz) * Elt<T>::ld(x, (size_t)p * D + d)
+                                   : gr * ctx_input(x, ctx, s, a, p, D, W, d);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) part[((size_t)s * 5 + k) * D + d] = dwc[k];
+        part[((size_t)s * 5 + 4) * D + d] = dbc;
+    }
+}
+
 // workgroups per 64-vector group of the backward (one partial row set each):
 // enough for one pass to cover every run of a short input
 static int64_t conv_bwd_groups(int64_t T_) {
@@ -367,6 +494,45 @@ static int64_t conv_bwd_groups(int64_t T_) {
 
 static bool vec_ok(const void* p, int D, int V, size_t elt) {
     return (D % V == 0) && ((reinterpret_cast<uintptr_t>(p) % (V * elt)) == 0);
+}
+
+template <typename T>
+static int launch_fwd_context(const void* x, const float* w, const float* b, const int32_t* cu, int nseq,
+                              const void* ctx, void* u, void* ctx_out, int D, int W, int silu, hipStream_t s) {
+    const int64_t n = (int64_t)nseq * D;
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+#define SSMP_CONV_CTX(WX)                                                                                        \
+    k_conv_fwd_context<T, WX><<<blocks, 256, 0, s>>>((const T*)x, w, b, cu, nseq, (const T*)ctx, (T*)u,          \
+                                                     (T*)ctx_out, D, silu)
+    switch (W) {
+        case 1: return SSMP_OK;  // no look-back, no context
+        case 2: SSMP_CONV_CTX(2); break;
+        case 3: SSMP_CONV_CTX(3); break;
+        default: SSMP_CONV_CTX(4); break;
+    }
+#undef SSMP_CONV_CTX
+    SSMP_LAUNCH_CHECK();
+    return SSMP_OK;
+}
+
+template <typename T>
+static int launch_bwd_context(const void* x, const float* w, const float* b, const int32_t* cu, int nseq,
+                              const void* ctx, const void* du, const void* dctx_out, void* dx, void* dctx,
+                              float* part, int D, int W, int silu, hipStream_t s) {
+    const int64_t n = (int64_t)nseq * D;
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+#define SSMP_CONV_CTX(WX)                                                                                        \
+    k_conv_bwd_context<T, WX><<<blocks, 256, 0, s>>>((const T*)x, w, b, cu, nseq, (const T*)ctx, (const T*)du,   \
+                                                     (const T*)dctx_out, (T*)dx, (T*)dctx, part, D, silu)
+    switch (W) {
+        case 1: return SSMP_OK;
+        case 2: SSMP_CONV_CTX(2); break;
+        case 3: SSMP_CONV_CTX(3); break;
+        default: SSMP_CONV_CTX(4); break;
+    }
+#undef SSMP_CONV_CTX
+    SSMP_LAUNCH_CHECK();
+    return SSMP_OK;
 }
 
 template <typename T>
@@ -399,9 +565,14 @@ static int launch_fwd(const void* x, const float* w, const float* b, const int32
     return SSMP_OK;
 }
 
+// extra_rows: per-sequence correction rows the context kernel wrote after the
+// streaming kernel's partial rows (zero without a context); the context
+// kernel runs between the streaming kernel and the reduction.
 template <typename T>
 static int launch_bwd(const void* x, const float* w, const float* b, const int32_t* pos, const void* du, void* dx,
-                      float* dw, float* db, float* part, int64_t T_, int D, int W, int silu, hipStream_t s) {
+                      float* dw, float* db, float* part, int64_t T_, int D, int W, int silu, hipStream_t s,
+                      int64_t extra_rows = 0, const int32_t* cu = nullptr, int nseq = 0, const void* ctx = nullptr,
+                      const void* dctx_out = nullptr, void* dctx = nullptr) {
     constexpr int VV = kBwdV<T>;
     const bool vec = vec_ok(x, D, VV, sizeof(T)) && vec_ok(du, D, VV, sizeof(T)) && vec_ok(dx, D, VV, sizeof(T));
     const int V = vec ? VV : 1;
@@ -427,7 +598,13 @@ static int launch_bwd(const void* x, const float* w, const float* b, const int32
 #undef SSMP_CONV_BWD_W
 #undef SSMP_CONV_BWD
     SSMP_LAUNCH_CHECK();
-    k_conv_bwd_reduce<<<(unsigned)((5 * (int64_t)D + 255) / 256), 256, 0, s>>>(part, ngrp, D, W, dw, db);
+    if (cu) {
+        const int st = launch_bwd_context<T>(x, w, b, cu, nseq, ctx, du, dctx_out, dx, dctx,
+                                             extra_rows ? part + (size_t)ngrp * 5 * D : nullptr, D, W, silu, s);
+        if (st) return st;
+    }
+    k_conv_bwd_reduce<<<(unsigned)((5 * (int64_t)D + 255) / 256), 256, 0, s>>>(part, ngrp + extra_rows, D, W, dw,
+                                                                               db);
     SSMP_LAUNCH_CHECK();
     return SSMP_OK;
 }
@@ -454,6 +631,34 @@ extern "C" int conv1d_pack_fwd(const void* x, const float* w, const float* b, co
                               : launch_fwd<float>(x, w, b, pos, u, T, D, W, silu != 0, s);
 }
 
+extern "C" int conv1d_pack_fwd_states(const void* x, const float* w, const float* b, const int32_t* pos, void* u,
+                                      int64_t T, int32_t D, int32_t W, int32_t dtype, int32_t silu,
+                                      const int32_t* cu_seqlens, int32_t nseq, const void* conv_initial,
+                                      void* conv_final, void* stream) {
+    using namespace ssmp;
+    int st = check_conv_args(T, D, W, dtype);
+    if (st) return st;
+    const bool states = conv_initial || conv_final;
+    if (states) {
+        if (!cu_seqlens) return SSMP_ERR_NULL;
+        if (nseq < 1 || (int64_t)nseq * D >= (int64_t(1) << 40)) return SSMP_ERR_SHAPE;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T > 0) {
+        if (!x || !w || !pos || !u) return SSMP_ERR_NULL;
+        st = dtype == SSMP_BF16 ? launch_fwd<uint16_t>(x, w, b, pos, u, T, D, W, silu != 0, s)
+                                : launch_fwd<float>(x, w, b, pos, u, T, D, W, silu != 0, s);
+        if (st) return st;
+    } else if (!w) {
+        return SSMP_ERR_NULL;
+    }
+    if (!states) return SSMP_OK;
+    return dtype == SSMP_BF16 ? launch_fwd_context<uint16_t>(x, w, b, cu_seqlens, nseq, conv_initial, u, conv_final,
+                                                             D, W, silu != 0, s)
+                              : launch_fwd_context<float>(x, w, b, cu_seqlens, nseq, conv_initial, u, conv_final, D,
+                                                          W, silu != 0, s);
+}
+
 extern "C" size_t conv1d_pack_bwd_workspace_bytes(int64_t T, int32_t D, int32_t W) {
     (void)W;
     if (T <= 0 || D <= 0) return 0;
@@ -478,4 +683,48 @@ extern "C" int conv1d_pack_bwd(const void* x, const float* w, const float* b, co
     return dtype == SSMP_BF16
                ? launch_bwd<uint16_t>(x, w, b, pos, du, dx, dw, db, (float*)workspace, T, D, W, silu != 0, s)
                : launch_bwd<float>(x, w, b, pos, du, dx, dw, db, (float*)workspace, T, D, W, silu != 0, s);
+}
+
+extern "C" size_t conv1d_pack_bwd_states_workspace_bytes(int64_t T, int32_t D, int32_t W, int32_t nseq) {
+    if (T <= 0 || D <= 0 || nseq < 0) return 0;
+    return conv1d_pack_bwd_workspace_bytes(T, D, W) + (size_t)nseq * 5 * (size_t)D * sizeof(float);
+}
+
+extern "C" int conv1d_pack_bwd_states(const void* x, const float* w, const float* b, const int32_t* pos,
+                                      const void* du, void* dx, float* dw, float* db, void* workspace,
+                                      size_t workspace_bytes, int64_t T, int32_t D, int32_t W, int32_t dtype,
+                                      int32_t silu, const int32_t* cu_seqlens, int32_t nseq,
+                                      const void* conv_initial, const void* dconv_final, void* dconv_initial,
+                                      void* stream) {
+    using namespace ssmp;
+    const bool states = conv_initial || dconv_final || dconv_initial;
+    if (!states)
+        return conv1d_pack_bwd(x, w, b, pos, du, dx, dw, db, workspace, workspace_bytes, T, D, W, dtype, silu,
+                               stream);
+    int st = check_conv_args(T, D, W, dtype);
+    if (st) return st;
+    if (!w || !dw || !cu_seqlens) return SSMP_ERR_NULL;
+    if (nseq < 1 || (int64_t)nseq * D >= (int64_t(1) << 40)) return SSMP_ERR_SHAPE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0) {
+        // no tokens: the sums are zero; every sequence hands the gradient of
+        // its handed-on context back to its own context
+        if ((st = zero_f32(dw, (int64_t)D * W, s))) return st;
+        if ((st = zero_f32(db, D, s))) return st;
+        if (!dconv_initial) return SSMP_OK;
+        return dtype == SSMP_BF16
+                   ? launch_bwd_context<uint16_t>(x, w, b, cu_seqlens, nseq, conv_initial, du, dconv_final, dx,
+                                                  dconv_initial, nullptr, D, W, silu != 0, s)
+                   : launch_bwd_context<float>(x, w, b, cu_seqlens, nseq, conv_initial, du, dconv_final, dx,
+                                               dconv_initial, nullptr, D, W, silu != 0, s);
+    }
+    if (!x || !pos || !du || !dx) return SSMP_ERR_NULL;
+    if (!workspace || workspace_bytes < conv1d_pack_bwd_states_workspace_bytes(T, D, W, nseq))
+        return SSMP_ERR_WORKSPACE;
+    const int64_t extra = (conv_initial && W > 1) ? nseq : 0;
+    return dtype == SSMP_BF16
+               ? launch_bwd<uint16_t>(x, w, b, pos, du, dx, dw, db, (float*)workspace, T, D, W, silu != 0, s, extra,
+                                      cu_seqlens, nseq, conv_initial, dconv_final, dconv_initial)
+               : launch_bwd<float>(x, w, b, pos, du, dx, dw, db, (float*)workspace, T, D, W, silu != 0, s, extra,
+                                   cu_seqlens, nseq, conv_initial, dconv_final, dconv_initial);
 }

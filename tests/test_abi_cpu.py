@@ -33,7 +33,8 @@ def test_header_lists_the_entry_points():
     for n in ("varlen_pack_indices", "conv1d_pack_fwd", "conv1d_pack_bwd", "selective_scan_pack_fwd",
               "selective_scan_pack_bwd", "selective_scan_pack_workspace_bytes", "conv1d_pack_bwd_workspace_bytes",
               "ssmp_status_string", "ssmp_abi_version", "selective_scan_pack_fwd_ex", "selective_scan_pack_bwd_ex",
-              "varlen_pack_plan", "selective_scan_pack_fwd_states", "selective_scan_pack_bwd_states"):
+              "varlen_pack_plan", "selective_scan_pack_fwd_states", "selective_scan_pack_bwd_states",
+              "conv1d_pack_fwd_states", "conv1d_pack_bwd_states", "conv1d_pack_bwd_states_workspace_bytes"):
         assert n in names, n
 
 

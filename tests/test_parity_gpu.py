@@ -490,3 +490,115 @@ def test_scan_cut_across_packs():
         assert_close(npy(torch.cat([g_a[k], g_b[k]])), npy(g_w[k]), TOL_GRAD[inp.dtype], k)
     for k in ("dA", "dD"):
         assert_close(npy(g_a[k] + g_b[k]), npy(g_w[k]), 1e-3, k)
+
+
+# ---------------------------------------------------------------------------
+# conv context per sequence (conv1d_pack_*_states)
+# ---------------------------------------------------------------------------
+
+CONV_STATE_CASES = [
+    # (dtype, D, W, silu, lengths, parts)
+    (torch.float32, 8, 4, True, [4, 2, 3, 7], "all"),
+    (torch.float32, 100, 3, True, [1, 5, 0, 130, 2, 70, 1], "all"),
+    (torch.bfloat16, 512, 4, True, [700, 1, 3, 0, 322, 129, 2], "all"),
+    (torch.bfloat16, 100, 4, True, [1, 5, 130, 2, 70, 1], "all"),       # per-element path
+    (torch.bfloat16, 256, 2, False, [256, 128, 3, 1], "all"),
+    (torch.bfloat16, 512, 4, True, [700, 1, 3, 322, 129], "initial"),
+    (torch.bfloat16, 512, 4, True, [700, 1, 3, 322, 129], "gradient"),
+    (torch.float32, 64, 1, True, [33, 1, 200], "all"),                 # width 1: no context at all
+]
+
+
+@pytest.mark.parametrize("case", range(len(CONV_STATE_CASES)))
+def test_conv_states_parity(orc, case):
+    dtype, D, W, silu, lengths, parts = CONV_STATE_CASES[case]
+    inp = synth.make_inputs(2, lengths=lengths, D=D, dtype=dtype, with_dout=True)
+    nseq = len(lengths)
+    rng = np.random.default_rng(case + 50)
+    w = torch.from_numpy(rng.uniform(-0.5, 0.5, (D, W)).astype(np.float32))
+    b = torch.from_numpy(rng.standard_normal(D).astype(np.float32))
+    ci = synth.to_dtype(rng.standard_normal((nseq, W - 1, D)), dtype) if parts in ("all", "initial") else None
+    dcf = synth.to_dtype(rng.standard_normal((nseq, W - 1, D)), dtype) if parts in ("all", "gradient") else None
+    d = Dev(inp)
+    wd, bd = to_dev(w), to_dev(b)
+    ci_d = to_dev(ci) if ci is not None else None
+    dcf_d = to_dev(dcf) if dcf is not None else None
+    u, cf = ssp().conv1d_pack_fwd(d.x, wd, bd, d.pos, silu=silu, cu_seqlens=d.cu, conv_initial=ci_d,
+                                  conv_final=True)
+    dx, dw, db, dci = ssp().conv1d_pack_bwd(d.x, wd, bd, d.pos, d.dout, silu=silu, cu_seqlens=d.cu,
+                                            conv_initial=ci_d, dconv_final=dcf_d, dconv_initial=True)
+    torch.cuda.synchronize()
+    f = lambda t: None if t is None else synth.f64(t)
+    _, ru, rcf = orc.conv_fwd_state(synth.f64(inp.x), w.double().numpy(), b.double().numpy(), inp.cu_seqlens,
+                                    f(ci), silu=silu, threads=4)
+    rdx, rdw, rdb, rdci = orc.conv_bwd_state(synth.f64(inp.x), w.double().numpy(), b.double().numpy(),
+                                             inp.cu_seqlens, synth.f64(inp.dout), f(ci), f(dcf), silu=silu,
+                                             threads=4)
+    assert_close(npy(u), ru, TOL_OUT[dtype], "u")
+    assert np.array_equal(npy(cf), rcf), "conv_final is a copy of inputs"
+    assert_close(npy(dx), rdx, TOL_GRAD[dtype], "dx")
+    assert_close(npy(dw), rdw, TOL_GRAD[dtype], "dw")
+    assert_close(npy(db), rdb, TOL_GRAD[dtype], "db")
+    if W > 1:
+        assert_close(npy(dci), rdci, TOL_GRAD[dtype], "dconv_initial")
+
+
+def test_pipeline_cut_across_packs(orc):
+    """A sequence cut at a pack end continues in the next pack through both
+    states: the conv context (the last W-1 inputs) and the SSM state, and
+    back through their gradients. Per-token results of the two packs match
+    the uncut pack; parameter gradients match the sum over the two packs; the
+    cut run also matches the oracle's state-carrying pipeline."""
+    lengths, cut_in = [900, 1500, 700], 611
+    inp = synth.make_inputs(2, lengths=lengths, D=128, with_dout=True)
+    cut = lengths[0] + cut_in
+    ss = ssp()
+
+    def run_pack(p, h0=None, ci=None, dhT=None, dcf=None):
+        d = Dev(p)
+        u, cf = ss.conv1d_pack_fwd(d.x, d.w, d.b, d.pos, silu=True, cu_seqlens=d.cu, conv_initial=ci,
+                                   conv_final=True)
+        out, ws, hT = ss.selective_scan_pack_fwd(u, d.delta, d.A, d.B, d.C, d.Dp, d.z, d.pos, cu_seqlens=d.cu,
+                                                 initial_state=h0, final_state=True)
+        g = ss.selective_scan_pack_bwd(u, d.delta, d.A, d.B, d.C, d.Dp, d.z, d.pos, d.dout, ws, cu_seqlens=d.cu,
+                                       initial_state=h0, dfinal_state=dhT, dinitial_state=True)
+        dx, dw, db, dci = ss.conv1d_pack_bwd(d.x, d.w, d.b, d.pos, g["du"], silu=True, cu_seqlens=d.cu,
+                                             conv_initial=ci, dconv_final=dcf, dconv_initial=True)
+        g.update({"dx": dx, "dw": dw, "db": db, "dci": dci, "out": out, "hT": hT, "cf": cf})
+        return g
+
+    import copy
+
+    def piece(rows, lens):
+        p = copy.copy(inp)
+        for k in ("x", "delta", "z", "B", "C", "dout"):
+            setattr(p, k, getattr(inp, k)[rows].contiguous())
+        p.lengths, p.cu_seqlens, p.T = lens, synth.cu_seqlens_of(lens), sum(lens)
+        return p
+
+    pa = piece(slice(0, cut), [lengths[0], cut_in])
+    pb = piece(slice(cut, inp.T), [lengths[1] - cut_in, lengths[2]])
+    whole = run_pack(inp)
+    D, N, W = inp.D, inp.N, inp.W
+    # forward: pack a, then pack b from a's last sequence's states
+    ga_fwd = run_pack(pa)
+    h0_b = torch.zeros((2, D, N), dtype=torch.float32, device="cuda"); h0_b[0] = ga_fwd["hT"][1]
+    ci_b = torch.zeros((2, W - 1, D), dtype=inp.x.dtype, device="cuda"); ci_b[0] = ga_fwd["cf"][1]
+    gb = run_pack(pb, h0=h0_b, ci=ci_b)
+    # backward: pack b first, then pack a with b's initial-state gradients
+    dhT_a = torch.zeros((2, D, N), dtype=torch.float32, device="cuda"); dhT_a[1] = gb["dinitial_state"][0]
+    dcf_a = torch.zeros((2, W - 1, D), dtype=inp.x.dtype, device="cuda"); dcf_a[1] = gb["dci"][0]
+    ga = run_pack(pa, dhT=dhT_a, dcf=dcf_a)
+    torch.cuda.synchronize()
+    to, tg = TOL_OUT[inp.dtype], TOL_GRAD[inp.dtype]
+    assert_close(npy(torch.cat([ga["out"], gb["out"]])), npy(whole["out"]), to, "out")
+    for k in ("dx", "du", "ddelta", "dz", "dB", "dC"):
+        assert_close(npy(torch.cat([ga[k], gb[k]])), npy(whole[k]), tg, k)
+    for k in ("dA", "dD", "dw", "db"):
+        assert_close(npy(ga[k] + gb[k]), npy(whole[k]), 1e-3, k)
+    # the second pack against the oracle's state-carrying pipeline
+    f64 = synth.f64
+    _, u_o, _ = orc.conv_fwd_state(f64(pb.x), f64(pb.w), f64(pb.b), pb.cu_seqlens, f64(ci_b), threads=8)
+    _, out_o, _ = orc.scan_fwd_state(u_o, f64(pb.delta), f64(pb.A), f64(pb.B), f64(pb.C), f64(pb.Dp), f64(pb.z),
+                                     pb.cu_seqlens, h0=npy(h0_b), threads=8)
+    assert_close(npy(gb["out"]), out_o, to, "out (oracle)")
