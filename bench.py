@@ -47,8 +47,8 @@ SCAN_BWD_FLOPS_PER_TDN = 22
 # Valid only for the kernel sources they were taken on (sha256 below); any
 # change to those sources reports null until the counters are taken again.
 MEASURED_TRAFFIC = {
-    "scan_bwd": {"bytes": 3774313321, "sources": ["scan_bwd.hip", "scan_common.h", "common.h"],
-                 "sha256": "fe63b6bfffd68fd349cabc1bfefabaf2d775270821444c570b2789d94393c970"},
+    "scan_bwd": {"bytes": 5326288541, "sources": ["scan_bwd.hip", "scan_common.h", "common.h"],
+                 "sha256": "2f6ede5b1b16ed21004a1c86242ebd00827d1057c1358bda14ed39e4c5249f66"},
 }
 
 
@@ -85,7 +85,7 @@ def log(msg: str) -> None:
 class Workload:
     """Device-resident inputs, outputs and workspaces of one packed batch."""
 
-    def __init__(self, inp: synth.Inputs, cu=None, dev="cuda:0"):
+    def __init__(self, inp: synth.Inputs, cu=None, dev="cuda:0", states: bool = False):
         import selective_state_space_varlen_amd as ssp
         self.ssp = ssp
         self.inp = inp
@@ -107,8 +107,22 @@ class Workload:
         self.dx = e(T, D)
         self.dw = e(D, W, dt=torch.float32)
         self.db = e(D, dt=torch.float32)
+        # every sequence starts from a given conv context and SSM state and
+        # hands on its own (the layout of sequences cut across packs)
+        self.states = states
+        if states:
+            nseq = len(cu_np) - 1
+            g = torch.Generator(device="cpu").manual_seed(5)
+            rnd = lambda *sh, dt=torch.float32: (torch.randn(*sh, generator=g) * 0.1).to(dt).to(d)
+            self.st = {"h0": rnd(nseq, D, N), "hT": e(nseq, D, N, dt=torch.float32), "dhT": rnd(nseq, D, N),
+                       "dh0": e(nseq, D, N, dt=torch.float32), "ci": rnd(nseq, W - 1, D, dt=self.x.dtype),
+                       "cf": e(nseq, W - 1, D), "dcf": rnd(nseq, W - 1, D, dt=self.x.dtype),
+                       "dci": e(nseq, W - 1, D)}
+            self.conv_ws = e(max(ssp.conv1d_pack_bwd_states_workspace_bytes(T, D, W, nseq), 1), dt=torch.uint8)
 
     def step(self, ev=None):
+        if self.states:
+            return self.step_states()
         s = self.ssp
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
         rec(0)
@@ -125,6 +139,22 @@ class Workload:
         s.conv1d_pack_bwd(self.x, self.w, self.b, self.pos, self.g["du"], silu=True, workspace=self.conv_ws,
                           out=(self.dx, self.dw, self.db))
         rec(5)
+
+
+    def step_states(self):
+        s, st, cu = self.ssp, self.st, self.cu
+        s.varlen_pack_indices(cu, self.T, heads=False, dev_err=False, out=self.pos)
+        s.conv1d_pack_fwd(self.x, self.w, self.b, self.pos, silu=True, out=self.u, cu_seqlens=cu,
+                          conv_initial=st["ci"], conv_final=st["cf"])
+        s.selective_scan_pack_fwd(self.u, self.delta, self.A, self.B, self.C, self.Dp, self.z, self.pos,
+                                  workspace=self.scan_ws, out=self.out, cu_seqlens=cu, initial_state=st["h0"],
+                                  final_state=st["hT"])
+        s.selective_scan_pack_bwd(self.u, self.delta, self.A, self.B, self.C, self.Dp, self.z, self.pos, self.dout,
+                                  self.scan_ws, out=self.g, cu_seqlens=cu, initial_state=st["h0"],
+                                  dfinal_state=st["dhT"], dinitial_state=st["dh0"])
+        s.conv1d_pack_bwd(self.x, self.w, self.b, self.pos, self.g["du"], silu=True, workspace=self.conv_ws,
+                          out=(self.dx, self.dw, self.db), cu_seqlens=cu, conv_initial=st["ci"],
+                          dconv_final=st["dcf"], dconv_initial=st["dci"])
 
 
 OPS = ["pack_indices", "conv_fwd", "scan_fwd", "scan_bwd", "conv_bwd"]
@@ -363,6 +393,13 @@ def main():
     layouts = None
     if not args.no_layouts:
         layouts = {"packed": round(tok_s, 1)}
+        # the same pack with every sequence carrying conv and SSM states in
+        # and out (forward and backward), as when sequences are cut at pack ends
+        wsx = Workload(inp, states=True)
+        nq = max(3, args.steps // 2)
+        ms_x, _ = time_steps(wsx, nq, 2, per_op=False)
+        layouts["packed_carry_states"] = round(T / (ms_x / nq * 1e-3), 1)
+        del wsx
         cu_concat = np.arange(0, T + 1, spec.pack_len, dtype=np.int32)
         wc = Workload(inp, cu=cu_concat)
         ms_c, _ = time_steps(wc, max(3, args.steps // 2), 2, per_op=False)

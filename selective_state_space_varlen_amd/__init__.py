@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     PackPlan,
     SsmpError,
     conv1d_pack_bwd,
+    conv1d_pack_bwd_states_workspace_bytes,
     conv1d_pack_bwd_workspace_bytes,
     conv1d_pack_fwd,
     load,
