@@ -530,9 +530,7 @@ __global__ __launch_bounds__(kWave * WV, 2) void k_scan_bwd_main(BwdArgs<T> p) {
     // Each sub-chunk restarts from the checkpoint at its first token; the
     // next sub-chunk's state (kK tokens earlier) is loaded while this one runs.
     auto load_state = [&](int64_t ts, float (&hs)[NH]) {
-        const float* hp = p.ckpt + (size_t)(ts / kCK) * ND;
-#pragma unroll
-        for (int i = 0; i < NH; ++i) hs[i] = act ? hp[(size_t)(n0 + i) * D + dd] : 0.0f;
+        ck_load<NS, NH>(p.ckpt + (size_t)(ts / kCK) * ND, dd, D, n0, act, hs);
     };
 
     const int64_t nblk = (t1 - t0 + kBB - 1) / kBB;

@@ -75,6 +75,46 @@ struct ScanOpts {
     float* dh0 = nullptr;
 };
 
+// A checkpoint slot holds the states of every channel in groups of four
+// ([n/4][d][4] for d_state a multiple of 4, else [n][d]): a wave's 16-byte
+// stores of one group cover 1 KiB of contiguous memory, and a lane loads its
+// states 16 bytes at a time.
+template <int NS>
+__device__ __forceinline__ size_t ck_index(int d, int n, int D) {
+    if constexpr (NS % 4 == 0) return (((size_t)(n >> 2) * D + d) << 2) + (n & 3);
+    else return (size_t)n * D + d;
+}
+template <int NS>
+__device__ __forceinline__ void ck_store(float* __restrict__ slot, int d, int D, const float (&h)[NS]) {
+    if constexpr (NS % 4 == 0) {
+#pragma unroll
+        for (int j = 0; j < NS / 4; ++j)
+            reinterpret_cast<float4*>(slot)[(size_t)j * D + d] =
+                make_float4(h[4 * j], h[4 * j + 1], h[4 * j + 2], h[4 * j + 3]);
+    } else {
+#pragma unroll
+        for (int n = 0; n < NS; ++n) slot[(size_t)n * D + d] = h[n];
+    }
+}
+// states n0 .. n0+NH-1 of channel d (zero when `on` is false)
+template <int NS, int NH>
+__device__ __forceinline__ void ck_load(const float* __restrict__ slot, int d, int D, int n0, bool on,
+                                           float (&h)[NH]) {
+    if (!on) {
+#pragma unroll
+        for (int i = 0; i < NH; ++i) h[i] = 0.0f;
+    } else if constexpr (NS % 4 == 0 && NH % 4 == 0) {
+#pragma unroll
+        for (int j = 0; j < NH / 4; ++j) {
+            const float4 v = reinterpret_cast<const float4*>(slot)[(size_t)((n0 >> 2) + j) * D + d];
+            h[4 * j] = v.x; h[4 * j + 1] = v.y; h[4 * j + 2] = v.z; h[4 * j + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NH; ++i) h[i] = slot[ck_index<NS>(d, n0 + i, D)];
+    }
+}
+
 // Sequence of token t: the largest s with cu[s] <= t (zero-length sequences
 // sharing that start come before it). Wave-uniform: every lane of a wave asks
 // about the same token, and it runs only at heads and ends. For any cu the
@@ -136,7 +176,7 @@ struct ScanWs {
     int64_t nsum;     // backward summary sub-chunks
     int64_t ngroup;   // channel groups of 64
     // offsets in floats from the workspace base
-    size_t ckpt;      // [nck][N][D]      forward -> backward
+    size_t ckpt;      // [nck][N/4][D][4] forward -> backward
     size_t bc;        // [T][2N]          fp32 copy of the B and C rows (each pass makes its own)
     size_t P, S;      // forward: P [nchunk][D] sum of delta (NaN: cut by a head), S [nchunk][N][D] local end state
     size_t Pr, Sr;    // backward, per summary sub-chunk: Pr [nsum][D] as P, Sr [nsum][N][D] reverse carry

@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void k_scan_fwd_carry(const float* __restrict_
         }
     };
     float h = 0.0f;
-    float* kp = ckpt + i;  // checkpoint slot of chunk c's first token
+    float* kp = ckpt + ck_index<NS>(dch, (int)(i / D), D);  // checkpoint slot of chunk c's first token
     const size_t kstride = (size_t)(lc / kCK) * ND;
     Batch cur, nxt;
     load(cur, 0);
@@ -266,8 +266,7 @@ __device__ __forceinline__ void out_block(const T* lds, const float* __restrict_
             if (k >= nt) break;
         }
         if (k % kCK == 0 && act && !(k == 0 && skip0)) {
-#pragma unroll
-            for (int n = 0; n < NS; ++n) ck[(size_t)(k / kCK) * ND + (size_t)n * D + d] = h[n];
+            ck_store<NS>(ck + (size_t)(k / kCK) * ND, d, D, h);
         }
         float nxt[2 * NS];
         const bool more = SAFE ? (k + 1 < nt) : (k + 1 < BT);
@@ -314,8 +313,11 @@ __device__ __forceinline__ void out_block(const T* lds, const float* __restrict_
     }
 }
 
+// Four waves per SIMD (128 VGPRs) for the reset-only kernel; the state
+// variant, whose heads load arbitrary states, would spill at that budget in
+// its hot loop and runs faster at up to 256 VGPRs (measured: 3 waves fit).
 template <typename T, int NS, bool GATE, bool XS, bool ST>
-__global__ __launch_bounds__(64, 4) void k_scan_fwd_out(const T* __restrict__ u, const T* __restrict__ delta,
+__global__ __launch_bounds__(64, ST ? 2 : 4) void k_scan_fwd_out(const T* __restrict__ u, const T* __restrict__ delta,
                                                      const float* __restrict__ A, const float* __restrict__ bc,
                                                      const float* __restrict__ Dskip, const T* __restrict__ z,
                                                      const int32_t* __restrict__ pos, T* __restrict__ out,
@@ -339,8 +341,9 @@ __global__ __launch_bounds__(64, 4) void k_scan_fwd_out(const T* __restrict__ u,
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
         A2[n] = A[(size_t)dd * NS + n] * kLog2e;
-        h[n] = act ? ckpt[(size_t)(t0 / kCK) * ND + (size_t)n * D + dd] : 0.0f;
+        h[n] = 0.0f;
     }
+    ck_load<NS, NS>(ckpt + (size_t)(t0 / kCK) * ND, dd, D, 0, act, h);
     const float Dv = (Dskip && act) ? Dskip[dd] : 0.0f;
     const StepMap sm = step_map(opt, dd);
     const T* const src[3] = {u, delta, GATE ? z : u};
