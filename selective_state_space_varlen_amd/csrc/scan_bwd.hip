@@ -263,16 +263,25 @@ struct BwdArgs {
 
 constexpr int kRedStride = kWave + 4;  // LDS row stride (floats) of the dB/dC transpose
 
+// The decays a = exp2(delta A2) of a sub-chunk's replay are kept for its
+// reverse step (32 VGPRs at d_state 16) where the registers allow: with 2-byte
+// inputs the backward's main kernel fits them without spilling, with fp32
+// inputs (larger staging) it would spill, so it computes them again.
+template <typename T>
+constexpr bool kCacheDecay = sizeof(T) == 2;
+
 // Replay of one kK-token sub-chunk from its entering state h: the states hh[k]
-// after each token and the pre-gate outputs yk[k]. SAFE sub-chunks may be
+// after each token, their decays ak[k] (kCacheDecay) and the pre-gate outputs
+// yk[k]. SAFE sub-chunks may be
 // short (ns < kK) and may hold heads; the fast ones are full and head-free.
 // With initial states, a head starts from its sequence's h0 (this lane's
 // share of the states) instead of zero.
 template <bool SAFE, bool XS, bool ST, int NS, int LPC, typename St, typename T>
 __device__ __forceinline__ void bwd_replay(const T* lds, const float* bcl, int kb, int ns, uint32_t heads, int ch,
                                            int n0, const float (&A2)[NS / LPC], float (&h)[NS / LPC],
-                                           float (&hh)[kK][NS / LPC], float (&yk)[kK], float Dv, const StepMap& sm,
-                                           const ScanOpts& opt, int64_t tb, int D, int dd) {
+                                           float (&hh)[kK][NS / LPC], float (&ak)[kK][NS / LPC], float (&yk)[kK],
+                                           float Dv, const StepMap& sm, const ScanOpts& opt, int64_t tb, int D,
+                                           int dd) {
     // on return h holds the state after the last replayed token
     constexpr int NH = NS / LPC;
 #pragma unroll
@@ -302,7 +311,9 @@ __device__ __forceinline__ void bwd_replay(const T* lds, const float* bcl, int k
         float y = 0.0f;
 #pragma unroll
         for (int i = 0; i < NH; ++i) {
-            h[i] = __builtin_fmaf(exp2_fast(dt * A2[i]), h[i], dtu * row[i]);
+            const float a = exp2_fast(dt * A2[i]);
+            if constexpr (kCacheDecay<T>) ak[kk][i] = a;
+            h[i] = __builtin_fmaf(a, h[i], dtu * row[i]);
             hh[kk][i] = h[i];
             y = __builtin_fmaf(row[NS + i], h[i], y);
         }
@@ -328,6 +339,7 @@ __device__ __forceinline__ void bwd_reverse(const T* lds, const float* bcl, floa
                                             int D, int d, const float (&A2)[NS / LPC], float (&carry)[NS / LPC],
                                             float (&dA)[NS / LPC], float& dDacc, float Dv,
                                             const float (&hin)[NS / LPC], const float (&hh)[kK][NS / LPC],
+                                            const float (&ak)[kK][NS / LPC],
                                             const float (&yk)[kK], const BwdRows<T>& rows, const StepMap& sm,
                                             float gf, float& dbacc, const ScanOpts& opt, int64_t tb, int dd) {
     constexpr int NH = NS / LPC;
@@ -375,7 +387,7 @@ __device__ __forceinline__ void bwd_reverse(const T* lds, const float* bcl, floa
                 red[NH + i][col] = gg * hh[kk][i];  // dC row
                 sumB = __builtin_fmaf(dh, row[i], sumB);
                 if (st) {
-                    const float cr = exp2_fast(dt * A2[i]) * dh;
+                    const float cr = (kCacheDecay<T> ? ak[kk][i] : exp2_fast(dt * A2[i])) * dh;
                     if (opt.h0) {
                         const float r = cr * opt.h0[so + i];
                         sumAr = __builtin_fmaf(r, A2[i], sumAr);
@@ -393,7 +405,7 @@ __device__ __forceinline__ void bwd_reverse(const T* lds, const float* bcl, floa
                 red[NH + i][col] = gg * hh[kk][i];
                 sumB = __builtin_fmaf(dh, row[i], sumB);
                 // carry to t-1: a_t dh_t; r = dh_t a_t h_{t-1}
-                carry[i] = exp2_fast(dt * A2[i]) * dh;
+                carry[i] = (kCacheDecay<T> ? ak[kk][i] : exp2_fast(dt * A2[i])) * dh;
                 const float r = carry[i] * (kk == 0 ? hin[i] : hh[kk > 0 ? kk - 1 : 0][i]);
                 sumAr = __builtin_fmaf(r, A2[i], sumAr);
                 dA[i] = __builtin_fmaf(r, dt, dA[i]);
@@ -561,7 +573,7 @@ __global__ __launch_bounds__(kWave * WV, 2) void k_scan_bwd_main(BwdArgs<T> p) {
         for (int sc = nsub - 1; sc >= 0; --sc) {
             const int kb = sc * kK;  // first token of the sub-chunk within the block
             const int ns = (nb - kb < kK) ? nb - kb : kK;
-            float h[NH], hin[NH], hh[kK][NH], yk[kK];
+            float h[NH], hin[NH], hh[kK][NH], ak[kK][NH], yk[kK];
 #pragma unroll
             for (int i = 0; i < NH; ++i) {
                 h[i] = hn[i];
@@ -570,16 +582,16 @@ __global__ __launch_bounds__(kWave * WV, 2) void k_scan_bwd_main(BwdArgs<T> p) {
             if (tb0 + kb - kK >= t0) load_state(tb0 + kb - kK, hn);
             const uint32_t sub_heads = (heads >> kb) & ((1u << kK) - 1u);
             if (sub_heads == 0 && ns == kK) {
-                bwd_replay<false, XS, ST, NS, LPC, St>(mylds, bcl, kb, kK, 0u, ch, n0, A2, h, hh, yk, Dv, sm, p.opt, tb0,
+                bwd_replay<false, XS, ST, NS, LPC, St>(mylds, bcl, kb, kK, 0u, ch, n0, A2, h, hh, ak, yk, Dv, sm, p.opt, tb0,
                                                    D, dd);
                 bwd_reverse<false, GATE, XS, ST, NS, LPC, St>(mylds, bcl, red[wv], kb, kK, 0u, lane, ch, sh, n0, act,
-                                                          full, D, d, A2, carry, dA, dDacc, Dv, hin, hh, yk, rows,
+                                                          full, D, d, A2, carry, dA, dDacc, Dv, hin, hh, ak, yk, rows,
                                                           sm, gf, dbacc, p.opt, tb0, dd);
             } else {
-                bwd_replay<true, XS, ST, NS, LPC, St>(mylds, bcl, kb, ns, heads, ch, n0, A2, h, hh, yk, Dv, sm, p.opt, tb0,
+                bwd_replay<true, XS, ST, NS, LPC, St>(mylds, bcl, kb, ns, heads, ch, n0, A2, h, hh, ak, yk, Dv, sm, p.opt, tb0,
                                                   D, dd);
                 bwd_reverse<true, GATE, XS, ST, NS, LPC, St>(mylds, bcl, red[wv], kb, ns, heads, lane, ch, sh, n0, act,
-                                                         full, D, d, A2, carry, dA, dDacc, Dv, hin, hh, yk, rows,
+                                                         full, D, d, A2, carry, dA, dDacc, Dv, hin, hh, ak, yk, rows,
                                                          sm, gf, dbacc, p.opt, tb0, dd);
             }
         }
