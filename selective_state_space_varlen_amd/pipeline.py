@@ -20,24 +20,59 @@ from . import binding as _b
 
 def forward(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor], delta: torch.Tensor, A: torch.Tensor,
             B: torch.Tensor, C: torch.Tensor, Dskip: Optional[torch.Tensor], z: Optional[torch.Tensor],
-            cu_seqlens: torch.Tensor, pos: Optional[torch.Tensor] = None, ws: Optional[dict] = None) -> dict:
-    """Returns {'pos', 'u', 'out', 'scan_ws'}; keep it for backward."""
+            cu_seqlens: torch.Tensor, pos: Optional[torch.Tensor] = None, ws: Optional[dict] = None,
+            initial_states: Optional[dict] = None, final_states: bool = False) -> dict:
+    """Returns {'pos', 'u', 'out', 'scan_ws'}; keep it for backward.
+
+    Sequences continued from an earlier pack (the article's section
+    "结论与讨论": a sequence cut at a pack end keeps passing state) take
+    initial_states = {'ssm': (nseq, D, N) fp32, 'conv': (nseq, W-1, D)} (either
+    may be None: zeros); with final_states=True, or with initial states, the
+    result also holds 'final_states' in the same form."""
     T = x.shape[0]
     if pos is None:
         pos, _, _ = _b.varlen_pack_indices(cu_seqlens, T, heads=False, dev_err=False)
-    u = _b.conv1d_pack_fwd(x, w, b, pos, silu=True, out=None if ws is None else ws.get("u"))
-    out, scan_ws = _b.selective_scan_pack_fwd(u, delta, A, B, C, Dskip, z, pos,
-                                              workspace=None if ws is None else ws.get("scan"),
-                                              out=None if ws is None else ws.get("out"))
-    return {"pos": pos, "u": u, "out": out, "scan_ws": scan_ws}
+    carry = initial_states is not None or final_states
+    res = {"pos": pos}
+    if carry:
+        st = initial_states or {}
+        u, cf = _b.conv1d_pack_fwd(x, w, b, pos, silu=True, out=None if ws is None else ws.get("u"),
+                                   cu_seqlens=cu_seqlens, conv_initial=st.get("conv"), conv_final=True)
+        out, scan_ws, hT = _b.selective_scan_pack_fwd(u, delta, A, B, C, Dskip, z, pos,
+                                                      workspace=None if ws is None else ws.get("scan"),
+                                                      out=None if ws is None else ws.get("out"),
+                                                      cu_seqlens=cu_seqlens, initial_state=st.get("ssm"),
+                                                      final_state=True)
+        res.update({"final_states": {"ssm": hT, "conv": cf}, "cu_seqlens": cu_seqlens, "initial_states": st})
+    else:
+        u = _b.conv1d_pack_fwd(x, w, b, pos, silu=True, out=None if ws is None else ws.get("u"))
+        out, scan_ws = _b.selective_scan_pack_fwd(u, delta, A, B, C, Dskip, z, pos,
+                                                  workspace=None if ws is None else ws.get("scan"),
+                                                  out=None if ws is None else ws.get("out"))
+    res.update({"u": u, "out": out, "scan_ws": scan_ws})
+    return res
 
 
 def backward(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor], delta: torch.Tensor, A: torch.Tensor,
              B: torch.Tensor, C: torch.Tensor, Dskip: Optional[torch.Tensor], z: Optional[torch.Tensor],
-             fwd: dict, dout: torch.Tensor, conv_ws: Optional[torch.Tensor] = None) -> dict:
-    """Gradients of sum(dout * out) for x, w, b, delta, A, B, C, Dskip, z."""
-    g = _b.selective_scan_pack_bwd(fwd["u"], delta, A, B, C, Dskip, z, fwd["pos"], dout, fwd["scan_ws"])
-    dx, dw, db = _b.conv1d_pack_bwd(x, w, b, fwd["pos"], g["du"], silu=True, workspace=conv_ws,
-                                    want_db=b is not None)
-    g.update({"dx": dx, "dw": dw, "db": db})
+             fwd: dict, dout: torch.Tensor, conv_ws: Optional[torch.Tensor] = None,
+             dfinal_states: Optional[dict] = None) -> dict:
+    """Gradients of sum(dout * out) (+ sum(dfinal * final) for carried states)
+    for x, w, b, delta, A, B, C, Dskip, z. When the forward carried states, the
+    result also holds 'dinitial_states' {'ssm', 'conv'}, the gradients to hand
+    to the earlier pack's backward as its dfinal_states."""
+    if "cu_seqlens" not in fwd:
+        g = _b.selective_scan_pack_bwd(fwd["u"], delta, A, B, C, Dskip, z, fwd["pos"], dout, fwd["scan_ws"])
+        dx, dw, db = _b.conv1d_pack_bwd(x, w, b, fwd["pos"], g["du"], silu=True, workspace=conv_ws,
+                                        want_db=b is not None)
+        g.update({"dx": dx, "dw": dw, "db": db})
+        return g
+    cu, st, dfs = fwd["cu_seqlens"], fwd["initial_states"], dfinal_states or {}
+    g = _b.selective_scan_pack_bwd(fwd["u"], delta, A, B, C, Dskip, z, fwd["pos"], dout, fwd["scan_ws"],
+                                   cu_seqlens=cu, initial_state=st.get("ssm"), dfinal_state=dfs.get("ssm"),
+                                   dinitial_state=True)
+    dx, dw, db, dci = _b.conv1d_pack_bwd(x, w, b, fwd["pos"], g["du"], silu=True, workspace=conv_ws,
+                                         want_db=b is not None, cu_seqlens=cu, conv_initial=st.get("conv"),
+                                         dconv_final=dfs.get("conv"), dconv_initial=True)
+    g.update({"dx": dx, "dw": dw, "db": db, "dinitial_states": {"ssm": g.pop("dinitial_state"), "conv": dci}})
     return g

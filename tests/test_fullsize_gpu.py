@@ -79,3 +79,55 @@ def test_fullsize_sampled(orc, workload):
                          f(inp.Dp), f(inp.z)[sl], one, f(inp.dout)[sl], threads=16)
         assert_close(npy(G["dB"][lo:hi]), R["dB"], tg, f"dB seq {s} (len {hi - lo})")
         assert_close(npy(G["dC"][lo:hi]), R["dC"], tg, f"dC seq {s} (len {hi - lo})")
+
+
+def test_fullsize_carried_states(orc):
+    """The benchmark pack (workload 4) with every sequence carrying an SSM state
+    and a conv context in and out, forward and backward, through the block
+    chain: every token of sampled channels against the oracle's
+    state-carrying pipeline, and the states and their gradients of those
+    channels for every sequence."""
+    import selective_state_space_varlen_amd as ssp
+    print("[fullsize] workload 4 with carried states", flush=True)
+    inp = synth.make_inputs(4, with_dout=True)
+    nseq, D, N, W = inp.nseq, inp.D, inp.N, inp.W
+    rng = np.random.default_rng(77)
+    h0 = (rng.standard_normal((nseq, D, N)) * 0.5).astype(np.float32)
+    dhT = rng.standard_normal((nseq, D, N)).astype(np.float32)
+    ci = synth.to_dtype(rng.standard_normal((nseq, W - 1, D)), inp.dtype)
+    dcf = synth.to_dtype(rng.standard_normal((nseq, W - 1, D)), inp.dtype)
+    d = Dev(inp)
+    dev = lambda a: torch.from_numpy(a).cuda() if isinstance(a, np.ndarray) else a.cuda()
+    F = ssp.forward(d.x, d.w, d.b, d.delta, d.A, d.B, d.C, d.Dp, d.z, d.cu, pos=d.pos,
+                    initial_states={"ssm": dev(h0), "conv": dev(ci)}, final_states=True)
+    G = ssp.backward(d.x, d.w, d.b, d.delta, d.A, d.B, d.C, d.Dp, d.z, F, d.dout,
+                     dfinal_states={"ssm": dev(dhT), "conv": dev(dcf)})
+    torch.cuda.synchronize()
+    to, tg = TOL_OUT[inp.dtype], TOL_GRAD[inp.dtype]
+
+    ch = sampled_channels(D)
+    f = synth.f64
+    cu = inp.cu_seqlens
+    x, w, b = f(inp.x)[:, ch], f(inp.w)[ch], f(inp.b)[ch]
+    delta, A, Dp, z, dout = f(inp.delta)[:, ch], f(inp.A)[ch], f(inp.Dp)[ch], f(inp.z)[:, ch], f(inp.dout)[:, ch]
+    B, C = f(inp.B), f(inp.C)
+    ci_s, dcf_s = f(ci)[:, :, ch], f(dcf)[:, :, ch]
+    h0_s, dhT_s = h0[:, ch].astype(np.float64), dhT[:, ch].astype(np.float64)
+    _, u, cf = orc.conv_fwd_state(x, w, b, cu, ci_s, threads=16)
+    _, out, hT = orc.scan_fwd_state(u, delta, A, B, C, Dp, z, cu, h0=h0_s, threads=16)
+    Rg = orc.scan_bwd_state(u, delta, A, B, C, Dp, z, cu, dout, h0=h0_s, dhT=dhT_s, threads=16)
+    dx, dw, db, dci = orc.conv_bwd_state(x, w, b, cu, Rg["du"], ci_s, dcf_s, threads=16)
+    cht = torch.from_numpy(ch).cuda()
+    assert_close(npy(F["u"][:, cht]), u, to, "u")
+    assert_close(npy(F["out"][:, cht]), out, to, "out")
+    assert_close(npy(F["final_states"]["ssm"][:, cht]), hT, to, "final ssm state")
+    assert np.array_equal(npy(F["final_states"]["conv"][:, :, cht]), cf), "final conv context"
+    for k in ("du", "ddelta", "dz"):
+        assert_close(npy(G[k][:, cht]), Rg[k], tg, k)
+    assert_close(npy(G["dx"][:, cht]), dx, tg, "dx")
+    assert_close(npy(G["dA"][cht]), Rg["dA"], tg, "dA")
+    assert_close(npy(G["dD"][cht]), Rg["dD"], tg, "dD")
+    assert_close(npy(G["dw"][cht]), dw, tg, "dw")
+    assert_close(npy(G["db"][cht]), db, tg, "db")
+    assert_close(npy(G["dinitial_states"]["ssm"][:, cht]), Rg["dh0"], tg, "dinitial ssm state")
+    assert_close(npy(G["dinitial_states"]["conv"][:, :, cht]), dci, tg, "dinitial conv context")

@@ -555,16 +555,14 @@ def test_pipeline_cut_across_packs(orc):
     ss = ssp()
 
     def run_pack(p, h0=None, ci=None, dhT=None, dcf=None):
+        # through the block-level chain (pipeline.forward / backward)
         d = Dev(p)
-        u, cf = ss.conv1d_pack_fwd(d.x, d.w, d.b, d.pos, silu=True, cu_seqlens=d.cu, conv_initial=ci,
-                                   conv_final=True)
-        out, ws, hT = ss.selective_scan_pack_fwd(u, d.delta, d.A, d.B, d.C, d.Dp, d.z, d.pos, cu_seqlens=d.cu,
-                                                 initial_state=h0, final_state=True)
-        g = ss.selective_scan_pack_bwd(u, d.delta, d.A, d.B, d.C, d.Dp, d.z, d.pos, d.dout, ws, cu_seqlens=d.cu,
-                                       initial_state=h0, dfinal_state=dhT, dinitial_state=True)
-        dx, dw, db, dci = ss.conv1d_pack_bwd(d.x, d.w, d.b, d.pos, g["du"], silu=True, cu_seqlens=d.cu,
-                                             conv_initial=ci, dconv_final=dcf, dconv_initial=True)
-        g.update({"dx": dx, "dw": dw, "db": db, "dci": dci, "out": out, "hT": hT, "cf": cf})
+        F = ss.forward(d.x, d.w, d.b, d.delta, d.A, d.B, d.C, d.Dp, d.z, d.cu, pos=d.pos,
+                       initial_states={"ssm": h0, "conv": ci}, final_states=True)
+        g = ss.backward(d.x, d.w, d.b, d.delta, d.A, d.B, d.C, d.Dp, d.z, F, d.dout,
+                        dfinal_states={"ssm": dhT, "conv": dcf})
+        g.update({"dinitial_state": g["dinitial_states"]["ssm"], "dci": g["dinitial_states"]["conv"],
+                  "out": F["out"], "hT": F["final_states"]["ssm"], "cf": F["final_states"]["conv"]})
         return g
 
     import copy
