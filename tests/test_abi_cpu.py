@@ -54,13 +54,16 @@ def test_status_strings(lib):
 
 
 def test_workspace_sizes(lib):
-    # checkpoints (one fp32 state per 16 tokens) dominate the scan workspace
+    # checkpoints (the fp32 states of every 4th token) dominate the scan workspace
     T, D, N = 32768, 4096, 16
     ws = lib.selective_scan_pack_workspace_bytes(T, D, N)
-    assert ws >= (T // 16) * D * N * 4
+    assert ws >= (T // 4) * D * N * 4
     assert lib.selective_scan_pack_workspace_bytes(0, D, N) == 0
     assert lib.conv1d_pack_bwd_workspace_bytes(T, D, 4) >= 5 * D * 4
     assert lib.conv1d_pack_bwd_workspace_bytes(0, D, 4) == 0
+    # the conv backward with contexts adds one correction row set per sequence
+    assert (lib.conv1d_pack_bwd_states_workspace_bytes(T, D, 4, 34)
+            == lib.conv1d_pack_bwd_workspace_bytes(T, D, 4) + 34 * 5 * D * 4)
 
 
 NULL = None
@@ -97,3 +100,34 @@ def test_host_validation(lib):
     # dD must be given exactly when Dskip is
     b2 = [fake] * 5 + [NULL] + [fake] * 3 + [fake, 1 << 30] + [fake] * 7
     assert lib.selective_scan_pack_bwd(*b2, 8, 4, 16, 1, NULL) == 1
+
+
+def test_host_validation_states(lib):
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+    # scan forward with states: a state pointer needs cu_seqlens and nseq >= 1
+    f = [fake] * 9 + [fake, 1 << 30, 8, 4, 16, 1, NULL, 0, ctypes.c_float(0.0)]
+    assert lib.selective_scan_pack_fwd_states(*f, NULL, 2, fake, NULL, NULL) == 1
+    assert lib.selective_scan_pack_fwd_states(*f, NULL, 2, NULL, fake, NULL) == 1
+    assert lib.selective_scan_pack_fwd_states(*f, fake, 0, fake, NULL, NULL) == 2
+    # ... and the usual checks still come first
+    f_bad_n = [fake] * 9 + [fake, 1 << 30, 8, 4, 3, 1, NULL, 0, ctypes.c_float(0.0)]
+    assert lib.selective_scan_pack_fwd_states(*f_bad_n, fake, 2, fake, fake, NULL) == 4
+    # scan backward with states
+    b = [fake] * 9 + [fake, 1 << 30] + [fake] * 7 + [8, 4, 16, 1, NULL, 0, ctypes.c_float(0.0), NULL]
+    assert lib.selective_scan_pack_bwd_states(*b, NULL, 2, fake, NULL, NULL, NULL) == 1
+    assert lib.selective_scan_pack_bwd_states(*b, NULL, 2, NULL, NULL, fake, NULL) == 1
+    assert lib.selective_scan_pack_bwd_states(*b, fake, 0, NULL, fake, NULL, NULL) == 2
+    # the step-bias gradient must be given exactly when the step bias is
+    b_bias = [fake] * 9 + [fake, 1 << 30] + [fake] * 7 + [8, 4, 16, 1, fake, 0, ctypes.c_float(0.0), NULL]
+    assert lib.selective_scan_pack_bwd_states(*b_bias, fake, 2, fake, NULL, NULL, NULL) == 1
+    # conv forward with contexts
+    c = [fake, fake, NULL, fake, fake, 8, 4, 4, 1, 1]
+    assert lib.conv1d_pack_fwd_states(*c, NULL, 2, fake, NULL, NULL) == 1
+    assert lib.conv1d_pack_fwd_states(*c, fake, 0, NULL, fake, NULL) == 2
+    assert lib.conv1d_pack_fwd_states(fake, fake, NULL, fake, fake, 8, 4, 5, 1, 1, fake, 2, fake, NULL, NULL) == 4
+    # conv backward with contexts: cu_seqlens, nseq, and the larger workspace
+    cb = [fake, fake, NULL, fake, fake, fake, fake, NULL]
+    assert lib.conv1d_pack_bwd_states(*cb, fake, 1 << 30, 8, 4, 4, 1, 1, NULL, 2, fake, NULL, NULL, NULL) == 1
+    assert lib.conv1d_pack_bwd_states(*cb, fake, 1 << 30, 8, 4, 4, 1, 1, fake, 0, fake, NULL, NULL, NULL) == 2
+    small = lib.conv1d_pack_bwd_workspace_bytes(8, 4, 4)  # enough without contexts, too small with them
+    assert lib.conv1d_pack_bwd_states(*cb, fake, small, 8, 4, 4, 1, 1, fake, 2, fake, NULL, NULL, NULL) == 6
