@@ -600,3 +600,36 @@ def test_pipeline_cut_across_packs(orc):
     _, out_o, _ = orc.scan_fwd_state(u_o, f64(pb.delta), f64(pb.A), f64(pb.B), f64(pb.C), f64(pb.Dp), f64(pb.z),
                                      pb.cu_seqlens, h0=npy(h0_b), threads=8)
     assert_close(npy(gb["out"]), out_o, to, "out (oracle)")
+
+
+def test_states_empty_pack():
+    """No tokens at all (every sequence empty): final states are the initial
+    ones and the initial-state gradients are the final-state ones, for the
+    SSM state and the conv context; the parameter sums are zero."""
+    ss = ssp()
+    nseq, D, N, W = 3, 64, 16, 4
+    cu = torch.zeros(nseq + 1, dtype=torch.int32, device="cuda")
+    g = torch.Generator().manual_seed(9)
+    h0 = torch.randn(nseq, D, N, generator=g).cuda()
+    dhT = torch.randn(nseq, D, N, generator=g).cuda()
+    ci = torch.randn(nseq, W - 1, D, generator=g).to(torch.bfloat16).cuda()
+    dcf = torch.randn(nseq, W - 1, D, generator=g).to(torch.bfloat16).cuda()
+    e2 = lambda *s: torch.empty(*s, dtype=torch.bfloat16, device="cuda")
+    x, z, delta = e2(0, D), e2(0, D), e2(0, D)
+    B, C = e2(0, N), e2(0, N)
+    A = -torch.ones(D, N, device="cuda")
+    Dp = torch.ones(D, device="cuda")
+    w = torch.ones(D, W, device="cuda")
+    b = torch.zeros(D, device="cuda")
+    pos = torch.empty(0, dtype=torch.int32, device="cuda")
+    u, cf = ss.conv1d_pack_fwd(x, w, b, pos, cu_seqlens=cu, conv_initial=ci, conv_final=True)
+    out, ws, hT = ss.selective_scan_pack_fwd(u, delta, A, B, C, Dp, z, pos, cu_seqlens=cu, initial_state=h0,
+                                             final_state=True)
+    gr = ss.selective_scan_pack_bwd(u, delta, A, B, C, Dp, z, pos, e2(0, D), ws, cu_seqlens=cu, initial_state=h0,
+                                    dfinal_state=dhT, dinitial_state=True)
+    dx, dw, db, dci = ss.conv1d_pack_bwd(x, w, b, pos, gr["du"], cu_seqlens=cu, conv_initial=ci, dconv_final=dcf,
+                                         dconv_initial=True)
+    torch.cuda.synchronize()
+    assert torch.equal(hT, h0) and torch.equal(cf, ci)
+    assert torch.equal(gr["dinitial_state"], dhT) and torch.equal(dci, dcf)
+    assert not gr["dA"].any() and not gr["dD"].any() and not dw.any() and not db.any()
