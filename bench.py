@@ -47,8 +47,8 @@ SCAN_BWD_FLOPS_PER_TDN = 22
 # Valid only for the kernel sources they were taken on (sha256 below); any
 # change to those sources reports null until the counters are taken again.
 MEASURED_TRAFFIC = {
-    "scan_bwd": {"bytes": 5326288541, "sources": ["scan_bwd.hip", "scan_common.h", "common.h"],
-                 "sha256": "2f6ede5b1b16ed21004a1c86242ebd00827d1057c1358bda14ed39e4c5249f66"},
+    "scan_bwd": {"bytes": 5326015045, "sources": ["scan_bwd.hip", "scan_common.h", "common.h"],
+                 "sha256": "9b1f8e8835bf5f93e5e48505d4462a2d7d319beaa4b095a781b50201a0144562"},
 }
 
 
@@ -178,6 +178,9 @@ def time_steps(wl: Workload, steps: int, warmup: int, per_op: bool = True):
         ops = {}
         for j, name in enumerate(OPS):
             ops[name] = float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
+        # per-step times of the two passes (forward: indices, conv, scan; backward: scan, conv)
+        wl.pass_ms = {"fwd": [evs[i][0].elapsed_time(evs[i][3]) for i in range(steps)],
+                      "bwd": [evs[i][3].elapsed_time(evs[i][5]) for i in range(steps)]}
     return total_ms, ops
 
 
@@ -306,21 +309,50 @@ def per_sequence_loop(wl: Workload, steps: int, warmup: int) -> float:
 
 def cpu_baseline(inp: synth.Inputs, channels: int, threads: int) -> dict:
     """The fp64 oracle (as it stands) on a bounded sample: every token of the
-    workload, a subset of its channels; tokens/s scaled to all channels."""
+    workload, a subset of its channels; tokens/s scaled to all channels. A
+    one-core figure on a sixteenth of those channels goes beside it."""
     import oracle
     orc = oracle.get()
-    sl = slice(0, channels)
     f = synth.f64
-    x, w, b = f(inp.x)[:, sl], f(inp.w)[sl], f(inp.b)[sl]
-    delta, A, Dp, z, dout = f(inp.delta)[:, sl], f(inp.A)[sl], f(inp.Dp)[sl], f(inp.z)[:, sl], f(inp.dout)[:, sl]
-    B, C = f(inp.B), f(inp.C)
-    t = time.perf_counter()
-    orc.forward(x, w, b, delta, A, B, C, Dp, z, inp.cu_seqlens, threads=threads)
-    orc.backward(x, w, b, delta, A, B, C, Dp, z, inp.cu_seqlens, dout, threads=threads)
-    sec = time.perf_counter() - t
+
+    def run(nch, nthreads):
+        sl = slice(0, nch)
+        x, w, b = f(inp.x)[:, sl], f(inp.w)[sl], f(inp.b)[sl]
+        delta, A, Dp = f(inp.delta)[:, sl], f(inp.A)[sl], f(inp.Dp)[sl]
+        z, dout = f(inp.z)[:, sl], f(inp.dout)[:, sl]
+        B, C = f(inp.B), f(inp.C)
+        t = time.perf_counter()
+        orc.forward(x, w, b, delta, A, B, C, Dp, z, inp.cu_seqlens, threads=nthreads)
+        orc.backward(x, w, b, delta, A, B, C, Dp, z, inp.cu_seqlens, dout, threads=nthreads)
+        return time.perf_counter() - t
+
+    sec = run(channels, threads)
+    ch1 = max(1, channels // 16)
+    sec1 = run(ch1, 1)
     return {"value": inp.T * (channels / inp.D) / sec, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"fwd+bwd of all {inp.T} tokens of the workload on {channels} of {inp.D} channels "
-                      f"({sec:.1f} s wall on {threads} threads), scaled by {inp.D}/{channels}"}
+                      f"({sec:.1f} s wall on {threads} threads), scaled by {inp.D}/{channels}",
+            "one_core": {"value": inp.T * (ch1 / inp.D) / sec1, "unit": "tokens/s", "cores": 1,
+                         "sample": f"all {inp.T} tokens on {ch1} channels ({sec1:.1f} s), scaled by "
+                                   f"{inp.D}/{ch1}"}}
+
+
+def copy_ceiling(nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """GB/s (read + write) of a plain device-to-device copy of nbytes, the
+    practical HBM ceiling beside the 8 TB/s vendor peak."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
 def main():
@@ -351,6 +383,9 @@ def main():
     wl = Workload(inp)
     log(f"[bench] T={T} D={D} N={N} nseq={inp.nseq}; warmup {args.warmup}, timing {args.steps} steps")
     total_ms, ops = time_steps(wl, args.steps, args.warmup, per_op=True)
+    pct = lambda v: {"median": round(float(np.median(v)), 4), "p10": round(float(np.percentile(v, 10)), 4),
+                     "p90": round(float(np.percentile(v, 90)), 4)}
+    passes = {k: pct(v) for k, v in wl.pass_ms.items()}
     # a second timed pass without per-op events (the headline number)
     total_ms, _ = time_steps(wl, args.steps, 1, per_op=False)
     ms_step = total_ms / args.steps
@@ -376,6 +411,12 @@ def main():
                     "traffic": None, "avg_ms": round(ops[dominant], 4), "algo_bytes_per_launch": ab[dominant]}
     log("[bench] per-op ms: " + ", ".join(f"{k} {ops[k]:.3f}" for k in OPS))
     log("[bench] per-op algorithmic GB/s: " + ", ".join(f"{k} {ops_gbs[k]:.0f}" for k in OPS))
+
+    # (counter runs take the copy calibration below instead: it must be the
+    # run's only device copy)
+    copy_gbs = None if args.copy_calib else copy_ceiling()
+    if copy_gbs:
+        log(f"[bench] device copy ceiling {copy_gbs:.0f} GB/s (read + write)")
 
     if args.copy_calib:
         # src is written, then a second buffer of the same size pushes it out of
@@ -413,6 +454,8 @@ def main():
         del wp, pinp
         ms_s = per_sequence_loop(wl, max(2, args.steps // 5), 1)
         layouts["per_sequence_loop"] = round(T / (ms_s * 1e-3), 1)
+        layouts["packed_over_per_sequence"] = round(tok_s * ms_s * 1e-3 / T, 3)
+        layouts["packed_over_concat"] = round(tok_s / layouts["concat_no_reset"], 3)
         # whole documents packed by the host packer, padding run as tokens;
         # the rate counts document tokens only
         for name, strategy in (("planned_sequential", 0), ("planned_greedy", 1)):
@@ -449,7 +492,9 @@ def main():
         "config": {"workload": synth.NAMES[wl_id], "d_inner": D, "d_state": N, "conv_width": inp.W,
                    "packs": spec.n_packs, "pack_len": spec.pack_len, "tokens": T, "sequences": inp.nseq,
                    "state_dtype": "fp32"},
+        "passes_ms": passes,
         "hbm_gbs": round(hbm_gbs, 1),
+        "hbm_copy_ceiling_gbs": None if copy_gbs is None else round(copy_gbs, 1),
         "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "ops_ms": {k: round(v, 4) for k, v in ops.items()},
         "ops_algo_gbs": {k: round(v, 1) for k, v in ops_gbs.items()},
