@@ -5,7 +5,7 @@
 // figure (a): pack() emits each token's position inside its own sequence.
 // One thread per token finds its sequence by binary search over cu_seqlens
 // (a few hundred bytes, L1/L2 resident); a single extra workgroup validates
-// cu_seqlens and writes the verdict, so no memory needs clearing beforehand.
+// cu_seqlens and writes its status word, so no memory needs clearing beforehand.
 #include "common.h"
 
 namespace ssmp {

@@ -24,7 +24,7 @@ def declared_functions():
 def lib():
     from selective_state_space_varlen_amd import binding
     if not os.path.exists(binding.LIB_PATH):
-        pytest.fail("libssmpack.so is not built (run __graft_entry__.build())")
+        pytest.fail("libssmpack.so is not built (python -m selective_state_space_varlen_amd.build)")
     return binding.load()
 
 
