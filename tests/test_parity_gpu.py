@@ -633,3 +633,32 @@ def test_states_empty_pack():
     assert torch.equal(hT, h0) and torch.equal(cf, ci)
     assert torch.equal(gr["dinitial_state"], dhT) and torch.equal(dci, dcf)
     assert not gr["dA"].any() and not gr["dD"].any() and not dw.any() and not db.any()
+
+
+def test_empty_input_plain_entry_points():
+    """T = 0 through the reset-only entry points: nothing to launch for the
+    per-token outputs, and the parameter sums (dw, db, dA, dD) are written as
+    zeros (their buffers start as NaN)."""
+    ss = ssp()
+    D, N, W = 96, 16, 4
+    e2 = lambda *s: torch.empty(*s, dtype=torch.bfloat16, device="cuda")
+    nan = lambda *s: torch.full(s, float("nan"), dtype=torch.float32, device="cuda")
+    x, z, delta, dout = e2(0, D), e2(0, D), e2(0, D), e2(0, D)
+    B, C = e2(0, N), e2(0, N)
+    A = -torch.ones(D, N, device="cuda")
+    Dp = torch.ones(D, device="cuda")
+    w = torch.ones(D, W, device="cuda")
+    b = torch.zeros(D, device="cuda")
+    cu = torch.zeros(2, dtype=torch.int32, device="cuda")
+    pos, _, err = ss.varlen_pack_indices(cu, 0)
+    u = ss.conv1d_pack_fwd(x, w, b, pos)
+    out, ws = ss.selective_scan_pack_fwd(u, delta, A, B, C, Dp, z, pos)
+    g = {"du": e2(0, D), "ddelta": e2(0, D), "dz": e2(0, D), "dA": nan(D, N), "dB": nan(0, N), "dC": nan(0, N),
+         "dD": nan(D)}
+    ss.selective_scan_pack_bwd(u, delta, A, B, C, Dp, z, pos, dout, ws, out=g)
+    dw, db = nan(D, W), nan(D)
+    ss.conv1d_pack_bwd(x, w, b, pos, g["du"], out=(e2(0, D), dw, db))
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0 and out.shape == (0, D)
+    for name, t in (("dA", g["dA"]), ("dD", g["dD"]), ("dw", dw), ("db", db)):
+        assert torch.equal(t, torch.zeros_like(t)), name
