@@ -48,7 +48,7 @@ SCAN_BWD_FLOPS_PER_TDN = 22
 # change to those sources reports null until the counters are taken again.
 MEASURED_TRAFFIC = {
     "scan_bwd": {"bytes": 5326015045, "sources": ["scan_bwd.hip", "scan_common.h", "common.h"],
-                 "sha256": "9b1f8e8835bf5f93e5e48505d4462a2d7d319beaa4b095a781b50201a0144562"},
+                 "sha256": "3a760c5d19c527fa6c9b13c1109fba2fa5ffe56fc31da37e704ef4137cf16739"},
 }
 
 

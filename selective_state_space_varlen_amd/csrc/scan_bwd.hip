@@ -11,8 +11,10 @@
 //   ddelta_t = u_t sum_n dh_t B_t[n] + sum_n [not head] A r_t,  r_t = dh_t a_t h_{t-1}
 //   dA    += [not head] delta_t r_t                      dDskip += g_t u_t
 //   dz_t   = dout_t y_t s (1 + z_t (1 - s)),  s = sigmoid(z_t)
-// r_t is formed as dh_t (h_t - delta_t u_t B_t[n]) = dh_t h_t - dB_t-term B_t[n],
-// so only the state after each token is needed.
+// r_t is formed as c_t h_{t-1}: the carry a_t dh_t the step computes anyway,
+// times the previous token's replayed state (the sub-chunk's entering state
+// for its first token). With carried sequence states, h_{-1} of a head is its
+// sequence's initial state and c_t there is that state's gradient.
 //
 // Time parallelism mirrors the forward, in reverse: a chunk's carry out of
 // its first token is c_out = P' c_in + S' with

@@ -10,8 +10,8 @@
 // Mapping: one lane per channel, the d_state values in VGPRs, one wave per
 // (chunk of lc tokens, 64 channels). B_t and C_t are the same for the whole
 // wave: an fp32 copy made first arrives through scalar loads. Per-lane inputs
-// are staged through LDS in kCK-token blocks, the next block in flight while
-// the current one is computed. The time axis is joined across chunks by the
+// are staged through LDS in kFwdBlock-token blocks, the next block in flight
+// while the current one is computed. The time axis is joined across chunks by the
 // article's reset rule applied to the affine carry (h_out = P h_in + S, with
 // the multiplier P zeroed once a head is passed):
 //   1. summary: per chunk, from its last head (or its start) to its end,
@@ -23,6 +23,9 @@
 //      entering each chunk.
 //   3. output: each chunk replays its tokens from that state, writes out and
 //      stores the state entering every kCK-th token for the backward.
+// The step map and gate floor (ScanOpts) apply where delta and z are read;
+// carried sequence states enter at heads and leave at ends, in the blocks
+// that already take the slow path for heads.
 #include "scan_common.h"
 
 namespace ssmp {
