@@ -662,3 +662,54 @@ def test_empty_input_plain_entry_points():
     assert int(err.item()) == 0 and out.shape == (0, D)
     for name, t in (("dA", g["dA"]), ("dD", g["dD"]), ("dw", dw), ("db", db)):
         assert torch.equal(t, torch.zeros_like(t)), name
+
+
+# numerical regimes at the edges of the recurrence: no decay (A = 0, the
+# state is a running sum), decays that underflow to zero, steps so small the
+# state keeps thousands of tokens of memory, and softplus far into its tails
+REGIMES = {
+    "no-decay-fp32": dict(dtype=torch.float32, A=0.0, delta=(0.01, 0.1)),
+    "underflowing-decay-fp32": dict(dtype=torch.float32, A=-16.0, delta=(8.0, 12.0)),
+    "long-memory-bf16": dict(dtype=torch.bfloat16, A=-1.0, delta=(1e-4, 5e-4)),
+    "softplus-tails-bf16": dict(dtype=torch.bfloat16, A=-1.0, raw=(-40.0, 40.0)),
+    "mixed-sign-A-fp32": dict(dtype=torch.float32, A="mixed", delta=(0.001, 0.01)),
+}
+
+
+@pytest.mark.parametrize("name", list(REGIMES))
+def test_scan_numerical_regimes(orc, name):
+    spec = REGIMES[name]
+    inp = synth.make_inputs(2, lengths=[3000, 17, 1, 500], D=64, dtype=spec["dtype"], with_u=True,
+                            with_dout=True)
+    rng = np.random.default_rng(11)
+    T, D, N = inp.T, inp.D, inp.N
+    if spec["A"] == "mixed":
+        # small positive A too: a growing state over a short memory
+        A = rng.uniform(-2.0, 0.5, (D, N)).astype(np.float32)
+    else:
+        A = np.full((D, N), spec["A"], dtype=np.float32)
+    inp.A = torch.from_numpy(A)
+    kw, okw = {}, {}
+    if "raw" in spec:
+        lo, hi = spec["raw"]
+        raw = rng.uniform(lo, hi, (T, D))
+        inp.delta = synth.to_dtype(raw, inp.dtype)
+        kw = dict(delta_softplus=True)
+        okw = dict(delta_softplus=True)
+    else:
+        lo, hi = spec["delta"]
+        inp.delta = synth.to_dtype(rng.uniform(lo, hi, (T, D)), inp.dtype)
+    d = Dev(inp)
+    out, ws = ssp().selective_scan_pack_fwd(d.u, d.delta, d.A, d.B, d.C, d.Dp, d.z, d.pos, **kw)
+    g = ssp().selective_scan_pack_bwd(d.u, d.delta, d.A, d.B, d.C, d.Dp, d.z, d.pos, d.dout, ws, **kw)
+    torch.cuda.synchronize()
+    pos, _ = orc.pack_indices(inp.cu_seqlens, inp.T)
+    args = (synth.f64(inp.u), synth.f64(inp.delta), synth.f64(inp.A), synth.f64(inp.B), synth.f64(inp.C),
+            synth.f64(inp.Dp), synth.f64(inp.z), pos)
+    _, rout = orc.scan_fwd(*args, threads=8, **okw)
+    rg = orc.scan_bwd(*args, synth.f64(inp.dout), threads=8, **okw)
+    to, tg = TOL_OUT[inp.dtype], TOL_GRAD[inp.dtype]
+    assert np.all(np.isfinite(npy(out)))
+    assert_close(npy(out), rout, to, "out")
+    for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz"):
+        assert_close(npy(g[k]), rg[k], tg, k)
