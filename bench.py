@@ -85,7 +85,7 @@ def log(msg: str) -> None:
 class Workload:
     """Device-resident inputs, outputs and workspaces of one packed batch."""
 
-    def __init__(self, inp: synth.Inputs, cu=None, dev="cuda:0", states: bool = False):
+    def __init__(self, inp: synth.Inputs, cu=None, dev="cuda:0", states: bool = False, ext: bool = False):
         import selective_state_space_varlen_amd as ssp
         self.ssp = ssp
         self.inp = inp
@@ -107,6 +107,14 @@ class Workload:
         self.dx = e(T, D)
         self.dw = e(D, W, dt=torch.float32)
         self.db = e(D, dt=torch.float32)
+        # the step map softplus(delta + bias) and the gate floor, fused into
+        # the scan (delta then holds the step before the map)
+        self.ext = {}
+        if ext:
+            g = torch.Generator(device="cpu").manual_seed(6)
+            self.ext = dict(delta_bias=(torch.randn(D, generator=g) * 0.1).to(d), delta_softplus=True,
+                            gate_floor=0.05)
+            self.g["ddelta_bias"] = e(D, dt=torch.float32)
         # every sequence starts from a given conv context and SSM state and
         # hands on its own (the layout of sequences cut across packs)
         self.states = states
@@ -131,10 +139,10 @@ class Workload:
         s.conv1d_pack_fwd(self.x, self.w, self.b, self.pos, silu=True, out=self.u)
         rec(2)
         s.selective_scan_pack_fwd(self.u, self.delta, self.A, self.B, self.C, self.Dp, self.z, self.pos,
-                                  workspace=self.scan_ws, out=self.out)
+                                  workspace=self.scan_ws, out=self.out, **self.ext)
         rec(3)
         s.selective_scan_pack_bwd(self.u, self.delta, self.A, self.B, self.C, self.Dp, self.z, self.pos, self.dout,
-                                  self.scan_ws, out=self.g)
+                                  self.scan_ws, out=self.g, **self.ext)
         rec(4)
         s.conv1d_pack_bwd(self.x, self.w, self.b, self.pos, self.g["du"], silu=True, workspace=self.conv_ws,
                           out=(self.dx, self.dw, self.db))
@@ -148,10 +156,10 @@ class Workload:
                           conv_initial=st["ci"], conv_final=st["cf"])
         s.selective_scan_pack_fwd(self.u, self.delta, self.A, self.B, self.C, self.Dp, self.z, self.pos,
                                   workspace=self.scan_ws, out=self.out, cu_seqlens=cu, initial_state=st["h0"],
-                                  final_state=st["hT"])
+                                  final_state=st["hT"], **self.ext)
         s.selective_scan_pack_bwd(self.u, self.delta, self.A, self.B, self.C, self.Dp, self.z, self.pos, self.dout,
                                   self.scan_ws, out=self.g, cu_seqlens=cu, initial_state=st["h0"],
-                                  dfinal_state=st["dhT"], dinitial_state=st["dh0"])
+                                  dfinal_state=st["dhT"], dinitial_state=st["dh0"], **self.ext)
         s.conv1d_pack_bwd(self.x, self.w, self.b, self.pos, self.g["du"], silu=True, workspace=self.conv_ws,
                           out=(self.dx, self.dw, self.db), cu_seqlens=cu, conv_initial=st["ci"],
                           dconv_final=st["dcf"], dconv_initial=st["dci"])
@@ -441,6 +449,12 @@ def main():
         ms_x, _ = time_steps(wsx, nq, 2, per_op=False)
         layouts["packed_carry_states"] = round(T / (ms_x / nq * 1e-3), 1)
         del wsx
+        # the same pack with the step map softplus(delta + bias) and the gate
+        # floor computed inside the scan (the _ex entry points)
+        wex = Workload(inp, ext=True)
+        ms_e, _ = time_steps(wex, nq, 2, per_op=False)
+        layouts["packed_step_map_gate_floor"] = round(T / (ms_e / nq * 1e-3), 1)
+        del wex
         cu_concat = np.arange(0, T + 1, spec.pack_len, dtype=np.int32)
         wc = Workload(inp, cu=cu_concat)
         ms_c, _ = time_steps(wc, max(3, args.steps // 2), 2, per_op=False)

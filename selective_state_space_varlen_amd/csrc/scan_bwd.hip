@@ -282,17 +282,39 @@ template <bool SAFE, bool XS, bool ST, int NS, int LPC, typename St, typename T>
 __device__ __forceinline__ void bwd_replay(const T* lds, const float* bcl, int kb, int ns, uint32_t heads, int ch,
                                            int n0, const float (&A2)[NS / LPC], float (&h)[NS / LPC],
                                            float (&hh)[kK][NS / LPC], float (&ak)[kK][NS / LPC], float (&yk)[kK],
-                                           float Dv, const StepMap& sm, const ScanOpts& opt, int64_t tb, int D,
-                                           int dd) {
+                                           float (&dtk)[kK], float (&slk)[kK], float Dv, const StepMap& sm,
+                                           const ScanOpts& opt, int64_t tb, int D, int dd) {
     // on return h holds the state after the last replayed token
     constexpr int NH = NS / LPC;
+    if constexpr (XS) {
+        // mapped steps and their slopes for the whole sub-chunk (past ns the
+        // staged rows are stale and the results unused). A lane pair shares
+        // its channel: each lane maps every other token and the pair swaps.
+        if constexpr (LPC == 2) {
+            static_assert(kK % 2 == 0, "tokens come in pairs");
+            const bool odd = n0 != 0;
+#pragma unroll
+            for (int j = 0; j < kK / 2; ++j) {
+                float sl_own;
+                const float dt_own = sm.eff(St::get(lds, 1, kb + 2 * j + (odd ? 1 : 0), ch), sl_own);
+                const float dt_oth = swap_adjacent(dt_own), sl_oth = swap_adjacent(sl_own);
+                dtk[2 * j] = odd ? dt_oth : dt_own;
+                dtk[2 * j + 1] = odd ? dt_own : dt_oth;
+                slk[2 * j] = odd ? sl_oth : sl_own;
+                slk[2 * j + 1] = odd ? sl_own : sl_oth;
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < kK; ++kk) dtk[kk] = sm.eff(St::get(lds, 1, kb + kk, ch), slk[kk]);
+        }
+    }
 #pragma unroll
     for (int kk = 0; kk < kK; ++kk) {
         if constexpr (SAFE) {
             if (kk >= ns) break;
         }
         const int k = kb + kk;
-        const float dt = XS ? sm.eff(St::get(lds, 1, k, ch)) : St::get(lds, 1, k, ch);
+        const float dt = XS ? dtk[kk] : St::get(lds, 1, k, ch);
         const float uu = St::get(lds, 0, k, ch);
         const float dtu = dt * uu;
         const float* row = bcl + k * 2 * NS + n0;
@@ -342,8 +364,9 @@ __device__ __forceinline__ void bwd_reverse(const T* lds, const float* bcl, floa
                                             float (&dA)[NS / LPC], float& dDacc, float Dv,
                                             const float (&hin)[NS / LPC], const float (&hh)[kK][NS / LPC],
                                             const float (&ak)[kK][NS / LPC],
-                                            const float (&yk)[kK], const BwdRows<T>& rows, const StepMap& sm,
-                                            float gf, float& dbacc, const ScanOpts& opt, int64_t tb, int dd) {
+                                            const float (&yk)[kK], const float (&dtk)[kK], const float (&slk)[kK],
+                                            const BwdRows<T>& rows, float gf, float& dbacc, const ScanOpts& opt,
+                                            int64_t tb, int dd) {
     constexpr int NH = NS / LPC;
     constexpr int CW = kWave / LPC;
 #pragma unroll
@@ -352,8 +375,7 @@ __device__ __forceinline__ void bwd_reverse(const T* lds, const float* bcl, floa
             if (kk >= ns) continue;
         }
         const int k = kb + kk;
-        const float draw = St::get(lds, 1, k, ch);
-        const float dt = XS ? sm.eff(draw) : draw;
+        const float dt = XS ? dtk[kk] : St::get(lds, 1, k, ch);
         const float uu = St::get(lds, 0, k, ch);
         const float go = St::get(lds, 3, k, ch);
         float gg = go, dzv = 0.0f;
@@ -420,7 +442,7 @@ __device__ __forceinline__ void bwd_reverse(const T* lds, const float* bcl, floa
         const float duv = __builtin_fmaf(gg, Dv, dt * sumB);
         float ddv = __builtin_fmaf(uu, sumB, sumAr * kLn2);
         if constexpr (XS) {
-            ddv *= sm.slope(draw);  // with respect to the stored step
+            ddv *= slk[kk];  // with respect to the stored step
             dbacc += act ? ddv : 0.0f;
         }
         dDacc = __builtin_fmaf(gg, uu, dDacc);
@@ -575,7 +597,7 @@ __global__ __launch_bounds__(kWave * WV, 2) void k_scan_bwd_main(BwdArgs<T> p) {
         for (int sc = nsub - 1; sc >= 0; --sc) {
             const int kb = sc * kK;  // first token of the sub-chunk within the block
             const int ns = (nb - kb < kK) ? nb - kb : kK;
-            float h[NH], hin[NH], hh[kK][NH], ak[kK][NH], yk[kK];
+            float h[NH], hin[NH], hh[kK][NH], ak[kK][NH], yk[kK], dtk[kK], slk[kK];
 #pragma unroll
             for (int i = 0; i < NH; ++i) {
                 h[i] = hn[i];
@@ -584,17 +606,17 @@ __global__ __launch_bounds__(kWave * WV, 2) void k_scan_bwd_main(BwdArgs<T> p) {
             if (tb0 + kb - kK >= t0) load_state(tb0 + kb - kK, hn);
             const uint32_t sub_heads = (heads >> kb) & ((1u << kK) - 1u);
             if (sub_heads == 0 && ns == kK) {
-                bwd_replay<false, XS, ST, NS, LPC, St>(mylds, bcl, kb, kK, 0u, ch, n0, A2, h, hh, ak, yk, Dv, sm, p.opt, tb0,
-                                                   D, dd);
+                bwd_replay<false, XS, ST, NS, LPC, St>(mylds, bcl, kb, kK, 0u, ch, n0, A2, h, hh, ak, yk, dtk, slk, Dv,
+                                                       sm, p.opt, tb0, D, dd);
                 bwd_reverse<false, GATE, XS, ST, NS, LPC, St>(mylds, bcl, red[wv], kb, kK, 0u, lane, ch, sh, n0, act,
-                                                          full, D, d, A2, carry, dA, dDacc, Dv, hin, hh, ak, yk, rows,
-                                                          sm, gf, dbacc, p.opt, tb0, dd);
+                                                              full, D, d, A2, carry, dA, dDacc, Dv, hin, hh, ak, yk,
+                                                              dtk, slk, rows, gf, dbacc, p.opt, tb0, dd);
             } else {
-                bwd_replay<true, XS, ST, NS, LPC, St>(mylds, bcl, kb, ns, heads, ch, n0, A2, h, hh, ak, yk, Dv, sm, p.opt, tb0,
-                                                  D, dd);
+                bwd_replay<true, XS, ST, NS, LPC, St>(mylds, bcl, kb, ns, heads, ch, n0, A2, h, hh, ak, yk, dtk, slk, Dv,
+                                                      sm, p.opt, tb0, D, dd);
                 bwd_reverse<true, GATE, XS, ST, NS, LPC, St>(mylds, bcl, red[wv], kb, ns, heads, lane, ch, sh, n0, act,
-                                                         full, D, d, A2, carry, dA, dDacc, Dv, hin, hh, ak, yk, rows,
-                                                         sm, gf, dbacc, p.opt, tb0, dd);
+                                                             full, D, d, A2, carry, dA, dDacc, Dv, hin, hh, ak, yk,
+                                                             dtk, slk, rows, gf, dbacc, p.opt, tb0, dd);
             }
         }
 

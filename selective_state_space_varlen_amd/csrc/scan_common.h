@@ -140,13 +140,22 @@ __global__ __launch_bounds__(256) void k_empty_seq_states(const int32_t* __restr
     if (cu[s] == cu[s + 1]) dst[i] = src ? src[i] : 0.0f;
 }
 
-// softplus(v) = max(v, 0) + log1p(exp(-|v|)); log1p(e) as log(w) e / (w - 1)
-// with w = 1 + e (exact-ish when e is tiny, where w - 1 rounds).
+// softplus(v) = max(v, 0) + log1p(e) with e = exp(-|v|) in (0, 1]. With
+// w = 1 + e rounded and c = e - (w - 1) its rounding error, log1p(e) =
+// log(w) + c / w to first order; c alone instead of c / w is off by c e / w,
+// under one ulp of log1p(e) >= e ln 2 (when e is below w's ulp, w = 1 and
+// the sum is e exactly). One v_exp and one v_log, no division.
 __device__ __forceinline__ float softplus_f(float v) {
     const float e = exp2_fast(-__builtin_fabsf(v) * kLog2e);
     const float w = 1.0f + e;
-    const float lp = (w == 1.0f) ? e : __builtin_amdgcn_logf(w) * kLn2 * (e / (w - 1.0f));
-    return __builtin_fmaxf(v, 0.0f) + lp;
+    return __builtin_fmaxf(v, 0.0f) + __builtin_fmaf(__builtin_amdgcn_logf(w), kLn2, e - (w - 1.0f));
+}
+// The same value and its derivative sigmoid(v): 1/w for v >= 0, e/w below.
+__device__ __forceinline__ float softplus_f(float v, float& slope) {
+    const float e = exp2_fast(-__builtin_fabsf(v) * kLog2e);
+    const float w = 1.0f + e;
+    slope = (v >= 0.0f ? 1.0f : e) * __builtin_amdgcn_rcpf(w);
+    return __builtin_fmaxf(v, 0.0f) + __builtin_fmaf(__builtin_amdgcn_logf(w), kLn2, e - (w - 1.0f));
 }
 
 // The step map of one channel. Off (no bias, no softplus) it is the identity,
@@ -159,8 +168,14 @@ struct StepMap {
         const float v = raw + bias;
         return sp ? softplus_f(v) : v;
     }
-    // d eff / d raw
-    __device__ __forceinline__ float slope(float raw) const { return sp ? sigmoid_fast(raw + bias) : 1.0f; }
+    // the step and its derivative with respect to raw
+    __device__ __forceinline__ float eff(float raw, float& slope) const {
+        const float v = raw + bias;
+        float s = 1.0f;
+        const float m = sp ? softplus_f(v, s) : v;
+        slope = s;
+        return m;
+    }
 };
 __device__ __forceinline__ StepMap step_map(const ScanOpts& o, int d) {
     StepMap m;

@@ -131,3 +131,51 @@ def test_fullsize_carried_states(orc):
     assert_close(npy(G["db"][cht]), db, tg, "db")
     assert_close(npy(G["dinitial_states"]["ssm"][:, cht]), Rg["dh0"], tg, "dinitial ssm state")
     assert_close(npy(G["dinitial_states"]["conv"][:, :, cht]), dci, tg, "dinitial conv context")
+
+
+def test_fullsize_step_map_gate_floor(orc):
+    """The benchmark pack (workload 4) through the scan with the step map
+    softplus(delta + bias) and the gate floor computed inside it, the form the
+    benchmark's step-map layout times: every token of sampled channels, the
+    per-channel sums (dA, dD, d bias) of those channels, and dB/dC of sampled
+    whole sequences."""
+    import selective_state_space_varlen_amd as ssp
+    print("[fullsize] workload 4 with step map and gate floor", flush=True)
+    inp = synth.make_inputs(4, with_dout=True, with_u=True)
+    D = inp.D
+    rng = np.random.default_rng(78)
+    bias = (rng.standard_normal(D) * 0.1).astype(np.float32)
+    floor = 0.05
+    d = Dev(inp)
+    bias_d = torch.from_numpy(bias).cuda()
+    ext = dict(delta_bias=bias_d, delta_softplus=True, gate_floor=floor)
+    ws = torch.empty(ssp.selective_scan_pack_workspace_bytes(inp.T, D, inp.N), dtype=torch.uint8, device="cuda")
+    out, _ = ssp.selective_scan_pack_fwd(d.u, d.delta, d.A, d.B, d.C, d.Dp, d.z, d.pos, workspace=ws, **ext)
+    G = ssp.selective_scan_pack_bwd(d.u, d.delta, d.A, d.B, d.C, d.Dp, d.z, d.pos, d.dout, ws, **ext)
+    torch.cuda.synchronize()
+    to, tg = TOL_OUT[inp.dtype], TOL_GRAD[inp.dtype]
+
+    rpos, _ = orc.pack_indices(inp.cu_seqlens, inp.T)
+    ch = sampled_channels(D)
+    f = synth.f64
+    oext = dict(delta_softplus=True, gate_floor=floor)
+    sub = lambda a: f(a)[:, ch]
+    _, ref = orc.scan_fwd(sub(inp.u), sub(inp.delta), f(inp.A)[ch], f(inp.B), f(inp.C), f(inp.Dp)[ch], sub(inp.z),
+                          rpos, threads=16, delta_bias=bias[ch].astype(np.float64), **oext)
+    R = orc.scan_bwd(sub(inp.u), sub(inp.delta), f(inp.A)[ch], f(inp.B), f(inp.C), f(inp.Dp)[ch], sub(inp.z), rpos,
+                     sub(inp.dout), threads=16, delta_bias=bias[ch].astype(np.float64), **oext)
+    cht = torch.from_numpy(ch).cuda()
+    assert_close(npy(out[:, cht]), ref, to, "out")
+    for k in ("du", "ddelta", "dz"):
+        assert_close(npy(G[k][:, cht]), R[k], tg, k)
+    for k in ("dA", "dD", "ddelta_bias"):
+        assert_close(npy(G[k][cht]), R[k], tg, k)
+
+    for s in pick_sequences(inp.lengths):
+        lo, hi = int(inp.cu_seqlens[s]), int(inp.cu_seqlens[s + 1])
+        sl = slice(lo, hi)
+        pos = np.arange(hi - lo, dtype=np.int32)
+        Rs = orc.scan_bwd(f(inp.u)[sl], f(inp.delta)[sl], f(inp.A), f(inp.B)[sl], f(inp.C)[sl], f(inp.Dp),
+                          f(inp.z)[sl], pos, f(inp.dout)[sl], threads=16, delta_bias=bias.astype(np.float64), **oext)
+        assert_close(npy(G["dB"][lo:hi]), Rs["dB"], tg, f"dB seq {s} (len {hi - lo})")
+        assert_close(npy(G["dC"][lo:hi]), Rs["dC"], tg, f"dC seq {s} (len {hi - lo})")
