@@ -22,16 +22,26 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_
 template <typename T>
 struct Elt;
 
+// st_nt: a non-temporal store, for outputs that no kernel of the pass reads
+// again soon (they then do not push shared inputs out of the L2). Only where a
+// wave's stores cover whole 128-byte lines: partial lines stored this way
+// reach memory unmerged.
 template <>
 struct Elt<float> {
     static __device__ __forceinline__ float ld(const float* __restrict__ p, size_t i) { return p[i]; }
     static __device__ __forceinline__ void st(float* __restrict__ p, size_t i, float v) { p[i] = v; }
+    static __device__ __forceinline__ void st_nt(float* __restrict__ p, size_t i, float v) {
+        __builtin_nontemporal_store(v, p + i);
+    }
 };
 
 template <>
 struct Elt<uint16_t> {
     static __device__ __forceinline__ float ld(const uint16_t* __restrict__ p, size_t i) { return bf16_to_f32(p[i]); }
     static __device__ __forceinline__ void st(uint16_t* __restrict__ p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+    static __device__ __forceinline__ void st_nt(uint16_t* __restrict__ p, size_t i, float v) {
+        __builtin_nontemporal_store(f32_to_bf16(v), p + i);
+    }
 };
 
 // One row of NS values of a (T, N) tensor at a wave-uniform address. bf16

@@ -612,8 +612,8 @@ __global__ __launch_bounds__(kWave * WV, 2) void k_scan_bwd_main(BwdArgs<T> p) {
                                                               full, D, d, A2, carry, dA, dDacc, Dv, hin, hh, ak, yk,
                                                               dtk, slk, rows, gf, dbacc, p.opt, tb0, dd);
             } else {
-                bwd_replay<true, XS, ST, NS, LPC, St>(mylds, bcl, kb, ns, heads, ch, n0, A2, h, hh, ak, yk, dtk, slk, Dv,
-                                                      sm, p.opt, tb0, D, dd);
+                bwd_replay<true, XS, ST, NS, LPC, St>(mylds, bcl, kb, ns, heads, ch, n0, A2, h, hh, ak, yk, dtk, slk,
+                                                      Dv, sm, p.opt, tb0, D, dd);
                 bwd_reverse<true, GATE, XS, ST, NS, LPC, St>(mylds, bcl, red[wv], kb, ns, heads, lane, ch, sh, n0, act,
                                                              full, D, d, A2, carry, dA, dDacc, Dv, hin, hh, ak, yk,
                                                              dtk, slk, rows, gf, dbacc, p.opt, tb0, dd);

@@ -78,7 +78,10 @@ struct ScanOpts {
 // A checkpoint slot holds the states of every channel in groups of four
 // ([n/4][d][4] for d_state a multiple of 4, else [n][d]): a wave's 16-byte
 // stores of one group cover 1 KiB of contiguous memory, and a lane loads its
-// states 16 bytes at a time.
+// states 16 bytes at a time. Checkpoints are written once by the forward and
+// read once by the backward, so both go through non-temporal accesses and
+// leave the L2 to the inputs the other waves of the chunk share.
+typedef float nf4 __attribute__((ext_vector_type(4)));
 template <int NS>
 __device__ __forceinline__ size_t ck_index(int d, int n, int D) {
     if constexpr (NS % 4 == 0) return (((size_t)(n >> 2) * D + d) << 2) + (n & 3);
@@ -89,8 +92,8 @@ __device__ __forceinline__ void ck_store(float* __restrict__ slot, int d, int D,
     if constexpr (NS % 4 == 0) {
 #pragma unroll
         for (int j = 0; j < NS / 4; ++j)
-            reinterpret_cast<float4*>(slot)[(size_t)j * D + d] =
-                make_float4(h[4 * j], h[4 * j + 1], h[4 * j + 2], h[4 * j + 3]);
+            __builtin_nontemporal_store(nf4{h[4 * j], h[4 * j + 1], h[4 * j + 2], h[4 * j + 3]},
+                                        reinterpret_cast<nf4*>(slot) + (size_t)j * D + d);
     } else {
 #pragma unroll
         for (int n = 0; n < NS; ++n) slot[(size_t)n * D + d] = h[n];
@@ -106,7 +109,8 @@ __device__ __forceinline__ void ck_load(const float* __restrict__ slot, int d, i
     } else if constexpr (NS % 4 == 0 && NH % 4 == 0) {
 #pragma unroll
         for (int j = 0; j < NH / 4; ++j) {
-            const float4 v = reinterpret_cast<const float4*>(slot)[(size_t)((n0 >> 2) + j) * D + d];
+            const nf4 v =
+                __builtin_nontemporal_load(reinterpret_cast<const nf4*>(slot) + (size_t)((n0 >> 2) + j) * D + d);
             h[4 * j] = v.x; h[4 * j + 1] = v.y; h[4 * j + 2] = v.z; h[4 * j + 3] = v.w;
         }
     } else {

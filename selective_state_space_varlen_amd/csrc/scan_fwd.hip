@@ -308,7 +308,7 @@ __device__ __forceinline__ void out_block(const T* lds, const float* __restrict_
             const float zz = zv[k];
             y *= __builtin_fmaf(zz, sigmoid_fast(zz), gf);
         }
-        if (store) Elt<T>::st(ob, (size_t)(k * D + d), y);
+        if (store) Elt<T>::st_nt(ob, (size_t)(k * D + d), y);
         if (more) {
 #pragma unroll
             for (int j = 0; j < 2 * NS; ++j) cur[j] = nxt[j];
@@ -321,12 +321,10 @@ __device__ __forceinline__ void out_block(const T* lds, const float* __restrict_
 // the softplus temporaries, would spill at that budget in the hot loop; both
 // run faster at up to 256 VGPRs (measured: 3 waves fit).
 template <typename T, int NS, bool GATE, bool XS, bool ST>
-__global__ __launch_bounds__(64, (ST || XS) ? 2 : 4) void k_scan_fwd_out(const T* __restrict__ u, const T* __restrict__ delta,
-                                                     const float* __restrict__ A, const float* __restrict__ bc,
-                                                     const float* __restrict__ Dskip, const T* __restrict__ z,
-                                                     const int32_t* __restrict__ pos, T* __restrict__ out,
-                                                     float* __restrict__ ckpt, int64_t T_, int D, int vec, int lc,
-                                                     ScanOpts opt) {
+__global__ __launch_bounds__(64, (ST || XS) ? 2 : 4) void k_scan_fwd_out(
+    const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A, const float* __restrict__ bc,
+    const float* __restrict__ Dskip, const T* __restrict__ z, const int32_t* __restrict__ pos, T* __restrict__ out,
+    float* __restrict__ ckpt, int64_t T_, int D, int vec, int lc, ScanOpts opt) {
     constexpr int BT = kFwdBlock;
     using St = Stager<T, 3, BT>;
     __shared__ __attribute__((aligned(16))) T lds[St::kElems];
