@@ -196,6 +196,13 @@ def _out_or_new(spec, shape, dtype, dev):
     return spec if isinstance(spec, torch.Tensor) else None
 
 
+def _nseq(cu_seqlens, dev) -> int:
+    if cu_seqlens is None:
+        raise ValueError("sequence states need cu_seqlens")
+    _check(cu_seqlens, "cu_seqlens", dtype=torch.int32, device=dev)
+    return cu_seqlens.numel() - 1
+
+
 def conv1d_pack_fwd(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor], pos: torch.Tensor,
                     silu: bool = True, out: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
                     conv_initial: Optional[torch.Tensor] = None, conv_final=False):
@@ -209,10 +216,7 @@ def conv1d_pack_fwd(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor],
     u = torch.empty_like(x) if out is None else out
     _check(u, "u", (T, D), x.dtype, x.device)
     if cu_seqlens is not None or conv_initial is not None or conv_final is not False:
-        if cu_seqlens is None:
-            raise ValueError("conv states need cu_seqlens")
-        _check(cu_seqlens, "cu_seqlens", dtype=torch.int32, device=x.device)
-        nseq = cu_seqlens.numel() - 1
+        nseq = _nseq(cu_seqlens, x.device)
         cf = _out_or_new(conv_final, (nseq, W - 1, D), x.dtype, x.device)
         _check(conv_initial, "conv_initial", (nseq, W - 1, D), x.dtype, x.device)
         _check(cf, "conv_final", (nseq, W - 1, D), x.dtype, x.device)
@@ -254,10 +258,7 @@ def conv1d_pack_bwd(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor],
     _check(dx, "dx", (T, D), x.dtype, x.device); _check(dw, "dw", (D, W), torch.float32, x.device)
     _check(db, "db", (D,), torch.float32, x.device)
     if cu_seqlens is not None or conv_initial is not None or dconv_final is not None or dconv_initial is not False:
-        if cu_seqlens is None:
-            raise ValueError("conv states need cu_seqlens")
-        _check(cu_seqlens, "cu_seqlens", dtype=torch.int32, device=x.device)
-        nseq = cu_seqlens.numel() - 1
+        nseq = _nseq(cu_seqlens, x.device)
         dci = _out_or_new(dconv_initial, (nseq, W - 1, D), x.dtype, x.device)
         for name, t in (("conv_initial", conv_initial), ("dconv_final", dconv_final), ("dconv_initial", dci)):
             _check(t, name, (nseq, W - 1, D), x.dtype, x.device)
@@ -285,14 +286,20 @@ def _extended(delta_bias, delta_softplus, gate_floor) -> bool:
     return delta_bias is not None or bool(delta_softplus) or float(gate_floor) != 0.0
 
 
-def _states_args(cu_seqlens, nseq_from, D, N, dev):
-    _check(cu_seqlens, "cu_seqlens", dtype=torch.int32, device=dev)
-    if cu_seqlens is None:
-        raise ValueError("sequence states need cu_seqlens")
-    nseq = cu_seqlens.numel() - 1
-    for name, t in nseq_from:
+def _check_states(nseq, named, D, N, dev):
+    for name, t in named:
         _check(t, name, (nseq, D, N), torch.float32, dev)
-    return nseq
+
+
+def _bias_grad(delta_bias, out, D, dev):
+    """The d bias output (from `out` when given there), or None without a bias."""
+    if delta_bias is None:
+        return None
+    ddb = out.get("ddelta_bias") if out is not None else None
+    if ddb is None:
+        ddb = torch.empty((D,), dtype=torch.float32, device=dev)
+    _check(ddb, "ddelta_bias", (D,), torch.float32, dev)
+    return ddb
 
 
 def selective_scan_pack_fwd(u, delta, A, B, C, Dskip, z, pos, workspace: Optional[torch.Tensor] = None,
@@ -321,12 +328,9 @@ def selective_scan_pack_fwd(u, delta, A, B, C, Dskip, z, pos, workspace: Optiona
             _ptr(workspace), workspace.numel() * workspace.element_size(), T, D, N, _dtype_code(u))
     if cu_seqlens is not None or initial_state is not None or final_state is not False:
         _check(delta_bias, "delta_bias", (D,), torch.float32, dev)
-        fs = None
-        if final_state is True:
-            fs = torch.empty((cu_seqlens.numel() - 1, D, N), dtype=torch.float32, device=dev)
-        elif isinstance(final_state, torch.Tensor):
-            fs = final_state
-        nseq = _states_args(cu_seqlens, (("initial_state", initial_state), ("final_state", fs)), D, N, dev)
+        nseq = _nseq(cu_seqlens, dev)
+        fs = _out_or_new(final_state, (nseq, D, N), torch.float32, dev)
+        _check_states(nseq, (("initial_state", initial_state), ("final_state", fs)), D, N, dev)
         _call("selective_scan_pack_fwd_states", *args, _ptr(delta_bias), int(bool(delta_softplus)),
               float(gate_floor), _ptr(cu_seqlens), nseq, _ptr(initial_state), _ptr(fs), _stream(u))
         return o, workspace, fs
@@ -379,19 +383,11 @@ def selective_scan_pack_bwd(u, delta, A, B, C, Dskip, z, pos, dout, workspace: t
     if (cu_seqlens is not None or initial_state is not None or dfinal_state is not None
             or dinitial_state is not False):
         _check(delta_bias, "delta_bias", (D,), torch.float32, dev)
-        ddb = None
-        if delta_bias is not None:
-            ddb = out.get("ddelta_bias") if out is not None else None
-            if ddb is None:
-                ddb = torch.empty((D,), dtype=torch.float32, device=dev)
-            _check(ddb, "ddelta_bias", (D,), torch.float32, dev)
-        di = None
-        if dinitial_state is True:
-            di = torch.empty((cu_seqlens.numel() - 1, D, N), dtype=torch.float32, device=dev)
-        elif isinstance(dinitial_state, torch.Tensor):
-            di = dinitial_state
-        nseq = _states_args(cu_seqlens, (("initial_state", initial_state), ("dfinal_state", dfinal_state),
-                                         ("dinitial_state", di)), D, N, dev)
+        ddb = _bias_grad(delta_bias, out, D, dev)
+        nseq = _nseq(cu_seqlens, dev)
+        di = _out_or_new(dinitial_state, (nseq, D, N), torch.float32, dev)
+        _check_states(nseq, (("initial_state", initial_state), ("dfinal_state", dfinal_state),
+                             ("dinitial_state", di)), D, N, dev)
         _call("selective_scan_pack_bwd_states", *args, _ptr(delta_bias), int(bool(delta_softplus)),
               float(gate_floor), _ptr(ddb), _ptr(cu_seqlens), nseq, _ptr(initial_state), _ptr(dfinal_state),
               _ptr(di), _stream(u))
@@ -400,12 +396,7 @@ def selective_scan_pack_bwd(u, delta, A, B, C, Dskip, z, pos, dout, workspace: t
         return res
     if _extended(delta_bias, delta_softplus, gate_floor):
         _check(delta_bias, "delta_bias", (D,), torch.float32, dev)
-        ddb = None
-        if delta_bias is not None:
-            ddb = out.get("ddelta_bias") if out is not None else None
-            if ddb is None:
-                ddb = torch.empty((D,), dtype=torch.float32, device=dev)
-            _check(ddb, "ddelta_bias", (D,), torch.float32, dev)
+        ddb = _bias_grad(delta_bias, out, D, dev)
         _call("selective_scan_pack_bwd_ex", *args, _ptr(delta_bias), int(bool(delta_softplus)), float(gate_floor),
               _ptr(ddb), _stream(u))
         res["ddelta_bias"] = ddb

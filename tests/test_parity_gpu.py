@@ -602,6 +602,51 @@ def test_pipeline_cut_across_packs(orc):
     assert_close(npy(gb["out"]), out_o, to, "out (oracle)")
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_pipeline_step_map_with_states(orc, dtype):
+    """The block chain with the step map softplus(delta + bias), the gate floor
+    and both carried states at once, forward and backward, against the
+    oracle's state-carrying functions run in the same order."""
+    lengths = [300, 1, 200, 513]
+    inp = synth.make_inputs(2, lengths=lengths, D=96, dtype=dtype, with_dout=True)
+    nseq, D, N, W = inp.nseq, inp.D, inp.N, inp.W
+    rng = np.random.default_rng(31)
+    bias = (rng.standard_normal(D) * 0.2).astype(np.float32)
+    h0 = (rng.standard_normal((nseq, D, N)) * 0.5).astype(np.float32)
+    dhT = rng.standard_normal((nseq, D, N)).astype(np.float32)
+    ci = synth.to_dtype(rng.standard_normal((nseq, W - 1, D)), dtype)
+    dcf = synth.to_dtype(rng.standard_normal((nseq, W - 1, D)), dtype)
+    floor = 0.05
+    d = Dev(inp)
+    F = ssp().forward(d.x, d.w, d.b, d.delta, d.A, d.B, d.C, d.Dp, d.z, d.cu, pos=d.pos,
+                      initial_states={"ssm": to_dev(torch.from_numpy(h0)), "conv": to_dev(ci)}, final_states=True,
+                      delta_bias=to_dev(torch.from_numpy(bias)), delta_softplus=True, gate_floor=floor)
+    G = ssp().backward(d.x, d.w, d.b, d.delta, d.A, d.B, d.C, d.Dp, d.z, F, d.dout,
+                       dfinal_states={"ssm": to_dev(torch.from_numpy(dhT)), "conv": to_dev(dcf)})
+    torch.cuda.synchronize()
+    f64, cu = synth.f64, inp.cu_seqlens
+    ext = dict(delta_bias=bias.astype(np.float64), delta_softplus=True, gate_floor=floor)
+    x, w, b, z, dout = f64(inp.x), f64(inp.w), f64(inp.b), f64(inp.z), f64(inp.dout)
+    delta, A, B, C, Dp = f64(inp.delta), f64(inp.A), f64(inp.B), f64(inp.C), f64(inp.Dp)
+    _, u, cf = orc.conv_fwd_state(x, w, b, cu, f64(ci), threads=8)
+    _, out, hT = orc.scan_fwd_state(u, delta, A, B, C, Dp, z, cu, h0=h0.astype(np.float64), threads=8, **ext)
+    R = orc.scan_bwd_state(u, delta, A, B, C, Dp, z, cu, dout, h0=h0.astype(np.float64),
+                           dhT=dhT.astype(np.float64), threads=8, **ext)
+    dx, dw, db, dci = orc.conv_bwd_state(x, w, b, cu, R["du"], f64(ci), f64(dcf), threads=8)
+    to, tg = TOL_OUT[dtype], TOL_GRAD[dtype]
+    assert_close(npy(F["u"]), u, to, "u")
+    assert_close(npy(F["out"]), out, to, "out")
+    assert_close(npy(F["final_states"]["ssm"]), hT, to, "final ssm state")
+    assert np.array_equal(npy(F["final_states"]["conv"]), cf), "final conv context"
+    for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias"):
+        assert_close(npy(G[k]), R[k], tg, k)
+    assert_close(npy(G["dx"]), dx, tg, "dx")
+    assert_close(npy(G["dw"]), dw, tg, "dw")
+    assert_close(npy(G["db"]), db, tg, "db")
+    assert_close(npy(G["dinitial_states"]["ssm"]), R["dh0"], tg, "dinitial ssm state")
+    assert_close(npy(G["dinitial_states"]["conv"]), dci, tg, "dinitial conv context")
+
+
 def test_states_empty_pack():
     """No tokens at all (every sequence empty): final states are the initial
     ones and the initial-state gradients are the final-state ones, for the
@@ -633,6 +678,22 @@ def test_states_empty_pack():
     assert torch.equal(hT, h0) and torch.equal(cf, ci)
     assert torch.equal(gr["dinitial_state"], dhT) and torch.equal(dci, dcf)
     assert not gr["dA"].any() and not gr["dD"].any() and not dw.any() and not db.any()
+
+
+def test_state_outputs_need_cu_seqlens():
+    """Asking the binding for a state output without cu_seqlens is a clear
+    ValueError raised before any launch."""
+    import selective_state_space_varlen_amd as ssp
+    inp = synth.make_inputs(2, lengths=[5, 7], D=8, N=4, with_dout=True, with_u=True)
+    d = Dev(inp)
+    with pytest.raises(ValueError, match="need cu_seqlens"):
+        ssp.selective_scan_pack_fwd(d.u, d.delta, d.A, d.B, d.C, d.Dp, d.z, d.pos, final_state=True)
+    _, ws = ssp.selective_scan_pack_fwd(d.u, d.delta, d.A, d.B, d.C, d.Dp, d.z, d.pos)
+    with pytest.raises(ValueError, match="need cu_seqlens"):
+        ssp.selective_scan_pack_bwd(d.u, d.delta, d.A, d.B, d.C, d.Dp, d.z, d.pos, d.dout, ws, dinitial_state=True)
+    with pytest.raises(ValueError, match="need cu_seqlens"):
+        ssp.conv1d_pack_fwd(d.x, d.w, d.b, d.pos, conv_final=True)
+    torch.cuda.synchronize()
 
 
 def test_empty_input_plain_entry_points():
