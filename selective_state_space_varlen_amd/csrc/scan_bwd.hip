@@ -547,12 +547,24 @@ __global__ __launch_bounds__(kWave * WV, 2) void k_scan_bwd_main(BwdArgs<T> p) {
     constexpr int BCP = (BCV + NT - 1) / NT;              // pieces per thread
     float4 bcr[BCP];
     auto fetch_bc = [&](int64_t tb) {
-        const float4* srcv = reinterpret_cast<const float4*>(p.bc + (size_t)tb * BCW);
-        const int64_t lim = ((p.T_ - tb < kBB) ? (p.T_ - tb) : kBB) * BCW / 4;
+        const float* srcf = p.bc + (size_t)tb * BCW;  // 16-byte aligned: tb is a multiple of kBB
+        const float4* srcv = reinterpret_cast<const float4*>(srcf);
+        // floats of the block's rows inside the tensor; with 2N not a multiple
+        // of 4 the last piece can be partial, and is read float by float
+        const int lim = (int)((p.T_ - tb < kBB) ? (p.T_ - tb) : kBB) * BCW;
 #pragma unroll
         for (int q = 0; q < BCP; ++q) {
             const int idx = q * NT + tid;
-            bcr[q] = (idx < BCV && idx < lim) ? srcv[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const int f0 = idx * 4;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (idx < BCV && f0 + 4 <= lim) {
+                v = srcv[idx];
+            } else if (idx < BCV && f0 < lim) {
+                v.x = srcf[f0];
+                if (f0 + 1 < lim) v.y = srcf[f0 + 1];
+                if (f0 + 2 < lim) v.z = srcf[f0 + 2];
+            }
+            bcr[q] = v;
         }
     };
     auto commit_bc = [&]() {

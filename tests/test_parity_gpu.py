@@ -119,6 +119,10 @@ SCAN_CASES = {
     "heads-on-chunk-starts": dict(wl=2, lengths=[256, 256, 512, 17], D=64),
     "zero-length-sequences": dict(wl=2, lengths=[5, 0, 300, 0, 0, 40, 1000], D=70),
     "d_state-1-fp32": dict(wl=2, lengths=[300, 2, 500], D=33, N=1, dtype=torch.float32),
+    # d_state 1 with an odd token count in the last 16-token block: that
+    # block's B/C rows end halfway through a 16-byte piece
+    "d_state-1-odd-tail-fp32": dict(wl=2, lengths=[109, 10, 1, 206, 11, 6, 6], D=130, N=1, dtype=torch.float32),
+    "d_state-1-odd-tail": dict(wl=2, lengths=[109, 10, 1, 206, 11, 6, 6], D=130, N=1),
     "d_state-2": dict(wl=2, lengths=[300, 2, 500], D=64, N=2),
     "d_state-8-fp32": dict(wl=2, lengths=[700, 90], D=130, N=8, dtype=torch.float32),
     "no-gate-no-skip": dict(wl=2, lengths=[400, 1, 299], D=64, gate=False, skip=False),

@@ -1,0 +1,125 @@
+"""Seeded random sweep of the block chain against the oracle.
+
+Each case draws its own d_inner, d_state, conv width, dtype, length mix (empty
+and single-token sequences, sequences that cross several chunks) and options:
+gate, skip, conv bias, the step map softplus(delta + bias) with a gate floor,
+and carried SSM states and conv contexts in both directions. The chain runs
+through pipeline.forward / backward (every library entry point but the
+packer) and every output and gradient is compared with the oracle's
+state-carrying functions, which with absent states are the reset-only ones.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests.gpu_harness import TOL_GRAD, TOL_OUT, Dev, assert_close, npy, to_dev
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 24
+
+
+def draw_case(i: int) -> dict:
+    rng = np.random.default_rng(1000 + i)
+    nseq = int(rng.integers(1, 13))
+    kinds = rng.choice(["empty", "one", "short", "medium", "long"], size=nseq, p=[0.1, 0.15, 0.25, 0.35, 0.15])
+    size = {"empty": (0, 1), "one": (1, 2), "short": (2, 12), "medium": (12, 300), "long": (300, 1100)}
+    lengths = [int(rng.integers(*size[k])) for k in kinds]
+    if sum(lengths) == 0:
+        lengths[0] = int(rng.integers(1, 400))
+    W = int(rng.choice([1, 2, 3, 4], p=[0.1, 0.15, 0.15, 0.6]))
+    return dict(
+        lengths=lengths,
+        D=int(rng.choice([1, 7, 33, 64, 65, 96, 130, 200])),
+        N=int(rng.choice([1, 2, 4, 8, 16], p=[0.1, 0.1, 0.2, 0.2, 0.4])),
+        W=W,
+        dtype=torch.bfloat16 if rng.random() < 0.6 else torch.float32,
+        gate=bool(rng.random() < 0.8),
+        skip=bool(rng.random() < 0.8),
+        conv_bias=bool(rng.random() < 0.8),
+        step_bias=bool(rng.random() < 0.5),
+        softplus=bool(rng.random() < 0.5),
+        floor=float(rng.choice([0.0, 0.05])),
+        # a conv context has W - 1 rows: none to carry at width 1
+        states=bool(rng.random() < 0.5) and W > 1,
+        seed=int(rng.integers(0, 2**31)),
+    )
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_block_chain_sweep(orc, i):
+    import selective_state_space_varlen_amd as ssp
+    c = draw_case(i)
+    print(f"[sweep {i}] {c}", flush=True)
+    inp = synth.make_inputs(2, lengths=c["lengths"], D=c["D"], N=c["N"], dtype=c["dtype"], seed=c["seed"],
+                            with_dout=True)
+    W, D, N, nseq = c["W"], inp.D, inp.N, inp.nseq
+    inp.w = inp.w[:, 4 - W:].contiguous()
+    inp.W = W
+    rng = np.random.default_rng(c["seed"] + 1)
+    bias = (rng.standard_normal(D) * 0.3).astype(np.float32) if c["step_bias"] else None
+    if c["softplus"] or bias is not None:
+        # stored steps chosen so that the mapped step keeps the workload's values
+        d64 = synth.f64(inp.delta)
+        raw = (np.log(np.expm1(d64)) if c["softplus"] else d64) - (bias[None, :] if bias is not None else 0.0)
+        inp.delta = synth.to_dtype(raw, inp.dtype)
+    h0 = dhT = ci = dcf = None
+    if c["states"]:
+        h0 = (rng.standard_normal((nseq, D, N)) * 0.5).astype(np.float32)
+        dhT = rng.standard_normal((nseq, D, N)).astype(np.float32)
+        ci = synth.to_dtype(rng.standard_normal((nseq, W - 1, D)), inp.dtype)
+        dcf = synth.to_dtype(rng.standard_normal((nseq, W - 1, D)), inp.dtype)
+
+    d = Dev(inp)
+    b = d.b if c["conv_bias"] else None
+    Dp = d.Dp if c["skip"] else None
+    z = d.z if c["gate"] else None
+    ext = dict(delta_bias=to_dev(torch.from_numpy(bias)) if bias is not None else None,
+               delta_softplus=c["softplus"], gate_floor=c["floor"])
+    st = dict(initial_states={"ssm": to_dev(torch.from_numpy(h0)), "conv": to_dev(ci)},
+              final_states=True) if c["states"] else {}
+    F = ssp.forward(d.x, d.w, b, d.delta, d.A, d.B, d.C, Dp, z, d.cu, pos=d.pos, **st, **ext)
+    dst = dict(dfinal_states={"ssm": to_dev(torch.from_numpy(dhT)), "conv": to_dev(dcf)}) if c["states"] else {}
+    G = ssp.backward(d.x, d.w, b, d.delta, d.A, d.B, d.C, Dp, z, F, d.dout, **dst)
+    torch.cuda.synchronize()
+
+    f64, cu = synth.f64, inp.cu_seqlens
+    x, w = f64(inp.x), f64(inp.w)
+    bo = f64(inp.b) if c["conv_bias"] else None
+    Dpo = f64(inp.Dp) if c["skip"] else None
+    zo = f64(inp.z) if c["gate"] else None
+    delta, A, B, C, dout = f64(inp.delta), f64(inp.A), f64(inp.B), f64(inp.C), f64(inp.dout)
+    oext = dict(delta_bias=bias.astype(np.float64) if bias is not None else None,
+                delta_softplus=c["softplus"], gate_floor=c["floor"])
+    h0o = h0.astype(np.float64) if h0 is not None else None
+    dhTo = dhT.astype(np.float64) if dhT is not None else None
+    cio = f64(ci) if ci is not None else None
+    dcfo = f64(dcf) if dcf is not None else None
+    _, u, cf = orc.conv_fwd_state(x, w, bo, cu, cio, threads=8)
+    _, out, hT = orc.scan_fwd_state(u, delta, A, B, C, Dpo, zo, cu, h0=h0o, threads=8, **oext)
+    R = orc.scan_bwd_state(u, delta, A, B, C, Dpo, zo, cu, dout, h0=h0o, dhT=dhTo, threads=8, **oext)
+    dx, dw, db, dci = orc.conv_bwd_state(x, w, bo, cu, R["du"], cio, dcfo, threads=8)
+
+    to, tg = TOL_OUT[inp.dtype], TOL_GRAD[inp.dtype]
+    assert_close(npy(F["u"]), u, to, "u")
+    assert_close(npy(F["out"]), out, to, "out")
+    for k in ("du", "ddelta", "dA", "dB", "dC"):
+        assert_close(npy(G[k]), R[k], tg, k)
+    if c["skip"]:
+        assert_close(npy(G["dD"]), R["dD"], tg, "dD")
+    if c["gate"]:
+        assert_close(npy(G["dz"]), R["dz"], tg, "dz")
+    if bias is not None:
+        assert_close(npy(G["ddelta_bias"]), R["ddelta_bias"], tg, "ddelta_bias")
+    assert_close(npy(G["dx"]), dx, tg, "dx")
+    assert_close(npy(G["dw"]), dw, tg, "dw")
+    if c["conv_bias"]:
+        assert_close(npy(G["db"]), db, tg, "db")
+    if c["states"]:
+        assert_close(npy(F["final_states"]["ssm"]), hT, to, "final ssm state")
+        assert np.array_equal(npy(F["final_states"]["conv"]), cf), "final conv context"
+        assert_close(npy(G["dinitial_states"]["ssm"]), R["dh0"], tg, "dinitial ssm state")
+        assert_close(npy(G["dinitial_states"]["conv"]), dci, tg, "dinitial conv context")
