@@ -316,12 +316,13 @@ __device__ __forceinline__ void out_block(const T* lds, const float* __restrict_
     }
 }
 
-// Four waves per SIMD (128 VGPRs) for the plain kernel. The state variant,
-// whose heads load arbitrary states, and the step-map variant, which holds
-// the softplus temporaries, would spill at that budget in the hot loop; both
-// run faster at up to 256 VGPRs (measured: 3 waves fit).
+// Four waves per SIMD (128 VGPRs) for the plain bf16 kernel. The state
+// variant, whose heads load arbitrary states, the step-map variant, which
+// holds the softplus temporaries, and fp32 inputs, whose staged block takes
+// twice the registers, would spill at that budget in the hot loop; all of
+// them run faster at up to 256 VGPRs (measured: 3 waves fit).
 template <typename T, int NS, bool GATE, bool XS, bool ST>
-__global__ __launch_bounds__(64, (ST || XS) ? 2 : 4) void k_scan_fwd_out(
+__global__ __launch_bounds__(64, (ST || XS || sizeof(T) == 4) ? 2 : 4) void k_scan_fwd_out(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A, const float* __restrict__ bc,
     const float* __restrict__ Dskip, const T* __restrict__ z, const int32_t* __restrict__ pos, T* __restrict__ out,
     float* __restrict__ ckpt, int64_t T_, int D, int vec, int lc, ScanOpts opt) {
