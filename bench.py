@@ -455,6 +455,11 @@ def main():
         ms_e, _ = time_steps(wex, nq, 2, per_op=False)
         layouts["packed_step_map_gate_floor"] = round(T / (ms_e / nq * 1e-3), 1)
         del wex
+        # both at once: carried states with the step map and gate floor
+        wxe = Workload(inp, states=True, ext=True)
+        ms_xe, _ = time_steps(wxe, nq, 2, per_op=False)
+        layouts["packed_carry_states_step_map"] = round(T / (ms_xe / nq * 1e-3), 1)
+        del wxe
         cu_concat = np.arange(0, T + 1, spec.pack_len, dtype=np.int32)
         wc = Workload(inp, cu=cu_concat)
         ms_c, _ = time_steps(wc, max(3, args.steps // 2), 2, per_op=False)
