@@ -18,23 +18,29 @@ from tests.gpu_harness import Dev
 pytestmark = pytest.mark.gpu
 
 
-def _run(ssp, d, x, delta, dout, states=None):
+def _run(ssp, d, x, delta, dout, states=None, ext=None):
     F = ssp.forward(x, d.w, d.b, delta, d.A, d.B, d.C, d.Dp, d.z, d.cu, pos=d.pos,
-                    initial_states=states, final_states=states is not None)
+                    initial_states=states, final_states=states is not None, **(ext or {}))
     G = ssp.backward(x, d.w, d.b, delta, d.A, d.B, d.C, d.Dp, d.z, F, dout,
                      dfinal_states=None if states is None else {"ssm": states["ssm"], "conv": None})
     out = {"out": F["out"], **{k: G[k] for k in ("dx", "dw", "db", "ddelta", "dA", "dB", "dC", "dD", "dz")}}
+    if ext:
+        out["ddelta_bias"] = G["ddelta_bias"]
     if states is not None:
         out["hT"] = F["final_states"]["ssm"]
         out["dh0"] = G["dinitial_states"]["ssm"]
     return out
 
 
-@pytest.mark.parametrize("with_states", [False, True])
-def test_graph_replay_matches_eager(with_states):
+@pytest.mark.parametrize("with_states,step_map", [(False, False), (True, False), (False, True), (True, True)])
+def test_graph_replay_matches_eager(with_states, step_map):
     import selective_state_space_varlen_amd as ssp
     inp = synth.make_inputs(2, n_packs=2, D=256, with_dout=True)
     d = Dev(inp)
+    ext = None
+    if step_map:
+        gb = torch.Generator().manual_seed(4)
+        ext = dict(delta_bias=(torch.randn(inp.D, generator=gb) * 0.1).cuda(), delta_softplus=True, gate_floor=0.05)
     states = None
     if with_states:
         g = torch.Generator().manual_seed(3)
@@ -52,17 +58,17 @@ def test_graph_replay_matches_eager(with_states):
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):  # warm up outside the graph
         sx.copy_(batches[0][0]); sdout.copy_(batches[0][2])
-        _run(ssp, d, sx, sdelta, sdout, states)
+        _run(ssp, d, sx, sdelta, sdout, states, ext)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        res = _run(ssp, d, sx, sdelta, sdout, states)
+        res = _run(ssp, d, sx, sdelta, sdout, states, ext)
     torch.cuda.synchronize()
     for i, (bx, bd, bo) in enumerate(batches):
         # eager reference on the same inputs, then the replay
         delta = (d.delta.float() + bd.float().abs()).to(inp.dtype)
-        ref = _run(ssp, d, bx, delta, bo, states)
+        ref = _run(ssp, d, bx, delta, bo, states, ext)
         torch.cuda.synchronize()
         ref = {k: v.clone() for k, v in ref.items()}
         sx.copy_(bx); sdelta.copy_(delta); sdout.copy_(bo)
