@@ -778,3 +778,51 @@ def test_scan_numerical_regimes(orc, name):
     assert_close(npy(out), rout, to, "out")
     for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz"):
         assert_close(npy(g[k]), rg[k], tg, k)
+
+
+def test_many_sequences_with_states(orc):
+    """40 000 sequences (empty, single-token and short ones mixed) with both
+    carried states and the step map, through the block chain: the head's
+    sequence lookup, the empty-sequence pass-through and the per-sequence
+    conv contexts at scale, against the oracle (each operator on the stored
+    inputs it consumed)."""
+    rng = np.random.default_rng(91)
+    lengths = [int(v) for v in rng.choice([0, 1, 2, 3, 5, 9], size=40000, p=[0.2, 0.3, 0.2, 0.1, 0.1, 0.1])]
+    inp = synth.make_inputs(2, lengths=lengths, D=64, N=16, dtype=torch.float32, with_dout=True)
+    nseq, D, N, W = inp.nseq, inp.D, inp.N, inp.W
+    print(f"[many] {nseq} sequences, T={inp.T}", flush=True)
+    bias = (rng.standard_normal(D) * 0.2).astype(np.float32)
+    h0 = (rng.standard_normal((nseq, D, N)) * 0.5).astype(np.float32)
+    dhT = rng.standard_normal((nseq, D, N)).astype(np.float32)
+    ci = synth.to_dtype(rng.standard_normal((nseq, W - 1, D)), inp.dtype)
+    dcf = synth.to_dtype(rng.standard_normal((nseq, W - 1, D)), inp.dtype)
+    d = Dev(inp)
+    s = ssp()
+    F = s.forward(d.x, d.w, d.b, d.delta, d.A, d.B, d.C, d.Dp, d.z, d.cu, pos=d.pos,
+                  initial_states={"ssm": to_dev(torch.from_numpy(h0)), "conv": to_dev(ci)}, final_states=True,
+                  delta_bias=to_dev(torch.from_numpy(bias)), delta_softplus=True, gate_floor=0.05)
+    G = s.backward(d.x, d.w, d.b, d.delta, d.A, d.B, d.C, d.Dp, d.z, F, d.dout,
+                   dfinal_states={"ssm": to_dev(torch.from_numpy(dhT)), "conv": to_dev(dcf)})
+    torch.cuda.synchronize()
+    f64, cu = synth.f64, inp.cu_seqlens
+    ext = dict(delta_bias=bias.astype(np.float64), delta_softplus=True, gate_floor=0.05)
+    x, w, b, z, dout = f64(inp.x), f64(inp.w), f64(inp.b), f64(inp.z), f64(inp.dout)
+    delta, A, B, C, Dp = f64(inp.delta), f64(inp.A), f64(inp.B), f64(inp.C), f64(inp.Dp)
+    to, tg = TOL_OUT[inp.dtype], TOL_GRAD[inp.dtype]
+    _, u, cf = orc.conv_fwd_state(x, w, b, cu, f64(ci), threads=8)
+    assert_close(npy(F["u"]), u, to, "u")
+    assert np.array_equal(npy(F["final_states"]["conv"]), cf), "final conv context"
+    u = npy(F["u"]).astype(np.float64)
+    _, out, hT = orc.scan_fwd_state(u, delta, A, B, C, Dp, z, cu, h0=h0.astype(np.float64), threads=8, **ext)
+    R = orc.scan_bwd_state(u, delta, A, B, C, Dp, z, cu, dout, h0=h0.astype(np.float64),
+                           dhT=dhT.astype(np.float64), threads=8, **ext)
+    assert_close(npy(F["out"]), out, to, "out")
+    assert_close(npy(F["final_states"]["ssm"]), hT, to, "final ssm state")
+    for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias"):
+        assert_close(npy(G[k]), R[k], tg, k)
+    assert_close(npy(G["dinitial_states"]["ssm"]), R["dh0"], tg, "dinitial ssm state")
+    dx, dw, db, dci = orc.conv_bwd_state(x, w, b, cu, npy(G["du"]).astype(np.float64), f64(ci), f64(dcf), threads=8)
+    assert_close(npy(G["dx"]), dx, tg, "dx")
+    assert_close(npy(G["dw"]), dw, tg, "dw")
+    assert_close(npy(G["db"]), db, tg, "db")
+    assert_close(npy(G["dinitial_states"]["conv"]), dci, tg, "dinitial conv context")
