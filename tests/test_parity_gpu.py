@@ -81,6 +81,7 @@ CONV_CASES = [
     (torch.bfloat16, 102, 4, True, [3, 260, 1, 40]),         # D % 4 != 0: per-element backward too
     (torch.float32, 33, 2, True, [9, 1, 300, 2]),            # odd D
     (torch.bfloat16, 520, 4, True, [300, 1, 2, 600, 17]),    # a partial 64-vector group
+    (torch.bfloat16, 8192, 4, True, [700, 1, 800]),          # twice the benchmark's d_inner
 ]
 
 
@@ -127,6 +128,7 @@ SCAN_CASES = {
     "d_state-8-fp32": dict(wl=2, lengths=[700, 90], D=130, N=8, dtype=torch.float32),
     "no-gate-no-skip": dict(wl=2, lengths=[400, 1, 299], D=64, gate=False, skip=False),
     "single-token-pack": dict(wl=2, lengths=[1], D=64),
+    "wide-d_inner-8192": dict(wl=2, lengths=[700, 1, 800], D=8192),
 }
 
 
