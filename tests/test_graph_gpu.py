@@ -76,3 +76,31 @@ def test_graph_replay_matches_eager(with_states, step_map):
         torch.cuda.synchronize()
         for k, v in ref.items():
             assert torch.equal(res[k], v), f"replay {i}: {k} differs from the eager run"
+
+
+def test_concurrent_streams_match_sequential():
+    """The library keeps no state between calls: two batches' forward and
+    backward issued at the same time on two streams (each with its own
+    workspaces) give bit for bit what each gives alone."""
+    import selective_state_space_varlen_amd as ssp
+    ins = [synth.make_inputs(2, n_packs=2, D=192, seed=s, with_dout=True) for s in (11, 12)]
+    devs = [Dev(i) for i in ins]
+    ref = []
+    for d in devs:
+        r = _run(ssp, d, d.x, d.delta, d.dout)
+        torch.cuda.synchronize()
+        ref.append({k: v.clone() for k, v in r.items()})
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        cur = torch.cuda.current_stream()
+        outs = [None, None]
+        for j, (d, s) in enumerate(zip(devs, streams)):
+            s.wait_stream(cur)
+            with torch.cuda.stream(s):
+                outs[j] = _run(ssp, d, d.x, d.delta, d.dout)
+        for s in streams:
+            cur.wait_stream(s)
+        torch.cuda.synchronize()
+        for j in range(2):
+            for k, v in ref[j].items():
+                assert torch.equal(outs[j][k], v), f"repeat {rep}, batch {j}: {k} differs from its sequential run"
