@@ -9,7 +9,7 @@
 //
 // Both kernels stream HBM: a thread owns V adjacent channels (one vector
 // load) and runs of consecutive tokens. Consecutive lanes own consecutive
-// vectors, so a wave reads 1 KiB (forward) or 512 B (backward) of one row per
+// vectors, so a wave reads 1 KiB (forward) or 256 B (backward) of one row per
 // load.
 //
 // Forward: runs of kRun tokens whose row loads (the run's and its W-1 halo
