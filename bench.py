@@ -366,7 +366,7 @@ def copy_ceiling(nbytes: int = 1 << 30, reps: int = 10) -> float:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4])
     ap.add_argument("--no-layouts", action="store_true")
