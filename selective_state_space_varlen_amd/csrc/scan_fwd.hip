@@ -256,10 +256,6 @@ __device__ __forceinline__ void out_block(const T* lds, const float* __restrict_
         uv[k] = St::get(lds, 0, k, lane);
         if constexpr (GATE) zv[k] = St::get(lds, 2, k, lane);
     }
-    if constexpr (XS) {
-#pragma unroll
-        for (int k = 0; k < BT; ++k) dtv[k] = sm.eff(dtv[k]);
-    }
     const float* __restrict__ rows = bc + (size_t)tb * 2 * NS;
     float cur[2 * NS];
     load_rowv<2 * NS>(rows, cur);
@@ -274,7 +270,9 @@ __device__ __forceinline__ void out_block(const T* lds, const float* __restrict_
         float nxt[2 * NS];
         const bool more = SAFE ? (k + 1 < nt) : (k + 1 < BT);
         if (more) load_rowv<2 * NS>(rows + (k + 1) * 2 * NS, nxt);
-        const float dt = dtv[k];
+        // the step map next to its use: mapping the whole block first held
+        // the first state update behind eight softplus chains
+        const float dt = XS ? sm.eff(dtv[k]) : dtv[k];
         const float uu = uv[k];
         const float dtu = dt * uu;
         if constexpr (SAFE) {
