@@ -21,9 +21,10 @@
 // the taps for every short run costs as much again. Halo rows are read again
 // by the neighbouring run and mostly hit in L2.
 //
-// Backward: the same runs and passes; a run also recomputes the activation
-// gradient of the W - 1 tokens after it, which its dx rows need, and its
-// workgroup sums the taps' and bias's gradients over its waves.
+// Backward: runs of kBwdRun tokens in the same band-wise passes; a run also
+// recomputes the activation gradient of the W - 1 tokens after it, which its
+// dx rows need, and its workgroup sums the taps' and bias's gradients over
+// its waves.
 #include <type_traits>
 
 #include "common.h"
@@ -73,6 +74,11 @@ template <typename T> constexpr int kBwdV = 4 / (int)sizeof(T);
 
 constexpr int kRun = 8;            // forward: tokens per run
 constexpr int kFwdPasses = 4;      // forward: runs per thread, one per pass
+// backward: tokens per run. Each run recomputes the activation gradient of
+// W - 1 tokens past its end; at 8 tokens that is 3/8 more of that work, at 12
+// only 1/4 (measured: 0.176 against 0.197 ms; 10 and 14 tie with 12, 16, 20,
+// 24 and 32 are slower as registers grow and fewer waves fit a SIMD)
+constexpr int kBwdRun = 12;
 constexpr int kConvBwdRuns = 4;    // backward: waves per workgroup, on consecutive runs
 constexpr int kConvBwdGroups = 128; // backward: workgroups per 64 vectors (a pass covers 512 runs)
 
@@ -188,8 +194,8 @@ __global__ __launch_bounds__(kWave * kConvBwdRuns) void k_conv_bwd(
     const int32_t* __restrict__ pos, const T* __restrict__ du, T* __restrict__ dx, float* __restrict__ part,
     int64_t T_, int D, int silu) {
     using A = Access<T, V>;
-    constexpr int NX = kRun + 2 * (W - 1);  // x rows t0-(W-1) .. t0+kRun+W-2
-    constexpr int NG = kRun + W - 1;        // gv of tokens t0 .. t0+kRun+W-2
+    constexpr int NX = kBwdRun + 2 * (W - 1);  // x rows t0-(W-1) .. t0+kBwdRun+W-2
+    constexpr int NG = kBwdRun + W - 1;        // gv of tokens t0 .. t0+kBwdRun+W-2
     __shared__ float red[kConvBwdRuns][5][kWave * V];
     const int nvec = D / V;
     const int nvg = (nvec + kWave - 1) / kWave;  // 64-vector groups
@@ -200,7 +206,7 @@ __global__ __launch_bounds__(kWave * kConvBwdRuns) void k_conv_bwd(
     const int cv = vg * kWave + lane;
     const bool actv = cv < nvec;
     const int d0 = (actv ? cv : 0) * V;
-    const int64_t nrun = (T_ + kRun - 1) / kRun;
+    const int64_t nrun = (T_ + kBwdRun - 1) / kBwdRun;
 
     float dwp[4][V], dbp[V];
 #pragma unroll
@@ -217,12 +223,12 @@ __global__ __launch_bounds__(kWave * kConvBwdRuns) void k_conv_bwd(
         for (int k = 0; k < W; ++k) wk[k][i] = w[(size_t)(d0 + i) * W + (W - 1 - k)];
     }
 
-    // one run; FULL runs (kRun own tokens and all W - 1 tokens after them
+    // one run; FULL runs (kBwdRun own tokens and all W - 1 tokens after them
     // inside the tensor) are straight-line code, so every load stays ahead of
     // the arithmetic
     auto run = [&](auto full_tag, int64_t t0) {
         constexpr bool FULL = decltype(full_tag)::value;
-        const int nt = FULL ? kRun : (int)((T_ - t0 < kRun) ? T_ - t0 : kRun);  // own tokens
+        const int nt = FULL ? kBwdRun : (int)((T_ - t0 < kBwdRun) ? T_ - t0 : kBwdRun);  // own tokens
         // rows outside [0, T) load row t0 and are never selected
         typename A::Raw rx[NX], rg[NG];
         int32_t pk[NG];
@@ -278,7 +284,7 @@ __global__ __launch_bounds__(kWave * kConvBwdRuns) void k_conv_bwd(
                 }
                 gv = have ? gv : 0.0f;
                 gw[j][i] = gv;
-                if (j < kRun && (FULL || j < nt)) {  // dw/db: the run's own tokens
+                if (j < kBwdRun && (FULL || j < nt)) {  // dw/db: the run's own tokens
                     if (clean) {
 #pragma unroll
                         for (int k = 0; k < W; ++k) dwp[k][i] = __builtin_fmaf(gv, xw[k][i], dwp[k][i]);
@@ -296,7 +302,7 @@ __global__ __launch_bounds__(kWave * kConvBwdRuns) void k_conv_bwd(
         }
         // dx[s], s = t0 + j: token s + k feeds tap k when k <= kmax(s + k)
 #pragma unroll
-        for (int j = 0; j < kRun; ++j) {
+        for (int j = 0; j < kBwdRun; ++j) {
             if (!FULL && j >= nt) break;
             float o[V];
 #pragma unroll
@@ -319,8 +325,8 @@ __global__ __launch_bounds__(kWave * kConvBwdRuns) void k_conv_bwd(
     const int64_t rfirst = (int64_t)__builtin_amdgcn_readfirstlane((int)(grp * kConvBwdRuns + wv));
     if (actv) {
         for (int64_t r = rfirst; r < nrun; r += ngrp * kConvBwdRuns) {
-            const int64_t t0 = r * kRun;
-            if (t0 + kRun + W - 1 <= T_)
+            const int64_t t0 = r * kBwdRun;
+            if (t0 + kBwdRun + W - 1 <= T_)
                 run(std::true_type{}, t0);
             else
                 run(std::false_type{}, t0);
@@ -489,7 +495,7 @@ __global__ __launch_bounds__(256) void k_conv_bwd_context(
 // workgroups per 64-vector group of the backward (one partial row set each):
 // enough for one pass to cover every run of a short input
 static int64_t conv_bwd_groups(int64_t T_) {
-    const int64_t nrun = (T_ + kRun - 1) / kRun;
+    const int64_t nrun = (T_ + kBwdRun - 1) / kBwdRun;
     const int64_t need = (nrun + kConvBwdRuns - 1) / kConvBwdRuns;
     return need < kConvBwdGroups ? need : kConvBwdGroups;
 }
