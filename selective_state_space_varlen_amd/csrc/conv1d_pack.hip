@@ -66,9 +66,9 @@ struct Access {
 
 // elements per access: 16 bytes in the forward; 4 in the backward, whose
 // per-channel state (taps, window, gradient sums) grows with the vector: at 4
-// bytes a thread holds 84 VGPRs and six waves share a SIMD, enough to cover
-// the run's loads (measured 0.196 ms against 0.225 at 8 bytes, 3 waves, and
-// 0.236 at 2 bytes)
+// bytes and 12-token runs a thread holds 89 VGPRs and five waves share a
+// SIMD, enough to cover the run's loads (measured at 8-token runs: 0.196 ms
+// against 0.225 at 8 bytes, 3 waves, and 0.236 at 2 bytes)
 template <typename T> constexpr int kFwdV = 16 / (int)sizeof(T);
 template <typename T> constexpr int kBwdV = 4 / (int)sizeof(T);
 
