@@ -5,6 +5,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "ssmpack.h"
 
 namespace ssmp {
@@ -26,9 +29,15 @@ struct Elt;
 // again soon (they then do not push shared inputs out of the L2). Only where a
 // wave's stores cover whole 128-byte lines: partial lines stored this way
 // reach memory unmerged.
+// raw: the element's bits, loaded without conversion (so a load issued ahead
+// of its use is not waited on at once); cvt: those bits as fp32.
 template <>
 struct Elt<float> {
     static __device__ __forceinline__ float ld(const float* __restrict__ p, size_t i) { return p[i]; }
+    static __device__ __forceinline__ uint32_t raw(const float* __restrict__ p, size_t i) {
+        return __builtin_bit_cast(uint32_t, p[i]);
+    }
+    static __device__ __forceinline__ float cvt(uint32_t b) { return __builtin_bit_cast(float, b); }
     static __device__ __forceinline__ void st(float* __restrict__ p, size_t i, float v) { p[i] = v; }
     static __device__ __forceinline__ void st_nt(float* __restrict__ p, size_t i, float v) {
         __builtin_nontemporal_store(v, p + i);
@@ -38,6 +47,8 @@ struct Elt<float> {
 template <>
 struct Elt<uint16_t> {
     static __device__ __forceinline__ float ld(const uint16_t* __restrict__ p, size_t i) { return bf16_to_f32(p[i]); }
+    static __device__ __forceinline__ uint32_t raw(const uint16_t* __restrict__ p, size_t i) { return p[i]; }
+    static __device__ __forceinline__ float cvt(uint32_t b) { return bf16_to_f32(b); }
     static __device__ __forceinline__ void st(uint16_t* __restrict__ p, size_t i, float v) { p[i] = f32_to_bf16(v); }
     static __device__ __forceinline__ void st_nt(uint16_t* __restrict__ p, size_t i, float v) {
         __builtin_nontemporal_store(f32_to_bf16(v), p + i);
@@ -116,6 +127,26 @@ __device__ __forceinline__ float ordered_sum(const float* __restrict__ p, int64_
     }
     for (; r < n; ++r) acc += p[(size_t)r * stride];
     return acc;
+}
+
+// f(integral_constant<0>), ..., f(integral_constant<N-1>): a loop whose index
+// is a compile-time constant in each step
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+// the same, stopping before step n (n <= N, wave-uniform)
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_until_impl(F& f, int n, std::integer_sequence<int, I...>) {
+    (void)((I < n && (f(std::integral_constant<int, I>{}), true)) && ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for_until(F&& f, int n) {
+    static_for_until_impl(f, n, std::make_integer_sequence<int, N>{});
 }
 
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }

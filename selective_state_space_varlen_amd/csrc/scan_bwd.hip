@@ -22,15 +22,18 @@
 // which one forward sweep over the chunk's leading tokens yields. A
 // sequential pass over chunks (right to left) turns these into the carry
 // entering each chunk. The main kernel then walks each chunk backwards in
-// kBB-token blocks (inputs staged through LDS, the next block in flight); each
-// kK-token sub-chunk restarts from the forward's checkpoint at its first token
-// and replays its tokens with their states held in VGPRs before running the
-// reverse step over them. dB and dC (sums over channels) are reduced
-// across each wave and then across the workgroup's waves through LDS, and
-// written per workgroup channel group; dA and dDskip
-// are written per chunk; small kernels finish both sums in a fixed order, so
-// results are deterministic.
+// kSub-token blocks: each block restarts from the forward's checkpoint at its
+// first token and replays its tokens with their states and decays held in
+// VGPRs before running the reverse step over them. A workgroup holds 128
+// channels (two per lane) and splits the states between its waves (layout
+// below); the sums over states are added across waves through LDS, and dB and
+// dC (sums over channels) are added over the lane's two channels in registers
+// and over the wave's lanes through LDS, then written per 128-channel group;
+// dA and dDskip are written per chunk; small kernels finish all sums in a
+// fixed order, so results are deterministic.
 #include "scan_common.h"
+
+#include <type_traits>
 
 namespace ssmp {
 
@@ -256,142 +259,216 @@ struct BwdArgs {
     float* dDpart;
     float* dbpart;
     float* dBC;
+    float* sink;  // lanes with nothing to store write here, so that every path issues the same stores
     int64_t T_;
     int D;
-    int vec;
     int lc;
+    int ckint;  // tokens between the checkpoint slots in ckpt
     ScanOpts opt;
 };
 
-constexpr int kRedStride = kWave + 4;  // LDS row stride (floats) of the dB/dC transpose
+// Layout of the reverse pass. A workgroup covers 128 adjacent channels, two
+// per lane (channels 2l and 2l+1 of its group), and splits the states between
+// its waves: wave q holds states q*NH .. q*NH+NH-1 of every channel, NH =
+// min(N, 4), so SW = N / NH waves cover them all. A wave's registers then hold
+// the states and decays of a whole block's replay, B_t[n] and C_t[n] are the
+// same across the wave, and the lane's two channels add their dB and dC terms
+// in registers before the sums over channels go through LDS.
+template <int NS>
+struct Split {
+    static constexpr int NH = NS < 4 ? NS : 4;
+    static constexpr int SW = NS / NH;
+};
+constexpr int kCl = 2;                     // channels per lane
+constexpr int kGroupCh = kCl * kWave;      // channels per workgroup
 
-// The decays a = exp2(delta A2) of a sub-chunk's replay are kept for its
-// reverse step (32 VGPRs at d_state 16) where the registers allow: with 2-byte
-// inputs the backward's main kernel fits them without spilling, with fp32
-// inputs (larger staging) it would spill, so it computes them again.
-template <typename T>
-constexpr bool kCacheDecay = sizeof(T) == 2;
+// Tokens per block: the backward restarts from a state checkpoint at every
+// block and replays it with its states in registers.
+constexpr int kSub = 4;
 
-// Replay of one kK-token sub-chunk from its entering state h: the states hh[k]
-// after each token, their decays ak[k] (kCacheDecay) and the pre-gate outputs
-// yk[k]. SAFE sub-chunks may be
-// short (ns < kK) and may hold heads; the fast ones are full and head-free.
-// With initial states, a head starts from its sequence's h0 (this lane's
-// share of the states) instead of zero.
-template <bool SAFE, bool XS, bool ST, int NS, int LPC, typename St, typename T>
-__device__ __forceinline__ void bwd_replay(const T* lds, const float* bcl, int kb, int ns, uint32_t heads, int ch,
-                                           int n0, const float (&A2)[NS / LPC], float (&h)[NS / LPC],
-                                           float (&hh)[kK][NS / LPC], float (&ak)[kK][NS / LPC], float (&yk)[kK],
-                                           float (&dtk)[kK], float (&slk)[kK], float Dv, const StepMap& sm,
-                                           const ScanOpts& opt, int64_t tb, int D, int dd) {
-    // on return h holds the state after the last replayed token
-    constexpr int NH = NS / LPC;
-    if constexpr (XS) {
-        // mapped steps and their slopes for the whole sub-chunk (past ns the
-        // staged rows are stale and the results unused). A lane pair shares
-        // its channel: each lane maps every other token and the pair swaps.
-        if constexpr (LPC == 2) {
-            static_assert(kK % 2 == 0, "tokens come in pairs");
-            const bool odd = n0 != 0;
+// Sum of v over groups of G consecutive lanes (G a power of two <= 16); every
+// lane of a group receives the total.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (G >= 2) v += swap_adjacent(v);
+    if constexpr (G >= 4)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+    if constexpr (G >= 8) v += __shfl_xor(v, 4);
+    if constexpr (G >= 16) v += __shfl_xor(v, 8);
+    return v;
+}
+
+// B_t and C_t of a block reach the arithmetic as DPP broadcasts: value j of
+// a 16-value group sits in lane j of every 16-lane row of a VGPR, and
+// row_newbcast:j hands it to all lanes as the first operand of the multiply or
+// FMA that uses it, at no cost. Written as inline assembly because the
+// compiler folds such broadcasts into multiplies only. A VALU write of a DPP
+// source register needs two wait states before the DPP read; the broadcast
+// registers are written by vector loads only, and a block's first read of
+// each starts with s_nop 1 (NOP) in case a copy was placed just before it.
+template <int J, bool NOP = false>
+__device__ __forceinline__ void fmac_bc(float& acc, float src, float x) {
+    if constexpr (NOP)
+        asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+            : "+v"(acc) : "v"(src), "v"(x), "n"(J));
+    else
+        asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(src), "v"(x),
+            "n"(J));
+}
+template <int J, bool NOP = false>
+__device__ __forceinline__ float mul_bc(float src, float x) {
+    float r;
+    if constexpr (NOP)
+        asm("s_nop 1\n\tv_mul_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+            : "=v"(r) : "v"(src), "v"(x), "n"(J));
+    else
+        asm("v_mul_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(src), "v"(x),
+            "n"(J));
+    return r;
+}
+
+// The block's B/C values of one wave: value v = kk*2NH + kind*NH + i (B for
+// kind 0, C for kind 1, state q*NH + i, token tb + kk) in lane v % 16 of the
+// rows of register v / 16.
+template <int NS>
+struct BcRegs {
+    static constexpr int NH = Split<NS>::NH;
+    static constexpr int V = kSub * 2 * NH;
+    static constexpr int R = (V + 15) / 16;
+    float r[R];
+    // bc: fp32 rows [T][2N] (B then C)
+    __device__ __forceinline__ void load(const float* __restrict__ bc, int64_t tb, int64_t T_, int q, int lane) {
+        const int j = lane % 16;
 #pragma unroll
-            for (int j = 0; j < kK / 2; ++j) {
-                float sl_own;
-                const float dt_own = sm.eff(St::get(lds, 1, kb + 2 * j + (odd ? 1 : 0), ch), sl_own);
-                const float dt_oth = swap_adjacent(dt_own), sl_oth = swap_adjacent(sl_own);
-                dtk[2 * j] = odd ? dt_oth : dt_own;
-                dtk[2 * j + 1] = odd ? dt_own : dt_oth;
-                slk[2 * j] = odd ? sl_oth : sl_own;
-                slk[2 * j + 1] = odd ? sl_own : sl_oth;
-            }
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < kK; ++kk) dtk[kk] = sm.eff(St::get(lds, 1, kb + kk, ch), slk[kk]);
+        for (int k = 0; k < R; ++k) {
+            const int v = k * 16 + j;
+            const int kk = v / (2 * NH), kind = (v / NH) % 2, i = v % NH;
+            const int64_t t = tb + kk;
+            r[k] = (v < V && t < T_) ? bc[(size_t)t * 2 * NS + kind * NS + q * NH + i] : 0.0f;
         }
     }
+};
+template <int NS, int KK, int KIND, int I>
+struct BcIdx {
+    static constexpr int v = KK * 2 * Split<NS>::NH + KIND * Split<NS>::NH + I;
+    static constexpr int reg = v / 16, lane = v % 16;
+};
+
+// Row stride (floats) of the per-lane dB/dC terms the sums over channels
+// read: rows of 64 lanes, padded so that the float4 reads of two neighbouring
+// rows by eight lanes fall on different banks.
+constexpr int kXRow = kWave + 16;
+
+// LDS of a backward workgroup
+template <int NS>
+struct BwdShared {
+    static constexpr int NH = Split<NS>::NH, SW = Split<NS>::SW, K = kSub;
+    float4 stp[K][kWave];             // per token, per lane: step and step*u of its two channels
+    float2 gg[K][kWave];              // per token, per lane: g of its two channels
+    float2 part[3][K][SW][kWave];     // per wave: y, sum_n dh B, sum_n A r of the lane's channels
+    float xb[SW][4 * NH][kXRow];      // per wave, a token pair: dB and dC terms of its states
+};
+
+// Replay of a block from the state hin entering its first token: each
+// token's states hh[kk] and decays ak[kk] (per channel of the lane), and this
+// wave's share of y. SAFE blocks may be short (nb < K) or hold heads; fast
+// blocks are neither.
+// The block's per-token values of the lane's two channels (step, step*u, g),
+// read from LDS in one batch so that no token waits on its own read.
+struct TokVals {
+    float dt[kSub][kCl], dtu[kSub][kCl], gg[kSub][kCl];
+};
+
+template <bool SAFE, bool ST, int NS, typename Sh>
+__device__ __forceinline__ void bwd_replay(Sh& sh, const TokVals& tv, const BcRegs<NS>& bc, int nb, uint32_t heads, int lane, int q,
+                                           const bool (&act)[kCl], const float (&A2)[kCl][Split<NS>::NH],
+                                           const float (&hin)[kCl][Split<NS>::NH],
+                                           float (&hh)[kSub][kCl][Split<NS>::NH],
+                                           float (&ak)[kSub][kCl][Split<NS>::NH], const ScanOpts& opt, int64_t tb,
+                                           int D, const int (&dd)[kCl]) {
+    constexpr int NH = Split<NS>::NH, K = kSub;
+    const int n0 = q * NH;
+    float h[kCl][NH];
 #pragma unroll
-    for (int kk = 0; kk < kK; ++kk) {
+    for (int c = 0; c < kCl; ++c)
+#pragma unroll
+        for (int i = 0; i < NH; ++i) h[c][i] = hin[c][i];
+    auto step = [&](auto KKc) {
+        constexpr int kk = decltype(KKc)::value;
+        const float(&dt)[kCl] = tv.dt[kk];
+        const float(&dtu)[kCl] = tv.dtu[kk];
         if constexpr (SAFE) {
-            if (kk >= ns) break;
-        }
-        const int k = kb + kk;
-        const float dt = XS ? dtk[kk] : St::get(lds, 1, k, ch);
-        const float uu = St::get(lds, 0, k, ch);
-        const float dtu = dt * uu;
-        const float* row = bcl + k * 2 * NS + n0;
-        if constexpr (SAFE) {
-            if ((heads >> k) & 1u) {
+            if ((heads >> kk) & 1u) {
                 asm volatile("");
-                if (ST && opt.h0) {
-                    const float* __restrict__ hp =
-                        opt.h0 + ((size_t)seq_of(opt.cu, opt.nseq, tb + k) * D + dd) * NS + n0;
 #pragma unroll
-                    for (int i = 0; i < NH; ++i) h[i] = hp[i];
-                } else {
+                for (int c = 0; c < kCl; ++c) {
+                    if (ST && opt.h0 && act[c]) {
+                        const float* __restrict__ hp =
+                            opt.h0 + ((size_t)seq_of(opt.cu, opt.nseq, tb + kk) * D + dd[c]) * NS + n0;
 #pragma unroll
-                    for (int i = 0; i < NH; ++i) h[i] = 0.0f;
+                        for (int i = 0; i < NH; ++i) h[c][i] = hp[i];
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < NH; ++i) h[c][i] = 0.0f;
+                    }
                 }
             }
         }
-        float y = 0.0f;
+        float y[kCl];
+        auto state = [&](auto Ic) {
+            constexpr int i = decltype(Ic)::value;
+            using Bi = BcIdx<NS, kk, 0, i>;
+            using Ci = BcIdx<NS, kk, 1, i>;
+            constexpr bool first = kk == 0 && i == 0;
 #pragma unroll
-        for (int i = 0; i < NH; ++i) {
-            const float a = exp2_fast(dt * A2[i]);
-            if constexpr (kCacheDecay<T>) ak[kk][i] = a;
-            h[i] = __builtin_fmaf(a, h[i], dtu * row[i]);
-            hh[kk][i] = h[i];
-            y = __builtin_fmaf(row[NS + i], h[i], y);
-        }
-        if constexpr (LPC == 2) y += swap_adjacent(y);
-        yk[kk] = __builtin_fmaf(Dv, uu, y);
-    }
+            for (int c = 0; c < kCl; ++c) {
+                const float a = exp2_fast(dt[c] * A2[c][i]);
+                ak[kk][c][i] = a;
+                const float b = (c == 0) ? mul_bc<Bi::lane, first>(bc.r[Bi::reg], dtu[c])
+                                         : mul_bc<Bi::lane>(bc.r[Bi::reg], dtu[c]);
+                h[c][i] = __builtin_fmaf(a, h[c][i], b);
+                hh[kk][c][i] = h[c][i];
+                if constexpr (i == 0) y[c] = mul_bc<Ci::lane>(bc.r[Ci::reg], h[c][i]);
+                else fmac_bc<Ci::lane>(y[c], bc.r[Ci::reg], h[c][i]);
+            }
+        };
+        static_for<NH>(state);
+        sh.part[0][kk][q][lane] = make_float2(y[0], y[1]);
+    };
+    static_for_until<K>(step, SAFE ? nb : K);
 }
 
-// Per-block outputs: du, ddelta, dz rows (dtype T) and the wave's per-token
-// dB/dC sums (LDS, [kBB][2NS]).
-template <typename T>
-struct BwdRows {
-    T* du;
-    T* ddelta;
-    T* dz;
-    float* dbc;
-};
-
-// Reverse step over one sub-chunk (tokens kb + ns - 1 down to kb).
-template <bool SAFE, bool GATE, bool XS, bool ST, int NS, int LPC, typename St, typename T>
-__device__ __forceinline__ void bwd_reverse(const T* lds, const float* bcl, float (*red)[kRedStride], int kb, int ns,
-                                            uint32_t heads, int lane, int ch, int sh, int n0, bool act, bool full,
-                                            int D, int d, const float (&A2)[NS / LPC], float (&carry)[NS / LPC],
-                                            float (&dA)[NS / LPC], float& dDacc, float Dv,
-                                            const float (&hin)[NS / LPC], const float (&hh)[kK][NS / LPC],
-                                            const float (&ak)[kK][NS / LPC],
-                                            const float (&yk)[kK], const float (&dtk)[kK], const float (&slk)[kK],
-                                            const BwdRows<T>& rows, float gf, float& dbacc, const ScanOpts& opt,
-                                            int64_t tb, int dd) {
-    constexpr int NH = NS / LPC;
-    constexpr int CW = kWave / LPC;
-#pragma unroll
-    for (int kk = kK - 1; kk >= 0; --kk) {
+// Reverse step over the block, a token pair at a time; after each pair, dB
+// (kind 0: sum over channels of dh * step*u) and dC (kind 1: of g * h) of its
+// two tokens. The lane's two channels are added in registers; each value is
+// then added up over the wave's lanes by LPO lanes reading the terms the wave
+// left in LDS.
+template <bool SAFE, bool ST, int NS, typename Sh>
+__device__ __forceinline__ void bwd_reverse(Sh& sh, const TokVals& tv, const BcRegs<NS>& bc, int nb, uint32_t heads, int lane, int q,
+                                            const bool (&act)[kCl], const float (&A2)[kCl][Split<NS>::NH],
+                                            const float (&hin)[kCl][Split<NS>::NH],
+                                            const float (&hh)[kSub][kCl][Split<NS>::NH],
+                                            const float (&ak)[kSub][kCl][Split<NS>::NH],
+                                            float (&carry)[kCl][Split<NS>::NH], float (&dA)[kCl][Split<NS>::NH],
+                                            float* __restrict__ dbc_row, float* __restrict__ sink, const ScanOpts& opt, int64_t tb, int D,
+                                            const int (&dd)[kCl]) {
+    constexpr int NH = Split<NS>::NH, K = kSub;
+    constexpr int LPO = kWave / (4 * NH);  // lanes adding up one dB/dC value of a token pair
+    constexpr int CPL = kWave / LPO;       // lanes' terms each of them adds
+    static_assert(K % 2 == 0 && CPL % 4 == 0, "tiling");
+    const int n0 = q * NH;
+    float* __restrict__ myx = &sh.xb[q][0][0];
+    auto tok = [&](auto KKc) {
+        constexpr int kk = decltype(KKc)::value;
+        constexpr int tk = kk % 2;
         if constexpr (SAFE) {
-            if (kk >= ns) continue;
+            if (kk >= nb) return;
         }
-        const int k = kb + kk;
-        const float dt = XS ? dtk[kk] : St::get(lds, 1, k, ch);
-        const float uu = St::get(lds, 0, k, ch);
-        const float go = St::get(lds, 3, k, ch);
-        float gg = go, dzv = 0.0f;
-        if constexpr (GATE) {
-            const float zz = St::get(lds, 2, k, ch);
-            const float sg = sigmoid_fast(zz);
-            gg = go * __builtin_fmaf(zz, sg, gf);
-            dzv = go * yk[kk] * sg * (1.0f + zz * (1.0f - sg));
-        }
-        gg = act ? gg : 0.0f;  // lanes past D add nothing to dB/dC
-        const float dtu = act ? dt * uu : 0.0f;
-        const float* row = bcl + k * 2 * NS + n0;
-        const int col = sh * CW + ch;
-        float sumB = 0.0f, sumAr = 0.0f;
-        const bool head = SAFE && ((heads >> k) & 1u);
-        if (head) {
+        const float(&dt)[kCl] = tv.dt[kk];
+        const float(&dtu)[kCl] = tv.dtu[kk];
+        const float(&gg)[kCl] = tv.gg[kk];
+        float sumB[kCl], sumAr[kCl] = {0.0f, 0.0f};
+        if (SAFE && ((heads >> kk) & 1u)) {
             asm volatile("");
             // With states, what the decay passes back out of the head is the
             // initial state's gradient, the initial state is the previous
@@ -399,254 +476,341 @@ __device__ __forceinline__ void bwd_reverse(const T* lds, const float* bcl, floa
             // head (the previous sequence's last) is that sequence's
             // final-state gradient.
             const bool st = ST && (opt.h0 || opt.dh0);
-            const int64_t t = tb + k;
-            const size_t so = st ? ((size_t)seq_of(opt.cu, opt.nseq, t) * D + dd) * NS + n0 : 0;
-            const float* __restrict__ gp = (ST && opt.dhT && t > 0)
-                                               ? opt.dhT + ((size_t)seq_of(opt.cu, opt.nseq, t - 1) * D + dd) * NS + n0
-                                               : nullptr;
+            const int64_t t = tb + kk;
+            const int s_here = st ? seq_of(opt.cu, opt.nseq, t) : 0;
+            const int s_prev = (ST && opt.dhT && t > 0) ? seq_of(opt.cu, opt.nseq, t - 1) : 0;
+            auto state = [&](auto Ic) {
+                constexpr int i = decltype(Ic)::value;
+                using Bi = BcIdx<NS, kk, 0, i>;
+                using Ci = BcIdx<NS, kk, 1, i>;
+                float xB = 0.0f, xC = 0.0f;
 #pragma unroll
-            for (int i = 0; i < NH; ++i) {
-                const float dh = __builtin_fmaf(gg, row[NS + i], carry[i]);
-                red[i][col] = dh * dtu;             // dB row
-                red[NH + i][col] = gg * hh[kk][i];  // dC row
-                sumB = __builtin_fmaf(dh, row[i], sumB);
-                if (st) {
-                    const float cr = (kCacheDecay<T> ? ak[kk][i] : exp2_fast(dt * A2[i])) * dh;
-                    if (opt.h0) {
-                        const float r = cr * opt.h0[so + i];
-                        sumAr = __builtin_fmaf(r, A2[i], sumAr);
-                        dA[i] = __builtin_fmaf(r, dt, dA[i]);
+                for (int c = 0; c < kCl; ++c) {
+                    fmac_bc<Ci::lane>(carry[c][i], bc.r[Ci::reg], gg[c]);
+                    const float dh = carry[c][i];
+                    if constexpr (i == 0) sumB[c] = mul_bc<Bi::lane>(bc.r[Bi::reg], dh);
+                    else fmac_bc<Bi::lane>(sumB[c], bc.r[Bi::reg], dh);
+                    xB = __builtin_fmaf(dh, dtu[c], xB);
+                    xC = __builtin_fmaf(gg[c], hh[kk][c][i], xC);
+                    if (st) {
+                        const size_t so = ((size_t)s_here * D + dd[c]) * NS + n0 + i;
+                        const float cr = ak[kk][c][i] * dh;
+                        if (opt.h0) {
+                            const float r = cr * (act[c] ? opt.h0[so] : 0.0f);
+                            sumAr[c] = __builtin_fmaf(r, A2[c][i], sumAr[c]);
+                            dA[c][i] = __builtin_fmaf(r, dt[c], dA[c][i]);
+                        }
+                        if (opt.dh0 && act[c]) opt.dh0[so] = cr;
                     }
-                    if (opt.dh0 && act) opt.dh0[so + i] = cr;
+                    const bool gp = ST && opt.dhT && t > 0 && act[c];
+                    carry[c][i] = gp ? opt.dhT[((size_t)s_prev * D + dd[c]) * NS + n0 + i] : 0.0f;
                 }
-                carry[i] = (gp && act) ? gp[i] : 0.0f;
-            }
+                myx[((tk * 2 + 0) * NH + i) * kXRow + lane] = xB;
+                myx[((tk * 2 + 1) * NH + i) * kXRow + lane] = xC;
+            };
+            static_for<NH>(state);
         } else {
+            auto state = [&](auto Ic) {
+                constexpr int i = decltype(Ic)::value;
+                using Bi = BcIdx<NS, kk, 0, i>;
+                using Ci = BcIdx<NS, kk, 1, i>;
+                constexpr bool first = kk == K - 1 && i == 0;
+                float xB = 0.0f, xC = 0.0f;
 #pragma unroll
-            for (int i = 0; i < NH; ++i) {
-                const float dh = __builtin_fmaf(gg, row[NS + i], carry[i]);
-                red[i][col] = dh * dtu;
-                red[NH + i][col] = gg * hh[kk][i];
-                sumB = __builtin_fmaf(dh, row[i], sumB);
-                // carry to t-1: a_t dh_t; r = dh_t a_t h_{t-1}
-                carry[i] = (kCacheDecay<T> ? ak[kk][i] : exp2_fast(dt * A2[i])) * dh;
-                const float r = carry[i] * (kk == 0 ? hin[i] : hh[kk > 0 ? kk - 1 : 0][i]);
-                sumAr = __builtin_fmaf(r, A2[i], sumAr);
-                dA[i] = __builtin_fmaf(r, dt, dA[i]);
-            }
+                for (int c = 0; c < kCl; ++c) {
+                    // dh = carry + g C, formed in the carry's own register
+                    if (c == 0) fmac_bc<Ci::lane, first>(carry[c][i], bc.r[Ci::reg], gg[c]);
+                    else fmac_bc<Ci::lane>(carry[c][i], bc.r[Ci::reg], gg[c]);
+                    const float dh = carry[c][i];
+                    if constexpr (i == 0) sumB[c] = mul_bc<Bi::lane>(bc.r[Bi::reg], dh);
+                    else fmac_bc<Bi::lane>(sumB[c], bc.r[Bi::reg], dh);
+                    xB = __builtin_fmaf(dh, dtu[c], xB);
+                    xC = __builtin_fmaf(gg[c], hh[kk][c][i], xC);
+                    // carry to t-1: a_t dh_t; r = dh_t a_t h_{t-1}
+                    carry[c][i] = ak[kk][c][i] * dh;
+                    const float r = carry[c][i] * (kk == 0 ? hin[c][i] : hh[kk > 0 ? kk - 1 : 0][c][i]);
+                    sumAr[c] = __builtin_fmaf(r, A2[c][i], sumAr[c]);
+                    dA[c][i] = __builtin_fmaf(r, dt[c], dA[c][i]);
+                }
+                myx[((tk * 2 + 0) * NH + i) * kXRow + lane] = xB;
+                myx[((tk * 2 + 1) * NH + i) * kXRow + lane] = xC;
+            };
+            static_for<NH>(state);
         }
-        if constexpr (LPC == 2) {
-            sumB += swap_adjacent(sumB);
-            sumAr += swap_adjacent(sumAr);
-        }
-        const float duv = __builtin_fmaf(gg, Dv, dt * sumB);
-        float ddv = __builtin_fmaf(uu, sumB, sumAr * kLn2);
-        if constexpr (XS) {
-            ddv *= slk[kk];  // with respect to the stored step
-            dbacc += act ? ddv : 0.0f;
-        }
-        dDacc = __builtin_fmaf(gg, uu, dDacc);
-        // both lanes of a pair hold the same values and store the same bytes
-        const uint32_t e = (uint32_t)(k * D + d);  // < kBB * D, fits 32 bits
-        if (full || act) {
-            Elt<T>::st(rows.du, e, duv);
-            Elt<T>::st(rows.ddelta, e, ddv);
-            if constexpr (GATE) Elt<T>::st(rows.dz, e, dzv);
-        }
-        // dB/dC of state n: the sum of row (n % NH) (dB) or NH + n % NH (dC)
-        // over the columns of share n / NH. Two lanes per output value, each
-        // adding half the columns; both then hold the total.
+        sh.part[1][kk][q][lane] = make_float2(sumB[0], sumB[1]);
+        sh.part[2][kk][q][lane] = make_float2(sumAr[0], sumAr[1]);
+    };
+    auto pair = [&](auto KPc) {
+        constexpr int kp = K / 2 - 1 - decltype(KPc)::value;  // pairs right to left
+        tok(std::integral_constant<int, 2 * kp + 1>{});
+        tok(std::integral_constant<int, 2 * kp>{});
         wave_sync();
-        const int o = lane >> 1, hf = lane & 1;  // output o: kind o / NS, state o % NS
-        constexpr bool all_out = 4 * NS >= kWave;
-        float v = 0.0f;
-        if (all_out || o < 2 * NS) {
-            const int kind = o / NS, n = o % NS;
-            const int rrow = kind * NH + (n % NH);
-            const int c0 = (n / NH) * CW + hf * (CW / 2);
-            const float4* rw = reinterpret_cast<const float4*>(&red[rrow][c0]);
-            float4 r4 = rw[0];
-            v = (r4.x + r4.y) + (r4.z + r4.w);
+        {
+            // the LPO lanes of an output read interleaved float4s: together a
+            // contiguous run, conflict-free
+            const int o = lane / LPO, sl = lane % LPO;
+            const int tk = o / (2 * NH), kind = (o / NH) % 2, i = o % NH;
+            const int kk = 2 * kp + tk;
+            const float4* xv = reinterpret_cast<const float4*>(myx + ((tk * 2 + kind) * NH + i) * kXRow) + sl;
+            float acc = 0.0f;
 #pragma unroll
-            for (int q = 1; q < CW / 8; ++q) {
-                r4 = rw[q];
-                v += (r4.x + r4.y) + (r4.z + r4.w);
+            for (int m = 0; m < CPL / 4; ++m) {
+                const float4 xa = xv[m * LPO];
+                acc += (xa.x + xa.y) + (xa.z + xa.w);
             }
+            acc = group_sum<LPO>(acc);
+            // every lane of the output stores the same value: no lane-dependent branch
+            float* dst = (!SAFE || kk < nb) ? dbc_row + (size_t)kk * 2 * NS + kind * NS + n0 + i : sink + lane;
+            *dst = acc;
         }
-        v += swap_adjacent(v);
-        if (all_out || o < 2 * NS) rows.dbc[(uint32_t)(k * 2 * NS + o)] = v;
         wave_sync();
-    }
+    };
+    static_for<K / 2>(pair);
 }
 
-// LPC lanes share a channel, each holding NS/LPC of its states, so a wave
-// covers 64/LPC channels. Two lanes per channel halve the registers and LDS a
-// wave needs, which lets two or more waves share a SIMD; per-channel sums over
-// the states are completed with one DPP exchange between the lane pair.
-// A workgroup holds WV waves on adjacent channel groups of one chunk: they
-// share the staged B/C rows of each block, and add their per-token dB/dC sums
-// in LDS, so one partial row per WV*64/LPC channels reaches memory.
-template <typename T, int NS, int LPC, int WV, bool GATE, bool XS, bool ST>
-__global__ __launch_bounds__(kWave * WV, 2) void k_scan_bwd_main(BwdArgs<T> p) {
-    constexpr int NH = NS / LPC;      // states per lane
-    constexpr int CW = kWave / LPC;   // channels per wave
-    static_assert(NH * LPC == NS && (LPC == 1 || LPC == 2), "lane split");
-    static_assert(CW * WV >= kWave, "dB/dC partial rows are sized for groups of at least 64 channels");
-    using St = Stager<T, 4, kBB, CW>;  // u, delta, z, dout
-    constexpr int NT = kWave * WV;     // threads
-    constexpr int BCW = 2 * NS;        // dB/dC values per token
-    __shared__ __attribute__((aligned(16))) T lds[WV][St::kElems];
-    __shared__ __attribute__((aligned(16))) float bcl[kBB * BCW];  // B/C rows of the block
-    __shared__ __attribute__((aligned(16))) float red[WV][2 * NH][kRedStride];
-    __shared__ float blk[WV][kBB * BCW];  // per-wave dB/dC sums of the block's tokens
+// The reverse pass over one chunk. Per kSub-token block, right to left:
+//  1. prologue: each wave maps the step, gate and their products for every
+//     SW-th token of the block (its own tokens) and shares them through LDS;
+//  2. replay: every wave runs its states through the block from the
+//     checkpoint at the block start, keeping each token's state and decay;
+//  3. reverse step with the block's dB and dC (bwd_reverse), written as this
+//     channel group's partial rows;
+//  4. epilogue: each wave finishes its own tokens: the per-wave sums over
+//     states (y, sum dh B, sum A r) are added in wave order, and du, ddelta
+//     and dz are stored.
+// Heads reset the replayed state and cut the reverse carry; with carried
+// states, a head starts from its sequence's h0 (replay), passes a * dh out as
+// dh0 and restarts the carry from the previous sequence's dhT (reverse).
+template <typename T, int NS, bool GATE, bool XS, bool ST>
+__global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
+    BwdArgs<T> p, const float* __restrict__ bcp) {
+    constexpr int NH = Split<NS>::NH, SW = Split<NS>::SW, K = kSub, KQ = K / SW;
+    static_assert(K % SW == 0, "tiling");
+    __shared__ __attribute__((aligned(16))) BwdShared<NS> sh;
 
     const int tid = threadIdx.x;
-    const int wv = tid / kWave;
     const int lane = tid % kWave;
-    const int ch = lane / LPC;        // channel within the wave's group
-    const int sh = lane % LPC;        // which share of the states
-    const Tile tl = tile_of_w<CW * WV>(p.D);
-    const int gw = tl.g;              // workgroup channel group
-    const int g = gw * WV + wv;       // wave channel group
-    const int d = g * CW + ch;
-    const bool act = d < p.D;
-    const bool full = (g + 1) * CW <= p.D;
-    const int dd = act ? d : p.D - 1;
-    const int64_t c = tl.c;
-    const int64_t t0 = c * p.lc;
-    const int64_t t1 = (t0 + p.lc < p.T_) ? t0 + p.lc : p.T_;
-    const size_t ND = (size_t)NS * p.D;
-    const int n0 = sh * NH;           // first state of this lane
+    const int q = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int D = p.D;
-    T* const mylds = lds[wv];
-
-    // lanes past D carry zeros throughout, so they add nothing to dB/dC
-    float A2[NH], carry[NH], dA[NH];
+    const int64_t T_ = p.T_;
+    const unsigned ngroup = (unsigned)((D + kGroupCh - 1) / kGroupCh);
+    const int g = (int)(blockIdx.x % ngroup);
+    const int64_t c_ = blockIdx.x / ngroup;
+    int d[kCl], dd[kCl];
+    bool act[kCl];
 #pragma unroll
-    for (int i = 0; i < NH; ++i) {
-        A2[i] = p.A[(size_t)dd * NS + n0 + i] * kLog2e;
-        carry[i] = act ? p.cin[(size_t)c * ND + (size_t)(n0 + i) * D + dd] : 0.0f;
-        dA[i] = 0.0f;
+    for (int c = 0; c < kCl; ++c) {
+        d[c] = g * kGroupCh + kCl * lane + c;
+        act[c] = d[c] < D;
+        dd[c] = act[c] ? d[c] : D - 1;
     }
-    if (ST && p.opt.dhT && act && (t1 == p.T_ || p.pos[t1] == 0)) {
+    const int64_t t0 = c_ * p.lc;
+    const int64_t t1 = (t0 + p.lc < T_) ? t0 + p.lc : T_;
+    const size_t ND = (size_t)NS * D;
+    const int n0 = q * NH;
+
+    float A2[kCl][NH], carry[kCl][NH], dA[kCl][NH];
+#pragma unroll
+    for (int c = 0; c < kCl; ++c)
+#pragma unroll
+        for (int i = 0; i < NH; ++i) {
+            A2[c][i] = p.A[(size_t)dd[c] * NS + n0 + i] * kLog2e;
+            carry[c][i] = act[c] ? p.cin[(size_t)c_ * ND + (size_t)(n0 + i) * D + dd[c]] : 0.0f;
+            dA[c][i] = 0.0f;
+        }
+    if (ST && p.opt.dhT && (t1 == T_ || p.pos[t1] == 0)) {
         // the chunk ends at a sequence's last token (the carry pass hands it
         // zero): it starts from that sequence's final-state gradient
-        const float* __restrict__ gp = p.opt.dhT + ((size_t)seq_of(p.opt.cu, p.opt.nseq, t1 - 1) * D + dd) * NS + n0;
+        const int s = seq_of(p.opt.cu, p.opt.nseq, t1 - 1);
 #pragma unroll
-        for (int i = 0; i < NH; ++i) carry[i] = gp[i];
+        for (int c = 0; c < kCl; ++c)
+            if (act[c]) {
+#pragma unroll
+                for (int i = 0; i < NH; ++i) carry[c][i] = p.opt.dhT[((size_t)s * D + dd[c]) * NS + n0 + i];
+            }
     }
-    const float Dv = (p.Dskip && act) ? p.Dskip[dd] : 0.0f;
-    float dDacc = 0.0f, dbacc = 0.0f;
-    const StepMap sm = step_map(p.opt, dd);
+    float Dv[kCl], dDacc[kCl] = {0.0f, 0.0f}, dbacc[kCl] = {0.0f, 0.0f};
+    StepMap sm[kCl];
+#pragma unroll
+    for (int c = 0; c < kCl; ++c) {
+        Dv[c] = (p.Dskip && act[c]) ? p.Dskip[dd[c]] : 0.0f;
+        sm[c] = step_map(p.opt, dd[c]);
+    }
     const float gf = p.opt.gate_floor;
-    const T* const src[4] = {p.u, p.delta, GATE ? p.z : p.u, p.dout};
 
-    // B/C rows of a block: kBB * 2NS floats, fetched with the block's inputs
-    // by the first BCV threads of the workgroup
-    constexpr int BCV = kBB * BCW / 4;                    // float4 pieces
-    constexpr int BCP = (BCV + NT - 1) / NT;              // pieces per thread
-    float4 bcr[BCP];
-    auto fetch_bc = [&](int64_t tb) {
-        const float* srcf = p.bc + (size_t)tb * BCW;  // 16-byte aligned: tb is a multiple of kBB
-        const float4* srcv = reinterpret_cast<const float4*>(srcf);
-        // floats of the block's rows inside the tensor; with 2N not a multiple
-        // of 4 the last piece can be partial, and is read float by float
-        const int lim = (int)((p.T_ - tb < kBB) ? (p.T_ - tb) : kBB) * BCW;
+    // Inputs of a block, loaded two blocks ahead into one of two buffers
+    // (the block loop is unrolled by two, so neither is ever copied): this
+    // wave's own tokens (every SW-th, from q), raw, for both channels; the
+    // checkpoint at the block start; the block's B/C values.
+    struct Pre {
+        uint32_t ru[KQ][kCl], rd[KQ][kCl], rz[KQ][kCl], rg[KQ][kCl];  // raw bits
+        float hn[kCl][NH];
+        BcRegs<NS> bc;
+        int32_t pos;  // lanes < K: position of token tb + lane (1 past the tensor)
+    };
+    Pre pre[2];
+    auto prefetch = [&](Pre& b, int64_t tb) {
+        // every load is issued on every path (addresses clamped into the
+        // tensors), so the waits for them can count the operations after them
 #pragma unroll
-        for (int q = 0; q < BCP; ++q) {
-            const int idx = q * NT + tid;
-            const int f0 = idx * 4;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (idx < BCV && f0 + 4 <= lim) {
-                v = srcv[idx];
-            } else if (idx < BCV && f0 < lim) {
-                v.x = srcf[f0];
-                if (f0 + 1 < lim) v.y = srcf[f0 + 1];
-                if (f0 + 2 < lim) v.z = srcf[f0 + 2];
+        for (int j = 0; j < KQ; ++j) {
+            const int64_t t = tb + q + j * SW;
+            // uniform row base, 32-bit lane offset
+            const size_t rb = (size_t)(t < T_ ? t : T_ - 1) * D;
+            const T* __restrict__ u_r = p.u + rb;
+            const T* __restrict__ d_r = p.delta + rb;
+            const T* __restrict__ z_r = GATE ? p.z + rb : nullptr;
+            const T* __restrict__ g_r = p.dout + rb;
+#pragma unroll
+            for (int c = 0; c < kCl; ++c) {
+                b.ru[j][c] = Elt<T>::raw(u_r, dd[c]);
+                b.rd[j][c] = Elt<T>::raw(d_r, dd[c]);
+                b.rz[j][c] = GATE ? Elt<T>::raw(z_r, dd[c]) : 0u;
+                b.rg[j][c] = Elt<T>::raw(g_r, dd[c]);
             }
-            bcr[q] = v;
         }
-    };
-    auto commit_bc = [&]() {
+        const float* __restrict__ slot = p.ckpt + (size_t)(tb / p.ckint) * ND;
 #pragma unroll
-        for (int q = 0; q < BCP; ++q) {
-            const int idx = q * NT + tid;
-            if (idx < BCV) reinterpret_cast<float4*>(bcl)[idx] = bcr[q];
+        for (int c = 0; c < kCl; ++c) ck_load<NS, NH>(slot, dd[c], D, n0, true, b.hn[c]);
+        b.bc.load(bcp, tb, T_, q, lane);
+        b.pos = p.pos[(tb + lane < T_) ? tb + lane : T_ - 1];
+    };
+
+    // one block: jb its index in the chunk, b its prefetched inputs, which it
+    // refills with those of block jb - 2
+    auto block = [&](Pre& b, int64_t jb) {
+        const int64_t tb = t0 + jb * K;
+        const int nb = (int)(((tb + K < t1) ? tb + K : t1) - tb);
+        // head flags of the block, from the prefetched positions: bit k for token tb + k
+        const uint32_t heads = (uint32_t)__ballot(lane < K && tb + lane < T_ && b.pos == 0);
+
+        // 1. prologue (own tokens)
+        float eu[KQ][kCl], edt[KQ][kCl], egg[KQ][kCl], esl[KQ][kCl], esg[KQ][kCl], ez[KQ][kCl], eg[KQ][kCl];
+#pragma unroll
+        for (int j = 0; j < KQ; ++j) {
+            const int kk = q + j * SW;
+            float dtv[kCl], dtu[kCl], ggv[kCl];
+#pragma unroll
+            for (int c = 0; c < kCl; ++c) {
+                const bool v = act[c] && kk < nb;
+                const float rdv = Elt<T>::cvt(b.rd[j][c]), rzv = Elt<T>::cvt(b.rz[j][c]);
+                const float rgv = Elt<T>::cvt(b.rg[j][c]);
+                float sl = 1.0f;
+                float dt = XS ? sm[c].eff(rdv, sl) : rdv;
+                dt = v ? dt : 0.0f;  // lanes past D and tokens past the block replay zeros
+                const float uu = v ? Elt<T>::cvt(b.ru[j][c]) : 0.0f;
+                float gg = rgv, sg = 0.0f;
+                if constexpr (GATE) {
+                    sg = sigmoid_fast(rzv);
+                    gg *= __builtin_fmaf(rzv, sg, gf);
+                }
+                gg = v ? gg : 0.0f;
+                dtv[c] = dt; dtu[c] = dt * uu; ggv[c] = gg;
+                eu[j][c] = uu; edt[j][c] = dt; egg[j][c] = gg; esl[j][c] = sl; esg[j][c] = sg;
+                ez[j][c] = rzv; eg[j][c] = rgv;
+            }
+            sh.stp[kk][lane] = make_float4(dtv[0], dtu[0], dtv[1], dtu[1]);
+            sh.gg[kk][lane] = make_float2(ggv[0], ggv[1]);
         }
-    };
-
-    // Each sub-chunk restarts from the checkpoint at its first token; the
-    // next sub-chunk's state (kK tokens earlier) is loaded while this one runs.
-    auto load_state = [&](int64_t ts, float (&hs)[NH]) {
-        ck_load<NS, NH>(p.ckpt + (size_t)(ts / kCK) * ND, dd, D, n0, act, hs);
-    };
-
-    const int64_t nblk = (t1 - t0 + kBB - 1) / kBB;
-    St st;
-    float hn[NH];
-    {
-        const int64_t tl0 = t0 + (nblk - 1) * kBB;
-        st.fetch(src, tl0, p.T_, D, g, lane, p.vec);
-        fetch_bc(tl0);
-        load_state(tl0 + ((t1 - tl0 - 1) / kK) * kK, hn);  // last sub-chunk of the chunk
-    }
-    for (int64_t jb = nblk - 1; jb >= 0; --jb) {
-        const int64_t tb0 = t0 + jb * kBB;
-        const int nb = (int)(((tb0 + kBB < t1) ? tb0 + kBB : t1) - tb0);  // tokens in this block
-        const int nsub = (nb + kK - 1) / kK;
-        const uint32_t heads = block_heads<kBB>(p.pos, tb0, p.T_, lane);
-        __syncthreads();  // every wave is done with the previous block's bcl and blk
-        st.commit(mylds, src, tb0, p.T_, D, g, lane, p.vec);
-        commit_bc();
         __syncthreads();
-        if (jb > 0) {
-            st.fetch(src, tb0 - kBB, p.T_, D, g, lane, p.vec);
-            fetch_bc(tb0 - kBB);
-        }
-        const BwdRows<T> rows{p.du + (size_t)tb0 * D, p.ddelta + (size_t)tb0 * D,
-                              GATE ? p.dz + (size_t)tb0 * D : nullptr, blk[wv]};
 
-        for (int sc = nsub - 1; sc >= 0; --sc) {
-            const int kb = sc * kK;  // first token of the sub-chunk within the block
-            const int ns = (nb - kb < kK) ? nb - kb : kK;
-            float h[NH], hin[NH], hh[kK][NH], ak[kK][NH], yk[kK], dtk[kK], slk[kK];
+        // 2-3. replay from the checkpoint at tb, then the reverse step
+        float hh[K][kCl][NH], ak[K][kCl][NH];
+        TokVals tv;
 #pragma unroll
-            for (int i = 0; i < NH; ++i) {
-                h[i] = hn[i];
-                hin[i] = hn[i];
-            }
-            if (tb0 + kb - kK >= t0) load_state(tb0 + kb - kK, hn);
-            const uint32_t sub_heads = (heads >> kb) & ((1u << kK) - 1u);
-            if (sub_heads == 0 && ns == kK) {
-                bwd_replay<false, XS, ST, NS, LPC, St>(mylds, bcl, kb, kK, 0u, ch, n0, A2, h, hh, ak, yk, dtk, slk, Dv,
-                                                       sm, p.opt, tb0, D, dd);
-                bwd_reverse<false, GATE, XS, ST, NS, LPC, St>(mylds, bcl, red[wv], kb, kK, 0u, lane, ch, sh, n0, act,
-                                                              full, D, d, A2, carry, dA, dDacc, Dv, hin, hh, ak, yk,
-                                                              dtk, slk, rows, gf, dbacc, p.opt, tb0, dd);
-            } else {
-                bwd_replay<true, XS, ST, NS, LPC, St>(mylds, bcl, kb, ns, heads, ch, n0, A2, h, hh, ak, yk, dtk, slk,
-                                                      Dv, sm, p.opt, tb0, D, dd);
-                bwd_reverse<true, GATE, XS, ST, NS, LPC, St>(mylds, bcl, red[wv], kb, ns, heads, lane, ch, sh, n0, act,
-                                                             full, D, d, A2, carry, dA, dDacc, Dv, hin, hh, ak, yk,
-                                                             dtk, slk, rows, gf, dbacc, p.opt, tb0, dd);
-            }
+        for (int kk = 0; kk < K; ++kk) {
+            const float4 st = sh.stp[kk][lane];
+            const float2 g2 = sh.gg[kk][lane];
+            tv.dt[kk][0] = st.x; tv.dtu[kk][0] = st.y; tv.dt[kk][1] = st.z; tv.dtu[kk][1] = st.w;
+            tv.gg[kk][0] = g2.x; tv.gg[kk][1] = g2.y;
         }
-
-        // the workgroup's dB/dC sums of the block, waves added in order
+        float* __restrict__ dbc_row = p.dBC + ((size_t)g * T_ + tb) * 2 * NS;
+        if (heads == 0 && nb == K) {
+            bwd_replay<false, ST, NS>(sh, tv, b.bc, nb, heads, lane, q, act, A2, b.hn, hh, ak, p.opt, tb, D, dd);
+            bwd_reverse<false, ST, NS>(sh, tv, b.bc, nb, heads, lane, q, act, A2, b.hn, hh, ak, carry, dA, dbc_row, p.sink, p.opt,
+                                       tb, D, dd);
+        } else {
+            bwd_replay<true, ST, NS>(sh, tv, b.bc, nb, heads, lane, q, act, A2, b.hn, hh, ak, p.opt, tb, D, dd);
+            bwd_reverse<true, ST, NS>(sh, tv, b.bc, nb, heads, lane, q, act, A2, b.hn, hh, ak, carry, dA, dbc_row, p.sink, p.opt,
+                                      tb, D, dd);
+        }
+        prefetch(b, tb >= t0 + 2 * K ? tb - 2 * K : t0);  // past the chunk start: a dummy reload
         __syncthreads();
-        float* const dst = p.dBC + ((size_t)gw * p.T_ + tb0) * BCW;
-        for (int e = tid; e < nb * BCW; e += NT) {
-            float v = blk[0][e];
+
+        // 4. epilogue (own tokens)
 #pragma unroll
-            for (int w = 1; w < WV; ++w) v += blk[w][e];
-            dst[e] = v;
+        for (int j = 0; j < KQ; ++j) {
+            const int kk = q + j * SW;
+            const bool tok = kk < nb;  // tokens past the block store to the sink
+            float2 y = make_float2(0.0f, 0.0f), sB = y, sA = y;
+#pragma unroll
+            for (int w = 0; w < SW; ++w) {
+                const float2 a = sh.part[0][kk][w][lane], bb = sh.part[1][kk][w][lane], cc = sh.part[2][kk][w][lane];
+                y.x += a.x; y.y += a.y;
+                sB.x += bb.x; sB.y += bb.y;
+                sA.x += cc.x; sA.y += cc.y;
+            }
+            const float yv[kCl] = {y.x, y.y}, sBv[kCl] = {sB.x, sB.y}, sAv[kCl] = {sA.x, sA.y};
+            const size_t rb = (size_t)(tok ? tb + kk : 0) * D;
+            T* __restrict__ sinkT = reinterpret_cast<T*>(p.sink);
+#pragma unroll
+            for (int c = 0; c < kCl; ++c) {
+                const float uu = eu[j][c];
+                const float yy = __builtin_fmaf(Dv[c], uu, yv[c]);
+                const float duv = __builtin_fmaf(egg[j][c], Dv[c], edt[j][c] * sBv[c]);
+                float ddv = __builtin_fmaf(uu, sBv[c], sAv[c] * kLn2);
+                if constexpr (XS) {
+                    ddv *= esl[j][c];  // with respect to the stored step
+                    dbacc[c] += (tok && act[c]) ? ddv : 0.0f;
+                }
+                dDacc[c] = __builtin_fmaf(egg[j][c], uu, dDacc[c]);
+                const bool w = tok && act[c];
+                Elt<T>::st(w ? p.du + rb : sinkT, w ? d[c] : 0, duv);
+                Elt<T>::st(w ? p.ddelta + rb : sinkT, w ? d[c] : 1, ddv);
+                if constexpr (GATE) {
+                    const float sg = esg[j][c], zz = ez[j][c];
+                    Elt<T>::st(w ? p.dz + rb : sinkT, w ? d[c] : 2, eg[j][c] * yy * sg * (1.0f + zz * (1.0f - sg)));
+                }
+            }
         }
+    };
+
+    const int64_t nblk = (t1 - t0 + K - 1) / K;
+    prefetch(pre[0], t0 + (nblk - 1) * K);
+    prefetch(pre[1], nblk >= 2 ? t0 + (nblk - 2) * K : t0);
+    int64_t jb = nblk - 1;
+    for (; jb >= 1; jb -= 2) {
+        block(pre[0], jb);
+        block(pre[1], jb - 1);
     }
-    if (act) {
+    if (jb == 0) block(pre[0], 0);
+
+    // per-chunk partial sums: dA per state; dD and d bias added over the waves in order
 #pragma unroll
-        for (int i = 0; i < NH; ++i) p.dApart[(size_t)c * ND + (size_t)(n0 + i) * D + d] = dA[i];
-        if (sh == 0) p.dDpart[(size_t)c * D + d] = dDacc;
-        if (XS && sh == 0) p.dbpart[(size_t)c * D + d] = dbacc;
+    for (int c = 0; c < kCl; ++c)
+        if (act[c]) {
+#pragma unroll
+            for (int i = 0; i < NH; ++i) p.dApart[(size_t)c_ * ND + (size_t)(n0 + i) * D + d[c]] = dA[c][i];
+        }
+    __syncthreads();
+    sh.part[0][0][q][lane] = make_float2(dDacc[0], dDacc[1]);
+    sh.part[1][0][q][lane] = make_float2(dbacc[0], dbacc[1]);
+    __syncthreads();
+    if (q == 0) {
+        float2 sD = make_float2(0.0f, 0.0f), sb = sD;
+#pragma unroll
+        for (int w = 0; w < SW; ++w) {
+            const float2 a = sh.part[0][0][w][lane], b = sh.part[1][0][w][lane];
+            sD.x += a.x; sD.y += a.y;
+            sb.x += b.x; sb.y += b.y;
+        }
+        const float sDv[kCl] = {sD.x, sD.y}, sbv[kCl] = {sb.x, sb.y};
+#pragma unroll
+        for (int c = 0; c < kCl; ++c)
+            if (act[c]) {
+                p.dDpart[(size_t)c_ * D + d[c]] = sDv[c];
+                if (XS) p.dbpart[(size_t)c_ * D + d[c]] = sbv[c];
+            }
     }
 }
 
@@ -717,16 +881,15 @@ static int scan_bwd_launch(const void* u, const void* delta, const float* A, con
     a.u = (const T*)u; a.delta = (const T*)delta; a.A = A; a.bc = ws + L.bc; a.Dskip = Dskip;
     a.z = (const T*)z; a.dout = (const T*)dout; a.pos = pos; a.ckpt = ws + L.ckpt; a.cin = ws + L.cin;
     a.du = (T*)du; a.ddelta = (T*)ddelta; a.dz = (T*)dz; a.dApart = ws + L.dApart; a.dDpart = ws + L.dDpart;
-    a.dbpart = ws + L.dbpart; a.dBC = ws + L.dBC; a.T_ = T_; a.D = D; a.vec = vec; a.lc = lc; a.opt = opt;
-    constexpr int LPC = NS >= 4 ? 2 : 1;  // bwd_lanes_per_channel
-    constexpr int WV = bwd_waves_per_group(sizeof(T));
-    const int64_t ngroup = bwd_bc_groups(D, NS, sizeof(T));
+    a.dbpart = ws + L.dbpart; a.dBC = ws + L.dBC; a.sink = ws + L.sink; a.T_ = T_; a.D = D; a.lc = lc; a.ckint = kCK; a.opt = opt;
+    constexpr int SW = Split<NS>::SW;
+    const int64_t ngroup = (D + kGroupCh - 1) / kGroupCh;
     const dim3 mgrid((unsigned)(ngroup * nchunk));
     const bool xs = opt.delta_bias != nullptr || opt.softplus != 0;
     // sequence states get kernels of their own, so the reset-only ones keep
     // their register allocation
     const bool st = opt.h0 != nullptr || opt.dhT != nullptr || opt.dh0 != nullptr;
-#define SSMP_BWD_MAIN(G, X, S) k_scan_bwd_main<T, NS, LPC, WV, G, X, S><<<mgrid, kWave * WV, 0, s>>>(a)
+#define SSMP_BWD_MAIN(G, X, S) k_scan_bwd_main<T, NS, G, X, S><<<mgrid, kWave * SW, 0, s>>>(a, ws + L.bc)
 #define SSMP_BWD_MAIN_S(G, X)               \
     if (st) SSMP_BWD_MAIN(G, X, true);      \
     else SSMP_BWD_MAIN(G, X, false)

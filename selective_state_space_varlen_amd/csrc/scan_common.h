@@ -23,17 +23,9 @@ constexpr int kLCMin = 64, kLCMax = 2048;
 constexpr int64_t kMinWaves = 8192;  // eight per SIMD on 256 CUs: enough to hide load latency
 static_assert(kK == kCK && kBB % kK == 0 && kLCMin % kBB == 0, "tiling");
 
-// channels per wave: the forward gives each channel one lane; the backward
-// two lanes (d_state >= 4) or one
-inline int bwd_lanes_per_channel(int N) { return N >= 4 ? 2 : 1; }
-// waves per backward workgroup: four for 2-byte inputs; two for fp32, whose
-// larger staging tiles would otherwise leave one workgroup per CU
-constexpr int bwd_waves_per_group(size_t elt_bytes) { return elt_bytes == 2 ? 4 : 2; }
-// channel groups of the backward's dB/dC partial rows (at most ceil(D/64))
-inline int64_t bwd_bc_groups(int D, int N, size_t elt_bytes) {
-    const int64_t cw = (int64_t)(kWave / bwd_lanes_per_channel(N)) * bwd_waves_per_group(elt_bytes);
-    return (D + cw - 1) / cw;
-}
+// waves per backward workgroup: each holds min(N, 4) of the states of the
+// workgroup's 128 channels
+inline int bwd_waves(int N) { return N / (N < 4 ? N : 4); }
 
 inline int scan_chunk_len(int64_t T, int D, int chw) {
     const int64_t ng = (D + chw - 1) / chw;
@@ -42,7 +34,7 @@ inline int scan_chunk_len(int64_t T, int D, int chw) {
     return lc;
 }
 inline int fwd_chunk_len(int64_t T, int D) { return scan_chunk_len(T, D, kWave); }
-inline int bwd_chunk_len(int64_t T, int D, int N) { return scan_chunk_len(T, D, kWave / bwd_lanes_per_channel(N)); }
+inline int bwd_chunk_len(int64_t T, int D, int N) { return scan_chunk_len(T, D, 2 * kWave / bwd_waves(N)); }
 // The backward's reverse-carry summaries run over sub-chunks of the main
 // kernel's chunks (down to kLCMin tokens): a summary wave's work depends on
 // where the heads fall, and more, shorter waves even it out across the SIMDs.
@@ -204,6 +196,7 @@ struct ScanWs {
     size_t dDpart;    // [nchunk][D]
     size_t dbpart;    // [nchunk][D]      backward: step-bias gradient partials
     size_t dBC;       // [<= ceil(D/64)][T][2N]  per channel-group partial sums of dB, dC
+    size_t sink;      // [64] target of stores by lanes with nothing to store (kept branch-free)
     size_t total;     // floats
 };
 
@@ -232,7 +225,8 @@ inline ScanWs scan_ws_layout(int64_t T, int D, int N) {
     w.dDpart = up(w.dApart + (size_t)w.nchunk * ND);
     w.dbpart = up(w.dDpart + (size_t)w.nchunk * D);
     w.dBC = up(w.dbpart + (size_t)w.nchunk * D);
-    const size_t bwd_end = up(w.dBC + (size_t)((D + kWave - 1) / kWave) * (size_t)T * 2 * N);
+    w.sink = up(w.dBC + (size_t)((D + kWave - 1) / kWave) * (size_t)T * 2 * N);
+    const size_t bwd_end = up(w.sink + 64);
     w.total = fwd_end > bwd_end ? fwd_end : bwd_end;
     return w;
 }
