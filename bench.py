@@ -27,14 +27,17 @@ if ROOT not in sys.path:
 import synth  # noqa: E402
 
 COPY_CALIB_BYTES = 1 << 30
-PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, vendor figure
-PEAK_FP32_TFLOPS = 157.3  # MI355X fp32 vector, vendor figure (counts packed FP32, which this build does not use)
+PEAK_HBM_GBS = 8000.0    # MI355X HBM3E, vendor figure
+# MI355X fp32 vector peak without packed-FP32 instructions (256 CUs x 4 SIMD16
+# x 2 FLOP per FMA x 2.4 GHz); the vendor's 157.3 TFLOP/s counts packed FP32,
+# which this build does not emit
+PEAK_FP32_TFLOPS = 78.6
 
-# Floating-point operations of the scan backward per (token, channel, state),
-# FMA = 2: the forward recompute (delta*A, exp, delta*u*B, state FMA = 5), y for
-# dz (2), and the reverse step (dh 2, dB and dC products plus their sums over
-# channels 4, sum dh*B 2, r = dh*(h - delta*u*B) 2, sum A*r 2, dA 2, carry 1).
-SCAN_BWD_FLOPS_PER_TDN = 22
+# Floating-point operations of the scan backward's own arithmetic per (token,
+# channel, state), FMA = 2, without the forward recompute the implementation
+# adds: dh 2, the dB and dC products and their sums over channels 4, sum dh*B 2,
+# r = dh*a*h_prev 2, sum A*r 2, dA 2, carry a*dh 1.
+SCAN_BWD_FLOPS_PER_TDN = 15
 
 # Algorithmic bytes (each operator reads its inputs once and writes its
 # outputs once; bf16 (T, D) tensors, bf16 B/C rows, fp32 dB/dC rows, int32
@@ -345,6 +348,34 @@ def cpu_baseline(inp: synth.Inputs, channels: int, threads: int) -> dict:
                                    f"{inp.D}/{ch1}"}}
 
 
+def workload_figures(wl_id: int, steps: int, warmup: int) -> dict:
+    """Per-pass times, tokens/s and algorithmic HBM rates of another workload
+    on the same calls (forward: indices, conv, scan; backward: scan, conv)."""
+    inp = synth.make_inputs(wl_id, with_dout=True)
+    T, D, N = inp.T, inp.D, inp.N
+    wl = Workload(inp)
+    total_ms, ops = time_steps(wl, steps, warmup, per_op=True)
+    ab = algo_bytes(T, D, N)
+    fwd_b = ab["pack_indices"] + ab["conv_fwd"] + ab["scan_fwd"]
+    bwd_b = ab["scan_bwd"] + ab["conv_bwd"]
+    fwd_ms = float(np.median(wl.pass_ms["fwd"]))
+    bwd_ms = float(np.median(wl.pass_ms["bwd"]))
+    step_ms = total_ms / steps
+    out = {"workload": synth.NAMES[wl_id], "tokens": T, "d_inner": D, "sequences": inp.nseq, "steps": steps,
+           "step_ms": round(step_ms, 4), "tokens_per_s": round(T / (step_ms * 1e-3), 1),
+           "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+           "fwd_tokens_per_s": round(T / (fwd_ms * 1e-3), 1), "bwd_tokens_per_s": round(T / (bwd_ms * 1e-3), 1),
+           "fwd_algo_gbs": round(fwd_b / (fwd_ms * 1e-3) / 1e9, 1), "bwd_algo_gbs": round(bwd_b / (bwd_ms * 1e-3) / 1e9, 1),
+           "step_algo_gbs": round(sum(ab.values()) / (step_ms * 1e-3) / 1e9, 1),
+           "ops_ms": {k: round(v, 4) for k, v in ops.items()}}
+    out["fwd_hbm_frac"] = round(out["fwd_algo_gbs"] / PEAK_HBM_GBS, 4)
+    out["bwd_hbm_frac"] = round(out["bwd_algo_gbs"] / PEAK_HBM_GBS, 4)
+    out["hbm_frac"] = round(out["step_algo_gbs"] / PEAK_HBM_GBS, 4)
+    del wl
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_ceiling(nbytes: int = 1 << 30, reps: int = 10) -> float:
     """GB/s (read + write) of a plain device-to-device copy of nbytes, the
     practical HBM ceiling beside the 8 TB/s vendor peak."""
@@ -371,6 +402,8 @@ def main():
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4])
     ap.add_argument("--no-layouts", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the figures of the d_inner 1536 and long-pack workloads")
     ap.add_argument("--cpu-channels", type=int, default=4096,
                     help="channels of the workload the oracle baseline runs (all of them by default)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -403,20 +436,20 @@ def main():
     hbm_gbs = step_bytes / (ms_step * 1e-3) / 1e9
     ops_gbs = {k: ab[k] / (ops[k] * 1e-3) / 1e9 for k in OPS}
     dominant = max(OPS, key=lambda k: ops[k])
+    # HBM roofline of the dominant library call (all its launches), the
+    # headline; its arithmetic view beside it
+    roofline = {"kernel": f"{dominant} (the library call, all its launches)", "bound": "hbm",
+                "achieved": round(ops_gbs[dominant], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ops_gbs[dominant] / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic(dominant) if (T, D, N) == (32768, 4096, 16) else None,
+                "avg_ms": round(ops[dominant], 4), "algo_bytes_per_launch": ab[dominant]}
     if dominant == "scan_bwd":
-        # ALU-bound: its minimal arithmetic takes longer than its bytes at peak
         flops = SCAN_BWD_FLOPS_PER_TDN * T * D * N
         ach = flops / (ops[dominant] * 1e-3) / 1e12
-        roofline = {"kernel": "selective_scan_pack_bwd (6 launches)", "bound": "alu", "achieved": round(ach, 2),
-                    "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_FP32_TFLOPS, 4),
-                    "traffic": measured_traffic("scan_bwd") if (T, D, N) == (32768, 4096, 16) else None, "avg_ms": round(ops[dominant], 4), "algo_flops_per_launch": flops,
-                    "hbm_view": {"achieved": round(ops_gbs[dominant], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                 "frac": round(ops_gbs[dominant] / PEAK_HBM_GBS, 4),
-                                 "algo_bytes_per_launch": ab[dominant]}}
-    else:
-        roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(ops_gbs[dominant], 1),
-                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ops_gbs[dominant] / PEAK_HBM_GBS, 4),
-                    "traffic": None, "avg_ms": round(ops[dominant], 4), "algo_bytes_per_launch": ab[dominant]}
+        roofline["alu_view"] = {"achieved": round(ach, 2), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                                "frac": round(ach / PEAK_FP32_TFLOPS, 4), "flops_per_launch": flops,
+                                "flop_count": "the backward's own arithmetic, 15 FLOP per (t, d, n), FMA = 2, "
+                                              "no forward recompute; peak without packed FP32"}
     log("[bench] per-op ms: " + ", ".join(f"{k} {ops[k]:.3f}" for k in OPS))
     log("[bench] per-op algorithmic GB/s: " + ", ".join(f"{k} {ops_gbs[k]:.0f}" for k in OPS))
 
@@ -438,6 +471,16 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: {COPY_CALIB_BYTES} bytes read, {COPY_CALIB_BYTES} bytes written")
         del src, evict, dst
+
+    workloads = None
+    if not args.no_workloads:
+        workloads = {}
+        for w in (1, 3):
+            if w == wl_id:
+                continue
+            log(f"[bench] workload {w} ({synth.NAMES[w]})")
+            workloads[synth.NAMES[w]] = workload_figures(w, max(3, args.steps // 2), 2)
+            log(f"[bench]   {workloads[synth.NAMES[w]]}")
 
     layouts = None
     if not args.no_layouts:
@@ -490,10 +533,14 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        threads = min(16, os.cpu_count() or 1)
+        # every host core the machine reports (os.cpu_count()); the cores this
+        # process may run on are reported beside it
+        threads = os.cpu_count() or 1
         ch = min(args.cpu_channels, D)
         log(f"[bench] oracle baseline on {ch} channels, {threads} threads")
         cpu = cpu_baseline(inp, ch, threads)
+        cpu["host_cpu_count"] = os.cpu_count()
+        cpu["affinity_cpus"] = len(os.sched_getaffinity(0))
 
     line = {
         "metric": "packed tokens/s + HBM GB/s (% peak), conv1d_pack+scan fwd/bwd, 1.4B shape",
@@ -512,6 +559,12 @@ def main():
                    "packs": spec.n_packs, "pack_len": spec.pack_len, "tokens": T, "sequences": inp.nseq,
                    "state_dtype": "fp32"},
         "passes_ms": passes,
+        "fwd_tokens_per_s": round(T / (passes["fwd"]["median"] * 1e-3), 1),
+        "fwd_hbm_frac": round((ab["pack_indices"] + ab["conv_fwd"] + ab["scan_fwd"]) / (passes["fwd"]["median"] * 1e-3)
+                              / 1e9 / PEAK_HBM_GBS, 4),
+        "bwd_hbm_frac": round((ab["scan_bwd"] + ab["conv_bwd"]) / (passes["bwd"]["median"] * 1e-3) / 1e9
+                              / PEAK_HBM_GBS, 4),
+        "other_workloads": workloads,
         "hbm_gbs": round(hbm_gbs, 1),
         "hbm_copy_ceiling_gbs": None if copy_gbs is None else round(copy_gbs, 1),
         "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),

@@ -384,6 +384,15 @@ __device__ __forceinline__ float ctx_input(const T* __restrict__ x, const T* __r
     return Elt<T>::ld(ctx, ((size_t)s * (W - 1) + (size_t)(i - (a - (W - 1)))) * D + d);
 }
 
+// Token range [a, e) of sequence s, clamped into [0, T] with e >= a: with an
+// invalid device cu_seqlens (reported by varlen_pack_indices' dev_err) the
+// context kernels still only touch rows of the tensors.
+__device__ __forceinline__ void seq_range(const int32_t* __restrict__ cu, int s, int64_t T_, int64_t& a, int64_t& e) {
+    const int64_t a0 = cu[s], e0 = cu[s + 1];
+    a = a0 < 0 ? 0 : (a0 > T_ ? T_ : a0);
+    e = e0 < a ? a : (e0 > T_ ? T_ : e0);
+}
+
 // forward: outputs of each sequence's first W-1 tokens with the context (ctx
 // non-null), and the context each sequence hands on (ctx_out non-null):
 // ctx_out[s][j] = input e - (W-1) + j of the extended input (e = cu[s+1])
@@ -391,11 +400,12 @@ template <typename T, int W>
 __global__ __launch_bounds__(256) void k_conv_fwd_context(const T* __restrict__ x, const float* __restrict__ w,
                                                           const float* __restrict__ b, const int32_t* __restrict__ cu,
                                                           int nseq, const T* __restrict__ ctx, T* __restrict__ u,
-                                                          T* __restrict__ ctx_out, int D, int silu) {
+                                                          T* __restrict__ ctx_out, int64_t T_, int D, int silu) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (int64_t)nseq * D) return;
     const int s = (int)(i / D), d = (int)(i % D);
-    const int64_t a = cu[s], e = cu[s + 1];
+    int64_t a, e;
+    seq_range(cu, s, T_, a, e);
     if (ctx) {
         float wk[W];
 #pragma unroll
@@ -427,12 +437,13 @@ template <typename T, int W>
 __global__ __launch_bounds__(256) void k_conv_bwd_context(
     const T* __restrict__ x, const float* __restrict__ w, const float* __restrict__ b,
     const int32_t* __restrict__ cu, int nseq, const T* __restrict__ ctx, const T* __restrict__ du,
-    const T* __restrict__ dctx_out, T* __restrict__ dx, T* __restrict__ dctx, float* __restrict__ part, int D,
-    int silu) {
+    const T* __restrict__ dctx_out, T* __restrict__ dx, T* __restrict__ dctx, float* __restrict__ part, int64_t T_,
+    int D, int silu) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (int64_t)nseq * D) return;
     const int s = (int)(i / D), d = (int)(i % D);
-    const int64_t a = cu[s], e = cu[s + 1];
+    int64_t a, e;
+    seq_range(cu, s, T_, a, e);
     float wk[W];
 #pragma unroll
     for (int k = 0; k < W; ++k) wk[k] = w[(size_t)d * W + (W - 1 - k)];
@@ -506,12 +517,13 @@ static bool vec_ok(const void* p, int D, int V, size_t elt) {
 
 template <typename T>
 static int launch_fwd_context(const void* x, const float* w, const float* b, const int32_t* cu, int nseq,
-                              const void* ctx, void* u, void* ctx_out, int D, int W, int silu, hipStream_t s) {
+                              const void* ctx, void* u, void* ctx_out, int64_t T_, int D, int W, int silu,
+                              hipStream_t s) {
     const int64_t n = (int64_t)nseq * D;
     const unsigned blocks = (unsigned)((n + 255) / 256);
 #define SSMP_CONV_CTX(WX)                                                                                        \
     k_conv_fwd_context<T, WX><<<blocks, 256, 0, s>>>((const T*)x, w, b, cu, nseq, (const T*)ctx, (T*)u,          \
-                                                     (T*)ctx_out, D, silu)
+                                                     (T*)ctx_out, T_, D, silu)
     switch (W) {
         case 1: return SSMP_OK;  // no look-back, no context
         case 2: SSMP_CONV_CTX(2); break;
@@ -526,12 +538,12 @@ static int launch_fwd_context(const void* x, const float* w, const float* b, con
 template <typename T>
 static int launch_bwd_context(const void* x, const float* w, const float* b, const int32_t* cu, int nseq,
                               const void* ctx, const void* du, const void* dctx_out, void* dx, void* dctx,
-                              float* part, int D, int W, int silu, hipStream_t s) {
+                              float* part, int64_t T_, int D, int W, int silu, hipStream_t s) {
     const int64_t n = (int64_t)nseq * D;
     const unsigned blocks = (unsigned)((n + 255) / 256);
 #define SSMP_CONV_CTX(WX)                                                                                        \
     k_conv_bwd_context<T, WX><<<blocks, 256, 0, s>>>((const T*)x, w, b, cu, nseq, (const T*)ctx, (const T*)du,   \
-                                                     (const T*)dctx_out, (T*)dx, (T*)dctx, part, D, silu)
+                                                     (const T*)dctx_out, (T*)dx, (T*)dctx, part, T_, D, silu)
     switch (W) {
         case 1: return SSMP_OK;
         case 2: SSMP_CONV_CTX(2); break;
@@ -608,7 +620,7 @@ static int launch_bwd(const void* x, const float* w, const float* b, const int32
     SSMP_LAUNCH_CHECK();
     if (cu) {
         const int st = launch_bwd_context<T>(x, w, b, cu, nseq, ctx, du, dctx_out, dx, dctx,
-                                             extra_rows ? part + (size_t)ngrp * 5 * D : nullptr, D, W, silu, s);
+                                             extra_rows ? part + (size_t)ngrp * 5 * D : nullptr, T_, D, W, silu, s);
         if (st) return st;
     }
     k_conv_bwd_reduce<<<(unsigned)((5 * (int64_t)D + 255) / 256), 256, 0, s>>>(part, ngrp + extra_rows, D, W, dw,
@@ -662,9 +674,9 @@ extern "C" int conv1d_pack_fwd_states(const void* x, const float* w, const float
     }
     if (!states) return SSMP_OK;
     return dtype == SSMP_BF16 ? launch_fwd_context<uint16_t>(x, w, b, cu_seqlens, nseq, conv_initial, u, conv_final,
-                                                             D, W, silu != 0, s)
-                              : launch_fwd_context<float>(x, w, b, cu_seqlens, nseq, conv_initial, u, conv_final, D,
-                                                          W, silu != 0, s);
+                                                             T, D, W, silu != 0, s)
+                              : launch_fwd_context<float>(x, w, b, cu_seqlens, nseq, conv_initial, u, conv_final, T,
+                                                          D, W, silu != 0, s);
 }
 
 extern "C" size_t conv1d_pack_bwd_workspace_bytes(int64_t T, int32_t D, int32_t W) {
@@ -722,9 +734,9 @@ extern "C" int conv1d_pack_bwd_states(const void* x, const float* w, const float
         if (!dconv_initial) return SSMP_OK;
         return dtype == SSMP_BF16
                    ? launch_bwd_context<uint16_t>(x, w, b, cu_seqlens, nseq, conv_initial, du, dconv_final, dx,
-                                                  dconv_initial, nullptr, D, W, silu != 0, s)
+                                                  dconv_initial, nullptr, T, D, W, silu != 0, s)
                    : launch_bwd_context<float>(x, w, b, cu_seqlens, nseq, conv_initial, du, dconv_final, dx,
-                                               dconv_initial, nullptr, D, W, silu != 0, s);
+                                               dconv_initial, nullptr, T, D, W, silu != 0, s);
     }
     if (!x || !pos || !du || !dx) return SSMP_ERR_NULL;
     if (!workspace || workspace_bytes < conv1d_pack_bwd_states_workspace_bytes(T, D, W, nseq))
