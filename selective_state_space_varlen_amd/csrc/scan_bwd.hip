@@ -99,7 +99,7 @@ __global__ __launch_bounds__(64, 4) void k_scan_bwd_summary(const T* __restrict_
                                                          const float* __restrict__ bc, const T* __restrict__ z,
                                                          const T* __restrict__ dout, const int32_t* __restrict__ pos,
                                                          float* __restrict__ Pr, float* __restrict__ Sr, int64_t T_,
-                                                         int D, int vec, int lc, ScanOpts opt) {
+                                                         int D, int vec, int lc, int logR, ScanOpts opt) {
     constexpr int BT = 8;
     using St = Stager<T, 3, BT>;
     __shared__ __attribute__((aligned(16))) T lds[St::kElems];
@@ -111,8 +111,12 @@ __global__ __launch_bounds__(64, 4) void k_scan_bwd_summary(const T* __restrict_
     const int64_t c = tl.c;
     const int64_t t0 = c * lc;
     const int64_t t1 = (t0 + lc < T_) ? t0 + lc : T_;
-    if (c == 0) return;            // nothing to the left
-    if (pos[t0] == 0) return;      // starts at a head: carries nothing out
+    // Only carries that reach the start of the main chunk (lc << logR tokens)
+    // holding this sub-chunk are used: the sub-chunk's sequence must have
+    // started before that point. Every other sub-chunk (one in the first main
+    // chunk, at a head, or in a sequence starting inside its main chunk) is
+    // skipped, and the carry pass counts it as a zero.
+    if (!bwd_sum_needed(pos[t0], t0, logR, lc)) return;
 
     // first head in (t0, t1): the summary covers [t0, fh)
     int64_t fh = t1;
@@ -188,13 +192,13 @@ __global__ __launch_bounds__(256) void k_scan_bwd_carry(const float* __restrict_
     const int lane = threadIdx.x % kWave;
     struct Batch {
         float P[kB], S[kB];
-        int32_t hp;  // pos at the start of chunk cb - lane (lanes < kB, chunks >= 1)
+        int32_t used;  // lanes < kB: chunk cb - lane holds a summary
     };
     const int dch = (int)(i % D);
     const float A2 = A[(size_t)dch * NS + (int)(i / D)] * kLog2e;
     auto load = [&](Batch& b, int64_t cb) {
         const int64_t cj = cb - lane;
-        b.hp = (lane < kB && cj >= 1) ? pos[cj * lc] : 1;
+        b.used = (lane < kB && cj >= 0) ? (int32_t)bwd_sum_needed(pos[cj * lc], cj * lc, logR, lc) : 0;
         const float* p = Pr + (size_t)cb * D + dch;
         const float* q = Sr + (size_t)cb * ND + i;
 #pragma unroll
@@ -219,7 +223,7 @@ __global__ __launch_bounds__(256) void k_scan_bwd_carry(const float* __restrict_
     load(cur, nchunk - 1);
     for (int64_t cb = nchunk - 1; cb >= 0; cb -= kB) {
         if (cb - kB >= 0) load(nxt, cb - kB);
-        const uint64_t heads = __ballot(cur.hp == 0);  // bit j: chunk cb - j >= 1 starts at a head
+        const uint64_t used = __ballot(cur.used != 0);  // bit j: chunk cb - j holds a summary
 #pragma unroll
         for (int j = 0; j < kB; ++j) {
             const int64_t c = cb - j;
@@ -227,11 +231,12 @@ __global__ __launch_bounds__(256) void k_scan_bwd_carry(const float* __restrict_
                 if (act) *cp = cc;
                 cp -= ND;
             }
-            // select at heads, as in the forward
+            // skipped sub-chunks (heads among them) hand on zero; the select
+            // keeps their unwritten summaries out, as in the forward
             const float tj = cur.P[j];
             const float Pj = (tj != tj) ? 0.0f : exp2_fast(A2 * tj);
-            const float cn = ((heads >> j) & 1u) ? 0.0f : (Pj == 0.0f) ? cur.S[j] : __builtin_fmaf(Pj, cc, cur.S[j]);
-            cc = (c >= 1) ? cn : cc;
+            const float cn = !((used >> j) & 1u) ? 0.0f : (Pj == 0.0f) ? cur.S[j] : __builtin_fmaf(Pj, cc, cur.S[j]);
+            cc = (c >= 0) ? cn : cc;
         }
         cur = nxt;
     }
@@ -867,11 +872,11 @@ static int scan_bwd_launch(const void* u, const void* delta, const float* A, con
         if (z)
             k_scan_bwd_summary<T, NS, true><<<grid, kWave, 0, s>>>((const T*)delta, A, ws + L.bc, (const T*)z,
                                                                    (const T*)dout, pos, ws + L.Pr, ws + L.Sr, T_, D,
-                                                                   vec, ls, opt);
+                                                                   vec, ls, logR, opt);
         else
             k_scan_bwd_summary<T, NS, false><<<grid, kWave, 0, s>>>((const T*)delta, A, ws + L.bc, nullptr,
                                                                     (const T*)dout, pos, ws + L.Pr, ws + L.Sr, T_, D,
-                                                                    vec, ls, opt);
+                                                                    vec, ls, logR, opt);
         SSMP_LAUNCH_CHECK();
     }
     k_scan_bwd_carry<NS><<<(unsigned)((ND + 255) / 256), 256, 0, s>>>(ws + L.Pr, ws + L.Sr, A, pos, ws + L.cin,

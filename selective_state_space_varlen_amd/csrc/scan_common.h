@@ -43,6 +43,13 @@ inline int bwd_sum_len(int64_t T, int D, int N) {
     const int ls = bwd_chunk_len(T, D, N) / kBwdSumSplit;
     return ls < kLCMin ? kLCMin : ls;
 }
+// A reverse summary of the sub-chunk starting at token t0 (position p0) is
+// used only if its sequence started before the start of its main chunk
+// (ls << logR tokens): then the carry it forms reaches that chunk's boundary.
+__device__ __forceinline__ bool bwd_sum_needed(int32_t p0, int64_t t0, int logR, int ls) {
+    const int64_t lc = (int64_t)ls << logR;
+    return (int64_t)p0 > t0 % lc;
+}
 
 // Optional element-wise neighbours of the scan, applied where the scan reads
 // its inputs: the step is softplus(delta + bias[d]) (softplus set) or
