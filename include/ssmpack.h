@@ -57,7 +57,8 @@ const char *ssmp_status_string(int status);
 
 /* Version of this ABI (incremented on any change to the set of entry points
  * or their meaning; 2 added the _ex scan entry points, 3 the host packer
- * varlen_pack_plan, 4 the scan and conv entry points with sequence states). */
+ * varlen_pack_plan, 4 the scan and conv entry points with sequence states,
+ * 5 the scan entry points with a checkpoint interval). */
 int ssmp_abi_version(void);
 
 /*
@@ -271,6 +272,63 @@ int selective_scan_pack_bwd_states(const void *u, const void *delta, const float
                                    float *ddelta_bias, const int32_t *cu_seqlens, int32_t nseq,
                                    const float *initial_state, const float *dfinal_state,
                                    float *dinitial_state, void *stream);
+
+/*
+ * selective_scan_pack_fwd_ck / _bwd_ck — the _states entry points with the
+ * memory kept between forward and backward chosen by the caller. The
+ * recurrence of [P5] "SSM_pack算子" is sequential in t, so the backward,
+ * which walks t in reverse, restarts from states the forward kept. The
+ * single workspace of the other entry points is split in two:
+ *   saved    kept by the caller from the forward to the backward (the only
+ *            per-layer memory between them): fp32 states entering every
+ *            ckpt_interval-th token, selective_scan_pack_saved_bytes(T, D,
+ *            N, ckpt_interval) bytes. Written by the forward, read by the
+ *            backward, which must get the same inputs and options.
+ *   scratch  used during one call only and free again when the call's work
+ *            on `stream` is done: selective_scan_pack_fwd_scratch_bytes(T,
+ *            D, N) for the forward, selective_scan_pack_bwd_scratch_bytes(T,
+ *            D, N, ckpt_interval) for the backward.
+ * ckpt_interval is 0 or a power of two from 4 to 2048:
+ *   4        the backward reads the kept states directly (fastest backward;
+ *            the _states entry points use this, their workspace being saved
+ *            followed by scratch);
+ *   8..2048  fewer kept states; the backward first replays the forward's
+ *            recurrence from them into dense states in its scratch;
+ *   0        nothing kept (saved may be NULL; a forward-only call, e.g. for
+ *            inference); a backward then recomputes every state from the
+ *            inputs.
+ * The forward's outputs do not depend on ckpt_interval. The backward's
+ * replay repeats the forward's arithmetic within each forward chunk (64 or
+ * more tokens), so intervals 0 to 64 give the interval-4 gradients bit for
+ * bit; a longer interval replays across chunk boundaries where the forward
+ * restarted from its chunk carry, which changes gradients by rounding only.
+ * Other arguments, outputs and
+ * errors as the _states entry points; ckpt_interval outside the set above
+ * is SSMP_ERR_SHAPE, a missing or short saved or scratch buffer
+ * SSMP_ERR_WORKSPACE. The size queries return 0 for arguments out of range.
+ */
+size_t selective_scan_pack_saved_bytes(int64_t T, int32_t D, int32_t N, int32_t ckpt_interval);
+size_t selective_scan_pack_fwd_scratch_bytes(int64_t T, int32_t D, int32_t N);
+size_t selective_scan_pack_bwd_scratch_bytes(int64_t T, int32_t D, int32_t N, int32_t ckpt_interval);
+int selective_scan_pack_fwd_ck(const void *u, const void *delta, const float *A, const void *B,
+                               const void *C, const float *Dskip, const void *z, const int32_t *pos,
+                               void *out, int64_t T, int32_t D, int32_t N, int32_t dtype,
+                               const float *delta_bias, int32_t delta_softplus, float gate_floor,
+                               const int32_t *cu_seqlens, int32_t nseq,
+                               const float *initial_state, float *final_state,
+                               int32_t ckpt_interval, void *saved, size_t saved_bytes,
+                               void *scratch, size_t scratch_bytes, void *stream);
+int selective_scan_pack_bwd_ck(const void *u, const void *delta, const float *A, const void *B,
+                               const void *C, const float *Dskip, const void *z, const int32_t *pos,
+                               const void *dout, void *du, void *ddelta, float *dA, float *dB,
+                               float *dC, float *dD, void *dz,
+                               int64_t T, int32_t D, int32_t N, int32_t dtype,
+                               const float *delta_bias, int32_t delta_softplus, float gate_floor,
+                               float *ddelta_bias, const int32_t *cu_seqlens, int32_t nseq,
+                               const float *initial_state, const float *dfinal_state,
+                               float *dinitial_state, int32_t ckpt_interval, const void *saved,
+                               size_t saved_bytes, void *scratch, size_t scratch_bytes,
+                               void *stream);
 
 /* Packing strategies of varlen_pack_plan. */
 enum ssmp_pack_strategy {

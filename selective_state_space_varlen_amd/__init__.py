@@ -14,7 +14,12 @@ from .binding import (  # noqa: F401
     conv1d_pack_fwd,
     load,
     selective_scan_pack_bwd,
+    selective_scan_pack_bwd_ck,
+    selective_scan_pack_bwd_scratch_bytes,
     selective_scan_pack_fwd,
+    selective_scan_pack_fwd_ck,
+    selective_scan_pack_fwd_scratch_bytes,
+    selective_scan_pack_saved_bytes,
     selective_scan_pack_workspace_bytes,
     varlen_pack_indices,
     varlen_pack_plan,

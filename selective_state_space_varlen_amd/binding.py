@@ -55,6 +55,18 @@ _SIGNATURES = {
                                                       _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32,
                                                       _c_vp, _c_i32, ctypes.c_float, _c_vp, _c_vp, _c_i32,
                                                       _c_vp, _c_vp, _c_vp, _c_vp]),
+    "selective_scan_pack_saved_bytes": (_c_sz, [_c_i64, _c_i32, _c_i32, _c_i32]),
+    "selective_scan_pack_fwd_scratch_bytes": (_c_sz, [_c_i64, _c_i32, _c_i32]),
+    "selective_scan_pack_bwd_scratch_bytes": (_c_sz, [_c_i64, _c_i32, _c_i32, _c_i32]),
+    "selective_scan_pack_fwd_ck": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                                  _c_i64, _c_i32, _c_i32, _c_i32, _c_vp, _c_i32, ctypes.c_float,
+                                                  _c_vp, _c_i32, _c_vp, _c_vp, _c_i32, _c_vp, _c_sz, _c_vp, _c_sz,
+                                                  _c_vp]),
+    "selective_scan_pack_bwd_ck": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                                  _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                                  _c_i64, _c_i32, _c_i32, _c_i32, _c_vp, _c_i32, ctypes.c_float,
+                                                  _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_sz,
+                                                  _c_vp, _c_sz, _c_vp]),
     "conv1d_pack_fwd_states": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32,
                                               _c_i32, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp]),
     "conv1d_pack_bwd_states_workspace_bytes": (_c_sz, [_c_i64, _c_i32, _c_i32, _c_i32]),
@@ -403,3 +415,112 @@ def selective_scan_pack_bwd(u, delta, A, B, C, Dskip, z, pos, dout, workspace: t
     else:
         _call("selective_scan_pack_bwd", *args, _stream(u))
     return res
+
+
+def selective_scan_pack_saved_bytes(T: int, D: int, N: int, ckpt_interval: int) -> int:
+    return int(load().selective_scan_pack_saved_bytes(T, D, N, ckpt_interval))
+
+
+def selective_scan_pack_fwd_scratch_bytes(T: int, D: int, N: int) -> int:
+    return int(load().selective_scan_pack_fwd_scratch_bytes(T, D, N))
+
+
+def selective_scan_pack_bwd_scratch_bytes(T: int, D: int, N: int, ckpt_interval: int) -> int:
+    return int(load().selective_scan_pack_bwd_scratch_bytes(T, D, N, ckpt_interval))
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _scratch(scratch, nbytes, dev):
+    if scratch is None:
+        scratch = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(scratch, "scratch", device=dev)
+    return scratch
+
+
+def selective_scan_pack_fwd_ck(u, delta, A, B, C, Dskip, z, pos, ckpt_interval: int,
+                               saved: Optional[torch.Tensor] = None, scratch: Optional[torch.Tensor] = None,
+                               out: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                               delta_softplus: bool = False, gate_floor: float = 0.0,
+                               cu_seqlens: Optional[torch.Tensor] = None,
+                               initial_state: Optional[torch.Tensor] = None, final_state=False):
+    """The forward keeping the states of every ckpt_interval-th token (0:
+    none) in `saved` for the backward. Returns (out, saved or None,
+    final_state or None); the scratch is free again once the call's work on
+    the current stream is done."""
+    T, D = u.shape
+    N = A.shape[1]
+    dev = u.device
+    _check(u, "u"); _check(delta, "delta", (T, D), u.dtype, dev); _check(A, "A", (D, N), torch.float32, dev)
+    _check(B, "B", (T, N), u.dtype, dev); _check(C, "C", (T, N), u.dtype, dev)
+    _check(Dskip, "Dskip", (D,), torch.float32, dev); _check(z, "z", (T, D), u.dtype, dev)
+    _check(pos, "pos", (T,), torch.int32, dev); _check(delta_bias, "delta_bias", (D,), torch.float32, dev)
+    if saved is None and ckpt_interval:
+        saved = torch.empty(max(selective_scan_pack_saved_bytes(T, D, N, ckpt_interval), 1), dtype=torch.uint8,
+                            device=dev)
+    _check(saved, "saved", device=dev)
+    scratch = _scratch(scratch, selective_scan_pack_fwd_scratch_bytes(T, D, N), dev)
+    o = torch.empty_like(u) if out is None else out
+    _check(o, "out", (T, D), u.dtype, dev)
+    nseq, fs = 0, None
+    if cu_seqlens is not None or initial_state is not None or final_state is not False:
+        nseq = _nseq(cu_seqlens, dev)
+        fs = _out_or_new(final_state, (nseq, D, N), torch.float32, dev)
+        _check_states(nseq, (("initial_state", initial_state), ("final_state", fs)), D, N, dev)
+    _call("selective_scan_pack_fwd_ck", _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z),
+          _ptr(pos), _ptr(o), T, D, N, _dtype_code(u), _ptr(delta_bias), int(bool(delta_softplus)),
+          float(gate_floor), _ptr(cu_seqlens), nseq, _ptr(initial_state), _ptr(fs), int(ckpt_interval),
+          _ptr(saved), _nbytes(saved), _ptr(scratch), _nbytes(scratch), _stream(u))
+    return o, saved, fs
+
+
+def selective_scan_pack_bwd_ck(u, delta, A, B, C, Dskip, z, pos, dout, ckpt_interval: int,
+                               saved: Optional[torch.Tensor], scratch: Optional[torch.Tensor] = None,
+                               out: Optional[dict] = None, delta_bias: Optional[torch.Tensor] = None,
+                               delta_softplus: bool = False, gate_floor: float = 0.0,
+                               cu_seqlens: Optional[torch.Tensor] = None,
+                               initial_state: Optional[torch.Tensor] = None,
+                               dfinal_state: Optional[torch.Tensor] = None, dinitial_state=False):
+    """Gradients of sum(dout * out) from the states the forward kept at the
+    same ckpt_interval (saved; None for 0). Result dict as
+    selective_scan_pack_bwd's, with "ddelta_bias" and "dinitial_state"."""
+    T, D = u.shape
+    N = A.shape[1]
+    dev = u.device
+    _check(u, "u"); _check(delta, "delta", (T, D), u.dtype, dev); _check(A, "A", (D, N), torch.float32, dev)
+    _check(B, "B", (T, N), u.dtype, dev); _check(C, "C", (T, N), u.dtype, dev)
+    _check(Dskip, "Dskip", (D,), torch.float32, dev); _check(z, "z", (T, D), u.dtype, dev)
+    _check(pos, "pos", (T,), torch.int32, dev); _check(dout, "dout", (T, D), u.dtype, dev)
+    _check(delta_bias, "delta_bias", (D,), torch.float32, dev); _check(saved, "saved", device=dev)
+    scratch = _scratch(scratch, selective_scan_pack_bwd_scratch_bytes(T, D, N, ckpt_interval), dev)
+    if out is not None:
+        du, ddelta, dA, dB, dC, dD, dz = (out[k] for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz"))
+    else:
+        du = torch.empty_like(u)
+        ddelta = torch.empty_like(u)
+        dA = torch.empty((D, N), dtype=torch.float32, device=dev)
+        dB = torch.empty((T, N), dtype=torch.float32, device=dev)
+        dC = torch.empty((T, N), dtype=torch.float32, device=dev)
+        dD = torch.empty((D,), dtype=torch.float32, device=dev) if Dskip is not None else None
+        dz = torch.empty_like(u) if z is not None else None
+    _check(du, "du", (T, D), u.dtype, dev); _check(ddelta, "ddelta", (T, D), u.dtype, dev)
+    _check(dA, "dA", (D, N), torch.float32, dev); _check(dB, "dB", (T, N), torch.float32, dev)
+    _check(dC, "dC", (T, N), torch.float32, dev); _check(dD, "dD", (D,), torch.float32, dev)
+    _check(dz, "dz", (T, D), u.dtype, dev)
+    ddb = _bias_grad(delta_bias, out, D, dev)
+    nseq, di = 0, None
+    if (cu_seqlens is not None or initial_state is not None or dfinal_state is not None
+            or dinitial_state is not False):
+        nseq = _nseq(cu_seqlens, dev)
+        di = _out_or_new(dinitial_state, (nseq, D, N), torch.float32, dev)
+        _check_states(nseq, (("initial_state", initial_state), ("dfinal_state", dfinal_state),
+                             ("dinitial_state", di)), D, N, dev)
+    _call("selective_scan_pack_bwd_ck", _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z),
+          _ptr(pos), _ptr(dout), _ptr(du), _ptr(ddelta), _ptr(dA), _ptr(dB), _ptr(dC), _ptr(dD), _ptr(dz), T, D, N,
+          _dtype_code(u), _ptr(delta_bias), int(bool(delta_softplus)), float(gate_floor), _ptr(ddb),
+          _ptr(cu_seqlens), nseq, _ptr(initial_state), _ptr(dfinal_state), _ptr(di), int(ckpt_interval),
+          _ptr(saved), _nbytes(saved), _ptr(scratch), _nbytes(scratch), _stream(u))
+    return {"du": du, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "dz": dz, "ddelta_bias": ddb,
+            "dinitial_state": di}

@@ -75,4 +75,4 @@ extern "C" const char* ssmp_status_string(int status) {
     }
 }
 
-extern "C" int ssmp_abi_version(void) { return 4; }
+extern "C" int ssmp_abi_version(void) { return 5; }

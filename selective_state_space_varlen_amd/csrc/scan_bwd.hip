@@ -854,10 +854,10 @@ __global__ __launch_bounds__(256) void k_scan_bwd_reduce_bc(const float* __restr
 
 template <typename T, int NS>
 static int scan_bwd_launch(const void* u, const void* delta, const float* A, const void* B, const void* C,
-                           const float* Dskip, const void* z, const int32_t* pos, const void* dout, float* ws,
-                           void* du, void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, int64_t T_,
+                           const float* Dskip, const void* z, const int32_t* pos, const void* dout,
+                           const float* saved, int ci, float* ws, void* du, void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, int64_t T_,
                            int D, const ScanOpts& opt, float* dbias, hipStream_t s) {
-    const ScanWs L = scan_ws_layout(T_, D, NS);
+    const ScanWs L = scan_ws_layout(T_, D, NS, ci);
     const int lc = bwd_chunk_len(T_, D, NS);
     const int64_t nchunk = (T_ + lc - 1) / lc;
     const int ls = bwd_sum_len(T_, D, NS);  // summary sub-chunk: lc = 2^logR ls
@@ -868,6 +868,14 @@ static int scan_bwd_launch(const void* u, const void* delta, const float* A, con
     k_bc_to_f32<T, NS><<<(unsigned)((T_ * 2 * NS + 255) / 256), 256, 0, s>>>((const T*)B, (const T*)C, ws + L.bc,
                                                                             T_);
     SSMP_LAUNCH_CHECK();
+    // the state entering every kCK-th token: kept by the forward, or replayed
+    const float* ckpt = saved;
+    if (ci != kCK) {
+        const int st = scan_dense_ckpt(NS, std::is_same<T, uint16_t>::value, u, delta, A, pos, saved, ci, ws, T_, D,
+                                       opt, s);
+        if (st) return st;
+        ckpt = ws + L.dense;
+    }
     if (L.nsum > 1) {
         if (z)
             k_scan_bwd_summary<T, NS, true><<<grid, kWave, 0, s>>>((const T*)delta, A, ws + L.bc, (const T*)z,
@@ -884,7 +892,7 @@ static int scan_bwd_launch(const void* u, const void* delta, const float* A, con
     SSMP_LAUNCH_CHECK();
     BwdArgs<T> a;
     a.u = (const T*)u; a.delta = (const T*)delta; a.A = A; a.bc = ws + L.bc; a.Dskip = Dskip;
-    a.z = (const T*)z; a.dout = (const T*)dout; a.pos = pos; a.ckpt = ws + L.ckpt; a.cin = ws + L.cin;
+    a.z = (const T*)z; a.dout = (const T*)dout; a.pos = pos; a.ckpt = ckpt; a.cin = ws + L.cin;
     a.du = (T*)du; a.ddelta = (T*)ddelta; a.dz = (T*)dz; a.dApart = ws + L.dApart; a.dDpart = ws + L.dDpart;
     a.dbpart = ws + L.dbpart; a.dBC = ws + L.dBC; a.sink = ws + L.sink; a.T_ = T_; a.D = D; a.lc = lc; a.ckint = kCK; a.opt = opt;
     constexpr int SW = Split<NS>::SW;
@@ -922,13 +930,13 @@ static int scan_bwd_launch(const void* u, const void* delta, const float* A, con
 
 template <typename T>
 static int scan_bwd_dispatch(int N, const void* u, const void* delta, const float* A, const void* B, const void* C,
-                             const float* Dskip, const void* z, const int32_t* pos, const void* dout, float* ws,
-                             void* du, void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz,
+                             const float* Dskip, const void* z, const int32_t* pos, const void* dout,
+                             const float* saved, int ci, float* ws, void* du, void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz,
                              int64_t T_, int D, const ScanOpts& o, float* dbias, hipStream_t s) {
 #define SSMP_BWD_CASE(NV)                                                                                         \
     case NV:                                                                                                      \
-        return scan_bwd_launch<T, NV>(u, delta, A, B, C, Dskip, z, pos, dout, ws, du, ddelta, dA, dB, dC, dD, dz, \
-                                      T_, D, o, dbias, s);
+        return scan_bwd_launch<T, NV>(u, delta, A, B, C, Dskip, z, pos, dout, saved, ci, ws, du, ddelta, dA, dB,   \
+                                      dC, dD, dz, T_, D, o, dbias, s);
     switch (N) {
         SSMP_BWD_CASE(1)
         SSMP_BWD_CASE(2)
@@ -942,18 +950,19 @@ static int scan_bwd_dispatch(int N, const void* u, const void* delta, const floa
 
 }  // namespace ssmp
 
-extern "C" int selective_scan_pack_bwd_states(const void* u, const void* delta, const float* A, const void* B,
-                                              const void* C, const float* Dskip, const void* z, const int32_t* pos,
-                                              const void* dout, void* workspace, size_t workspace_bytes, void* du,
-                                              void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz,
-                                              int64_t T, int32_t D, int32_t N, int32_t dtype,
-                                              const float* delta_bias, int32_t delta_softplus, float gate_floor,
-                                              float* ddelta_bias, const int32_t* cu_seqlens, int32_t nseq,
-                                              const float* initial_state, const float* dfinal_state,
-                                              float* dinitial_state, void* stream) {
+extern "C" int selective_scan_pack_bwd_ck(const void* u, const void* delta, const float* A, const void* B,
+                                          const void* C, const float* Dskip, const void* z, const int32_t* pos,
+                                          const void* dout, void* du, void* ddelta, float* dA, float* dB, float* dC,
+                                          float* dD, void* dz, int64_t T, int32_t D, int32_t N, int32_t dtype,
+                                          const float* delta_bias, int32_t delta_softplus, float gate_floor,
+                                          float* ddelta_bias, const int32_t* cu_seqlens, int32_t nseq,
+                                          const float* initial_state, const float* dfinal_state,
+                                          float* dinitial_state, int32_t ckpt_interval, const void* saved,
+                                          size_t saved_bytes, void* scratch, size_t scratch_bytes, void* stream) {
     using namespace ssmp;
     int st = scan_check_args(T, D, N, dtype);
     if (st) return st;
+    if (!ck_interval_ok(ckpt_interval)) return SSMP_ERR_SHAPE;
     if (!A || !dA) return SSMP_ERR_NULL;
     if ((Dskip == nullptr) != (dD == nullptr)) return SSMP_ERR_NULL;
     if ((z == nullptr) != (dz == nullptr)) return SSMP_ERR_NULL;
@@ -985,12 +994,38 @@ extern "C" int selective_scan_pack_bwd_states(const void* u, const void* delta, 
         return hipGetLastError() == hipSuccess ? SSMP_OK : SSMP_ERR_HIP;
     }
     if (!u || !delta || !B || !C || !pos || !dout || !du || !ddelta || !dB || !dC) return SSMP_ERR_NULL;
-    if (!workspace || workspace_bytes < selective_scan_pack_workspace_bytes(T, D, N)) return SSMP_ERR_WORKSPACE;
-    float* ws = static_cast<float*>(workspace);
-    return dtype == SSMP_BF16 ? scan_bwd_dispatch<uint16_t>(N, u, delta, A, B, C, Dskip, z, pos, dout, ws, du,
-                                                            ddelta, dA, dB, dC, dD, dz, T, D, o, ddelta_bias, s)
-                              : scan_bwd_dispatch<float>(N, u, delta, A, B, C, Dskip, z, pos, dout, ws, du, ddelta,
-                                                         dA, dB, dC, dD, dz, T, D, o, ddelta_bias, s);
+    if (ckpt_interval && (!saved || saved_bytes < selective_scan_pack_saved_bytes(T, D, N, ckpt_interval)))
+        return SSMP_ERR_WORKSPACE;
+    if (!scratch || scratch_bytes < selective_scan_pack_bwd_scratch_bytes(T, D, N, ckpt_interval))
+        return SSMP_ERR_WORKSPACE;
+    const float* sv = ckpt_interval ? static_cast<const float*>(saved) : nullptr;
+    float* ws = static_cast<float*>(scratch);
+    return dtype == SSMP_BF16
+               ? scan_bwd_dispatch<uint16_t>(N, u, delta, A, B, C, Dskip, z, pos, dout, sv, ckpt_interval, ws, du,
+                                             ddelta, dA, dB, dC, dD, dz, T, D, o, ddelta_bias, s)
+               : scan_bwd_dispatch<float>(N, u, delta, A, B, C, Dskip, z, pos, dout, sv, ckpt_interval, ws, du,
+                                          ddelta, dA, dB, dC, dD, dz, T, D, o, ddelta_bias, s);
+}
+
+extern "C" int selective_scan_pack_bwd_states(const void* u, const void* delta, const float* A, const void* B,
+                                              const void* C, const float* Dskip, const void* z, const int32_t* pos,
+                                              const void* dout, void* workspace, size_t workspace_bytes, void* du,
+                                              void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz,
+                                              int64_t T, int32_t D, int32_t N, int32_t dtype,
+                                              const float* delta_bias, int32_t delta_softplus, float gate_floor,
+                                              float* ddelta_bias, const int32_t* cu_seqlens, int32_t nseq,
+                                              const float* initial_state, const float* dfinal_state,
+                                              float* dinitial_state, void* stream) {
+    // the workspace: the forward's checkpoints every kCK tokens, then the
+    // scratch (a short one is passed on as none, so that the argument checks
+    // come first)
+    const size_t sb = selective_scan_pack_saved_bytes(T, D, N, ssmp::kCK);
+    const bool ok = workspace && workspace_bytes >= selective_scan_pack_workspace_bytes(T, D, N);
+    char* w = ok ? static_cast<char*>(workspace) : nullptr;
+    return selective_scan_pack_bwd_ck(u, delta, A, B, C, Dskip, z, pos, dout, du, ddelta, dA, dB, dC, dD, dz, T, D,
+                                      N, dtype, delta_bias, delta_softplus, gate_floor, ddelta_bias, cu_seqlens,
+                                      nseq, initial_state, dfinal_state, dinitial_state, ssmp::kCK, w, ok ? sb : 0,
+                                      w ? w + sb : nullptr, ok ? workspace_bytes - sb : 0, stream);
 }
 
 extern "C" int selective_scan_pack_bwd_ex(const void* u, const void* delta, const float* A, const void* B,

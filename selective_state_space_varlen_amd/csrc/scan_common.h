@@ -188,55 +188,83 @@ __device__ __forceinline__ StepMap step_map(const ScanOpts& o, int d) {
     return m;
 }
 
+// Checkpoint intervals. The forward may keep the state entering every ci-th
+// token for the backward (ci a power of two in [kCK, kLCMax]), or none (ci =
+// 0). The backward restarts every kCK-token block from such a state: with ci
+// = kCK it reads the kept ones, otherwise it first replays the forward's
+// recurrence from them (from the chunk states of a fresh summary pass for ci
+// = 0) into dense checkpoints of its own.
+inline bool ck_interval_ok(int ci) {
+    return ci == 0 || (ci >= kCK && ci <= kLCMax && (ci & (ci - 1)) == 0);
+}
+inline size_t ws_up(size_t v) { return (v + 63) & ~size_t(63); }  // 256-byte aligned regions
+// floats the forward keeps for the backward: [ceil(T/ci)][N/4][D][4]
+inline size_t saved_floats(int64_t T, int D, int N, int ci) {
+    return ci ? ws_up((size_t)((T + ci - 1) / ci) * (size_t)N * D) : 0;
+}
+
+// The scratch of one pass (offsets in floats from its base). Nothing in it
+// outlives the call.
 struct ScanWs {
-    int64_t nck;      // checkpoint slots: slot j holds the state entering token j*kCK
-    int64_t nchunk;   // chunks (the larger count of the forward's and the backward's chunking)
+    int64_t nck;      // dense checkpoint slots: slot j holds the state entering token j*kCK
+    int64_t nfchunk;  // forward chunks
+    int64_t nbchunk;  // backward chunks
     int64_t nsum;     // backward summary sub-chunks
     int64_t ngroup;   // channel groups of 64
-    // offsets in floats from the workspace base
-    size_t ckpt;      // [nck][N/4][D][4] forward -> backward
     size_t bc;        // [T][2N]          fp32 copy of the B and C rows (each pass makes its own)
-    size_t P, S;      // forward: P [nchunk][D] sum of delta (NaN: cut by a head), S [nchunk][N][D] local end state
+    size_t P, S;      // forward: P [nfchunk][D] sum of delta (NaN: cut by a head), S [nfchunk][N][D] local end state
+    size_t hin;       // [nfchunk][N/4][D][4] forward: state entering each chunk
+    size_t dense;     // [nck][N/4][D][4] backward with ci != kCK: replayed checkpoints
     size_t Pr, Sr;    // backward, per summary sub-chunk: Pr [nsum][D] as P, Sr [nsum][N][D] reverse carry
-    size_t cin;       // [nchunk][N][D]   backward: carry entering each chunk from the right
-    size_t dApart;    // [nchunk][N][D]
-    size_t dDpart;    // [nchunk][D]
-    size_t dbpart;    // [nchunk][D]      backward: step-bias gradient partials
+    size_t cin;       // [nbchunk][N][D]  backward: carry entering each chunk from the right
+    size_t dApart;    // [nbchunk][N][D]
+    size_t dDpart;    // [nbchunk][D]
+    size_t dbpart;    // [nbchunk][D]     backward: step-bias gradient partials
     size_t dBC;       // [<= ceil(D/64)][T][2N]  per channel-group partial sums of dB, dC
     size_t sink;      // [64] target of stores by lanes with nothing to store (kept branch-free)
-    size_t total;     // floats
+    size_t fwd_total; // floats the forward uses
+    size_t bwd_total; // floats the backward uses with checkpoint interval ci
 };
 
-inline ScanWs scan_ws_layout(int64_t T, int D, int N) {
+// The forward's regions come first; the backward with ci = 0 reruns the
+// forward's summary and carry passes in them before its own.
+inline ScanWs scan_ws_layout(int64_t T, int D, int N, int ci) {
     ScanWs w{};
     w.nck = (T + kCK - 1) / kCK;
-    {
-        const int64_t lf = fwd_chunk_len(T, D), lb = bwd_chunk_len(T, D, N);
-        const int64_t nf = (T + lf - 1) / lf, nb = (T + lb - 1) / lb;
-        w.nchunk = nf > nb ? nf : nb;
-        const int64_t ls = bwd_sum_len(T, D, N);
-        w.nsum = (T + ls - 1) / ls;
-    }
+    const int64_t lf = fwd_chunk_len(T, D), lb = bwd_chunk_len(T, D, N);
+    w.nfchunk = (T + lf - 1) / lf;
+    w.nbchunk = (T + lb - 1) / lb;
+    const int64_t ls = bwd_sum_len(T, D, N);
+    w.nsum = (T + ls - 1) / ls;
     w.ngroup = (D + kWave - 1) / kWave;
     const size_t ND = (size_t)N * D;
-    auto up = [](size_t v) { return (v + 63) & ~size_t(63); };  // 256-byte aligned regions
     size_t off = 0;
-    w.ckpt = off; off = up(off + (size_t)w.nck * ND);
-    w.bc = off; off = up(off + (size_t)T * 2 * N);
-    const size_t scratch = off;
-    w.P = scratch; w.S = up(w.P + (size_t)w.nchunk * D);
-    const size_t fwd_end = up(w.S + (size_t)w.nchunk * ND);
-    w.Pr = scratch; w.Sr = up(w.Pr + (size_t)w.nsum * D);
-    w.cin = up(w.Sr + (size_t)w.nsum * ND);
-    w.dApart = up(w.cin + (size_t)w.nchunk * ND);
-    w.dDpart = up(w.dApart + (size_t)w.nchunk * ND);
-    w.dbpart = up(w.dDpart + (size_t)w.nchunk * D);
-    w.dBC = up(w.dbpart + (size_t)w.nchunk * D);
-    w.sink = up(w.dBC + (size_t)((D + kWave - 1) / kWave) * (size_t)T * 2 * N);
-    const size_t bwd_end = up(w.sink + 64);
-    w.total = fwd_end > bwd_end ? fwd_end : bwd_end;
+    w.bc = off; off = ws_up(off + (size_t)T * 2 * N);
+    const size_t after_bc = off;
+    w.P = off; off = ws_up(off + (size_t)w.nfchunk * D);
+    w.S = off; off = ws_up(off + (size_t)w.nfchunk * ND);
+    w.hin = off; off = ws_up(off + (size_t)w.nfchunk * ND);
+    w.fwd_total = off;
+    off = (ci == 0) ? w.fwd_total : after_bc;
+    if (ci != kCK) { w.dense = off; off = ws_up(off + (size_t)w.nck * ND); }
+    w.Pr = off; off = ws_up(off + (size_t)w.nsum * D);
+    w.Sr = off; off = ws_up(off + (size_t)w.nsum * ND);
+    w.cin = off; off = ws_up(off + (size_t)w.nbchunk * ND);
+    w.dApart = off; off = ws_up(off + (size_t)w.nbchunk * ND);
+    w.dDpart = off; off = ws_up(off + (size_t)w.nbchunk * D);
+    w.dbpart = off; off = ws_up(off + (size_t)w.nbchunk * D);
+    w.dBC = off; off = ws_up(off + (size_t)((D + kWave - 1) / kWave) * (size_t)T * 2 * N);
+    w.sink = off; off = ws_up(off + 64);
+    w.bwd_total = off;
     return w;
 }
+
+// Dense checkpoints for the backward (scratch + L.dense), replayed from the
+// forward's kept states at interval ci, or for ci = 0 from the chunk states of
+// a fresh forward summary pass. Needs the fp32 B/C rows at scratch + L.bc.
+// Defined with the forward kernels.
+int scan_dense_ckpt(int N, bool bf16, const void* u, const void* delta, const float* A, const int32_t* pos,
+                    const float* saved, int ci, float* scratch, int64_t T, int D, const ScanOpts& o, hipStream_t s);
 
 // Flat 1-D grid over (chunk, 64-channel group), group fastest: concurrently
 // running waves cover adjacent channels of the same tokens.

@@ -21,8 +21,11 @@
 //      starts with a head.
 //   2. carry: per (n, d), a sequential pass over chunks gives the state
 //      entering each chunk.
-//   3. output: each chunk replays its tokens from that state, writes out and
-//      stores the state entering every kCK-th token for the backward.
+//   3. output: each chunk replays its tokens from that state, writes out and,
+//      when the caller keeps checkpoints for the backward, stores the state
+//      entering every ci-th token.
+// A fourth kernel, used by the backward, replays the recurrence without the
+// output from kept states to the dense checkpoints the backward restarts from.
 // The step map and gate floor (ScanOpts) apply where delta and z are read;
 // carried sequence states enter at heads and leave at ends, in the blocks
 // that already take the slow path for heads.
@@ -161,12 +164,12 @@ __global__ __launch_bounds__(64, 4) void k_scan_fwd_summary(const T* __restrict_
     }
 }
 
-// State entering each chunk, written to the checkpoint slot of its first token.
+// State entering each chunk, in the checkpoint layout (hin[c]).
 // P holds each chunk's sum of delta per channel (NaN: a head cuts the chunk).
 template <int NS>
 __global__ __launch_bounds__(256) void k_scan_fwd_carry(const float* __restrict__ P, const float* __restrict__ S,
                                                         const float* __restrict__ A,
-                                                        const int32_t* __restrict__ pos, float* __restrict__ ckpt,
+                                                        const int32_t* __restrict__ pos, float* __restrict__ hin,
                                                         int64_t T_, int D, int64_t nchunk, int lc) {
     const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // n*D + d
     const int64_t ND = (int64_t)NS * D;
@@ -205,8 +208,8 @@ __global__ __launch_bounds__(256) void k_scan_fwd_carry(const float* __restrict_
         }
     };
     float h = 0.0f;
-    float* kp = ckpt + ck_index<NS>(dch, (int)(i / D), D);  // checkpoint slot of chunk c's first token
-    const size_t kstride = (size_t)(lc / kCK) * ND;
+    float* kp = hin + ck_index<NS>(dch, (int)(i / D), D);  // chunk c's entry state (checkpoint layout)
+    const size_t kstride = (size_t)ND;
     Batch cur, nxt;
     load(cur, 0);
     for (int64_t cb = 0; cb < nchunk; cb += kB) {
@@ -233,9 +236,8 @@ __global__ __launch_bounds__(256) void k_scan_fwd_carry(const float* __restrict_
 // Output recurrence over one block of BT tokens. SAFE blocks may end early
 // (nt < BT) and may hold heads; fast blocks are full and head-free, so their
 // tokens run straight through with the next token's B/C rows in flight.
-// The state entering every kCK-th token goes to its checkpoint slot (ck:
-// the slot of the block's first token), except at the chunk start (skip0),
-// whose slot the carry pass wrote.
+// With cish >= 0 the state entering every token t with t % 2^cish == 0 goes
+// to checkpoint slot t >> cish of `saved`.
 //
 // With sequence states, a head starts from its sequence's initial state
 // instead of zero, and the state after an end token (ends: bit k) is that
@@ -244,8 +246,8 @@ template <bool SAFE, bool GATE, bool XS, bool ST, typename T, int NS, int BT, ty
 __device__ __forceinline__ void out_block(const T* lds, const float* __restrict__ bc, int64_t tb, int nt,
                                           uint32_t heads, uint32_t ends, const float (&A2)[NS], float (&h)[NS],
                                           float Dv, int lane, T* __restrict__ ob, int D, int d, int dd, bool store,
-                                          float* __restrict__ ck, size_t ND, bool skip0, bool act, const StepMap& sm,
-                                          const ScanOpts& opt) {
+                                          float* __restrict__ saved, int cish, size_t ND, bool act,
+                                          const StepMap& sm, const ScanOpts& opt) {
     const float gf = opt.gate_floor;
     // the block's per-lane inputs are read from LDS before the first scalar
     // load: a wait for LDS data also waits for scalar loads in flight
@@ -264,8 +266,8 @@ __device__ __forceinline__ void out_block(const T* lds, const float* __restrict_
         if constexpr (SAFE) {
             if (k >= nt) break;
         }
-        if (k % kCK == 0 && act && !(k == 0 && skip0)) {
-            ck_store<NS>(ck + (size_t)(k / kCK) * ND, d, D, h);
+        if (k % kCK == 0 && cish >= 0 && ((tb + k) & ((int64_t(1) << cish) - 1)) == 0 && act) {
+            ck_store<NS>(saved + (size_t)((tb + k) >> cish) * ND, d, D, h);
         }
         float nxt[2 * NS];
         const bool more = SAFE ? (k + 1 < nt) : (k + 1 < BT);
@@ -323,7 +325,8 @@ template <typename T, int NS, bool GATE, bool XS, bool ST>
 __global__ __launch_bounds__(64, (ST || XS || sizeof(T) == 4) ? 2 : 4) void k_scan_fwd_out(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A, const float* __restrict__ bc,
     const float* __restrict__ Dskip, const T* __restrict__ z, const int32_t* __restrict__ pos, T* __restrict__ out,
-    float* __restrict__ ckpt, int64_t T_, int D, int vec, int lc, ScanOpts opt) {
+    const float* __restrict__ hin, float* __restrict__ saved, int cish, int64_t T_, int D, int vec, int lc,
+    ScanOpts opt) {
     constexpr int BT = kFwdBlock;
     using St = Stager<T, 3, BT>;
     __shared__ __attribute__((aligned(16))) T lds[St::kElems];
@@ -344,7 +347,7 @@ __global__ __launch_bounds__(64, (ST || XS || sizeof(T) == 4) ? 2 : 4) void k_sc
         A2[n] = A[(size_t)dd * NS + n] * kLog2e;
         h[n] = 0.0f;
     }
-    ck_load<NS, NS>(ckpt + (size_t)(t0 / kCK) * ND, dd, D, 0, act, h);
+    ck_load<NS, NS>(hin + (size_t)c * ND, dd, D, 0, act, h);
     const float Dv = (Dskip && act) ? Dskip[dd] : 0.0f;
     const StepMap sm = step_map(opt, dd);
     const T* const src[3] = {u, delta, GATE ? z : u};
@@ -359,47 +362,154 @@ __global__ __launch_bounds__(64, (ST || XS || sizeof(T) == 4) ? 2 : 4) void k_sc
         if (tb + BT < t1) st.fetch(src, tb + BT, T_, D, tl.g, lane, vec);
         const int nt = (int)((tb + BT < t1) ? BT : t1 - tb);
         T* __restrict__ ob = out + (size_t)tb * D;
-        float* __restrict__ ck = ckpt + (size_t)(tb / kCK) * ND;
         if ((heads | ends) == 0 && nt == BT)
             out_block<false, GATE, XS, ST, T, NS, BT, St>(lds, bc, tb, BT, 0u, 0u, A2, h, Dv, lane, ob, D, d, dd, store,
-                                                  ck, ND, tb == t0, act, sm, opt);
+                                                  saved, cish, ND, act, sm, opt);
         else
             out_block<true, GATE, XS, ST, T, NS, BT, St>(lds, bc, tb, nt, heads, ends, A2, h, Dv, lane, ob, D, d, dd,
-                                                 store, ck, ND, tb == t0, act, sm, opt);
+                                                 store, saved, cish, ND, act, sm, opt);
     }
 }
 
+// Dense checkpoints: the output pass's recurrence without its output, from a
+// kept state every G tokens, storing the state entering every kCK-th token.
+// The arithmetic is the output pass's, operation for operation, so the
+// replayed states equal the ones that pass would have kept.
+template <bool SAFE, bool XS, bool ST, typename T, int NS, int BT, typename St>
+__device__ __forceinline__ void replay_block(const T* lds, const float* __restrict__ bc, int64_t tb, int nt,
+                                             uint32_t heads, const float (&A2)[NS], float (&h)[NS], int lane,
+                                             float* __restrict__ ck, size_t ND, int d, int D, int dd, bool act,
+                                             const StepMap& sm, const ScanOpts& opt) {
+    float dtv[BT], uv[BT];
+#pragma unroll
+    for (int k = 0; k < BT; ++k) {
+        dtv[k] = St::get(lds, 1, k, lane);
+        uv[k] = St::get(lds, 0, k, lane);
+    }
+    const float* __restrict__ rows = bc + (size_t)tb * 2 * NS;  // B: the first NS of each row
+    float cur[NS];
+    load_rowv<NS>(rows, cur);
+#pragma unroll
+    for (int k = 0; k < BT; ++k) {
+        if constexpr (SAFE) {
+            if (k >= nt) break;
+        }
+        if (k % kCK == 0 && act) ck_store<NS>(ck + (size_t)(k / kCK) * ND, d, D, h);
+        float nxt[NS];
+        const bool more = SAFE ? (k + 1 < nt) : (k + 1 < BT);
+        if (more) load_rowv<NS>(rows + (k + 1) * 2 * NS, nxt);
+        const float dt = XS ? sm.eff(dtv[k]) : dtv[k];
+        const float dtu = dt * uv[k];
+        if constexpr (SAFE) {
+            if ((heads >> k) & 1u) {
+                asm volatile("");
+                if (ST && opt.h0) {
+                    const float* __restrict__ hp = opt.h0 + ((size_t)seq_of(opt.cu, opt.nseq, tb + k) * D + dd) * NS;
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) h[n] = hp[n];
+                } else {
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) h[n] = 0.0f;
+                }
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NS; ++n) h[n] = __builtin_fmaf(exp2_fast(dt * A2[n]), h[n], dtu * cur[n]);
+        if (more) {
+#pragma unroll
+            for (int n = 0; n < NS; ++n) cur[n] = nxt[n];
+        }
+    }
+}
+
+// One wave per (segment of G tokens, 64 channels): segment c starts from
+// start[c * sstride] (checkpoint layout) and writes dense slots t / kCK.
+template <typename T, int NS, bool XS, bool ST>
+__global__ __launch_bounds__(64, (ST || XS || sizeof(T) == 4) ? 2 : 4) void k_scan_fwd_replay(
+    const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A, const float* __restrict__ bc,
+    const int32_t* __restrict__ pos, const float* __restrict__ start, size_t sstride, float* __restrict__ dense,
+    int64_t T_, int D, int vec, int G, ScanOpts opt) {
+    constexpr int BT = kFwdBlock;
+    using St = Stager<T, 2, BT>;
+    __shared__ __attribute__((aligned(16))) T lds[St::kElems];
+    const int lane = threadIdx.x;
+    const Tile tl = tile_of(D);
+    const int d = tl.g * kWave + lane;
+    const bool act = d < D;
+    const int dd = act ? d : D - 1;
+    const int64_t c = tl.c;
+    const int64_t t0 = c * G;
+    const int64_t t1 = (t0 + G < T_) ? t0 + G : T_;
+    const size_t ND = (size_t)NS * D;
+    float A2[NS], h[NS];
+#pragma unroll
+    for (int n = 0; n < NS; ++n) A2[n] = A[(size_t)dd * NS + n] * kLog2e;
+    ck_load<NS, NS>(start + (size_t)c * sstride, dd, D, 0, act, h);
+    const StepMap sm = step_map(opt, dd);
+    const T* const src[2] = {u, delta};
+    St st;
+    st.fetch(src, t0, T_, D, tl.g, lane, vec);
+    for (int64_t tb = t0; tb < t1; tb += BT) {
+        const uint32_t heads = block_heads<BT>(pos, tb, T_, lane);
+        wave_sync();
+        st.commit(lds, src, tb, T_, D, tl.g, lane, vec);
+        wave_sync();
+        if (tb + BT < t1) st.fetch(src, tb + BT, T_, D, tl.g, lane, vec);
+        const int nt = (int)((tb + BT < t1) ? BT : t1 - tb);
+        float* __restrict__ ck = dense + (size_t)(tb / kCK) * ND;
+        if (heads == 0 && nt == BT)
+            replay_block<false, XS, ST, T, NS, BT, St>(lds, bc, tb, BT, 0u, A2, h, lane, ck, ND, d, D, dd, act, sm,
+                                                       opt);
+        else
+            replay_block<true, XS, ST, T, NS, BT, St>(lds, bc, tb, nt, heads, A2, h, lane, ck, ND, d, D, dd, act, sm,
+                                                      opt);
+    }
+}
+
+// Summary and carry passes: the state entering each chunk, at scratch + L.hin.
 template <typename T, int NS>
-static int scan_fwd_launch(const void* u, const void* delta, const float* A, const void* B, const void* C,
-                           const float* Dskip, const void* z, const int32_t* pos, void* out, float* ws, int64_t T_,
-                           int D, const ScanOpts& opt, hipStream_t s) {
-    const ScanWs L = scan_ws_layout(T_, D, NS);
+static int scan_fwd_chunk_states(const void* u, const void* delta, const float* A, const int32_t* pos, float* ws,
+                                 const ScanWs& L, int64_t T_, int D, const ScanOpts& opt, hipStream_t s) {
     const int lc = fwd_chunk_len(T_, D);
-    const int64_t nchunk = (T_ + lc - 1) / lc;
+    const int64_t nchunk = L.nfchunk;
     const dim3 grid((unsigned)(L.ngroup * nchunk));
-    const int vec = stage_vec_ok<T>(D, {u, delta, z}) ? 1 : 0;
-    k_bc_to_f32<T, NS><<<(unsigned)((T_ * 2 * NS + 255) / 256), 256, 0, s>>>((const T*)B, (const T*)C, ws + L.bc,
-                                                                            T_);
-    SSMP_LAUNCH_CHECK();
+    const int vec = stage_vec_ok<T>(D, {u, delta}) ? 1 : 0;
     if (nchunk > 1) {
         k_scan_fwd_summary<T, NS><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, ws + L.bc, pos, ws + L.P,
                                                          ws + L.S, T_, D, vec, lc, opt);
         SSMP_LAUNCH_CHECK();
     }
     const int64_t ND = (int64_t)NS * D;
-    k_scan_fwd_carry<NS><<<(unsigned)((ND + 255) / 256), 256, 0, s>>>(ws + L.P, ws + L.S, A, pos, ws + L.ckpt, T_,
+    k_scan_fwd_carry<NS><<<(unsigned)((ND + 255) / 256), 256, 0, s>>>(ws + L.P, ws + L.S, A, pos, ws + L.hin, T_,
                                                                       D, nchunk, lc);
     SSMP_LAUNCH_CHECK();
+    return SSMP_OK;
+}
+
+template <typename T, int NS>
+static int scan_fwd_launch(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                           const float* Dskip, const void* z, const int32_t* pos, void* out, float* saved, int ci,
+                           float* ws, int64_t T_, int D, const ScanOpts& opt, hipStream_t s) {
+    const ScanWs L = scan_ws_layout(T_, D, NS, ci);
+    const int lc = fwd_chunk_len(T_, D);
+    const dim3 grid((unsigned)(L.ngroup * L.nfchunk));
+    const int vec = stage_vec_ok<T>(D, {u, delta, z}) ? 1 : 0;
+    k_bc_to_f32<T, NS><<<(unsigned)((T_ * 2 * NS + 255) / 256), 256, 0, s>>>((const T*)B, (const T*)C, ws + L.bc,
+                                                                            T_);
+    SSMP_LAUNCH_CHECK();
+    int st = scan_fwd_chunk_states<T, NS>(u, delta, A, pos, ws, L, T_, D, opt, s);
+    if (st) return st;
+    const int cish = ci ? __builtin_ctz((unsigned)ci) : -1;
     const bool xs = opt.delta_bias != nullptr || opt.softplus != 0;
     // sequence states get kernels of their own, so the reset-only ones keep
     // their register allocation
-    const bool st = opt.h0 != nullptr || opt.hT != nullptr;
-#define SSMP_FWD_OUT(G, X, S)                                                                                    \
-    k_scan_fwd_out<T, NS, G, X, S><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, ws + L.bc, Dskip,      \
-                                                          G ? (const T*)z : nullptr, pos, (T*)out, ws + L.ckpt, T_, \
-                                                          D, vec, lc, opt)
+    const bool sv = opt.h0 != nullptr || opt.hT != nullptr;
+#define SSMP_FWD_OUT(G, X, S)                                                                                   \
+    k_scan_fwd_out<T, NS, G, X, S><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, ws + L.bc, Dskip,     \
+                                                          G ? (const T*)z : nullptr, pos, (T*)out, ws + L.hin,    \
+                                                          saved, cish, T_, D, vec, lc, opt)
 #define SSMP_FWD_OUT_S(G, X)                \
-    if (st) SSMP_FWD_OUT(G, X, true);       \
+    if (sv) SSMP_FWD_OUT(G, X, true);       \
     else SSMP_FWD_OUT(G, X, false)
     if (z) {
         if (xs) { SSMP_FWD_OUT_S(true, true); } else { SSMP_FWD_OUT_S(true, false); }
@@ -410,6 +520,7 @@ static int scan_fwd_launch(const void* u, const void* delta, const float* A, con
 #undef SSMP_FWD_OUT
     SSMP_LAUNCH_CHECK();
     if (opt.hT) {
+        const int64_t ND = (int64_t)NS * D;
         const int64_t n = (int64_t)opt.nseq * ND;
         k_empty_seq_states<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(opt.cu, opt.nseq, ND, opt.h0, opt.hT);
         SSMP_LAUNCH_CHECK();
@@ -417,37 +528,114 @@ static int scan_fwd_launch(const void* u, const void* delta, const float* A, con
     return SSMP_OK;
 }
 
+template <typename T, int NS>
+static int scan_dense_launch(const void* u, const void* delta, const float* A, const int32_t* pos,
+                             const float* saved, int ci, float* ws, int64_t T_, int D, const ScanOpts& opt,
+                             hipStream_t s) {
+    const ScanWs L = scan_ws_layout(T_, D, NS, ci);
+    const size_t ND = (size_t)NS * D;
+    const float* start;
+    size_t sstride;
+    int G;
+    if (ci == 0) {
+        int st = scan_fwd_chunk_states<T, NS>(u, delta, A, pos, ws, L, T_, D, opt, s);
+        if (st) return st;
+        start = ws + L.hin;
+        sstride = ND;
+        G = fwd_chunk_len(T_, D);
+    } else {
+        // segments of at least 64 tokens, each from the kept state at its start
+        G = ci > kLCMin ? ci : kLCMin;
+        start = saved;
+        sstride = (size_t)(G / ci) * ND;
+    }
+    const int64_t nseg = (T_ + G - 1) / G;
+    const dim3 grid((unsigned)(L.ngroup * nseg));
+    const int vec = stage_vec_ok<T>(D, {u, delta}) ? 1 : 0;
+    const bool xs = opt.delta_bias != nullptr || opt.softplus != 0;
+    const bool sv = opt.h0 != nullptr;
+#define SSMP_REPLAY(X, S)                                                                                      \
+    k_scan_fwd_replay<T, NS, X, S><<<grid, kWave, 0, s>>>((const T*)u, (const T*)delta, A, ws + L.bc, pos, start, \
+                                                          sstride, ws + L.dense, T_, D, vec, G, opt)
+    if (xs) {
+        if (sv) SSMP_REPLAY(true, true); else SSMP_REPLAY(true, false);
+    } else {
+        if (sv) SSMP_REPLAY(false, true); else SSMP_REPLAY(false, false);
+    }
+#undef SSMP_REPLAY
+    SSMP_LAUNCH_CHECK();
+    return SSMP_OK;
+}
+
 template <typename T>
 static int scan_fwd_dispatch(int N, const void* u, const void* delta, const float* A, const void* B, const void* C,
-                             const float* Dskip, const void* z, const int32_t* pos, void* out, float* ws, int64_t T_,
-                             int D, const ScanOpts& o, hipStream_t s) {
+                             const float* Dskip, const void* z, const int32_t* pos, void* out, float* saved, int ci,
+                             float* ws, int64_t T_, int D, const ScanOpts& o, hipStream_t s) {
+#define SSMP_FWD_CASE(NV) \
+    case NV: return scan_fwd_launch<T, NV>(u, delta, A, B, C, Dskip, z, pos, out, saved, ci, ws, T_, D, o, s);
     switch (N) {
-        case 1: return scan_fwd_launch<T, 1>(u, delta, A, B, C, Dskip, z, pos, out, ws, T_, D, o, s);
-        case 2: return scan_fwd_launch<T, 2>(u, delta, A, B, C, Dskip, z, pos, out, ws, T_, D, o, s);
-        case 4: return scan_fwd_launch<T, 4>(u, delta, A, B, C, Dskip, z, pos, out, ws, T_, D, o, s);
-        case 8: return scan_fwd_launch<T, 8>(u, delta, A, B, C, Dskip, z, pos, out, ws, T_, D, o, s);
-        case 16: return scan_fwd_launch<T, 16>(u, delta, A, B, C, Dskip, z, pos, out, ws, T_, D, o, s);
+        SSMP_FWD_CASE(1)
+        SSMP_FWD_CASE(2)
+        SSMP_FWD_CASE(4)
+        SSMP_FWD_CASE(8)
+        SSMP_FWD_CASE(16)
         default: return SSMP_ERR_UNSUPPORTED;
     }
+#undef SSMP_FWD_CASE
+}
+
+int scan_dense_ckpt(int N, bool bf16, const void* u, const void* delta, const float* A, const int32_t* pos,
+                    const float* saved, int ci, float* scratch, int64_t T, int D, const ScanOpts& o, hipStream_t s) {
+#define SSMP_DENSE_CASE(NV)                                                                                     \
+    case NV:                                                                                                    \
+        return bf16 ? scan_dense_launch<uint16_t, NV>(u, delta, A, pos, saved, ci, scratch, T, D, o, s)         \
+                    : scan_dense_launch<float, NV>(u, delta, A, pos, saved, ci, scratch, T, D, o, s);
+    switch (N) {
+        SSMP_DENSE_CASE(1)
+        SSMP_DENSE_CASE(2)
+        SSMP_DENSE_CASE(4)
+        SSMP_DENSE_CASE(8)
+        SSMP_DENSE_CASE(16)
+        default: return SSMP_ERR_UNSUPPORTED;
+    }
+#undef SSMP_DENSE_CASE
 }
 
 }  // namespace ssmp
 
-extern "C" size_t selective_scan_pack_workspace_bytes(int64_t T, int32_t D, int32_t N) {
-    if (T <= 0 || D <= 0 || N <= 0) return 0;
-    return ssmp::scan_ws_layout(T, D, N).total * sizeof(float);
+extern "C" size_t selective_scan_pack_saved_bytes(int64_t T, int32_t D, int32_t N, int32_t ckpt_interval) {
+    if (T <= 0 || D <= 0 || N <= 0 || !ssmp::ck_interval_ok(ckpt_interval)) return 0;
+    return ssmp::saved_floats(T, D, N, ckpt_interval) * sizeof(float);
 }
 
-extern "C" int selective_scan_pack_fwd_states(const void* u, const void* delta, const float* A, const void* B,
-                                              const void* C, const float* Dskip, const void* z, const int32_t* pos,
-                                              void* out, void* workspace, size_t workspace_bytes, int64_t T,
-                                              int32_t D, int32_t N, int32_t dtype, const float* delta_bias,
-                                              int32_t delta_softplus, float gate_floor, const int32_t* cu_seqlens,
-                                              int32_t nseq, const float* initial_state, float* final_state,
-                                              void* stream) {
+extern "C" size_t selective_scan_pack_fwd_scratch_bytes(int64_t T, int32_t D, int32_t N) {
+    if (T <= 0 || D <= 0 || N <= 0) return 0;
+    return ssmp::scan_ws_layout(T, D, N, 0).fwd_total * sizeof(float);
+}
+
+extern "C" size_t selective_scan_pack_bwd_scratch_bytes(int64_t T, int32_t D, int32_t N, int32_t ckpt_interval) {
+    if (T <= 0 || D <= 0 || N <= 0 || !ssmp::ck_interval_ok(ckpt_interval)) return 0;
+    return ssmp::scan_ws_layout(T, D, N, ckpt_interval).bwd_total * sizeof(float);
+}
+
+extern "C" size_t selective_scan_pack_workspace_bytes(int64_t T, int32_t D, int32_t N) {
+    if (T <= 0 || D <= 0 || N <= 0) return 0;
+    const size_t f = selective_scan_pack_fwd_scratch_bytes(T, D, N);
+    const size_t b = selective_scan_pack_bwd_scratch_bytes(T, D, N, ssmp::kCK);
+    return selective_scan_pack_saved_bytes(T, D, N, ssmp::kCK) + (f > b ? f : b);
+}
+
+extern "C" int selective_scan_pack_fwd_ck(const void* u, const void* delta, const float* A, const void* B,
+                                          const void* C, const float* Dskip, const void* z, const int32_t* pos,
+                                          void* out, int64_t T, int32_t D, int32_t N, int32_t dtype,
+                                          const float* delta_bias, int32_t delta_softplus, float gate_floor,
+                                          const int32_t* cu_seqlens, int32_t nseq, const float* initial_state,
+                                          float* final_state, int32_t ckpt_interval, void* saved,
+                                          size_t saved_bytes, void* scratch, size_t scratch_bytes, void* stream) {
     using namespace ssmp;
     int st = scan_check_args(T, D, N, dtype);
     if (st) return st;
+    if (!ck_interval_ok(ckpt_interval)) return SSMP_ERR_SHAPE;
     const bool states = initial_state || final_state;
     if (states) {
         if (!cu_seqlens) return SSMP_ERR_NULL;
@@ -470,10 +658,34 @@ extern "C" int selective_scan_pack_fwd_states(const void* u, const void* delta, 
         return hipGetLastError() == hipSuccess ? SSMP_OK : SSMP_ERR_HIP;
     }
     if (!u || !delta || !A || !B || !C || !pos || !out) return SSMP_ERR_NULL;
-    if (!workspace || workspace_bytes < selective_scan_pack_workspace_bytes(T, D, N)) return SSMP_ERR_WORKSPACE;
-    float* ws = static_cast<float*>(workspace);
-    return dtype == SSMP_BF16 ? scan_fwd_dispatch<uint16_t>(N, u, delta, A, B, C, Dskip, z, pos, out, ws, T, D, o, s)
-                              : scan_fwd_dispatch<float>(N, u, delta, A, B, C, Dskip, z, pos, out, ws, T, D, o, s);
+    if (ckpt_interval && (!saved || saved_bytes < selective_scan_pack_saved_bytes(T, D, N, ckpt_interval)))
+        return SSMP_ERR_WORKSPACE;
+    if (!scratch || scratch_bytes < selective_scan_pack_fwd_scratch_bytes(T, D, N)) return SSMP_ERR_WORKSPACE;
+    float* sv = ckpt_interval ? static_cast<float*>(saved) : nullptr;
+    float* ws = static_cast<float*>(scratch);
+    return dtype == SSMP_BF16
+               ? scan_fwd_dispatch<uint16_t>(N, u, delta, A, B, C, Dskip, z, pos, out, sv, ckpt_interval, ws, T, D,
+                                             o, s)
+               : scan_fwd_dispatch<float>(N, u, delta, A, B, C, Dskip, z, pos, out, sv, ckpt_interval, ws, T, D, o,
+                                          s);
+}
+
+extern "C" int selective_scan_pack_fwd_states(const void* u, const void* delta, const float* A, const void* B,
+                                              const void* C, const float* Dskip, const void* z, const int32_t* pos,
+                                              void* out, void* workspace, size_t workspace_bytes, int64_t T,
+                                              int32_t D, int32_t N, int32_t dtype, const float* delta_bias,
+                                              int32_t delta_softplus, float gate_floor, const int32_t* cu_seqlens,
+                                              int32_t nseq, const float* initial_state, float* final_state,
+                                              void* stream) {
+    // the workspace: checkpoints every kCK tokens, then the scratch (a short
+    // one is passed on as none, so that the argument checks come first)
+    const size_t sb = selective_scan_pack_saved_bytes(T, D, N, ssmp::kCK);
+    const bool ok = workspace && workspace_bytes >= selective_scan_pack_workspace_bytes(T, D, N);
+    char* w = ok ? static_cast<char*>(workspace) : nullptr;
+    return selective_scan_pack_fwd_ck(u, delta, A, B, C, Dskip, z, pos, out, T, D, N, dtype, delta_bias,
+                                      delta_softplus, gate_floor, cu_seqlens, nseq, initial_state, final_state,
+                                      ssmp::kCK, w, ok ? sb : 0, w ? w + sb : nullptr, ok ? workspace_bytes - sb : 0,
+                                      stream);
 }
 
 extern "C" int selective_scan_pack_fwd_ex(const void* u, const void* delta, const float* A, const void* B,

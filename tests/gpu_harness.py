@@ -30,6 +30,25 @@ def npy(t):
     return None if t is None else t.detach().to("cpu").to(torch.float64).numpy()
 
 
+def nan_buffer(nbytes: int) -> torch.Tensor:
+    """A device byte buffer whose every fp32 word is a NaN (0xFFFFFFFF):
+    workspaces start this way, so that a read of anything a kernel did not
+    write shows up in the results."""
+    return torch.full((max(nbytes, 1),), 255, dtype=torch.uint8, device=dev())
+
+
+def scan_workspace(T: int, D: int, N: int) -> torch.Tensor:
+    import selective_state_space_varlen_amd as ssp
+    return nan_buffer(ssp.selective_scan_pack_workspace_bytes(T, D, N))
+
+
+def poison_scan_scratch(ws: torch.Tensor, T: int, D: int, N: int) -> None:
+    """NaN-fill the part of a single scan workspace after the forward's kept
+    states (the backward's scratch), between forward and backward."""
+    import selective_state_space_varlen_amd as ssp
+    ws[ssp.selective_scan_pack_saved_bytes(T, D, N, 4):].fill_(255)
+
+
 def assert_close(got, ref, tol, name):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)

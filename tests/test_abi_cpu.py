@@ -34,7 +34,9 @@ def test_header_lists_the_entry_points():
               "selective_scan_pack_bwd", "selective_scan_pack_workspace_bytes", "conv1d_pack_bwd_workspace_bytes",
               "ssmp_status_string", "ssmp_abi_version", "selective_scan_pack_fwd_ex", "selective_scan_pack_bwd_ex",
               "varlen_pack_plan", "selective_scan_pack_fwd_states", "selective_scan_pack_bwd_states",
-              "conv1d_pack_fwd_states", "conv1d_pack_bwd_states", "conv1d_pack_bwd_states_workspace_bytes"):
+              "conv1d_pack_fwd_states", "conv1d_pack_bwd_states", "conv1d_pack_bwd_states_workspace_bytes",
+              "selective_scan_pack_fwd_ck", "selective_scan_pack_bwd_ck", "selective_scan_pack_saved_bytes",
+              "selective_scan_pack_fwd_scratch_bytes", "selective_scan_pack_bwd_scratch_bytes"):
         assert n in names, n
 
 
@@ -50,7 +52,7 @@ def test_status_strings(lib):
     for s in range(1, 7):
         assert lib.ssmp_status_string(s) and lib.ssmp_status_string(s) != b"unknown status"
     assert lib.ssmp_status_string(99) == b"unknown status"
-    assert lib.ssmp_abi_version() == 4
+    assert lib.ssmp_abi_version() == 5
 
 
 def test_workspace_sizes(lib):
@@ -131,3 +133,52 @@ def test_host_validation_states(lib):
     assert lib.conv1d_pack_bwd_states(*cb, fake, 1 << 30, 8, 4, 4, 1, 1, fake, 0, fake, NULL, NULL, NULL) == 2
     small = lib.conv1d_pack_bwd_workspace_bytes(8, 4, 4)  # enough without contexts, too small with them
     assert lib.conv1d_pack_bwd_states(*cb, fake, small, 8, 4, 4, 1, 1, fake, 2, fake, NULL, NULL, NULL) == 6
+
+
+def test_checkpoint_interval_sizes(lib):
+    T, D, N = 32768, 4096, 16
+    # kept states: one fp32 (D, N) slot per ckpt_interval tokens (256-byte rounded)
+    for ci in (4, 8, 64, 256, 2048):
+        assert lib.selective_scan_pack_saved_bytes(T, D, N, ci) == (T // ci) * D * N * 4
+    assert lib.selective_scan_pack_saved_bytes(T + 1, D, N, 64) == (T // 64 + 1) * D * N * 4
+    assert lib.selective_scan_pack_saved_bytes(T, D, N, 0) == 0
+    for bad in (-4, 1, 2, 3, 6, 12, 4096):
+        assert lib.selective_scan_pack_saved_bytes(T, D, N, bad) == 0
+        assert lib.selective_scan_pack_bwd_scratch_bytes(T, D, N, bad) == 0
+    # the forward's scratch is small next to the dense states; the backward's
+    # holds dense replayed states unless it reads the forward's every 4 tokens
+    fwd = lib.selective_scan_pack_fwd_scratch_bytes(T, D, N)
+    dense = (T // 4) * D * N * 4
+    assert 0 < fwd < dense // 8
+    b4 = lib.selective_scan_pack_bwd_scratch_bytes(T, D, N, 4)
+    for ci in (0, 8, 2048):
+        assert lib.selective_scan_pack_bwd_scratch_bytes(T, D, N, ci) >= b4 + dense
+    # the single workspace of the other entry points: kept states every 4 tokens, then the scratch
+    assert lib.selective_scan_pack_workspace_bytes(T, D, N) == (lib.selective_scan_pack_saved_bytes(T, D, N, 4)
+                                                                + max(fwd, b4))
+
+
+def test_host_validation_checkpoint_interval(lib):
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+    big = 1 << 40
+    f = [fake] * 9 + [8, 4, 16, 1, NULL, 0, ctypes.c_float(0.0), NULL, 0, NULL, NULL]
+    for bad in (2, 12, 4096, -8):
+        assert lib.selective_scan_pack_fwd_ck(*f, bad, fake, big, fake, big, NULL) == 2
+    # a kept-state buffer is needed unless the interval is 0; the scratch always
+    assert lib.selective_scan_pack_fwd_ck(*f, 8, NULL, 0, fake, big, NULL) == 6
+    assert lib.selective_scan_pack_fwd_ck(*f, 8, fake, 16, fake, big, NULL) == 6
+    assert lib.selective_scan_pack_fwd_ck(*f, 0, NULL, 0, NULL, 0, NULL) == 6
+    assert lib.selective_scan_pack_fwd_ck(*f, 0, NULL, 0, fake, 16, NULL) == 6
+    # argument checks come before the buffers
+    f_bad_n = [fake] * 9 + [8, 4, 3, 1, NULL, 0, ctypes.c_float(0.0), NULL, 0, NULL, NULL]
+    assert lib.selective_scan_pack_fwd_ck(*f_bad_n, 8, NULL, 0, NULL, 0, NULL) == 4
+    b = [fake] * 16 + [8, 4, 16, 1, NULL, 0, ctypes.c_float(0.0), NULL, NULL, 0, NULL, NULL, NULL]
+    for bad in (3, 4096):
+        assert lib.selective_scan_pack_bwd_ck(*b, bad, fake, big, fake, big, NULL) == 2
+    assert lib.selective_scan_pack_bwd_ck(*b, 16, NULL, 0, fake, big, NULL) == 6
+    # with the interval 0 nothing was kept, but the scratch holds the replayed states
+    small = lib.selective_scan_pack_bwd_scratch_bytes(8, 4, 16, 4)
+    assert lib.selective_scan_pack_bwd_ck(*b, 0, NULL, 0, fake, small, NULL) == 6
+    b_nodD = [fake] * 5 + [NULL] + [fake] * 10 + [8, 4, 16, 1, NULL, 0, ctypes.c_float(0.0), NULL, NULL, 0, NULL,
+                                                  NULL, NULL]
+    assert lib.selective_scan_pack_bwd_ck(*b_nodD, 4, fake, big, fake, big, NULL) == 1

@@ -10,7 +10,8 @@ import pytest
 import torch
 
 import synth
-from tests.gpu_harness import TOL_GRAD, TOL_OUT, Dev, assert_close, npy, oracle_pipeline, to_dev
+from tests.gpu_harness import (TOL_GRAD, TOL_OUT, Dev, assert_close, nan_buffer, npy, oracle_pipeline,
+                               poison_scan_scratch, scan_workspace, to_dev)
 from tests.oracle_checks import read_golden
 
 pytestmark = pytest.mark.gpu
@@ -94,7 +95,8 @@ def test_conv_parity(orc, case):
     d = Dev(inp)
     wd, bd = to_dev(w), to_dev(b)
     u = ssp().conv1d_pack_fwd(d.x, wd, bd, d.pos, silu=silu)
-    dx, dw, db = ssp().conv1d_pack_bwd(d.x, wd, bd, d.pos, d.dout, silu=silu)
+    cws = nan_buffer(ssp().conv1d_pack_bwd_workspace_bytes(inp.T, D, W))
+    dx, dw, db = ssp().conv1d_pack_bwd(d.x, wd, bd, d.pos, d.dout, silu=silu, workspace=cws)
     pos, _ = orc.pack_indices(inp.cu_seqlens, inp.T)
     _, ru = orc.conv_fwd(synth.f64(inp.x), w.double().numpy(), b.double().numpy(), pos, silu=silu, threads=4)
     rdx, rdw, rdb = orc.conv_bwd(synth.f64(inp.x), w.double().numpy(), b.double().numpy(), pos,
@@ -145,7 +147,9 @@ def run_scan_gpu(inp, gate, skip):
     d = Dev(inp)
     z = d.z if gate else None
     Dp = d.Dp if skip else None
-    out, ws = ssp().selective_scan_pack_fwd(d.u, d.delta, d.A, d.B, d.C, Dp, z, d.pos)
+    ws = scan_workspace(inp.T, inp.D, inp.N)
+    out, ws = ssp().selective_scan_pack_fwd(d.u, d.delta, d.A, d.B, d.C, Dp, z, d.pos, workspace=ws)
+    poison_scan_scratch(ws, inp.T, inp.D, inp.N)
     g = ssp().selective_scan_pack_bwd(d.u, d.delta, d.A, d.B, d.C, Dp, z, d.pos, d.dout, ws)
     torch.cuda.synchronize()
     return out, g
@@ -203,7 +207,9 @@ def test_scan_ext_parity(orc, name):
     z = d.z if gate else None
     bt = to_dev(torch.from_numpy(bias)) if has_bias else None
     kw = dict(delta_bias=bt, delta_softplus=sp, gate_floor=floor)
-    out, ws = ssp().selective_scan_pack_fwd(d.u, d.delta, d.A, d.B, d.C, d.Dp, z, d.pos, **kw)
+    ws = scan_workspace(inp.T, inp.D, inp.N)
+    out, ws = ssp().selective_scan_pack_fwd(d.u, d.delta, d.A, d.B, d.C, d.Dp, z, d.pos, workspace=ws, **kw)
+    poison_scan_scratch(ws, inp.T, inp.D, inp.N)
     g = ssp().selective_scan_pack_bwd(d.u, d.delta, d.A, d.B, d.C, d.Dp, z, d.pos, d.dout, ws, **kw)
     torch.cuda.synchronize()
     pos, _ = orc.pack_indices(inp.cu_seqlens, inp.T)
@@ -407,8 +413,10 @@ def test_scan_states_parity(orc, name):
     Dp = d.Dp if skip else None
     h0_d = to_dev(torch.from_numpy(h0)) if h0 is not None else None
     dhT_d = to_dev(torch.from_numpy(dhT)) if dhT is not None else None
-    out, ws, hT = ssp().selective_scan_pack_fwd(d.u, d.delta, d.A, d.B, d.C, Dp, z, d.pos, cu_seqlens=d.cu,
-                                                initial_state=h0_d, final_state="hT" in parts, **kw)
+    ws = scan_workspace(inp.T, inp.D, inp.N)
+    out, ws, hT = ssp().selective_scan_pack_fwd(d.u, d.delta, d.A, d.B, d.C, Dp, z, d.pos, workspace=ws,
+                                                cu_seqlens=d.cu, initial_state=h0_d, final_state="hT" in parts, **kw)
+    poison_scan_scratch(ws, inp.T, inp.D, inp.N)
     g = ssp().selective_scan_pack_bwd(d.u, d.delta, d.A, d.B, d.C, Dp, z, d.pos, d.dout, ws, cu_seqlens=d.cu,
                                       initial_state=h0_d, dfinal_state=dhT_d, dinitial_state="dh0" in parts, **kw)
     torch.cuda.synchronize()
@@ -531,7 +539,8 @@ def test_conv_states_parity(orc, case):
     dcf_d = to_dev(dcf) if dcf is not None else None
     u, cf = ssp().conv1d_pack_fwd(d.x, wd, bd, d.pos, silu=silu, cu_seqlens=d.cu, conv_initial=ci_d,
                                   conv_final=True)
-    dx, dw, db, dci = ssp().conv1d_pack_bwd(d.x, wd, bd, d.pos, d.dout, silu=silu, cu_seqlens=d.cu,
+    cws = nan_buffer(ssp().conv1d_pack_bwd_states_workspace_bytes(inp.T, inp.D, W, inp.nseq))
+    dx, dw, db, dci = ssp().conv1d_pack_bwd(d.x, wd, bd, d.pos, d.dout, silu=silu, workspace=cws, cu_seqlens=d.cu,
                                             conv_initial=ci_d, dconv_final=dcf_d, dconv_initial=True)
     torch.cuda.synchronize()
     f = lambda t: None if t is None else synth.f64(t)
