@@ -47,7 +47,8 @@ typedef enum {
     SSMP_ERR_CU_SEQLENS = 3,  /* cu_seqlens invalid (written to dev_err) */
     SSMP_ERR_UNSUPPORTED = 4, /* dtype, d_state or conv width not supported */
     SSMP_ERR_HIP = 5,         /* a kernel launch failed */
-    SSMP_ERR_WORKSPACE = 6    /* workspace missing or smaller than queried */
+    SSMP_ERR_WORKSPACE = 6,   /* workspace missing or smaller than queried */
+    SSMP_ERR_TOO_LARGE = 7    /* needs more than the library's own scratch */
 } ssmp_status;
 
 typedef enum { SSMP_F32 = 0, SSMP_BF16 = 1 } ssmp_dtype;
@@ -58,7 +59,8 @@ const char *ssmp_status_string(int status);
 /* Version of this ABI (incremented on any change to the set of entry points
  * or their meaning; 2 added the _ex scan entry points, 3 the host packer
  * varlen_pack_plan, 4 the scan and conv entry points with sequence states,
- * 5 the scan entry points with a checkpoint interval). */
+ * 5 the scan entry points with a checkpoint interval, 6 the forward scan
+ * without allocation). */
 int ssmp_abi_version(void);
 
 /*
@@ -329,6 +331,31 @@ int selective_scan_pack_bwd_ck(const void *u, const void *delta, const float *A,
                                float *dinitial_state, int32_t ckpt_interval, const void *saved,
                                size_t saved_bytes, void *scratch, size_t scratch_bytes,
                                void *stream);
+
+/*
+ * selective_scan_pack_fwd_noalloc — selective_scan_pack_fwd_ck with
+ * ckpt_interval 0 (forward only, nothing kept) that allocates nothing and
+ * takes no workspace. For callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid it.
+ * Its scratch is a buffer of SSMP_NOALLOC_SCRATCH_BYTES inside the library,
+ * one per device, held by every device the library runs on until the
+ * process ends; a problem whose selective_scan_pack_fwd_scratch_bytes
+ * exceeds it is refused with SSMP_ERR_TOO_LARGE (with d_state 16: beyond
+ * about 256k tokens at d_inner 1536, 342k at 4096, 112k at 16384). Every
+ * call on a device shares that device's
+ * buffer: calls that may overlap on one device (different streams, or
+ * several host threads) race and must be serialised by the caller; calls in
+ * order on one stream are safe. The buffer needs no clearing between calls.
+ * The caller still passes inputs and outputs; other arguments, results and
+ * errors as selective_scan_pack_fwd_ck.
+ */
+#define SSMP_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int selective_scan_pack_fwd_noalloc(const void *u, const void *delta, const float *A, const void *B,
+                                    const void *C, const float *Dskip, const void *z,
+                                    const int32_t *pos, void *out, int64_t T, int32_t D, int32_t N,
+                                    int32_t dtype, const float *delta_bias, int32_t delta_softplus,
+                                    float gate_floor, const int32_t *cu_seqlens, int32_t nseq,
+                                    const float *initial_state, float *final_state, void *stream);
 
 /* Packing strategies of varlen_pack_plan. */
 enum ssmp_pack_strategy {

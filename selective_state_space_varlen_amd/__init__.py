@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     selective_scan_pack_bwd_scratch_bytes,
     selective_scan_pack_fwd,
     selective_scan_pack_fwd_ck,
+    selective_scan_pack_fwd_noalloc,
     selective_scan_pack_fwd_scratch_bytes,
     selective_scan_pack_saved_bytes,
     selective_scan_pack_workspace_bytes,

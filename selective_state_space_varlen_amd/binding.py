@@ -67,6 +67,9 @@ _SIGNATURES = {
                                                   _c_i64, _c_i32, _c_i32, _c_i32, _c_vp, _c_i32, ctypes.c_float,
                                                   _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_sz,
                                                   _c_vp, _c_sz, _c_vp]),
+    "selective_scan_pack_fwd_noalloc": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                                       _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_vp, _c_i32,
+                                                       ctypes.c_float, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp]),
     "conv1d_pack_fwd_states": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32,
                                               _c_i32, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp]),
     "conv1d_pack_bwd_states_workspace_bytes": (_c_sz, [_c_i64, _c_i32, _c_i32, _c_i32]),
@@ -524,3 +527,34 @@ def selective_scan_pack_bwd_ck(u, delta, A, B, C, Dskip, z, pos, dout, ckpt_inte
           _ptr(saved), _nbytes(saved), _ptr(scratch), _nbytes(scratch), _stream(u))
     return {"du": du, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "dz": dz, "ddelta_bias": ddb,
             "dinitial_state": di}
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20  # SSMP_NOALLOC_SCRATCH_BYTES
+
+
+def selective_scan_pack_fwd_noalloc(u, delta, A, B, C, Dskip, z, pos, out: Optional[torch.Tensor] = None,
+                                    delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
+                                    gate_floor: float = 0.0, cu_seqlens: Optional[torch.Tensor] = None,
+                                    initial_state: Optional[torch.Tensor] = None, final_state=False):
+    """The forward-only scan on the library's own scratch (the C entry point
+    allocates nothing; pass `out` and a final_state tensor to allocate
+    nothing here either). Returns (out, final_state or None). Calls that
+    may overlap on one device race."""
+    T, D = u.shape
+    N = A.shape[1]
+    dev = u.device
+    _check(u, "u"); _check(delta, "delta", (T, D), u.dtype, dev); _check(A, "A", (D, N), torch.float32, dev)
+    _check(B, "B", (T, N), u.dtype, dev); _check(C, "C", (T, N), u.dtype, dev)
+    _check(Dskip, "Dskip", (D,), torch.float32, dev); _check(z, "z", (T, D), u.dtype, dev)
+    _check(pos, "pos", (T,), torch.int32, dev); _check(delta_bias, "delta_bias", (D,), torch.float32, dev)
+    o = torch.empty_like(u) if out is None else out
+    _check(o, "out", (T, D), u.dtype, dev)
+    nseq, fs = 0, None
+    if cu_seqlens is not None or initial_state is not None or final_state is not False:
+        nseq = _nseq(cu_seqlens, dev)
+        fs = _out_or_new(final_state, (nseq, D, N), torch.float32, dev)
+        _check_states(nseq, (("initial_state", initial_state), ("final_state", fs)), D, N, dev)
+    _call("selective_scan_pack_fwd_noalloc", _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip),
+          _ptr(z), _ptr(pos), _ptr(o), T, D, N, _dtype_code(u), _ptr(delta_bias), int(bool(delta_softplus)),
+          float(gate_floor), _ptr(cu_seqlens), nseq, _ptr(initial_state), _ptr(fs), _stream(u))
+    return o, fs

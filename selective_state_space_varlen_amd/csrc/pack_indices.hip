@@ -71,8 +71,9 @@ extern "C" const char* ssmp_status_string(int status) {
         case SSMP_ERR_UNSUPPORTED: return "dtype, d_state or conv width not supported";
         case SSMP_ERR_HIP: return "a HIP kernel launch failed";
         case SSMP_ERR_WORKSPACE: return "workspace missing or too small";
+        case SSMP_ERR_TOO_LARGE: return "the problem needs more scratch than the library's own buffer holds";
         default: return "unknown status";
     }
 }
 
-extern "C" int ssmp_abi_version(void) { return 5; }
+extern "C" int ssmp_abi_version(void) { return 6; }

@@ -31,6 +31,8 @@
 // that already take the slow path for heads.
 #include "scan_common.h"
 
+#include <mutex>
+
 namespace ssmp {
 
 constexpr int kFwdBlock = 8;  // tokens per staged block in the forward kernels
@@ -668,6 +670,53 @@ extern "C" int selective_scan_pack_fwd_ck(const void* u, const void* delta, cons
                                              o, s)
                : scan_fwd_dispatch<float>(N, u, delta, A, B, C, Dskip, z, pos, out, sv, ckpt_interval, ws, T, D, o,
                                           s);
+}
+
+// ---------------------------------------------------------------------------
+// The forward-only scan without allocation: its scratch lives in a buffer of
+// the library's own, one per device, held until the process ends.
+// ---------------------------------------------------------------------------
+namespace ssmp {
+constexpr size_t kNoAllocBytes = SSMP_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kNoAllocBytes / sizeof(float)];
+
+// The device address of `scratch` on each device, looked up once per device
+// with that device current (host code must not use the array's name: it is
+// a host-side stand-in, not a device address).
+constexpr int kMaxDevices = 64;
+static float* g_scratch[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+static int noalloc_scratch(float** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SSMP_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SSMP_ERR_HIP;
+        g_scratch[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch[dev];
+    return SSMP_OK;
+}
+}  // namespace ssmp
+
+extern "C" int selective_scan_pack_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B,
+                                               const void* C, const float* Dskip, const void* z,
+                                               const int32_t* pos, void* out, int64_t T, int32_t D, int32_t N,
+                                               int32_t dtype, const float* delta_bias, int32_t delta_softplus,
+                                               float gate_floor, const int32_t* cu_seqlens, int32_t nseq,
+                                               const float* initial_state, float* final_state, void* stream) {
+    using namespace ssmp;
+    int st = scan_check_args(T, D, N, dtype);
+    if (st) return st;
+    const size_t need = selective_scan_pack_fwd_scratch_bytes(T, D, N);
+    if (need > kNoAllocBytes) return SSMP_ERR_TOO_LARGE;
+    float* scr = nullptr;
+    if (T > 0 && (st = noalloc_scratch(&scr))) return st;
+    return selective_scan_pack_fwd_ck(u, delta, A, B, C, Dskip, z, pos, out, T, D, N, dtype, delta_bias,
+                                      delta_softplus, gate_floor, cu_seqlens, nseq, initial_state, final_state, 0,
+                                      nullptr, 0, scr, kNoAllocBytes, stream);
 }
 
 extern "C" int selective_scan_pack_fwd_states(const void* u, const void* delta, const float* A, const void* B,

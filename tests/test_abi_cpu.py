@@ -49,10 +49,10 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings(lib):
     assert lib.ssmp_status_string(0) == b"ok"
-    for s in range(1, 7):
+    for s in range(1, 8):
         assert lib.ssmp_status_string(s) and lib.ssmp_status_string(s) != b"unknown status"
     assert lib.ssmp_status_string(99) == b"unknown status"
-    assert lib.ssmp_abi_version() == 5
+    assert lib.ssmp_abi_version() == 6
 
 
 def test_workspace_sizes(lib):
