@@ -44,6 +44,17 @@ struct Elt<float> {
     }
 };
 
+// p advanced by a 32-bit byte offset: a wave-uniform base plus a lane offset
+// that loads and stores take as they are (no 64-bit address arithmetic)
+template <typename T>
+__device__ __forceinline__ T* at_bytes(T* p, uint32_t o) {
+    return reinterpret_cast<T*>(reinterpret_cast<char*>(p) + o);
+}
+template <typename T>
+__device__ __forceinline__ const T* at_bytes(const T* p, uint32_t o) {
+    return reinterpret_cast<const T*>(reinterpret_cast<const char*>(p) + o);
+}
+
 template <>
 struct Elt<uint16_t> {
     static __device__ __forceinline__ float ld(const uint16_t* __restrict__ p, size_t i) { return bf16_to_f32(p[i]); }

@@ -255,7 +255,7 @@ struct BwdArgs {
     const T* z;
     const T* dout;
     const int32_t* pos;
-    const float* ckpt;
+    const float* ckpt;  // the state entering every kCK-th token
     const float* cin;
     T* du;
     T* ddelta;
@@ -268,7 +268,6 @@ struct BwdArgs {
     int64_t T_;
     int D;
     int lc;
-    int ckint;  // tokens between the checkpoint slots in ckpt
     ScanOpts opt;
 };
 
@@ -337,19 +336,25 @@ __device__ __forceinline__ float mul_bc(float src, float x) {
 // rows of register v / 16.
 template <int NS>
 struct BcRegs {
-    static constexpr int NH = Split<NS>::NH;
-    static constexpr int V = kSub * 2 * NH;
+    static constexpr int NH = Split<NS>::NH, K = kSub;
+    static constexpr int V = K * 2 * NH;
     static constexpr int R = (V + 15) / 16;
     float r[R];
     // bc: fp32 rows [T][2N] (B then C)
     __device__ __forceinline__ void load(const float* __restrict__ bc, int64_t tb, int64_t T_, int q, int lane) {
         const int j = lane % 16;
+        const float* __restrict__ rows = bc + (size_t)tb * 2 * NS;  // uniform: the block's first row
+        const int last = (int)((T_ - 1 - tb) < K ? (T_ - 1 - tb) : K);  // rows past the tensor read its last
 #pragma unroll
         for (int k = 0; k < R; ++k) {
             const int v = k * 16 + j;
             const int kk = v / (2 * NH), kind = (v / NH) % 2, i = v % NH;
-            const int64_t t = tb + kk;
-            r[k] = (v < V && t < T_) ? bc[(size_t)t * 2 * NS + kind * NS + q * NH + i] : 0.0f;
+            // every lane loads (the token clamped into the tensor), so that no
+            // load waits behind a branch; tokens past the block's end are
+            // never used
+            const int row = kk < last ? kk : last;
+            const float x = *at_bytes(rows, (uint32_t)((row * 2 * NS + kind * NS + q * NH + i) * 4));
+            r[k] = (v < V) ? x : 0.0f;
         }
     }
 };
@@ -557,11 +562,12 @@ __device__ __forceinline__ void bwd_reverse(Sh& sh, const TokVals& tv, const BcR
             const int tk = o / (2 * NH), kind = (o / NH) % 2, i = o % NH;
             const int kk = 2 * kp + tk;
             const float4* xv = reinterpret_cast<const float4*>(myx + ((tk * 2 + kind) * NH + i) * kXRow) + sl;
-            float acc = 0.0f;
+            float acc;
 #pragma unroll
             for (int m = 0; m < CPL / 4; ++m) {
                 const float4 xa = xv[m * LPO];
-                acc += (xa.x + xa.y) + (xa.z + xa.w);
+                const float v = (xa.x + xa.y) + (xa.z + xa.w);
+                acc = (m == 0) ? v : acc + v;
             }
             acc = group_sum<LPO>(acc);
             // every lane of the output stores the same value: no lane-dependent branch
@@ -603,12 +609,16 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
     const int64_t c_ = blockIdx.x / ngroup;
     int d[kCl], dd[kCl];
     bool act[kCl];
+    const bool whole = (g + 1) * kGroupCh <= D;  // every lane's channels exist
 #pragma unroll
     for (int c = 0; c < kCl; ++c) {
         d[c] = g * kGroupCh + kCl * lane + c;
         act[c] = d[c] < D;
         dd[c] = act[c] ? d[c] : D - 1;
     }
+    uint32_t bo[kCl];  // byte offsets of the lane's channels in a (T, D) row
+#pragma unroll
+    for (int c = 0; c < kCl; ++c) bo[c] = (uint32_t)dd[c] * (uint32_t)sizeof(T);
     const int64_t t0 = c_ * p.lc;
     const int64_t t1 = (t0 + p.lc < T_) ? t0 + p.lc : T_;
     const size_t ND = (size_t)NS * D;
@@ -668,17 +678,18 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
             const T* __restrict__ g_r = p.dout + rb;
 #pragma unroll
             for (int c = 0; c < kCl; ++c) {
-                b.ru[j][c] = Elt<T>::raw(u_r, dd[c]);
-                b.rd[j][c] = Elt<T>::raw(d_r, dd[c]);
-                b.rz[j][c] = GATE ? Elt<T>::raw(z_r, dd[c]) : 0u;
-                b.rg[j][c] = Elt<T>::raw(g_r, dd[c]);
+                b.ru[j][c] = Elt<T>::raw(at_bytes(u_r, bo[c]), 0);
+                b.rd[j][c] = Elt<T>::raw(at_bytes(d_r, bo[c]), 0);
+                b.rz[j][c] = GATE ? Elt<T>::raw(at_bytes(z_r, bo[c]), 0) : 0u;
+                b.rg[j][c] = Elt<T>::raw(at_bytes(g_r, bo[c]), 0);
             }
         }
-        const float* __restrict__ slot = p.ckpt + (size_t)(tb / p.ckint) * ND;
+        const float* __restrict__ slot = p.ckpt + ((uint64_t)tb / kCK) * ND;  // tb >= 0
 #pragma unroll
         for (int c = 0; c < kCl; ++c) ck_load<NS, NH>(slot, dd[c], D, n0, true, b.hn[c]);
         b.bc.load(bcp, tb, T_, q, lane);
-        b.pos = p.pos[(tb + lane < T_) ? tb + lane : T_ - 1];
+        const int pl = (int)((T_ - 1 - tb) < lane ? (T_ - 1 - tb) : lane);
+        b.pos = *at_bytes(p.pos + tb, (uint32_t)pl * 4u);
     };
 
     // one block: jb its index in the chunk, b its prefetched inputs, which it
@@ -747,9 +758,9 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
         for (int j = 0; j < KQ; ++j) {
             const int kk = q + j * SW;
             const bool tok = kk < nb;  // tokens past the block store to the sink
-            float2 y = make_float2(0.0f, 0.0f), sB = y, sA = y;
+            float2 y = sh.part[0][kk][0][lane], sB = sh.part[1][kk][0][lane], sA = sh.part[2][kk][0][lane];
 #pragma unroll
-            for (int w = 0; w < SW; ++w) {
+            for (int w = 1; w < SW; ++w) {
                 const float2 a = sh.part[0][kk][w][lane], bb = sh.part[1][kk][w][lane], cc = sh.part[2][kk][w][lane];
                 y.x += a.x; y.y += a.y;
                 sB.x += bb.x; sB.y += bb.y;
@@ -769,12 +780,17 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
                     dbacc[c] += (tok && act[c]) ? ddv : 0.0f;
                 }
                 dDacc[c] = __builtin_fmaf(egg[j][c], uu, dDacc[c]);
-                const bool w = tok && act[c];
-                Elt<T>::st(w ? p.du + rb : sinkT, w ? d[c] : 0, duv);
-                Elt<T>::st(w ? p.ddelta + rb : sinkT, w ? d[c] : 1, ddv);
-                if constexpr (GATE) {
-                    const float sg = esg[j][c], zz = ez[j][c];
-                    Elt<T>::st(w ? p.dz + rb : sinkT, w ? d[c] : 2, eg[j][c] * yy * sg * (1.0f + zz * (1.0f - sg)));
+                const float dzv = GATE ? eg[j][c] * yy * esg[j][c] * (1.0f + ez[j][c] * (1.0f - esg[j][c])) : 0.0f;
+                if (whole && nb == K) {
+                    // every lane stores into the tensors (a uniform branch)
+                    Elt<T>::st(at_bytes(p.du + rb, bo[c]), 0, duv);
+                    Elt<T>::st(at_bytes(p.ddelta + rb, bo[c]), 0, ddv);
+                    if constexpr (GATE) Elt<T>::st(at_bytes(p.dz + rb, bo[c]), 0, dzv);
+                } else {
+                    const bool w = tok && act[c];
+                    Elt<T>::st(w ? p.du + rb : sinkT, w ? d[c] : 0, duv);
+                    Elt<T>::st(w ? p.ddelta + rb : sinkT, w ? d[c] : 1, ddv);
+                    if constexpr (GATE) Elt<T>::st(w ? p.dz + rb : sinkT, w ? d[c] : 2, dzv);
                 }
             }
         }
@@ -894,7 +910,7 @@ static int scan_bwd_launch(const void* u, const void* delta, const float* A, con
     a.u = (const T*)u; a.delta = (const T*)delta; a.A = A; a.bc = ws + L.bc; a.Dskip = Dskip;
     a.z = (const T*)z; a.dout = (const T*)dout; a.pos = pos; a.ckpt = ckpt; a.cin = ws + L.cin;
     a.du = (T*)du; a.ddelta = (T*)ddelta; a.dz = (T*)dz; a.dApart = ws + L.dApart; a.dDpart = ws + L.dDpart;
-    a.dbpart = ws + L.dbpart; a.dBC = ws + L.dBC; a.sink = ws + L.sink; a.T_ = T_; a.D = D; a.lc = lc; a.ckint = kCK; a.opt = opt;
+    a.dbpart = ws + L.dbpart; a.dBC = ws + L.dBC; a.sink = ws + L.sink; a.T_ = T_; a.D = D; a.lc = lc; a.opt = opt;
     constexpr int SW = Split<NS>::SW;
     const int64_t ngroup = (D + kGroupCh - 1) / kGroupCh;
     const dim3 mgrid((unsigned)(ngroup * nchunk));
