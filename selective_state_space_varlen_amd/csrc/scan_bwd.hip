@@ -369,13 +369,20 @@ struct BcIdx {
 // rows by eight lanes fall on different banks.
 constexpr int kXRow = kWave + 16;
 
-// LDS of a backward workgroup
+// What one block shares between the waves; blocks alternate between two of
+// them, so that one barrier a block orders every access (see the block loop).
 template <int NS>
-struct BwdShared {
-    static constexpr int NH = Split<NS>::NH, SW = Split<NS>::SW, K = kSub;
+struct BwdBuf {
+    static constexpr int SW = Split<NS>::SW, K = kSub;
     float4 stp[K][kWave];             // per token, per lane: step and step*u of its two channels
     float2 gg[K][kWave];              // per token, per lane: g of its two channels
     float2 part[3][K][SW][kWave];     // per wave: y, sum_n dh B, sum_n A r of the lane's channels
+};
+// LDS of a backward workgroup
+template <int NS>
+struct BwdShared {
+    static constexpr int NH = Split<NS>::NH, SW = Split<NS>::SW;
+    BwdBuf<NS> buf[2];
     float xb[SW][4 * NH][kXRow];      // per wave, a token pair: dB and dC terms of its states
 };
 
@@ -389,8 +396,8 @@ struct TokVals {
     float dt[kSub][kCl], dtu[kSub][kCl], gg[kSub][kCl];
 };
 
-template <bool SAFE, bool ST, int NS, typename Sh>
-__device__ __forceinline__ void bwd_replay(Sh& sh, const TokVals& tv, const BcRegs<NS>& bc, int nb, uint32_t heads, int lane, int q,
+template <bool SAFE, bool ST, int NS>
+__device__ __forceinline__ void bwd_replay(BwdBuf<NS>& bf, const TokVals& tv, const BcRegs<NS>& bc, int nb, uint32_t heads, int lane, int q,
                                            const bool (&act)[kCl], const float (&A2)[kCl][Split<NS>::NH],
                                            const float (&hin)[kCl][Split<NS>::NH],
                                            float (&hh)[kSub][kCl][Split<NS>::NH],
@@ -443,7 +450,7 @@ __device__ __forceinline__ void bwd_replay(Sh& sh, const TokVals& tv, const BcRe
             }
         };
         static_for<NH>(state);
-        sh.part[0][kk][q][lane] = make_float2(y[0], y[1]);
+        bf.part[0][kk][q][lane] = make_float2(y[0], y[1]);
     };
     static_for_until<K>(step, SAFE ? nb : K);
 }
@@ -453,8 +460,8 @@ __device__ __forceinline__ void bwd_replay(Sh& sh, const TokVals& tv, const BcRe
 // two tokens. The lane's two channels are added in registers; each value is
 // then added up over the wave's lanes by LPO lanes reading the terms the wave
 // left in LDS.
-template <bool SAFE, bool ST, int NS, typename Sh>
-__device__ __forceinline__ void bwd_reverse(Sh& sh, const TokVals& tv, const BcRegs<NS>& bc, int nb, uint32_t heads, int lane, int q,
+template <bool SAFE, bool ST, int NS>
+__device__ __forceinline__ void bwd_reverse(BwdBuf<NS>& bf, float* __restrict__ myx, const TokVals& tv, const BcRegs<NS>& bc, int nb, uint32_t heads, int lane, int q,
                                             const bool (&act)[kCl], const float (&A2)[kCl][Split<NS>::NH],
                                             const float (&hin)[kCl][Split<NS>::NH],
                                             const float (&hh)[kSub][kCl][Split<NS>::NH],
@@ -467,7 +474,6 @@ __device__ __forceinline__ void bwd_reverse(Sh& sh, const TokVals& tv, const BcR
     constexpr int CPL = kWave / LPO;       // lanes' terms each of them adds
     static_assert(K % 2 == 0 && CPL % 4 == 0, "tiling");
     const int n0 = q * NH;
-    float* __restrict__ myx = &sh.xb[q][0][0];
     auto tok = [&](auto KKc) {
         constexpr int kk = decltype(KKc)::value;
         constexpr int tk = kk % 2;
@@ -547,8 +553,8 @@ __device__ __forceinline__ void bwd_reverse(Sh& sh, const TokVals& tv, const BcR
             };
             static_for<NH>(state);
         }
-        sh.part[1][kk][q][lane] = make_float2(sumB[0], sumB[1]);
-        sh.part[2][kk][q][lane] = make_float2(sumAr[0], sumAr[1]);
+        bf.part[1][kk][q][lane] = make_float2(sumB[0], sumB[1]);
+        bf.part[2][kk][q][lane] = make_float2(sumAr[0], sumAr[1]);
     };
     auto pair = [&](auto KPc) {
         constexpr int kp = K / 2 - 1 - decltype(KPc)::value;  // pairs right to left
@@ -692,16 +698,26 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
         b.pos = *at_bytes(p.pos + tb, (uint32_t)pl * 4u);
     };
 
-    // one block: jb its index in the chunk, b its prefetched inputs, which it
-    // refills with those of block jb - 2
-    auto block = [&](Pre& b, int64_t jb) {
+    // The per-block work in three parts: the prologue maps this wave's own
+    // tokens (every SW-th) and shares them through bf; the main part replays
+    // the block and runs the reverse step, leaving the per-wave sums in bf and
+    // refilling b with the inputs of block jb - 2; the epilogue adds those
+    // sums for the wave's own tokens and stores their gradients.
+    // The loop runs main(jb), prologue(jb - 1), one barrier, epilogue(jb), so
+    // with blocks alternating between the two bf buffers one barrier a block
+    // orders every shared access: prologue(jb - 1) writes the buffer that
+    // main(jb + 1) read before the previous barrier, main(jb - 1) reads it
+    // after this one, and the per-wave sums of main(jb) are read after this
+    // barrier and written again (by main(jb - 2)) after the next one.
+    struct EVals {
+        float u[KQ][kCl], dt[KQ][kCl], gg[KQ][kCl], fz[KQ][kCl], sl[KQ][kCl];  // fz: dz = (y + Dskip u) fz
+    };
+    auto block_nb = [&](int64_t jb) {
         const int64_t tb = t0 + jb * K;
-        const int nb = (int)(((tb + K < t1) ? tb + K : t1) - tb);
-        // head flags of the block, from the prefetched positions: bit k for token tb + k
-        const uint32_t heads = (uint32_t)__ballot(lane < K && tb + lane < T_ && b.pos == 0);
-
-        // 1. prologue (own tokens)
-        float eu[KQ][kCl], edt[KQ][kCl], egg[KQ][kCl], esl[KQ][kCl], esg[KQ][kCl], ez[KQ][kCl], eg[KQ][kCl];
+        return (int)(((tb + K < t1) ? tb + K : t1) - tb);
+    };
+    auto prologue = [&](const Pre& b, int64_t jb, BwdBuf<NS>& bf, EVals& ev) {
+        const int nb = block_nb(jb);
 #pragma unroll
         for (int j = 0; j < KQ; ++j) {
             const int kk = q + j * SW;
@@ -715,53 +731,58 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
                 float dt = XS ? sm[c].eff(rdv, sl) : rdv;
                 dt = v ? dt : 0.0f;  // lanes past D and tokens past the block replay zeros
                 const float uu = v ? Elt<T>::cvt(b.ru[j][c]) : 0.0f;
-                float gg = rgv, sg = 0.0f;
+                float gg = rgv, fz = 0.0f;
                 if constexpr (GATE) {
-                    sg = sigmoid_fast(rzv);
+                    const float sg = sigmoid_fast(rzv);
                     gg *= __builtin_fmaf(rzv, sg, gf);
+                    fz = rgv * sg * (1.0f + rzv * (1.0f - sg));
                 }
                 gg = v ? gg : 0.0f;
                 dtv[c] = dt; dtu[c] = dt * uu; ggv[c] = gg;
-                eu[j][c] = uu; edt[j][c] = dt; egg[j][c] = gg; esl[j][c] = sl; esg[j][c] = sg;
-                ez[j][c] = rzv; eg[j][c] = rgv;
+                ev.u[j][c] = uu; ev.dt[j][c] = dt; ev.gg[j][c] = gg; ev.fz[j][c] = fz; ev.sl[j][c] = sl;
             }
-            sh.stp[kk][lane] = make_float4(dtv[0], dtu[0], dtv[1], dtu[1]);
-            sh.gg[kk][lane] = make_float2(ggv[0], ggv[1]);
+            bf.stp[kk][lane] = make_float4(dtv[0], dtu[0], dtv[1], dtu[1]);
+            bf.gg[kk][lane] = make_float2(ggv[0], ggv[1]);
         }
-        __syncthreads();
-
-        // 2-3. replay from the checkpoint at tb, then the reverse step
+    };
+    auto main_part = [&](Pre& b, int64_t jb, BwdBuf<NS>& bf) {
+        const int64_t tb = t0 + jb * K;
+        const int nb = block_nb(jb);
+        // head flags of the block, from the prefetched positions: bit k for token tb + k
+        const uint32_t heads = (uint32_t)__ballot(lane < K && tb + lane < T_ && b.pos == 0);
         float hh[K][kCl][NH], ak[K][kCl][NH];
         TokVals tv;
 #pragma unroll
         for (int kk = 0; kk < K; ++kk) {
-            const float4 st = sh.stp[kk][lane];
-            const float2 g2 = sh.gg[kk][lane];
+            const float4 st = bf.stp[kk][lane];
+            const float2 g2 = bf.gg[kk][lane];
             tv.dt[kk][0] = st.x; tv.dtu[kk][0] = st.y; tv.dt[kk][1] = st.z; tv.dtu[kk][1] = st.w;
             tv.gg[kk][0] = g2.x; tv.gg[kk][1] = g2.y;
         }
         float* __restrict__ dbc_row = p.dBC + ((size_t)g * T_ + tb) * 2 * NS;
+        float* __restrict__ myx = &sh.xb[q][0][0];
         if (heads == 0 && nb == K) {
-            bwd_replay<false, ST, NS>(sh, tv, b.bc, nb, heads, lane, q, act, A2, b.hn, hh, ak, p.opt, tb, D, dd);
-            bwd_reverse<false, ST, NS>(sh, tv, b.bc, nb, heads, lane, q, act, A2, b.hn, hh, ak, carry, dA, dbc_row, p.sink, p.opt,
-                                       tb, D, dd);
+            bwd_replay<false, ST, NS>(bf, tv, b.bc, nb, heads, lane, q, act, A2, b.hn, hh, ak, p.opt, tb, D, dd);
+            bwd_reverse<false, ST, NS>(bf, myx, tv, b.bc, nb, heads, lane, q, act, A2, b.hn, hh, ak, carry, dA,
+                                       dbc_row, p.sink, p.opt, tb, D, dd);
         } else {
-            bwd_replay<true, ST, NS>(sh, tv, b.bc, nb, heads, lane, q, act, A2, b.hn, hh, ak, p.opt, tb, D, dd);
-            bwd_reverse<true, ST, NS>(sh, tv, b.bc, nb, heads, lane, q, act, A2, b.hn, hh, ak, carry, dA, dbc_row, p.sink, p.opt,
-                                      tb, D, dd);
+            bwd_replay<true, ST, NS>(bf, tv, b.bc, nb, heads, lane, q, act, A2, b.hn, hh, ak, p.opt, tb, D, dd);
+            bwd_reverse<true, ST, NS>(bf, myx, tv, b.bc, nb, heads, lane, q, act, A2, b.hn, hh, ak, carry, dA,
+                                      dbc_row, p.sink, p.opt, tb, D, dd);
         }
         prefetch(b, tb >= t0 + 2 * K ? tb - 2 * K : t0);  // past the chunk start: a dummy reload
-        __syncthreads();
-
-        // 4. epilogue (own tokens)
+    };
+    auto epilogue = [&](int64_t jb, const BwdBuf<NS>& bf, const EVals& ev) {
+        const int64_t tb = t0 + jb * K;
+        const int nb = block_nb(jb);
 #pragma unroll
         for (int j = 0; j < KQ; ++j) {
             const int kk = q + j * SW;
             const bool tok = kk < nb;  // tokens past the block store to the sink
-            float2 y = sh.part[0][kk][0][lane], sB = sh.part[1][kk][0][lane], sA = sh.part[2][kk][0][lane];
+            float2 y = bf.part[0][kk][0][lane], sB = bf.part[1][kk][0][lane], sA = bf.part[2][kk][0][lane];
 #pragma unroll
             for (int w = 1; w < SW; ++w) {
-                const float2 a = sh.part[0][kk][w][lane], bb = sh.part[1][kk][w][lane], cc = sh.part[2][kk][w][lane];
+                const float2 a = bf.part[0][kk][w][lane], bb = bf.part[1][kk][w][lane], cc = bf.part[2][kk][w][lane];
                 y.x += a.x; y.y += a.y;
                 sB.x += bb.x; sB.y += bb.y;
                 sA.x += cc.x; sA.y += cc.y;
@@ -771,16 +792,16 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
             T* __restrict__ sinkT = reinterpret_cast<T*>(p.sink);
 #pragma unroll
             for (int c = 0; c < kCl; ++c) {
-                const float uu = eu[j][c];
+                const float uu = ev.u[j][c];
                 const float yy = __builtin_fmaf(Dv[c], uu, yv[c]);
-                const float duv = __builtin_fmaf(egg[j][c], Dv[c], edt[j][c] * sBv[c]);
+                const float duv = __builtin_fmaf(ev.gg[j][c], Dv[c], ev.dt[j][c] * sBv[c]);
                 float ddv = __builtin_fmaf(uu, sBv[c], sAv[c] * kLn2);
                 if constexpr (XS) {
-                    ddv *= esl[j][c];  // with respect to the stored step
+                    ddv *= ev.sl[j][c];  // with respect to the stored step
                     dbacc[c] += (tok && act[c]) ? ddv : 0.0f;
                 }
-                dDacc[c] = __builtin_fmaf(egg[j][c], uu, dDacc[c]);
-                const float dzv = GATE ? eg[j][c] * yy * esg[j][c] * (1.0f + ez[j][c] * (1.0f - esg[j][c])) : 0.0f;
+                dDacc[c] = __builtin_fmaf(ev.gg[j][c], uu, dDacc[c]);
+                const float dzv = yy * ev.fz[j][c];
                 if (whole && nb == K) {
                     // every lane stores into the tensors (a uniform branch)
                     Elt<T>::st(at_bytes(p.du + rb, bo[c]), 0, duv);
@@ -796,15 +817,46 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
         }
     };
 
+    // blocks right to left; block jb uses pre[(nblk - 1 - jb) % 2], buf and
+    // e-values of the same parity
     const int64_t nblk = (t1 - t0 + K - 1) / K;
     prefetch(pre[0], t0 + (nblk - 1) * K);
     prefetch(pre[1], nblk >= 2 ? t0 + (nblk - 2) * K : t0);
-    int64_t jb = nblk - 1;
-    for (; jb >= 1; jb -= 2) {
-        block(pre[0], jb);
-        block(pre[1], jb - 1);
+    if constexpr (SW == 1) {
+        // one wave: its barriers cost nothing, and one set of e-values keeps
+        // its registers
+        EVals ev;
+        for (int64_t jb = nblk - 1; jb >= 0; jb -= 2) {
+            prologue(pre[0], jb, sh.buf[0], ev);
+            __syncthreads();
+            main_part(pre[0], jb, sh.buf[0]);
+            __syncthreads();
+            epilogue(jb, sh.buf[0], ev);
+            if (jb == 0) break;
+            __syncthreads();
+            prologue(pre[1], jb - 1, sh.buf[0], ev);
+            __syncthreads();
+            main_part(pre[1], jb - 1, sh.buf[0]);
+            __syncthreads();
+            epilogue(jb - 1, sh.buf[0], ev);
+            __syncthreads();
+        }
+    } else {
+        EVals ev[2];
+        prologue(pre[0], nblk - 1, sh.buf[0], ev[0]);
+        __syncthreads();
+        for (int64_t jb = nblk - 1; jb >= 0; jb -= 2) {
+            main_part(pre[0], jb, sh.buf[0]);
+            if (jb >= 1) prologue(pre[1], jb - 1, sh.buf[1], ev[1]);
+            __syncthreads();
+            epilogue(jb, sh.buf[0], ev[0]);
+            if (jb == 0) break;
+            main_part(pre[1], jb - 1, sh.buf[1]);
+            if (jb >= 2) prologue(pre[0], jb - 2, sh.buf[0], ev[0]);
+            __syncthreads();
+            epilogue(jb - 1, sh.buf[1], ev[1]);
+        }
     }
-    if (jb == 0) block(pre[0], 0);
 
     // per-chunk partial sums: dA per state; dD and d bias added over the waves in order
 #pragma unroll
@@ -814,14 +866,14 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
             for (int i = 0; i < NH; ++i) p.dApart[(size_t)c_ * ND + (size_t)(n0 + i) * D + d[c]] = dA[c][i];
         }
     __syncthreads();
-    sh.part[0][0][q][lane] = make_float2(dDacc[0], dDacc[1]);
-    sh.part[1][0][q][lane] = make_float2(dbacc[0], dbacc[1]);
+    sh.buf[0].part[0][0][q][lane] = make_float2(dDacc[0], dDacc[1]);
+    sh.buf[0].part[1][0][q][lane] = make_float2(dbacc[0], dbacc[1]);
     __syncthreads();
     if (q == 0) {
         float2 sD = make_float2(0.0f, 0.0f), sb = sD;
 #pragma unroll
         for (int w = 0; w < SW; ++w) {
-            const float2 a = sh.part[0][0][w][lane], b = sh.part[1][0][w][lane];
+            const float2 a = sh.buf[0].part[0][0][w][lane], b = sh.buf[0].part[1][0][w][lane];
             sD.x += a.x; sD.y += a.y;
             sb.x += b.x; sb.y += b.y;
         }
