@@ -12,6 +12,7 @@ dB/dC, whose per-block partials are summed here in block order.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -76,6 +77,8 @@ class Oracle:
         L.oracle_scan_fwd_state.restype = ctypes.c_int
         L.oracle_scan_fwd_state.argtypes = [i64, i32, i32, _ip, i32, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
                                             _dp, i32, ctypes.c_double, _dp, i32, i32, _dp, _dp, _dp]
+        L.oracle_set_abs_terms.restype = None
+        L.oracle_set_abs_terms.argtypes = [ctypes.c_int]
         L.oracle_scan_bwd_state.restype = ctypes.c_int
         L.oracle_scan_bwd_state.argtypes = [i64, i32, i32, _ip, i32, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
                                             _dp, i32, ctypes.c_double, _dp, _dp, _dp, i32, i32,
@@ -104,6 +107,18 @@ class Oracle:
             return list(ex.map(lambda blk: fn(*blk), blocks))
 
     # -------------------------------------------------------------- interface
+    @contextlib.contextmanager
+    def error_scales(self):
+        """Within the block, the backward functions (scan_bwd, scan_bwd_state,
+        conv_bwd, conv_bwd_state, backward) return for every output the sum
+        of the magnitudes of the terms that make it up, the scale of the
+        rounding error of that sum (see oracle_set_abs_terms in the C file)."""
+        self.lib.oracle_set_abs_terms(1)
+        try:
+            yield
+        finally:
+            self.lib.oracle_set_abs_terms(0)
+
     def pack_indices(self, cu_seqlens, T: int):
         cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
         nseq = len(cu) - 1

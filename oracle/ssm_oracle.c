@@ -38,6 +38,22 @@
 #define ORACLE_ERR_CU_SEQLENS 3
 #define ORACLE_ERR_ALLOC 6
 
+/*
+ * Error-scale mode of the backward functions. With it on, every sum they
+ * form (over tokens, channels, states, taps, and the recursions over time)
+ * adds the absolute value of each term instead of the term, and products
+ * take the absolute value of their signed factors; the nonlinear factors
+ * (sigmoid, the SiLU derivative, exp) keep their values. Each output is then
+ * the sum of the magnitudes of the terms that make it up: the scale of the
+ * rounding error of any evaluation of that sum, which a comparison of a sum
+ * that cancels needs in place of the size of its result. Off, term() is the
+ * identity and every expression rounds exactly as written. Process-wide; set
+ * it only while no oracle call runs.
+ */
+static int g_abs_terms = 0;
+void oracle_set_abs_terms(int on) { g_abs_terms = on != 0; }
+static double term(double v) { return g_abs_terms ? fabs(v) : v; }
+
 static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
 /* softplus(v) = log(1 + exp(v)), in a form that neither overflows nor loses
  * the tail: max(v, 0) + log1p(exp(-|v|)) */
@@ -204,15 +220,15 @@ int oracle_scan_bwd_ex(int64_t T, int32_t D, int32_t N, const int32_t *pos,
                 const double bu = dt * B[t * N + n] * uu;
                 double hn;
                 if (head) {
-                    hn = bu;
+                    hn = term(bu);
                 } else {
                     const double a = exp(dt * A[(int64_t)d * N + n]);
-                    hn = a * hs[(t - 1) * N + n] + bu;
+                    hn = a * hs[(t - 1) * N + n] + term(bu);
                 }
                 hs[t * N + n] = hn;
-                acc += C[t * N + n] * hn;
+                acc += term(C[t * N + n] * hn);
             }
-            if (Dp) acc += Dp[d] * uu;
+            if (Dp) acc += term(Dp[d] * uu);
             ys[t] = acc;
         }
         /* reverse */
@@ -230,29 +246,29 @@ int oracle_scan_bwd_ex(int64_t T, int32_t D, int32_t N, const int32_t *pos,
             if (z) {
                 const double zz = z[t * D + d];
                 const double s = sigmoid(zz);
-                g = go * (zz * s + gate_floor);
-                if (dz) dz[t * D + d] = go * ys[t] * s * (1.0 + zz * (1.0 - s));
+                g = term(go) * (term(zz * s) + gate_floor);
+                if (dz) dz[t * D + d] = term(go * ys[t] * s * (1.0 + zz * (1.0 - s)));
             } else if (dz) {
                 dz[t * D + d] = 0.0;
             }
-            double du_acc = Dp ? g * Dp[d] : 0.0;
+            double du_acc = Dp ? term(g * Dp[d]) : 0.0;
             double ddt = 0.0;
-            dDp_acc += g * uu;
+            dDp_acc += term(g * uu);
             for (int32_t n = 0; n < N; ++n) {
                 const double Bn = B[t * N + n];
-                const double dh = g * C[t * N + n] + c[n];
-                dC[t * N + n] += g * hs[t * N + n];
-                dB[t * N + n] += dh * dt * uu;
-                du_acc += dh * dt * Bn;
+                const double dh = term(g * C[t * N + n]) + c[n];
+                dC[t * N + n] += term(g * hs[t * N + n]);
+                dB[t * N + n] += term(dh * dt * uu);
+                du_acc += term(dh * dt * Bn);
                 if (head) {
-                    ddt += dh * (Bn * uu);
+                    ddt += term(dh * (Bn * uu));
                     c[n] = 0.0;
                 } else {
                     const double An = A[(int64_t)d * N + n];
                     const double a = exp(dt * An);
                     const double hp = hs[(t - 1) * N + n];
-                    ddt += dh * (Bn * uu + An * a * hp);
-                    dA_d[n] += dh * dt * a * hp;
+                    ddt += term(dh) * (term(Bn * uu) + term(An * a * hp));
+                    dA_d[n] += term(dh * dt * a * hp);
                     c[n] = a * dh;
                 }
             }
@@ -260,7 +276,7 @@ int oracle_scan_bwd_ex(int64_t T, int32_t D, int32_t N, const int32_t *pos,
             /* through the step map: d delta_eff / d delta */
             const double ddraw = ddt * delta_grad(delta[t * D + d], dbias, d, sp);
             ddelta[t * D + d] = ddraw;
-            ddb_acc += ddraw;
+            ddb_acc += term(ddraw);
         }
         if (dDp) dDp[d] = dDp_acc;
         if (ddbias) ddbias[d] = ddb_acc;
@@ -306,9 +322,9 @@ int oracle_conv_bwd(int64_t T, int32_t D, int32_t W, const int32_t *pos,
             const double g = du[t * D + d];
             if (silu) {
                 const double s = sigmoid(v);
-                gv[t] = g * s * (1.0 + v * (1.0 - s));
+                gv[t] = term(g * s * (1.0 + v * (1.0 - s)));
             } else {
-                gv[t] = g;
+                gv[t] = term(g);
             }
         }
         double dbd = 0.0;
@@ -317,13 +333,13 @@ int oracle_conv_bwd(int64_t T, int32_t D, int32_t W, const int32_t *pos,
         for (int32_t k = 0; k < W; ++k) {
             double acc = 0.0;
             for (int64_t t = 0; t < T; ++t)
-                if (k <= pos[t]) acc += gv[t] * x[(t - k) * D + d];
+                if (k <= pos[t]) acc += term(gv[t] * x[(t - k) * D + d]);
             dw[(int64_t)d * W + (W - 1 - k)] = acc;
         }
         for (int64_t s = 0; s < T; ++s) {
             double acc = 0.0;
             for (int32_t k = 0; k < W; ++k)
-                if (s + k < T && k <= pos[s + k]) acc += w[(int64_t)d * W + (W - 1 - k)] * gv[s + k];
+                if (s + k < T && k <= pos[s + k]) acc += term(w[(int64_t)d * W + (W - 1 - k)] * gv[s + k]);
             dx[s * D + d] = acc;
         }
     }
@@ -431,9 +447,9 @@ int oracle_conv_bwd_state(int64_t T, int32_t D, int32_t W, const int32_t *cu, in
                 const double g = du[t * D + d];
                 if (silu) {
                     const double sg = sigmoid(vv);
-                    gv[t] = g * sg * (1.0 + vv * (1.0 - sg));
+                    gv[t] = term(g * sg * (1.0 + vv * (1.0 - sg)));
                 } else {
-                    gv[t] = g;
+                    gv[t] = term(g);
                 }
             }
         }
@@ -443,7 +459,7 @@ int oracle_conv_bwd_state(int64_t T, int32_t D, int32_t W, const int32_t *cu, in
             for (int32_t s = 0; s < nseq; ++s)
                 for (int64_t t = cu[s]; t < cu[s + 1]; ++t) {
                     if (t - k < cu[s] && !xc0) continue;
-                    acc += gv[t] * conv_input(x, xc0, cu, s, t - k, D, W, d);
+                    acc += term(gv[t] * conv_input(x, xc0, cu, s, t - k, D, W, d));
                 }
             dw[(int64_t)d * W + (W - 1 - k)] = acc;
         }
@@ -453,9 +469,9 @@ int oracle_conv_bwd_state(int64_t T, int32_t D, int32_t W, const int32_t *cu, in
             for (int64_t i = a - (W - 1); i < e; ++i) {
                 double acc = 0.0;
                 for (int32_t k = 0; k < W; ++k)
-                    if (i + k >= a && i + k < e) acc += w[(int64_t)d * W + (W - 1 - k)] * gv[i + k];
+                    if (i + k >= a && i + k < e) acc += term(w[(int64_t)d * W + (W - 1 - k)] * gv[i + k]);
                 const int64_t jt = i - (e - (W - 1));
-                if (dxcT && jt >= 0 && jt < W - 1) acc += dxcT[((int64_t)s * (W - 1) + jt) * D + d];
+                if (dxcT && jt >= 0 && jt < W - 1) acc += term(dxcT[((int64_t)s * (W - 1) + jt) * D + d]);
                 if (i >= a) {
                     dx[i * D + d] = acc;
                 } else if (dxc0) {
@@ -545,13 +561,13 @@ int oracle_scan_bwd_state(int64_t T, int32_t D, int32_t N, const int32_t *cu, in
                 const double uu = u[t * D + d];
                 double acc = 0.0;
                 for (int32_t n = 0; n < N; ++n) {
-                    const double hp = (t == cu[s]) ? (h0 ? h0[((int64_t)s * D + d) * N + n] : 0.0)
+                    const double hp = (t == cu[s]) ? (h0 ? term(h0[((int64_t)s * D + d) * N + n]) : 0.0)
                                                    : hs[(t - 1) * N + n];
-                    const double hn = exp(dt * A[(int64_t)d * N + n]) * hp + dt * B[t * N + n] * uu;
+                    const double hn = exp(dt * A[(int64_t)d * N + n]) * hp + term(dt * B[t * N + n] * uu);
                     hs[t * N + n] = hn;
-                    acc += C[t * N + n] * hn;
+                    acc += term(C[t * N + n] * hn);
                 }
-                if (Dp) acc += Dp[d] * uu;
+                if (Dp) acc += term(Dp[d] * uu);
                 ys[t] = acc;
             }
         }
@@ -561,8 +577,8 @@ int oracle_scan_bwd_state(int64_t T, int32_t D, int32_t N, const int32_t *cu, in
         for (int32_t n = 0; n < N; ++n) dA_d[n] = 0.0;
         for (int32_t s = nseq - 1; s >= 0; --s) {
             for (int32_t n = 0; n < N; ++n) {
-                c[n] = dhT ? dhT[((int64_t)s * D + d) * N + n] : 0.0;
-                hinit[n] = h0 ? h0[((int64_t)s * D + d) * N + n] : 0.0;
+                c[n] = dhT ? term(dhT[((int64_t)s * D + d) * N + n]) : 0.0;
+                hinit[n] = h0 ? term(h0[((int64_t)s * D + d) * N + n]) : 0.0;
             }
             for (int64_t t = (int64_t)cu[s + 1] - 1; t >= cu[s]; --t) {
                 const double dt = delta_eff(delta[t * D + d], dbias, d, sp);
@@ -572,30 +588,30 @@ int oracle_scan_bwd_state(int64_t T, int32_t D, int32_t N, const int32_t *cu, in
                 if (z) {
                     const double zz = z[t * D + d];
                     const double sg = sigmoid(zz);
-                    g = go * (zz * sg + gate_floor);
-                    if (dz) dz[t * D + d] = go * ys[t] * sg * (1.0 + zz * (1.0 - sg));
+                    g = term(go) * (term(zz * sg) + gate_floor);
+                    if (dz) dz[t * D + d] = term(go * ys[t] * sg * (1.0 + zz * (1.0 - sg)));
                 } else if (dz) {
                     dz[t * D + d] = 0.0;
                 }
-                double du_acc = Dp ? g * Dp[d] : 0.0;
+                double du_acc = Dp ? term(g * Dp[d]) : 0.0;
                 double ddt = 0.0;
-                dDp_acc += g * uu;
+                dDp_acc += term(g * uu);
                 for (int32_t n = 0; n < N; ++n) {
                     const double Bn = B[t * N + n], An = A[(int64_t)d * N + n];
-                    const double dh = g * C[t * N + n] + c[n];
+                    const double dh = term(g * C[t * N + n]) + c[n];
                     const double a = exp(dt * An);
                     const double hp = (t == cu[s]) ? hinit[n] : hs[(t - 1) * N + n];
-                    dC[t * N + n] += g * hs[t * N + n];
-                    dB[t * N + n] += dh * dt * uu;
-                    du_acc += dh * dt * Bn;
-                    ddt += dh * (Bn * uu + An * a * hp);
-                    dA_d[n] += dh * dt * a * hp;
+                    dC[t * N + n] += term(g * hs[t * N + n]);
+                    dB[t * N + n] += term(dh * dt * uu);
+                    du_acc += term(dh * dt * Bn);
+                    ddt += term(dh) * (term(Bn * uu) + term(An * a * hp));
+                    dA_d[n] += term(dh * dt * a * hp);
                     c[n] = a * dh;
                 }
                 du[t * D + d] = du_acc;
                 const double ddraw = ddt * delta_grad(delta[t * D + d], dbias, d, sp);
                 ddelta[t * D + d] = ddraw;
-                ddb_acc += ddraw;
+                ddb_acc += term(ddraw);
             }
             if (dh0)
                 for (int32_t n = 0; n < N; ++n) dh0[((int64_t)s * D + d) * N + n] = c[n];

@@ -63,6 +63,29 @@ def assert_close(got, ref, tol, name):
         f"at {np.unravel_index(int(np.nanargmax(np.where(np.isfinite(err), err, np.inf))), err.shape)}")
 
 
+def assert_sum_close(got, ref, scale, tol, name):
+    """A sum that may cancel, element by element: |got - ref| <= tol * scale,
+    where scale is the sum of the magnitudes of the terms of each element
+    (the oracle's error_scales mode), the scale of any evaluation's rounding
+    error. A bound relative to max |ref| would instead compare the rounding
+    of the terms whenever the sum cancels to near zero."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    scale = np.asarray(scale, dtype=np.float64)
+    assert got.shape == ref.shape == scale.shape, f"{name}: shapes {got.shape} {ref.shape} {scale.shape}"
+    if ref.size == 0:
+        return
+    assert np.all(scale >= np.abs(ref) * (1 - 1e-9)), f"{name}: scale below |ref| (not an error scale)"
+    err = np.abs(got - ref)
+    bound = tol * scale
+    ok = err <= bound
+    if not np.all(ok):
+        ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.inf)
+        at = np.unravel_index(int(np.nanargmax(ratio)), err.shape)
+        raise AssertionError(f"{name}: |err| {err[at]:.3e} > {tol:g} * scale {scale[at]:.3e} at {at} "
+                             f"(ref {ref[at]:.3e}, got {got[at]:.3e}); {int((~ok).sum())} elements out")
+
+
 class Dev:
     """Device copies of an Inputs batch plus cu_seqlens and pos."""
 

@@ -37,6 +37,43 @@ def pick_sequences(lengths, k=2):
     return sorted({int(order[0]), int(order[len(order) // 2])})[:k]
 
 
+def test_fullsize_every_element(orc):
+    """The benchmark workload (d_inner 4096, 8 x 4096 tokens, bf16) through
+    the benchmark's calls, every output and gradient compared with the
+    oracle's fp64 chain element by element (the oracle on every host core).
+    Per-token tensors are compared relative to their largest value; sums over
+    tokens or channels (dA, dB, dC, dDskip, dconv_w, dconv_b) against the
+    sum of the magnitudes of their terms (the oracle's error-scale mode)."""
+    import os
+    from tests.gpu_harness import assert_sum_close
+    assert torch.cuda.is_available()
+    threads = os.cpu_count() or 1
+    print(f"[fullsize] workload 4, every element, oracle on {threads} threads", flush=True)
+    inp = synth.make_inputs(4, with_dout=True)
+    d = Dev(inp)
+    F = d.forward()
+    G = d.backward(F)
+    torch.cuda.synchronize()
+    to, tg = TOL_OUT[inp.dtype], TOL_GRAD[inp.dtype]
+    f = synth.f64
+    args = (f(inp.x), f(inp.w), f(inp.b), f(inp.delta), f(inp.A), f(inp.B), f(inp.C), f(inp.Dp), f(inp.z),
+            inp.cu_seqlens)
+    Rf = orc.forward(*args, threads=threads)
+    assert np.array_equal(F["pos"].cpu().numpy(), Rf["pos"])
+    assert_close(npy(F["u"]), Rf["u"], to, "u")
+    assert_close(npy(F["out"]), Rf["out"], to, "out")
+    del Rf
+    dout = f(inp.dout)
+    Rb = orc.backward(*args, dout, threads=threads)
+    for k in ("dx", "du", "ddelta", "dz"):
+        assert_close(npy(G[k]), Rb[k], tg, k)
+    with orc.error_scales():
+        Sb = orc.backward(*args, dout, threads=threads)
+    for k in ("dA", "dB", "dC", "dD", "dw", "db"):
+        assert_sum_close(npy(G[k]), Rb[k], Sb[k], tg, k)
+    print(f"[fullsize] every element of {len(Rb)} outputs checked", flush=True)
+
+
 @pytest.mark.parametrize("workload", [4, 1, 3])
 def test_fullsize_sampled(orc, workload):
     assert torch.cuda.is_available()

@@ -42,15 +42,17 @@ MUTATIONS = [
      "const double a = exp(-dt * A[(int64_t)d * N + n]);\n                    h[n] = a * h[n] + bu;"),
     ("scan: no reset at heads", "const int head = pos[t] == 0;\n            const double dt = delta_eff(delta[t * D + d], dbias, d, sp);\n            const double uu = u[t * D + d];\n            double acc = 0.0;\n            for (int32_t n = 0; n < N; ++n) {\n                const double bu = dt * B[t * N + n] * uu;\n                if (head) {\n                    h[n] = bu;",
      "const int head = t == 0;\n            const double dt = delta_eff(delta[t * D + d], dbias, d, sp);\n            const double uu = u[t * D + d];\n            double acc = 0.0;\n            for (int32_t n = 0; n < N; ++n) {\n                const double bu = dt * B[t * N + n] * uu;\n                if (head) {\n                    h[n] = bu;"),
-    ("bwd: dA loses the delta factor", "dA_d[n] += dh * dt * a * hp;", "dA_d[n] += dh * a * hp;"),
-    ("bwd: carry crosses heads", "ddt += dh * (Bn * uu);\n                    c[n] = 0.0;", "ddt += dh * (Bn * uu);\n                    c[n] = dh;"),
+    ("bwd: dA loses the delta factor", "dA_d[n] += term(dh * dt * a * hp);", "dA_d[n] += term(dh * a * hp);"),
+    ("bwd: carry crosses heads", "ddt += term(dh * (Bn * uu));\n                    c[n] = 0.0;",
+     "ddt += term(dh * (Bn * uu));\n                    c[n] = dh;"),
     ("bwd: previous state index off by one", "const double hp = hs[(t - 1) * N + n];", "const double hp = hs[t * N + n];"),
     ("bwd: dz uses the wrong sigmoid derivative", "s * (1.0 + zz * (1.0 - s))", "s * (1.0 + zz * s)"),
-    ("bwd: dB misses u", "dB[t * N + n] += dh * dt * uu;", "dB[t * N + n] += dh * dt;"),
-    ("bwd: dC uses the previous state", "dC[t * N + n] += g * hs[t * N + n];", "dC[t * N + n] += g * (t > 0 ? hs[(t - 1) * N + n] : 0.0);"),
+    ("bwd: dB misses u", "dB[t * N + n] += term(dh * dt * uu);", "dB[t * N + n] += term(dh * dt);"),
+    ("bwd: dC uses the previous state", "dC[t * N + n] += term(g * hs[t * N + n]);",
+     "dC[t * N + n] += term(g * (t > 0 ? hs[(t - 1) * N + n] : 0.0));"),
     ("conv bwd: reverse rule off by one", "if (s + k < T && k <= pos[s + k])", "if (s + k < T && k < pos[s + k])"),
     ("conv bwd: dw tap index transposed", "dw[(int64_t)d * W + (W - 1 - k)] = acc;", "dw[(int64_t)d * W + k] = acc;"),
-    ("conv bwd: silu derivative drops a term", "gv[t] = g * s * (1.0 + v * (1.0 - s));", "gv[t] = g * s;"),
+    ("conv bwd: silu derivative drops a term", "gv[t] = term(g * s * (1.0 + v * (1.0 - s)));", "gv[t] = term(g * s);"),
     ("pack: heads off by one", "pos[t] = (int32_t)(t - cu[s]);", "pos[t] = (int32_t)(t - cu[s] + (s > 0));"),
     ("step map: softplus loses its log1p tail", "return (v > 0.0 ? v : 0.0) + log1p(exp(-fabs(v)));",
      "return (v > 0.0 ? v : 0.0);"),
@@ -60,19 +62,19 @@ MUTATIONS = [
      "return 1.0;"),
     ("gate floor: forward drops it", "acc * (z[t * D + d] * sigmoid(z[t * D + d]) + gate_floor)",
      "acc * (z[t * D + d] * sigmoid(z[t * D + d]))"),
-    ("gate floor: backward drops it", "g = go * (zz * s + gate_floor);", "g = go * (zz * s);"),
-    ("step map: bias gradient keeps only one token", "ddb_acc += ddraw;", "ddb_acc = ddraw;"),
+    ("gate floor: backward drops it", "g = term(go) * (term(zz * s) + gate_floor);", "g = term(go) * (term(zz * s));"),
+    ("step map: bias gradient keeps only one token", "ddb_acc += term(ddraw);", "ddb_acc = term(ddraw);"),
     ("state: initial state ignored", "for (int32_t n = 0; n < N; ++n) h[n] = h0 ? h0[((int64_t)s * D + d) * N + n] : 0.0;",
      "for (int32_t n = 0; n < N; ++n) h[n] = 0.0;"),
     ("state: final state transposed", "for (int32_t n = 0; n < N; ++n) hT[((int64_t)s * D + d) * N + n] = h[n];",
      "for (int32_t n = 0; n < N; ++n) hT[((int64_t)s * N + n) * D + d] = h[n];"),
-    ("state bwd: final-state gradient ignored", "c[n] = dhT ? dhT[((int64_t)s * D + d) * N + n] : 0.0;",
+    ("state bwd: final-state gradient ignored", "c[n] = dhT ? term(dhT[((int64_t)s * D + d) * N + n]) : 0.0;",
      "c[n] = 0.0;"),
     ("state bwd: previous state at the head taken as zero",
      "const double hp = (t == cu[s]) ? hinit[n] : hs[(t - 1) * N + n];",
      "const double hp = (t == cu[s]) ? 0.0 : hs[(t - 1) * N + n];"),
     ("state bwd: replay ignores the initial state",
-     "const double hp = (t == cu[s]) ? (h0 ? h0[((int64_t)s * D + d) * N + n] : 0.0)",
+     "const double hp = (t == cu[s]) ? (h0 ? term(h0[((int64_t)s * D + d) * N + n]) : 0.0)",
      "const double hp = (t == cu[s]) ? 0.0"),
     ("state bwd: initial-state gradient for the wrong sequence",
      "for (int32_t n = 0; n < N; ++n) dh0[((int64_t)s * D + d) * N + n] = c[n];",
@@ -85,8 +87,8 @@ MUTATIONS = [
     ("conv context bwd: gradient not passed through short sequences",
      "if (dxcT && jt >= 0 && jt < W - 1) acc +=", "if (dxcT && jt >= 0 && jt < W - 1 && i >= a) acc +="),
     ("conv context bwd: dw misses the context",
-     "if (t - k < cu[s] && !xc0) continue;\n                    acc += gv[t]",
-     "if (t - k < cu[s]) continue;\n                    acc += gv[t]"),
+     "if (t - k < cu[s] && !xc0) continue;\n                    acc += term(gv[t]",
+     "if (t - k < cu[s]) continue;\n                    acc += term(gv[t]"),
 ]
 
 
@@ -101,14 +103,14 @@ def mutant_dir():
 # planted in each: (name, text, planted, k) plants in the k-th of exactly two
 # occurrences (0: the reset-only function, 1: the state-carrying one).
 _SHARED = [
-    ("bwd: dA loses the delta factor", "dA_d[n] += dh * dt * a * hp;", "dA_d[n] += dh * a * hp;"),
-    ("bwd: dB misses u", "dB[t * N + n] += dh * dt * uu;", "dB[t * N + n] += dh * dt;"),
-    ("bwd: dC uses the wrong state", "dC[t * N + n] += g * hs[t * N + n];",
-     "dC[t * N + n] += g * hs[(t > 0 ? t - 1 : t) * N + n];"),
+    ("bwd: dA loses the delta factor", "dA_d[n] += term(dh * dt * a * hp);", "dA_d[n] += term(dh * a * hp);"),
+    ("bwd: dB misses u", "dB[t * N + n] += term(dh * dt * uu);", "dB[t * N + n] += term(dh * dt);"),
+    ("bwd: dC uses the wrong state", "dC[t * N + n] += term(g * hs[t * N + n]);",
+     "dC[t * N + n] += term(g * hs[(t > 0 ? t - 1 : t) * N + n]);"),
     ("conv bwd: dw tap index transposed", "dw[(int64_t)d * W + (W - 1 - k)] = acc;", "dw[(int64_t)d * W + k] = acc;"),
     ("gate floor: forward drops it", "acc * (z[t * D + d] * sigmoid(z[t * D + d]) + gate_floor)",
      "acc * (z[t * D + d] * sigmoid(z[t * D + d]))"),
-    ("step map: bias gradient keeps only one token", "ddb_acc += ddraw;", "ddb_acc = ddraw;"),
+    ("step map: bias gradient keeps only one token", "ddb_acc += term(ddraw);", "ddb_acc = term(ddraw);"),
 ]
 MUTATIONS = [m for m in MUTATIONS if m[1] not in {sh[1] for sh in _SHARED}]
 MUTATIONS = [m + (None,) for m in MUTATIONS] + [

@@ -318,6 +318,41 @@ def test_padded_layout_matches_packed():
         assert_close(npy(pg[k]), npy(g[k]), 1e-3, k)
 
 
+def test_per_sequence_loop_matches_packed():
+    """The gradient-accumulation layout (each sequence alone through the
+    block chain, parameter gradients summed over sequences), which the
+    benchmark times against the packed one, gives the packed results."""
+    import selective_state_space_varlen_amd as ss
+    inp = synth.make_inputs(2, n_packs=1, D=256, with_dout=True)
+    d = Dev(inp)
+    F = d.forward()
+    G = d.backward(F)
+    per_tok = {k: torch.empty_like(F[k]) for k in ("u", "out")}
+    per_tok.update({k: torch.empty_like(G[k]) for k in ("dx", "du", "ddelta", "dz", "dB", "dC")})
+    acc = {k: torch.zeros_like(G[k]) for k in ("dA", "dD", "dw", "db")}
+    for s in range(inp.nseq):
+        a, b = int(inp.cu_seqlens[s]), int(inp.cu_seqlens[s + 1])
+        if b == a:
+            continue
+        cu = torch.tensor([0, b - a], dtype=torch.int32, device="cuda")
+        sl = slice(a, b)
+        Fs = ss.forward(d.x[sl], d.w, d.b, d.delta[sl], d.A, d.B[sl], d.C[sl], d.Dp, d.z[sl], cu)
+        Gs = ss.backward(d.x[sl], d.w, d.b, d.delta[sl], d.A, d.B[sl], d.C[sl], d.Dp, d.z[sl], Fs, d.dout[sl])
+        for k in ("u", "out"):
+            per_tok[k][sl] = Fs[k]
+        for k in ("dx", "du", "ddelta", "dz", "dB", "dC"):
+            per_tok[k][sl] = Gs[k]
+        for k in acc:
+            acc[k] += Gs[k]
+    torch.cuda.synchronize()
+    for k in ("u", "out"):
+        assert_close(npy(per_tok[k]), npy(F[k]), TOL_OUT[inp.dtype], k)
+    for k in ("dx", "du", "ddelta", "dz", "dB", "dC"):
+        assert_close(npy(per_tok[k]), npy(G[k]), TOL_GRAD[inp.dtype], k)
+    for k in acc:
+        assert_close(npy(acc[k]), npy(G[k]), 1e-3, k)
+
+
 def test_planned_layout_parity(orc):
     """Whole documents grouped by the host packer (first-fit decreasing) into
     packs of 1024 tokens, each pack's unused tail run as one extra segment:

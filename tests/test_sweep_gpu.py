@@ -6,8 +6,8 @@ gate, skip, conv bias, the step map softplus(delta + bias) with a gate floor,
 and carried SSM states and conv contexts in both directions. The chain runs
 through pipeline.forward / backward (every library entry point but the
 packer) and every output and gradient is compared with the oracle's
-state-carrying functions, which with absent states are the reset-only ones,
-each operator on the stored inputs it consumed.
+state-carrying functions (with absent states the reset-only ones) run as one
+fp64 chain from the same inputs.
 """
 from __future__ import annotations
 
@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import synth
-from tests.gpu_harness import TOL_GRAD, TOL_OUT, Dev, assert_close, npy, to_dev
+from tests.gpu_harness import TOL_GRAD, TOL_OUT, Dev, assert_close, assert_sum_close, npy, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -99,35 +99,38 @@ def test_block_chain_sweep(orc, i):
     dhTo = dhT.astype(np.float64) if dhT is not None else None
     cio = f64(ci) if ci is not None else None
     dcfo = f64(dcf) if dcf is not None else None
-    # each operator is checked on the inputs it consumed: the scan on the
-    # stored u the conv wrote, the conv backward on the stored du (both are
-    # checked against the oracle first). Sums over many tokens that cancel
-    # (d bias at small d_inner) would otherwise compare the rounding of u
-    # and du, not the kernels.
-    _, u, cf = orc.conv_fwd_state(x, w, bo, cu, cio, threads=8)
+    # The end-to-end chain: the oracle runs its own conv, scan and conv
+    # backward in fp64. Per-token outputs are compared relative to their
+    # tensor's largest value; sums over tokens or channels, which may cancel,
+    # against the sum of the magnitudes of their terms, which the oracle's
+    # error-scale mode gives along the same chain.
     to, tg = TOL_OUT[inp.dtype], TOL_GRAD[inp.dtype]
-    assert_close(npy(F["u"]), u, to, "u")
-    u = npy(F["u"]).astype(np.float64)
+    _, u, cf = orc.conv_fwd_state(x, w, bo, cu, cio, threads=8)
     _, out, hT = orc.scan_fwd_state(u, delta, A, B, C, Dpo, zo, cu, h0=h0o, threads=8, **oext)
     R = orc.scan_bwd_state(u, delta, A, B, C, Dpo, zo, cu, dout, h0=h0o, dhT=dhTo, threads=8, **oext)
-    assert_close(npy(G["du"]), R["du"], tg, "du")
-    dx, dw, db, dci = orc.conv_bwd_state(x, w, bo, cu, npy(G["du"]).astype(np.float64), cio, dcfo, threads=8)
+    dx, dw, db, dci = orc.conv_bwd_state(x, w, bo, cu, R["du"], cio, dcfo, threads=8)
+    with orc.error_scales():
+        S = orc.scan_bwd_state(u, delta, A, B, C, Dpo, zo, cu, dout, h0=h0o, dhT=dhTo, threads=8, **oext)
+        sdx, sdw, sdb, sdci = orc.conv_bwd_state(x, w, bo, cu, S["du"], cio, dcfo, threads=8)
 
+    assert_close(npy(F["u"]), u, to, "u")
     assert_close(npy(F["out"]), out, to, "out")
-    for k in ("ddelta", "dA", "dB", "dC"):
+    for k in ("du", "ddelta"):
         assert_close(npy(G[k]), R[k], tg, k)
+    for k in ("dA", "dB", "dC"):
+        assert_sum_close(npy(G[k]), R[k], S[k], tg, k)
     if c["skip"]:
-        assert_close(npy(G["dD"]), R["dD"], tg, "dD")
+        assert_sum_close(npy(G["dD"]), R["dD"], S["dD"], tg, "dD")
     if c["gate"]:
         assert_close(npy(G["dz"]), R["dz"], tg, "dz")
     if bias is not None:
-        assert_close(npy(G["ddelta_bias"]), R["ddelta_bias"], tg, "ddelta_bias")
+        assert_sum_close(npy(G["ddelta_bias"]), R["ddelta_bias"], S["ddelta_bias"], tg, "ddelta_bias")
     assert_close(npy(G["dx"]), dx, tg, "dx")
-    assert_close(npy(G["dw"]), dw, tg, "dw")
+    assert_sum_close(npy(G["dw"]), dw, sdw, tg, "dw")
     if c["conv_bias"]:
-        assert_close(npy(G["db"]), db, tg, "db")
+        assert_sum_close(npy(G["db"]), db, sdb, tg, "db")
     if c["states"]:
         assert_close(npy(F["final_states"]["ssm"]), hT, to, "final ssm state")
         assert np.array_equal(npy(F["final_states"]["conv"]), cf), "final conv context"
-        assert_close(npy(G["dinitial_states"]["ssm"]), R["dh0"], tg, "dinitial ssm state")
-        assert_close(npy(G["dinitial_states"]["conv"]), dci, tg, "dinitial conv context")
+        assert_sum_close(npy(G["dinitial_states"]["ssm"]), R["dh0"], S["dh0"], tg, "dinitial ssm state")
+        assert_sum_close(npy(G["dinitial_states"]["conv"]), dci, sdci, tg, "dinitial conv context")
