@@ -376,6 +376,73 @@ def workload_figures(wl_id: int, steps: int, warmup: int) -> dict:
     return out
 
 
+# checkpoint intervals of the scan (0: the forward keeps nothing)
+CK_INTERVALS = (4, 16, 64, 256, 2048, 0)
+
+
+def _timed(fn, steps: int, warmup: int) -> float:
+    """Median ms of fn() over `steps` calls, each bracketed by events on the
+    current stream (where the library launches)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+
+def checkpoint_modes(wl: "Workload", steps: int, warmup: int = 2) -> dict:
+    """Per checkpoint interval: the bytes one layer keeps from its scan
+    forward to its backward, the backward's scratch, and the scan forward
+    and backward times (selective_scan_pack_fwd_ck / _bwd_ck)."""
+    ssp = wl.ssp
+    T, D, N = wl.T, wl.D, wl.N
+    args = (wl.u, wl.delta, wl.A, wl.B, wl.C, wl.Dp, wl.z, wl.pos)
+    fscr = torch.empty(max(ssp.selective_scan_pack_fwd_scratch_bytes(T, D, N), 1), dtype=torch.uint8,
+                       device=wl.x.device)
+    out = {}
+    for ci in CK_INTERVALS:
+        sb = ssp.selective_scan_pack_saved_bytes(T, D, N, ci)
+        bb = ssp.selective_scan_pack_bwd_scratch_bytes(T, D, N, ci)
+        saved = torch.empty(max(sb, 1), dtype=torch.uint8, device=wl.x.device) if ci else None
+        bscr = torch.empty(max(bb, 1), dtype=torch.uint8, device=wl.x.device)
+        fwd = lambda: ssp.selective_scan_pack_fwd_ck(*args, ci, saved=saved, scratch=fscr, out=wl.out)
+        bwd = lambda: ssp.selective_scan_pack_bwd_ck(*args, wl.dout, ci, saved, scratch=bscr, out=wl.g)
+        fwd()
+        fms = _timed(fwd, steps, warmup)
+        bms = _timed(bwd, steps, warmup)
+        out[str(ci)] = {"saved_bytes_per_layer": sb, "fwd_scratch_bytes": fscr.numel(), "bwd_scratch_bytes": bb,
+                        "scan_fwd_ms": round(fms, 4), "scan_bwd_ms": round(bms, 4)}
+        del saved, bscr
+        torch.cuda.empty_cache()
+    return out
+
+
+def forward_only(wl: "Workload", steps: int, warmup: int = 2) -> dict:
+    """The inference forward: indices, conv, and the scan keeping no states."""
+    ssp = wl.ssp
+    T, D, N = wl.T, wl.D, wl.N
+    fscr = torch.empty(max(ssp.selective_scan_pack_fwd_scratch_bytes(T, D, N), 1), dtype=torch.uint8,
+                       device=wl.x.device)
+
+    def fwd():
+        ssp.varlen_pack_indices(wl.cu, T, heads=False, dev_err=False, out=wl.pos)
+        ssp.conv1d_pack_fwd(wl.x, wl.w, wl.b, wl.pos, silu=True, out=wl.u)
+        ssp.selective_scan_pack_fwd_ck(wl.u, wl.delta, wl.A, wl.B, wl.C, wl.Dp, wl.z, wl.pos, 0, scratch=fscr,
+                                       out=wl.out)
+
+    ms = _timed(fwd, steps, warmup)
+    ab = algo_bytes(T, D, N)
+    b = ab["pack_indices"] + ab["conv_fwd"] + ab["scan_fwd"]
+    return {"ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "algo_gbs": round(b / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "scratch_bytes": fscr.numel(), "kept_bytes": 0}
+
+
 def copy_ceiling(nbytes: int = 1 << 30, reps: int = 10) -> float:
     """GB/s (read + write) of a plain device-to-device copy of nbytes, the
     practical HBM ceiling beside the 8 TB/s vendor peak."""
@@ -404,6 +471,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the figures of the d_inner 1536 and long-pack workloads")
+    ap.add_argument("--no-modes", action="store_true",
+                    help="skip the forward-only pass and the scan's checkpoint-interval modes")
     ap.add_argument("--cpu-channels", type=int, default=4096,
                     help="channels of the workload the oracle baseline runs (all of them by default)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -452,6 +521,13 @@ def main():
                                               "no forward recompute; peak without packed FP32"}
     log("[bench] per-op ms: " + ", ".join(f"{k} {ops[k]:.3f}" for k in OPS))
     log("[bench] per-op algorithmic GB/s: " + ", ".join(f"{k} {ops_gbs[k]:.0f}" for k in OPS))
+
+    fo = cm = None
+    if not args.no_modes:
+        fo = forward_only(wl, args.steps)
+        log(f"[bench] forward only (scan keeps no states): {fo}")
+        cm = checkpoint_modes(wl, max(3, args.steps // 2))
+        log(f"[bench] scan checkpoint modes: {cm}")
 
     # (counter runs take the copy calibration below instead: it must be the
     # run's only device copy)
@@ -564,6 +640,8 @@ def main():
                               / 1e9 / PEAK_HBM_GBS, 4),
         "bwd_hbm_frac": round((ab["scan_bwd"] + ab["conv_bwd"]) / (passes["bwd"]["median"] * 1e-3) / 1e9
                               / PEAK_HBM_GBS, 4),
+        "forward_only": fo,
+        "scan_checkpoint_modes": cm,
         "other_workloads": workloads,
         "hbm_gbs": round(hbm_gbs, 1),
         "hbm_copy_ceiling_gbs": None if copy_gbs is None else round(copy_gbs, 1),
