@@ -377,7 +377,7 @@ def workload_figures(wl_id: int, steps: int, warmup: int) -> dict:
 
 
 # checkpoint intervals of the scan (0: the forward keeps nothing)
-CK_INTERVALS = (4, 16, 64, 256, 2048, 0)
+CK_INTERVALS = (4, 8, 16, 64, 256, 2048, 0)
 
 
 def _timed(fn, steps: int, warmup: int) -> float:

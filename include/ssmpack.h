@@ -291,17 +291,17 @@ int selective_scan_pack_bwd_states(const void *u, const void *delta, const float
  *            D, N) for the forward, selective_scan_pack_bwd_scratch_bytes(T,
  *            D, N, ckpt_interval) for the backward.
  * ckpt_interval is 0 or a power of two from 4 to 2048:
- *   4        the backward reads the kept states directly (fastest backward;
- *            the _states entry points use this, their workspace being saved
+ *   4, 8     the backward reads the kept states directly (fastest backward;
+ *            the _states entry points use 8, their workspace being saved
  *            followed by scratch);
- *   8..2048  fewer kept states; the backward first replays the forward's
- *            recurrence from them into dense states in its scratch;
+ *   16..2048 fewer kept states; the backward first replays the forward's
+ *            recurrence from them into states 8 tokens apart in its scratch;
  *   0        nothing kept (saved may be NULL; a forward-only call, e.g. for
  *            inference); a backward then recomputes every state from the
  *            inputs.
  * The forward's outputs do not depend on ckpt_interval. The backward's
  * replay repeats the forward's arithmetic within each forward chunk (64 or
- * more tokens), so intervals 0 to 64 give the interval-4 gradients bit for
+ * more tokens), so intervals 0 to 64 give the interval-8 gradients bit for
  * bit; a longer interval replays across chunk boundaries where the forward
  * restarted from its chunk carry, which changes gradients by rounding only.
  * Other arguments, outputs and

@@ -24,13 +24,13 @@
 // entering each chunk. The main kernel then walks each chunk backwards in
 // kSub-token blocks: each block restarts from the forward's checkpoint at its
 // first token and replays its tokens with their states and decays held in
-// VGPRs before running the reverse step over them. A workgroup holds 128
-// channels (two per lane) and splits the states between its waves (layout
+// VGPRs before running the reverse step over them. A workgroup holds kCl * 64
+// channels (kCl per lane) and splits the states between its waves (layout
 // below); the sums over states are added across waves through LDS, and dB and
-// dC (sums over channels) are added over the lane's two channels in registers
-// and over the wave's lanes through LDS, then written per 128-channel group;
-// dA and dDskip are written per chunk; small kernels finish all sums in a
-// fixed order, so results are deterministic.
+// dC (sums over channels) are added over the lane's channels in registers and
+// over the wave's lanes through LDS, then written per channel group; dA and
+// dDskip are written per chunk; small kernels finish all sums in a fixed
+// order, so results are deterministic.
 #include "scan_common.h"
 
 #include <type_traits>
@@ -255,7 +255,8 @@ struct BwdArgs {
     const T* z;
     const T* dout;
     const int32_t* pos;
-    const float* ckpt;  // the state entering every kCK-th token
+    const float* ckpt;  // the state entering every 2^ckshift-th token (a multiple of kCK)
+    int ckshift;
     const float* cin;
     T* du;
     T* ddelta;
@@ -271,24 +272,27 @@ struct BwdArgs {
     ScanOpts opt;
 };
 
-// Layout of the reverse pass. A workgroup covers 128 adjacent channels, two
-// per lane (channels 2l and 2l+1 of its group), and splits the states between
-// its waves: wave q holds states q*NH .. q*NH+NH-1 of every channel, NH =
-// min(N, 4), so SW = N / NH waves cover them all. A wave's registers then hold
-// the states and decays of a whole block's replay, B_t[n] and C_t[n] are the
-// same across the wave, and the lane's two channels add their dB and dC terms
-// in registers before the sums over channels go through LDS.
+// Layout of the reverse pass. A workgroup covers kCl * 64 adjacent channels,
+// kCl per lane (channels kCl*l .. kCl*l+kCl-1 of its group), and splits the
+// states between its waves: wave q holds states q*NH .. q*NH+NH-1 of every
+// channel, NH = min(N, 4), so SW = N / NH waves cover them all. A wave's
+// registers then hold the states and decays of a whole block's replay,
+// B_t[n] and C_t[n] are the same across the wave, and a lane's channels add
+// their dB and dC terms in registers before the sums over channels go
+// through LDS. One channel per lane over 8-token blocks measured faster (with
+// the forward's checkpoint traffic halved) than two over 4-token blocks, at
+// the same registers: the block's states and decays take K * kCl * NH each.
 template <int NS>
 struct Split {
     static constexpr int NH = NS < 4 ? NS : 4;
     static constexpr int SW = NS / NH;
 };
-constexpr int kCl = 2;                     // channels per lane
+constexpr int kCl = kBwdCl;                // channels per lane
 constexpr int kGroupCh = kCl * kWave;      // channels per workgroup
 
 // Tokens per block: the backward restarts from a state checkpoint at every
 // block and replays it with its states in registers.
-constexpr int kSub = 4;
+constexpr int kSub = kCK;
 
 // Sum of v over groups of G consecutive lanes (G a power of two <= 16); every
 // lane of a group receives the total.
@@ -369,15 +373,28 @@ struct BcIdx {
 // rows by eight lanes fall on different banks.
 constexpr int kXRow = kWave + 16;
 
+// M floats that LDS moves in one access
+template <int M>
+struct alignas(4 * M) LdsVec {
+    float v[M];
+};
 // What one block shares between the waves; blocks alternate between two of
 // them, so that one barrier a block orders every access (see the block loop).
 template <int NS>
 struct BwdBuf {
     static constexpr int SW = Split<NS>::SW, K = kSub;
-    float4 stp[K][kWave];             // per token, per lane: step and step*u of its two channels
-    float2 gg[K][kWave];              // per token, per lane: g of its two channels
-    float2 part[3][K][SW][kWave];     // per wave: y, sum_n dh B, sum_n A r of the lane's channels
+    LdsVec<2 * kCl> stp[K][kWave];    // per token, per lane: step and step*u of each of its channels
+    LdsVec<kCl> gg[K][kWave];         // per token, per lane: g of each of its channels
+    LdsVec<kCl> part[3][K][SW][kWave];  // per wave: y, sum_n dh B, sum_n A r of the lane's channels
 };
+template <int M>
+__device__ __forceinline__ LdsVec<M> lds_vec(const float (&v)[M]) {
+    LdsVec<M> r;
+#pragma unroll
+    for (int i = 0; i < M; ++i) r.v[i] = v[i];
+    return r;
+}
+
 // LDS of a backward workgroup
 template <int NS>
 struct BwdShared {
@@ -390,14 +407,15 @@ struct BwdShared {
 // token's states hh[kk] and decays ak[kk] (per channel of the lane), and this
 // wave's share of y. SAFE blocks may be short (nb < K) or hold heads; fast
 // blocks are neither.
-// The block's per-token values of the lane's two channels (step, step*u, g),
+// The block's per-token values of the lane's channels (step, step*u, g),
 // read from LDS in one batch so that no token waits on its own read.
 struct TokVals {
     float dt[kSub][kCl], dtu[kSub][kCl], gg[kSub][kCl];
 };
 
 template <bool SAFE, bool ST, int NS>
-__device__ __forceinline__ void bwd_replay(BwdBuf<NS>& bf, const TokVals& tv, const BcRegs<NS>& bc, int nb, uint32_t heads, int lane, int q,
+__device__ __forceinline__ void bwd_replay(BwdBuf<NS>& bf, const TokVals& tv, const BcRegs<NS>& bc, int nb,
+                                           uint32_t heads, int lane, int q,
                                            const bool (&act)[kCl], const float (&A2)[kCl][Split<NS>::NH],
                                            const float (&hin)[kCl][Split<NS>::NH],
                                            float (&hh)[kSub][kCl][Split<NS>::NH],
@@ -450,18 +468,19 @@ __device__ __forceinline__ void bwd_replay(BwdBuf<NS>& bf, const TokVals& tv, co
             }
         };
         static_for<NH>(state);
-        bf.part[0][kk][q][lane] = make_float2(y[0], y[1]);
+        bf.part[0][kk][q][lane] = lds_vec(y);
     };
     static_for_until<K>(step, SAFE ? nb : K);
 }
 
 // Reverse step over the block, a token pair at a time; after each pair, dB
 // (kind 0: sum over channels of dh * step*u) and dC (kind 1: of g * h) of its
-// two tokens. The lane's two channels are added in registers; each value is
-// then added up over the wave's lanes by LPO lanes reading the terms the wave
-// left in LDS.
+// two tokens. A lane's channels are added in registers; each value is then
+// added up over the wave's lanes by LPO lanes reading the terms the wave left
+// in LDS.
 template <bool SAFE, bool ST, int NS>
-__device__ __forceinline__ void bwd_reverse(BwdBuf<NS>& bf, float* __restrict__ myx, const TokVals& tv, const BcRegs<NS>& bc, int nb, uint32_t heads, int lane, int q,
+__device__ __forceinline__ void bwd_reverse(BwdBuf<NS>& bf, float* __restrict__ myx, const TokVals& tv,
+                                            const BcRegs<NS>& bc, int nb, uint32_t heads, int lane, int q,
                                             const bool (&act)[kCl], const float (&A2)[kCl][Split<NS>::NH],
                                             const float (&hin)[kCl][Split<NS>::NH],
                                             const float (&hh)[kSub][kCl][Split<NS>::NH],
@@ -483,7 +502,9 @@ __device__ __forceinline__ void bwd_reverse(BwdBuf<NS>& bf, float* __restrict__ 
         const float(&dt)[kCl] = tv.dt[kk];
         const float(&dtu)[kCl] = tv.dtu[kk];
         const float(&gg)[kCl] = tv.gg[kk];
-        float sumB[kCl], sumAr[kCl] = {0.0f, 0.0f};
+        float sumB[kCl], sumAr[kCl];
+#pragma unroll
+        for (int c = 0; c < kCl; ++c) sumAr[c] = 0.0f;
         if (SAFE && ((heads >> kk) & 1u)) {
             asm volatile("");
             // With states, what the decay passes back out of the head is the
@@ -553,8 +574,8 @@ __device__ __forceinline__ void bwd_reverse(BwdBuf<NS>& bf, float* __restrict__ 
             };
             static_for<NH>(state);
         }
-        bf.part[1][kk][q][lane] = make_float2(sumB[0], sumB[1]);
-        bf.part[2][kk][q][lane] = make_float2(sumAr[0], sumAr[1]);
+        bf.part[1][kk][q][lane] = lds_vec(sumB);
+        bf.part[2][kk][q][lane] = lds_vec(sumAr);
     };
     auto pair = [&](auto KPc) {
         constexpr int kp = K / 2 - 1 - decltype(KPc)::value;  // pairs right to left
@@ -650,7 +671,9 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
                 for (int i = 0; i < NH; ++i) carry[c][i] = p.opt.dhT[((size_t)s * D + dd[c]) * NS + n0 + i];
             }
     }
-    float Dv[kCl], dDacc[kCl] = {0.0f, 0.0f}, dbacc[kCl] = {0.0f, 0.0f};
+    float Dv[kCl], dDacc[kCl], dbacc[kCl];
+#pragma unroll
+    for (int c = 0; c < kCl; ++c) dDacc[c] = dbacc[c] = 0.0f;
     StepMap sm[kCl];
 #pragma unroll
     for (int c = 0; c < kCl; ++c) {
@@ -690,7 +713,7 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
                 b.rg[j][c] = Elt<T>::raw(at_bytes(g_r, bo[c]), 0);
             }
         }
-        const float* __restrict__ slot = p.ckpt + ((uint64_t)tb / kCK) * ND;  // tb >= 0
+        const float* __restrict__ slot = p.ckpt + ((uint64_t)tb >> p.ckshift) * ND;  // tb >= 0
 #pragma unroll
         for (int c = 0; c < kCl; ++c) ck_load<NS, NH>(slot, dd[c], D, n0, true, b.hn[c]);
         b.bc.load(bcp, tb, T_, q, lane);
@@ -741,8 +764,14 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
                 dtv[c] = dt; dtu[c] = dt * uu; ggv[c] = gg;
                 ev.u[j][c] = uu; ev.dt[j][c] = dt; ev.gg[j][c] = gg; ev.fz[j][c] = fz; ev.sl[j][c] = sl;
             }
-            bf.stp[kk][lane] = make_float4(dtv[0], dtu[0], dtv[1], dtu[1]);
-            bf.gg[kk][lane] = make_float2(ggv[0], ggv[1]);
+            float sv[2 * kCl];
+#pragma unroll
+            for (int c = 0; c < kCl; ++c) {
+                sv[2 * c] = dtv[c];
+                sv[2 * c + 1] = dtu[c];
+            }
+            bf.stp[kk][lane] = lds_vec(sv);
+            bf.gg[kk][lane] = lds_vec(ggv);
         }
     };
     auto main_part = [&](Pre& b, int64_t jb, BwdBuf<NS>& bf) {
@@ -754,10 +783,14 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
         TokVals tv;
 #pragma unroll
         for (int kk = 0; kk < K; ++kk) {
-            const float4 st = bf.stp[kk][lane];
-            const float2 g2 = bf.gg[kk][lane];
-            tv.dt[kk][0] = st.x; tv.dtu[kk][0] = st.y; tv.dt[kk][1] = st.z; tv.dtu[kk][1] = st.w;
-            tv.gg[kk][0] = g2.x; tv.gg[kk][1] = g2.y;
+            const LdsVec<2 * kCl> st = bf.stp[kk][lane];
+            const LdsVec<kCl> g2 = bf.gg[kk][lane];
+#pragma unroll
+            for (int c = 0; c < kCl; ++c) {
+                tv.dt[kk][c] = st.v[2 * c];
+                tv.dtu[kk][c] = st.v[2 * c + 1];
+                tv.gg[kk][c] = g2.v[c];
+            }
         }
         float* __restrict__ dbc_row = p.dBC + ((size_t)g * T_ + tb) * 2 * NS;
         float* __restrict__ myx = &sh.xb[q][0][0];
@@ -779,15 +812,21 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
         for (int j = 0; j < KQ; ++j) {
             const int kk = q + j * SW;
             const bool tok = kk < nb;  // tokens past the block store to the sink
-            float2 y = bf.part[0][kk][0][lane], sB = bf.part[1][kk][0][lane], sA = bf.part[2][kk][0][lane];
+            LdsVec<kCl> y = bf.part[0][kk][0][lane], sB = bf.part[1][kk][0][lane], sA = bf.part[2][kk][0][lane];
 #pragma unroll
             for (int w = 1; w < SW; ++w) {
-                const float2 a = bf.part[0][kk][w][lane], bb = bf.part[1][kk][w][lane], cc = bf.part[2][kk][w][lane];
-                y.x += a.x; y.y += a.y;
-                sB.x += bb.x; sB.y += bb.y;
-                sA.x += cc.x; sA.y += cc.y;
+                const LdsVec<kCl> a = bf.part[0][kk][w][lane], bb = bf.part[1][kk][w][lane],
+                                  cc = bf.part[2][kk][w][lane];
+#pragma unroll
+                for (int c = 0; c < kCl; ++c) {
+                    y.v[c] += a.v[c];
+                    sB.v[c] += bb.v[c];
+                    sA.v[c] += cc.v[c];
+                }
             }
-            const float yv[kCl] = {y.x, y.y}, sBv[kCl] = {sB.x, sB.y}, sAv[kCl] = {sA.x, sA.y};
+            const float(&yv)[kCl] = y.v;
+            const float(&sBv)[kCl] = sB.v;
+            const float(&sAv)[kCl] = sA.v;
             const size_t rb = (size_t)(tok ? tb + kk : 0) * D;
             T* __restrict__ sinkT = reinterpret_cast<T*>(p.sink);
 #pragma unroll
@@ -866,18 +905,22 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
             for (int i = 0; i < NH; ++i) p.dApart[(size_t)c_ * ND + (size_t)(n0 + i) * D + d[c]] = dA[c][i];
         }
     __syncthreads();
-    sh.buf[0].part[0][0][q][lane] = make_float2(dDacc[0], dDacc[1]);
-    sh.buf[0].part[1][0][q][lane] = make_float2(dbacc[0], dbacc[1]);
+    sh.buf[0].part[0][0][q][lane] = lds_vec(dDacc);
+    sh.buf[0].part[1][0][q][lane] = lds_vec(dbacc);
     __syncthreads();
     if (q == 0) {
-        float2 sD = make_float2(0.0f, 0.0f), sb = sD;
+        float sDv[kCl], sbv[kCl];
+#pragma unroll
+        for (int c = 0; c < kCl; ++c) sDv[c] = sbv[c] = 0.0f;
 #pragma unroll
         for (int w = 0; w < SW; ++w) {
-            const float2 a = sh.buf[0].part[0][0][w][lane], b = sh.buf[0].part[1][0][w][lane];
-            sD.x += a.x; sD.y += a.y;
-            sb.x += b.x; sb.y += b.y;
+            const LdsVec<kCl> a = sh.buf[0].part[0][0][w][lane], b = sh.buf[0].part[1][0][w][lane];
+#pragma unroll
+            for (int c = 0; c < kCl; ++c) {
+                sDv[c] += a.v[c];
+                sbv[c] += b.v[c];
+            }
         }
-        const float sDv[kCl] = {sD.x, sD.y}, sbv[kCl] = {sb.x, sb.y};
 #pragma unroll
         for (int c = 0; c < kCl; ++c)
             if (act[c]) {
@@ -938,7 +981,9 @@ static int scan_bwd_launch(const void* u, const void* delta, const float* A, con
     SSMP_LAUNCH_CHECK();
     // the state entering every kCK-th token: kept by the forward, or replayed
     const float* ckpt = saved;
-    if (ci != kCK) {
+    int ckshift = ci ? __builtin_ctz((unsigned)ci) : 0;
+    if (!ck_direct(ci)) {
+        ckshift = __builtin_ctz((unsigned)kCK);
         const int st = scan_dense_ckpt(NS, std::is_same<T, uint16_t>::value, u, delta, A, pos, saved, ci, ws, T_, D,
                                        opt, s);
         if (st) return st;
@@ -960,7 +1005,7 @@ static int scan_bwd_launch(const void* u, const void* delta, const float* A, con
     SSMP_LAUNCH_CHECK();
     BwdArgs<T> a;
     a.u = (const T*)u; a.delta = (const T*)delta; a.A = A; a.bc = ws + L.bc; a.Dskip = Dskip;
-    a.z = (const T*)z; a.dout = (const T*)dout; a.pos = pos; a.ckpt = ckpt; a.cin = ws + L.cin;
+    a.z = (const T*)z; a.dout = (const T*)dout; a.pos = pos; a.ckpt = ckpt; a.ckshift = ckshift; a.cin = ws + L.cin;
     a.du = (T*)du; a.ddelta = (T*)ddelta; a.dz = (T*)dz; a.dApart = ws + L.dApart; a.dDpart = ws + L.dDpart;
     a.dbpart = ws + L.dbpart; a.dBC = ws + L.dBC; a.sink = ws + L.sink; a.T_ = T_; a.D = D; a.lc = lc; a.opt = opt;
     constexpr int SW = Split<NS>::SW;

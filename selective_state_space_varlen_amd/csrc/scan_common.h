@@ -11,21 +11,24 @@ namespace ssmp {
 // affine carry h_out = P h_in + S (P = 0 once the chunk holds a head). Every
 // chunk whose successor continues a sequence costs a summary pass, so chunks
 // are as long as the grid allows: the longest power of two (64 .. 2048 tokens)
-// that still gives kMinWaves waves. The forward stores the state entering
-// every kCK-th token; the backward stages its inputs in kBB-token blocks and
-// restarts each kK-token sub-chunk from its checkpoint, replaying it with the
-// states in registers. Checkpoints cost 16 B of HBM per (t, d) each way, which
-// the ALU-bound scans absorb, and spare the backward a second replay pass.
-constexpr int kCK = 4;
-constexpr int kK = 4;
+// that still gives kMinWaves waves. The backward restarts every kCK-token
+// block from the state entering it, which the forward keeps (every kCK-th
+// token, or every kMinCK-th) or the backward replays, and replays the block
+// with its states in registers. Kept every kCK tokens, checkpoints cost 8 B
+// of HBM per (t, d) each way and spare the backward a second replay pass.
+constexpr int kCK = 8;
+constexpr int kMinCK = 4;  // the shortest interval the forward keeps
 constexpr int kBB = 16;
 constexpr int kLCMin = 64, kLCMax = 2048;
 constexpr int64_t kMinWaves = 8192;  // eight per SIMD on 256 CUs: enough to hide load latency
-static_assert(kK == kCK && kBB % kK == 0 && kLCMin % kBB == 0, "tiling");
+static_assert(kCK % kMinCK == 0 && kLCMin % kBB == 0 && kLCMin % kCK == 0, "tiling");
 
 // waves per backward workgroup: each holds min(N, 4) of the states of the
-// workgroup's 128 channels
+// workgroup's channels
 inline int bwd_waves(int N) { return N / (N < 4 ? N : 4); }
+// channels per lane of the backward's main pass (a workgroup covers kBwdCl * 64
+// channels)
+constexpr int kBwdCl = 1;
 
 inline int scan_chunk_len(int64_t T, int D, int chw) {
     const int64_t ng = (D + chw - 1) / chw;
@@ -34,7 +37,7 @@ inline int scan_chunk_len(int64_t T, int D, int chw) {
     return lc;
 }
 inline int fwd_chunk_len(int64_t T, int D) { return scan_chunk_len(T, D, kWave); }
-inline int bwd_chunk_len(int64_t T, int D, int N) { return scan_chunk_len(T, D, 2 * kWave / bwd_waves(N)); }
+inline int bwd_chunk_len(int64_t T, int D, int N) { return scan_chunk_len(T, D, kBwdCl * kWave / bwd_waves(N)); }
 // The backward's reverse-carry summaries run over sub-chunks of the main
 // kernel's chunks (down to kLCMin tokens): a summary wave's work depends on
 // where the heads fall, and more, shorter waves even it out across the SIMDs.
@@ -189,14 +192,15 @@ __device__ __forceinline__ StepMap step_map(const ScanOpts& o, int d) {
 }
 
 // Checkpoint intervals. The forward may keep the state entering every ci-th
-// token for the backward (ci a power of two in [kCK, kLCMax]), or none (ci =
-// 0). The backward restarts every kCK-token block from such a state: with ci
-// = kCK it reads the kept ones, otherwise it first replays the forward's
-// recurrence from them (from the chunk states of a fresh summary pass for ci
-// = 0) into dense checkpoints of its own.
+// token for the backward (ci a power of two in [kMinCK, kLCMax]), or none (ci
+// = 0). The backward restarts every kCK-token block from such a state: with
+// ci dividing kCK it reads the kept ones, otherwise it first replays the
+// forward's recurrence from them (from the chunk states of a fresh summary
+// pass for ci = 0) into dense checkpoints of its own, kCK tokens apart.
 inline bool ck_interval_ok(int ci) {
-    return ci == 0 || (ci >= kCK && ci <= kLCMax && (ci & (ci - 1)) == 0);
+    return ci == 0 || (ci >= kMinCK && ci <= kLCMax && (ci & (ci - 1)) == 0);
 }
+inline bool ck_direct(int ci) { return ci != 0 && kCK % ci == 0; }
 inline size_t ws_up(size_t v) { return (v + 63) & ~size_t(63); }  // 256-byte aligned regions
 // floats the forward keeps for the backward: [ceil(T/ci)][N/4][D][4]
 inline size_t saved_floats(int64_t T, int D, int N, int ci) {
@@ -214,7 +218,7 @@ struct ScanWs {
     size_t bc;        // [T][2N]          fp32 copy of the B and C rows (each pass makes its own)
     size_t P, S;      // forward: P [nfchunk][D] sum of delta (NaN: cut by a head), S [nfchunk][N][D] local end state
     size_t hin;       // [nfchunk][N/4][D][4] forward: state entering each chunk
-    size_t dense;     // [nck][N/4][D][4] backward with ci != kCK: replayed checkpoints
+    size_t dense;     // [nck][N/4][D][4] backward unless ck_direct(ci): replayed checkpoints
     size_t Pr, Sr;    // backward, per summary sub-chunk: Pr [nsum][D] as P, Sr [nsum][N][D] reverse carry
     size_t cin;       // [nbchunk][N][D]  backward: carry entering each chunk from the right
     size_t dApart;    // [nbchunk][N][D]
@@ -246,7 +250,7 @@ inline ScanWs scan_ws_layout(int64_t T, int D, int N, int ci) {
     w.hin = off; off = ws_up(off + (size_t)w.nfchunk * ND);
     w.fwd_total = off;
     off = (ci == 0) ? w.fwd_total : after_bc;
-    if (ci != kCK) { w.dense = off; off = ws_up(off + (size_t)w.nck * ND); }
+    if (!ck_direct(ci)) { w.dense = off; off = ws_up(off + (size_t)w.nck * ND); }
     w.Pr = off; off = ws_up(off + (size_t)w.nsum * D);
     w.Sr = off; off = ws_up(off + (size_t)w.nsum * ND);
     w.cin = off; off = ws_up(off + (size_t)w.nbchunk * ND);

@@ -268,7 +268,7 @@ __device__ __forceinline__ void out_block(const T* lds, const float* __restrict_
         if constexpr (SAFE) {
             if (k >= nt) break;
         }
-        if (k % kCK == 0 && cish >= 0 && ((tb + k) & ((int64_t(1) << cish) - 1)) == 0 && act) {
+        if (k % kMinCK == 0 && cish >= 0 && ((tb + k) & ((int64_t(1) << cish) - 1)) == 0 && act) {
             ck_store<NS>(saved + (size_t)((tb + k) >> cish) * ND, d, D, h);
         }
         float nxt[2 * NS];

@@ -56,10 +56,10 @@ def test_status_strings(lib):
 
 
 def test_workspace_sizes(lib):
-    # checkpoints (the fp32 states of every 4th token) dominate the scan workspace
+    # checkpoints (the fp32 states of every 8th token) dominate the scan workspace
     T, D, N = 32768, 4096, 16
     ws = lib.selective_scan_pack_workspace_bytes(T, D, N)
-    assert ws >= (T // 4) * D * N * 4
+    assert ws >= (T // 8) * D * N * 4
     assert lib.selective_scan_pack_workspace_bytes(0, D, N) == 0
     assert lib.conv1d_pack_bwd_workspace_bytes(T, D, 4) >= 5 * D * 4
     assert lib.conv1d_pack_bwd_workspace_bytes(0, D, 4) == 0
@@ -146,16 +146,18 @@ def test_checkpoint_interval_sizes(lib):
         assert lib.selective_scan_pack_saved_bytes(T, D, N, bad) == 0
         assert lib.selective_scan_pack_bwd_scratch_bytes(T, D, N, bad) == 0
     # the forward's scratch is small next to the dense states; the backward's
-    # holds dense replayed states unless it reads the forward's every 4 tokens
+    # holds states 8 tokens apart, replayed, unless the forward kept every
+    # 4th or 8th
     fwd = lib.selective_scan_pack_fwd_scratch_bytes(T, D, N)
-    dense = (T // 4) * D * N * 4
-    assert 0 < fwd < dense // 8
-    b4 = lib.selective_scan_pack_bwd_scratch_bytes(T, D, N, 4)
-    for ci in (0, 8, 2048):
-        assert lib.selective_scan_pack_bwd_scratch_bytes(T, D, N, ci) >= b4 + dense
-    # the single workspace of the other entry points: kept states every 4 tokens, then the scratch
-    assert lib.selective_scan_pack_workspace_bytes(T, D, N) == (lib.selective_scan_pack_saved_bytes(T, D, N, 4)
-                                                                + max(fwd, b4))
+    dense = (T // 8) * D * N * 4
+    assert 0 < fwd < dense // 4
+    b8 = lib.selective_scan_pack_bwd_scratch_bytes(T, D, N, 8)
+    assert lib.selective_scan_pack_bwd_scratch_bytes(T, D, N, 4) == b8
+    for ci in (0, 16, 2048):
+        assert lib.selective_scan_pack_bwd_scratch_bytes(T, D, N, ci) >= b8 + dense
+    # the single workspace of the other entry points: kept states every 8 tokens, then the scratch
+    assert lib.selective_scan_pack_workspace_bytes(T, D, N) == (lib.selective_scan_pack_saved_bytes(T, D, N, 8)
+                                                                + max(fwd, b8))
 
 
 def test_host_validation_checkpoint_interval(lib):

@@ -6,7 +6,7 @@ gets the others back (read, replayed from sparser ones, or recomputed from the
 inputs). The replay repeats the forward's arithmetic operation for operation
 within a forward chunk (64 tokens or more), so intervals up to 64 and the
 recomputing interval 0 must give the same bits as the forward that keeps
-every 4th state. Longer intervals replay across chunk boundaries, where the
+every 4th state (which the backward reads every 8th of). Longer intervals replay across chunk boundaries, where the
 forward restarted from its carry pass's state: the same states up to
 rounding, so those results agree to the gradient tolerance. Intervals 0, 64
 and 2048 are also checked against the fp64 oracle.
@@ -100,7 +100,7 @@ def test_every_interval_gives_the_same_bits(name):
     inp, gate, kw, _, st, _ = _case(name)
     d = Dev(inp)
     ref_out, ref_hT, ref_g = _run(d, inp, gate, kw, st, 4)
-    # the single-workspace entry points are the interval-4 case
+    # the single-workspace entry points are the interval-8 case
     lw = {}
     if st:
         lw = dict(cu_seqlens=d.cu, initial_state=st["initial_state"], final_state=True)
