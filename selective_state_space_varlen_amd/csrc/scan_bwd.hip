@@ -400,7 +400,9 @@ template <int NS>
 struct BwdShared {
     static constexpr int NH = Split<NS>::NH, SW = Split<NS>::SW;
     BwdBuf<NS> buf[2];
-    float xb[SW][4 * NH][kXRow];      // per wave, a token pair: dB and dC terms of its states
+    // per wave, a token pair: dB and dC terms of its states (summed in
+    // registers instead with 4 states a wave)
+    float xb[NH == 4 ? 1 : SW][4 * NH][kXRow];
 };
 
 // Replay of a block from the state hin entering its first token: each
@@ -473,11 +475,63 @@ __device__ __forceinline__ void bwd_replay(BwdBuf<NS>& bf, const TokVals& tv, co
     static_for_until<K>(step, SAFE ? nb : K);
 }
 
+// Sum over the 64 lanes of a wave of 16 values per lane, in registers. Each
+// step folds two halves of the lanes onto each other and pairs two values,
+// so the values per lane halve with the lanes each partial sum spans:
+//  - 32-lane halves: v_permlane32_swap exchanges the upper half of one
+//    register with the lower half of another, and the two results add up to
+//    value j on lanes 0-31 and value j + 8 on lanes 32-63;
+//  - 16-lane rows: v_permlane16_swap (odd rows of one register with even rows
+//    of the other), likewise;
+//  - 8- and 4-lane halves of a row: a DPP rotate by 8, or shift by 4, adds
+//    each lane's partner, and the bank mask keeps the half that holds the
+//    value;
+//  - the four lanes of a quad: two DPP adds.
+// Lane l ends with the total of value l / 4. The swaps are inline assembly
+// (the compiler's builtins for them return the first register twice), and so
+// are the DPP adds, for the bank masks. Each block first waits the two states
+// a swap or DPP read needs after a VALU write of its source, and the last
+// waits them after itself, since the compiler does not count inline assembly
+// as VALU.
+__device__ __forceinline__ float wave_sum16(const float (&v)[16]) {
+    float w[16], x[4], y[2], z;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) w[j] = v[j];
+    // after a swap of (a, b): a = (a lo, b lo), b = (a hi, b hi). One wait
+    // state pair first: a swap reading a register a VALU just wrote needs them.
+    asm("s_nop 1\n\t"
+        "v_permlane32_swap_b32 %0, %8\n\tv_permlane32_swap_b32 %1, %9\n\t"
+        "v_permlane32_swap_b32 %2, %10\n\tv_permlane32_swap_b32 %3, %11\n\t"
+        "v_permlane32_swap_b32 %4, %12\n\tv_permlane32_swap_b32 %5, %13\n\t"
+        "v_permlane32_swap_b32 %6, %14\n\tv_permlane32_swap_b32 %7, %15"
+        : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]), "+v"(w[6]), "+v"(w[7]),
+          "+v"(w[8]), "+v"(w[9]), "+v"(w[10]), "+v"(w[11]), "+v"(w[12]), "+v"(w[13]), "+v"(w[14]), "+v"(w[15]));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] += w[j + 8];
+    // odd rows of the first with even rows of the second
+    asm("s_nop 1\n\t"
+        "v_permlane16_swap_b32 %0, %4\n\tv_permlane16_swap_b32 %1, %5\n\t"
+        "v_permlane16_swap_b32 %2, %6\n\tv_permlane16_swap_b32 %3, %7"
+        : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]), "+v"(w[6]), "+v"(w[7]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = w[j] + w[j + 4];
+    // x[j]: value j + 4 * (l / 16). y[j]: value j (lanes 0-7 of a row) or j + 2 (lanes 8-15) + 4 * row
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0x3" : "=v"(y[j]) : "v"(x[j]));
+        asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0xc" : "+v"(y[j]) : "v"(x[j + 2]));
+    }
+    // z: value l / 4 (lanes 0-3 and 8-11 of a row take lane + 4, the others lane - 4)
+    asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_shl:4 row_mask:0xf bank_mask:0x5" : "=v"(z) : "v"(y[0]));
+    asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_shr:4 row_mask:0xf bank_mask:0xa\n\ts_nop 1" : "+v"(z) : "v"(y[1]));
+    return group_sum<4>(z);
+}
+
 // Reverse step over the block, a token pair at a time; after each pair, dB
 // (kind 0: sum over channels of dh * step*u) and dC (kind 1: of g * h) of its
-// two tokens. A lane's channels are added in registers; each value is then
-// added up over the wave's lanes by LPO lanes reading the terms the wave left
-// in LDS.
+// two tokens. A lane's channels are added in registers, then each value over
+// the wave's lanes: with 4 states a wave (16 values a pair) by wave_sum16;
+// with fewer, by LPO lanes reading the terms the wave left in LDS.
 template <bool SAFE, bool ST, int NS>
 __device__ __forceinline__ void bwd_reverse(BwdBuf<NS>& bf, float* __restrict__ myx, const TokVals& tv,
                                             const BcRegs<NS>& bc, int nb, uint32_t heads, int lane, int q,
@@ -489,10 +543,16 @@ __device__ __forceinline__ void bwd_reverse(BwdBuf<NS>& bf, float* __restrict__ 
                                             float* __restrict__ dbc_row, float* __restrict__ sink, const ScanOpts& opt, int64_t tb, int D,
                                             const int (&dd)[kCl]) {
     constexpr int NH = Split<NS>::NH, K = kSub;
+    constexpr bool kRegSum = NH == 4;
     constexpr int LPO = kWave / (4 * NH);  // lanes adding up one dB/dC value of a token pair
     constexpr int CPL = kWave / LPO;       // lanes' terms each of them adds
     static_assert(K % 2 == 0 && CPL % 4 == 0, "tiling");
     const int n0 = q * NH;
+    float xr[2][2][NH];  // a pair's dB/dC terms: [token][kind][state]
+    auto put = [&](int tk, int kind, int i, float v) {
+        if constexpr (kRegSum) xr[tk][kind][i] = v;
+        else myx[((tk * 2 + kind) * NH + i) * kXRow + lane] = v;
+    };
     auto tok = [&](auto KKc) {
         constexpr int kk = decltype(KKc)::value;
         constexpr int tk = kk % 2;
@@ -542,8 +602,8 @@ __device__ __forceinline__ void bwd_reverse(BwdBuf<NS>& bf, float* __restrict__ 
                     const bool gp = ST && opt.dhT && t > 0 && act[c];
                     carry[c][i] = gp ? opt.dhT[((size_t)s_prev * D + dd[c]) * NS + n0 + i] : 0.0f;
                 }
-                myx[((tk * 2 + 0) * NH + i) * kXRow + lane] = xB;
-                myx[((tk * 2 + 1) * NH + i) * kXRow + lane] = xC;
+                put(tk, 0, i, xB);
+                put(tk, 1, i, xC);
             };
             static_for<NH>(state);
         } else {
@@ -569,41 +629,81 @@ __device__ __forceinline__ void bwd_reverse(BwdBuf<NS>& bf, float* __restrict__ 
                     sumAr[c] = __builtin_fmaf(r, A2[c][i], sumAr[c]);
                     dA[c][i] = __builtin_fmaf(r, dt[c], dA[c][i]);
                 }
-                myx[((tk * 2 + 0) * NH + i) * kXRow + lane] = xB;
-                myx[((tk * 2 + 1) * NH + i) * kXRow + lane] = xC;
+                put(tk, 0, i, xB);
+                put(tk, 1, i, xC);
             };
             static_for<NH>(state);
         }
         bf.part[1][kk][q][lane] = lds_vec(sumB);
         bf.part[2][kk][q][lane] = lds_vec(sumAr);
     };
-    auto pair = [&](auto KPc) {
-        constexpr int kp = K / 2 - 1 - decltype(KPc)::value;  // pairs right to left
-        tok(std::integral_constant<int, 2 * kp + 1>{});
-        tok(std::integral_constant<int, 2 * kp>{});
-        wave_sync();
-        {
-            // the LPO lanes of an output read interleaved float4s: together a
-            // contiguous run, conflict-free
-            const int o = lane / LPO, sl = lane % LPO;
-            const int tk = o / (2 * NH), kind = (o / NH) % 2, i = o % NH;
-            const int kk = 2 * kp + tk;
-            const float4* xv = reinterpret_cast<const float4*>(myx + ((tk * 2 + kind) * NH + i) * kXRow) + sl;
+    // where lane's total of a pair goes: value o = lane / LPO, i.e. token tk,
+    // kind, state oi of the pair
+    const int o = lane / LPO;
+    const int tk = o / (2 * NH), kind = (o / NH) % 2, oi = o % NH;
+    auto store = [&](int kp, float acc) {
+        const int kk = 2 * kp + tk;
+        // every lane of the output stores the same value: no lane-dependent branch
+        float* dst = (!SAFE || kk < nb) ? dbc_row + (size_t)kk * 2 * NS + kind * NS + n0 + oi : sink + lane;
+        *dst = acc;
+    };
+    if constexpr (kRegSum) {
+        auto pair = [&](auto KPc) {
+            constexpr int kp = K / 2 - 1 - decltype(KPc)::value;  // pairs right to left
+            if constexpr (SAFE) {
+                // tokens past a short block leave their terms unset; their
+                // totals go to the sink
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+                    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+                        for (int i = 0; i < NH; ++i) xr[t2][k2][i] = 0.0f;
+            }
+            tok(std::integral_constant<int, 2 * kp + 1>{});
+            tok(std::integral_constant<int, 2 * kp>{});
+            float v[16];
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+                    for (int i = 0; i < NH; ++i) v[(t2 * 2 + k2) * NH + i] = xr[t2][k2][i];
+            store(kp, wave_sum16(v));
+        };
+        static_for<K / 2>(pair);
+    } else {
+        // The terms of a pair are read back right after they are written and
+        // added up after the next pair's reverse step: a wave's LDS accesses
+        // complete in issue order, so the next pair's writes cannot overtake
+        // the reads, and the reads' latency hides behind that step. The LPO
+        // lanes of an output read interleaved float4s: together a contiguous
+        // run, conflict-free.
+        const float4* __restrict__ xv =
+            reinterpret_cast<const float4*>(myx + ((tk * 2 + kind) * NH + oi) * kXRow) + lane % LPO;
+        float4 rx[CPL / 4];
+        auto finish = [&](int kp) {
             float acc;
 #pragma unroll
             for (int m = 0; m < CPL / 4; ++m) {
-                const float4 xa = xv[m * LPO];
-                const float v = (xa.x + xa.y) + (xa.z + xa.w);
-                acc = (m == 0) ? v : acc + v;
+                const float s4 = (rx[m].x + rx[m].y) + (rx[m].z + rx[m].w);
+                acc = (m == 0) ? s4 : acc + s4;
             }
-            acc = group_sum<LPO>(acc);
-            // every lane of the output stores the same value: no lane-dependent branch
-            float* dst = (!SAFE || kk < nb) ? dbc_row + (size_t)kk * 2 * NS + kind * NS + n0 + i : sink + lane;
-            *dst = acc;
-        }
-        wave_sync();
-    };
-    static_for<K / 2>(pair);
+            store(kp, group_sum<LPO>(acc));
+        };
+        auto pair = [&](auto KPc) {
+            constexpr int kp = K / 2 - 1 - decltype(KPc)::value;  // pairs right to left
+            tok(std::integral_constant<int, 2 * kp + 1>{});
+            tok(std::integral_constant<int, 2 * kp>{});
+            if constexpr (kp + 1 < K / 2) finish(kp + 1);
+            wave_sync();
+#pragma unroll
+            for (int m = 0; m < CPL / 4; ++m) rx[m] = xv[m * LPO];
+            wave_sync();
+        };
+        static_for<K / 2>(pair);
+        finish(0);
+    }
 }
 
 // The reverse pass over one chunk. Per kSub-token block, right to left:
@@ -793,7 +893,7 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
             }
         }
         float* __restrict__ dbc_row = p.dBC + ((size_t)g * T_ + tb) * 2 * NS;
-        float* __restrict__ myx = &sh.xb[q][0][0];
+        float* __restrict__ myx = &sh.xb[NH == 4 ? 0 : q][0][0];
         if (heads == 0 && nb == K) {
             bwd_replay<false, ST, NS>(bf, tv, b.bc, nb, heads, lane, q, act, A2, b.hn, hh, ak, p.opt, tb, D, dd);
             bwd_reverse<false, ST, NS>(bf, myx, tv, b.bc, nb, heads, lane, q, act, A2, b.hn, hh, ak, carry, dA,
