@@ -22,6 +22,14 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __builtin_b
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t word) { return __builtin_bit_cast(float, word & 0xffff0000u); }
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
+// A buffer resource over n bytes at p. Raw buffer stores past the n bytes are
+// dropped by the hardware, so lanes (and rows, with n = 0) that have nothing
+// to store need neither a branch nor a dummy target. The third word is the
+// gfx9 raw-buffer format (32-bit data format, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bytes_rsrc(const void* p, uint32_t n) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)n, 0x00020000);
+}
+
 template <typename T>
 struct Elt;
 
@@ -39,6 +47,10 @@ struct Elt<float> {
     }
     static __device__ __forceinline__ float cvt(uint32_t b) { return __builtin_bit_cast(float, b); }
     static __device__ __forceinline__ void st(float* __restrict__ p, size_t i, float v) { p[i] = v; }
+    // store at byte offset o of a buffer resource (dropped past its end)
+    static __device__ __forceinline__ void st_rsrc(__amdgpu_buffer_rsrc_t r, uint32_t o, float v) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)o, 0, 0);
+    }
     static __device__ __forceinline__ void st_nt(float* __restrict__ p, size_t i, float v) {
         __builtin_nontemporal_store(v, p + i);
     }
@@ -61,6 +73,9 @@ struct Elt<uint16_t> {
     static __device__ __forceinline__ uint32_t raw(const uint16_t* __restrict__ p, size_t i) { return p[i]; }
     static __device__ __forceinline__ float cvt(uint32_t b) { return bf16_to_f32(b); }
     static __device__ __forceinline__ void st(uint16_t* __restrict__ p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+    static __device__ __forceinline__ void st_rsrc(__amdgpu_buffer_rsrc_t r, uint32_t o, float v) {
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, (int)o, 0, 0);
+    }
     static __device__ __forceinline__ void st_nt(uint16_t* __restrict__ p, size_t i, float v) {
         __builtin_nontemporal_store(f32_to_bf16(v), p + i);
     }

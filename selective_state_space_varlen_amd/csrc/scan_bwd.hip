@@ -736,7 +736,6 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
     const int64_t c_ = blockIdx.x / ngroup;
     int d[kCl], dd[kCl];
     bool act[kCl];
-    const bool whole = (g + 1) * kGroupCh <= D;  // every lane's channels exist
 #pragma unroll
     for (int c = 0; c < kCl; ++c) {
         d[c] = g * kGroupCh + kCl * lane + c;
@@ -927,8 +926,12 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
             const float(&yv)[kCl] = y.v;
             const float(&sBv)[kCl] = sB.v;
             const float(&sAv)[kCl] = sA.v;
+            // the token's rows as buffer resources: a token past the block gets
+            // empty ones, a lane past D an offset past the row; both stores drop
             const size_t rb = (size_t)(tok ? tb + kk : 0) * D;
-            T* __restrict__ sinkT = reinterpret_cast<T*>(p.sink);
+            const uint32_t rowb = tok ? (uint32_t)D * (uint32_t)sizeof(T) : 0u;
+            const auto rdu = bytes_rsrc(p.du + rb, rowb), rdd = bytes_rsrc(p.ddelta + rb, rowb);
+            const auto rdz = bytes_rsrc(GATE ? p.dz + rb : p.du, GATE ? rowb : 0u);
 #pragma unroll
             for (int c = 0; c < kCl; ++c) {
                 const float uu = ev.u[j][c];
@@ -941,17 +944,10 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
                 }
                 dDacc[c] = __builtin_fmaf(ev.gg[j][c], uu, dDacc[c]);
                 const float dzv = yy * ev.fz[j][c];
-                if (whole && nb == K) {
-                    // every lane stores into the tensors (a uniform branch)
-                    Elt<T>::st(at_bytes(p.du + rb, bo[c]), 0, duv);
-                    Elt<T>::st(at_bytes(p.ddelta + rb, bo[c]), 0, ddv);
-                    if constexpr (GATE) Elt<T>::st(at_bytes(p.dz + rb, bo[c]), 0, dzv);
-                } else {
-                    const bool w = tok && act[c];
-                    Elt<T>::st(w ? p.du + rb : sinkT, w ? d[c] : 0, duv);
-                    Elt<T>::st(w ? p.ddelta + rb : sinkT, w ? d[c] : 1, ddv);
-                    if constexpr (GATE) Elt<T>::st(w ? p.dz + rb : sinkT, w ? d[c] : 2, dzv);
-                }
+                const uint32_t o = (uint32_t)d[c] * (uint32_t)sizeof(T);
+                Elt<T>::st_rsrc(rdu, o, duv);
+                Elt<T>::st_rsrc(rdd, o, ddv);
+                if constexpr (GATE) Elt<T>::st_rsrc(rdz, o, dzv);
             }
         }
     };
