@@ -29,6 +29,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t bytes_rsrc(const void* p, uint32_t n) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)n, 0x00020000);
 }
+// cache-policy argument of a raw buffer access: non-temporal
+constexpr int kBufNT = 2;
 
 template <typename T>
 struct Elt;
@@ -47,9 +49,11 @@ struct Elt<float> {
     }
     static __device__ __forceinline__ float cvt(uint32_t b) { return __builtin_bit_cast(float, b); }
     static __device__ __forceinline__ void st(float* __restrict__ p, size_t i, float v) { p[i] = v; }
-    // store at byte offset o of a buffer resource (dropped past its end)
+    // store at byte offset o of a buffer resource (dropped past its end);
+    // AUX 2 marks it non-temporal
+    template <int AUX = 0>
     static __device__ __forceinline__ void st_rsrc(__amdgpu_buffer_rsrc_t r, uint32_t o, float v) {
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)o, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)o, 0, AUX);
     }
     static __device__ __forceinline__ void st_nt(float* __restrict__ p, size_t i, float v) {
         __builtin_nontemporal_store(v, p + i);
@@ -73,8 +77,9 @@ struct Elt<uint16_t> {
     static __device__ __forceinline__ uint32_t raw(const uint16_t* __restrict__ p, size_t i) { return p[i]; }
     static __device__ __forceinline__ float cvt(uint32_t b) { return bf16_to_f32(b); }
     static __device__ __forceinline__ void st(uint16_t* __restrict__ p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+    template <int AUX = 0>
     static __device__ __forceinline__ void st_rsrc(__amdgpu_buffer_rsrc_t r, uint32_t o, float v) {
-        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, (int)o, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, (int)o, 0, AUX);
     }
     static __device__ __forceinline__ void st_nt(uint16_t* __restrict__ p, size_t i, float v) {
         __builtin_nontemporal_store(f32_to_bf16(v), p + i);

@@ -89,16 +89,23 @@ __device__ __forceinline__ size_t ck_index(int d, int n, int D) {
     if constexpr (NS % 4 == 0) return (((size_t)(n >> 2) * D + d) << 2) + (n & 3);
     else return (size_t)n * D + d;
 }
+// Non-temporal stores through buffer resources over the slot's rows: a lane
+// past D (d >= D) lands past its row's end, which the hardware drops, so
+// callers need no per-lane branch.
 template <int NS>
 __device__ __forceinline__ void ck_store(float* __restrict__ slot, int d, int D, const float (&h)[NS]) {
     if constexpr (NS % 4 == 0) {
 #pragma unroll
-        for (int j = 0; j < NS / 4; ++j)
-            __builtin_nontemporal_store(nf4{h[4 * j], h[4 * j + 1], h[4 * j + 2], h[4 * j + 3]},
-                                        reinterpret_cast<nf4*>(slot) + (size_t)j * D + d);
+        for (int j = 0; j < NS / 4; ++j) {
+            const auto r = bytes_rsrc(slot + (size_t)j * D * 4, (uint32_t)D * 16u);
+            const nf4 v = {h[4 * j], h[4 * j + 1], h[4 * j + 2], h[4 * j + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v),
+                                                   r, (int)((uint32_t)d * 16u), 0, kBufNT);
+        }
     } else {
 #pragma unroll
-        for (int n = 0; n < NS; ++n) slot[(size_t)n * D + d] = h[n];
+        for (int n = 0; n < NS; ++n)
+            Elt<float>::st_rsrc<kBufNT>(bytes_rsrc(slot + (size_t)n * D, (uint32_t)D * 4u), (uint32_t)d * 4u, h[n]);
     }
 }
 // states n0 .. n0+NH-1 of channel d (zero when `on` is false)

@@ -247,7 +247,7 @@ __global__ __launch_bounds__(256) void k_scan_fwd_carry(const float* __restrict_
 template <bool SAFE, bool GATE, bool XS, bool ST, typename T, int NS, int BT, typename St>
 __device__ __forceinline__ void out_block(const T* lds, const float* __restrict__ bc, int64_t tb, int nt,
                                           uint32_t heads, uint32_t ends, const float (&A2)[NS], float (&h)[NS],
-                                          float Dv, int lane, T* __restrict__ ob, int D, int d, int dd, bool store,
+                                          float Dv, int lane, T* __restrict__ ob, int D, int d, int dd,
                                           float* __restrict__ saved, int cish, size_t ND, bool act,
                                           const StepMap& sm, const ScanOpts& opt) {
     const float gf = opt.gate_floor;
@@ -268,9 +268,8 @@ __device__ __forceinline__ void out_block(const T* lds, const float* __restrict_
         if constexpr (SAFE) {
             if (k >= nt) break;
         }
-        if (k % kMinCK == 0 && cish >= 0 && ((tb + k) & ((int64_t(1) << cish) - 1)) == 0 && act) {
+        if (k % kMinCK == 0 && cish >= 0 && ((tb + k) & ((int64_t(1) << cish) - 1)) == 0)
             ck_store<NS>(saved + (size_t)((tb + k) >> cish) * ND, d, D, h);
-        }
         float nxt[2 * NS];
         const bool more = SAFE ? (k + 1 < nt) : (k + 1 < BT);
         if (more) load_rowv<2 * NS>(rows + (k + 1) * 2 * NS, nxt);
@@ -310,7 +309,10 @@ __device__ __forceinline__ void out_block(const T* lds, const float* __restrict_
             const float zz = zv[k];
             y *= __builtin_fmaf(zz, sigmoid_fast(zz), gf);
         }
-        if (store) Elt<T>::st_nt(ob, (size_t)(k * D + d), y);
+        // the token's row as a buffer resource: a lane past D stores past its
+        // end, which the hardware drops
+        Elt<T>::template st_rsrc<kBufNT>(bytes_rsrc(ob + (size_t)k * D, (uint32_t)D * (uint32_t)sizeof(T)),
+                                         (uint32_t)d * (uint32_t)sizeof(T), y);
         if (more) {
 #pragma unroll
             for (int j = 0; j < 2 * NS; ++j) cur[j] = nxt[j];
@@ -341,7 +343,6 @@ __global__ __launch_bounds__(64, (ST || XS || sizeof(T) == 4) ? 2 : 4) void k_sc
     const int64_t t0 = c * lc;
     const int64_t t1 = (t0 + lc < T_) ? t0 + lc : T_;
     const size_t ND = (size_t)NS * D;
-    const bool store = act || (tl.g + 1) * kWave <= D;
 
     float A2[NS], h[NS];
 #pragma unroll
@@ -365,11 +366,11 @@ __global__ __launch_bounds__(64, (ST || XS || sizeof(T) == 4) ? 2 : 4) void k_sc
         const int nt = (int)((tb + BT < t1) ? BT : t1 - tb);
         T* __restrict__ ob = out + (size_t)tb * D;
         if ((heads | ends) == 0 && nt == BT)
-            out_block<false, GATE, XS, ST, T, NS, BT, St>(lds, bc, tb, BT, 0u, 0u, A2, h, Dv, lane, ob, D, d, dd, store,
+            out_block<false, GATE, XS, ST, T, NS, BT, St>(lds, bc, tb, BT, 0u, 0u, A2, h, Dv, lane, ob, D, d, dd,
                                                   saved, cish, ND, act, sm, opt);
         else
             out_block<true, GATE, XS, ST, T, NS, BT, St>(lds, bc, tb, nt, heads, ends, A2, h, Dv, lane, ob, D, d, dd,
-                                                 store, saved, cish, ND, act, sm, opt);
+                                                 saved, cish, ND, act, sm, opt);
     }
 }
 
@@ -396,7 +397,7 @@ __device__ __forceinline__ void replay_block(const T* lds, const float* __restri
         if constexpr (SAFE) {
             if (k >= nt) break;
         }
-        if (k % kCK == 0 && act) ck_store<NS>(ck + (size_t)(k / kCK) * ND, d, D, h);
+        if (k % kCK == 0) ck_store<NS>(ck + (size_t)(k / kCK) * ND, d, D, h);
         float nxt[NS];
         const bool more = SAFE ? (k + 1 < nt) : (k + 1 < BT);
         if (more) load_rowv<NS>(rows + (k + 1) * 2 * NS, nxt);
