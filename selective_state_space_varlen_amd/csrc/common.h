@@ -124,6 +124,18 @@ __device__ __forceinline__ float sigmoid_fast(float v) {
 // only stops the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void wave_sync() { __builtin_amdgcn_wave_barrier(); }
 
+// Wait for every scalar load (and LDS access) in flight, as a real s_waitcnt
+// that the compiler's wait pass sees, and keep later instructions after it.
+// Scalar loads complete out of order, so any wait for one waits for all:
+// issued before the loads of the next token's rows, it keeps the wait for
+// this token's rows from landing after them, which would expose their whole
+// latency on every token.
+__device__ __forceinline__ void scalar_loads_done() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+    asm volatile("" ::: "memory");       // no load moves above it
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Value of the neighbouring lane (lane ^ 1) through DPP, without the LDS path.
 __device__ __forceinline__ float swap_adjacent(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));

@@ -75,10 +75,12 @@ __device__ __forceinline__ void bsum_block(const T* lds, const float* __restrict
         }
         float nxt[NS];
         const bool more = SAFE ? (k + 1 < nt) : (k + 1 < BT);
+        scalar_loads_done();
         if (more) {
 #pragma unroll
             for (int n = 0; n < NS; ++n) nxt[n] = rows[(k + 1) * 2 * NS + n];
         }
+        __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of this token's arithmetic
         const float dt = dtv[k];
         const float g = gv[k];
         const float yk = dt - cdt;

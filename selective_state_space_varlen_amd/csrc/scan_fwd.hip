@@ -75,7 +75,9 @@ __device__ __forceinline__ void summary_block(const T* lds, const float* __restr
         }
         float nxt[NS];
         const bool more = SAFE ? (k + 1 < nt) : (k + 1 < BT);
+        scalar_loads_done();
         if (more) load_rowv<NS>(rows + (k + 1) * 2 * NS, nxt);
+        __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of this token's arithmetic
         const float dt = dtv[k];
         const float dtu = dt * uv[k];
         // compensated sum of delta: the chunk's decay is exp2(A2 * sum delta)
@@ -272,7 +274,9 @@ __device__ __forceinline__ void out_block(const T* lds, const float* __restrict_
             ck_store<NS>(saved + (size_t)((tb + k) >> cish) * ND, d, D, h);
         float nxt[2 * NS];
         const bool more = SAFE ? (k + 1 < nt) : (k + 1 < BT);
+        scalar_loads_done();
         if (more) load_rowv<2 * NS>(rows + (k + 1) * 2 * NS, nxt);
+        __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of this token's arithmetic
         // the step map next to its use: mapping the whole block first held
         // the first state update behind eight softplus chains
         const float dt = XS ? sm.eff(dtv[k]) : dtv[k];
@@ -400,7 +404,9 @@ __device__ __forceinline__ void replay_block(const T* lds, const float* __restri
         if (k % kCK == 0) ck_store<NS>(ck + (size_t)(k / kCK) * ND, d, D, h);
         float nxt[NS];
         const bool more = SAFE ? (k + 1 < nt) : (k + 1 < BT);
+        scalar_loads_done();
         if (more) load_rowv<NS>(rows + (k + 1) * 2 * NS, nxt);
+        __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of this token's arithmetic
         const float dt = XS ? sm.eff(dtv[k]) : dtv[k];
         const float dtu = dt * uv[k];
         if constexpr (SAFE) {
