@@ -51,7 +51,7 @@ SCAN_BWD_FLOPS_PER_TDN = 15
 # change to those sources reports null until the counters are taken again.
 MEASURED_TRAFFIC = {
     "scan_bwd": {"bytes": 4044326498, "sources": ["scan_bwd.hip", "scan_common.h", "common.h"],
-                 "sha256": "558328bb72809e9ec12fac5ccf831701ffbddedd577f37c8d91ced11e0438602"},
+                 "sha256": "720193869c129889f6948a3414803bbeb8beab903f29203fcf7cfc799da966f6"},
 }
 
 

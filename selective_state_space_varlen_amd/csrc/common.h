@@ -35,10 +35,10 @@ constexpr int kBufNT = 2;
 template <typename T>
 struct Elt;
 
-// st_nt: a non-temporal store, for outputs that no kernel of the pass reads
-// again soon (they then do not push shared inputs out of the L2). Only where a
-// wave's stores cover whole 128-byte lines: partial lines stored this way
-// reach memory unmerged.
+// st_rsrc<kBufNT>: a non-temporal store, for outputs that no kernel of the
+// pass reads again soon (they then do not push shared inputs out of the L2).
+// Only where a wave's stores cover whole 128-byte lines: partial lines stored
+// this way reach memory unmerged.
 // raw: the element's bits, loaded without conversion (so a load issued ahead
 // of its use is not waited on at once); cvt: those bits as fp32.
 template <>
@@ -54,9 +54,6 @@ struct Elt<float> {
     template <int AUX = 0>
     static __device__ __forceinline__ void st_rsrc(__amdgpu_buffer_rsrc_t r, uint32_t o, float v) {
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)o, 0, AUX);
-    }
-    static __device__ __forceinline__ void st_nt(float* __restrict__ p, size_t i, float v) {
-        __builtin_nontemporal_store(v, p + i);
     }
 };
 
@@ -80,9 +77,6 @@ struct Elt<uint16_t> {
     template <int AUX = 0>
     static __device__ __forceinline__ void st_rsrc(__amdgpu_buffer_rsrc_t r, uint32_t o, float v) {
         __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, (int)o, 0, AUX);
-    }
-    static __device__ __forceinline__ void st_nt(uint16_t* __restrict__ p, size_t i, float v) {
-        __builtin_nontemporal_store(f32_to_bf16(v), p + i);
     }
 };
 

@@ -912,7 +912,7 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
 #pragma unroll
         for (int j = 0; j < KQ; ++j) {
             const int kk = q + j * SW;
-            const bool tok = kk < nb;  // tokens past the block store to the sink
+            const bool tok = kk < nb;  // tokens past the block store nothing
             LdsVec<kCl> y = bf.part[0][kk][0][lane], sB = bf.part[1][kk][0][lane], sA = bf.part[2][kk][0][lane];
 #pragma unroll
             for (int w = 1; w < SW; ++w) {
