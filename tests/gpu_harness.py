@@ -63,6 +63,35 @@ def assert_close(got, ref, tol, name):
         f"at {np.unravel_index(int(np.nanargmax(np.where(np.isfinite(err), err, np.inf))), err.shape)}")
 
 
+# Rounding of the conv pre-activation v = b + sum_k w x. The library forms v
+# in fp32 whatever the storage dtype, so v is off by at most about
+# GAMMA_PRE * 2^-24 * vs, vs = |b| + sum_k |w x| (the forward error bound of
+# a short dot product, Higham, Accuracy and Stability of Numerical
+# Algorithms, section 3.1). Where v cancels (|v| << vs) that is far above the
+# rounding of v's own size: u = silu(v) moves by up to max|silu'| (< 1.1)
+# times it, and silu'(v) in the conv backward by up to max|silu''| (= 0.5,
+# at v = 0) times it, most visibly near v = -1.2785 where silu' is zero. A
+# sum over channels that holds one or a few such terms inherits that error,
+# which the magnitudes of its terms do not bound.
+GAMMA_PRE = 8
+SILU1_MAX = 1.1
+SILU2_MAX = 0.5
+
+
+def preact_scale(orc, x, w, b, cu_seqlens, xc0, tol):
+    """kappa * vs per token and channel, kappa = GAMMA_PRE * 2^-24 / tol: the
+    pre-activation's rounding bound in units of the tolerance. A chain's
+    error scales taken with |u| + SILU1_MAX * this in place of u (in the
+    scan) and with SILU2_MAX * this times the scale of du added to silu'(v)
+    (in the conv backward) bound, times tol, the rounding of each sum plus
+    what the pre-activation's rounding adds to it. vs comes from the
+    oracle's conv on the magnitudes of its inputs, without the activation."""
+    def ab(a):
+        return None if a is None else np.abs(a)
+    vs, _, _ = orc.conv_fwd_state(ab(x), ab(w), ab(b), cu_seqlens, ab(xc0), silu=False, threads=8)
+    return vs * (GAMMA_PRE * 2.0 ** -24 / tol)
+
+
 def assert_sum_close(got, ref, scale, tol, name):
     """A sum that may cancel, element by element: |got - ref| <= tol * scale,
     where scale is the sum of the magnitudes of the terms of each element
