@@ -23,9 +23,11 @@ __device__ __forceinline__ float bf16_hi_to_f32(uint32_t word) { return __builti
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // A buffer resource over n bytes at p. Raw buffer stores past the n bytes are
-// dropped by the hardware, so lanes (and rows, with n = 0) that have nothing
-// to store need neither a branch nor a dummy target. The third word is the
-// gfx9 raw-buffer format (32-bit data format, no swizzle).
+// dropped by the hardware and loads there return zero, so lanes (and rows,
+// with n = 0) that have nothing to store or read need neither a branch nor a
+// clamped address. The address is a 64-bit scalar base plus a 32-bit lane
+// offset, with no per-lane 64-bit arithmetic. The third word is the gfx9
+// raw-buffer format (32-bit data format, no swizzle).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t bytes_rsrc(const void* p, uint32_t n) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)n, 0x00020000);
 }
@@ -48,6 +50,10 @@ struct Elt<float> {
         return __builtin_bit_cast(uint32_t, p[i]);
     }
     static __device__ __forceinline__ float cvt(uint32_t b) { return __builtin_bit_cast(float, b); }
+    // raw bits at byte offset o of a buffer resource (zero past its end)
+    static __device__ __forceinline__ uint32_t raw_rsrc(__amdgpu_buffer_rsrc_t r, uint32_t o) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, (int)o, 0, 0);
+    }
     static __device__ __forceinline__ void st(float* __restrict__ p, size_t i, float v) { p[i] = v; }
     // store at byte offset o of a buffer resource (dropped past its end);
     // AUX 2 marks it non-temporal
@@ -73,6 +79,9 @@ struct Elt<uint16_t> {
     static __device__ __forceinline__ float ld(const uint16_t* __restrict__ p, size_t i) { return bf16_to_f32(p[i]); }
     static __device__ __forceinline__ uint32_t raw(const uint16_t* __restrict__ p, size_t i) { return p[i]; }
     static __device__ __forceinline__ float cvt(uint32_t b) { return bf16_to_f32(b); }
+    static __device__ __forceinline__ uint32_t raw_rsrc(__amdgpu_buffer_rsrc_t r, uint32_t o) {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, (int)o, 0, 0);
+    }
     static __device__ __forceinline__ void st(uint16_t* __restrict__ p, size_t i, float v) { p[i] = f32_to_bf16(v); }
     template <int AUX = 0>
     static __device__ __forceinline__ void st_rsrc(__amdgpu_buffer_rsrc_t r, uint32_t o, float v) {

@@ -346,20 +346,20 @@ struct BcRegs {
     static constexpr int V = K * 2 * NH;
     static constexpr int R = (V + 15) / 16;
     float r[R];
-    // bc: fp32 rows [T][2N] (B then C)
-    __device__ __forceinline__ void load(const float* __restrict__ bc, int64_t tb, int64_t T_, int q, int lane) {
+    // bc: fp32 rows [T][2N] (B then C); T < 2^31
+    __device__ __forceinline__ void load(const float* __restrict__ bc, int tb, int T_, int q, int lane) {
         const int j = lane % 16;
-        const float* __restrict__ rows = bc + (size_t)tb * 2 * NS;  // uniform: the block's first row
-        const int last = (int)((T_ - 1 - tb) < K ? (T_ - 1 - tb) : K);  // rows past the tensor read its last
+        // the block's rows inside the tensor as a buffer resource: every lane
+        // loads (no load waits behind a branch) at an offset that does not
+        // change from block to block, and rows past the tensor read zeros
+        // (tokens past the block's end are never used)
+        const int nrow = (T_ - tb) < K ? (T_ - tb) : K;
+        const auto rows = bytes_rsrc(bc + (size_t)tb * 2 * NS, (uint32_t)nrow * (uint32_t)(2 * NS * 4));
 #pragma unroll
         for (int k = 0; k < R; ++k) {
             const int v = k * 16 + j;
             const int kk = v / (2 * NH), kind = (v / NH) % 2, i = v % NH;
-            // every lane loads (the token clamped into the tensor), so that no
-            // load waits behind a branch; tokens past the block's end are
-            // never used
-            const int row = kk < last ? kk : last;
-            const float x = *at_bytes(rows, (uint32_t)((row * 2 * NS + kind * NS + q * NH + i) * 4));
+            const float x = Elt<float>::cvt(Elt<float>::raw_rsrc(rows, (uint32_t)((kk * 2 * NS + kind * NS + q * NH + i) * 4)));
             r[k] = (v < V) ? x : 0.0f;
         }
     }
@@ -791,35 +791,40 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
         uint32_t ru[KQ][kCl], rd[KQ][kCl], rz[KQ][kCl], rg[KQ][kCl];  // raw bits
         float hn[kCl][NH];
         BcRegs<NS> bc;
-        int32_t pos;  // lanes < K: position of token tb + lane (1 past the tensor)
+        int32_t pos;  // lanes < K: position of token tb + lane (0 past the tensor)
     };
     Pre pre[2];
+    // token indices in 32 bits (T < 2^31): their compares and selects stay
+    // on the scalar unit
+    const int T32 = (int)T_;
     auto prefetch = [&](Pre& b, int64_t tb) {
-        // every load is issued on every path (addresses clamped into the
-        // tensors), so the waits for them can count the operations after them
+        // every load is issued on every path, so the waits for them can count
+        // the operations after them: a row past the tensor is an empty buffer
+        // resource and reads zeros
+        const int tb32 = (int)tb;
 #pragma unroll
         for (int j = 0; j < KQ; ++j) {
-            const int64_t t = tb + q + j * SW;
-            // uniform row base, 32-bit lane offset
-            const size_t rb = (size_t)(t < T_ ? t : T_ - 1) * D;
-            const T* __restrict__ u_r = p.u + rb;
-            const T* __restrict__ d_r = p.delta + rb;
-            const T* __restrict__ z_r = GATE ? p.z + rb : nullptr;
-            const T* __restrict__ g_r = p.dout + rb;
+            const int t = tb32 + q + j * SW;
+            const bool in = t < T32;
+            const size_t rb = (size_t)(in ? t : 0) * (size_t)D;
+            const uint32_t nbytes = in ? (uint32_t)D * (uint32_t)sizeof(T) : 0u;
+            const auto ru = bytes_rsrc(p.u + rb, nbytes), rd = bytes_rsrc(p.delta + rb, nbytes);
+            const auto rg = bytes_rsrc(p.dout + rb, nbytes);
+            const auto rz = bytes_rsrc(GATE ? p.z + rb : p.u, GATE ? nbytes : 0u);
 #pragma unroll
             for (int c = 0; c < kCl; ++c) {
-                b.ru[j][c] = Elt<T>::raw(at_bytes(u_r, bo[c]), 0);
-                b.rd[j][c] = Elt<T>::raw(at_bytes(d_r, bo[c]), 0);
-                b.rz[j][c] = GATE ? Elt<T>::raw(at_bytes(z_r, bo[c]), 0) : 0u;
-                b.rg[j][c] = Elt<T>::raw(at_bytes(g_r, bo[c]), 0);
+                b.ru[j][c] = Elt<T>::raw_rsrc(ru, bo[c]);
+                b.rd[j][c] = Elt<T>::raw_rsrc(rd, bo[c]);
+                b.rz[j][c] = GATE ? Elt<T>::raw_rsrc(rz, bo[c]) : 0u;
+                b.rg[j][c] = Elt<T>::raw_rsrc(rg, bo[c]);
             }
         }
         const float* __restrict__ slot = p.ckpt + ((uint64_t)tb >> p.ckshift) * ND;  // tb >= 0
 #pragma unroll
         for (int c = 0; c < kCl; ++c) ck_load<NS, NH>(slot, dd[c], D, n0, true, b.hn[c]);
-        b.bc.load(bcp, tb, T_, q, lane);
-        const int pl = (int)((T_ - 1 - tb) < lane ? (T_ - 1 - tb) : lane);
-        b.pos = *at_bytes(p.pos + tb, (uint32_t)pl * 4u);
+        b.bc.load(bcp, tb32, T32, q, lane);
+        const int np = (T32 - tb32) < kWave ? (T32 - tb32) : kWave;
+        b.pos = (int32_t)Elt<float>::raw_rsrc(bytes_rsrc(p.pos + tb, (uint32_t)np * 4u), (uint32_t)lane * 4u);
     };
 
     // The per-block work in three parts: the prologue maps this wave's own
@@ -879,7 +884,8 @@ __global__ __launch_bounds__(kWave * Split<NS>::SW, 2) void k_scan_bwd_main(
         const int64_t tb = t0 + jb * K;
         const int nb = block_nb(jb);
         // head flags of the block, from the prefetched positions: bit k for token tb + k
-        const uint32_t heads = (uint32_t)__ballot(lane < K && tb + lane < T_ && b.pos == 0);
+        const int hl = (T32 - (int)tb) < K ? (T32 - (int)tb) : K;  // the block's tokens inside the tensor
+        const uint32_t heads = (uint32_t)__ballot(lane < hl && b.pos == 0);
         float hh[K][kCl][NH], ak[K][kCl][NH];
         TokVals tv;
 #pragma unroll
