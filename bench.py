@@ -30,7 +30,7 @@ COPY_CALIB_BYTES = 1 << 30
 PEAK_HBM_GBS = 8000.0    # MI355X HBM3E, vendor figure
 # MI355X fp32 vector peak without packed-FP32 instructions (256 CUs x 4 SIMD16
 # x 2 FLOP per FMA x 2.4 GHz); the vendor's 157.3 TFLOP/s counts packed FP32,
-# which this build does not emit
+# which the library's kernels are compiled without
 PEAK_FP32_TFLOPS = 78.6
 
 # Floating-point operations of the scan backward's own arithmetic per (token,
