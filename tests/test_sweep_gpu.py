@@ -21,7 +21,7 @@ from tests.gpu_harness import (SILU1_MAX, SILU2_MAX, TOL_GRAD, TOL_OUT, Dev, ass
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 400
+N_CASES = 1000
 
 
 def draw_case(i: int) -> dict:
